@@ -1,0 +1,187 @@
+"""CPU oracle, fp64 part: the plain definitions of the sparse main branch, the
+dense LoRA branch, SwiGLU and the FFN block.
+
+TEST INFRASTRUCTURE ONLY (tests, smoke check, CPU-baseline leg of the benchmark).
+
+Pages followed, all titled "SparseLoRA: Accelerating LLM Fine-Tuning with
+Contextual Sparsity":
+  * paper-graph summary §3.4, "Preliminary: What channel sparsity means
+    structurally": y = x W with W in R^{D_in x D_out}; channel sparsity keeps a
+    subset of the D_out output channels and the dropped channels are zero;
+  * §3.4 "FFN structure ... cascaded sparsity": h = SiLU(x W_gate) * (x W_up),
+    y = h W_down; channel i of h is one column of W_gate and W_up and one row
+    of W_down, so the down projection's selection is reused for gate and up;
+  * §3.4 "VO projection sparsity": the selection propagates to W_V;
+  * §3.4 Algorithm 1 steps 4-6: slice, multiply, add the dense LoRA output BAx;
+  * §3.4 "Token Sensitivity", implementation (Figure 8): output tokens take the
+    dense path, context tokens the sparse path, results merged at their
+    original positions, LoRA added for every position;
+  * §3.2 "Information flow during a backward pass": gradients flow only through
+    the channels active in the forward pass; LoRA gradients are dense; the
+    frozen weights receive no gradient;
+  * Paper-Notes page, "整体框架" (same structure) and "Token 敏感性".
+
+Weights are in nn.Linear layout [D_out, D_in] (y = x W_lin^T).  "Output-side"
+sparsity (gate, up, q, k, v) selects output features; "input-side" sparsity
+(down, o) selects input features.  Everything is computed in float64 from
+the given values; the selection (an integer result) comes from ``csa``.
+The masked-dense formulation below is the plain definition: it multiplies by
+a 0/1 mask instead of gathering, so a reader can check it against the pages.
+"""
+from fractions import Fraction
+
+import numpy as np
+
+f64 = np.float64
+
+
+def token_lists(roles):
+    """Context rows (role 0) and output rows (role 1), each ascending.
+    Pinned: tests/test_oracle_dense.py::test_token_lists (brute force)."""
+    r = np.asarray(roles).reshape(-1)
+    return (np.nonzero(r == 0)[0].astype(np.int32), np.nonzero(r != 0)[0].astype(np.int32))
+
+
+def n_keep(C, num, den):
+    """Number of kept channels at sparsity num/den: ceil(C * (1 - num/den)),
+    formed exactly (paper-graph summary §3.4 Algorithm 1 step 3: the top
+    ceil(r * D_out) channels, r = keep ratio).
+    Pinned: tests/test_oracle_dense.py::test_n_keep (Fraction + golden table)."""
+    C, num, den = int(C), int(num), int(den)
+    assert 0 <= num <= den and den > 0
+    return (C * (den - num) + den - 1) // den
+
+
+def expand_gqa(idx_kv, n_rep, head_dim):
+    """Key/value-space selection -> query (or o-input) channel selection:
+    query channel h*d + j is kept iff key/value channel (h // n_rep)*d + j is.
+    Ascending output.  Pinned: tests/test_oracle_dense.py::test_expand_gqa."""
+    idx_kv = np.asarray(idx_kv, dtype=np.int64)
+    g, j = idx_kv // head_dim, idx_kv % head_dim
+    out = [(g * n_rep + r) * head_dim + j for r in range(n_rep)]
+    return np.sort(np.concatenate(out)).astype(np.int32) if out else np.zeros(0, np.int32)
+
+
+def keep_mask(T, C, roles, idx):
+    """M[t, c] = 1 if token t is an output token or channel c is selected."""
+    sel = np.zeros(C, dtype=bool)
+    sel[np.asarray(idx, dtype=np.int64)] = True
+    out = (np.asarray(roles).reshape(-1) != 0)
+    return (out[:T, None] | sel[None, :]).astype(f64)
+
+
+def sparse_linear_fwd(side, x, W, roles, idx):
+    """Main-branch forward, masked dense.
+    side "out": y[t, c] = sum_i x[t, i] W[c, i], set to 0 for context t and
+                unselected c.
+    side "in" : y[t, o] = sum_{c kept for t} x[t, c] W[o, c], kept = all c for
+                output tokens and the selected c for context tokens.
+    Pinned: tests/test_oracle_dense.py (sparsity 0 = dense; sliced = masked;
+    output rows invariant under the selection; adjoint identity with bwd)."""
+    x, W = np.asarray(x, f64), np.asarray(W, f64)
+    T = x.shape[0]
+    if side == "out":
+        return (x @ W.T) * keep_mask(T, W.shape[0], roles, idx)
+    if side == "in":
+        return (x * keep_mask(T, W.shape[1], roles, idx)) @ W.T
+    raise ValueError(side)
+
+
+def sparse_linear_bwd(side, dy, W, roles, idx):
+    """Input gradient of ``sparse_linear_fwd`` with the selection held fixed
+    (the adjoint of the same masked linear map); the frozen W gets none.
+    side "out": dx = (dy * M) W;  side "in": dx = (dy W) * M.
+    Pinned: adjoint identity and torch.autograd in tests/test_oracle_dense.py."""
+    dy, W = np.asarray(dy, f64), np.asarray(W, f64)
+    T = dy.shape[0]
+    if side == "out":
+        return (dy * keep_mask(T, W.shape[0], roles, idx)) @ W
+    if side == "in":
+        return (dy @ W) * keep_mask(T, W.shape[1], roles, idx)
+    raise ValueError(side)
+
+
+def lora_fwd(x, A, B, scale):
+    """Dense LoRA branch: xl = x A^T, y_lora = scale * xl B^T (every token and
+    every channel).  A: [r, D_in], B: [D_out, r].  Returns (xl, y_lora)."""
+    x, A, B = np.asarray(x, f64), np.asarray(A, f64), np.asarray(B, f64)
+    xl = x @ A.T
+    return xl, scale * (xl @ B.T)
+
+
+def lora_bwd(x, xl, dy, A, B, scale):
+    """Gradients of the LoRA branch: gB = dy B; dA = scale gB^T x;
+    dB = scale dy^T xl; dx = scale gB A.  Returns (dx, dA, dB).
+    Pinned: finite differences and torch.autograd in tests/test_oracle_dense.py."""
+    x, xl, dy = np.asarray(x, f64), np.asarray(xl, f64), np.asarray(dy, f64)
+    A, B = np.asarray(A, f64), np.asarray(B, f64)
+    gB = dy @ B
+    return scale * (gB @ A), scale * (gB.T @ x), scale * (dy.T @ xl)
+
+
+def silu(z):
+    z = np.asarray(z, f64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_fwd(g, u):
+    """h = SiLU(g) * u (paper-graph summary §3.4, FFN structure)."""
+    return silu(g) * np.asarray(u, f64)
+
+
+def swiglu_bwd(dh, g, u):
+    """dg = dh * u * SiLU'(g), du = dh * SiLU(g), SiLU'(z) = s (1 + z (1 - s)),
+    s = sigmoid(z)."""
+    dh, g, u = np.asarray(dh, f64), np.asarray(g, f64), np.asarray(u, f64)
+    s = 1.0 / (1.0 + np.exp(-g))
+    return dh * u * (s * (1.0 + g * (1.0 - s))), dh * (g * s)
+
+
+def ffn_block_fwd(inp, idx, g_u=None):
+    """Forward of one sparse SwiGLU FFN block with LoRA on gate, up, down.
+    idx: selected intermediate channels (shared by gate, up and down).
+    ``g_u`` optionally overrides (g, u) with given values (per-op checks)."""
+    x, roles, s = inp["x"], inp["roles"], inp["scale"]
+    out = {}
+    if g_u is None:
+        xl_g, lg = lora_fwd(x, inp["A_gate"], inp["B_gate"], s)
+        xl_u, lu = lora_fwd(x, inp["A_up"], inp["B_up"], s)
+        g = sparse_linear_fwd("out", x, inp["W_gate"], roles, idx) + lg
+        u = sparse_linear_fwd("out", x, inp["W_up"], roles, idx) + lu
+        out.update(xl_gate=xl_g, xl_up=xl_u)
+    else:
+        g, u = (np.asarray(a, f64) for a in g_u)
+    h = swiglu_fwd(g, u)
+    xl_d, ld = lora_fwd(h, inp["A_down"], inp["B_down"], s)
+    y = sparse_linear_fwd("in", h, inp["W_down"], roles, idx) + ld
+    out.update(g=g, u=u, h=h, xl_down=xl_d, y=y)
+    return out
+
+
+def ffn_block_bwd(inp, fwd, idx, dy=None):
+    """Backward of ``ffn_block_fwd`` for upstream gradient dy (default inp["dy"]):
+    input gradient dx and the six LoRA gradients; no frozen-weight gradient."""
+    x, roles, s = inp["x"], inp["roles"], inp["scale"]
+    dy = inp["dy"] if dy is None else dy
+    dh_l, dA_d, dB_d = lora_bwd(fwd["h"], fwd["xl_down"], dy, inp["A_down"], inp["B_down"], s)
+    dh = sparse_linear_bwd("in", dy, inp["W_down"], roles, idx) + dh_l
+    dg, du = swiglu_bwd(dh, fwd["g"], fwd["u"])
+    dx_g, dA_g, dB_g = lora_bwd(x, fwd["xl_gate"], dg, inp["A_gate"], inp["B_gate"], s)
+    dx_u, dA_u, dB_u = lora_bwd(x, fwd["xl_up"], du, inp["A_up"], inp["B_up"], s)
+    dx = (sparse_linear_bwd("out", dg, inp["W_gate"], roles, idx)
+          + sparse_linear_bwd("out", du, inp["W_up"], roles, idx) + dx_g + dx_u)
+    return dict(dh=dh, dg=dg, du=du, dx=dx, dA_gate=dA_g, dB_gate=dB_g, dA_up=dA_u,
+                dB_up=dB_u, dA_down=dA_d, dB_down=dB_d)
+
+
+def max_abs_rel(got, ref):
+    """max |got - ref| / max(max |ref|, 1e-30), per tensor."""
+    got, ref = np.asarray(got, f64), np.asarray(ref, f64)
+    return float(np.max(np.abs(got - ref)) / max(float(np.max(np.abs(ref))) if ref.size else 0.0,
+                                                  1e-30)) if ref.size else 0.0
+
+
+def estimator_cost_ratio(k, d_in, d_out):
+    """Estimator cost relative to the dense product: k (D_in + D_out) / (D_in D_out)
+    (paper-graph summary §3.4, SVD estimator "Cost analysis")."""
+    return Fraction(k * (d_in + d_out), d_in * d_out)

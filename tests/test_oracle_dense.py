@@ -1,0 +1,223 @@
+"""Pins of the oracle's fp64 part (main branch, LoRA, SwiGLU, FFN block) and of
+the input recipe's estimator factors, against special cases, library
+routines, exact identities and calculus."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from workloads.configs import CONFIGS, scaled
+from workloads.gen import make_ffn_inputs, roles_for, svd_factor_pair
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")
+
+
+# ---------------------------------------------------------------- small helpers
+
+def test_token_lists():
+    roles = np.array([0, 1, 1, 0, 0, 1, 0], np.uint8)
+    ctx, out = ref.token_lists(roles)
+    assert ctx.tolist() == [0, 3, 4, 6] and out.tolist() == [1, 2, 5]
+    for cid, cfg in CONFIGS.items():
+        ctx, out = ref.token_lists(roles_for(cfg))
+        assert len(out) == cfg.batch * cfg.out_per_seq
+        assert sorted(np.concatenate([ctx, out]).tolist()) == list(range(cfg.tokens))
+        for b in range(cfg.batch):                        # contiguous tail per sequence
+            tail = list(range(b * cfg.seq + cfg.seq - cfg.out_per_seq, (b + 1) * cfg.seq))
+            assert set(tail) <= set(out.tolist())
+
+
+def test_n_keep_integer_and_float_trap():
+    for C in (1, 7, 688, 1000, 1024, 5120, 13824, 14336):
+        for num, den in ((0, 1), (1, 2), (7, 10), (3, 10), (1, 35), (4, 5), (99, 100), (1, 1)):
+            exact = Fraction(C) * (1 - Fraction(num, den))
+            want = -((-exact.numerator) // exact.denominator)
+            assert ref.n_keep(C, num, den) == want
+    # the floating-point reading would keep 301 of 1000 at 70% sparsity
+    assert int(np.ceil((1 - 0.7) * 1000)) == 301 and ref.n_keep(1000, 7, 10) == 300
+    # configuration table
+    assert ref.n_keep(688, 1, 2) == 344
+    assert ref.n_keep(14336, 7, 10) == 4301
+    assert ref.n_keep(13824, 7, 10) == 4148
+    cfg5 = CONFIGS[5]
+    got = [ref.n_keep(14336, *cfg5.layer_sparsity(l)) for l in (0, 3, 4, 17, 31)]
+    assert got == [14336, 14336, 13927, 8602, 2868]
+    got = [ref.n_keep(1024, *cfg5.layer_sparsity(l)) for l in (4, 17, 31)]
+    assert got == [995, 615, 205]
+
+
+def test_golden_estimator_cost_ratio():
+    with open(GOLDEN) as f:
+        g = json.load(f)["estimator_cost_ratio"]
+    r = ref.estimator_cost_ratio(g["k"], g["d_in"], g["d_out"])
+    assert round(float(r), g["printed_digits"]) == g["printed"]
+
+
+def test_expand_gqa_enumeration(rng):
+    H_kv, n_rep, d = 4, 3, 8
+    idx_kv = np.sort(rng.choice(H_kv * d, 11, replace=False)).astype(np.int32)
+    q = ref.expand_gqa(idx_kv, n_rep, d)
+    kv_set = set(idx_kv.tolist())
+    want = [c for c in range(H_kv * n_rep * d) if ((c // d) // n_rep) * d + c % d in kv_set]
+    assert q.tolist() == want and len(q) == n_rep * len(idx_kv)
+    assert ref.expand_gqa(idx_kv, 1, d).tolist() == idx_kv.tolist()
+
+
+# ---------------------------------------------------------------- main branch
+
+def _small(rng, T=40, Din=24, Dout=30, r=3):
+    roles = (np.arange(T) % 10 >= 7).astype(np.uint8)
+    x = rng.standard_normal((T, Din))
+    W = rng.standard_normal((Dout, Din))
+    A = rng.standard_normal((r, Din))
+    B = rng.standard_normal((Dout, r))
+    return roles, x, W, A, B
+
+
+def test_sparsity_zero_is_textbook_dense_lora(rng):
+    roles, x, W, A, B = _small(rng)
+    s = 2.0
+    xt, Wt, At, Bt = (torch.tensor(a, dtype=torch.float64) for a in (x, W, A, B))
+    dense = torch.nn.functional.linear(xt, Wt) + s * torch.nn.functional.linear(
+        torch.nn.functional.linear(xt, At), Bt)
+    all_out = np.arange(W.shape[0])
+    y = ref.sparse_linear_fwd("out", x, W, roles, all_out) + ref.lora_fwd(x, A, B, s)[1]
+    assert np.allclose(y, dense.numpy(), rtol=1e-13, atol=1e-13)
+    all_in = np.arange(W.shape[1])
+    y2 = ref.sparse_linear_fwd("in", x, W, roles, all_in) + ref.lora_fwd(x, A, B, s)[1]
+    assert np.allclose(y2, dense.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_sliced_equals_masked(rng):
+    roles, x, W, A, B = _small(rng)
+    ctx, out = ref.token_lists(roles)
+    idx = np.sort(rng.choice(W.shape[0], 11, replace=False))
+    y = ref.sparse_linear_fwd("out", x, W, roles, idx)
+    sliced = np.zeros_like(y)
+    sliced[out] = x[out] @ W.T
+    sliced[np.ix_(ctx, idx)] = x[ctx] @ W[idx].T
+    assert np.allclose(y, sliced, rtol=1e-13, atol=1e-13)
+    assert np.all(y[np.ix_(ctx, np.setdiff1d(np.arange(W.shape[0]), idx))] == 0.0)
+    idx_in = np.sort(rng.choice(W.shape[1], 9, replace=False))
+    y = ref.sparse_linear_fwd("in", x, W, roles, idx_in)
+    sliced = np.zeros_like(y)
+    sliced[out] = x[out] @ W.T
+    sliced[ctx] = x[np.ix_(ctx, idx_in)] @ W[:, idx_in].T
+    assert np.allclose(y, sliced, rtol=1e-13, atol=1e-13)
+
+
+def test_output_rows_untouched_by_selection(rng):
+    roles, x, W, A, B = _small(rng)
+    _, out = ref.token_lists(roles)
+    for side, C in (("out", W.shape[0]), ("in", W.shape[1])):
+        a = ref.sparse_linear_fwd(side, x, W, roles, np.arange(0, C, 2))
+        b = ref.sparse_linear_fwd(side, x, W, roles, np.arange(3))
+        c = ref.sparse_linear_fwd(side, x, W, roles, np.arange(0))
+        assert np.array_equal(a[out], b[out]) and np.array_equal(a[out], c[out])
+        dy = rng.standard_normal((x.shape[0], W.shape[0]))
+        da = ref.sparse_linear_bwd(side, dy, W, roles, np.arange(0, C, 2))
+        db = ref.sparse_linear_bwd(side, dy, W, roles, np.arange(0))
+        assert np.array_equal(da[out], db[out])
+
+
+def test_adjoint_identity(rng):
+    roles, x, W, A, B = _small(rng)
+    for side, C in (("out", W.shape[0]), ("in", W.shape[1])):
+        idx = np.sort(rng.choice(C, C // 3, replace=False))
+        dy = rng.standard_normal((x.shape[0], W.shape[0]))
+        lhs = np.sum(ref.sparse_linear_fwd(side, x, W, roles, idx) * dy)
+        rhs = np.sum(x * ref.sparse_linear_bwd(side, dy, W, roles, idx))
+        assert abs(lhs - rhs) <= 1e-12 * (abs(lhs) + 1.0)
+
+
+def _ffn_small(rng):
+    cfg = scaled(CONFIGS[1], batch=2, seq=12, out_per_seq=3, hidden=10, inter=14,
+                 lora_rank=3, est_rank=2, dtype="f32")
+    inp = make_ffn_inputs(cfg, with_factors=False)
+    inp = {k: (np.asarray(v, np.float64) if isinstance(v, np.ndarray) and k != "roles" else v)
+           for k, v in inp.items()}
+    # larger LoRA factors so their gradients are well above rounding noise
+    for k in ("A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down"):
+        inp[k] = rng.standard_normal(inp[k].shape) * 0.5
+    idx = np.sort(rng.choice(cfg.inter, 6, replace=False))
+    return cfg, inp, idx
+
+
+def test_ffn_block_backward_matches_autograd(rng):
+    cfg, inp, idx = _ffn_small(rng)
+    fwd = ref.ffn_block_fwd(inp, idx)
+    bwd = ref.ffn_block_bwd(inp, fwd, idx)
+    T = cfg.tokens
+    M = torch.tensor(ref.keep_mask(T, cfg.inter, inp["roles"], idx))
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
+    s = inp["scale"]
+    lin = torch.nn.functional.linear
+    g = lin(t["x"], t["W_gate"]) * M + s * lin(lin(t["x"], t["A_gate"]), t["B_gate"])
+    u = lin(t["x"], t["W_up"]) * M + s * lin(lin(t["x"], t["A_up"]), t["B_up"])
+    h = torch.nn.functional.silu(g) * u
+    y = lin(h * M, t["W_down"]) + s * lin(lin(h, t["A_down"]), t["B_down"])
+    assert np.allclose(y.detach().numpy(), fwd["y"], rtol=1e-12, atol=1e-12)
+    (y * t["dy"]).sum().backward()
+    assert np.allclose(t["x"].grad.numpy(), bwd["dx"], rtol=1e-10, atol=1e-12)
+    for p in ("gate", "up", "down"):
+        assert np.allclose(t["A_" + p].grad.numpy(), bwd["dA_" + p], rtol=1e-10, atol=1e-12)
+        assert np.allclose(t["B_" + p].grad.numpy(), bwd["dB_" + p], rtol=1e-10, atol=1e-12)
+
+
+def test_lora_grads_finite_differences(rng):
+    cfg, inp, idx = _ffn_small(rng)
+
+    def loss(d):
+        return float(np.sum(ref.ffn_block_fwd(d, idx)["y"] * inp["dy"]))
+
+    bwd = ref.ffn_block_bwd(inp, ref.ffn_block_fwd(inp, idx), idx)
+    eps = 1e-6
+    for name in ("A_gate", "B_up", "A_down", "B_down"):
+        for _ in range(4):
+            pos = tuple(rng.integers(0, s) for s in inp[name].shape)
+            d1, d2 = dict(inp), dict(inp)
+            d1[name] = inp[name].copy()
+            d2[name] = inp[name].copy()
+            d1[name][pos] += eps
+            d2[name][pos] -= eps
+            fd = (loss(d1) - loss(d2)) / (2 * eps)
+            assert abs(fd - bwd["d" + name][pos]) <= 1e-6 * (1 + abs(fd))
+
+
+def test_unselected_context_channels_carry_lora_only(rng):
+    cfg, inp, idx = _ffn_small(rng)
+    fwd = ref.ffn_block_fwd(inp, idx)
+    ctx, _ = ref.token_lists(inp["roles"])
+    drop = np.setdiff1d(np.arange(cfg.inter), idx)
+    lora_g = ref.lora_fwd(inp["x"], inp["A_gate"], inp["B_gate"], inp["scale"])[1]
+    assert np.array_equal(fwd["g"][np.ix_(ctx, drop)], lora_g[np.ix_(ctx, drop)])
+
+
+# ---------------------------------------------------------------- factors (input recipe)
+
+@pytest.mark.parametrize("shape,k", [((120, 80), 8), ((60, 200), 16), ((2100, 2300), 16)])
+def test_factors_eckart_young(rng, shape, k):
+    W = (rng.standard_normal(shape) * 0.02).astype(np.float32)   # nn.Linear [D_out, D_in]
+    WA_t, WB = svd_factor_pair(W, k)
+    Wm = W.T.astype(np.float64)
+    s = np.linalg.svd(Wm, compute_uv=False)
+    P = WA_t.T.astype(np.float64) @ WB.astype(np.float64)
+    R = Wm - P
+    assert abs(np.sum(R * R) - np.sum(s[k:] ** 2)) <= 1e-5 * np.sum(Wm * Wm)
+    assert abs(np.linalg.norm(R, 2) - s[k]) <= 1e-4 * s[0]
+    # W_A^T W_A = diag(s_k) = W_B W_B^T (the sqrt(s) split on both sides)
+    GA = WA_t.astype(np.float64) @ WA_t.T.astype(np.float64)
+    GB = WB.astype(np.float64) @ WB.T.astype(np.float64)
+    assert np.allclose(GA, np.diag(s[:k]), atol=1e-5 * s[0])
+    assert np.allclose(GB, np.diag(s[:k]), atol=1e-5 * s[0])
+
+
+def test_full_rank_factors_reconstruct(rng):
+    W = rng.standard_normal((30, 20)).astype(np.float32)
+    WA_t, WB = svd_factor_pair(W, 20)
+    assert np.allclose(WA_t.T.astype(np.float64) @ WB, W.T, atol=1e-5)
