@@ -1,0 +1,196 @@
+#!/usr/bin/env python3
+"""Benchmark of the contextually-sparse LoRA FFN block (forward + backward) on
+one MI355X at the LLaMA3-8B FFN shape: hidden 4096, intermediate 14336,
+batch 8 x seq 512 (last 128 tokens of each sequence are output tokens),
+bf16, LoRA rank 16 on gate/up/down, estimator rank 16, 70% channel sparsity.
+
+One step = token split, estimator, SwiGLU-L2 scoring, top-n selection,
+gathered/dense main-branch GEMMs, dense LoRA, SwiGLU, and the whole backward
+(input gradient and the six LoRA gradients), on synthetic inputs already in
+HBM.  Prints one JSON line (rank 0, N = 1).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def build_block(inp, cfg, dense):
+    import numpy as np
+    import torch
+    from contextual_sparsity_lora_amd.ffn import SparseFFN
+    dev = "cuda:0"
+    t = {k: torch.from_numpy(v).to(torch.bfloat16).to(dev) for k, v in inp.items()
+         if isinstance(v, np.ndarray) and k.startswith(("x", "W_", "A_", "B_", "dy"))}
+    blk = SparseFFN(t["W_gate"], t["W_up"], t["W_down"], t["A_gate"], t["B_gate"], t["A_up"],
+                    t["B_up"], t["A_down"], t["B_down"],
+                    torch.from_numpy(np.ascontiguousarray(inp["WA_t_gu"].T)).to(dev),
+                    torch.from_numpy(inp["WB_gate"]).to(dev), torch.from_numpy(inp["WB_up"]).to(dev),
+                    inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense)
+    roles = torch.from_numpy(inp["roles"]).to(dev)
+    return blk, t["x"], roles, t["dy"]
+
+
+def time_steps(blk, x, roles, dy, T_c, steps, warmup, ops, record=False):
+    import torch
+    for _ in range(warmup):
+        blk.forward(x, roles, T_c)
+        blk.backward(dy)
+    torch.cuda.synchronize()
+    if record:
+        ops.timing_reset(0)
+        ops.timing_enable(0, True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        blk.forward(x, roles, T_c)
+        blk.backward(dy)
+    stop.record()
+    torch.cuda.synchronize()
+    if record:
+        ops.timing_enable(0, False)
+    return start.elapsed_time(stop) / steps
+
+
+def cpu_baseline(inp, cfg):
+    """The CPU oracle on one sequence of the workload (512 tokens: 384 context,
+    128 output): selection (fp32 C) + masked-dense fp64 forward and backward."""
+    import numpy as np
+    from oracle import csa, reference as ref
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    S = cfg.seq
+    sub = dict(inp)
+    for k in ("x", "dy"):
+        sub[k] = inp[k][:S]
+    sub["roles"] = inp["roles"][:S]
+    t0 = time.perf_counter()
+    ctx, _ = ref.token_lists(sub["roles"])
+    sc = csa.ssq_swiglu(csa.stage1(sub["x"], ctx, inp["WA_t_gu"]), inp["WB_gate"], inp["WB_up"])
+    idx = csa.select(sc, ref.n_keep(cfg.inter, *cfg.ffn_sparsity))
+    f = ref.ffn_block_fwd(sub, idx)
+    ref.ffn_block_bwd(sub, f, idx)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one sequence of the workload ({S} tokens: {S - cfg.out_per_seq} context, "
+                      f"{cfg.out_per_seq} output), fp32 selection + fp64 masked-dense fwd+bwd, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from contextual_sparsity_lora_amd import ops
+    from workloads.configs import CONFIGS
+    from workloads.gen import make_ffn_inputs
+
+    cfg = CONFIGS[2]
+    t0 = time.perf_counter()
+    inp = make_ffn_inputs(cfg)
+    print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    blk, x, roles, dy = build_block(inp, cfg, dense=False)
+    ms = time_steps(blk, x, roles, dy, cfg.ctx_tokens, args.steps, args.warmup, ops, record=True)
+    T = cfg.tokens
+    per_class = {}
+    for c in ops.timing_classes():
+        n, tms, fl, by = ops.timing_query(0, c)
+        if n:
+            per_class[c] = {"launches_per_step": n / args.steps, "ms_per_step": tms / args.steps,
+                            "gflop_per_step": fl / args.steps / 1e9,
+                            "gbyte_per_step": by / args.steps / 1e9}
+    print(f"[bench] sparse step {ms:.3f} ms", file=sys.stderr, flush=True)
+    for c, v in sorted(per_class.items(), key=lambda kv: -kv[1]["ms_per_step"]):
+        print(f"[bench]   {c:13s} {v['ms_per_step']:8.3f} ms  {v['gflop_per_step']:9.2f} GF  "
+              f"{v['gbyte_per_step']:7.3f} GB  x{v['launches_per_step']:.0f}", file=sys.stderr)
+    # dominant kernel: the class with the most time per step
+    dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
+    dn, dms, dfl, dby = ops.timing_query(0, dom)
+    if dom.startswith("gemm"):
+        achieved = dfl / (dms * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "launches": dn, "avg_launch_ms": round(dms / dn, 4)}
+    else:
+        achieved = dby / (dms * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": None, "launches": dn, "avg_launch_ms": round(dms / dn, 4)}
+    gemm_fl = sum(v["gflop_per_step"] for c, v in per_class.items() if c.startswith("gemm"))
+    gemm_ms = sum(v["ms_per_step"] for c, v in per_class.items() if c.startswith("gemm"))
+    step_gf = sum(v["gflop_per_step"] for v in per_class.values())
+    ops.timing_reset(0)
+    extra = {"gemm_tflops": round(gemm_fl / gemm_ms, 2) if gemm_ms else None,
+             "mfma_util_gemm": round(gemm_fl / gemm_ms / PEAK_BF16_TFLOPS, 4) if gemm_ms else None,
+             "step_tflops": round(step_gf / ms, 2), "per_class": per_class}
+    if not args.no_dense:
+        del blk
+        torch.cuda.empty_cache()
+        dblk, x, roles, dy = build_block(inp, cfg, dense=True)
+        dms_step = time_steps(dblk, x, roles, dy, cfg.ctx_tokens, args.steps, args.warmup, ops)
+        extra["dense_ms_per_step"] = round(dms_step, 4)
+        extra["speedup_vs_dense"] = round(dms_step / ms, 3)
+        print(f"[bench] dense step {dms_step:.3f} ms", file=sys.stderr, flush=True)
+        del dblk
+    out = {
+        "metric": "sparse-LoRA linear fwd+bwd tokens/s and MFMA util at LLaMA3-8B FFN shape, 1 GPU",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-ffn-block-fwd-bwd", "hidden": cfg.hidden,
+                   "intermediate": cfg.inter, "batch": cfg.batch, "seq": cfg.seq,
+                   "output_tokens_per_seq": cfg.out_per_seq, "lora_rank": cfg.lora_rank,
+                   "estimator_rank": cfg.est_rank, "ffn_sparsity": "7/10",
+                   "kept_channels": blk_n(cfg), "global_batch": cfg.batch, "seq_len": cfg.seq,
+                   "parallelism": "single-gpu"},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    out.update(extra)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, cfg)
+        print(f"[bench] cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s", file=sys.stderr,
+              flush=True)
+    print(json.dumps(out), flush=True)
+
+
+def blk_n(cfg):
+    from contextual_sparsity_lora_amd.ffn import keep_count
+    return keep_count(cfg.inter, *cfg.ffn_sparsity)
+
+
+if __name__ == "__main__":
+    main()

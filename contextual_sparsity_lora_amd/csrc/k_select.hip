@@ -1,0 +1,473 @@
+// Channel-selection kernels: token-role split, estimator stage 1, estimator
+// stage 2 fused with the channel criteria, the QK group product, radix top-n,
+// and index propagation.
+//
+// Pages (all titled "SparseLoRA: Accelerating LLM Fine-Tuning with Contextual
+// Sparsity"): paper-graph summary ("PG") §3.4 "SVD Sparsity Estimator" and its
+// Algorithm 1 (runtime usage), §3.4 "Oracle Sparse Neuron Selection
+// Criteria", §3.4 "Token Sensitivity"; Paper-Notes ("PN") "SVD 稀疏估计器",
+// "L2 Norm 准则", "QK Norm 准则".
+//
+// The pages fix no floating-point detail, so the score arithmetic is fixed
+// here as a sequence of binary32 operations (this file is built with
+// -ffp-contract=off and IEEE denormals; every fused multiply-add is written
+// out).  With that, the selected channel set is reproducible bit for bit:
+//   R64(a, b, L): p[0..63] = +0; p[m mod 64] = fma(a[m], b[m], p[m mod 64])
+//   for m ascending; then p[l] += p[l + w] for w = 32, 16, ..., 1 (l < w);
+//   result p[0].
+//   stage 1:  xa[m, j] = R64 over i of (x[ctx[m], i], W_A[i, j])
+//   stage 2:  y_hat[m, c] = fma chain over j ascending from +0
+//   SiLU:     z / (1 + exp_sl(-z)), exp_sl below
+//   ssq[c]:   R64 over context tokens m of (v[m, c], v[m, c])
+#include "sl_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr int WAVE = 64;
+
+// ---------------------------------------------------------------- exp / SiLU
+// exp by Cody-Waite additive range reduction (Cody & Waite, "Software Manual
+// for the Elementary Functions", 1980) and the degree-7 Taylor polynomial.
+// Constants, each the binary32 rounding of its mathematical value:
+//   1/ln 2                          0x3FB8AA3B
+//   ln 2 to 12 significant bits     2839/4096 = 0x3F317000 (exact multiples)
+//   ln 2 - 2839/4096                0x3805FDF4
+//   1/i!, i = 0..7                  1, 1, 1/2, 0x3E2AAAAB, 0x3D2AAAAB,
+//                                   0x3C088889, 0x3AB60B61, 0x39500D01
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
+__device__ __forceinline__ float exp_sl(float z) {
+    if (__builtin_isnan(z)) return z;
+    if (z >= 89.0f) return __builtin_huge_valf();
+    if (z <= -104.0f) return 0.0f;
+    const float LOG2E = __uint_as_float(0x3FB8AA3Bu);
+    const float LN2_HI = __uint_as_float(0x3F317000u);
+    const float LN2_LO = __uint_as_float(0x3805FDF4u);
+    float t = z * LOG2E;
+    float n = __builtin_rintf(t);
+    float r = __builtin_fmaf(-n, LN2_HI, z);
+    r = __builtin_fmaf(-n, LN2_LO, r);
+    float p = __uint_as_float(0x39500D01u);
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3AB60B61u));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3C088889u));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3D2AAAABu));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3E2AAAABu));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    int ni = (int)n;
+    int a = ni >> 1;  // floor(ni / 2)
+    int b = ni - a;
+    float s = p * pow2i(a);
+    return s * pow2i(b);
+}
+
+__device__ __forceinline__ float silu_sl(float z) {
+    float e = exp_sl(-z);
+    float den = 1.0f + e;
+    return z / den;
+}
+
+__device__ __forceinline__ uint32_t score_key(float s) {
+    return __builtin_isnan(s) ? 0x7FC00000u : __float_as_uint(s);
+}
+
+// ---------------------------------------------------------------- block scan
+// Exclusive prefix sum over a 1024-thread block; returns the exclusive value
+// and writes the block total to *total.
+__device__ int block_exclusive_scan(int v, int* sh /*[32]*/, int* total) {
+    const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
+    int x = v;
+    for (int o = 1; o < WAVE; o <<= 1) {
+        int y = __shfl_up(x, o, WAVE);
+        if (lane >= o) x += y;
+    }
+    if (lane == WAVE - 1) sh[wid] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int w = 0; w < (int)(blockDim.x / WAVE); ++w) {
+            int t = sh[w];
+            sh[w] = run;
+            run += t;
+        }
+        sh[16] = run;
+    }
+    __syncthreads();
+    int excl = sh[wid] + x - v;
+    *total = sh[16];
+    __syncthreads();
+    return excl;
+}
+
+// ---------------------------------------------------------------- token split
+__global__ __launch_bounds__(1024) void token_split_kernel(const uint8_t* __restrict__ roles,
+                                                           int64_t T, int32_t* ctx, int64_t Tc,
+                                                           int32_t* out, int64_t To, int* flag) {
+    __shared__ int sh[32];
+    const int64_t chunk = (T + blockDim.x - 1) / blockDim.x;
+    const int64_t beg = (int64_t)threadIdx.x * chunk;
+    const int64_t end = beg + chunk < T ? beg + chunk : T;
+    int nc = 0;
+    for (int64_t t = beg; t < end; ++t) nc += roles[t] == 0;
+    int total;
+    int pc = block_exclusive_scan(nc, sh, &total);
+    int64_t po = beg < T ? beg - pc : 0;  // output rows before this chunk
+    for (int64_t t = beg; t < end; ++t) {
+        if (roles[t] == 0) {
+            if (pc < Tc) ctx[pc] = (int32_t)t;
+            ++pc;
+        } else {
+            if (po < To) out[po] = (int32_t)t;
+            ++po;
+        }
+    }
+    if (threadIdx.x == 0 && (int64_t)total != Tc) atomicOr(flag, 1);
+}
+
+// ---------------------------------------------------------------- stage 1
+// One wave per pair of context tokens; lane l owns the chains i = l (mod 64).
+// W_A is read in its math layout [D, kt] so a lane loads 4 j-values at once.
+template <bool BF16>
+__global__ __launch_bounds__(256) void stage1_kernel(const void* __restrict__ xv, int64_t ldx,
+                                                     const int32_t* __restrict__ rows, int64_t Tc,
+                                                     int64_t D, const float* __restrict__ WA,
+                                                     int64_t kt, float* __restrict__ xa) {
+    constexpr int TPW = 2;   // tokens per wave
+    constexpr int JC = 32;   // j-chunk held in registers
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
+    const int64_t m0 = wave * TPW;
+    if (m0 >= Tc) return;
+    int64_t rowoff[TPW];
+    bool rv[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        rv[t] = m0 + t < Tc;
+        rowoff[t] = rv[t] ? (int64_t)rows[m0 + t] * ldx : 0;
+    }
+    for (int64_t jc = 0; jc < kt; jc += JC) {
+        const int jn = (int)((kt - jc) < JC ? (kt - jc) : JC);
+        float acc[TPW][JC];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int j = 0; j < JC; ++j) acc[t][j] = 0.0f;
+        for (int64_t i = lane; i < D; i += WAVE) {
+            float xs[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                if (BF16) xs[t] = bf16_to_f32(((const bf16_t*)xv)[rowoff[t] + i]);
+                else xs[t] = ((const float*)xv)[rowoff[t] + i];
+            }
+            const float* wr = WA + i * kt + jc;
+            if (jn == JC && (kt % 4) == 0) {
+#pragma unroll
+                for (int j4 = 0; j4 < JC; j4 += 4) {
+                    float4 w = *(const float4*)(wr + j4);
+#pragma unroll
+                    for (int t = 0; t < TPW; ++t) {
+                        acc[t][j4 + 0] = __builtin_fmaf(xs[t], w.x, acc[t][j4 + 0]);
+                        acc[t][j4 + 1] = __builtin_fmaf(xs[t], w.y, acc[t][j4 + 1]);
+                        acc[t][j4 + 2] = __builtin_fmaf(xs[t], w.z, acc[t][j4 + 2]);
+                        acc[t][j4 + 3] = __builtin_fmaf(xs[t], w.w, acc[t][j4 + 3]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < JC; ++j) {
+                    if (j < jn) {
+                        float w = wr[j];
+#pragma unroll
+                        for (int t = 0; t < TPW; ++t) acc[t][j] = __builtin_fmaf(xs[t], w, acc[t][j]);
+                    }
+                }
+            }
+        }
+        // pairwise tree over the 64 chains: p[l] = p[l] + p[l + w]
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int j = 0; j < JC; ++j) {
+                float v = acc[t][j];
+#pragma unroll
+                for (int w = 32; w >= 1; w >>= 1) {
+                    float o = __shfl_down(v, w, WAVE);
+                    v = v + o;
+                }
+                acc[t][j] = v;
+            }
+        if (lane == 0) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                if (rv[t])
+#pragma unroll
+                    for (int j = 0; j < JC; ++j)
+                        if (j < jn) xa[(m0 + t) * kt + jc + j] = acc[t][j];
+        }
+    }
+}
+
+// ---------------------------------------------------------------- stage 2 + criterion
+// Block = 8 waves over 64 channels (one channel per lane).  Wave w owns the
+// token chains l = 8w .. 8w+7 (tokens m with m mod 64 = l), so the 64 chains
+// of a channel are spread over the block; xa rows are wave-uniform and come
+// in through scalar loads.  The chains meet in LDS for the pairwise tree.
+template <int CRIT, int K>
+__device__ __forceinline__ float crit_value(const float* __restrict__ row, int64_t off0,
+                                            int64_t off1, const float* wg, const float* wu,
+                                            int krt) {
+    if (K > 0) {
+        float g = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) g = __builtin_fmaf(row[off0 + j], wg[j], g);
+        if (CRIT == 0) return g;
+        float u = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) u = __builtin_fmaf(row[off1 + j], wu[j], u);
+        return silu_sl(g) * u;
+    } else {
+        float g = 0.0f;
+        for (int j = 0; j < krt; ++j) g = __builtin_fmaf(row[off0 + j], wg[j], g);
+        if (CRIT == 0) return g;
+        float u = 0.0f;
+        for (int j = 0; j < krt; ++j) u = __builtin_fmaf(row[off1 + j], wu[j], u);
+        return silu_sl(g) * u;
+    }
+}
+
+template <int CRIT, int K>
+__global__ __launch_bounds__(512) void ssq_kernel(const float* __restrict__ xa, int64_t ld,
+                                                  int64_t Tc, int64_t off0,
+                                                  const float* __restrict__ WB0, int64_t off1,
+                                                  const float* __restrict__ WB1, int krt,
+                                                  int64_t C, float* __restrict__ ssq) {
+    constexpr int KR = K > 0 ? K : 64;
+    __shared__ float chains[64 * 64];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c = (int64_t)blockIdx.x * WAVE + lane;
+    const int64_t cc = c < C ? c : C - 1;
+    const int kk = K > 0 ? K : krt;
+    float wg[KR], wu[KR];
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+        wg[j] = (j < kk) ? WB0[(int64_t)j * C + cc] : 0.0f;
+        wu[j] = (CRIT == 1 && j < kk) ? WB1[(int64_t)j * C + cc] : 0.0f;
+    }
+    float p[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) p[q] = 0.0f;
+    for (int64_t mb = 0; mb < Tc; mb += 64) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int64_t m = mb + 8 * w + q;
+            if (m < Tc) {
+                const float* row = xa + m * ld;
+                float v = crit_value<CRIT, K>(row, off0, off1, wg, wu, kk);
+                p[q] = __builtin_fmaf(v, v, p[q]);
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) chains[(8 * w + q) * 64 + lane] = p[q];
+    __syncthreads();
+    if (w == 0) {
+        float v[64];
+#pragma unroll
+        for (int l = 0; l < 64; ++l) v[l] = chains[l * 64 + lane];
+#pragma unroll
+        for (int s = 32; s >= 1; s >>= 1)
+#pragma unroll
+            for (int l = 0; l < s; ++l) v[l] = v[l] + v[l + s];
+        if (c < C) ssq[c] = v[0];
+    }
+}
+
+__global__ void qk_combine_kernel(const float* __restrict__ Q, const float* __restrict__ Kk,
+                                  int64_t H_kv, int64_t n_rep, int64_t d, float* __restrict__ s) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= H_kv * d) return;
+    const int64_t g = i / d, j = i % d;
+    float q2 = 0.0f;
+    for (int64_t r = 0; r < n_rep; ++r) q2 = q2 + Q[(g * n_rep + r) * d + j];
+    s[i] = q2 * Kk[i];
+}
+
+// ---------------------------------------------------------------- top-n (radix select)
+// One 1024-thread block.  Four 8-bit passes from the most significant byte
+// find the n-th largest key K*; channels with key > K* are kept, and of the
+// channels with key == K* the lowest-indexed ones fill the remainder.  A
+// block scan writes the kept channels in ascending order.
+__global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc, int64_t C,
+                                                    int64_t n, int32_t* __restrict__ idx) {
+    __shared__ unsigned hist[256];
+    __shared__ int sh[32];
+    __shared__ uint32_t s_prefix;
+    __shared__ int64_t s_rem;
+    if (n <= 0) return;
+    uint32_t prefix = 0, pmask = 0;
+    int64_t rem = n;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+        __syncthreads();
+        for (int64_t c = threadIdx.x; c < C; c += blockDim.x) {
+            uint32_t k = score_key(sc[c]);
+            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int64_t cum = 0;
+            int d = 0;
+            for (d = 255; d >= 0; --d) {
+                if (cum + (int64_t)hist[d] >= rem) break;
+                cum += hist[d];
+            }
+            s_prefix = prefix | ((uint32_t)d << shift);
+            s_rem = rem - cum;
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        rem = s_rem;
+        pmask |= 255u << shift;
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;
+    const int64_t need_eq = rem;
+    const int64_t chunk = (C + blockDim.x - 1) / blockDim.x;
+    const int64_t beg = (int64_t)threadIdx.x * chunk;
+    const int64_t end = beg + chunk < C ? beg + chunk : C;
+    int neq = 0;
+    for (int64_t c = beg; c < end; ++c) neq += score_key(sc[c]) == thr;
+    int tot;
+    int eq_before = block_exclusive_scan(neq, sh, &tot);
+    int nsel = 0;
+    {
+        int e = eq_before;
+        for (int64_t c = beg; c < end; ++c) {
+            uint32_t k = score_key(sc[c]);
+            if (k > thr) ++nsel;
+            else if (k == thr) { if (e < need_eq) ++nsel; ++e; }
+        }
+    }
+    int pos = block_exclusive_scan(nsel, sh, &tot);
+    {
+        int e = eq_before;
+        for (int64_t c = beg; c < end; ++c) {
+            uint32_t k = score_key(sc[c]);
+            bool take = false;
+            if (k > thr) take = true;
+            else if (k == thr) { take = e < need_eq; ++e; }
+            if (take) {
+                if (pos < n) idx[pos] = (int32_t)c;
+                ++pos;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- index propagation
+__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* a, int64_t n, int64_t v) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+__global__ void expand_gqa_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t n_rep,
+                                  int64_t d, int32_t* __restrict__ out) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n) return;
+    const int64_t e = idx[p], g = e / d, j = e % d;
+    const int64_t sg = lower_bound_i32(idx, n, g * d);
+    const int64_t cg = lower_bound_i32(idx, n, (g + 1) * d) - sg;
+    for (int64_t r = 0; r < n_rep; ++r)
+        out[sg * n_rep + r * cg + (p - sg)] = (int32_t)((g * n_rep + r) * d + j);
+}
+
+__global__ void stack_index_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t C,
+                                   int64_t copies, int32_t* __restrict__ out) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n * copies) return;
+    const int64_t b = p / n, q = p % n;
+    out[p] = (int32_t)(idx[q] + b * C);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int64_t Tc,
+                              int32_t* out, int64_t To, int* flag, hipStream_t st) {
+    hipLaunchKernelGGL(token_split_kernel, dim3(1), dim3(1024), 0, st, roles, T, ctx, Tc, out, To,
+                       flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* rows, int64_t Tc,
+                         int64_t D, const float* WA, int64_t kt, float* xa, hipStream_t st) {
+    if (Tc <= 0) return hipSuccess;
+    const int64_t waves = ceil_div(Tc, 2);
+    const int64_t blocks = ceil_div(waves, 4);
+    if (bf16)
+        hipLaunchKernelGGL(stage1_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx,
+                           rows, Tc, D, WA, kt, xa);
+    else
+        hipLaunchKernelGGL(stage1_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx,
+                           rows, Tc, D, WA, kt, xa);
+    return hipGetLastError();
+}
+
+hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t off0,
+                      const float* WB0, int64_t off1, const float* WB1, int64_t k, int64_t C,
+                      float* ssq, hipStream_t st) {
+    const dim3 grid((unsigned)ceil_div(C, 64)), block(512);
+    const int kr = (int)k;
+#define SSQ_LAUNCH(CR, KK)                                                                       \
+    hipLaunchKernelGGL((ssq_kernel<CR, KK>), grid, block, 0, st, xa, ld, Tc, off0, WB0, off1, WB1, \
+                       kr, C, ssq)
+    if (crit == 0) {
+        if (k == 8) SSQ_LAUNCH(0, 8);
+        else if (k == 16) SSQ_LAUNCH(0, 16);
+        else SSQ_LAUNCH(0, 0);
+    } else {
+        if (k == 8) SSQ_LAUNCH(1, 8);
+        else if (k == 16) SSQ_LAUNCH(1, 16);
+        else SSQ_LAUNCH(1, 0);
+    }
+#undef SSQ_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_qk_combine(const float* ssqQ, const float* ssqK, int64_t H_kv, int64_t n_rep,
+                             int64_t d, float* score, hipStream_t st) {
+    const int64_t n = H_kv * d;
+    hipLaunchKernelGGL(qk_combine_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, ssqQ,
+                       ssqK, H_kv, n_rep, d, score);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* scores, int64_t C, int64_t n, int32_t* idx, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, st, scores, C, n, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64_t d,
+                             int32_t* out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(expand_gqa_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, idx,
+                       n, n_rep, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t copies,
+                              int32_t* out, hipStream_t st) {
+    if (n <= 0 || copies <= 0) return hipSuccess;
+    hipLaunchKernelGGL(stack_index_kernel, dim3((unsigned)ceil_div(n * copies, 256)), dim3(256), 0,
+                       st, idx, n, C, copies, out);
+    return hipGetLastError();
+}

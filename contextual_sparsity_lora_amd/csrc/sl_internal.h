@@ -1,0 +1,97 @@
+// Internal declarations of the sparse LoRA linear library (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string>
+#include <vector>
+
+#include "../../include/sparselora.h"
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+
+struct sl_timed_launch {
+    int kclass;              // index into the kernel-class name table
+    hipEvent_t start, stop;
+    double flops, bytes;     // algorithmic work of this launch
+};
+
+struct sl_handle {
+    int device = 0;
+    bool timing = false;                  // record events around the main launches
+    std::vector<sl_timed_launch> timed;   // launches recorded since timing was enabled
+    std::vector<hipEvent_t> event_pool;
+    hipStream_t stream = nullptr;
+    void* ws = nullptr;          // workspace (device)
+    size_t ws_bytes = 0;
+    int* dev_flags = nullptr;    // device error flags (token split count mismatch, ...)
+    int num_cu = 256;
+    std::string err;
+};
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+// round to nearest even (NaN kept quiet)
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- launchers
+// Every launcher enqueues on `st` and returns hipGetLastError().
+struct GemmProblem {
+    const void* A;  int64_t lda;  const int32_t* a_rows;   // A row m -> a_rows[m] (or m)
+    const void* B;  int64_t ldb;  const int32_t* b_rows;   // NT: B row n; NN: B row k
+    void* C;        int64_t ldc;  const int32_t* c_rows;   // C row m -> c_rows[m] (or m)
+    const int32_t* c_cols;                                 // C col n -> c_cols[n] (or n)
+    int64_t M, N, K;
+    int beta;                                              // 1: C += result
+};
+// bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
+// nn = true: B is [K, N] ("NN").  Up to two problems in one launch.
+hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
+// fp32 version (VALU), same semantics.
+hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
+
+hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int64_t Tc,
+                              int32_t* out, int64_t To, int* flag, hipStream_t st);
+hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* rows, int64_t Tc,
+                         int64_t D, const float* WA_t, int64_t kt, float* xa, hipStream_t st);
+hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t off0,
+                      const float* WB0, int64_t off1, const float* WB1, int64_t k, int64_t C,
+                      float* ssq, hipStream_t st);
+hipError_t launch_qk_combine(const float* ssqQ, const float* ssqK, int64_t H_kv, int64_t n_rep,
+                             int64_t d, float* score, hipStream_t st);
+hipError_t launch_topk(const float* scores, int64_t C, int64_t n, int32_t* idx, hipStream_t st);
+hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64_t d,
+                             int32_t* out, hipStream_t st);
+hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t copies,
+                              int32_t* out, hipStream_t st);
+hipError_t launch_gather_cols(bool bf16, const void* in, int64_t ldi, const int32_t* rows,
+                              int64_t nrows, const int32_t* cols, int64_t ncols, void* out,
+                              int64_t ldo, hipStream_t st);
+hipError_t launch_zero_unselected(bool bf16, void* y, int64_t ldy, const int32_t* rows,
+                                  int64_t nrows, const int32_t* idx, int64_t n, int64_t C,
+                                  uint8_t* mask_ws, hipStream_t st);
+hipError_t launch_lora_xl(bool bf16, const void* x, int64_t ldx, int64_t T, int64_t D,
+                          const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
+                          float* ws, hipStream_t st);
+hipError_t launch_lora_add(bool bf16, const float* P, int64_t ldp, int64_t T, int64_t r,
+                           const void* Bm, int64_t sb_c, int64_t sb_j, int64_t Ncols,
+                           float scale, void* y, int64_t ldy, hipStream_t st);
+hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T, int64_t r,
+                              const void* Q, int64_t ldq, int64_t Ncols, float scale,
+                              float* out, int64_t so_j, int64_t so_c, float* ws, size_t ws_floats,
+                              hipStream_t st);
+hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,
+                            void* out, int64_t ldo, hipStream_t st);
+hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* u, int64_t ldu,
+                             int64_t T, int64_t F, void* h, int64_t ldh, hipStream_t st);
+hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void* g, int64_t ldg,
+                             const void* u, int64_t ldu, int64_t T, int64_t F, void* dg,
+                             int64_t lddg, void* du, int64_t lddu, hipStream_t st);
+
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -1,0 +1,123 @@
+"""One contextually-sparse SwiGLU FFN block (gate, up, down) with dense LoRA on
+all three projections: the forward and backward of the frozen main branch as a
+sequence of library calls.
+
+Pages ("SparseLoRA: Accelerating LLM Fine-Tuning with Contextual Sparsity"),
+paper-graph summary: §3.4 Algorithm 1 (estimate, score, keep the top
+ceil(r D_out), sliced matmul, add dense LoRA); §3.4 "FFN structure": the
+selection over the intermediate channels is shared by gate, up and down; §3.4
+"Token Sensitivity": output tokens dense, context tokens sparse; §3.2
+backward: gradients only through active channels, LoRA gradients dense.
+
+Layout in device memory (allocated once, reused every step):
+  W_gu  [2F, D]  gate rows then up rows (channel-major, nn.Linear layout)
+  Wt_dn [F, D]   transposed down weight: one intermediate channel per row
+  A_gu  [2r, D]  LoRA A of gate then up; B_* in nn.Linear LoRA layout
+  WA    [D, 2k]  estimator W_A of gate then up (fp32); WB_* [k, F] (fp32)
+  gu    [T, 2F]  gate pre-activation | up pre-activation (main + LoRA)
+  dgu   [T, 2F]  their gradients
+Everything below is marshalling: each step is one C-ABI call.
+"""
+import torch
+
+from . import ops
+
+
+def keep_count(C: int, num: int, den: int) -> int:
+    """Kept channels at sparsity num/den: ceil(C (den - num) / den), in integers."""
+    return (C * (den - num) + den - 1) // den
+
+
+class SparseFFN:
+    def __init__(self, W_gate, W_up, W_down, A_gate, B_gate, A_up, B_up, A_down, B_down,
+                 WA_gu, WB_gate, WB_up, scale, sparsity=(7, 10), dense=False):
+        dev = W_gate.device
+        self.dtype = W_gate.dtype
+        self.F, self.D = W_gate.shape
+        self.r = A_gate.shape[0]
+        self.k = WB_gate.shape[0]
+        self.scale = float(scale)
+        # dense=True: the library's dense path at the same shape (every channel
+        # kept, no estimator, same LoRA) -- the baseline the sparse block is
+        # compared with.
+        self.dense = dense
+        self.n = self.F if dense else keep_count(self.F, *sparsity)
+        self.W_gu = torch.cat([W_gate, W_up], 0).contiguous()
+        self.Wt_dn = torch.empty(self.F, self.D, dtype=self.dtype, device=dev)
+        ops.transpose(W_down.contiguous(), self.Wt_dn)
+        self.A_gu = torch.cat([A_gate, A_up], 0).contiguous()
+        self.B_gate, self.B_up = B_gate.contiguous(), B_up.contiguous()
+        self.A_down, self.B_down = A_down.contiguous(), B_down.contiguous()
+        self.WA = WA_gu.contiguous()                 # [D, 2k] fp32
+        self.WB_gate, self.WB_up = WB_gate.contiguous(), WB_up.contiguous()
+        self._T = None
+
+    def _alloc(self, T, T_c, T_o, dev):
+        if self._T == (T, T_c, T_o):
+            return
+        F, D, r, k, dt = self.F, self.D, self.r, self.k, self.dtype
+        e = lambda *s, **kw: torch.empty(*s, device=dev, **kw)
+        self.ctx_rows = e(T_c, dtype=torch.int32)
+        self.out_rows = e(T_o, dtype=torch.int32)
+        self.xa = e(T_c, 2 * k, dtype=torch.float32)
+        self.scores = e(F, dtype=torch.float32)
+        self.idx = e(self.n, dtype=torch.int32)
+        self.idx2 = e(2 * self.n, dtype=torch.int32)
+        if self.dense:
+            torch.arange(self.F, out=self.idx)
+            torch.arange(2 * self.F, out=self.idx2)
+        self.gu = e(T, 2 * F, dtype=dt)
+        self.h = e(T, F, dtype=dt)
+        self.y = e(T, D, dtype=dt)
+        self.xl_gu = e(T, 2 * r, dtype=torch.float32)
+        self.xl_dn = e(T, r, dtype=torch.float32)
+        self.dh = e(T, F, dtype=dt)
+        self.dgu = e(T, 2 * F, dtype=dt)
+        self.dx = e(T, D, dtype=dt)
+        f32 = torch.float32
+        self.dA_gate, self.dA_up = e(r, D, dtype=f32), e(r, D, dtype=f32)
+        self.dB_gate, self.dB_up = e(F, r, dtype=f32), e(F, r, dtype=f32)
+        self.dA_down, self.dB_down = e(r, F, dtype=f32), e(D, r, dtype=f32)
+        self._T = (T, T_c, T_o)
+
+    def forward(self, x, roles, T_c):
+        T = x.shape[0]
+        F, r = self.F, self.r
+        self._alloc(T, T_c, T - T_c, x.device)
+        self.x = x
+        ops.token_split(roles, self.ctx_rows, self.out_rows)
+        if not self.dense:
+            # estimator on context tokens, SwiGLU-L2 criterion, top-n (shared by gate/up/down)
+            ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
+            ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
+                             scores=self.scores, off0=0, off1=self.k)
+            ops.stack_index(self.idx, F, 2, self.idx2)
+        # gate|up main branch: dense output rows, gathered channels for context rows
+        ops.sparse_linear_fwd("out", x, self.W_gu, self.ctx_rows, self.out_rows, self.idx2, self.gu)
+        # dense LoRA on gate and up
+        ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
+        g, u = self.gu[:, :F], self.gu[:, F:]
+        ops.lora_fwd_bwd(ops.LORA_ADD, None, None, self.B_gate, self.scale, self.xl_gu[:, :r], y=g)
+        ops.lora_fwd_bwd(ops.LORA_ADD, None, None, self.B_up, self.scale, self.xl_gu[:, r:], y=u)
+        ops.swiglu_fwd(g, u, self.h)
+        # down main branch: input channels = the same selection
+        ops.sparse_linear_fwd("in", self.h, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx, self.y)
+        ops.lora_fwd_bwd(ops.LORA_XL | ops.LORA_ADD, self.h, self.A_down, self.B_down, self.scale,
+                         self.xl_dn, y=self.y)
+        return self.y
+
+    def backward(self, dy):
+        F, r = self.F, self.r
+        ops.sparse_linear_bwd("in", dy, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx, self.dh)
+        ops.lora_fwd_bwd(ops.LORA_BWD, self.h, self.A_down, self.B_down, self.scale, self.xl_dn,
+                         dy=dy, dx=self.dh, dA=self.dA_down, dB=self.dB_down)
+        g, u = self.gu[:, :F], self.gu[:, F:]
+        dg, du = self.dgu[:, :F], self.dgu[:, F:]
+        ops.swiglu_bwd(self.dh, g, u, dg, du)
+        ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.ctx_rows, self.out_rows, self.idx2,
+                              self.dx)
+        ops.lora_fwd_bwd(ops.LORA_BWD, self.x, self.A_gu[:r], self.B_gate, self.scale,
+                         self.xl_gu[:, :r], dy=dg, dx=self.dx, dA=self.dA_gate, dB=self.dB_gate)
+        ops.lora_fwd_bwd(ops.LORA_BWD, self.x, self.A_gu[r:], self.B_up, self.scale,
+                         self.xl_gu[:, r:], dy=du, dx=self.dx, dA=self.dA_up, dB=self.dB_up)
+        return self.dx

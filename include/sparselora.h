@@ -1,0 +1,271 @@
+/*
+ * sparselora.h -- C ABI of the MI355X (gfx950) library for the contextually
+ * sparse frozen main-branch linear layer of LoRA fine-tuning (SparseLoRA).
+ *
+ * Pages cited (all titled "SparseLoRA: Accelerating LLM Fine-Tuning with
+ * Contextual Sparsity"): the paper-graph summary ("PG"), sections given as
+ * §n "heading"; the Paper-Notes page ("PN"), sections given by heading.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers marked "device" point to device memory on the handle's device;
+ *    the caller allocates and owns all of them.  The library owns only its
+ *    handle and an internal workspace (grown on demand, or sized up front
+ *    with sl_reserve_workspace so that no allocation happens in the hot path).
+ *  - Matrices are row-major with an explicit leading dimension (in elements).
+ *    bf16 matrices must start on a 16-byte boundary and have a leading
+ *    dimension that is a multiple of 8; fp32 matrices: 16-byte boundary and a
+ *    multiple of 4.
+ *  - "Channel-major" weights store one selectable channel per row:
+ *    output-side projections (gate, up, q, k, v) use the nn.Linear layout
+ *    [D_out, D_in]; input-side projections (down, o) use the transposed copy
+ *    [D_in, D_out] (made once with sl_transpose).
+ *  - Sizes (T, T_c, T_o, n, ...) are host integers: nothing on the hot path
+ *    copies data back to the host or synchronises.
+ *  - Work is enqueued on the handle's stream (sl_set_stream) and runs
+ *    asynchronously.  Every call validates its arguments before launching
+ *    anything: a non-SL_OK return means nothing was enqueued and no output
+ *    was written.  The message of the last error is sl_last_error(h).
+ *    Device-side faults surface at a later call or at sl_sync.
+ *  - One handle per host thread; calls that overlap on one handle race.
+ *  - bf16 results are rounded to nearest even from fp32 accumulators.
+ */
+#ifndef SPARSELORA_H
+#define SPARSELORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sl_handle sl_handle;
+
+typedef enum {
+    SL_OK = 0,
+    SL_ERR_INVALID = -1,      /* bad argument: null pointer, size, alignment, range */
+    SL_ERR_UNSUPPORTED = -2,  /* valid but not implemented (dtype / shape class)   */
+    SL_ERR_HIP = -3,          /* a HIP runtime call failed                          */
+    SL_ERR_WORKSPACE = -4     /* the internal workspace could not be allocated      */
+} sl_status;
+
+typedef enum { SL_F32 = 0, SL_BF16 = 1 } sl_dtype;
+
+/* Channel criteria (PG §3.4 "Oracle Sparse Neuron Selection Criteria"). */
+typedef enum {
+    SL_CRIT_L2 = 0,        /* score[c] = sum over context tokens of y_hat[., c]^2      */
+    SL_CRIT_SWIGLU_L2 = 1, /* score[c] = sum of (SiLU(g_hat) * u_hat)[., c]^2          */
+    SL_CRIT_QK = 2         /* score[c] = (sum over the group's query heads of
+                              sum q_hat^2) * (sum k_hat^2), in key/value space     */
+} sl_criterion;
+
+/* Which side of the weight the selection applies to. */
+typedef enum {
+    SL_SIDE_OUT = 0,  /* output channels (gate, up, q, k, v); W is [D_out, D_in]  */
+    SL_SIDE_IN = 1    /* input channels (down, o); W is the copy [D_in, D_out]    */
+} sl_side;
+
+/* sl_lora_fwd_bwd mode bits. */
+enum {
+    SL_LORA_XL = 1,   /* forward: xl = x A^T                                      */
+    SL_LORA_ADD = 2,  /* forward: y += scale * xl B^T (uses xl as given)          */
+    SL_LORA_BWD = 4   /* backward: dA, dB, and dx += scale * (dy B) A             */
+};
+
+/* ---------------------------------------------------------------- handle */
+
+/* Create a handle bound to HIP device `device` (makes it current while the
+ * handle's calls run).  The stream defaults to the null stream. */
+sl_status sl_create(sl_handle** h, int device);
+/* Destroy a handle and free its workspace (synchronises its stream first). */
+sl_status sl_destroy(sl_handle* h);
+/* Set the hipStream_t (passed as void*) that all later calls enqueue on. */
+sl_status sl_set_stream(sl_handle* h, void* hip_stream);
+/* Ensure the internal workspace holds at least `bytes` (allocates now). */
+sl_status sl_reserve_workspace(sl_handle* h, size_t bytes);
+/* Wait for the handle's stream; reports asynchronous HIP errors. */
+sl_status sl_sync(sl_handle* h);
+/* Human-readable text of the last error on this handle ("" if none). */
+const char* sl_last_error(const sl_handle* h);
+/* Name of a status code. */
+const char* sl_status_str(sl_status s);
+/* Library version string. */
+const char* sl_version(void);
+
+/* ---------------------------------------------------------------- measurement */
+
+/* While enabled, each main launch of the library (kernel classes
+ * "gemm_bf16_nt", "gemm_bf16_nn", "gemm_f32", "estimate", "score", "topk",
+ * "lora", "swiglu", "gather", "fill", "token_split") is bracketed by HIP
+ * events recorded on the handle's stream, together with its algorithmic
+ * work (flops, and HBM bytes as if every operand element were read once and
+ * every result written once).  Enabling does not clear earlier records. */
+sl_status sl_timing_enable(sl_handle* h, int enable);
+/* Drop all records (waits for the stream first). */
+sl_status sl_timing_reset(sl_handle* h);
+/* Totals over the records of one kernel class: number of launches, summed
+ * event time in ms, summed algorithmic flops and bytes.  Waits for the stream.
+ * Unknown class: SL_ERR_INVALID. */
+sl_status sl_timing_query(sl_handle* h, const char* kernel_class, int64_t* launches,
+                          double* total_ms, double* flops, double* bytes);
+/* Name of kernel class i (NULL past the last). */
+const char* sl_timing_class_name(int i);
+
+/* ---------------------------------------------------------------- a1: token roles */
+
+/* Split tokens by role (PG §3.4 "Token Sensitivity", implementation and
+ * Figure 8: output tokens take the dense path, context tokens the sparse path;
+ * PN "Token 敏感性").
+ *   roles    device uint8[T]; 0 = context token, any other value = output token
+ *   ctx_rows device int32[T_c] out: context rows, ascending
+ *   out_rows device int32[T_o] out: output rows, ascending
+ * T_c and T_o are the caller's counts (known from the sequence structure),
+ * T_c + T_o = T.  If the roles hold a different count, the lists are written
+ * only up to the given sizes and sl_sync reports SL_ERR_INVALID. */
+sl_status sl_token_split(sl_handle* h, const uint8_t* roles, int64_t T,
+                         int32_t* ctx_rows, int64_t T_c, int32_t* out_rows, int64_t T_o);
+
+/* ---------------------------------------------------------------- a2: estimator stage 1 */
+
+/* Low-rank estimator, first product (PG §3.4 "SVD Sparsity Estimator",
+ * Algorithm 1 step 1: y_hat = (x W_A) W_B; PN "SVD 稀疏估计器"), context
+ * tokens only:
+ *   xa[m, j] = sum_i x[ctx_rows[m], i] * W_A[i, j],   m < T_c, j < k_tot,
+ * summed in fp32 as R64 (64 strided fused multiply-add chains over i, then a
+ * pairwise tree 32, 16, ..., 1), which fixes the result bit for bit.
+ *   x        device [*, ldx] of dtype xdt (rows indexed by ctx_rows)
+ *   WA       device fp32 [D_in, k_tot]: W_A in its math layout (row i holds
+ *            W_A[i, :]); factors of projections that share the input are
+ *            placed side by side (gate|up: 2k columns; q|k|v: 3k)
+ *   xa       device fp32 [T_c, k_tot] out
+ * Constraints: 1 <= k_tot <= 128, D_in >= 1.  T_c = 0 is a no-op. */
+sl_status sl_svd_estimate(sl_handle* h, const void* x, sl_dtype xdt, int64_t ldx,
+                          const int32_t* ctx_rows, int64_t T_c, int64_t D_in,
+                          const float* WA, int64_t k_tot, float* xa);
+
+/* ---------------------------------------------------------------- a3+a4: score, select */
+
+/* Estimator second product fused with the criterion, then top-n selection
+ * (PG §3.4 Algorithm 1 steps 2-3; "Oracle Sparse Neuron Selection Criteria";
+ * PN "L2 Norm 准则", "QK Norm 准则").
+ *   y_hat[m, c] = sum_j xa[m, off + j] * WB[j, c]  (fp32 fused chain, j ascending)
+ *   SL_CRIT_L2:        v = y_hat from (off0, WB0)
+ *   SL_CRIT_SWIGLU_L2: v = silu(g_hat) * u_hat, g_hat from (off0, WB0),
+ *                      u_hat from (off1, WB1); silu(z) = z / (1 + exp(-z)) with
+ *                      the library's fixed fp32 exp (Cody-Waite reduction and a
+ *                      degree-7 Taylor polynomial, within 1 ulp)
+ *   ssq[c] = sum over context tokens of v^2, in R64 order over m
+ *   SL_CRIT_QK: C = H_kv * head_dim (key/value channel space);
+ *     WB0 = W_B of q [k, C * n_rep], WB1 = W_B of k [k, C];
+ *     score[g*d + j] = (sum_r ssq_q[(g*n_rep + r)*d + j]) * ssq_k[g*d + j]
+ *   otherwise score = ssq (squared norms rank like norms).
+ * Selection: the n_keep channels with the largest score bit patterns (NaN
+ * above +inf), equal scores ordered by lower channel index; idx is written
+ * ascending.  n_keep = ceil(keep_ratio * C) is the caller's integer.
+ *   xa      device fp32 [T_c, ld_xa]
+ *   WB0/WB1 device fp32 [k, *] row-major (WB1 unused, may be NULL, for L2)
+ *   scores  device fp32 [C] out, or NULL (then kept in the workspace)
+ *   idx     device int32[n_keep] out
+ * Constraints: 1 <= k <= 64; 0 <= n_keep <= C; n_rep >= 1 and head_dim >= 1
+ * for QK (ignored otherwise).  T_c = 0 gives all-zero scores. */
+sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
+                          int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
+                          const float* WB1, int64_t k, int64_t C, int64_t n_rep,
+                          int64_t head_dim, int64_t n_keep, float* scores, int32_t* idx);
+
+/* ---------------------------------------------------------------- a5: index propagation */
+
+/* Key/value-space selection -> query-space (or o-input) selection under
+ * grouped-query attention: query channel (g*n_rep + r)*head_dim + j is kept
+ * iff key/value channel g*head_dim + j is (PG §3.4 "VO projection sparsity":
+ * indices propagate between projections sharing a channel space).
+ *   idx_kv device int32[n] ascending; idx_q device int32[n * n_rep] out, ascending. */
+sl_status sl_expand_gqa(sl_handle* h, const int32_t* idx_kv, int64_t n, int64_t n_rep,
+                        int64_t head_dim, int32_t* idx_q);
+
+/* Channel selection shared by stacked projections (PG §3.4 "FFN structure":
+ * one index serves gate and up): idx_out[b*n + q] = idx[q] + b*C for
+ * b < copies.  idx_out device int32[n * copies], ascending. */
+sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
+                         int64_t copies, int32_t* idx_out);
+
+/* ---------------------------------------------------------------- a6/a7: main forward */
+
+/* Sparse main-branch forward (PG §3.4 Algorithm 1 steps 4-5 and "Token
+ * Sensitivity" implementation; §3.4 "Preliminary": dropped channels are zero):
+ *   output rows:  y[t, :] = x[t, :] W^T                       (dense)
+ *   context rows, side OUT: y[t, c] = x[t, :] . W[c, :] for c in idx, 0 else
+ *   context rows, side IN:  y[t, :] = sum_{c in idx} x[t, c] Wt[c, :]
+ * computed as gathered-channel GEMMs (only the selected weight rows are read
+ * for context rows).  beta = 1 adds into y instead of overwriting.
+ *   x   device [T, ldx] (dt), channels of side IN are its columns
+ *   W   device channel-major weight (dt): OUT [D_out, ldw >= D_in],
+ *       IN [D_in, ldw >= D_out]
+ *   ctx_rows/out_rows  device int32 row lists (sl_token_split)
+ *   idx device int32[n], ascending, in [0, C), C = D_out (OUT) or D_in (IN)
+ *   y   device [T, ldy] (dt) out
+ * dt = SL_BF16 (MFMA path) or SL_F32. */
+sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
+                               const void* x, int64_t ldx, int64_t T, int64_t D_in,
+                               const void* W, int64_t ldw, int64_t D_out,
+                               const int32_t* ctx_rows, int64_t T_c,
+                               const int32_t* out_rows, int64_t T_o,
+                               const int32_t* idx, int64_t n,
+                               void* y, int64_t ldy, int beta);
+
+/* ---------------------------------------------------------------- a10/a11: main backward */
+
+/* Input gradient of sl_sparse_linear_fwd with the selection held fixed (PG
+ * §3.2 "Information flow during a backward pass": gradients flow only
+ * through the active channels; the frozen weight receives none):
+ *   output rows:  dx[t, :] = dy[t, :] W                        (dense)
+ *   context rows, side OUT: dx[t, :] = sum_{c in idx} dy[t, c] W[c, :]
+ *   context rows, side IN:  dx[t, c] = dy[t, :] . Wt[c, :] for c in idx, 0 else
+ *   dy  device [T, lddy] (dt), W as in the forward (same buffer),
+ *   dx  device [T, lddx] (dt) out; beta = 1 accumulates. */
+sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
+                               const void* dy, int64_t lddy, int64_t T, int64_t D_out,
+                               const void* W, int64_t ldw, int64_t D_in,
+                               const int32_t* ctx_rows, int64_t T_c,
+                               const int32_t* out_rows, int64_t T_o,
+                               const int32_t* idx, int64_t n,
+                               void* dx, int64_t lddx, int beta);
+
+/* ---------------------------------------------------------------- a8/a12: dense LoRA */
+
+/* Dense LoRA branch on every token and channel (PG §3.4 Algorithm 1 step 6:
+ * y_final = y_sparse + B A x; §3.2: LoRA gradients are always computed fully).
+ * A [r, D_in], B [D_out, r] (dt), scale = alpha / r.
+ *   mode & SL_LORA_XL:  xl = x A^T                 (xl fp32 [T, ldxl], out)
+ *   mode & SL_LORA_ADD: y += scale * xl B^T         (y dt [T, ldy], in/out)
+ *   mode & SL_LORA_BWD: gB = dy B;  dA = scale gB^T x  (fp32 [r, D_in], out);
+ *                       dB = scale dy^T xl             (fp32 [D_out, r], out);
+ *                       dx += scale gB A if dx != NULL (dt [T, lddx])
+ * Pointers not used by the mode may be NULL.  1 <= r <= 64. */
+sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt,
+                          const void* x, int64_t ldx, int64_t T, int64_t D_in, int64_t D_out,
+                          const void* A, const void* B, int64_t r, float scale,
+                          float* xl, int64_t ldxl, void* y, int64_t ldy,
+                          const void* dy, int64_t lddy, void* dx, int64_t lddx,
+                          float* dA, float* dB);
+
+/* ---------------------------------------------------------------- support (glue) */
+
+/* SwiGLU (PG §3.4 "FFN structure"): h = silu(g) * u (fp32 math, dt storage).
+ * g, u, h: device [T, ld*] with F columns. */
+sl_status sl_swiglu_fwd(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg,
+                        const void* u, int64_t ldu, int64_t T, int64_t F,
+                        void* hout, int64_t ldh);
+/* dg = dh * u * silu'(g), du = dh * silu(g). */
+sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
+                        const void* g, int64_t ldg, const void* u, int64_t ldu,
+                        int64_t T, int64_t F, void* dg, int64_t lddg, void* du, int64_t lddu);
+/* out[j, i] = in[i, j]; in [rows, ldi], out [cols, ldo] (dt). */
+sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi,
+                       int64_t rows, int64_t cols, void* out, int64_t ldo);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSELORA_H */

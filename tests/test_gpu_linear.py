@@ -1,0 +1,143 @@
+"""GPU parity of the sparse main branch (forward and backward, both sides) and
+of the dense LoRA branch against the fp64 oracle, within the stated
+tolerances (max-abs-relative 1e-4 for fp32, 2e-2 for bf16)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from tests.gpu_util import DEV, TOL, dev_pad, empty_pad, host, mar, need_lib, tdt, to_dev
+from workloads.gen import round_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    return ops
+
+
+def _roles(B, S, O):
+    r = np.zeros((B, S), np.uint8)
+    r[:, S - O:] = 1
+    return r.reshape(-1)
+
+
+def _lists(ops, roles):
+    ctx, out = ref.token_lists(roles)
+    return ctx, out, to_dev(ctx, None), to_dev(out, None)
+
+
+CASES = [
+    # dtype, B, S, O, D_in, D_out, keep
+    ("f32", 2, 64, 16, 256, 688, 344),        # the fp32 FFN shape
+    ("bf16", 2, 300, 70, 520, 1000, 333),     # several tiles and ragged tails everywhere
+    ("bf16", 1, 129, 0, 136, 130, 1),         # no output tokens, one kept channel
+    ("bf16", 3, 40, 40, 64, 200, 0),          # no context tokens, nothing kept
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_sparse_linear_fwd_bwd(case, rng):
+    ops = _ops()
+    dtype, B, S, O, Din, Dout, keep = case
+    print(f"[linear] {case}", flush=True)
+    roles = _roles(B, S, O)
+    T = B * S
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    x = round_dtype(rng.standard_normal((T, Din)), dtype)
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, dtype)     # [D_out, D_in]
+    dy = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    tol = TOL[dtype]
+    # output side: channels = output features
+    idx = np.sort(rng.choice(Dout, min(keep, Dout), replace=False)).astype(np.int32)
+    y = empty_pad(T, Dout, dtype)
+    ops.sparse_linear_fwd("out", dev_pad(x, dtype), dev_pad(W, dtype), c_d, o_d, to_dev(idx, None), y)
+    yr = ref.sparse_linear_fwd("out", x, W, roles, idx)
+    assert mar(host(y), yr) <= tol
+    drop = np.setdiff1d(np.arange(Dout), idx)
+    assert np.all(host(y)[np.ix_(ctx, drop)] == 0.0)
+    dx = empty_pad(T, Din, dtype)
+    ops.sparse_linear_bwd("out", dev_pad(dy, dtype), dev_pad(W, dtype), c_d, o_d, to_dev(idx, None), dx)
+    assert mar(host(dx), ref.sparse_linear_bwd("out", dy, W, roles, idx)) <= tol
+    # input side: the weight is passed as its transposed copy [D_in, D_out]
+    Wi = round_dtype(rng.standard_normal((Din, Dout)) * 0.05, dtype)    # nn.Linear [out=Din, in=Dout]
+    Wt = np.ascontiguousarray(Wi.T)
+    idx_in = np.sort(rng.choice(Dout, min(keep, Dout), replace=False)).astype(np.int32)
+    xi = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    yi = empty_pad(T, Din, dtype)
+    ops.sparse_linear_fwd("in", dev_pad(xi, dtype), dev_pad(Wt, dtype), c_d, o_d, to_dev(idx_in, None), yi)
+    assert mar(host(yi), ref.sparse_linear_fwd("in", xi, Wi, roles, idx_in)) <= tol
+    dyi = round_dtype(rng.standard_normal((T, Din)), dtype)
+    dxi = empty_pad(T, Dout, dtype)
+    ops.sparse_linear_bwd("in", dev_pad(dyi, dtype), dev_pad(Wt, dtype), c_d, o_d, to_dev(idx_in, None), dxi)
+    dxr = ref.sparse_linear_bwd("in", dyi, Wi, roles, idx_in)
+    assert mar(host(dxi), dxr) <= tol
+    assert np.all(host(dxi)[np.ix_(ctx, np.setdiff1d(np.arange(Dout), idx_in))] == 0.0)
+
+
+def test_output_rows_invariant_and_full_keep_is_dense(rng):
+    ops = _ops()
+    roles = _roles(2, 256, 64)
+    T, Din, Dout = 512, 384, 640
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    x = to_dev(round_dtype(rng.standard_normal((T, Din)), "bf16"), "bf16")
+    Wn = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    W = to_dev(Wn, "bf16")
+    ys = []
+    for idx in (np.arange(0, Dout, 3), np.arange(5), np.arange(Dout)):
+        y = torch.empty(T, Dout, dtype=torch.bfloat16, device=DEV)
+        ops.sparse_linear_fwd("out", x, W, c_d, o_d, to_dev(idx.astype(np.int32), None), y)
+        ys.append(host(y))
+    for y in ys[1:]:
+        assert np.array_equal(y[out], ys[0][out])          # bitwise: output rows never see idx
+    dense = ref.sparse_linear_fwd("out", host(x), Wn, np.ones(T, np.uint8), np.zeros(0, np.int32))
+    assert mar(ys[2], dense) <= TOL["bf16"]                 # keep = C is the dense layer
+
+
+def test_beta_accumulates(rng):
+    ops = _ops()
+    roles = _roles(1, 200, 50)
+    T, Din, Dout = 200, 128, 256
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    y0 = round_dtype(rng.standard_normal((T, Dout)), "bf16")
+    idx = np.sort(rng.choice(Dout, 77, replace=False)).astype(np.int32)
+    y = to_dev(y0, "bf16")
+    ops.sparse_linear_fwd("out", to_dev(x, "bf16"), to_dev(W, "bf16"), c_d, o_d, to_dev(idx, None), y, beta=1)
+    assert mar(host(y), y0 + ref.sparse_linear_fwd("out", x, W, roles, idx)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,T,Din,Dout,r", [("f32", 128, 256, 688, 8), ("bf16", 300, 520, 1000, 16),
+                                                ("bf16", 64, 4096, 14336, 16), ("bf16", 33, 200, 72, 32)])
+def test_lora_fwd_bwd(dtype, T, Din, Dout, r, rng):
+    ops = _ops()
+    print(f"[lora] {dtype} T={T} D_in={Din} D_out={Dout} r={r}", flush=True)
+    s = 2.0
+    x = round_dtype(rng.standard_normal((T, Din)), dtype)
+    A = round_dtype(rng.standard_normal((r, Din)) * 0.02, dtype)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.02, dtype)
+    y0 = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    dy = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    dx0 = round_dtype(rng.standard_normal((T, Din)), dtype)
+    tol = TOL[dtype]
+    xl = torch.empty(T, r, dtype=torch.float32, device=DEV)
+    y = to_dev(y0, dtype)
+    xd, Ad, Bd = to_dev(x, dtype), to_dev(A, dtype), to_dev(Bm, dtype)
+    ops.lora_fwd_bwd(ops.LORA_XL | ops.LORA_ADD, xd, Ad, Bd, s, xl, y=y)
+    xl_r, yl_r = ref.lora_fwd(x, A, Bm, s)
+    assert mar(host(xl), xl_r) <= 1e-5
+    assert mar(host(y), y0 + yl_r) <= tol
+    y_only = torch.zeros(T, Dout, dtype=tdt(dtype), device=DEV)
+    ops.lora_fwd_bwd(ops.LORA_ADD, None, None, Bd, s, xl, y=y_only)
+    assert mar(host(y_only), yl_r) <= tol
+    dA = torch.empty(r, Din, dtype=torch.float32, device=DEV)
+    dB = torch.empty(Dout, r, dtype=torch.float32, device=DEV)
+    dx = to_dev(dx0, dtype)
+    ops.lora_fwd_bwd(ops.LORA_BWD, xd, Ad, Bd, s, xl, dy=to_dev(dy, dtype), dx=dx, dA=dA, dB=dB)
+    dx_r, dA_r, dB_r = ref.lora_bwd(x, host(xl), dy, A, Bm, s)
+    assert mar(host(dA), dA_r) <= 1e-4
+    assert mar(host(dB), dB_r) <= 1e-4
+    assert mar(host(dx), dx0 + dx_r) <= tol
