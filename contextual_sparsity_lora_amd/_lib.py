@@ -37,12 +37,14 @@ SIGNATURES = {
                               _i64, _i64, _i64, _vp, _vp]),
     "sl_expand_gqa": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_stack_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
-    "sl_sparse_linear_fwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _i64,
-                                   _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int]),
-    "sl_sparse_linear_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _i64,
-                                   _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int]),
+    "sl_sparse_linear_fwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                   _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
+                                   _vp, _i64, _vp, _i64, _i64, _f]),
+    "sl_sparse_linear_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                   _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
+                                   _vp, _i64, _vp, _i64, _i64, _f]),
     "sl_lora_fwd_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _f,
-                              _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp]),
+                              _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64]),
     "sl_swiglu_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),
     "sl_swiglu_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
                             _vp, _i64]),

@@ -9,13 +9,21 @@
 // (b_rows = selected channels over a compacted activation).  Only the selected
 // weight rows are read; each is a contiguous row of the channel-major weight.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 128x128x64 block tile, 4 waves of
-// 64x64, register-staged double-buffered LDS (row stride 72 bf16 so the
-// 16-byte MFMA operand reads are conflict-free).  NN tiles are transposed on
-// their way into LDS (pairs of rows repacked with byte permutes) so both
-// layouts feed the same K-contiguous LDS format.  Block ids are remapped so
-// that each XCD works on a contiguous run of tiles (shared weight tiles stay
-// in that XCD's L2).
+// bf16 path: v_mfma_f32_32x32x16_bf16.  Block tile BM x BN x 64 split over
+// WGM x WGN waves; register-staged, double-buffered LDS with a 72-element row
+// stride so the 16-byte MFMA operand reads are conflict-free.  NN tiles are
+// transposed on their way into LDS (pairs of rows repacked) so both layouts
+// feed the same K-contiguous LDS format.  Block ids are remapped so that each
+// XCD works on a contiguous run of tiles (tiles sharing a weight tile stay in
+// one XCD's L2), with the M tile index fastest.
+//
+// Optional rank-r term (the dense LoRA branch): before the single rounding of
+// C, lscale * lP[cm, :] . lB[cn, :] is accumulated into the same fp32
+// accumulators with v_mfma_f32_32x32x2_f32 (fp32 operands), cm / cn being the
+// mapped output row / channel.  A problem with K = 0 carries only this term
+// (the unselected channels of context rows).
+#include <cstdlib>
+
 #include "sl_internal.h"
 
 namespace {
@@ -23,13 +31,32 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = 72;
+constexpr int BK = 64, LDK = 72;
+constexpr int MAXP = 5;
 constexpr int NXCD = 8;
 
 struct GemmArgs {
-    GemmProblem p0, p1;
-    int tiles0, tiles_m0, tiles_m1, total;
+    GemmProblem p[MAXP];
+    int first[MAXP + 1];   // first tile of each problem (prefix sums)
+    int tiles_m[MAXP];
+    int nprob;
 };
+
+__device__ __forceinline__ void pick_problem(const GemmArgs& args, int L, GemmProblem& P, int& t,
+                                             int& tiles_m) {
+    // uniform selects (no dynamic indexing of the argument block)
+    int i = 0;
+#pragma unroll
+    for (int q = 1; q < MAXP; ++q)
+        if (q < args.nprob && L >= args.first[q]) i = q;
+#pragma unroll
+    for (int q = 0; q < MAXP; ++q)
+        if (q == i) {
+            P = args.p[q];
+            t = L - args.first[q];
+            tiles_m = args.tiles_m[q];
+        }
+}
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
     const int xcd = b % NXCD, slot = b / NXCD;
@@ -48,41 +75,48 @@ __device__ __forceinline__ uint4 load16_guard(const bf16_t* rowp, int64_t k, int
     return v;
 }
 
-template <bool NN>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs args) {
-    __shared__ __attribute__((aligned(16))) bf16_t As[2][BM * LDK];
-    __shared__ __attribute__((aligned(16))) bf16_t Bs[2][BN * LDK];
+template <int BM, int BN, int WGM, int WGN, bool NN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs args) {
+    constexpr int NTH = 64 * WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;   // wave tile
+    constexpr int FM = WTM / 32, FN = WTN / 32;     // 32x32 MFMA blocks per wave
+    constexpr int ACH = BM * 8 / NTH;               // 16-byte A chunks per thread
+    constexpr int BCH = BN * 8 / NTH;               // 16-byte B chunks per thread (NT)
+    constexpr int NNG = BN * 4 / NTH;               // (8 rows x 2 cols) groups per thread (NN)
+    static_assert(ACH >= 1 && BCH >= 1 && NNG >= 1, "tile too small for the block");
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    bf16_t* As = smem;                       // [2][BM * LDK]
+    bf16_t* Bs = smem + 2 * BM * LDK;        // [2][BN * LDK]
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
-    const bool second = L >= args.tiles0;
-    const GemmProblem P = second ? args.p1 : args.p0;
-    const int t = second ? L - args.tiles0 : L;
-    const int tiles_m = second ? args.tiles_m1 : args.tiles_m0;
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, L, P, t, tiles_m);
     const int64_t m0 = (int64_t)(t % tiles_m) * BM;
     const int64_t n0 = (int64_t)(t / tiles_m) * BN;
     const int64_t M = P.M, N = P.N, K = P.K;
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid & 1, wn = wid >> 1;
+    const int wm = wid % WGM, wn = wid / WGM;
     const bf16_t* __restrict__ Ag = (const bf16_t*)P.A;
     const bf16_t* __restrict__ Bg = (const bf16_t*)P.B;
 
-    // A-tile (and NT B-tile) load slots: 4 chunks of 16 B per thread.
-    const bf16_t* arow[4];
-    bool av[4];
-    int aslot[4], akc[4];
-    const bf16_t* brow[4];
-    bool bv[4];
+    const bf16_t* arow[ACH];
+    bool av[ACH];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-        const int q = tid + 256 * c, r = q >> 3;
-        aslot[c] = r;
-        akc[c] = (q & 7) * 8;
+    for (int c = 0; c < ACH; ++c) {
+        const int q = tid + NTH * c, r = q >> 3;
         const int64_t m = m0 + r;
         av[c] = m < M;
         const int64_t ar = av[c] ? (P.a_rows ? (int64_t)P.a_rows[m] : m) : 0;
         arow[c] = Ag + ar * P.lda;
-        if (!NN) {
+    }
+    const bf16_t* brow[NN ? 1 : BCH];
+    bool bv[NN ? 1 : BCH];
+    if (!NN) {
+#pragma unroll
+        for (int c = 0; c < (NN ? 1 : BCH); ++c) {
+            const int q = tid + NTH * c, r = q >> 3;
             const int64_t n = n0 + r;
             bv[c] = n < N;
             const int64_t br = bv[c] ? (P.b_rows ? (int64_t)P.b_rows[n] : n) : 0;
@@ -90,19 +124,21 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs args) {
         }
     }
 
-    uint4 ra[4], rb[4];
-    uint32_t rnn[2][8];
+    uint4 ra[ACH];
+    uint4 rb[NN ? 1 : BCH];
+    uint32_t rnn[NN ? NNG : 1][8];
 
     auto load_tile = [&](int64_t k0) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ra[c] = load16_guard(arow[c], k0 + akc[c], K, av[c]);
+        for (int c = 0; c < ACH; ++c) ra[c] = load16_guard(arow[c], k0 + ((tid + NTH * c) & 7) * 8, K, av[c]);
         if (!NN) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) rb[c] = load16_guard(brow[c], k0 + akc[c], K, bv[c]);
+            for (int c = 0; c < (NN ? 1 : BCH); ++c)
+                rb[c] = load16_guard(brow[c], k0 + ((tid + NTH * c) & 7) * 8, K, bv[c]);
         } else {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int q = tid + 256 * g, kq = q >> 6, np = q & 63;
+            for (int g = 0; g < (NN ? NNG : 1); ++g) {
+                const int q = tid + NTH * g, np = q % (BN / 2), kq = q / (BN / 2);
                 const int64_t n = n0 + 2 * np;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -120,15 +156,23 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs args) {
         }
     };
     auto store_tile = [&](int buf) {
+        bf16_t* as = As + buf * BM * LDK;
+        bf16_t* bs = Bs + buf * BN * LDK;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) *(uint4*)&As[buf][aslot[c] * LDK + akc[c]] = ra[c];
+        for (int c = 0; c < ACH; ++c) {
+            const int q = tid + NTH * c;
+            *(uint4*)&as[(q >> 3) * LDK + (q & 7) * 8] = ra[c];
+        }
         if (!NN) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) *(uint4*)&Bs[buf][aslot[c] * LDK + akc[c]] = rb[c];
+            for (int c = 0; c < (NN ? 1 : BCH); ++c) {
+                const int q = tid + NTH * c;
+                *(uint4*)&bs[(q >> 3) * LDK + (q & 7) * 8] = rb[c];
+            }
         } else {
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int q = tid + 256 * g, kq = q >> 6, np = q & 63;
+            for (int g = 0; g < (NN ? NNG : 1); ++g) {
+                const int q = tid + NTH * g, np = q % (BN / 2), kq = q / (BN / 2);
                 uint4 lo, hi;  // column 2np (low halves) and 2np+1 (high halves)
                 lo.x = (rnn[g][0] & 0xffffu) | (rnn[g][1] << 16);
                 lo.y = (rnn[g][2] & 0xffffu) | (rnn[g][3] << 16);
@@ -138,62 +182,116 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs args) {
                 hi.y = (rnn[g][2] >> 16) | (rnn[g][3] & 0xffff0000u);
                 hi.z = (rnn[g][4] >> 16) | (rnn[g][5] & 0xffff0000u);
                 hi.w = (rnn[g][6] >> 16) | (rnn[g][7] & 0xffff0000u);
-                *(uint4*)&Bs[buf][(2 * np) * LDK + 8 * kq] = lo;
-                *(uint4*)&Bs[buf][(2 * np + 1) * LDK + 8 * kq] = hi;
+                *(uint4*)&bs[(2 * np) * LDK + 8 * kq] = lo;
+                *(uint4*)&bs[(2 * np + 1) * LDK + 8 * kq] = hi;
             }
         }
     };
 
-    f32x16 acc[2][2];
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int64_t nk = (K + BK - 1) / BK;
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    if (nk > 0) {
+        load_tile(0);
+        store_tile(0);
+        __syncthreads();
+    }
     for (int64_t kt = 0; kt < nk; ++kt) {
         const int cur = (int)(kt & 1);
         if (kt + 1 < nk) load_tile((kt + 1) * BK);
+        const bf16_t* as = As + cur * BM * LDK;
+        const bf16_t* bs = Bs + cur * BN * LDK;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 a[2], b[2];
+            bf16x8 a[FM], b[FN];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = wm * 64 + i * 32 + (lane & 31);
-                a[i] = *(const bf16x8*)&As[cur][r * LDK + ks * 16 + (lane >> 5) * 8];
+            for (int i = 0; i < FM; ++i) {
+                const int r = wm * WTM + i * 32 + (lane & 31);
+                a[i] = *(const bf16x8*)&as[r * LDK + ks * 16 + (lane >> 5) * 8];
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int r = wn * 64 + j * 32 + (lane & 31);
-                b[j] = *(const bf16x8*)&Bs[cur][r * LDK + ks * 16 + (lane >> 5) * 8];
+            for (int j = 0; j < FN; ++j) {
+                const int r = wn * WTN + j * 32 + (lane & 31);
+                b[j] = *(const bf16x8*)&bs[r * LDK + ks * 16 + (lane >> 5) * 8];
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < FN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
         if (kt + 1 < nk) store_tile(cur ^ 1);
         __syncthreads();
     }
 
+    // rank-r term: A operand lP[cm, k], B operand lB[cn, k] (k = kk + lane/32)
+    if (P.lr > 0) {
+        const float* __restrict__ lP = P.lP;
+        const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
+        const float* prow[FM];
+        const bf16_t* bcol[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const int32_t* lmap = P.l_rows ? P.l_rows : P.c_rows;
+            const int64_t cm = m < M ? (lmap ? (int64_t)lmap[m] : m) : -1;
+            prow[i] = cm >= 0 ? lP + cm * P.ldlP : nullptr;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+            const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
+            bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
+        }
+        for (int kk = 0; kk < P.lr; kk += 2) {
+            const int k = kk + (lane >> 5);
+            float a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    }
+
     // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
+    if (P.f32out) {   // split-K partial: raw fp32, unmapped
+        float* __restrict__ Cf = (float*)P.C;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (m < M) Cf[m * P.ldc + n] = acc[i][j][e];
+                }
+        }
+        return;
+    }
     bf16_t* __restrict__ Cg = (bf16_t*)P.C;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+    for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
         if (n >= N) continue;
         const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 if (m >= M) continue;
                 const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
                 bf16_t* dst = Cg + cm * P.ldc + cn;
@@ -211,11 +309,9 @@ template <bool NN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
     __shared__ float As[FK][FB + 1];
     __shared__ float Bs[FK][FB + 1];
-    const int L = blockIdx.x;
-    const bool second = L >= args.tiles0;
-    const GemmProblem P = second ? args.p1 : args.p0;
-    const int t = second ? L - args.tiles0 : L;
-    const int tiles_m = second ? args.tiles_m1 : args.tiles_m0;
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, blockIdx.x, P, t, tiles_m);
     const int64_t m0 = (int64_t)(t % tiles_m) * FB, n0 = (int64_t)(t / tiles_m) * FB;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
     const float* Ag = (const float*)P.A;
@@ -256,44 +352,128 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
             const int64_t n = n0 + tx * 4 + j;
             if (n >= P.N) continue;
             const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
+            float v = acc[i][j];
+            if (P.lr > 0) {
+                const int64_t lm = P.l_rows ? (int64_t)P.l_rows[m] : cm;
+                const float* lP = P.lP + lm * P.ldlP;
+                const float* lB = (const float*)P.lB + cn * P.ldlB;
+                float l = 0.0f;
+                for (int k = 0; k < P.lr; ++k) l += lP[k] * lB[k];
+                v += P.lscale * l;
+            }
+            if (P.f32out) {
+                Cg[m * P.ldc + n] = v;
+                continue;
+            }
             float* dst = Cg + cm * P.ldc + cn;
-            *dst = acc[i][j] + (P.beta ? *dst : 0.0f);
+            *dst = v + (P.beta ? *dst : 0.0f);
         }
     }
 }
 
 GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn) {
-    GemmArgs a;
-    a.p0 = probs[0];
-    a.p1 = nprob > 1 ? probs[1] : probs[0];
-    const int tm0 = (int)ceil_div(a.p0.M, bm), tn0 = (int)ceil_div(a.p0.N, bn);
-    a.tiles_m0 = tm0 > 0 ? tm0 : 1;
-    a.tiles0 = (a.p0.M > 0 && a.p0.N > 0) ? tm0 * tn0 : 0;
-    int tiles1 = 0;
-    a.tiles_m1 = 1;
-    if (nprob > 1 && a.p1.M > 0 && a.p1.N > 0) {
-        const int tm1 = (int)ceil_div(a.p1.M, bm), tn1 = (int)ceil_div(a.p1.N, bn);
-        a.tiles_m1 = tm1;
-        tiles1 = tm1 * tn1;
+    GemmArgs a = {};
+    a.nprob = nprob;
+    a.first[0] = 0;
+    for (int i = 0; i < MAXP; ++i) {
+        if (i < nprob) {
+            a.p[i] = probs[i];
+            const int tm = (int)ceil_div(probs[i].M, bm), tn = (int)ceil_div(probs[i].N, bn);
+            a.tiles_m[i] = tm > 0 ? tm : 1;
+            a.first[i + 1] = a.first[i] + ((probs[i].M > 0 && probs[i].N > 0) ? tm * tn : 0);
+        } else {
+            a.p[i] = probs[0];
+            a.tiles_m[i] = 1;
+            a.first[i + 1] = a.first[i];
+        }
     }
-    a.total = a.tiles0 + tiles1;
     return a;
+}
+
+template <int BM, int BN, int WGM, int WGN, bool NN>
+hipError_t launch_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
+    GemmArgs a = make_args(probs, nprob, BM, BN);
+    const int total = a.first[MAXP];
+    if (total == 0) return hipSuccess;
+    bool any_k = false;
+    for (int i = 0; i < nprob; ++i) any_k |= probs[i].K > 0;
+    // rank-r-only launches (K = 0 everywhere) never touch the staging LDS
+    const size_t lds = any_k ? (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t) : 0;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WGM, WGN, NN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WGM, WGN, NN>), dim3(total), dim3(64 * WGM * WGN),
+                       lds, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+__global__ void splitk_reduce_kernel(const float* __restrict__ part, int64_t S, int64_t M,
+                                     int64_t N, T* __restrict__ Z, int64_t ldz,
+                                     const int32_t* __restrict__ c_rows,
+                                     const int32_t* __restrict__ c_cols, int beta) {
+    const int64_t m = blockIdx.y;
+    const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    float v = 0.0f;
+    for (int64_t s = 0; s < S; ++s) v += part[(s * M + m) * N + n];
+    const int64_t cm = c_rows ? (int64_t)c_rows[m] : m;
+    const int64_t cn = c_cols ? (int64_t)c_cols[n] : n;
+    T* dst = Z + cm * ldz + cn;
+    if (sizeof(T) == 2) {
+        bf16_t* d = (bf16_t*)dst;
+        if (beta) v += bf16_to_f32(*d);
+        *d = f32_to_bf16(v);
+    } else {
+        float* d = (float*)dst;
+        if (beta) v += *d;
+        *d = v;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st) {
-    GemmArgs a = make_args(probs, nprob, BM, BN);
-    if (a.total == 0) return hipSuccess;
-    if (nn) hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(a.total), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(a.total), dim3(256), 0, st, a);
-    return hipGetLastError();
+    // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
+    const char* env = getenv("SL_GEMM_CFG");
+    int cfg = env ? atoi(env) : 2;
+    switch (cfg) {
+        case 0: return nn ? launch_cfg<128, 128, 2, 2, true>(probs, nprob, st)
+                          : launch_cfg<128, 128, 2, 2, false>(probs, nprob, st);
+        case 1: return nn ? launch_cfg<256, 256, 2, 2, true>(probs, nprob, st)
+                          : launch_cfg<256, 256, 2, 2, false>(probs, nprob, st);
+        case 2: return nn ? launch_cfg<256, 256, 2, 4, true>(probs, nprob, st)
+                          : launch_cfg<256, 256, 2, 4, false>(probs, nprob, st);
+        case 3: return nn ? launch_cfg<256, 128, 2, 2, true>(probs, nprob, st)
+                          : launch_cfg<256, 128, 2, 2, false>(probs, nprob, st);
+        default: return nn ? launch_cfg<128, 256, 2, 2, true>(probs, nprob, st)
+                           : launch_cfg<128, 256, 2, 2, false>(probs, nprob, st);
+    }
 }
 
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st) {
     GemmArgs a = make_args(probs, nprob, FB, FB);
-    if (a.total == 0) return hipSuccess;
-    if (nn) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(a.total), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(a.total), dim3(256), 0, st, a);
+    const int total = a.first[MAXP];
+    if (total == 0) return hipSuccess;
+    if (nn) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(total), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(total), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(bool bf16, const float* part, int64_t S, int64_t M, int64_t N,
+                                void* Z, int64_t ldz, const int32_t* c_rows, const int32_t* c_cols,
+                                int beta, hipStream_t st) {
+    if (M <= 0 || N <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(N, 256), (unsigned)M);
+    if (bf16)
+        hipLaunchKernelGGL(splitk_reduce_kernel<bf16_t>, grid, dim3(256), 0, st, part, S, M, N,
+                           (bf16_t*)Z, ldz, c_rows, c_cols, beta);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, st, part, S, M, N,
+                           (float*)Z, ldz, c_rows, c_cols, beta);
     return hipGetLastError();
 }

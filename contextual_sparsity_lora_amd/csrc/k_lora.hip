@@ -109,90 +109,100 @@ __global__ void lora_xl_f32_kernel(const float* __restrict__ x, int64_t ldx, int
 }
 
 // ---------------------------------------------------------------- y += s P Bm^T
-// Tile 32 rows x 256 columns; thread = 8 consecutive columns x 4 rows.
-template <typename T>
+// A wave covers 64*CPL consecutive columns (CPL per lane, their Bm rows held
+// in registers) and walks a run of rows; the row of P is wave-uniform and is
+// read with scalar loads.  fp32 math, one rounding of y per element.
+template <typename T, int R, int CPL>
 __global__ __launch_bounds__(256) void lora_add_kernel(const float* __restrict__ P, int64_t ldp,
                                                        int64_t Tn, int64_t r,
                                                        const T* __restrict__ Bm, int64_t sbc,
                                                        int64_t sbj, int64_t Nc, float scale,
-                                                       T* __restrict__ y, int64_t ldy) {
-    __shared__ float Ps[32][65];
-    __shared__ float Bs[256][65];
-    const int64_t t0 = (int64_t)blockIdx.y * 32, c0 = (int64_t)blockIdx.x * 256;
-    for (int q = threadIdx.x; q < 32 * r; q += 256) {
-        const int rr = q / (int)r, j = q % (int)r;
-        const int64_t t = t0 + rr;
-        Ps[rr][j] = t < Tn ? P[t * ldp + j] : 0.0f;
-    }
-    if (sbc == 1) {  // B(c, j) contiguous along c: walk c fastest (coalesced)
-        for (int q = threadIdx.x; q < 256 * r; q += 256) {
-            const int cc = q & 255, j = q >> 8;
-            const int64_t c = c0 + cc;
-            Bs[cc][j] = c < Nc ? ld<T>(Bm, c + j * sbj) : 0.0f;
-        }
-    } else {         // contiguous along j: walk j fastest
-        for (int q = threadIdx.x; q < 256 * r; q += 256) {
-            const int cc = q / (int)r, j = q % (int)r;
-            const int64_t c = c0 + cc;
-            Bs[cc][j] = c < Nc ? ld<T>(Bm, c * sbc + j * sbj) : 0.0f;
-        }
-    }
-    __syncthreads();
-    const int cg = threadIdx.x & 31, rs = threadIdx.x >> 5;
-    for (int i = 0; i < 4; ++i) {
-        const int rr = rs * 4 + i;
-        const int64_t t = t0 + rr;
-        if (t >= Tn) continue;
-        float a[8];
+                                                       T* __restrict__ y, int64_t ldy, int64_t rpw) {
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c0 = (int64_t)blockIdx.x * (64 * CPL) + lane * CPL;
+    float b[CPL][R];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = 0.0f;
-        for (int j = 0; j < r; ++j) {
-            const float pv = Ps[rr][j];
+    for (int q = 0; q < CPL; ++q)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] += pv * Bs[cg * 8 + e][j];
+        for (int j = 0; j < R; ++j) {
+            const int64_t c = c0 + q;
+            b[q][j] = (c < Nc && j < r) ? ld<T>(Bm, c * sbc + j * sbj) : 0.0f;
         }
+    const int64_t t0 = ((int64_t)blockIdx.y * 4 + w) * rpw;
+    const int64_t t1 = (t0 + rpw < Tn) ? t0 + rpw : Tn;
+    const bool full = c0 + CPL <= Nc;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float* __restrict__ prow = P + t * ldp;
+        float pj[R];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t c = c0 + cg * 8 + e;
-            if (c < Nc) {
-                const int64_t o = t * ldy + c;
-                st<T>(y, o, ld<T>(y, o) + scale * a[e]);
-            }
+        for (int j = 0; j < R; ++j) pj[j] = (j < r) ? prow[j] : 0.0f;
+        float acc[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+            float a = 0.0f;
+#pragma unroll
+            for (int j = 0; j < R; ++j) a += pj[j] * b[q][j];
+            acc[q] = a;
+        }
+        T* yr = y + t * ldy + c0;
+        if (full) {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) st<T>(yr, q, ld<T>(yr, q) + scale * acc[q]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q)
+                if (c0 + q < Nc) st<T>(yr, q, ld<T>(yr, q) + scale * acc[q]);
         }
     }
 }
 
 // ---------------------------------------------------------------- out = s P^T Q
-// Partial sums over 256-token chunks into ws[chunk][j][c], then an ordered
-// reduction over chunks (deterministic).
-template <typename T, int RB>
+// Wave = 64*CPL columns x one chunk of TCH tokens; the row of P is
+// wave-uniform (scalar loads).  Partial sums per chunk go to ws[chunk][j][c];
+// an ordered reduction over chunks follows (deterministic).
+constexpr int TCH = 256;
+
+template <typename T, int R, int CPL>
 __global__ __launch_bounds__(256) void outer_partial_kernel(const float* __restrict__ P,
                                                             int64_t ldp, int64_t Tn, int64_t r,
                                                             const T* __restrict__ Q, int64_t ldq,
                                                             int64_t Nc, float* __restrict__ ws) {
-    constexpr int TCH = 256;
-    __shared__ float Ps[TCH][65];
-    const int64_t ch = blockIdx.y, t0 = ch * TCH;
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    for (int q = threadIdx.x; q < TCH * r; q += 256) {
-        const int tt = q / (int)r, j = q % (int)r;
-        const int64_t t = t0 + tt;
-        Ps[tt][j] = t < Tn ? P[t * ldp + j] : 0.0f;
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t chunk = (int64_t)blockIdx.y * 4 + w;
+    const int64_t t0 = chunk * TCH;
+    if (t0 >= Tn) return;
+    const int64_t t1 = (t0 + TCH < Tn) ? t0 + TCH : Tn;
+    const int64_t c0 = (int64_t)blockIdx.x * (64 * CPL) + lane * CPL;
+    const bool full = c0 + CPL <= Nc;
+    float acc[CPL][R];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q)
+#pragma unroll
+        for (int j = 0; j < R; ++j) acc[q][j] = 0.0f;
+    for (int64_t t = t0; t < t1; ++t) {
+        const float* __restrict__ prow = P + t * ldp;
+        float pj[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) pj[j] = (j < r) ? prow[j] : 0.0f;
+        const T* qr = Q + t * ldq + c0;
+        float qv[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) qv[q] = (full || c0 + q < Nc) ? ld<T>(qr, q) : 0.0f;
+#pragma unroll
+        for (int q = 0; q < CPL; ++q)
+#pragma unroll
+            for (int j = 0; j < R; ++j) acc[q][j] += pj[j] * qv[q];
     }
-    __syncthreads();
-    if (c >= Nc) return;
-    float acc[RB];
 #pragma unroll
-    for (int j = 0; j < RB; ++j) acc[j] = 0.0f;
-    const int64_t tn = (Tn - t0) < TCH ? (Tn - t0) : TCH;
-    for (int tt = 0; tt < tn; ++tt) {
-        const float qv = ld<T>(Q, (t0 + tt) * ldq + c);
+    for (int q = 0; q < CPL; ++q) {
+        const int64_t c = c0 + q;
+        if (c >= Nc) continue;
 #pragma unroll
-        for (int j = 0; j < RB; ++j) acc[j] += Ps[tt][j] * qv;
+        for (int j = 0; j < R; ++j)
+            if (j < r) ws[(chunk * r + j) * Nc + c] = acc[q][j];
     }
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-        if (j < r) ws[(ch * r + j) * Nc + c] = acc[j];
 }
 
 __global__ void outer_reduce_kernel(const float* __restrict__ ws, int64_t nch, int64_t r,
@@ -223,16 +233,53 @@ __global__ void transpose_kernel(const T* __restrict__ in, int64_t ldi, int64_t 
     }
 }
 
+// 8 consecutive elements, 16-byte aligned (bf16) / 32-byte aligned (fp32)
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 template <typename T>
 __global__ void swiglu_fwd_kernel(const T* __restrict__ g, int64_t ldg, const T* __restrict__ u,
                                   int64_t ldu, int64_t Tn, int64_t F, T* __restrict__ h,
                                   int64_t ldh) {
     const int64_t t = blockIdx.y;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < F;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const float gv = ld<T>(g, t * ldg + c), uv = ld<T>(u, t * ldu + c);
-        const float s = gv / (1.0f + expf(-gv));
-        st<T>(h, t * ldh + c, s * uv);
+    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (c0 >= F) return;
+    float gv[8], uv[8], hv[8];
+    if (c0 + 8 <= F) {
+        load8<T>(g + t * ldg + c0, gv);
+        load8<T>(u + t * ldu + c0, uv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[e] = gv[e] / (1.0f + expf(-gv[e])) * uv[e];
+        store8<T>(h + t * ldh + c0, hv);
+    } else {
+        for (int64_t c = c0; c < F; ++c) {
+            const float a = ld<T>(g, t * ldg + c), b = ld<T>(u, t * ldu + c);
+            st<T>(h, t * ldh + c, a / (1.0f + expf(-a)) * b);
+        }
     }
 }
 
@@ -242,57 +289,122 @@ __global__ void swiglu_bwd_kernel(const T* __restrict__ dh, int64_t lddh, const 
                                   int64_t F, T* __restrict__ dg, int64_t lddg, T* __restrict__ du,
                                   int64_t lddu) {
     const int64_t t = blockIdx.y;
-    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < F;
-         c += (int64_t)gridDim.x * blockDim.x) {
-        const float d = ld<T>(dh, t * lddh + c), gv = ld<T>(g, t * ldg + c),
-                    uv = ld<T>(u, t * ldu + c);
-        const float sg = 1.0f / (1.0f + expf(-gv));
-        const float silu = gv * sg;
-        const float dsilu = sg * (1.0f + gv * (1.0f - sg));
-        st<T>(dg, t * lddg + c, d * uv * dsilu);
-        st<T>(du, t * lddu + c, d * silu);
+    const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (c0 >= F) return;
+    if (c0 + 8 <= F) {
+        float d[8], gv[8], uv[8], a[8], b[8];
+        load8<T>(dh + t * lddh + c0, d);
+        load8<T>(g + t * ldg + c0, gv);
+        load8<T>(u + t * ldu + c0, uv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sg = 1.0f / (1.0f + expf(-gv[e]));
+            a[e] = d[e] * uv[e] * (sg * (1.0f + gv[e] * (1.0f - sg)));
+            b[e] = d[e] * (gv[e] * sg);
+        }
+        store8<T>(dg + t * lddg + c0, a);
+        store8<T>(du + t * lddu + c0, b);
+    } else {
+        for (int64_t c = c0; c < F; ++c) {
+            const float d = ld<T>(dh, t * lddh + c), gv = ld<T>(g, t * ldg + c),
+                        uv = ld<T>(u, t * ldu + c);
+            const float sg = 1.0f / (1.0f + expf(-gv));
+            st<T>(dg, t * lddg + c, d * uv * (sg * (1.0f + gv * (1.0f - sg))));
+            st<T>(du, t * lddu + c, d * (gv * sg));
+        }
     }
 }
 
+// out[m, q..q+7] = in[rows[m], cols[q..q+7]]: gathered loads, one vector store.
 template <typename T>
 __global__ void gather_cols_kernel(const T* __restrict__ in, int64_t ldi,
                                    const int32_t* __restrict__ rows, int64_t nrows,
                                    const int32_t* __restrict__ cols, int64_t ncols,
                                    T* __restrict__ out, int64_t ldo) {
     const int64_t m = blockIdx.y;
-    const int64_t src = (int64_t)rows[m] * ldi;
-    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < ncols;
-         q += (int64_t)gridDim.x * blockDim.x)
-        out[m * ldo + q] = in[src + cols[q]];
+    const int64_t q0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (q0 >= ncols) return;
+    const T* src = in + (int64_t)rows[m] * ldi;
+    T* dst = out + m * ldo + q0;
+    if (q0 + 8 <= ncols) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = ld<T>(src, cols[q0 + e]);
+        store8<T>(dst, v);
+    } else {
+        for (int64_t q = q0; q < ncols; ++q) dst[q - q0] = src[cols[q]];
+    }
 }
 
 // Zero the unselected channels of the given rows.  Thread = 8 consecutive
-// channels; membership by a binary search in the ascending index list.
+// channels (membership found once by a binary search in the ascending index
+// list) x 16 rows; all-unselected groups are cleared with one vector store.
 template <typename T>
 __global__ void zero_unselected_kernel(T* __restrict__ y, int64_t ldy,
-                                       const int32_t* __restrict__ rows, int64_t C,
+                                       const int32_t* __restrict__ rows, int64_t nrows, int64_t C,
                                        const int32_t* __restrict__ idx, int64_t n) {
     const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (c0 >= C) return;
-    T* yr = y + (int64_t)rows[blockIdx.y] * ldy;
     int64_t lo = 0, hi = n;
     while (lo < hi) {
         const int64_t mid = (lo + hi) >> 1;
         if (idx[mid] < c0) lo = mid + 1; else hi = mid;
     }
-    int64_t p = lo;
-#pragma unroll
+    unsigned keep = 0;
     for (int e = 0; e < 8; ++e) {
         const int64_t c = c0 + e;
-        if (c >= C) break;
-        while (p < n && idx[p] < c) ++p;
-        if (!(p < n && idx[p] == c)) yr[c] = (T)0;
+        while (lo < n && idx[lo] < c) ++lo;
+        if (lo < n && idx[lo] == c) keep |= 1u << e;
+    }
+    const int64_t r0 = (int64_t)blockIdx.y * 16;
+    const int64_t r1 = (r0 + 16 < nrows) ? r0 + 16 : nrows;
+    const float zeros[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int64_t rr = r0; rr < r1; ++rr) {
+        T* yr = y + (int64_t)rows[rr] * ldy + c0;
+        if (keep == 0 && c0 + 8 <= C) {
+            store8<T>(yr, zeros);
+        } else {
+            for (int e = 0; e < 8; ++e)
+                if (c0 + e < C && !((keep >> e) & 1u)) yr[e] = (T)0;
+        }
     }
 }
 
-unsigned grid_x(int64_t n, int per) {
-    int64_t g = ceil_div(n, per);
-    return (unsigned)(g < 1 ? 1 : (g > 65535 ? 65535 : g));
+
+// out[j, q] = src[idx[q], j]: gather rows of a channel-major matrix and
+// transpose them (a 64 x 64 tile through LDS; coalesced on both sides).
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_t_kernel(const T* __restrict__ src, int64_t lds,
+                                                            const int32_t* __restrict__ idx,
+                                                            int64_t n, int64_t Dd,
+                                                            T* __restrict__ out, int64_t ldo) {
+    __shared__ T tile[64][65];
+    const int64_t q0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t q = q0 + i, j = j0 + tx;
+        T v = (T)0;
+        if (q < n && j < Dd) v = src[(int64_t)idx[q] * lds + j];
+        tile[i][tx] = v;
+    }
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4) {
+        const int64_t j = j0 + i, q = q0 + tx;
+        if (j < Dd && q < n) out[j * ldo + q] = tile[tx][i];
+    }
+}
+
+// comp[c - #selected below c] = c for every unselected channel c
+__global__ void complement_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t C,
+                                  int32_t* __restrict__ comp) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (idx[mid] < c) lo = mid + 1; else hi = mid;
+    }
+    if (!(lo < n && idx[lo] == c)) comp[c - lo] = (int32_t)c;
 }
 
 }  // namespace
@@ -315,13 +427,25 @@ hipError_t launch_lora_add(bool bf16, const float* P, int64_t ldp, int64_t T, in
                            const void* Bm, int64_t sb_c, int64_t sb_j, int64_t Ncols,
                            float scale, void* y, int64_t ldy, hipStream_t st) {
     if (T <= 0 || Ncols <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(Ncols, 256), (unsigned)ceil_div(T, 32));
-    if (bf16)
-        hipLaunchKernelGGL(lora_add_kernel<bf16_t>, grid, dim3(256), 0, st, P, ldp, T, r,
-                           (const bf16_t*)Bm, sb_c, sb_j, Ncols, scale, (bf16_t*)y, ldy);
-    else
-        hipLaunchKernelGGL(lora_add_kernel<float>, grid, dim3(256), 0, st, P, ldp, T, r,
-                           (const float*)Bm, sb_c, sb_j, Ncols, scale, (float*)y, ldy);
+    constexpr int64_t RPW = 32;  // rows per wave
+    const dim3 block(256);
+#define ADD(TT, RR, CP)                                                                        \
+    hipLaunchKernelGGL((lora_add_kernel<TT, RR, CP>),                                          \
+                       dim3((unsigned)ceil_div(Ncols, 64 * CP), (unsigned)ceil_div(T, 4 * RPW)), \
+                       block, 0, st, P, ldp, T, r, (const TT*)Bm, sb_c, sb_j, Ncols, scale,     \
+                       (TT*)y, ldy, RPW)
+    if (bf16) {
+        if (r <= 8) ADD(bf16_t, 8, 4);
+        else if (r <= 16) ADD(bf16_t, 16, 4);
+        else if (r <= 32) ADD(bf16_t, 32, 4);
+        else ADD(bf16_t, 64, 2);
+    } else {
+        if (r <= 8) ADD(float, 8, 4);
+        else if (r <= 16) ADD(float, 16, 4);
+        else if (r <= 32) ADD(float, 32, 4);
+        else ADD(float, 64, 2);
+    }
+#undef ADD
     return hipGetLastError();
 }
 
@@ -330,28 +454,28 @@ hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T,
                               int64_t so_j, int64_t so_c, float* ws, size_t ws_floats,
                               hipStream_t st) {
     if (Ncols <= 0 || r <= 0) return hipSuccess;
-    const int64_t nch = T > 0 ? ceil_div(T, 256) : 1;
+    const int64_t nch = T > 0 ? ceil_div(T, TCH) : 0;
     if ((size_t)(nch * r * Ncols) > ws_floats) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ceil_div(Ncols, 256), (unsigned)nch);
     if (T > 0) {
-#define OUTER(TT, RB)                                                                         \
-    hipLaunchKernelGGL((outer_partial_kernel<TT, RB>), grid, dim3(256), 0, st, P, ldp, T, r, \
-                       (const TT*)Q, ldq, Ncols, ws)
+#define OUTER(TT, RR, CP)                                                                       \
+    hipLaunchKernelGGL((outer_partial_kernel<TT, RR, CP>),                                      \
+                       dim3((unsigned)ceil_div(Ncols, 64 * CP), (unsigned)ceil_div(nch, 4)),     \
+                       dim3(256), 0, st, P, ldp, T, r, (const TT*)Q, ldq, Ncols, ws)
         if (bf16) {
-            if (r <= 8) OUTER(bf16_t, 8);
-            else if (r <= 16) OUTER(bf16_t, 16);
-            else if (r <= 32) OUTER(bf16_t, 32);
-            else OUTER(bf16_t, 64);
+            if (r <= 8) OUTER(bf16_t, 8, 4);
+            else if (r <= 16) OUTER(bf16_t, 16, 4);
+            else if (r <= 32) OUTER(bf16_t, 32, 4);
+            else OUTER(bf16_t, 64, 2);
         } else {
-            if (r <= 8) OUTER(float, 8);
-            else if (r <= 16) OUTER(float, 16);
-            else if (r <= 32) OUTER(float, 32);
-            else OUTER(float, 64);
+            if (r <= 8) OUTER(float, 8, 4);
+            else if (r <= 16) OUTER(float, 16, 4);
+            else if (r <= 32) OUTER(float, 32, 4);
+            else OUTER(float, 64, 2);
         }
 #undef OUTER
     }
     hipLaunchKernelGGL(outer_reduce_kernel, dim3((unsigned)ceil_div(r * Ncols, 256)), dim3(256), 0,
-                       st, ws, T > 0 ? nch : 0, r, Ncols, scale, out, so_j, so_c);
+                       st, ws, nch, r, Ncols, scale, out, so_j, so_c);
     return hipGetLastError();
 }
 
@@ -371,7 +495,7 @@ hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows
 hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* u, int64_t ldu,
                              int64_t T, int64_t F, void* h, int64_t ldh, hipStream_t st) {
     if (T <= 0 || F <= 0) return hipSuccess;
-    const dim3 grid(grid_x(F, 256), (unsigned)T);
+    const dim3 grid((unsigned)ceil_div(F, 256 * 8), (unsigned)T);
     if (bf16)
         hipLaunchKernelGGL(swiglu_fwd_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)g, ldg,
                            (const bf16_t*)u, ldu, T, F, (bf16_t*)h, ldh);
@@ -385,7 +509,7 @@ hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void
                              const void* u, int64_t ldu, int64_t T, int64_t F, void* dg,
                              int64_t lddg, void* du, int64_t lddu, hipStream_t st) {
     if (T <= 0 || F <= 0) return hipSuccess;
-    const dim3 grid(grid_x(F, 256), (unsigned)T);
+    const dim3 grid((unsigned)ceil_div(F, 256 * 8), (unsigned)T);
     if (bf16)
         hipLaunchKernelGGL(swiglu_bwd_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)dh,
                            lddh, (const bf16_t*)g, ldg, (const bf16_t*)u, ldu, T, F, (bf16_t*)dg,
@@ -401,7 +525,7 @@ hipError_t launch_gather_cols(bool bf16, const void* in, int64_t ldi, const int3
                               int64_t nrows, const int32_t* cols, int64_t ncols, void* out,
                               int64_t ldo, hipStream_t st) {
     if (nrows <= 0 || ncols <= 0) return hipSuccess;
-    const dim3 grid(grid_x(ncols, 256), (unsigned)nrows);
+    const dim3 grid((unsigned)ceil_div(ncols, 256 * 8), (unsigned)nrows);
     if (bf16)
         hipLaunchKernelGGL(gather_cols_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)in,
                            ldi, rows, nrows, cols, ncols, (bf16_t*)out, ldo);
@@ -416,12 +540,33 @@ hipError_t launch_zero_unselected(bool bf16, void* y, int64_t ldy, const int32_t
                                   uint8_t* unused, hipStream_t st) {
     (void)unused;
     if (nrows <= 0 || C <= 0 || n >= C) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(C, 256 * 8), (unsigned)nrows);
+    const dim3 grid((unsigned)ceil_div(C, 256 * 8), (unsigned)ceil_div(nrows, 16));
     if (bf16)
         hipLaunchKernelGGL(zero_unselected_kernel<bf16_t>, grid, dim3(256), 0, st, (bf16_t*)y, ldy,
-                           rows, C, idx, n);
+                           rows, nrows, C, idx, n);
     else
         hipLaunchKernelGGL(zero_unselected_kernel<float>, grid, dim3(256), 0, st, (float*)y, ldy,
-                           rows, C, idx, n);
+                           rows, nrows, C, idx, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_complement(const int32_t* idx, int64_t n, int64_t C, int32_t* comp,
+                             hipStream_t st) {
+    if (C <= 0 || n >= C) return hipSuccess;
+    hipLaunchKernelGGL(complement_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, st, idx, n,
+                       C, comp);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const int32_t* idx,
+                                int64_t n, int64_t Dd, void* out, int64_t ldo, hipStream_t st) {
+    if (n <= 0 || Dd <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(n, 64), (unsigned)ceil_div(Dd, 64));
+    if (bf16)
+        hipLaunchKernelGGL(gather_rows_t_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src,
+                           lds, idx, n, Dd, (bf16_t*)out, ldo);
+    else
+        hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, (const float*)src,
+                           lds, idx, n, Dd, (float*)out, ldo);
     return hipGetLastError();
 }

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
+#include <cstdlib>
 #include <cstdio>
 #include <new>
 
@@ -89,10 +90,11 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // stream while timing is enabled.
 const char* const kClassNames[] = {"gemm_bf16_nt", "gemm_bf16_nn", "gemm_f32",   "estimate",
                                    "score",        "topk",         "lora",       "swiglu",
-                                   "gather",       "fill",         "token_split", "index"};
+                                   "gather",       "fill",         "token_split", "index",
+                                   "splitk_reduce"};
 constexpr int kNumClasses = sizeof(kClassNames) / sizeof(kClassNames[0]);
 enum { K_GEMM_NT, K_GEMM_NN, K_GEMM_F32, K_EST, K_SCORE, K_TOPK, K_LORA, K_SWIGLU, K_GATHER,
-       K_FILL, K_SPLIT, K_INDEX };
+       K_FILL, K_SPLIT, K_INDEX, K_REDUCE };
 
 hipEvent_t take_event(sl_handle* h) {
     if (!h->event_pool.empty()) {
@@ -415,11 +417,181 @@ static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem*
     return hip_check(h, e, "gemm");
 }
 
+}  // extern "C"
+
+namespace {
+
+struct LoraEpi {
+    const float* P;
+    int64_t ldP;
+    const void* B;
+    int64_t ldB;
+    int64_t r;
+    float scale;
+};
+
+sl_status check_lora(sl_handle* h, const LoraEpi& l, int64_t T, int64_t Nout, sl_dtype dt) {
+    if (!l.P) return SL_OK;
+    SL_REQUIRE(h, l.r >= 1 && l.r <= 64, "lora_r must be in [1, 64]");
+    SL_REQUIRE(h, l.ldP >= l.r && l.ldB >= l.r, "LoRA leading dimension < lora_r");
+    SL_REQUIRE(h, l.B != nullptr, "lora_B is NULL");
+    (void)T; (void)Nout; (void)dt;
+    return SL_OK;
+}
+
+void set_lora(GemmProblem& p, const LoraEpi& l) {
+    p.lP = l.P;
+    p.ldlP = l.ldP;
+    p.lB = l.B;
+    p.ldlB = l.ldB;
+    p.lr = l.P ? (int)l.r : 0;
+    p.lscale = l.scale;
+}
+
+GemmProblem problem(const void* A, int64_t lda, const int32_t* a_rows, const void* B, int64_t ldb,
+                    const int32_t* b_rows, void* C, int64_t ldc, const int32_t* c_rows,
+                    const int32_t* c_cols, int64_t M, int64_t N, int64_t K, int beta,
+                    const LoraEpi& l) {
+    GemmProblem p = {A, lda, a_rows, B, ldb, b_rows, C, ldc, c_rows, c_cols, M, N, K, beta,
+                     nullptr, 0, nullptr, 0, 0, 0.f, 0, nullptr};
+    set_lora(p, l);
+    return p;
+}
+
+// Output-channel-sparse product (context rows keep only the selected output
+// channels): fwd side OUT and bwd side IN share this shape.
+//   Z[t, :] = X[t, :] Wc^T  over all channels for output rows,
+//   Z[t, c] = X[t, :] . Wc[c, :] for selected c on context rows,
+//   unselected context channels: the rank-r term if given, else 0.
+sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64_t T,
+                     int64_t Kdim, const void* Wc, int64_t ldw, int64_t C,
+                     const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
+                     const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
+                     const LoraEpi& l) {
+    if (n == C || T_c == 0) {
+        GemmProblem p = problem(X, ldx, nullptr, Wc, ldw, nullptr, Z, ldz, nullptr, nullptr, T, C,
+                                Kdim, beta, l);
+        return run_gemm(h, dt, false, &p, 1);
+    }
+    GemmProblem p[2];
+    p[0] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim, beta, l);
+    p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l);
+    const int np = 2;
+    if (l.P) {
+        SL_CHECK(ensure_ws(h, round_up((size_t)(C - n) * 4, 256)));
+        int32_t* comp = (int32_t*)h->ws;
+        {
+            Timed tm(h, K_INDEX, 0, 4.0 * (C + n));
+            SL_HIP(h, launch_complement(idx, n, C, comp, h->stream), "complement");
+        }
+        // unselected channels of context rows: the rank-r term alone, as its own
+        // launch (a K = 0 product needs no staging memory, so it runs many
+        // blocks per CU and does not take XCDs away from the main tiles)
+        GemmProblem pc = problem(nullptr, 0, ctx_rows, nullptr, 0, nullptr, Z, ldz, ctx_rows, comp,
+                                 T_c, C - n, 0, beta, l);
+        {
+            Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C - n) * esize(dt));
+            SL_HIP(h, dt == SL_BF16 ? launch_gemm_bf16(false, &pc, 1, h->stream)
+                                    : launch_gemm_f32(false, &pc, 1, h->stream), "lora_fill");
+        }
+    } else if (!beta) {
+        Timed tm(h, K_FILL, 0, (double)T_c * (C - n) * esize(dt));
+        SL_HIP(h, launch_zero_unselected(dt == SL_BF16, Z, ldz, ctx_rows, T_c, idx, n, C, nullptr,
+                                         h->stream), "zero_unselected");
+    }
+    return run_gemm(h, dt, false, p, np);
+}
+
+// Input-channel-sparse product (context rows contract over the selected
+// channels only): fwd side IN and bwd side OUT share this shape.
+//   Wd [Nout, C]: the product's weight with K = C contiguous (dense rows);
+//   Wc [C, Nout]: the same weight with one channel per row.
+// Output rows: Z = X[out] Wd^T over all C channels.  Context rows: the
+// selected columns of X are compacted (Xc [T_c, n]) and the selected rows of
+// Wc are gathered and transposed into a slice Ws [Nout, n] (contiguous K), so
+// both products run on the NT kernel.
+sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64_t T, int64_t C,
+                    const void* Wd, int64_t ldwd, const void* Wc, int64_t ldwc, int64_t Nout,
+                    const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
+                    const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
+                    const LoraEpi& l) {
+    if (n == C || T_c == 0) {
+        GemmProblem p = problem(X, ldx, nullptr, Wd, ldwd, nullptr, Z, ldz, nullptr, nullptr, T, Nout,
+                                C, beta, l);
+        return run_gemm(h, dt, false, &p, 1);
+    }
+    const int64_t ldn = n > 0 ? (n + 7) / 8 * 8 : 8;
+    // The dense output-row product contracts over all C channels, the
+    // context-row product over n of them.  When C is several times n the dense
+    // part may be split along K (fp32 partials + one ordered reduction) so the
+    // tiles of the launch carry similar work.  SL_SPLITK_MAX caps the split
+    // (tuning sweeps; default 4).
+    const char* env = getenv("SL_SPLITK_MAX");
+    const int64_t smax = env ? atoll(env) : 4;
+    int64_t S = 1, Ks = C;
+    if (dt == SL_BF16 && T_o > 0 && n > 0 && smax > 1) {
+        S = (C + n / 2) / n;
+        S = S < 1 ? 1 : (S > smax ? smax : S);
+        if (S > 1) {
+            Ks = ceil_div(ceil_div(C, S), 64) * 64;
+            S = ceil_div(C, Ks);
+        }
+    }
+    const size_t xc_bytes = round_up((size_t)(T_c * ldn) * esize(dt), 256);
+    const size_t ws_bytes = round_up((size_t)(Nout * ldn) * esize(dt), 256);
+    const size_t part_bytes = S > 1 ? round_up((size_t)(S * T_o * Nout) * 4, 256) : 0;
+    SL_CHECK(ensure_ws(h, xc_bytes + ws_bytes + part_bytes));
+    void* xc = h->ws;
+    void* wsl = (char*)h->ws + xc_bytes;
+    float* part = (float*)((char*)h->ws + xc_bytes + ws_bytes);
+    if (n > 0) {
+        Timed tm(h, K_GATHER, 0, 2.0 * (T_c + Nout) * n * esize(dt));
+        SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, xc, ldn,
+                                     h->stream), "gather_cols");
+        SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, Nout, wsl, ldn, h->stream),
+               "gather_rows_t");
+    }
+    GemmProblem p[5];
+    int np = 0;
+    if (S == 1) {
+        p[np++] = problem(X, ldx, out_rows, Wd, ldwd, nullptr, Z, ldz, out_rows, nullptr, T_o, Nout, C,
+                          beta, l);
+    } else {
+        for (int64_t q = 0; q < S; ++q) {
+            const int64_t k0 = q * Ks, kn = (C - k0) < Ks ? (C - k0) : Ks;
+            LoraEpi lq = l;
+            if (q > 0) lq.P = nullptr;      // the rank-r term goes into the first partial
+            GemmProblem pp = problem((const char*)X + k0 * esize(dt), ldx, out_rows,
+                                     (const char*)Wd + k0 * esize(dt), ldwd, nullptr,
+                                     part + q * T_o * Nout, Nout, nullptr, nullptr, T_o, Nout, kn, 0,
+                                     lq);
+            pp.f32out = 1;
+            pp.l_rows = out_rows;
+            p[np++] = pp;
+        }
+    }
+    p[np++] = problem(xc, ldn, nullptr, wsl, ldn, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout, n,
+                      beta, l);
+    SL_CHECK(run_gemm(h, dt, false, p, np));
+    if (S > 1) {
+        Timed tm(h, K_REDUCE, (double)S * T_o * Nout, (double)(S * 4 + 2 * esize(dt)) * T_o * Nout);
+        SL_HIP(h, launch_splitk_reduce(dt == SL_BF16, part, S, T_o, Nout, Z, ldz, out_rows, nullptr,
+                                       beta, h->stream), "splitk_reduce");
+    }
+    return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const void* x,
                                int64_t ldx, int64_t T, int64_t D_in, const void* W, int64_t ldw,
-                               int64_t D_out, const int32_t* ctx_rows, int64_t T_c,
+                               const void* Wt, int64_t ldwt, int64_t D_out, const int32_t* ctx_rows, int64_t T_c,
                                const int32_t* out_rows, int64_t T_o, const int32_t* idx,
-                               int64_t n, void* y, int64_t ldy, int beta) {
+                               int64_t n, void* y, int64_t ldy, int beta, const float* lora_P,
+                               int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
+                               int64_t lora_r, float lora_scale) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
@@ -428,52 +600,30 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
+    const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
+    SL_CHECK(check_lora(h, l, T, D_out, dt));
     if (T == 0) return SL_OK;
     SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
     SL_CHECK(check_matrix(h, y, ldy, D_out, dt, "y"));
-    if (side == SL_SIDE_OUT) SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
-    else SL_CHECK(check_matrix(h, W, ldw, D_out, dt, "W"));
+    SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
+    const bool need_t = side == SL_SIDE_IN && n < C && T_c > 0;
+    if (need_t) SL_CHECK(check_matrix(h, Wt, ldwt, D_out, dt, "Wt"));
     DeviceGuard g(h->device);
-    const bool nn = side == SL_SIDE_IN;
-    if (n == C || T_c == 0) {
-        // every channel kept (or no context rows): the dense product over all rows
-        GemmProblem p = {x, ldx, nullptr, W, ldw, nullptr, y, ldy, nullptr, nullptr, T, D_out, D_in, beta};
-        return run_gemm(h, dt, nn, &p, 1);
-    }
-    if (side == SL_SIDE_OUT) {
-        // output rows dense; context rows gather the selected weight rows (N-gather)
-        if (!beta && n < C) {
-            Timed tm(h, K_FILL, 0, (double)T_c * (C - n) * esize(dt));
-            SL_HIP(h, launch_zero_unselected(dt == SL_BF16, y, ldy, ctx_rows, T_c, idx, n, C,
-                                             nullptr, h->stream), "zero_unselected");
-        }
-        GemmProblem p[2] = {};
-        p[0] = {x, ldx, out_rows, W, ldw, nullptr, y, ldy, out_rows, nullptr, T_o, D_out, D_in, beta};
-        p[1] = {x, ldx, ctx_rows, W, ldw, idx, y, ldy, ctx_rows, idx, T_c, n, D_in, beta};
-        return run_gemm(h, dt, false, p, 2);
-    }
-    // side IN: output rows dense over all input channels; context rows use the
-    // selected input channels: compact x[ctx][:, idx] then a K-gathered GEMM.
-    const int64_t ldc = n > 0 ? (n + 7) / 8 * 8 : 8;
-    SL_CHECK(ensure_ws(h, round_up((size_t)(T_c * ldc) * esize(dt), 256)));
-    void* xc = h->ws;
-    if (n > 0) {
-        Timed tm(h, K_GATHER, 0, 2.0 * T_c * n * esize(dt));
-        SL_HIP(h, launch_gather_cols(dt == SL_BF16, x, ldx, ctx_rows, T_c, idx, n, xc, ldc,
-                                     h->stream), "gather_cols");
-    }
-    GemmProblem p[2] = {};
-    p[0] = {x, ldx, out_rows, W, ldw, nullptr, y, ldy, out_rows, nullptr, T_o, D_out, D_in, beta};
-    p[1] = {xc, ldc, nullptr, W, ldw, idx, y, ldy, ctx_rows, nullptr, T_c, D_out, n, beta};
-    return run_gemm(h, dt, true, p, 2);
+    if (side == SL_SIDE_OUT)
+        return out_sparse(h, dt, x, ldx, T, D_in, W, ldw, D_out, ctx_rows, T_c, out_rows, T_o, idx,
+                          n, y, ldy, beta, l);
+    return in_sparse(h, dt, x, ldx, T, D_in, W, ldw, Wt, ldwt, D_out, ctx_rows, T_c, out_rows, T_o,
+                     idx, n, y, ldy, beta, l);
 }
 
 // ---------------------------------------------------------------- a10/a11
 sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const void* dy,
                                int64_t lddy, int64_t T, int64_t D_out, const void* W, int64_t ldw,
-                               int64_t D_in, const int32_t* ctx_rows, int64_t T_c,
+                               const void* Wt, int64_t ldwt, int64_t D_in, const int32_t* ctx_rows, int64_t T_c,
                                const int32_t* out_rows, int64_t T_o, const int32_t* idx,
-                               int64_t n, void* dx, int64_t lddx, int beta) {
+                               int64_t n, void* dx, int64_t lddx, int beta, const float* lora_P,
+                               int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
+                               int64_t lora_r, float lora_scale) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
@@ -482,42 +632,21 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
+    const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
+    SL_CHECK(check_lora(h, l, T, D_in, dt));
     if (T == 0) return SL_OK;
     SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
     SL_CHECK(check_matrix(h, dx, lddx, D_in, dt, "dx"));
-    if (side == SL_SIDE_OUT) SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
-    else SL_CHECK(check_matrix(h, W, ldw, D_out, dt, "W"));
+    SL_CHECK(check_matrix(h, Wt, ldwt, D_out, dt, "Wt"));
+    const bool need_w = side == SL_SIDE_OUT && n < C && T_c > 0;
+    if (need_w) SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
     DeviceGuard g(h->device);
-    const bool nn = side == SL_SIDE_OUT;   // dx = dy W contracts over W's rows
-    if (n == C || T_c == 0) {
-        GemmProblem p = {dy, lddy, nullptr, W, ldw, nullptr, dx, lddx, nullptr, nullptr, T, D_in, D_out, beta};
-        return run_gemm(h, dt, nn, &p, 1);
-    }
-    if (side == SL_SIDE_IN) {
-        // dx = dy Wt^T; context rows produce only the selected input channels
-        if (!beta && n < C) {
-            Timed tm(h, K_FILL, 0, (double)T_c * (C - n) * esize(dt));
-            SL_HIP(h, launch_zero_unselected(dt == SL_BF16, dx, lddx, ctx_rows, T_c, idx, n, C,
-                                             nullptr, h->stream), "zero_unselected");
-        }
-        GemmProblem p[2] = {};
-        p[0] = {dy, lddy, out_rows, W, ldw, nullptr, dx, lddx, out_rows, nullptr, T_o, D_in, D_out, beta};
-        p[1] = {dy, lddy, ctx_rows, W, ldw, idx, dx, lddx, ctx_rows, idx, T_c, n, D_out, beta};
-        return run_gemm(h, dt, false, p, 2);
-    }
-    // side OUT: dx = dy W; context rows contract over the selected channels only
-    const int64_t ldc = n > 0 ? (n + 7) / 8 * 8 : 8;
-    SL_CHECK(ensure_ws(h, round_up((size_t)(T_c * ldc) * esize(dt), 256)));
-    void* dyc = h->ws;
-    if (n > 0) {
-        Timed tm(h, K_GATHER, 0, 2.0 * T_c * n * esize(dt));
-        SL_HIP(h, launch_gather_cols(dt == SL_BF16, dy, lddy, ctx_rows, T_c, idx, n, dyc, ldc,
-                                     h->stream), "gather_cols");
-    }
-    GemmProblem p[2] = {};
-    p[0] = {dy, lddy, out_rows, W, ldw, nullptr, dx, lddx, out_rows, nullptr, T_o, D_in, D_out, beta};
-    p[1] = {dyc, ldc, nullptr, W, ldw, idx, dx, lddx, ctx_rows, nullptr, T_c, D_in, n, beta};
-    return run_gemm(h, dt, true, p, 2);
+    if (side == SL_SIDE_IN)   // dx = dy W: context rows produce the selected channels only
+        return out_sparse(h, dt, dy, lddy, T, D_out, Wt, ldwt, D_in, ctx_rows, T_c, out_rows, T_o,
+                          idx, n, dx, lddx, beta, l);
+    // side OUT: context rows contract over the selected output channels only
+    return in_sparse(h, dt, dy, lddy, T, D_out, Wt, ldwt, W, ldw, D_in, ctx_rows, T_c, out_rows,
+                     T_o, idx, n, dx, lddx, beta, l);
 }
 
 // ---------------------------------------------------------------- a8/a12
@@ -525,40 +654,46 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
                           int64_t T, int64_t D_in, int64_t D_out, const void* A, const void* B,
                           int64_t r, float scale, float* xl, int64_t ldxl, void* y, int64_t ldy,
                           const void* dy, int64_t lddy, void* dx, int64_t lddx, float* dA,
-                          float* dB) {
+                          float* dB, float* gB_io, int64_t ldgB) {
     if (!h) return SL_ERR_INVALID;
-    SL_REQUIRE(h, (mode & ~7) == 0 && mode != 0, "bad mode");
+    const int all = SL_LORA_XL | SL_LORA_ADD | SL_LORA_GB | SL_LORA_DA | SL_LORA_DB | SL_LORA_DX;
+    SL_REQUIRE(h, (mode & ~all) == 0 && mode != 0, "bad mode");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, r >= 1 && r <= 64, "r must be in [1, 64]");
     SL_REQUIRE(h, T >= 0 && T <= 65535 * 32 && D_in >= 1 && D_out >= 1, "bad sizes");
-    SL_REQUIRE(h, xl != nullptr && ldxl >= r, "xl is NULL or ldxl < r");
     const bool bf = dt == SL_BF16;
-    if (mode & (SL_LORA_XL | SL_LORA_BWD)) {
-        SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
-        SL_CHECK(check_matrix(h, A, D_in, D_in, dt, "A"));
-    }
-    if (mode & (SL_LORA_ADD | SL_LORA_BWD)) SL_REQUIRE(h, B != nullptr, "B is NULL");
+    const bool gb = mode & SL_LORA_GB, da = mode & SL_LORA_DA, db = mode & SL_LORA_DB,
+               dxm = mode & SL_LORA_DX;
+    if (mode & (SL_LORA_XL | SL_LORA_ADD | SL_LORA_DB))
+        SL_REQUIRE(h, xl != nullptr && ldxl >= r, "xl is NULL or ldxl < r");
+    if (mode & (SL_LORA_XL | SL_LORA_DA)) SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
+    if (mode & (SL_LORA_XL | SL_LORA_DX)) SL_CHECK(check_matrix(h, A, D_in, D_in, dt, "A"));
+    if (mode & (SL_LORA_ADD | SL_LORA_GB)) SL_REQUIRE(h, B != nullptr, "B is NULL");
     if (mode & SL_LORA_ADD) SL_CHECK(check_matrix(h, y, ldy, D_out, dt, "y"));
-    if (mode & SL_LORA_BWD) {
-        SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
-        SL_REQUIRE(h, dA && dB, "dA / dB is NULL");
-        if (dx) SL_CHECK(check_matrix(h, dx, lddx, D_in, dt, "dx"));
-    }
+    if (gb || db) SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
+    if (da) SL_REQUIRE(h, dA != nullptr, "dA is NULL");
+    if (db) SL_REQUIRE(h, dB != nullptr, "dB is NULL");
+    if (dxm) SL_CHECK(check_matrix(h, dx, lddx, D_in, dt, "dx"));
+    if ((da || dxm) && !gb) SL_REQUIRE(h, gB_io != nullptr, "gB input is NULL");
+    if (gB_io) SL_REQUIRE(h, ldgB >= r, "ldgB < r");
     DeviceGuard g(h->device);
     const double es = (double)esize(dt);
-    Timed tm(h, K_LORA,
-             ((mode & SL_LORA_XL) ? 2.0 * T * D_in * r : 0) + ((mode & SL_LORA_ADD) ? 2.0 * T * D_out * r : 0) +
-                 ((mode & SL_LORA_BWD) ? 2.0 * T * r * (2.0 * D_out + D_in + (dx ? D_in : 0)) : 0),
-             ((mode & SL_LORA_XL) ? es * T * D_in + 4.0 * T * r : 0) +
-                 ((mode & SL_LORA_ADD) ? 2 * es * T * D_out + 4.0 * T * r : 0) +
-                 ((mode & SL_LORA_BWD) ? es * T * (D_in + D_out) + (dx ? 2 * es * T * D_in : 0) : 0));
+    const double fl = ((mode & SL_LORA_XL) ? 2.0 * T * D_in * r : 0) +
+                      ((mode & SL_LORA_ADD) ? 2.0 * T * D_out * r : 0) + (gb ? 2.0 * T * D_out * r : 0) +
+                      (da ? 2.0 * T * D_in * r : 0) + (db ? 2.0 * T * D_out * r : 0) +
+                      (dxm ? 2.0 * T * D_in * r : 0);
+    const double by = ((mode & SL_LORA_XL) ? es * T * D_in + 4.0 * T * r : 0) +
+                      ((mode & SL_LORA_ADD) ? 2 * es * T * D_out + 4.0 * T * r : 0) +
+                      (gb ? es * T * D_out + 4.0 * T * r : 0) + (da ? es * T * D_in : 0) +
+                      (db ? es * T * D_out : 0) + (dxm ? 2 * es * T * D_in : 0);
+    Timed tm(h, K_LORA, fl, by);
     if (mode & SL_LORA_XL)
         SL_HIP(h, launch_lora_xl(bf, x, ldx, T, D_in, A, D_in, r, xl, ldxl, nullptr, h->stream),
                "lora_xl");
     if (mode & SL_LORA_ADD)
         SL_HIP(h, launch_lora_add(bf, xl, ldxl, T, r, B, r, 1, D_out, scale, y, ldy, h->stream),
                "lora_add");
-    if (mode & SL_LORA_BWD) {
+    if (gb || da || db || dxm) {
         // workspace: B^T [r, D_out] (dt), gB [T, r] fp32, chunk partials
         const int64_t nch = T > 0 ? ceil_div(T, 256) : 1;
         const int64_t ldbt = ceil_div(D_out, 8) * 8;
@@ -569,17 +704,22 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         SL_CHECK(ensure_ws(h, bt_bytes + gb_bytes + part_floats * 4));
         char* ws = (char*)h->ws;
         void* Bt = ws;
-        float* gB = (float*)(ws + bt_bytes);
+        float* gB = gB_io ? gB_io : (float*)(ws + bt_bytes);
+        const int64_t ldg = gB_io ? ldgB : r;
         float* part = (float*)(ws + bt_bytes + gb_bytes);
-        SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
-        SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, Bt, ldbt, r, gB, r, nullptr, h->stream),
-               "lora_gB");
-        SL_HIP(h, launch_outer_accum(bf, gB, r, T, r, x, ldx, D_in, scale, dA, D_in, 1, part,
-                                     part_floats, h->stream), "lora_dA");
-        SL_HIP(h, launch_outer_accum(bf, xl, ldxl, T, r, dy, lddy, D_out, scale, dB, 1, r, part,
-                                     part_floats, h->stream), "lora_dB");
-        if (dx)
-            SL_HIP(h, launch_lora_add(bf, gB, r, T, r, A, 1, D_in, D_in, scale, dx, lddx, h->stream),
+        if (gb) {
+            SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
+            SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, Bt, ldbt, r, gB, ldg, nullptr, h->stream),
+                   "lora_gB");
+        }
+        if (da)
+            SL_HIP(h, launch_outer_accum(bf, gB, ldg, T, r, x, ldx, D_in, scale, dA, D_in, 1, part,
+                                         part_floats, h->stream), "lora_dA");
+        if (db)
+            SL_HIP(h, launch_outer_accum(bf, xl, ldxl, T, r, dy, lddy, D_out, scale, dB, 1, r, part,
+                                         part_floats, h->stream), "lora_dB");
+        if (dxm)
+            SL_HIP(h, launch_lora_add(bf, gB, ldg, T, r, A, 1, D_in, D_in, scale, dx, lddx, h->stream),
                    "lora_dx");
     }
     return SL_OK;

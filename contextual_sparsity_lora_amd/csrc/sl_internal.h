@@ -49,9 +49,16 @@ struct GemmProblem {
     const int32_t* c_cols;                                 // C col n -> c_cols[n] (or n)
     int64_t M, N, K;
     int beta;                                              // 1: C += result
+    // optional rank-lr term added before the single rounding of C:
+    //   C[cm, cn] += lscale * sum_j lP[cm, j] * lB[cn, j]   (cm, cn: mapped row/col)
+    const float* lP;  int64_t ldlP;
+    const void* lB;   int64_t ldlB;
+    int lr;           float lscale;
+    int f32out;       // 1: store the raw fp32 accumulators (split-K partials)
+    const int32_t* l_rows;  // rank-r row map (token rows) when C rows are unmapped partials
 };
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
-// nn = true: B is [K, N] ("NN").  Up to two problems in one launch.
+// nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 // fp32 version (VALU), same semantics.
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
@@ -73,6 +80,16 @@ hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t 
 hipError_t launch_gather_cols(bool bf16, const void* in, int64_t ldi, const int32_t* rows,
                               int64_t nrows, const int32_t* cols, int64_t ncols, void* out,
                               int64_t ldo, hipStream_t st);
+// Z[c_rows[m], c_cols[n]] = round(sum_s part[s][m][n] (+ Z if beta)), s ascending
+hipError_t launch_splitk_reduce(bool bf16, const float* part, int64_t S, int64_t M, int64_t N,
+                                void* Z, int64_t ldz, const int32_t* c_rows, const int32_t* c_cols,
+                                int beta, hipStream_t st);
+// out[j, q] = src[idx[q], j] for j < Dd, q < n (row gather + transpose)
+hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const int32_t* idx,
+                                int64_t n, int64_t Dd, void* out, int64_t ldo, hipStream_t st);
+// comp[q] = the q-th channel in [0, C) not in the ascending list idx[0..n)
+hipError_t launch_complement(const int32_t* idx, int64_t n, int64_t C, int32_t* comp,
+                             hipStream_t st);
 hipError_t launch_zero_unselected(bool bf16, void* y, int64_t ldy, const int32_t* rows,
                                   int64_t nrows, const int32_t* idx, int64_t n, int64_t C,
                                   uint8_t* mask_ws, hipStream_t st);

@@ -10,13 +10,21 @@ selection over the intermediate channels is shared by gate, up and down; §3.4
 backward: gradients only through active channels, LoRA gradients dense.
 
 Layout in device memory (allocated once, reused every step):
-  W_gu  [2F, D]  gate rows then up rows (channel-major, nn.Linear layout)
-  Wt_dn [F, D]   transposed down weight: one intermediate channel per row
-  A_gu  [2r, D]  LoRA A of gate then up; B_* in nn.Linear LoRA layout
-  WA    [D, 2k]  estimator W_A of gate then up (fp32); WB_* [k, F] (fp32)
-  gu    [T, 2F]  gate pre-activation | up pre-activation (main + LoRA)
-  dgu   [T, 2F]  their gradients
-Everything below is marshalling: each step is one C-ABI call.
+  W_gu  [2F, D]   gate rows then up rows (nn.Linear layout)
+  W_guT [D, 2F]   its transposed copy (backward products)
+  W_dn  [D, F]    down weight (nn.Linear layout, forward products)
+  Wt_dn [F, D]    its transposed copy: one intermediate channel per row
+  A_gu  [2r, D]   LoRA A of gate then up
+  B_bd  [2F, 2r]  LoRA B of gate and up, block diagonal (gate in [:F, :r], up in
+                  [F:, r:], zeros elsewhere), so one rank-2r term serves the
+                  stacked gate|up product
+  WA    [D, 2k]   estimator W_A of gate then up (fp32); WB_* [k, F] (fp32)
+  gu    [T, 2F]   gate pre-activation | up pre-activation (main + LoRA)
+  dgu   [T, 2F]   their gradients
+The LoRA terms of the outputs (y += s xl B^T) and of the input gradients
+(dx += s gB A) are fused into the main-branch GEMMs; LoRA gradients dA, dB are
+separate reductions over tokens.  Everything below is marshalling: each step
+is one C-ABI call.
 """
 import torch
 
@@ -43,11 +51,19 @@ class SparseFFN:
         self.dense = dense
         self.n = self.F if dense else keep_count(self.F, *sparsity)
         self.W_gu = torch.cat([W_gate, W_up], 0).contiguous()
+        self.W_guT = torch.empty(self.D, 2 * self.F, dtype=self.dtype, device=dev)
+        ops.transpose(self.W_gu, self.W_guT)
+        self.W_dn = W_down.contiguous()
         self.Wt_dn = torch.empty(self.F, self.D, dtype=self.dtype, device=dev)
-        ops.transpose(W_down.contiguous(), self.Wt_dn)
+        ops.transpose(self.W_dn, self.Wt_dn)
         self.A_gu = torch.cat([A_gate, A_up], 0).contiguous()
-        self.B_gate, self.B_up = B_gate.contiguous(), B_up.contiguous()
+        r = self.r
+        self.B_bd = torch.zeros(2 * self.F, 2 * r, dtype=self.dtype, device=dev)
+        self.B_bd[:self.F, :r] = B_gate
+        self.B_bd[self.F:, r:] = B_up
         self.A_down, self.B_down = A_down.contiguous(), B_down.contiguous()
+        self.A_guT = torch.empty(self.D, 2 * r, dtype=self.dtype, device=dev)
+        self.A_dT = torch.empty(self.F, r, dtype=self.dtype, device=dev)
         self.WA = WA_gu.contiguous()                 # [D, 2k] fp32
         self.WB_gate, self.WB_up = WB_gate.contiguous(), WB_up.contiguous()
         self._T = None
@@ -75,9 +91,12 @@ class SparseFFN:
         self.dgu = e(T, 2 * F, dtype=dt)
         self.dx = e(T, D, dtype=dt)
         f32 = torch.float32
-        self.dA_gate, self.dA_up = e(r, D, dtype=f32), e(r, D, dtype=f32)
+        self.dA_gu = e(2 * r, D, dtype=f32)
+        self.dA_gate, self.dA_up = self.dA_gu[:r], self.dA_gu[r:]
         self.dB_gate, self.dB_up = e(F, r, dtype=f32), e(F, r, dtype=f32)
         self.dA_down, self.dB_down = e(r, F, dtype=f32), e(D, r, dtype=f32)
+        self.gB_gu = e(T, 2 * r, dtype=f32)
+        self.gB_dn = e(T, r, dtype=f32)
         self._T = (T, T_c, T_o)
 
     def forward(self, x, roles, T_c):
@@ -92,32 +111,39 @@ class SparseFFN:
             ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
                              scores=self.scores, off0=0, off1=self.k)
             ops.stack_index(self.idx, F, 2, self.idx2)
-        # gate|up main branch: dense output rows, gathered channels for context rows
-        ops.sparse_linear_fwd("out", x, self.W_gu, self.ctx_rows, self.out_rows, self.idx2, self.gu)
-        # dense LoRA on gate and up
+        # LoRA down-projection of the block input, then the gate|up main branch
+        # (dense output rows, gathered channels for context rows) with the
+        # LoRA term fused into the same accumulators
         ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
+        ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
+                              lora=(self.xl_gu, self.B_bd, 2 * r, self.scale))
         g, u = self.gu[:, :F], self.gu[:, F:]
-        ops.lora_fwd_bwd(ops.LORA_ADD, None, None, self.B_gate, self.scale, self.xl_gu[:, :r], y=g)
-        ops.lora_fwd_bwd(ops.LORA_ADD, None, None, self.B_up, self.scale, self.xl_gu[:, r:], y=u)
         ops.swiglu_fwd(g, u, self.h)
-        # down main branch: input channels = the same selection
-        ops.sparse_linear_fwd("in", self.h, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx, self.y)
-        ops.lora_fwd_bwd(ops.LORA_XL | ops.LORA_ADD, self.h, self.A_down, self.B_down, self.scale,
-                         self.xl_dn, y=self.y)
+        # down main branch: input channels = the same selection; LoRA fused
+        ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
+        ops.sparse_linear_fwd("in", self.h, self.W_dn, self.Wt_dn, self.ctx_rows, self.out_rows,
+                              self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale))
         return self.y
 
     def backward(self, dy):
-        F, r = self.F, self.r
-        ops.sparse_linear_bwd("in", dy, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx, self.dh)
-        ops.lora_fwd_bwd(ops.LORA_BWD, self.h, self.A_down, self.B_down, self.scale, self.xl_dn,
-                         dy=dy, dx=self.dh, dA=self.dA_down, dB=self.dB_down)
+        F, D, r, s = self.F, self.D, self.r, self.scale
+        # down: LoRA gB, dA, dB; then dh with the LoRA input-gradient term fused
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.h, None, self.B_down, s,
+                         self.xl_dn, dy=dy, dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F)
+        ops.transpose(self.A_down, self.A_dT)
+        ops.sparse_linear_bwd("in", dy, None, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx,
+                              self.dh, lora=(self.gB_dn, self.A_dT, r, s))
         g, u = self.gu[:, :F], self.gu[:, F:]
         dg, du = self.dgu[:, :F], self.dgu[:, F:]
         ops.swiglu_bwd(self.dh, g, u, dg, du)
-        ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.ctx_rows, self.out_rows, self.idx2,
-                              self.dx)
-        ops.lora_fwd_bwd(ops.LORA_BWD, self.x, self.A_gu[:r], self.B_gate, self.scale,
-                         self.xl_gu[:, :r], dy=dg, dx=self.dx, dA=self.dA_gate, dB=self.dB_gate)
-        ops.lora_fwd_bwd(ops.LORA_BWD, self.x, self.A_gu[r:], self.B_up, self.scale,
-                         self.xl_gu[:, r:], dy=du, dx=self.dx, dA=self.dA_up, dB=self.dB_up)
+        # gate|up: gB and dA for both through the block-diagonal B, dB per projection
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA, self.x, None, self.B_bd, s, None, dy=self.dgu,
+                         dA=self.dA_gu, gB=self.gB_gu, D_in=D)
+        ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,
+                         dB=self.dB_gate, r=r, D_in=D)
+        ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
+                         dB=self.dB_up, r=r, D_in=D)
+        ops.transpose(self.A_gu, self.A_guT)
+        ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
+                              self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s))
         return self.dx

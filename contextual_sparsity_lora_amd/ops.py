@@ -15,7 +15,8 @@ from . import _lib
 SL_F32, SL_BF16 = 0, 1
 CRIT = {"l2": 0, "swiglu": 1, "qk": 2}
 SIDE = {"out": 0, "in": 1}
-LORA_XL, LORA_ADD, LORA_BWD = 1, 2, 4
+LORA_XL, LORA_ADD, LORA_GB, LORA_DA, LORA_DB, LORA_DX = 1, 2, 4, 8, 16, 32
+LORA_BWD = LORA_GB | LORA_DA | LORA_DB | LORA_DX
 
 _handles = {}
 
@@ -157,47 +158,74 @@ def stack_index(idx, C, copies, idx_out):
     _check(h, st, "sl_stack_index")
 
 
-def sparse_linear_fwd(side, x, W, ctx_rows, out_rows, idx, y, beta=0):
-    """side "out": W [D_out, D_in]; side "in": W is the transposed copy [D_in, D_out]."""
+def _lora_args(lora):
+    """lora = (P fp32 [T, >= r], Bm [C, >= r], r, scale) or None."""
+    if lora is None:
+        return (None, 0, None, 0, 0, 0.0)
+    P, Bm, r, scale = lora
+    return (_ptr(P), _ld(P), _ptr(Bm), _ld(Bm), int(r), float(scale))
+
+
+def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=None):
+    """W: frozen weight [D_out, D_in] (nn.Linear layout); Wt: its transposed
+    copy [D_in, D_out] (read for side "in" only; may be None for side "out").
+    lora = (xl, B, r, scale) fuses y += scale * xl B^T into the same pass."""
     h = handle(_dev(x))
     T, D_in = x.shape
-    D_out = W.shape[0] if side == "out" else W.shape[1]
+    D_out = W.shape[0]
     n = idx.numel() if idx is not None else 0
     st = _lib.load().sl_sparse_linear_fwd(h, SIDE[side], _dt(x), _ptr(x), _ld(x), T, D_in,
-                                          _ptr(W), _ld(W), D_out, _ptr(ctx_rows), ctx_rows.numel(),
-                                          _ptr(out_rows), out_rows.numel(), _ptr(idx), n, _ptr(y),
-                                          _ld(y), int(beta))
+                                          _ptr(W), _ld(W), _ptr(Wt), _ld(Wt) if Wt is not None else 0,
+                                          D_out, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
+                                          out_rows.numel(), _ptr(idx), n, _ptr(y), _ld(y), int(beta),
+                                          *_lora_args(lora))
     _check(h, st, "sl_sparse_linear_fwd")
 
 
-def sparse_linear_bwd(side, dy, W, ctx_rows, out_rows, idx, dx, beta=0):
+def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora=None):
+    """Input gradient of sparse_linear_fwd.  Wt [D_in, D_out] is read by every
+    product; W [D_out, D_in] only for side "out" (may be None for side "in").
+    lora = (gB, A^T, r, scale) fuses dx += scale * gB A into the same pass."""
     h = handle(_dev(dy))
     T, D_out = dy.shape
-    D_in = W.shape[1] if side == "out" else W.shape[0]
+    D_in = Wt.shape[0]
     n = idx.numel() if idx is not None else 0
     st = _lib.load().sl_sparse_linear_bwd(h, SIDE[side], _dt(dy), _ptr(dy), _ld(dy), T, D_out,
-                                          _ptr(W), _ld(W), D_in, _ptr(ctx_rows), ctx_rows.numel(),
-                                          _ptr(out_rows), out_rows.numel(), _ptr(idx), n, _ptr(dx),
-                                          _ld(dx), int(beta))
+                                          _ptr(W), _ld(W) if W is not None else 0, _ptr(Wt), _ld(Wt),
+                                          D_in, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
+                                          out_rows.numel(), _ptr(idx), n, _ptr(dx), _ld(dx),
+                                          int(beta), *_lora_args(lora))
     _check(h, st, "sl_sparse_linear_bwd")
 
 
 def lora_fwd_bwd(mode, x, A, B, scale, xl, y=None, dy=None, dx=None, dA=None, dB=None,
-                 D_out=None):
-    """A: [r, D_in]; B: [D_out, r]; xl: fp32 [T, >= r]."""
-    t = x if x is not None else xl
+                 D_out=None, gB=None, r=None, D_in=None):
+    """A: [r, D_in]; B: [D_out, r]; xl, gB: fp32 [T, >= r].  Sizes are taken from
+    whichever arguments are present unless given."""
+    t = next(v for v in (x, xl, dy, gB) if v is not None)
     h = handle(_dev(t))
-    r = A.shape[0] if A is not None else B.shape[1]
-    T = xl.shape[0]
-    D_in = A.shape[1] if A is not None else (x.shape[1] if x is not None else 1)
+    if r is None:
+        r = next(v for v in (A.shape[0] if A is not None else None,
+                             B.shape[1] if B is not None else None,
+                             dA.shape[0] if dA is not None else None,
+                             dB.shape[1] if dB is not None else None) if v is not None)
+    T = next(v.shape[0] for v in (x, xl, dy, gB, y, dx) if v is not None)
+    if D_in is None:
+        D_in = next((v for v in (A.shape[1] if A is not None else None,
+                                 x.shape[1] if x is not None else None,
+                                 dA.shape[1] if dA is not None else None,
+                                 dx.shape[1] if dx is not None else None) if v is not None), 1)
     if D_out is None:
-        D_out = B.shape[0] if B is not None else 1
-    dt = _dt(x if x is not None else (y if y is not None else dy))
+        D_out = next((v for v in (B.shape[0] if B is not None else None,
+                                  dy.shape[1] if dy is not None else None,
+                                  y.shape[1] if y is not None else None,
+                                  dB.shape[0] if dB is not None else None) if v is not None), 1)
+    dt = _dt(next(v for v in (x, y, dy, dx, A, B) if v is not None))
+    ld = lambda v: _ld(v) if v is not None else 0
     st = _lib.load().sl_lora_fwd_bwd(
-        h, mode, dt, _ptr(x), _ld(x) if x is not None else 0, T, D_in, D_out, _ptr(A), _ptr(B), r,
-        float(scale), _ptr(xl), _ld(xl), _ptr(y), _ld(y) if y is not None else 0, _ptr(dy),
-        _ld(dy) if dy is not None else 0, _ptr(dx), _ld(dx) if dx is not None else 0, _ptr(dA),
-        _ptr(dB))
+        h, mode, dt, _ptr(x), ld(x), T, D_in, D_out, _ptr(A), _ptr(B), r, float(scale), _ptr(xl),
+        ld(xl), _ptr(y), ld(y), _ptr(dy), ld(dy), _ptr(dx), ld(dx), _ptr(dA), _ptr(dB), _ptr(gB),
+        ld(gB))
     _check(h, st, "sl_lora_fwd_bwd")
 
 

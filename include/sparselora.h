@@ -16,10 +16,12 @@
  *    bf16 matrices must start on a 16-byte boundary and have a leading
  *    dimension that is a multiple of 8; fp32 matrices: 16-byte boundary and a
  *    multiple of 4.
- *  - "Channel-major" weights store one selectable channel per row:
- *    output-side projections (gate, up, q, k, v) use the nn.Linear layout
- *    [D_out, D_in]; input-side projections (down, o) use the transposed copy
- *    [D_in, D_out] (made once with sl_transpose).
+ *  - Frozen weights are passed in both layouts: W in the nn.Linear layout
+ *    [D_out, D_in] (y = x W^T) and its transposed copy Wt [D_in, D_out]
+ *    (made once with sl_transpose).  Every main-branch product then reads
+ *    contiguous weight rows: forward products read W, backward products Wt,
+ *    and a selection over input channels (forward) or output channels
+ *    (backward) gathers rows of the other copy into a per-call slice.
  *  - Sizes (T, T_c, T_o, n, ...) are host integers: nothing on the hot path
  *    copies data back to the host or synchronises.
  *  - Work is enqueued on the handle's stream (sl_set_stream) and runs
@@ -70,7 +72,11 @@ typedef enum {
 enum {
     SL_LORA_XL = 1,   /* forward: xl = x A^T                                      */
     SL_LORA_ADD = 2,  /* forward: y += scale * xl B^T (uses xl as given)          */
-    SL_LORA_BWD = 4   /* backward: dA, dB, and dx += scale * (dy B) A             */
+    SL_LORA_GB = 4,   /* backward: gB = dy B                                      */
+    SL_LORA_DA = 8,   /* backward: dA = scale gB^T x                              */
+    SL_LORA_DB = 16,  /* backward: dB = scale dy^T xl                             */
+    SL_LORA_DX = 32,  /* backward: dx += scale gB A                               */
+    SL_LORA_BWD = 60  /* all four backward steps                                  */
 };
 
 /* ---------------------------------------------------------------- handle */
@@ -199,20 +205,31 @@ sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
  *   context rows, side IN:  y[t, :] = sum_{c in idx} x[t, c] Wt[c, :]
  * computed as gathered-channel GEMMs (only the selected weight rows are read
  * for context rows).  beta = 1 adds into y instead of overwriting.
+ * Optional fused dense LoRA term (Algorithm 1 step 6), lora_P != NULL:
+ *   y[t, o] += lora_scale * sum_{j < lora_r} lora_P[t, j] * lora_B[o, j]
+ * on every row and every output channel, accumulated in fp32 before the one
+ * rounding of y; the unselected channels of context rows (side OUT) then hold
+ * this term instead of 0.  lora_P: device fp32 [T, ld_lora_P] (xl = x A^T);
+ * lora_B: device (dt) [D_out, ld_lora_B] (the LoRA B).  1 <= lora_r <= 64.
  *   x   device [T, ldx] (dt), channels of side IN are its columns
- *   W   device channel-major weight (dt): OUT [D_out, ldw >= D_in],
- *       IN [D_in, ldw >= D_out]
+ *   W   device (dt) [D_out, ldw >= D_in], nn.Linear layout
+ *   Wt  device (dt) [D_in, ldwt >= D_out], W transposed; read only for side IN
+ *       (its selected rows form the context-row slice), may be NULL otherwise
  *   ctx_rows/out_rows  device int32 row lists (sl_token_split)
  *   idx device int32[n], ascending, in [0, C), C = D_out (OUT) or D_in (IN)
  *   y   device [T, ldy] (dt) out
  * dt = SL_BF16 (MFMA path) or SL_F32. */
 sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* x, int64_t ldx, int64_t T, int64_t D_in,
-                               const void* W, int64_t ldw, int64_t D_out,
+                               const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
+                               int64_t D_out,
                                const int32_t* ctx_rows, int64_t T_c,
                                const int32_t* out_rows, int64_t T_o,
                                const int32_t* idx, int64_t n,
-                               void* y, int64_t ldy, int beta);
+                               void* y, int64_t ldy, int beta,
+                               const float* lora_P, int64_t ld_lora_P,
+                               const void* lora_B, int64_t ld_lora_B,
+                               int64_t lora_r, float lora_scale);
 
 /* ---------------------------------------------------------------- a10/a11: main backward */
 
@@ -222,33 +239,50 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
  *   output rows:  dx[t, :] = dy[t, :] W                        (dense)
  *   context rows, side OUT: dx[t, :] = sum_{c in idx} dy[t, c] W[c, :]
  *   context rows, side IN:  dx[t, c] = dy[t, :] . Wt[c, :] for c in idx, 0 else
- *   dy  device [T, lddy] (dt), W as in the forward (same buffer),
- *   dx  device [T, lddx] (dt) out; beta = 1 accumulates. */
+ *   dy  device [T, lddy] (dt); Wt device (dt) [D_in, ldwt >= D_out] (read by
+ *       every backward product); W device (dt) [D_out, ldw >= D_in], read only
+ *       for side OUT (its selected rows form the context-row slice)
+ *   dx  device [T, lddx] (dt) out; beta = 1 accumulates.
+ * Optional fused LoRA input-gradient term, lora_P != NULL:
+ *   dx[t, i] += lora_scale * sum_j lora_P[t, j] * lora_B[i, j]
+ * with lora_P = gB = dy B (fp32 [T, ld], from sl_lora_fwd_bwd) and
+ * lora_B = A^T (dt [D_in, ld]); unselected context channels (side IN) then
+ * hold this term instead of 0. */
 sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* dy, int64_t lddy, int64_t T, int64_t D_out,
-                               const void* W, int64_t ldw, int64_t D_in,
+                               const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
+                               int64_t D_in,
                                const int32_t* ctx_rows, int64_t T_c,
                                const int32_t* out_rows, int64_t T_o,
                                const int32_t* idx, int64_t n,
-                               void* dx, int64_t lddx, int beta);
+                               void* dx, int64_t lddx, int beta,
+                               const float* lora_P, int64_t ld_lora_P,
+                               const void* lora_B, int64_t ld_lora_B,
+                               int64_t lora_r, float lora_scale);
 
 /* ---------------------------------------------------------------- a8/a12: dense LoRA */
 
 /* Dense LoRA branch on every token and channel (PG §3.4 Algorithm 1 step 6:
  * y_final = y_sparse + B A x; §3.2: LoRA gradients are always computed fully).
- * A [r, D_in], B [D_out, r] (dt), scale = alpha / r.
- *   mode & SL_LORA_XL:  xl = x A^T                 (xl fp32 [T, ldxl], out)
- *   mode & SL_LORA_ADD: y += scale * xl B^T         (y dt [T, ldy], in/out)
- *   mode & SL_LORA_BWD: gB = dy B;  dA = scale gB^T x  (fp32 [r, D_in], out);
- *                       dB = scale dy^T xl             (fp32 [D_out, r], out);
- *                       dx += scale gB A if dx != NULL (dt [T, lddx])
- * Pointers not used by the mode may be NULL.  1 <= r <= 64. */
+ * A [r, D_in], B [D_out, r] (dt, contiguous), scale = alpha / r.
+ *   SL_LORA_XL:  xl = x A^T                       (xl fp32 [T, ldxl], out)
+ *   SL_LORA_ADD: y += scale * xl B^T               (y dt [T, ldy], in/out)
+ *   SL_LORA_GB:  gB = dy B                         (gB fp32 [T, ldgB] out; if gB
+ *                                                   is NULL it stays internal)
+ *   SL_LORA_DA:  dA = scale gB^T x                 (fp32 [r, D_in] out; gB from
+ *                                                   this call or given)
+ *   SL_LORA_DB:  dB = scale dy^T xl                (fp32 [D_out, r] out)
+ *   SL_LORA_DX:  dx += scale gB A                  (dt [T, lddx]); leave it out
+ *                and pass gB to sl_sparse_linear_bwd to fuse that term there
+ * Modes combine; the steps run in the order listed.  Pointers not used by the
+ * mode may be NULL.  1 <= r <= 64.  dA / dB are deterministic (fixed-order
+ * token reduction). */
 sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt,
                           const void* x, int64_t ldx, int64_t T, int64_t D_in, int64_t D_out,
                           const void* A, const void* B, int64_t r, float scale,
                           float* xl, int64_t ldxl, void* y, int64_t ldy,
                           const void* dy, int64_t lddy, void* dx, int64_t lddx,
-                          float* dA, float* dB);
+                          float* dA, float* dB, float* gB, int64_t ldgB);
 
 /* ---------------------------------------------------------------- support (glue) */
 

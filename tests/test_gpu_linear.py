@@ -53,25 +53,27 @@ def test_sparse_linear_fwd_bwd(case, rng):
     # output side: channels = output features
     idx = np.sort(rng.choice(Dout, min(keep, Dout), replace=False)).astype(np.int32)
     y = empty_pad(T, Dout, dtype)
-    ops.sparse_linear_fwd("out", dev_pad(x, dtype), dev_pad(W, dtype), c_d, o_d, to_dev(idx, None), y)
+    Wd, Wtd = dev_pad(W, dtype), dev_pad(np.ascontiguousarray(W.T), dtype)
+    ops.sparse_linear_fwd("out", dev_pad(x, dtype), Wd, None, c_d, o_d, to_dev(idx, None), y)
     yr = ref.sparse_linear_fwd("out", x, W, roles, idx)
     assert mar(host(y), yr) <= tol
     drop = np.setdiff1d(np.arange(Dout), idx)
     assert np.all(host(y)[np.ix_(ctx, drop)] == 0.0)
     dx = empty_pad(T, Din, dtype)
-    ops.sparse_linear_bwd("out", dev_pad(dy, dtype), dev_pad(W, dtype), c_d, o_d, to_dev(idx, None), dx)
+    ops.sparse_linear_bwd("out", dev_pad(dy, dtype), Wd, Wtd, c_d, o_d, to_dev(idx, None), dx)
     assert mar(host(dx), ref.sparse_linear_bwd("out", dy, W, roles, idx)) <= tol
-    # input side: the weight is passed as its transposed copy [D_in, D_out]
+    # input side: W in nn.Linear layout and its transposed copy
     Wi = round_dtype(rng.standard_normal((Din, Dout)) * 0.05, dtype)    # nn.Linear [out=Din, in=Dout]
     Wt = np.ascontiguousarray(Wi.T)
+    Wid, Witd = dev_pad(Wi, dtype), dev_pad(Wt, dtype)
     idx_in = np.sort(rng.choice(Dout, min(keep, Dout), replace=False)).astype(np.int32)
     xi = round_dtype(rng.standard_normal((T, Dout)), dtype)
     yi = empty_pad(T, Din, dtype)
-    ops.sparse_linear_fwd("in", dev_pad(xi, dtype), dev_pad(Wt, dtype), c_d, o_d, to_dev(idx_in, None), yi)
+    ops.sparse_linear_fwd("in", dev_pad(xi, dtype), Wid, Witd, c_d, o_d, to_dev(idx_in, None), yi)
     assert mar(host(yi), ref.sparse_linear_fwd("in", xi, Wi, roles, idx_in)) <= tol
     dyi = round_dtype(rng.standard_normal((T, Din)), dtype)
     dxi = empty_pad(T, Dout, dtype)
-    ops.sparse_linear_bwd("in", dev_pad(dyi, dtype), dev_pad(Wt, dtype), c_d, o_d, to_dev(idx_in, None), dxi)
+    ops.sparse_linear_bwd("in", dev_pad(dyi, dtype), None, Witd, c_d, o_d, to_dev(idx_in, None), dxi)
     dxr = ref.sparse_linear_bwd("in", dyi, Wi, roles, idx_in)
     assert mar(host(dxi), dxr) <= tol
     assert np.all(host(dxi)[np.ix_(ctx, np.setdiff1d(np.arange(Dout), idx_in))] == 0.0)
@@ -88,7 +90,7 @@ def test_output_rows_invariant_and_full_keep_is_dense(rng):
     ys = []
     for idx in (np.arange(0, Dout, 3), np.arange(5), np.arange(Dout)):
         y = torch.empty(T, Dout, dtype=torch.bfloat16, device=DEV)
-        ops.sparse_linear_fwd("out", x, W, c_d, o_d, to_dev(idx.astype(np.int32), None), y)
+        ops.sparse_linear_fwd("out", x, W, None, c_d, o_d, to_dev(idx.astype(np.int32), None), y)
         ys.append(host(y))
     for y in ys[1:]:
         assert np.array_equal(y[out], ys[0][out])          # bitwise: output rows never see idx
@@ -106,7 +108,8 @@ def test_beta_accumulates(rng):
     y0 = round_dtype(rng.standard_normal((T, Dout)), "bf16")
     idx = np.sort(rng.choice(Dout, 77, replace=False)).astype(np.int32)
     y = to_dev(y0, "bf16")
-    ops.sparse_linear_fwd("out", to_dev(x, "bf16"), to_dev(W, "bf16"), c_d, o_d, to_dev(idx, None), y, beta=1)
+    ops.sparse_linear_fwd("out", to_dev(x, "bf16"), to_dev(W, "bf16"), None, c_d, o_d, to_dev(idx, None), y,
+                          beta=1)
     assert mar(host(y), y0 + ref.sparse_linear_fwd("out", x, W, roles, idx)) <= TOL["bf16"]
 
 
@@ -141,3 +144,49 @@ def test_lora_fwd_bwd(dtype, T, Din, Dout, r, rng):
     assert mar(host(dA), dA_r) <= 1e-4
     assert mar(host(dB), dB_r) <= 1e-4
     assert mar(host(dx), dx0 + dx_r) <= tol
+
+
+@pytest.mark.parametrize("dtype,r", [("f32", 8), ("bf16", 16), ("bf16", 32)])
+def test_fused_lora_term(dtype, r, rng):
+    """The LoRA term fused into the main-branch product equals main + s xl B^T,
+    and unselected context channels carry the LoRA term alone."""
+    ops = _ops()
+    roles = _roles(2, 300, 70)
+    T, Din, Dout = 600, 520, 1000
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    tol = TOL[dtype]
+    s = 2.0
+    x = round_dtype(rng.standard_normal((T, Din)), dtype)
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, dtype)
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, dtype)
+    idx = np.sort(rng.choice(Dout, 333, replace=False)).astype(np.int32)
+    y = empty_pad(T, Dout, dtype)
+    Wd, Wtd = dev_pad(W, dtype), dev_pad(np.ascontiguousarray(W.T), dtype)
+    ops.sparse_linear_fwd("out", dev_pad(x, dtype), Wd, None, c_d, o_d, to_dev(idx, None), y,
+                          lora=(to_dev(P, "f32"), dev_pad(Bm, dtype), r, s))
+    lora = s * (P.astype(np.float64) @ Bm.T.astype(np.float64))
+    assert mar(host(y), ref.sparse_linear_fwd("out", x, W, roles, idx) + lora) <= tol
+    drop = np.setdiff1d(np.arange(Dout), idx)
+    assert mar(host(y)[np.ix_(ctx, drop)], lora[np.ix_(ctx, drop)]) <= tol
+    # input side (K-gathered) with the LoRA term, and the backward forms
+    Wi = round_dtype(rng.standard_normal((Din, Dout)) * 0.05, dtype)
+    xi = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    Bi = round_dtype(rng.standard_normal((Din, r)) * 0.3, dtype)
+    yi = empty_pad(T, Din, dtype)
+    Wid, Witd = dev_pad(Wi, dtype), dev_pad(np.ascontiguousarray(Wi.T), dtype)
+    ops.sparse_linear_fwd("in", dev_pad(xi, dtype), Wid, Witd, c_d, o_d,
+                          to_dev(idx, None), yi, lora=(to_dev(P, "f32"), dev_pad(Bi, dtype), r, s))
+    lora_i = s * (P.astype(np.float64) @ Bi.T.astype(np.float64))
+    assert mar(host(yi), ref.sparse_linear_fwd("in", xi, Wi, roles, idx) + lora_i) <= tol
+    dy = round_dtype(rng.standard_normal((T, Din)), dtype)
+    dx = empty_pad(T, Dout, dtype)
+    ops.sparse_linear_bwd("in", dev_pad(dy, dtype), None, Witd, c_d, o_d,
+                          to_dev(idx, None), dx, lora=(to_dev(P, "f32"), dev_pad(Bm, dtype), r, s))
+    assert mar(host(dx), ref.sparse_linear_bwd("in", dy, Wi, roles, idx) + lora) <= tol
+    assert mar(host(dx)[np.ix_(ctx, drop)], lora[np.ix_(ctx, drop)]) <= tol
+    dy2 = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    dx2 = empty_pad(T, Din, dtype)
+    ops.sparse_linear_bwd("out", dev_pad(dy2, dtype), Wd, Wtd, c_d, o_d, to_dev(idx, None), dx2,
+                          lora=(to_dev(P, "f32"), dev_pad(Bi, dtype), r, s))
+    assert mar(host(dx2), ref.sparse_linear_bwd("out", dy2, W, roles, idx) + lora_i) <= tol
