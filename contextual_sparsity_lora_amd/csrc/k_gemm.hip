@@ -249,18 +249,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs args
             const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
             bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
         }
-        for (int kk = 0; kk < P.lr; kk += 2) {
-            const int k = kk + (lane >> 5);
-            float a[FM], b[FN];
+        constexpr int KC = 8;   // k-steps whose operands are loaded before use
+        for (int kk0 = 0; kk0 < P.lr; kk0 += 2 * KC) {
+            float a[KC][FM], b[KC][FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
+            for (int q = 0; q < KC; ++q) {
+                const int k = kk0 + 2 * q + (lane >> 5);
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
+                for (int i = 0; i < FM; ++i) a[q][i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
+                for (int j = 0; j < FN; ++j) b[q][j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
+            }
 #pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int q = 0; q < KC; ++q)
+                if (kk0 + 2 * q < P.lr)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q][i], b[q][j], acc[i][j], 0, 0, 0);
         }
     }
 
@@ -411,6 +418,80 @@ hipError_t launch_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- rank-r only
+// Z[c_rows[m], c_cols[n]] (+)= lscale * sum_j lP[c_rows[m], j] lB[c_cols[n], j]
+// for the channels the main product does not produce (the unselected channels
+// of context rows).  128 x 128 tile, 4 waves of 64 x 64; the tile's rows of lP
+// and lB are staged in LDS (fp32), then v_mfma_f32_32x32x2_f32.
+constexpr int LF = 128;
+
+__global__ __launch_bounds__(256) void lora_fill_kernel(GemmProblem P) {
+    __shared__ float Ps[LF][65];
+    __shared__ float Bs[LF][65];
+    const int tiles_m = (int)((P.M + LF - 1) / LF);
+    const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * LF;
+    const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * LF;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid & 1, wn = wid >> 1;
+    const int lr = P.lr;
+    const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
+    for (int q = tid; q < LF * lr; q += 256) {
+        const int rr = q / lr, j = q % lr;
+        const int64_t m = m0 + rr, n = n0 + rr;
+        float pv = 0.0f, bv = 0.0f;
+        if (m < P.M) {
+            const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+            pv = P.lscale * P.lP[cm * P.ldlP + j];
+        }
+        if (n < P.N) {
+            const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
+            bv = bf16_to_f32(lB[cn * P.ldlB + j]);
+        }
+        Ps[rr][j] = pv;
+        Bs[rr][j] = bv;
+    }
+    __syncthreads();
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    for (int kk = 0; kk < lr; kk += 2) {
+        const int k = kk + (lane >> 5);
+        float a[2], b[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) a[i] = k < lr ? Ps[wm * 64 + i * 32 + (lane & 31)][k] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) b[j] = k < lr ? Bs[wn * 64 + j * 32 + (lane & 31)][k] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    bf16_t* __restrict__ Cg = (bf16_t*)P.C;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (n >= P.N) continue;
+        const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m >= P.M) continue;
+                const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+                bf16_t* dst = Cg + cm * P.ldc + cn;
+                float v = acc[i][j][e];
+                if (P.beta) v += bf16_to_f32(*dst);
+                *dst = f32_to_bf16(v);
+            }
+    }
+}
+
 template <typename T>
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int64_t S, int64_t M,
                                      int64_t N, T* __restrict__ Z, int64_t ldz,
@@ -475,5 +556,13 @@ hipError_t launch_splitk_reduce(bool bf16, const float* part, int64_t S, int64_t
     else
         hipLaunchKernelGGL(splitk_reduce_kernel<float>, grid, dim3(256), 0, st, part, S, M, N,
                            (float*)Z, ldz, c_rows, c_cols, beta);
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_fill_bf16(const GemmProblem* p, hipStream_t st) {
+    if (p->M <= 0 || p->N <= 0) return hipSuccess;
+    if (p->lr > 64 || p->lr < 1) return hipErrorInvalidValue;
+    const int64_t tiles = ceil_div(p->M, LF) * ceil_div(p->N, LF);
+    hipLaunchKernelGGL(lora_fill_kernel, dim3((unsigned)tiles), dim3(256), 0, st, *p);
     return hipGetLastError();
 }

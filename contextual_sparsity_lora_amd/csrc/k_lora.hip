@@ -46,36 +46,39 @@ __global__ __launch_bounds__(256) void lora_xl_bf16_kernel(const bf16_t* __restr
     const int64_t row = t0 + (lane & 15);
     const bool rv = row < T;
     const int ko = (lane >> 4) * 8;
-    for (int64_t k0 = kbeg; k0 < kend; k0 += 32) {
-        const int64_t k = k0 + ko;
-        uint4 av = {0u, 0u, 0u, 0u};
-        if (rv) {
-            if (k + 8 <= kend) av = *(const uint4*)(x + row * ldx + k);
-            else {
-                uint32_t w[4] = {0u, 0u, 0u, 0u};
-                for (int e = 0; e < 8; ++e)
-                    if (k + e < kend) w[e >> 1] |= (uint32_t)x[row * ldx + k + e] << ((e & 1) * 16);
-                av = {w[0], w[1], w[2], w[3]};
-            }
-        }
-        bf16x8 a = *(bf16x8*)&av;
+    auto loadv = [&](const bf16_t* base, int64_t k) -> uint4 {
+        if (k + 8 <= kend) return *(const uint4*)(base + k);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e)
+            if (k + e < kend) w[e >> 1] |= (uint32_t)base[k + e] << ((e & 1) * 16);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+    const bf16_t* xrow = x + (rv ? row : 0) * ldx;
+    const bf16_t* arow[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (b < nb) {
-                const int64_t j = b * 16 + (lane & 15);
-                uint4 bv = {0u, 0u, 0u, 0u};
-                if (j < r) {
-                    if (k + 8 <= kend) bv = *(const uint4*)(A + j * lda + k);
-                    else {
-                        uint32_t w[4] = {0u, 0u, 0u, 0u};
-                        for (int e = 0; e < 8; ++e)
-                            if (k + e < kend) w[e >> 1] |= (uint32_t)A[j * lda + k + e] << ((e & 1) * 16);
-                        bv = {w[0], w[1], w[2], w[3]};
-                    }
-                }
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, *(bf16x8*)&bv, acc[b], 0, 0, 0);
-            }
+    for (int b = 0; b < 4; ++b) {
+        const int64_t j = b * 16 + (lane & 15);
+        arow[b] = (b < nb && j < r) ? A + j * lda : nullptr;
+    }
+    constexpr int U = 4;   // K steps in flight
+    for (int64_t k0 = kbeg; k0 < kend; k0 += 32 * U) {
+        uint4 av[U], bv[U][4];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + 32 * u + ko;
+            const bool kin = k < kend;
+            av[u] = (rv && kin) ? loadv(xrow, k) : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                bv[u][b] = (arow[b] && kin) ? loadv(arow[b], k) : make_uint4(0u, 0u, 0u, 0u);
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (b < nb)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(bf16x8*)&av[u], *(bf16x8*)&bv[u][b],
+                                                                     acc[b], 0, 0, 0);
     }
     // lane holds C[4*(lane/16) + e][lane % 16]
 #pragma unroll
@@ -158,51 +161,58 @@ __global__ __launch_bounds__(256) void lora_add_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------- out = s P^T Q
-// Wave = 64*CPL columns x one chunk of TCH tokens; the row of P is
-// wave-uniform (scalar loads).  Partial sums per chunk go to ws[chunk][j][c];
-// an ordered reduction over chunks follows (deterministic).
+// Block = 256 columns (one per thread) x one chunk of TCH tokens.  The chunk of
+// P is staged in LDS once and read back as wave-wide broadcasts; Q is read
+// once, 8 tokens in flight per thread.  Partial sums per chunk go to
+// ws[chunk][j][c]; an ordered reduction over chunks follows (deterministic).
 constexpr int TCH = 256;
 
-template <typename T, int R, int CPL>
+template <typename T, int R>
 __global__ __launch_bounds__(256) void outer_partial_kernel(const float* __restrict__ P,
                                                             int64_t ldp, int64_t Tn, int64_t r,
                                                             const T* __restrict__ Q, int64_t ldq,
                                                             int64_t Nc, float* __restrict__ ws) {
-    const int lane = threadIdx.x & 63;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t chunk = (int64_t)blockIdx.y * 4 + w;
+    __shared__ __attribute__((aligned(16))) float Ps[TCH][R];
+    const int64_t chunk = blockIdx.y;
     const int64_t t0 = chunk * TCH;
-    if (t0 >= Tn) return;
-    const int64_t t1 = (t0 + TCH < Tn) ? t0 + TCH : Tn;
-    const int64_t c0 = (int64_t)blockIdx.x * (64 * CPL) + lane * CPL;
-    const bool full = c0 + CPL <= Nc;
-    float acc[CPL][R];
+    const int64_t tn = (Tn - t0) < TCH ? (Tn - t0) : TCH;
+    for (int q = threadIdx.x; q < TCH * R; q += 256) {
+        const int tt = q / R, j = q % R;
+        Ps[tt][j] = (tt < tn && j < r) ? P[(t0 + tt) * ldp + j] : 0.0f;
+    }
+    __syncthreads();
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= Nc) return;
+    float acc[R];
 #pragma unroll
-    for (int q = 0; q < CPL; ++q)
+    for (int j = 0; j < R; ++j) acc[j] = 0.0f;
+    const T* qc = Q + t0 * ldq + c;
+    int tt = 0;
+    for (; tt + 8 <= tn; tt += 8) {
+        float qv[8];
 #pragma unroll
-        for (int j = 0; j < R; ++j) acc[q][j] = 0.0f;
-    for (int64_t t = t0; t < t1; ++t) {
-        const float* __restrict__ prow = P + t * ldp;
-        float pj[R];
+        for (int u = 0; u < 8; ++u) qv[u] = ld<T>(qc, (int64_t)(tt + u) * ldq);
 #pragma unroll
-        for (int j = 0; j < R; ++j) pj[j] = (j < r) ? prow[j] : 0.0f;
-        const T* qr = Q + t * ldq + c0;
-        float qv[CPL];
+        for (int u = 0; u < 8; ++u) {
+            const float4* pr = (const float4*)&Ps[tt + u][0];
 #pragma unroll
-        for (int q = 0; q < CPL; ++q) qv[q] = (full || c0 + q < Nc) ? ld<T>(qr, q) : 0.0f;
+            for (int j4 = 0; j4 < R / 4; ++j4) {
+                const float4 p4 = pr[j4];
+                acc[4 * j4 + 0] += p4.x * qv[u];
+                acc[4 * j4 + 1] += p4.y * qv[u];
+                acc[4 * j4 + 2] += p4.z * qv[u];
+                acc[4 * j4 + 3] += p4.w * qv[u];
+            }
+        }
+    }
+    for (; tt < tn; ++tt) {
+        const float qv = ld<T>(qc, (int64_t)tt * ldq);
 #pragma unroll
-        for (int q = 0; q < CPL; ++q)
-#pragma unroll
-            for (int j = 0; j < R; ++j) acc[q][j] += pj[j] * qv[q];
+        for (int j = 0; j < R; ++j) acc[j] += Ps[tt][j] * qv;
     }
 #pragma unroll
-    for (int q = 0; q < CPL; ++q) {
-        const int64_t c = c0 + q;
-        if (c >= Nc) continue;
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            if (j < r) ws[(chunk * r + j) * Nc + c] = acc[q][j];
-    }
+    for (int j = 0; j < R; ++j)
+        if (j < r) ws[(chunk * r + j) * Nc + c] = acc[j];
 }
 
 __global__ void outer_reduce_kernel(const float* __restrict__ ws, int64_t nch, int64_t r,
@@ -457,20 +467,20 @@ hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T,
     const int64_t nch = T > 0 ? ceil_div(T, TCH) : 0;
     if ((size_t)(nch * r * Ncols) > ws_floats) return hipErrorInvalidValue;
     if (T > 0) {
-#define OUTER(TT, RR, CP)                                                                       \
-    hipLaunchKernelGGL((outer_partial_kernel<TT, RR, CP>),                                      \
-                       dim3((unsigned)ceil_div(Ncols, 64 * CP), (unsigned)ceil_div(nch, 4)),     \
-                       dim3(256), 0, st, P, ldp, T, r, (const TT*)Q, ldq, Ncols, ws)
+        const dim3 grid((unsigned)ceil_div(Ncols, 256), (unsigned)nch);
+#define OUTER(TT, RR)                                                                          \
+    hipLaunchKernelGGL((outer_partial_kernel<TT, RR>), grid, dim3(256), 0, st, P, ldp, T, r,   \
+                       (const TT*)Q, ldq, Ncols, ws)
         if (bf16) {
-            if (r <= 8) OUTER(bf16_t, 8, 4);
-            else if (r <= 16) OUTER(bf16_t, 16, 4);
-            else if (r <= 32) OUTER(bf16_t, 32, 4);
-            else OUTER(bf16_t, 64, 2);
+            if (r <= 8) OUTER(bf16_t, 8);
+            else if (r <= 16) OUTER(bf16_t, 16);
+            else if (r <= 32) OUTER(bf16_t, 32);
+            else OUTER(bf16_t, 64);
         } else {
-            if (r <= 8) OUTER(float, 8, 4);
-            else if (r <= 16) OUTER(float, 16, 4);
-            else if (r <= 32) OUTER(float, 32, 4);
-            else OUTER(float, 64, 2);
+            if (r <= 8) OUTER(float, 8);
+            else if (r <= 16) OUTER(float, 16);
+            else if (r <= 32) OUTER(float, 32);
+            else OUTER(float, 64);
         }
 #undef OUTER
     }

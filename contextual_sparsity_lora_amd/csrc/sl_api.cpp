@@ -491,7 +491,7 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
                                  T_c, C - n, 0, beta, l);
         {
             Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C - n) * esize(dt));
-            SL_HIP(h, dt == SL_BF16 ? launch_gemm_bf16(false, &pc, 1, h->stream)
+            SL_HIP(h, dt == SL_BF16 ? launch_lora_fill_bf16(&pc, h->stream)
                                     : launch_gemm_f32(false, &pc, 1, h->stream), "lora_fill");
         }
     } else if (!beta) {

@@ -60,6 +60,8 @@ struct GemmProblem {
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
+// rank-r term only (K = 0 problem), bf16 output
+hipError_t launch_lora_fill_bf16(const GemmProblem* p, hipStream_t st);
 // fp32 version (VALU), same semantics.
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 
