@@ -75,6 +75,93 @@ __device__ __forceinline__ uint4 load16_guard(const bf16_t* rowp, int64_t k, int
     return v;
 }
 
+// Epilogue shared by the bf16 kernels: optional rank-r term into the fp32
+// accumulators, then one rounding and the store through the row / column maps
+// (or raw fp32 partials).  Lane holds column (lane & 31) and rows
+// 8*(e/4) + 4*(lane/32) + e%4 of each 32 x 32 block.
+template <int FM, int FN, int WTM, int WTN>
+__device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    const int64_t M = P.M, N = P.N;
+    // rank-r term: A operand lP[cm, k], B operand lB[cn, k] (k = kk + lane/32)
+    if (P.lr > 0) {
+        const float* __restrict__ lP = P.lP;
+        const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
+        const float* prow[FM];
+        const bf16_t* bcol[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const int32_t* lmap = P.l_rows ? P.l_rows : P.c_rows;
+            const int64_t cm = m < M ? (lmap ? (int64_t)lmap[m] : m) : -1;
+            prow[i] = cm >= 0 ? lP + cm * P.ldlP : nullptr;
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+            const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
+            bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
+        }
+        constexpr int KC = FM * FN >= 16 ? 4 : 8;   // k-steps whose operands are loaded before use
+        for (int kk0 = 0; kk0 < P.lr; kk0 += 2 * KC) {
+            float a[KC][FM], b[KC][FN];
+#pragma unroll
+            for (int q = 0; q < KC; ++q) {
+                const int k = kk0 + 2 * q + (lane >> 5);
+#pragma unroll
+                for (int i = 0; i < FM; ++i) a[q][i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < FN; ++j) b[q][j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
+            }
+#pragma unroll
+            for (int q = 0; q < KC; ++q)
+                if (kk0 + 2 * q < P.lr)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q][i], b[q][j], acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
+    if (P.f32out) {   // split-K partial: raw fp32, unmapped
+        float* __restrict__ Cf = (float*)P.C;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    if (m < M) Cf[m * P.ldc + n] = acc[i][j][e];
+                }
+        }
+        return;
+    }
+    bf16_t* __restrict__ Cg = (bf16_t*)P.C;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+        const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
+        if (n >= N) continue;
+        const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m >= M) continue;
+                const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+                bf16_t* dst = Cg + cm * P.ldc + cn;
+                float v = acc[i][j][e];
+                if (P.beta) v += bf16_to_f32(*dst);
+                *dst = f32_to_bf16(v);
+            }
+    }
+}
+
 template <int BM, int BN, int WGM, int WGN, bool NN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs args) {
     constexpr int NTH = 64 * WGM * WGN;
@@ -230,83 +317,151 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_bf16_kernel(GemmArgs args
         __syncthreads();
     }
 
-    // rank-r term: A operand lP[cm, k], B operand lB[cn, k] (k = kk + lane/32)
-    if (P.lr > 0) {
-        const float* __restrict__ lP = P.lP;
-        const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
-        const float* prow[FM];
-        const bf16_t* bcol[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-            const int64_t m = m0 + wm * WTM + i * 32 + (lane & 31);
-            const int32_t* lmap = P.l_rows ? P.l_rows : P.c_rows;
-            const int64_t cm = m < M ? (lmap ? (int64_t)lmap[m] : m) : -1;
-            prow[i] = cm >= 0 ? lP + cm * P.ldlP : nullptr;
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
-            const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
-            bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
-        }
-        constexpr int KC = 8;   // k-steps whose operands are loaded before use
-        for (int kk0 = 0; kk0 < P.lr; kk0 += 2 * KC) {
-            float a[KC][FM], b[KC][FN];
-#pragma unroll
-            for (int q = 0; q < KC; ++q) {
-                const int k = kk0 + 2 * q + (lane >> 5);
-#pragma unroll
-                for (int i = 0; i < FM; ++i) a[q][i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
-#pragma unroll
-                for (int j = 0; j < FN; ++j) b[q][j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
-            }
-#pragma unroll
-            for (int q = 0; q < KC; ++q)
-                if (kk0 + 2 * q < P.lr)
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q][i], b[q][j], acc[i][j], 0, 0, 0);
-        }
-    }
+    gemm_epilogue<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+}
 
-    // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
-    if (P.f32out) {   // split-K partial: raw fp32, unmapped
-        float* __restrict__ Cf = (float*)P.C;
+// ---------------------------------------------------------------- NT main loop v3
+// NT only, K a multiple of 8 (operands zero-padded to it).  Loads are raw
+// buffer loads: a 32-bit per-lane byte offset (row base + k sub-offset, fixed
+// for the whole tile) plus the K-tile offset in a scalar register, so the loop
+// spends no vector instructions on addresses; rows past M / N and chunks past
+// K use an out-of-range offset and read zeros.  Two register sets keep the
+// loads of tiles kt+1 and kt+2 in flight while tile kt is multiplied out of
+// LDS; the block barrier is a bare s_barrier (this wave's LDS writes are
+// waited for, its outstanding global loads are not).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t OOB_OFF = 0x80000000u;   // >= num_records: the load returns zeros
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7fffffff, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    __builtin_amdgcn_s_barrier();
+}
+
+template <int BM, int BN, int WGM, int WGN, int NSET>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) {
+    constexpr int NTH = 64 * WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int ACH = BM * 8 / NTH, BCH = BN * 8 / NTH;
+    static_assert(ACH >= 1 && BCH >= 1 && (NTH % 8) == 0, "tile too small for the block");
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    bf16_t* As = smem;
+    bf16_t* Bs = smem + 2 * BM * LDK;
+
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, L, P, t, tiles_m);
+    const int64_t m0 = (int64_t)(t % tiles_m) * BM;
+    const int64_t n0 = (int64_t)(t / tiles_m) * BN;
+    const int64_t M = P.M, N = P.N, K = P.K;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid % WGM, wn = wid / WGM;
+    const int kc8 = (tid & 7) * 8;          // every chunk of this thread has the same k sub-offset
+
+    uint32_t aoff[ACH], boff[BCH];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-            const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
-            if (n >= N) continue;
+    for (int c = 0; c < ACH; ++c) {
+        const int64_t m = m0 + ((tid + NTH * c) >> 3);
+        aoff[c] = m < M ? (uint32_t)(((P.a_rows ? (int64_t)P.a_rows[m] : m) * P.lda + kc8) * 2) : OOB_OFF;
+    }
+#pragma unroll
+    for (int c = 0; c < BCH; ++c) {
+        const int64_t n = n0 + ((tid + NTH * c) >> 3);
+        boff[c] = n < N ? (uint32_t)(((P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb + kc8) * 2) : OOB_OFF;
+    }
+    const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
+    const int64_t nk = (K + BK - 1) / BK;
+
+    auto load = [&](uint4 (&sa)[ACH], uint4 (&sb)[BCH], int64_t kt) {
+        const uint32_t soff = (uint32_t)(kt * BK * 2);
+        const bool kin = kt * BK + kc8 < K;   // whole 8-element chunk inside K (K % 8 == 0)
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) sa[c] = bload16(ra, kin ? aoff[c] : OOB_OFF, soff);
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) sb[c] = bload16(rb, kin ? boff[c] : OOB_OFF, soff);
+    };
+    auto store = [&](int buf, const uint4 (&sa)[ACH], const uint4 (&sb)[BCH]) {
+        bf16_t* as = As + buf * BM * LDK;
+        bf16_t* bs = Bs + buf * BN * LDK;
+#pragma unroll
+        for (int c = 0; c < ACH; ++c) *(uint4*)&as[((tid + NTH * c) >> 3) * LDK + kc8] = sa[c];
+#pragma unroll
+        for (int c = 0; c < BCH; ++c) *(uint4*)&bs[((tid + NTH * c) >> 3) * LDK + kc8] = sb[c];
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto compute = [&](int buf) {
+        const bf16_t* as = As + buf * BM * LDK;
+        const bf16_t* bs = Bs + buf * BN * LDK;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            bf16x8 a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                a[i] = *(const bf16x8*)&as[(wm * WTM + i * 32 + (lane & 31)) * LDK + ks * 16 + (lane >> 5) * 8];
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+                b[j] = *(const bf16x8*)&bs[(wn * WTN + j * 32 + (lane & 31)) * LDK + ks * 16 + (lane >> 5) * 8];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                    if (m < M) Cf[m * P.ldc + n] = acc[i][j][e];
-                }
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        return;
+    };
+
+    if (NSET == 1 && nk > 0) {
+        // one register set: tile kt+1 is in flight while tile kt is multiplied
+        uint4 sa[ACH], sb[BCH];
+        const int64_t last = nk - 1;
+        load(sa, sb, 0);
+        store(0, sa, sb);
+        lds_barrier();
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            const int buf = (int)(kt & 1);
+            load(sa, sb, kt + 1 <= last ? kt + 1 : last);
+            compute(buf);
+            if (kt + 1 <= last) store(buf ^ 1, sa, sb);
+            lds_barrier();
+        }
+    } else if (NSET == 2 && nk > 0) {
+        uint4 sa0[ACH], sb0[BCH], sa1[ACH], sb1[BCH];
+        const int64_t last = nk - 1;
+        load(sa0, sb0, 0);
+        load(sa1, sb1, nk > 1 ? 1 : last);
+        store(0, sa0, sb0);
+        lds_barrier();
+        for (int64_t kt = 0; kt < nk; kt += 2) {
+            // even step: tile kt in LDS 0; tile kt+1 in set 1; fetch tile kt+2 into set 0
+            load(sa0, sb0, kt + 2 <= last ? kt + 2 : last);
+            compute(0);
+            if (kt + 1 <= last) store(1, sa1, sb1);
+            lds_barrier();
+            if (kt + 1 > last) break;
+            // odd step: tile kt+1 in LDS 1; tile kt+2 in set 0; fetch tile kt+3 into set 1
+            load(sa1, sb1, kt + 3 <= last ? kt + 3 : last);
+            compute(1);
+            if (kt + 2 <= last) store(0, sa0, sb0);
+            lds_barrier();
+        }
     }
-    bf16_t* __restrict__ Cg = (bf16_t*)P.C;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-        const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
-        if (n >= N) continue;
-        const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m >= M) continue;
-                const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
-                bf16_t* dst = Cg + cm * P.ldc + cn;
-                float v = acc[i][j][e];
-                if (P.beta) v += bf16_to_f32(*dst);
-                *dst = f32_to_bf16(v);
-            }
-    }
+    gemm_epilogue<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
 }
 
 // ---------------------------------------------------------------- fp32 (VALU)
@@ -518,10 +673,58 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int64_t S, 
 
 }  // namespace
 
+namespace {
+
+template <int BM, int BN, int WGM, int WGN, int NSET>
+hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
+    GemmArgs a = make_args(probs, nprob, BM, BN);
+    const int total = a.first[MAXP];
+    if (total == 0) return hipSuccess;
+    bool any_k = false;
+    for (int i = 0; i < nprob; ++i) any_k |= probs[i].K > 0;
+    const size_t lds = any_k ? (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t) : 0;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_nt_kernel<BM, BN, WGM, WGN, NSET>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET>), dim3(total), dim3(64 * WGM * WGN), lds, st, a);
+    return hipGetLastError();
+}
+
+// The v3 loop needs K % 8 == 0 (zero-padded operands) and byte offsets that
+// stay below 2^31 (row index * ld + K, in bytes).
+bool nt_v3_ok(const GemmProblem* probs, int nprob) {
+    for (int i = 0; i < nprob; ++i) {
+        const GemmProblem& p = probs[i];
+        if (p.M <= 0 || p.N <= 0 || p.K <= 0) continue;
+        if (p.K % 8 != 0 || p.lda % 8 != 0 || p.ldb % 8 != 0) return false;
+        if (p.a_nrows <= 0 || p.b_nrows <= 0) return false;
+        if ((p.a_nrows * p.lda + p.K) * 2 >= (int64_t)0x7fffffff) return false;
+        if ((p.b_nrows * p.ldb + p.K) * 2 >= (int64_t)0x7fffffff) return false;
+    }
+    return true;
+}
+
+}  // namespace
+
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st) {
     // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
     const char* env = getenv("SL_GEMM_CFG");
-    int cfg = env ? atoi(env) : 2;
+    int cfg = env ? atoi(env) : 10;
+    if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {
+        switch (cfg) {
+            case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
+            case 12: return launch_nt_cfg<256, 256, 2, 4, 1>(probs, nprob, st);
+            case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st);
+            case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st);
+            case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st);
+            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
+        }
+    }
+    if (cfg >= 10) cfg = 2;
     switch (cfg) {
         case 0: return nn ? launch_cfg<128, 128, 2, 2, true>(probs, nprob, st)
                           : launch_cfg<128, 128, 2, 2, false>(probs, nprob, st);

@@ -330,10 +330,10 @@ template <typename T>
 __global__ void gather_cols_kernel(const T* __restrict__ in, int64_t ldi,
                                    const int32_t* __restrict__ rows, int64_t nrows,
                                    const int32_t* __restrict__ cols, int64_t ncols,
-                                   T* __restrict__ out, int64_t ldo) {
+                                   int64_t npad, T* __restrict__ out, int64_t ldo) {
     const int64_t m = blockIdx.y;
     const int64_t q0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-    if (q0 >= ncols) return;
+    if (q0 >= npad) return;
     const T* src = in + (int64_t)rows[m] * ldi;
     T* dst = out + m * ldo + q0;
     if (q0 + 8 <= ncols) {
@@ -342,7 +342,8 @@ __global__ void gather_cols_kernel(const T* __restrict__ in, int64_t ldi,
         for (int e = 0; e < 8; ++e) v[e] = ld<T>(src, cols[q0 + e]);
         store8<T>(dst, v);
     } else {
-        for (int64_t q = q0; q < ncols; ++q) dst[q - q0] = src[cols[q]];
+        // ragged end: the last selected columns, then zeros up to npad
+        for (int64_t q = q0; q < npad && q < q0 + 8; ++q) dst[q - q0] = q < ncols ? src[cols[q]] : (T)0;
     }
 }
 
@@ -386,7 +387,7 @@ __global__ void zero_unselected_kernel(T* __restrict__ y, int64_t ldy,
 template <typename T>
 __global__ __launch_bounds__(256) void gather_rows_t_kernel(const T* __restrict__ src, int64_t lds,
                                                             const int32_t* __restrict__ idx,
-                                                            int64_t n, int64_t Dd,
+                                                            int64_t n, int64_t npad, int64_t Dd,
                                                             T* __restrict__ out, int64_t ldo) {
     __shared__ T tile[64][65];
     const int64_t q0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 64;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(256) void gather_rows_t_kernel(const T* __restrict_
     __syncthreads();
     for (int i = ty; i < 64; i += 4) {
         const int64_t j = j0 + i, q = q0 + tx;
-        if (j < Dd && q < n) out[j * ldo + q] = tile[tx][i];
+        if (j < Dd && q < npad) out[j * ldo + q] = tile[tx][i];   // zeros past n
     }
 }
 
@@ -532,16 +533,16 @@ hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void
 }
 
 hipError_t launch_gather_cols(bool bf16, const void* in, int64_t ldi, const int32_t* rows,
-                              int64_t nrows, const int32_t* cols, int64_t ncols, void* out,
-                              int64_t ldo, hipStream_t st) {
-    if (nrows <= 0 || ncols <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(ncols, 256 * 8), (unsigned)nrows);
+                              int64_t nrows, const int32_t* cols, int64_t ncols, int64_t npad,
+                              void* out, int64_t ldo, hipStream_t st) {
+    if (nrows <= 0 || npad <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(npad, 256 * 8), (unsigned)nrows);
     if (bf16)
         hipLaunchKernelGGL(gather_cols_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)in,
-                           ldi, rows, nrows, cols, ncols, (bf16_t*)out, ldo);
+                           ldi, rows, nrows, cols, ncols, npad, (bf16_t*)out, ldo);
     else
         hipLaunchKernelGGL(gather_cols_kernel<float>, grid, dim3(256), 0, st, (const float*)in, ldi,
-                           rows, nrows, cols, ncols, (float*)out, ldo);
+                           rows, nrows, cols, ncols, npad, (float*)out, ldo);
     return hipGetLastError();
 }
 
@@ -569,14 +570,15 @@ hipError_t launch_complement(const int32_t* idx, int64_t n, int64_t C, int32_t* 
 }
 
 hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const int32_t* idx,
-                                int64_t n, int64_t Dd, void* out, int64_t ldo, hipStream_t st) {
-    if (n <= 0 || Dd <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(n, 64), (unsigned)ceil_div(Dd, 64));
+                                int64_t n, int64_t npad, int64_t Dd, void* out, int64_t ldo,
+                                hipStream_t st) {
+    if (npad <= 0 || Dd <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(npad, 64), (unsigned)ceil_div(Dd, 64));
     if (bf16)
         hipLaunchKernelGGL(gather_rows_t_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src,
-                           lds, idx, n, Dd, (bf16_t*)out, ldo);
+                           lds, idx, n, npad, Dd, (bf16_t*)out, ldo);
     else
         hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, (const float*)src,
-                           lds, idx, n, Dd, (float*)out, ldo);
+                           lds, idx, n, npad, Dd, (float*)out, ldo);
     return hipGetLastError();
 }

@@ -131,16 +131,19 @@ struct Timed {
 
 double gemm_flops(const GemmProblem* p, int np) {
     double f = 0;
-    for (int i = 0; i < np; ++i) f += 2.0 * (double)p[i].M * (double)p[i].N * (double)p[i].K;
+    for (int i = 0; i < np; ++i)
+        f += 2.0 * (double)p[i].M * (double)p[i].N * (double)(p[i].k_alg ? p[i].k_alg : p[i].K);
     return f;
 }
 // Algorithmic HBM bytes of a GEMM launch: each operand element read once,
 // each output element written once (read too when accumulating).
 double gemm_bytes(const GemmProblem* p, int np, size_t es) {
     double b = 0;
-    for (int i = 0; i < np; ++i)
-        b += (double)es * ((double)p[i].M * p[i].K + (double)p[i].N * p[i].K +
+    for (int i = 0; i < np; ++i) {
+        const double k = (double)(p[i].k_alg ? p[i].k_alg : p[i].K);
+        b += (double)es * ((double)p[i].M * k + (double)p[i].N * k +
                            (double)p[i].M * p[i].N * (p[i].beta ? 2 : 1));
+    }
     return b;
 }
 
@@ -451,9 +454,9 @@ void set_lora(GemmProblem& p, const LoraEpi& l) {
 GemmProblem problem(const void* A, int64_t lda, const int32_t* a_rows, const void* B, int64_t ldb,
                     const int32_t* b_rows, void* C, int64_t ldc, const int32_t* c_rows,
                     const int32_t* c_cols, int64_t M, int64_t N, int64_t K, int beta,
-                    const LoraEpi& l) {
+                    const LoraEpi& l, int64_t a_nrows, int64_t b_nrows) {
     GemmProblem p = {A, lda, a_rows, B, ldb, b_rows, C, ldc, c_rows, c_cols, M, N, K, beta,
-                     nullptr, 0, nullptr, 0, 0, 0.f, 0, nullptr};
+                     nullptr, 0, nullptr, 0, 0, 0.f, 0, nullptr, a_nrows, b_nrows, 0};
     set_lora(p, l);
     return p;
 }
@@ -470,12 +473,14 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
                      const LoraEpi& l) {
     if (n == C || T_c == 0) {
         GemmProblem p = problem(X, ldx, nullptr, Wc, ldw, nullptr, Z, ldz, nullptr, nullptr, T, C,
-                                Kdim, beta, l);
+                                Kdim, beta, l, T, C);
         return run_gemm(h, dt, false, &p, 1);
     }
     GemmProblem p[2];
-    p[0] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim, beta, l);
-    p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l);
+    p[0] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim, beta,
+                   l, T, C);
+    p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
+                   C);
     const int np = 2;
     if (l.P) {
         SL_CHECK(ensure_ws(h, round_up((size_t)(C - n) * 4, 256)));
@@ -488,7 +493,7 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
         // launch (a K = 0 product needs no staging memory, so it runs many
         // blocks per CU and does not take XCDs away from the main tiles)
         GemmProblem pc = problem(nullptr, 0, ctx_rows, nullptr, 0, nullptr, Z, ldz, ctx_rows, comp,
-                                 T_c, C - n, 0, beta, l);
+                                 T_c, C - n, 0, beta, l, 0, 0);
         {
             Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C - n) * esize(dt));
             SL_HIP(h, dt == SL_BF16 ? launch_lora_fill_bf16(&pc, h->stream)
@@ -517,7 +522,7 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
                     const LoraEpi& l) {
     if (n == C || T_c == 0) {
         GemmProblem p = problem(X, ldx, nullptr, Wd, ldwd, nullptr, Z, ldz, nullptr, nullptr, T, Nout,
-                                C, beta, l);
+                                C, beta, l, T, Nout);
         return run_gemm(h, dt, false, &p, 1);
     }
     const int64_t ldn = n > 0 ? (n + 7) / 8 * 8 : 8;
@@ -546,16 +551,18 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
     float* part = (float*)((char*)h->ws + xc_bytes + ws_bytes);
     if (n > 0) {
         Timed tm(h, K_GATHER, 0, 2.0 * (T_c + Nout) * n * esize(dt));
-        SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, xc, ldn,
+        // both compacted operands are zero-padded to ldn columns, so the
+        // context product may contract over K = ldn (a multiple of 8)
+        SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, ldn, xc, ldn,
                                      h->stream), "gather_cols");
-        SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, Nout, wsl, ldn, h->stream),
-               "gather_rows_t");
+        SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, wsl, ldn,
+                                       h->stream), "gather_rows_t");
     }
     GemmProblem p[5];
     int np = 0;
     if (S == 1) {
         p[np++] = problem(X, ldx, out_rows, Wd, ldwd, nullptr, Z, ldz, out_rows, nullptr, T_o, Nout, C,
-                          beta, l);
+                          beta, l, T, Nout);
     } else {
         for (int64_t q = 0; q < S; ++q) {
             const int64_t k0 = q * Ks, kn = (C - k0) < Ks ? (C - k0) : Ks;
@@ -564,14 +571,16 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
             GemmProblem pp = problem((const char*)X + k0 * esize(dt), ldx, out_rows,
                                      (const char*)Wd + k0 * esize(dt), ldwd, nullptr,
                                      part + q * T_o * Nout, Nout, nullptr, nullptr, T_o, Nout, kn, 0,
-                                     lq);
+                                     lq, T, Nout);
             pp.f32out = 1;
             pp.l_rows = out_rows;
             p[np++] = pp;
         }
     }
-    p[np++] = problem(xc, ldn, nullptr, wsl, ldn, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout, n,
-                      beta, l);
+    // n > 0: contract over the zero-padded width ldn; n == 0: an empty sum
+    p[np++] = problem(xc, ldn, nullptr, wsl, ldn, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
+                      n > 0 ? ldn : 0, beta, l, T_c, Nout);
+    p[np - 1].k_alg = n;
     SL_CHECK(run_gemm(h, dt, false, p, np));
     if (S > 1) {
         Timed tm(h, K_REDUCE, (double)S * T_o * Nout, (double)(S * 4 + 2 * esize(dt)) * T_o * Nout);

@@ -56,6 +56,8 @@ struct GemmProblem {
     int lr;           float lscale;
     int f32out;       // 1: store the raw fp32 accumulators (split-K partials)
     const int32_t* l_rows;  // rank-r row map (token rows) when C rows are unmapped partials
+    int64_t a_nrows, b_nrows;  // heights of the A / B matrices (0: unknown)
+    int64_t k_alg;             // contraction length counted as work (0: K; K may include zero padding)
 };
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
@@ -79,16 +81,19 @@ hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64
                              int32_t* out, hipStream_t st);
 hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t copies,
                               int32_t* out, hipStream_t st);
+// out[m, q] = in[rows[m], cols[q]] for q < ncols, 0 for ncols <= q < npad
 hipError_t launch_gather_cols(bool bf16, const void* in, int64_t ldi, const int32_t* rows,
-                              int64_t nrows, const int32_t* cols, int64_t ncols, void* out,
-                              int64_t ldo, hipStream_t st);
+                              int64_t nrows, const int32_t* cols, int64_t ncols, int64_t npad,
+                              void* out, int64_t ldo, hipStream_t st);
 // Z[c_rows[m], c_cols[n]] = round(sum_s part[s][m][n] (+ Z if beta)), s ascending
 hipError_t launch_splitk_reduce(bool bf16, const float* part, int64_t S, int64_t M, int64_t N,
                                 void* Z, int64_t ldz, const int32_t* c_rows, const int32_t* c_cols,
                                 int beta, hipStream_t st);
 // out[j, q] = src[idx[q], j] for j < Dd, q < n (row gather + transpose)
+// out[j, q] = src[idx[q], j] for q < n, 0 for n <= q < npad
 hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const int32_t* idx,
-                                int64_t n, int64_t Dd, void* out, int64_t ldo, hipStream_t st);
+                                int64_t n, int64_t npad, int64_t Dd, void* out, int64_t ldo,
+                                hipStream_t st);
 // comp[q] = the q-th channel in [0, C) not in the ascending list idx[0..n)
 hipError_t launch_complement(const int32_t* idx, int64_t n, int64_t C, int32_t* comp,
                              hipStream_t st);
