@@ -83,10 +83,16 @@ template <int FM, int FN, int WTM, int WTN>
 __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc)[FM][FN],
                                               int64_t m0, int64_t n0, int wm, int wn, int lane) {
     const int64_t M = P.M, N = P.N;
-    // rank-r term: A operand lP[cm, k], B operand lB[cn, k] (k = kk + lane/32)
+    // rank-r term on the bf16 matrix cores: A operand lP[cm, k..k+7] (fp32,
+    // rounded to bf16 as a bf16 LoRA product rounds its down-projection), B
+    // operand lB[cn, k..k+7], k = kk + 8 (lane / 32); fp32 accumulation into the
+    // same accumulators as the main product
     if (P.lr > 0) {
         const float* __restrict__ lP = P.lP;
         const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
+        const int lr = P.lr;
+        const bool pvec = (P.ldlP % 4 == 0) && (((uintptr_t)lP & 15) == 0);
+        const bool bvec = (P.ldlB % 8 == 0) && (((uintptr_t)lB & 15) == 0);
         const float* prow[FM];
         const bf16_t* bcol[FN];
 #pragma unroll
@@ -102,25 +108,45 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc
             const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
             bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
         }
-        constexpr int KC = FM * FN >= 16 ? 4 : 8;   // k-steps whose operands are loaded before use
-        for (int kk0 = 0; kk0 < P.lr; kk0 += 2 * KC) {
-            float a[KC][FM], b[KC][FN];
+        for (int kk = 0; kk < lr; kk += 16) {
+            const int k = kk + 8 * (lane >> 5);
+            bf16x8 a[FM], b[FN];
 #pragma unroll
-            for (int q = 0; q < KC; ++q) {
-                const int k = kk0 + 2 * q + (lane >> 5);
+            for (int i = 0; i < FM; ++i) {
+                float v[8];
+                if (prow[i] && pvec && k + 8 <= lr) {
+                    const float4 v0 = *(const float4*)(prow[i] + k), v1 = *(const float4*)(prow[i] + k + 4);
+                    v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                    v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+                } else {
 #pragma unroll
-                for (int i = 0; i < FM; ++i) a[q][i] = (prow[i] && k < P.lr) ? P.lscale * prow[i][k] : 0.0f;
+                    for (int e = 0; e < 8; ++e) v[e] = (prow[i] && k + e < lr) ? prow[i][k + e] : 0.0f;
+                }
+                uint32_t w[4];
 #pragma unroll
-                for (int j = 0; j < FN; ++j) b[q][j] = (bcol[j] && k < P.lr) ? bf16_to_f32(bcol[j][k]) : 0.0f;
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (uint32_t)f32_to_bf16(P.lscale * v[2 * e]) |
+                           ((uint32_t)f32_to_bf16(P.lscale * v[2 * e + 1]) << 16);
+                a[i] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
             }
 #pragma unroll
-            for (int q = 0; q < KC; ++q)
-                if (kk0 + 2 * q < P.lr)
+            for (int j = 0; j < FN; ++j) {
+                uint4 u = make_uint4(0u, 0u, 0u, 0u);
+                if (bcol[j] && bvec && k + 8 <= lr) {
+                    u = *(const uint4*)(bcol[j] + k);
+                } else if (bcol[j]) {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    for (int e = 0; e < 8; ++e)
+                        if (k + e < lr) w[e >> 1] |= (uint32_t)bcol[j][k + e] << ((e & 1) * 16);
+                    u = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+                b[j] = __builtin_bit_cast(bf16x8, u);
+            }
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q][i], b[q][j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
 
@@ -573,80 +599,6 @@ hipError_t launch_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     return hipGetLastError();
 }
 
-// ---------------------------------------------------------------- rank-r only
-// Z[c_rows[m], c_cols[n]] (+)= lscale * sum_j lP[c_rows[m], j] lB[c_cols[n], j]
-// for the channels the main product does not produce (the unselected channels
-// of context rows).  128 x 128 tile, 4 waves of 64 x 64; the tile's rows of lP
-// and lB are staged in LDS (fp32), then v_mfma_f32_32x32x2_f32.
-constexpr int LF = 128;
-
-__global__ __launch_bounds__(256) void lora_fill_kernel(GemmProblem P) {
-    __shared__ float Ps[LF][65];
-    __shared__ float Bs[LF][65];
-    const int tiles_m = (int)((P.M + LF - 1) / LF);
-    const int64_t m0 = (int64_t)(blockIdx.x % tiles_m) * LF;
-    const int64_t n0 = (int64_t)(blockIdx.x / tiles_m) * LF;
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const int wm = wid & 1, wn = wid >> 1;
-    const int lr = P.lr;
-    const bf16_t* __restrict__ lB = (const bf16_t*)P.lB;
-    for (int q = tid; q < LF * lr; q += 256) {
-        const int rr = q / lr, j = q % lr;
-        const int64_t m = m0 + rr, n = n0 + rr;
-        float pv = 0.0f, bv = 0.0f;
-        if (m < P.M) {
-            const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
-            pv = P.lscale * P.lP[cm * P.ldlP + j];
-        }
-        if (n < P.N) {
-            const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
-            bv = bf16_to_f32(lB[cn * P.ldlB + j]);
-        }
-        Ps[rr][j] = pv;
-        Bs[rr][j] = bv;
-    }
-    __syncthreads();
-    f32x16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    for (int kk = 0; kk < lr; kk += 2) {
-        const int k = kk + (lane >> 5);
-        float a[2], b[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) a[i] = k < lr ? Ps[wm * 64 + i * 32 + (lane & 31)][k] : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) b[j] = k < lr ? Bs[wn * 64 + j * 32 + (lane & 31)][k] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-    bf16_t* __restrict__ Cg = (bf16_t*)P.C;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (n >= P.N) continue;
-        const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-                if (m >= P.M) continue;
-                const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
-                bf16_t* dst = Cg + cm * P.ldc + cn;
-                float v = acc[i][j][e];
-                if (P.beta) v += bf16_to_f32(*dst);
-                *dst = f32_to_bf16(v);
-            }
-    }
-}
-
 template <typename T>
 __global__ void splitk_reduce_kernel(const float* __restrict__ part, int64_t S, int64_t M,
                                      int64_t N, T* __restrict__ Z, int64_t ldz,
@@ -762,10 +714,3 @@ hipError_t launch_splitk_reduce(bool bf16, const float* part, int64_t S, int64_t
     return hipGetLastError();
 }
 
-hipError_t launch_lora_fill_bf16(const GemmProblem* p, hipStream_t st) {
-    if (p->M <= 0 || p->N <= 0) return hipSuccess;
-    if (p->lr > 64 || p->lr < 1) return hipErrorInvalidValue;
-    const int64_t tiles = ceil_div(p->M, LF) * ceil_div(p->N, LF);
-    hipLaunchKernelGGL(lora_fill_kernel, dim3((unsigned)tiles), dim3(256), 0, st, *p);
-    return hipGetLastError();
-}

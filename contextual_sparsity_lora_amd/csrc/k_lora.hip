@@ -26,18 +26,49 @@ template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, int64_t i, flo
     p[i] = f32_to_bf16(v);
 }
 
+// 8 consecutive elements, 16-byte aligned (bf16) / 32-byte aligned (fp32)
+template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
+template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
+    const uint4 u = *(const uint4*)p;
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
+    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
+template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
+    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
+    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // ---------------------------------------------------------------- xl = x A^T
-// Block of 4 waves covers 16 rows; each wave takes a quarter of K and all
-// r columns (16 per MFMA block); partial sums meet in LDS in wave order.
-__global__ __launch_bounds__(256) void lora_xl_bf16_kernel(const bf16_t* __restrict__ x,
-                                                           int64_t ldx, int64_t T, int64_t D,
-                                                           const bf16_t* __restrict__ A,
-                                                           int64_t lda, int64_t r,
-                                                           float* __restrict__ xl, int64_t ldxl) {
-    __shared__ float part[4][4][16 * 16];
+// Block of XW waves covers 16 rows; each wave takes one XW-th of K (a multiple
+// of 32) and all r columns (16 per MFMA block), with XU 32-wide K steps in
+// flight; partial sums meet in LDS and are added in wave order.
+constexpr int XW = 8, XU = 8;
+
+__global__ __launch_bounds__(XW * 64) void lora_xl_bf16_kernel(const bf16_t* __restrict__ x,
+                                                               int64_t ldx, int64_t T, int64_t D,
+                                                               const bf16_t* __restrict__ A,
+                                                               int64_t lda, int64_t r,
+                                                               float* __restrict__ xl, int64_t ldxl) {
+    __shared__ float part[XW][4][16 * 16];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t t0 = (int64_t)blockIdx.x * 16;
-    const int64_t kq = ((D + 127) / 128) * 32;  // per-wave K range, multiple of 32
+    const int64_t kq = ((D + 32 * XW - 1) / (32 * XW)) * 32;  // per-wave K range, multiple of 32
     const int64_t kbeg = wid * kq, kend = (kbeg + kq < D) ? kbeg + kq : D;
     const int nb = (int)((r + 15) / 16);
     f32x4 acc[4];
@@ -46,8 +77,10 @@ __global__ __launch_bounds__(256) void lora_xl_bf16_kernel(const bf16_t* __restr
     const int64_t row = t0 + (lane & 15);
     const bool rv = row < T;
     const int ko = (lane >> 4) * 8;
+    const bool vec = (ldx % 8 == 0) && (lda % 8 == 0) && ((uintptr_t)x & 15) == 0 &&
+                     ((uintptr_t)A & 15) == 0;
     auto loadv = [&](const bf16_t* base, int64_t k) -> uint4 {
-        if (k + 8 <= kend) return *(const uint4*)(base + k);
+        if (vec && k + 8 <= kend) return *(const uint4*)(base + k);
         uint32_t w[4] = {0u, 0u, 0u, 0u};
         for (int e = 0; e < 8; ++e)
             if (k + e < kend) w[e >> 1] |= (uint32_t)base[k + e] << ((e & 1) * 16);
@@ -60,20 +93,19 @@ __global__ __launch_bounds__(256) void lora_xl_bf16_kernel(const bf16_t* __restr
         const int64_t j = b * 16 + (lane & 15);
         arow[b] = (b < nb && j < r) ? A + j * lda : nullptr;
     }
-    constexpr int U = 4;   // K steps in flight
-    for (int64_t k0 = kbeg; k0 < kend; k0 += 32 * U) {
-        uint4 av[U], bv[U][4];
+    for (int64_t k0 = kbeg; k0 < kend; k0 += 32 * XU) {
+        uint4 av[XU], bv[XU][4];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < XU; ++u) {
             const int64_t k = k0 + 32 * u + ko;
             const bool kin = k < kend;
             av[u] = (rv && kin) ? loadv(xrow, k) : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
             for (int b = 0; b < 4; ++b)
-                bv[u][b] = (arow[b] && kin) ? loadv(arow[b], k) : make_uint4(0u, 0u, 0u, 0u);
+                bv[u][b] = (b < nb && arow[b] && kin) ? loadv(arow[b], k) : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < XU; ++u)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 if (b < nb)
@@ -86,16 +118,15 @@ __global__ __launch_bounds__(256) void lora_xl_bf16_kernel(const bf16_t* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e) part[wid][b][(4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[b][e];
     __syncthreads();
-    for (int q = threadIdx.x; q < 16 * 64; q += 256) {
+    for (int q = threadIdx.x; q < 16 * 64; q += XW * 64) {
         const int rr = q / 64, j = q % 64;
         if (j >= r) continue;
         const int64_t t = t0 + rr;
         if (t >= T) continue;
         const int b = j / 16, jj = j % 16;
-        float s = part[0][b][rr * 16 + jj];
-        s += part[1][b][rr * 16 + jj];
-        s += part[2][b][rr * 16 + jj];
-        s += part[3][b][rr * 16 + jj];
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < XW; ++w) s += part[w][b][rr * 16 + jj];
         xl[t * ldxl + j] = s;
     }
 }
@@ -160,6 +191,127 @@ __global__ __launch_bounds__(256) void lora_add_kernel(const float* __restrict__
     }
 }
 
+// ---------------------------------------------------------------- rank-r fill of rows
+// y[rows[m], c] (+)= s * sum_j P[rows[m], j] B[c, j] for every channel c of the
+// given rows; with beta = 0 every channel is written (the main product of the
+// selected channels is launched afterwards and overwrites them), with beta = 1
+// only channels whose bit in `mask` is clear are updated.
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16), channel as M, row as N, rank as
+// K: s P is rounded to bf16 as a bf16 LoRA product rounds its down-projection,
+// accumulation is fp32.  Row slot m of MFMA (g, e) is channel
+// c0 + 32 g + 8 (m / 4) + 4 e + m % 4, so lane l ends up holding the 8
+// consecutive channels c0 + 32 g + 8 (l / 16) + 0..7 of row l % 16 (one
+// 16-byte store per g).  A wave keeps the B rows of its 128 channels in
+// registers and walks FTW rows; a block of 4 waves covers 128 x 4 FTW.
+constexpr int FTW = 64;
+
+template <int R>
+__global__ __launch_bounds__(256) void lora_fill_rows_kernel(
+    bf16_t* __restrict__ y, int64_t ldy, const int32_t* __restrict__ rows, int64_t nrows, int64_t C,
+    const float* __restrict__ P, int64_t ldp, const bf16_t* __restrict__ B, int64_t ldb, int64_t r,
+    float scale, const uint32_t* __restrict__ mask, int beta) {
+    constexpr int KS = (R + 31) / 32;     // 32-wide rank steps
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 128;
+    const int64_t t0 = ((int64_t)blockIdx.y * 4 + wid) * FTW;
+    const int kl = 8 * (lane >> 4);       // this lane's first rank within a step
+    const bool bvec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
+    const bool pvec = (ldp % 4 == 0) && (((uintptr_t)P & 15) == 0);
+    bf16x8 wa[KS][4][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int m = lane & 15;
+                const int64_t c = c0 + 32 * g + 8 * (m >> 2) + 4 * e + (m & 3);
+                const int k = 32 * ks + kl;
+                uint4 u = make_uint4(0u, 0u, 0u, 0u);
+                if (c < C) {
+                    const bf16_t* br = B + c * ldb;
+                    if (bvec && k + 8 <= r) {
+                        u = *(const uint4*)(br + k);
+                    } else {
+                        uint32_t w[4] = {0u, 0u, 0u, 0u};
+                        for (int q = 0; q < 8; ++q)
+                            if (k + q < r) w[q >> 1] |= (uint32_t)br[k + q] << ((q & 1) * 16);
+                        u = make_uint4(w[0], w[1], w[2], w[3]);
+                    }
+                }
+                wa[ks][g][e] = __builtin_bit_cast(bf16x8, u);
+            }
+    const int64_t cl = c0 + 8 * (lane >> 4);   // + 32 g: this lane's 8 output channels
+    const bool aligned = (ldy % 8 == 0) && (((uintptr_t)y & 15) == 0);
+    for (int64_t tg = t0; tg < t0 + FTW && tg < nrows; tg += 16) {
+        const int64_t m = tg + (lane & 15);
+        const bool mv = m < nrows;
+        const int64_t row = mv ? (int64_t)rows[m] : 0;
+        const float* prow = P + row * ldp;
+        bf16x8 pb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k = 32 * ks + kl;
+            float v[8];
+            if (mv && pvec && k + 8 <= r) {
+                const float4 v0 = *(const float4*)(prow + k), v1 = *(const float4*)(prow + k + 4);
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = (mv && k + q < r) ? prow[k + q] : 0.0f;
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = (uint32_t)f32_to_bf16(scale * v[2 * q]) | ((uint32_t)f32_to_bf16(scale * v[2 * q + 1]) << 16);
+            pb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 acc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][g][e], pb[ks], acc[e], 0, 0, 0);
+            const int64_t c = cl + 32 * g;
+            if (!mv || c >= C) continue;
+            float v[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[i] = acc[0][i];
+                v[4 + i] = acc[1][i];
+            }
+            bf16_t* dst = y + row * ldy + c;
+            if (!beta && aligned && c + 8 <= C) {
+                store8<bf16_t>(dst, v);
+            } else {
+                const uint32_t bits = beta ? (mask[c >> 5] >> (c & 31)) : 0u;   // c % 8 == 0: one word
+                for (int q = 0; q < 8; ++q) {
+                    if (c + q >= C || ((bits >> q) & 1u)) continue;
+                    dst[q] = f32_to_bf16(v[q] + (beta ? bf16_to_f32(dst[q]) : 0.0f));
+                }
+            }
+        }
+    }
+}
+
+// mask[w] bit b set <=> channel 32 w + b is in the ascending list idx
+__global__ void select_mask_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t C,
+                                   uint32_t* __restrict__ mask) {
+    const int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (w * 32 >= C) return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (idx[mid] < w * 32) lo = mid + 1; else hi = mid;
+    }
+    uint32_t bits = 0u;
+    for (; lo < n && idx[lo] < w * 32 + 32; ++lo) bits |= 1u << (idx[lo] - w * 32);
+    mask[w] = bits;
+}
+
 // ---------------------------------------------------------------- out = s P^T Q
 // Block = 256 columns (one per thread) x one chunk of TCH tokens.  The chunk of
 // P is staged in LDS once and read back as wave-wide broadcasts; Q is read
@@ -215,6 +367,97 @@ __global__ __launch_bounds__(256) void outer_partial_kernel(const float* __restr
         if (j < r) ws[(chunk * r + j) * Nc + c] = acc[j];
 }
 
+// bf16 Q on the matrix cores: v_mfma_f32_16x16x4_f32 with the rank as M, the
+// token as K and a channel slot as N.  Lane l of a step owns token l/16 and the
+// 8 consecutive channels c0 + 8 (l % 16) + e (one 16-byte load); MFMA number e
+// takes element e, so output column n of MFMA e is channel c0 + 8 n + e and a
+// lane ends up holding 8 consecutive channels of 4 ranks.  A block of OW waves
+// shares 128 channels; wave w takes OTW tokens of the block's chunk; the waves'
+// partial sums meet in LDS in wave order, and the block writes its chunk's
+// partial to ws[chunk][j][c] for the ordered reduction over chunks.
+constexpr int OW = 8, OTW = 64, OTC = OW * OTW;   // 512 tokens per chunk
+
+template <int R>
+__global__ __launch_bounds__(OW * 64) void outer_mfma_kernel(const float* __restrict__ P, int64_t ldp,
+                                                             int64_t Tn, int64_t r,
+                                                             const bf16_t* __restrict__ Q,
+                                                             int64_t ldq, int64_t Nc,
+                                                             float* __restrict__ ws) {
+    constexpr int JB = R / 16;
+    constexpr int U = 8;                      // 4-token steps in flight
+    __shared__ float red[R * 128];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 128;
+    const int64_t chunk = blockIdx.y;
+    const int64_t tb = chunk * OTC + (int64_t)wid * OTW;
+    const int64_t cl = c0 + 8 * (lane & 15);
+    const int kt = lane >> 4;
+    const bool cfull = cl + 8 <= Nc;
+    f32x4 acc[JB][8];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[jb][e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s0 = 0; s0 < OTW / 4; s0 += U) {
+        uint4 qv[U];
+        float pv[U][JB];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t t = tb + 4 * (s0 + u) + kt;
+            qv[u] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb) pv[u][jb] = 0.0f;
+            if (t < Tn) {
+                const bf16_t* qr = Q + t * ldq + cl;
+                if (cfull) {
+                    qv[u] = *(const uint4*)qr;
+                } else {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    for (int e = 0; e < 8; ++e)
+                        if (cl + e < Nc) w[e >> 1] |= (uint32_t)qr[e] << ((e & 1) * 16);
+                    qv[u] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb) {
+                    const int j = 16 * jb + (lane & 15);
+                    pv[u][jb] = j < r ? P[t * ldp + j] : 0.0f;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t w[4] = {qv[u].x, qv[u].y, qv[u].z, qv[u].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float b = __uint_as_float((e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16));
+#pragma unroll
+                for (int jb = 0; jb < JB; ++jb)
+                    acc[jb][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(pv[u][jb], b, acc[jb][e], 0, 0, 0);
+            }
+        }
+    }
+    // lane holds rank 16 jb + 4 (lane / 16) + i of channel slot 8 (lane % 16) + e
+    for (int w = 0; w < OW; ++w) {
+        if (wid == w) {
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float& d = red[(16 * jb + 4 * kt + i) * 128 + 8 * (lane & 15) + e];
+                        d = (w == 0 ? 0.0f : d) + acc[jb][e][i];
+                    }
+        }
+        __syncthreads();
+    }
+    for (int q = threadIdx.x; q < R * 128; q += OW * 64) {
+        const int j = q >> 7, cc = q & 127;
+        if (j < r && c0 + cc < Nc) ws[(chunk * r + j) * Nc + c0 + cc] = red[q];
+    }
+}
+
 __global__ void outer_reduce_kernel(const float* __restrict__ ws, int64_t nch, int64_t r,
                                     int64_t Nc, float scale, float* __restrict__ out, int64_t soj,
                                     int64_t soc) {
@@ -241,34 +484,6 @@ __global__ void transpose_kernel(const T* __restrict__ in, int64_t ldi, int64_t 
         const int64_t c = c0 + i, r = r0 + threadIdx.x;
         if (r < rows && c < cols) out[c * ldo + r] = tile[threadIdx.x][i];
     }
-}
-
-// 8 consecutive elements, 16-byte aligned (bf16) / 32-byte aligned (fp32)
-template <typename T> __device__ __forceinline__ void load8(const T* p, float* v);
-template <> __device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float* v) {
-    const uint4 u = *(const uint4*)p;
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = __uint_as_float(w[i] << 16);
-        v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-    }
-}
-template <> __device__ __forceinline__ void load8<float>(const float* p, float* v) {
-    const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-template <typename T> __device__ __forceinline__ void store8(T* p, const float* v);
-template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float* v) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
-    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
-}
-template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
-    *(float4*)p = make_float4(v[0], v[1], v[2], v[3]);
-    *(float4*)(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 template <typename T>
@@ -426,7 +641,7 @@ hipError_t launch_lora_xl(bool bf16, const void* x, int64_t ldx, int64_t T, int6
     (void)ws;
     if (T <= 0) return hipSuccess;
     if (bf16)
-        hipLaunchKernelGGL(lora_xl_bf16_kernel, dim3((unsigned)ceil_div(T, 16)), dim3(256), 0, st,
+        hipLaunchKernelGGL(lora_xl_bf16_kernel, dim3((unsigned)ceil_div(T, 16)), dim3(XW * 64), 0, st,
                            (const bf16_t*)x, ldx, T, D, (const bf16_t*)A, lda, r, xl, ldxl);
     else
         hipLaunchKernelGGL(lora_xl_f32_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0,
@@ -465,9 +680,21 @@ hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T,
                               int64_t so_j, int64_t so_c, float* ws, size_t ws_floats,
                               hipStream_t st) {
     if (Ncols <= 0 || r <= 0) return hipSuccess;
-    const int64_t nch = T > 0 ? ceil_div(T, TCH) : 0;
+    // bf16 Q with 16-byte aligned rows: matrix-core kernel, 512-token chunks
+    const bool mfma = bf16 && ldq % 8 == 0 && ((uintptr_t)Q & 15) == 0;
+    const int64_t tch = mfma ? OTC : TCH;
+    const int64_t nch = T > 0 ? ceil_div(T, tch) : 0;
     if ((size_t)(nch * r * Ncols) > ws_floats) return hipErrorInvalidValue;
-    if (T > 0) {
+    if (T > 0 && mfma) {
+        const dim3 grid((unsigned)ceil_div(Ncols, 128), (unsigned)nch);
+#define OUTERM(RR)                                                                             \
+    hipLaunchKernelGGL((outer_mfma_kernel<RR>), grid, dim3(OW * 64), 0, st, P, ldp, T, r,      \
+                       (const bf16_t*)Q, ldq, Ncols, ws)
+        if (r <= 16) OUTERM(16);
+        else if (r <= 32) OUTERM(32);
+        else OUTERM(64);
+#undef OUTERM
+    } else if (T > 0) {
         const dim3 grid((unsigned)ceil_div(Ncols, 256), (unsigned)nch);
 #define OUTER(TT, RR)                                                                          \
     hipLaunchKernelGGL((outer_partial_kernel<TT, RR>), grid, dim3(256), 0, st, P, ldp, T, r,   \
@@ -487,6 +714,26 @@ hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T,
     }
     hipLaunchKernelGGL(outer_reduce_kernel, dim3((unsigned)ceil_div(r * Ncols, 256)), dim3(256), 0,
                        st, ws, nch, r, Ncols, scale, out, so_j, so_c);
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
+                                 int64_t C, const float* P, int64_t ldp, const void* B,
+                                 int64_t ldb, int64_t r, float scale, const int32_t* idx,
+                                 int64_t n, uint32_t* mask, int beta, hipStream_t st) {
+    if (nrows <= 0 || C <= 0) return hipSuccess;
+    if (r < 1 || r > 64) return hipErrorInvalidValue;
+    if (beta) {
+        hipLaunchKernelGGL(select_mask_kernel, dim3((unsigned)ceil_div(ceil_div(C, 32), 256)),
+                           dim3(256), 0, st, idx, n, C, mask);
+    }
+    const dim3 grid((unsigned)ceil_div(C, 128), (unsigned)ceil_div(nrows, 4 * FTW));
+#define FILL(RR)                                                                                  \
+    hipLaunchKernelGGL((lora_fill_rows_kernel<RR>), grid, dim3(256), 0, st, (bf16_t*)y, ldy, rows, \
+                       nrows, C, P, ldp, (const bf16_t*)B, ldb, r, scale, (const uint32_t*)mask, beta)
+    if (r <= 32) FILL(32);
+    else FILL(64);
+#undef FILL
     return hipGetLastError();
 }
 

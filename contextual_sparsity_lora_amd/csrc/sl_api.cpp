@@ -482,22 +482,28 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
     p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
                    C);
     const int np = 2;
-    if (l.P) {
+    if (l.P && dt == SL_BF16) {
+        // rank-r term of the unselected channels of context rows: written for
+        // every channel (beta = 0: the product below then overwrites the
+        // selected ones) or, when accumulating, for the unselected ones only
+        SL_CHECK(ensure_ws(h, round_up((size_t)ceil_div(C, 32) * 4, 256)));
+        Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (beta ? 2 * (C - n) : C) * esize(dt));
+        SL_HIP(h, launch_lora_fill_rows(Z, ldz, ctx_rows, T_c, C, l.P, l.ldP, l.B, l.ldB, l.r,
+                                        l.scale, idx, n, (uint32_t*)h->ws, beta, h->stream),
+               "lora_fill");
+    } else if (l.P) {
         SL_CHECK(ensure_ws(h, round_up((size_t)(C - n) * 4, 256)));
         int32_t* comp = (int32_t*)h->ws;
         {
             Timed tm(h, K_INDEX, 0, 4.0 * (C + n));
             SL_HIP(h, launch_complement(idx, n, C, comp, h->stream), "complement");
         }
-        // unselected channels of context rows: the rank-r term alone, as its own
-        // launch (a K = 0 product needs no staging memory, so it runs many
-        // blocks per CU and does not take XCDs away from the main tiles)
+        // fp32: the unselected channels of context rows get the rank-r term alone
         GemmProblem pc = problem(nullptr, 0, ctx_rows, nullptr, 0, nullptr, Z, ldz, ctx_rows, comp,
                                  T_c, C - n, 0, beta, l, 0, 0);
         {
             Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C - n) * esize(dt));
-            SL_HIP(h, dt == SL_BF16 ? launch_lora_fill_bf16(&pc, h->stream)
-                                    : launch_gemm_f32(false, &pc, 1, h->stream), "lora_fill");
+            SL_HIP(h, launch_gemm_f32(false, &pc, 1, h->stream), "lora_fill");
         }
     } else if (!beta) {
         Timed tm(h, K_FILL, 0, (double)T_c * (C - n) * esize(dt));

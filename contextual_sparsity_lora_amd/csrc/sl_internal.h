@@ -63,7 +63,13 @@ struct GemmProblem {
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 // rank-r term only (K = 0 problem), bf16 output
-hipError_t launch_lora_fill_bf16(const GemmProblem* p, hipStream_t st);
+// y[rows[m], c] (+)= scale * P[rows[m], :] . B[c, :] over all C channels (bf16 y,
+// fp32 P, bf16 B [C, r]); beta = 0 writes every channel, beta = 1 only the
+// channels not in the ascending list idx (mask: ceil(C / 32) words of scratch)
+hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
+                                 int64_t C, const float* P, int64_t ldp, const void* B,
+                                 int64_t ldb, int64_t r, float scale, const int32_t* idx,
+                                 int64_t n, uint32_t* mask, int beta, hipStream_t st);
 // fp32 version (VALU), same semantics.
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 

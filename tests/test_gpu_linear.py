@@ -114,7 +114,8 @@ def test_beta_accumulates(rng):
 
 
 @pytest.mark.parametrize("dtype,T,Din,Dout,r", [("f32", 128, 256, 688, 8), ("bf16", 300, 520, 1000, 16),
-                                                ("bf16", 64, 4096, 14336, 16), ("bf16", 33, 200, 72, 32)])
+                                                ("bf16", 64, 4096, 14336, 16), ("bf16", 33, 200, 72, 32),
+                                                ("bf16", 1100, 256, 520, 16), ("bf16", 100, 136, 264, 64)])
 def test_lora_fwd_bwd(dtype, T, Din, Dout, r, rng):
     ops = _ops()
     print(f"[lora] {dtype} T={T} D_in={Din} D_out={Dout} r={r}", flush=True)
@@ -190,3 +191,30 @@ def test_fused_lora_term(dtype, r, rng):
     ops.sparse_linear_bwd("out", dev_pad(dy2, dtype), Wd, Wtd, c_d, o_d, to_dev(idx, None), dx2,
                           lora=(to_dev(P, "f32"), dev_pad(Bi, dtype), r, s))
     assert mar(host(dx2), ref.sparse_linear_bwd("out", dy2, W, roles, idx) + lora_i) <= tol
+
+
+@pytest.mark.parametrize("r,Dout", [(16, 1000), (32, 1003), (64, 136)])
+def test_fused_lora_term_accumulates(r, Dout, rng):
+    """beta = 1 with the LoRA term: every channel of every row gains exactly one
+    copy of the rank-r term (unselected context channels from the rank-r fill,
+    the rest from the product's epilogue), on top of what the output held."""
+    ops = _ops()
+    roles = _roles(3, 130, 30)
+    T, Din = 390, 264
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    s = 0.5
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+    y0 = round_dtype(rng.standard_normal((T, Dout)), "bf16")
+    idx = np.sort(rng.choice(Dout, Dout // 3, replace=False)).astype(np.int32)
+    y = dev_pad(y0, "bf16")
+    ops.sparse_linear_fwd("out", dev_pad(x, "bf16"), dev_pad(W, "bf16"), None, c_d, o_d,
+                          to_dev(idx, None), y, beta=1,
+                          lora=(to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s))
+    lora = s * (P.astype(np.float64) @ Bm.T.astype(np.float64))
+    want = y0 + ref.sparse_linear_fwd("out", x, W, roles, idx) + lora
+    assert mar(host(y), want) <= TOL["bf16"]
+    drop = np.setdiff1d(np.arange(Dout), idx)
+    assert mar(host(y)[np.ix_(ctx, drop)], (y0 + lora)[np.ix_(ctx, drop)]) <= TOL["bf16"]
