@@ -45,6 +45,11 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel whose host-side stub was not emitted links fine and fails at load
+    nm = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True)
+    missing = [l for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from the library:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

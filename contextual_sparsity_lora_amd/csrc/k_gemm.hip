@@ -80,7 +80,7 @@ __device__ __forceinline__ uint4 load16_guard(const bf16_t* rowp, int64_t k, int
 // (or raw fp32 partials).  Lane holds column (lane & 31) and rows
 // 8*(e/4) + 4*(lane/32) + e%4 of each 32 x 32 block.
 template <int FM, int FN, int WTM, int WTN>
-__device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+__device__ __forceinline__ void gemm_lora_term(const GemmProblem& P, f32x16 (&acc)[FM][FN],
                                               int64_t m0, int64_t n0, int wm, int wn, int lane) {
     const int64_t M = P.M, N = P.N;
     // rank-r term on the bf16 matrix cores: A operand lP[cm, k..k+7] (fp32,
@@ -149,7 +149,14 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
+}
 
+// Direct store of the accumulators (one element per lane and instruction),
+// through the row / column maps, or raw fp32 partials.
+template <int FM, int FN, int WTM, int WTN>
+__device__ __forceinline__ void gemm_store_direct(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+                                                  int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    const int64_t M = P.M, N = P.N;
     // epilogue: lane holds column (lane & 31) and rows 8*(e/4) + 4*(lane/32) + e%4
     if (P.f32out) {   // split-K partial: raw fp32, unmapped
         float* __restrict__ Cf = (float*)P.C;
@@ -186,6 +193,119 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc
                 *dst = f32_to_bf16(v);
             }
     }
+}
+
+template <int FM, int FN, int WTM, int WTN>
+__device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+                                              int64_t m0, int64_t n0, int wm, int wn, int lane) {
+    gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+    gemm_store_direct<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+}
+
+// Store through LDS (the staging buffers are free once the K loop is done): the
+// tile goes out in FM passes of 32 WGM rows; each pass writes its rows to LDS
+// as fp32 (lanes 0-31 of a wave: 32 consecutive columns, conflict free), then
+// every thread takes runs of 8 consecutive columns of one row: one 16-byte
+// bf16 store (or two for fp32 partials) per run, read-modify-write when
+// accumulating.  With a column map each lane stores single elements, the lanes
+// of a wave on consecutive columns of one row.
+template <int FM, int FN, int WTM, int WTN, int WGM, int WGN>
+__device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+                                               int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                               int tid, float* const (&csr)[WGM]) {
+    constexpr int NTH = 64 * WGM * WGN;
+    constexpr int BN = WGN * WTN;
+    constexpr int PR = 32 * WGM;                 // rows per pass
+    constexpr int LDC = BN + 4;                  // fp32 row pitch in LDS
+    constexpr int RUNS = PR * (BN / 8);          // 8-column runs per pass
+    const int64_t M = P.M, N = P.N;
+    const bool vec = P.c_cols == nullptr && (P.ldc % 8 == 0) && (((uintptr_t)P.C & 15) == 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        __syncthreads();                          // LDS free (K loop done / previous pass read)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                csr[wm][(r - wm * 32) * LDC + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][e];
+            }
+        __syncthreads();
+        if (P.c_cols && !P.f32out) {
+            // mapped columns: one element per lane, consecutive lanes on consecutive
+            // columns of one row (each store instruction covers 64 columns)
+            for (int q = tid; q < PR * BN; q += NTH) {
+                const int r = q / BN, c = q % BN;
+                const int64_t m = m0 + (r / 32) * WTM + 32 * i + (r % 32);
+                const int64_t n = n0 + c;
+                if (m >= M || n >= N) continue;
+                const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+                bf16_t* dst = (bf16_t*)P.C + cm * P.ldc + P.c_cols[n];
+                float x = csr[r / 32][(r % 32) * LDC + c];
+                if (P.beta) x += bf16_to_f32(*dst);
+                *dst = f32_to_bf16(x);
+            }
+            continue;
+        }
+        for (int q = tid; q < RUNS; q += NTH) {
+            const int r = q / (BN / 8), c8 = (q % (BN / 8)) * 8;
+            const int64_t m = m0 + (r / 32) * WTM + 32 * i + (r % 32);
+            const int64_t n = n0 + c8;
+            if (m >= M || n >= N) continue;
+            const float* src = csr[r / 32] + (r % 32) * LDC + c8;
+            const float4 v0 = *(const float4*)src, v1 = *(const float4*)(src + 4);
+            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            const bool full = n + 8 <= N;
+            if (P.f32out) {                       // split-K partial: raw fp32, unmapped
+                float* dst = (float*)P.C + m * P.ldc + n;
+                if (full && (P.ldc % 4 == 0) && (((uintptr_t)P.C & 15) == 0)) {
+                    *(float4*)dst = v0;
+                    *(float4*)(dst + 4) = v1;
+                } else {
+                    for (int q2 = 0; q2 < 8; ++q2)
+                        if (n + q2 < N) dst[q2] = v[q2];
+                }
+                continue;
+            }
+            const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+            bf16_t* Cg = (bf16_t*)P.C + cm * P.ldc;
+            if (vec && full) {
+                bf16_t* dst = Cg + n;
+                if (P.beta) {
+                    const uint4 o = *(const uint4*)dst;
+                    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                    for (int q2 = 0; q2 < 4; ++q2) {
+                        v[2 * q2] += bf16_to_f32((bf16_t)(w[q2] & 0xffffu));
+                        v[2 * q2 + 1] += bf16_to_f32((bf16_t)(w[q2] >> 16));
+                    }
+                }
+                uint32_t w[4];
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2)
+                    w[q2] = (uint32_t)f32_to_bf16(v[2 * q2]) | ((uint32_t)f32_to_bf16(v[2 * q2 + 1]) << 16);
+                *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                for (int q2 = 0; q2 < 8; ++q2) {
+                    if (n + q2 >= N) break;
+                    bf16_t* dst = Cg + n + q2;
+                    float x = v[q2];
+                    if (P.beta) x += bf16_to_f32(*dst);
+                    *dst = f32_to_bf16(x);
+                }
+            }
+        }
+    }
+}
+
+template <int FM, int FN, int WTM, int WTN, int WGM, int WGN>
+__device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&acc)[FM][FN],
+                                               int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                               int tid, float* cs) {
+    float* csr[WGM];
+#pragma unroll
+    for (int g = 0; g < WGM; ++g) csr[g] = cs + g * 32 * (WGN * WTN + 4);
+    gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, csr);
 }
 
 template <int BM, int BN, int WGM, int WGN, bool NN>
@@ -487,8 +607,153 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
             lds_barrier();
         }
     }
-    gemm_epilogue<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+    gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+    gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, (float*)smem);
 }
+
+// ---------------------------------------------------------------- NT main loop v5 (LDS DMA)
+// 256 x 256 tile, K in stages of 32, four LDS stages filled by buffer loads
+// that write LDS directly (buffer_load_dwordx4 ... lds): no register staging and
+// no LDS store instructions.  A load instruction of a wave fills one 1 KB slab
+// (16 rows of 64 bytes) with lane i at byte 16 i, so lane i fetches row i / 4
+// of the slab and the 8-element k-chunk that the row swizzle puts at position
+// i % 4: chunk c of row R sits at position c ^ ((R >> 1) & 3), which keeps the
+// MFMA fragment reads (8 lanes = 8 consecutive rows, same chunk) free of bank
+// conflicts.  The stages are four separate LDS arrays and the K loop is
+// unrolled by four so that every read names its stage; a wave waits for its own
+// loads of tile t (the loads of t+1, t+2 stay in flight), then one barrier per
+// stage publishes tile t and retires the reads of tile t-1, whose stage takes
+// the loads of tile t+3.
+constexpr int BK5 = 32;
+constexpr int ST5 = 17408;   // bf16 per stage array: 512 rows x 32 (32 KB), room for the store epilogue
+
+__host__ __device__ constexpr uint16_t vmcnt_imm(int n) {
+    // s_waitcnt immediate: vmcnt(n) only (expcnt, lgkmcnt at their maxima)
+    return (uint16_t)((n & 15) | 0x70 | 0xF00 | ((n >> 4) << 14));
+}
+
+template <int NW, int DPT>
+__device__ __forceinline__ void nt5_dma(rsrc_t ra, rsrc_t rb, bf16_t* st, int64_t kt, int64_t K, int ck,
+                                        int wid, const uint32_t (&goff)[DPT]) {
+    const uint32_t soff = (uint32_t)(kt * BK5 * 2);
+    const bool kin = kt * BK5 + ck * 8 < K;
+#pragma unroll
+    for (int d = 0; d < DPT / 2; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + (wid + NW * d) * 512),
+                                                 16, kin ? goff[d] : OOB_OFF, soff, 0, 0);
+#pragma unroll
+    for (int d = DPT / 2; d < DPT; ++d)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(st + (wid + NW * d) * 512),
+                                                 16, kin ? goff[d] : OOB_OFF, soff, 0, 0);
+}
+
+template <int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args) {
+    constexpr int BM = 256, BN = 256;
+    constexpr int NW = WGM * WGN;
+    constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
+    constexpr int DPT = 32 / NW;                 // slabs (load instructions) per wave per stage
+    static_assert(DPT * NW == 32 && DPT % 2 == 0, "32 slabs per stage: A in slabs 0-15, B in 16-31");
+    __shared__ __attribute__((aligned(16))) bf16_t s0[ST5];
+    __shared__ __attribute__((aligned(16))) bf16_t s1[ST5];
+    __shared__ __attribute__((aligned(16))) bf16_t s2[ST5];
+    __shared__ __attribute__((aligned(16))) bf16_t s3[ST5];
+
+    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, L, P, t, tiles_m);
+    const int64_t m0 = (int64_t)(t % tiles_m) * BM;
+    const int64_t n0 = (int64_t)(t / tiles_m) * BN;
+    const int64_t M = P.M, N = P.N, K = P.K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wid % WGM, wn = wid / WGM;
+
+    // loads: slab q = wid + NW d (q < 16: A rows 16 q.., else B rows 16 (q - 16)..)
+    const int ck = (lane & 3) ^ ((lane >> 3) & 3);       // k-chunk this lane fetches
+    uint32_t goff[DPT];
+#pragma unroll
+    for (int d = 0; d < DPT; ++d) {
+        const int q = wid + NW * d;
+        const int64_t rr = 16 * (q & 15) + (lane >> 2);
+        if (d < DPT / 2) {
+            const int64_t m = m0 + rr;
+            goff[d] = m < M ? (uint32_t)(((P.a_rows ? (int64_t)P.a_rows[m] : m) * P.lda + ck * 8) * 2) : OOB_OFF;
+        } else {
+            const int64_t n = n0 + rr;
+            goff[d] = n < N ? (uint32_t)(((P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb + ck * 8) * 2) : OOB_OFF;
+        }
+    }
+    const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
+    const int64_t nk = (K + BK5 - 1) / BK5;
+    const int64_t last = nk > 0 ? nk - 1 : 0;
+    auto dma = [&](bf16_t* st, int64_t kt) { nt5_dma<NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
+
+    // fragment reads: row R = base + lane % 32 (base a multiple of 32), chunk 2 ks + lane / 32
+    const int swz = ((lane & 31) >> 1) & 3;
+    const int koff0 = ((0 + (lane >> 5)) ^ swz) * 8, koff1 = ((2 + (lane >> 5)) ^ swz) * 8;
+    const int arow = (wm * WTM + (lane & 31)) * 32;
+    const int brow = (256 + wn * WTN + (lane & 31)) * 32;
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    auto compute = [&](const bf16_t* st) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int ko = ks ? koff1 : koff0;
+            bf16x8 a[FM], b[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)&st[arow + i * 32 * 32 + ko];
+#pragma unroll
+            for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&st[brow + j * 32 * 32 + ko];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+
+    if (K > 0) {
+        dma(s0, 0);
+        dma(s1, 1 <= last ? 1 : last);
+        dma(s2, 2 <= last ? 2 : last);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPT));
+        __builtin_amdgcn_s_barrier();
+        // step T: load tile T+3 into the stage of tile T-1, multiply tile T, then
+        // wait for this wave's loads of tile T+1 and publish it with the barrier
+#define NT5_STEP(CUR, NXT, T)                                                 \
+        dma(NXT, (T) + 3 <= last ? (T) + 3 : last);                           \
+        compute(CUR);                                                         \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPT));                       \
+        __builtin_amdgcn_s_barrier();
+        for (int64_t kt = 0; kt < nk; kt += 4) {
+            NT5_STEP(s0, s3, kt)
+            if (kt + 1 >= nk) break;
+            NT5_STEP(s1, s0, kt + 1)
+            if (kt + 2 >= nk) break;
+            NT5_STEP(s2, s1, kt + 2)
+            if (kt + 3 >= nk) break;
+            NT5_STEP(s3, s2, kt + 3)
+        }
+#undef NT5_STEP
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the stages are reused below
+    }
+    gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+    float* csr[2];
+    csr[0] = (float*)s0;
+    csr[1] = (float*)s1;
+    static_assert(WGM == 2, "store epilogue: one stage array per row group");
+    gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, csr);
+}
+
 
 // ---------------------------------------------------------------- fp32 (VALU)
 constexpr int FB = 64, FK = 16;
@@ -632,9 +897,8 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     GemmArgs a = make_args(probs, nprob, BM, BN);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
-    bool any_k = false;
-    for (int i = 0; i < nprob; ++i) any_k |= probs[i].K > 0;
-    const size_t lds = any_k ? (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t) : 0;
+    // staging buffers; the store epilogue reuses them (always needed)
+    const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void*)gemm_nt_kernel<BM, BN, WGM, WGN, NSET>,
@@ -645,6 +909,16 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET>), dim3(total), dim3(64 * WGM * WGN), lds, st, a);
     return hipGetLastError();
 }
+
+template <int WGM, int WGN>
+hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st) {
+    GemmArgs a = make_args(probs, nprob, 256, 256);
+    const int total = a.first[MAXP];
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN>), dim3(total), dim3(64 * WGM * WGN), 0, st, a);
+    return hipGetLastError();
+}
+
 
 // The v3 loop needs K % 8 == 0 (zero-padded operands) and byte offsets that
 // stay below 2^31 (row index * ld + K, in bytes).
@@ -673,6 +947,8 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
             case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st);
             case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st);
             case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st);
+            case 20: return launch_nt5<2, 4>(probs, nprob, st);
+            case 21: return launch_nt5<2, 2>(probs, nprob, st);
             default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
         }
     }
