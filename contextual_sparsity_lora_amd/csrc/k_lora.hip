@@ -131,6 +131,85 @@ __global__ __launch_bounds__(XW * 64) void lora_xl_bf16_kernel(const bf16_t* __r
     }
 }
 
+// Split-K form for bf16: a block of 4 waves takes 64 rows (16 per wave) and
+// one K chunk; the chunk is walked in steps of 256 whose slice of A
+// (r x 256) is staged in LDS once for the four waves, while each wave keeps 8
+// 16-byte loads of its rows in flight.  Partial sums go to part[ks][t][R] and
+// an ordered reduction over the chunks follows (deterministic).
+constexpr int XR = 64, XKC = 256;
+
+template <int R>
+__global__ __launch_bounds__(256) void lora_xl_split_kernel(const bf16_t* __restrict__ x, int64_t ldx,
+                                                            int64_t T, int64_t D,
+                                                            const bf16_t* __restrict__ A, int64_t lda,
+                                                            int64_t r, int64_t kchunk,
+                                                            float* __restrict__ part) {
+    constexpr int NB = R / 16;
+    __shared__ __attribute__((aligned(16))) bf16_t As[R][XKC + 8];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * XR;
+    const int64_t ks = blockIdx.y;
+    const int64_t kb = ks * kchunk, ke = (kb + kchunk < D) ? kb + kchunk : D;
+    const int64_t row = t0 + wid * 16 + (lane & 15);
+    const bool rv = row < T;
+    const int ko = (lane >> 4) * 8;
+    const bool xvec = (ldx % 8 == 0) && (((uintptr_t)x & 15) == 0);
+    const bool avec = (lda % 8 == 0) && (((uintptr_t)A & 15) == 0);
+    const bf16_t* xrow = x + (rv ? row : 0) * ldx;
+    auto load8 = [&](const bf16_t* base, int64_t k, bool vec) -> uint4 {
+        if (vec && k + 8 <= ke) return *(const uint4*)(base + k);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        for (int e = 0; e < 8; ++e)
+            if (k + e < ke) w[e >> 1] |= (uint32_t)base[k + e] << ((e & 1) * 16);
+        return make_uint4(w[0], w[1], w[2], w[3]);
+    };
+    f32x4 acc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int64_t k0 = kb; k0 < ke; k0 += XKC) {
+        uint4 xv[XKC / 32];
+#pragma unroll
+        for (int u = 0; u < XKC / 32; ++u) {
+            const int64_t k = k0 + 32 * u + ko;
+            xv[u] = (rv && k < ke) ? load8(xrow, k, xvec) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();                          // the previous slice has been read
+#pragma unroll
+        for (int c = 0; c < R / 8; ++c) {
+            const int q = tid + 256 * c;
+            const int j = q / 32, kk = (q % 32) * 8;
+            const int64_t k = k0 + kk;
+            *(uint4*)&As[j][kk] = (j < r && k < ke) ? load8(A + j * lda, k, avec) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < XKC / 32; ++u)
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    *(bf16x8*)&xv[u], *(const bf16x8*)&As[16 * b + (lane & 15)][32 * u + ko], acc[b], 0, 0, 0);
+    }
+    // lane holds C[4 (lane / 16) + e][lane % 16] of rank block b
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int64_t t = t0 + wid * 16 + 4 * (lane >> 4) + e;
+            const int j = 16 * b + (lane & 15);
+            if (t < T && j < r) part[(ks * T + t) * R + j] = acc[b][e];
+        }
+}
+
+__global__ void lora_xl_reduce_kernel(const float* __restrict__ part, int64_t KS, int64_t T, int64_t r,
+                                      int64_t R, float* __restrict__ xl, int64_t ldxl) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= T * r) return;
+    const int64_t t = q / r, j = q % r;
+    float s = 0.0f;
+    for (int64_t k = 0; k < KS; ++k) s += part[(k * T + t) * R + j];
+    xl[t * ldxl + j] = s;
+}
+
 __global__ void lora_xl_f32_kernel(const float* __restrict__ x, int64_t ldx, int64_t T, int64_t D,
                                    const float* __restrict__ A, int64_t lda, int64_t r,
                                    float* __restrict__ xl, int64_t ldxl) {
@@ -619,6 +698,57 @@ __global__ __launch_bounds__(256) void gather_rows_t_kernel(const T* __restrict_
         if (j < Dd && q < npad) out[j * ldo + q] = tile[tx][i];   // zeros past n
     }
 }
+// bf16 form: tile of 64 selected channels x 128 output rows; 16-byte loads
+// along the source rows, 16-byte stores along the output rows, the transpose
+// in LDS (row pitch 136 elements: the 8 strided 2-byte reads of a store hit
+// different banks).
+__global__ __launch_bounds__(256) void gather_rows_t_bf16_kernel(const bf16_t* __restrict__ src,
+                                                                 int64_t lds,
+                                                                 const int32_t* __restrict__ idx,
+                                                                 int64_t n, int64_t npad, int64_t Dd,
+                                                                 bf16_t* __restrict__ out, int64_t ldo) {
+    __shared__ __attribute__((aligned(16))) bf16_t tile[64][136];
+    const int64_t q0 = (int64_t)blockIdx.x * 64, j0 = (int64_t)blockIdx.y * 128;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int qq = tid + 256 * c;
+        const int i = qq >> 4, jj = (qq & 15) * 8;        // source row i of the tile, columns jj..jj+7
+        const int64_t q = q0 + i, j = j0 + jj;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (q < n && j < Dd) {
+            const bf16_t* sp = src + (int64_t)idx[q] * lds + j;
+            if (j + 8 <= Dd) {
+                v = *(const uint4*)sp;
+            } else {
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+                for (int e = 0; e < 8; ++e)
+                    if (j + e < Dd) w[e >> 1] |= (uint32_t)sp[e] << ((e & 1) * 16);
+                v = make_uint4(w[0], w[1], w[2], w[3]);
+            }
+        }
+        *(uint4*)&tile[i][jj] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int qq = tid + 256 * c;
+        const int jj = qq >> 3, i8 = (qq & 7) * 8;        // output row jj of the tile, channels i8..i8+7
+        const int64_t j = j0 + jj, q = q0 + i8;
+        if (j >= Dd || q >= npad) continue;
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)tile[i8 + 2 * e][jj] | ((uint32_t)tile[i8 + 2 * e + 1][jj] << 16);
+        bf16_t* op = out + j * ldo + q;
+        if (q + 8 <= npad) {
+            *(uint4*)op = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+            for (int e = 0; e < 8 && q + e < npad; ++e) op[e] = (bf16_t)(w[e >> 1] >> ((e & 1) * 16));
+        }
+    }
+}
+
 
 // comp[c - #selected below c] = c for every unselected channel c
 __global__ void complement_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t C,
@@ -635,17 +765,46 @@ __global__ void complement_kernel(const int32_t* __restrict__ idx, int64_t n, in
 
 }  // namespace
 
+// workspace floats the bf16 split-K form needs (0: none)
+size_t lora_xl_ws_floats(int64_t T, int64_t D, int64_t r) {
+    if (T <= 0 || r <= 0) return 0;
+    const int64_t rb = ceil_div(T, XR);
+    int64_t ks = ceil_div(D, 1024);
+    if (rb * ks < 512) ks = ceil_div(512, rb);
+    if (ks > 16) ks = 16;
+    const int64_t kmax = ceil_div(D, XKC);
+    if (ks > kmax) ks = kmax;
+    const int64_t R = r <= 16 ? 16 : (r <= 32 ? 32 : 64);
+    return (size_t)(ks * T * R);
+}
+
 hipError_t launch_lora_xl(bool bf16, const void* x, int64_t ldx, int64_t T, int64_t D,
                           const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
                           float* ws, hipStream_t st) {
-    (void)ws;
     if (T <= 0) return hipSuccess;
-    if (bf16)
+    if (bf16 && ws) {
+        const int64_t rb = ceil_div(T, XR);
+        const int64_t R = r <= 16 ? 16 : (r <= 32 ? 32 : 64);
+        const int64_t ks = (int64_t)(lora_xl_ws_floats(T, D, r) / (size_t)(T * R));
+        const int64_t kchunk = ceil_div(ceil_div(D, ks), XKC) * XKC;
+        const int64_t ksn = ceil_div(D, kchunk);     // chunks actually used
+        const dim3 grid((unsigned)rb, (unsigned)ksn);
+#define XL(RR)                                                                                  \
+    hipLaunchKernelGGL((lora_xl_split_kernel<RR>), grid, dim3(256), 0, st, (const bf16_t*)x, ldx, T, \
+                       D, (const bf16_t*)A, lda, r, kchunk, ws)
+        if (R == 16) XL(16);
+        else if (R == 32) XL(32);
+        else XL(64);
+#undef XL
+        hipLaunchKernelGGL(lora_xl_reduce_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0, st,
+                           ws, ksn, T, r, R, xl, ldxl);
+    } else if (bf16) {
         hipLaunchKernelGGL(lora_xl_bf16_kernel, dim3((unsigned)ceil_div(T, 16)), dim3(XW * 64), 0, st,
                            (const bf16_t*)x, ldx, T, D, (const bf16_t*)A, lda, r, xl, ldxl);
-    else
+    } else {
         hipLaunchKernelGGL(lora_xl_f32_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0,
                            st, (const float*)x, ldx, T, D, (const float*)A, lda, r, xl, ldxl);
+    }
     return hipGetLastError();
 }
 
@@ -821,7 +980,11 @@ hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const i
                                 hipStream_t st) {
     if (npad <= 0 || Dd <= 0) return hipSuccess;
     const dim3 grid((unsigned)ceil_div(npad, 64), (unsigned)ceil_div(Dd, 64));
-    if (bf16)
+    const bool vec = lds % 8 == 0 && ldo % 8 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)out & 15) == 0;
+    if (bf16 && vec)
+        hipLaunchKernelGGL(gather_rows_t_bf16_kernel, dim3((unsigned)ceil_div(npad, 64), (unsigned)ceil_div(Dd, 128)),
+                           dim3(256), 0, st, (const bf16_t*)src, lds, idx, n, npad, Dd, (bf16_t*)out, ldo);
+    else if (bf16)
         hipLaunchKernelGGL(gather_rows_t_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)src,
                            lds, idx, n, npad, Dd, (bf16_t*)out, ldo);
     else

@@ -297,36 +297,79 @@ __global__ void qk_combine_kernel(const float* __restrict__ Q, const float* __re
 }
 
 // ---------------------------------------------------------------- top-n (radix select)
-// One 1024-thread block.  Four 8-bit passes from the most significant byte
-// find the n-th largest key K*; channels with key > K* are kept, and of the
-// channels with key == K* the lowest-indexed ones fill the remainder.  A
-// block scan writes the kept channels in ascending order.
+// One 1024-thread block; thread t owns the contiguous channel range
+// [t chunk, (t+1) chunk) and keeps up to TKR of its keys in registers.  Four
+// 8-bit passes from the most significant byte find the n-th largest key K*:
+// each wave counts into its own 256-bin histogram, the 16 histograms are summed
+// per bin, and a scan over the bins (from the top) locates the bin that holds
+// the n-th key.  Channels with key > K* are kept, and of those with key == K*
+// the lowest-indexed fill the remainder; a block scan writes the kept channels
+// in ascending order.
+constexpr int TKR = 16;
+
 __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc, int64_t C,
                                                     int64_t n, int32_t* __restrict__ idx) {
-    __shared__ unsigned hist[256];
+    __shared__ unsigned hist[16][256];
+    __shared__ unsigned tot[256];
     __shared__ int sh[32];
     __shared__ uint32_t s_prefix;
     __shared__ int64_t s_rem;
     if (n <= 0) return;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wid = tid / WAVE;
+    const int64_t chunk = (C + blockDim.x - 1) / blockDim.x;
+    const int64_t beg = (int64_t)tid * chunk;
+    const int64_t end = beg + chunk < C ? beg + chunk : C;
+    const bool inreg = chunk <= TKR;
+    uint32_t kr[TKR];
+#pragma unroll
+    for (int i = 0; i < TKR; ++i) kr[i] = (inreg && beg + i < end) ? score_key(sc[beg + i]) : 0u;
+    auto key = [&](int64_t c) -> uint32_t { return score_key(sc[c]); };
+
     uint32_t prefix = 0, pmask = 0;
     int64_t rem = n;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+        for (int i = tid; i < 16 * 256; i += blockDim.x) (&hist[0][0])[i] = 0;
         __syncthreads();
-        for (int64_t c = threadIdx.x; c < C; c += blockDim.x) {
-            uint32_t k = score_key(sc[c]);
-            if ((k & pmask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+        if (inreg) {
+#pragma unroll
+            for (int i = 0; i < TKR; ++i)
+                if (beg + i < end && (kr[i] & pmask) == prefix) atomicAdd(&hist[wid][(kr[i] >> shift) & 255u], 1u);
+        } else {
+            for (int64_t c = beg; c < end; ++c) {
+                const uint32_t k = key(c);
+                if ((k & pmask) == prefix) atomicAdd(&hist[wid][(k >> shift) & 255u], 1u);
+            }
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int64_t cum = 0;
-            int d = 0;
-            for (d = 255; d >= 0; --d) {
-                if (cum + (int64_t)hist[d] >= rem) break;
-                cum += hist[d];
+        if (tid < 256) {
+            unsigned t = 0;
+            for (int w = 0; w < 16; ++w) t += hist[w][tid];
+            tot[tid] = t;
+        }
+        __syncthreads();
+        // bins from the top: thread d < 256 handles bin 255 - d; inclusive scan over d
+        if (tid < 256) {
+            const int d = 255 - tid;
+            unsigned v = tot[d];
+            unsigned x = v;
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const unsigned y = __shfl_up(x, o, WAVE);
+                if (lane >= o) x += y;
             }
-            s_prefix = prefix | ((uint32_t)d << shift);
-            s_rem = rem - cum;
+            if (lane == WAVE - 1) sh[wid] = (int)x;
+            // wave sums of the 4 waves are combined below
+            hist[0][tid] = x;   // inclusive within the wave (hist row 0 is free now)
+        }
+        __syncthreads();
+        if (tid < 256) {
+            unsigned base = 0;
+            for (int w = 0; w < wid; ++w) base += (unsigned)sh[w];
+            const unsigned incl = base + hist[0][tid];
+            const unsigned excl = incl - tot[255 - tid];
+            if ((int64_t)excl < rem && rem <= (int64_t)incl) {
+                s_prefix = prefix | ((uint32_t)(255 - tid) << shift);
+                s_rem = rem - (int64_t)excl;
+            }
         }
         __syncthreads();
         prefix = s_prefix;
@@ -336,27 +379,29 @@ __global__ __launch_bounds__(1024) void topk_kernel(const float* __restrict__ sc
     }
     const uint32_t thr = prefix;
     const int64_t need_eq = rem;
-    const int64_t chunk = (C + blockDim.x - 1) / blockDim.x;
-    const int64_t beg = (int64_t)threadIdx.x * chunk;
-    const int64_t end = beg + chunk < C ? beg + chunk : C;
     int neq = 0;
-    for (int64_t c = beg; c < end; ++c) neq += score_key(sc[c]) == thr;
-    int tot;
-    int eq_before = block_exclusive_scan(neq, sh, &tot);
+    if (inreg) {
+#pragma unroll
+        for (int i = 0; i < TKR; ++i) neq += (beg + i < end && kr[i] == thr);
+    } else {
+        for (int64_t c = beg; c < end; ++c) neq += key(c) == thr;
+    }
+    int total;
+    const int eq_before = block_exclusive_scan(neq, sh, &total);
     int nsel = 0;
     {
         int e = eq_before;
         for (int64_t c = beg; c < end; ++c) {
-            uint32_t k = score_key(sc[c]);
+            const uint32_t k = inreg ? kr[c - beg] : key(c);
             if (k > thr) ++nsel;
             else if (k == thr) { if (e < need_eq) ++nsel; ++e; }
         }
     }
-    int pos = block_exclusive_scan(nsel, sh, &tot);
+    int pos = block_exclusive_scan(nsel, sh, &total);
     {
         int e = eq_before;
         for (int64_t c = beg; c < end; ++c) {
-            uint32_t k = score_key(sc[c]);
+            const uint32_t k = inreg ? kr[c - beg] : key(c);
             bool take = false;
             if (k > thr) take = true;
             else if (k == thr) { take = e < need_eq; ++e; }

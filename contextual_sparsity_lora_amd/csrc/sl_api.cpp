@@ -702,9 +702,15 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
                       (gb ? es * T * D_out + 4.0 * T * r : 0) + (da ? es * T * D_in : 0) +
                       (db ? es * T * D_out : 0) + (dxm ? 2 * es * T * D_in : 0);
     Timed tm(h, K_LORA, fl, by);
-    if (mode & SL_LORA_XL)
-        SL_HIP(h, launch_lora_xl(bf, x, ldx, T, D_in, A, D_in, r, xl, ldxl, nullptr, h->stream),
+    if (mode & SL_LORA_XL) {
+        float* xw = nullptr;   // split-K partials (bf16)
+        if (bf) {
+            SL_CHECK(ensure_ws(h, round_up(lora_xl_ws_floats(T, D_in, r) * 4, 256)));
+            xw = (float*)h->ws;
+        }
+        SL_HIP(h, launch_lora_xl(bf, x, ldx, T, D_in, A, D_in, r, xl, ldxl, xw, h->stream),
                "lora_xl");
+    }
     if (mode & SL_LORA_ADD)
         SL_HIP(h, launch_lora_add(bf, xl, ldxl, T, r, B, r, 1, D_out, scale, y, ldy, h->stream),
                "lora_add");
@@ -715,7 +721,9 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         const size_t bt_bytes = round_up((size_t)(r * ldbt) * esize(dt), 256);
         const size_t gb_bytes = round_up((size_t)(T > 0 ? T : 1) * r * 4, 256);
         const int64_t ncol = D_in > D_out ? D_in : D_out;
-        const size_t part_floats = (size_t)(nch * r * ncol);
+        size_t part_floats = (size_t)(nch * r * ncol);
+        const size_t xl_floats = bf ? lora_xl_ws_floats(T, D_out, r) : 0;
+        if (part_floats < xl_floats) part_floats = xl_floats;
         SL_CHECK(ensure_ws(h, bt_bytes + gb_bytes + part_floats * 4));
         char* ws = (char*)h->ws;
         void* Bt = ws;
@@ -724,8 +732,8 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         float* part = (float*)(ws + bt_bytes + gb_bytes);
         if (gb) {
             SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
-            SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, Bt, ldbt, r, gB, ldg, nullptr, h->stream),
-                   "lora_gB");
+            SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, Bt, ldbt, r, gB, ldg, bf ? part : nullptr,
+                                     h->stream), "lora_gB");
         }
         if (da)
             SL_HIP(h, launch_outer_accum(bf, gB, ldg, T, r, x, ldx, D_in, scale, dA, D_in, 1, part,

@@ -106,6 +106,8 @@ hipError_t launch_complement(const int32_t* idx, int64_t n, int64_t C, int32_t* 
 hipError_t launch_zero_unselected(bool bf16, void* y, int64_t ldy, const int32_t* rows,
                                   int64_t nrows, const int32_t* idx, int64_t n, int64_t C,
                                   uint8_t* mask_ws, hipStream_t st);
+// bf16 xl uses a split-K form when a workspace of lora_xl_ws_floats() floats is given
+size_t lora_xl_ws_floats(int64_t T, int64_t D, int64_t r);
 hipError_t launch_lora_xl(bool bf16, const void* x, int64_t ldx, int64_t T, int64_t D,
                           const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
                           float* ws, hipStream_t st);
