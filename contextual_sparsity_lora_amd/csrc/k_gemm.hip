@@ -75,6 +75,17 @@ __device__ __forceinline__ uint4 load16_guard(const bf16_t* rowp, int64_t k, int
     return v;
 }
 
+// LDS-typed float pointer: keeps accesses on ds_read / ds_write (a generic
+// pointer chosen at run time would become flat accesses)
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// Block barrier for LDS hand-offs: waits for this wave's LDS operations only
+// (lgkmcnt(0)), not for its outstanding global loads or stores.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+}
+
 // Epilogue shared by the bf16 kernels: optional rank-r term into the fp32
 // accumulators, then one rounding and the store through the row / column maps
 // (or raw fp32 partials).  Lane holds column (lane & 31) and rows
@@ -125,8 +136,7 @@ __device__ __forceinline__ void gemm_lora_term(const GemmProblem& P, f32x16 (&ac
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = (uint32_t)f32_to_bf16(P.lscale * v[2 * e]) |
-                           ((uint32_t)f32_to_bf16(P.lscale * v[2 * e + 1]) << 16);
+                    w[e] = pack_bf16x2(P.lscale * v[2 * e], P.lscale * v[2 * e + 1]);
                 a[i] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
             }
 #pragma unroll
@@ -212,7 +222,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmProblem& P, f32x16 (&acc
 template <int FM, int FN, int WTM, int WTN, int WGM, int WGN>
 __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&acc)[FM][FN],
                                                int64_t m0, int64_t n0, int wm, int wn, int lane,
-                                               int tid, float* const (&csr)[WGM]) {
+                                               int tid, lds_f32* const (&csr)[WGM]) {
     constexpr int NTH = 64 * WGM * WGN;
     constexpr int BN = WGN * WTN;
     constexpr int PR = 32 * WGM;                 // rows per pass
@@ -222,7 +232,7 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
     const bool vec = P.c_cols == nullptr && (P.ldc % 8 == 0) && (((uintptr_t)P.C & 15) == 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        __syncthreads();                          // LDS free (K loop done / previous pass read)
+        lds_barrier();                          // LDS free (K loop done / previous pass read)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -230,7 +240,7 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
                 const int r = wm * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
                 csr[wm][(r - wm * 32) * LDC + wn * WTN + j * 32 + (lane & 31)] = acc[i][j][e];
             }
-        __syncthreads();
+        lds_barrier();
         if (P.c_cols && !P.f32out) {
             // mapped columns: one element per lane, consecutive lanes on consecutive
             // columns of one row (each store instruction covers 64 columns)
@@ -252,8 +262,9 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
             const int64_t m = m0 + (r / 32) * WTM + 32 * i + (r % 32);
             const int64_t n = n0 + c8;
             if (m >= M || n >= N) continue;
-            const float* src = csr[r / 32] + (r % 32) * LDC + c8;
-            const float4 v0 = *(const float4*)src, v1 = *(const float4*)(src + 4);
+            const lds_f32* src = csr[r / 32] + (r % 32) * LDC + c8;
+            const float4 v0 = *(const __attribute__((address_space(3))) float4*)src;
+            const float4 v1 = *(const __attribute__((address_space(3))) float4*)(src + 4);
             float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
             const bool full = n + 8 <= N;
             if (P.f32out) {                       // split-K partial: raw fp32, unmapped
@@ -283,7 +294,7 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
                 uint32_t w[4];
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2)
-                    w[q2] = (uint32_t)f32_to_bf16(v[2 * q2]) | ((uint32_t)f32_to_bf16(v[2 * q2 + 1]) << 16);
+                    w[q2] = pack_bf16x2(v[2 * q2], v[2 * q2 + 1]);
                 *(uint4*)dst = make_uint4(w[0], w[1], w[2], w[3]);
             } else {
                 for (int q2 = 0; q2 < 8; ++q2) {
@@ -302,9 +313,9 @@ template <int FM, int FN, int WTM, int WTN, int WGM, int WGN>
 __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&acc)[FM][FN],
                                                int64_t m0, int64_t n0, int wm, int wn, int lane,
                                                int tid, float* cs) {
-    float* csr[WGM];
+    lds_f32* csr[WGM];
 #pragma unroll
-    for (int g = 0; g < WGM; ++g) csr[g] = cs + g * 32 * (WGN * WTN + 4);
+    for (int g = 0; g < WGM; ++g) csr[g] = (lds_f32*)cs + g * 32 * (WGN * WTN + 4);
     gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, csr);
 }
 
@@ -486,10 +497,6 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
-    __builtin_amdgcn_s_barrier();
-}
 
 template <int BM, int BN, int WGM, int WGN, int NSET>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) {
@@ -612,31 +619,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
 }
 
 // ---------------------------------------------------------------- NT main loop v5 (LDS DMA)
-// 256 x 256 tile, K in stages of 32, four LDS stages filled by buffer loads
-// that write LDS directly (buffer_load_dwordx4 ... lds): no register staging and
-// no LDS store instructions.  A load instruction of a wave fills one 1 KB slab
-// (16 rows of 64 bytes) with lane i at byte 16 i, so lane i fetches row i / 4
-// of the slab and the 8-element k-chunk that the row swizzle puts at position
-// i % 4: chunk c of row R sits at position c ^ ((R >> 1) & 3), which keeps the
-// MFMA fragment reads (8 lanes = 8 consecutive rows, same chunk) free of bank
-// conflicts.  The stages are four separate LDS arrays and the K loop is
-// unrolled by four so that every read names its stage; a wave waits for its own
-// loads of tile t (the loads of t+1, t+2 stay in flight), then one barrier per
-// stage publishes tile t and retires the reads of tile t-1, whose stage takes
-// the loads of tile t+3.
-constexpr int BK5 = 32;
-constexpr int ST5 = 17408;   // bf16 per stage array: 512 rows x 32 (32 KB), room for the store epilogue
-
+// 256 x 256 tile; K in stages of BKS (32 or 64) held in NST LDS stages (4 or 2)
+// that buffer loads fill directly (buffer_load_dwordx4 ... lds): no register
+// staging and no LDS store instructions.  A stage is 512 rows (A rows 0-255,
+// B rows 256-511) of BKS bf16, i.e. CPR 16-byte chunks per row.  One load
+// instruction of a wave fills a 1 KB slab with lane i at byte 16 i, so lane i
+// fetches row i / CPR of the slab and the k-chunk that the row swizzle puts at
+// position i % CPR: chunk c of row R sits at position c ^ ((R / (8 / CPR)) % CPR),
+// which keeps the MFMA fragment reads (8 lanes = 8 consecutive rows, same chunk)
+// free of bank conflicts.  The stages are separate LDS arrays and the K loop is
+// unrolled by NST so that every read names its stage.  Step t issues the loads
+// of tile t + NST - 1 into the stage of tile t - 1, multiplies tile t, waits
+// for this wave's loads of tile t + 1 and ends with the one barrier of the step
+// (it publishes tile t + 1 and retires the reads of tile t).
 __host__ __device__ constexpr uint16_t vmcnt_imm(int n) {
     // s_waitcnt immediate: vmcnt(n) only (expcnt, lgkmcnt at their maxima)
     return (uint16_t)((n & 15) | 0x70 | 0xF00 | ((n >> 4) << 14));
 }
 
-template <int NW, int DPT>
+template <int BKS, int NW, int DPT>
 __device__ __forceinline__ void nt5_dma(rsrc_t ra, rsrc_t rb, bf16_t* st, int64_t kt, int64_t K, int ck,
                                         int wid, const uint32_t (&goff)[DPT]) {
-    const uint32_t soff = (uint32_t)(kt * BK5 * 2);
-    const bool kin = kt * BK5 + ck * 8 < K;
+    const uint32_t soff = (uint32_t)(kt * BKS * 2);
+    const bool kin = kt * BKS + ck * 8 < K;
 #pragma unroll
     for (int d = 0; d < DPT / 2; ++d)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(st + (wid + NW * d) * 512),
@@ -647,17 +652,23 @@ __device__ __forceinline__ void nt5_dma(rsrc_t ra, rsrc_t rb, bf16_t* st, int64_
                                                  16, kin ? goff[d] : OOB_OFF, soff, 0, 0);
 }
 
-template <int WGM, int WGN>
+template <int WGM, int WGN, int BKS, int NST>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args) {
     constexpr int BM = 256, BN = 256;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
-    constexpr int DPT = 32 / NW;                 // slabs (load instructions) per wave per stage
-    static_assert(DPT * NW == 32 && DPT % 2 == 0, "32 slabs per stage: A in slabs 0-15, B in 16-31");
-    __shared__ __attribute__((aligned(16))) bf16_t s0[ST5];
-    __shared__ __attribute__((aligned(16))) bf16_t s1[ST5];
-    __shared__ __attribute__((aligned(16))) bf16_t s2[ST5];
-    __shared__ __attribute__((aligned(16))) bf16_t s3[ST5];
+    constexpr int CPR = BKS / 8;                 // 16-byte chunks per row
+    constexpr int SLABS = 512 * BKS * 2 / 1024;  // 1 KB slabs per stage
+    constexpr int DPT = SLABS / NW;              // load instructions per wave per stage
+    static_assert(DPT * NW == SLABS && DPT % 2 == 0, "A slabs first half, B slabs second half");
+    static_assert(NST == 2 || NST == 4, "two or four stages");
+    static_assert(WGM == 2, "store epilogue: one stage array per row group");
+    // a stage array also holds 32 rows x (BN + 4) fp32 of the store epilogue
+    constexpr int SZ = (512 * BKS > 32 * (BN + 4) * 2) ? 512 * BKS : 32 * (BN + 4) * 2;
+    __shared__ __attribute__((aligned(16))) bf16_t s0[SZ];
+    __shared__ __attribute__((aligned(16))) bf16_t s1[SZ];
+    __shared__ __attribute__((aligned(16))) bf16_t s2[NST == 4 ? SZ : 8];
+    __shared__ __attribute__((aligned(16))) bf16_t s3[NST == 4 ? SZ : 8];
 
     const int L = xcd_remap(blockIdx.x, gridDim.x);
     GemmProblem P;
@@ -670,31 +681,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wid % WGM, wn = wid / WGM;
 
-    // loads: slab q = wid + NW d (q < 16: A rows 16 q.., else B rows 16 (q - 16)..)
-    const int ck = (lane & 3) ^ ((lane >> 3) & 3);       // k-chunk this lane fetches
+    // loads: slab q = wid + NW d holds rows (1024 / (2 BKS)) q ..; lane i: row i / CPR of it
+    constexpr int SR = 1024 / (2 * BKS);         // rows per slab
+    const int ck = (lane % CPR) ^ (((lane / CPR) / (8 / CPR)) % CPR);   // k-chunk this lane fetches
     uint32_t goff[DPT];
 #pragma unroll
     for (int d = 0; d < DPT; ++d) {
         const int q = wid + NW * d;
-        const int64_t rr = 16 * (q & 15) + (lane >> 2);
+        const int64_t rr = SR * q + lane / CPR;            // stage row
         if (d < DPT / 2) {
             const int64_t m = m0 + rr;
             goff[d] = m < M ? (uint32_t)(((P.a_rows ? (int64_t)P.a_rows[m] : m) * P.lda + ck * 8) * 2) : OOB_OFF;
         } else {
-            const int64_t n = n0 + rr;
+            const int64_t n = n0 + rr - 256;
             goff[d] = n < N ? (uint32_t)(((P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb + ck * 8) * 2) : OOB_OFF;
         }
     }
     const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
-    const int64_t nk = (K + BK5 - 1) / BK5;
+    const int64_t nk = (K + BKS - 1) / BKS;
     const int64_t last = nk > 0 ? nk - 1 : 0;
-    auto dma = [&](bf16_t* st, int64_t kt) { nt5_dma<NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
+    auto dma = [&](bf16_t* st, int64_t kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
 
     // fragment reads: row R = base + lane % 32 (base a multiple of 32), chunk 2 ks + lane / 32
-    const int swz = ((lane & 31) >> 1) & 3;
-    const int koff0 = ((0 + (lane >> 5)) ^ swz) * 8, koff1 = ((2 + (lane >> 5)) ^ swz) * 8;
-    const int arow = (wm * WTM + (lane & 31)) * 32;
-    const int brow = (256 + wn * WTN + (lane & 31)) * 32;
+    const int swz = ((lane & 31) / (8 / CPR)) % CPR;
+    const int arow = (wm * WTM + (lane & 31)) * BKS;
+    const int brow = (256 + wn * WTN + (lane & 31)) * BKS;
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -706,13 +717,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
 
     auto compute = [&](const bf16_t* st) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int ko = ks ? koff1 : koff0;
+        for (int ks = 0; ks < BKS / 16; ++ks) {
+            const int ko = ((2 * ks + (lane >> 5)) ^ swz) * 8;
             bf16x8 a[FM], b[FN];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)&st[arow + i * 32 * 32 + ko];
+            for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)&st[arow + i * 32 * BKS + ko];
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&st[brow + j * 32 * 32 + ko];
+            for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&st[brow + j * 32 * BKS + ko];
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -722,38 +733,45 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     };
 
     if (K > 0) {
+        constexpr int INFL = (NST - 2) * DPT;     // this wave's loads allowed in flight at a step's end
         dma(s0, 0);
-        dma(s1, 1 <= last ? 1 : last);
-        dma(s2, 2 <= last ? 2 : last);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPT));
+        if (NST == 4) {
+            dma(s1, 1 <= last ? 1 : last);
+            dma(s2, 2 <= last ? 2 : last);
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));
         __builtin_amdgcn_s_barrier();
-        // step T: load tile T+3 into the stage of tile T-1, multiply tile T, then
-        // wait for this wave's loads of tile T+1 and publish it with the barrier
 #define NT5_STEP(CUR, NXT, T)                                                 \
-        dma(NXT, (T) + 3 <= last ? (T) + 3 : last);                           \
+        dma(NXT, (T) + NST - 1 <= last ? (T) + NST - 1 : last);               \
         compute(CUR);                                                         \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DPT));                       \
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));                          \
         __builtin_amdgcn_s_barrier();
-        for (int64_t kt = 0; kt < nk; kt += 4) {
-            NT5_STEP(s0, s3, kt)
-            if (kt + 1 >= nk) break;
-            NT5_STEP(s1, s0, kt + 1)
-            if (kt + 2 >= nk) break;
-            NT5_STEP(s2, s1, kt + 2)
-            if (kt + 3 >= nk) break;
-            NT5_STEP(s3, s2, kt + 3)
+        if (NST == 4) {
+            for (int64_t kt = 0; kt < nk; kt += 4) {
+                NT5_STEP(s0, s3, kt)
+                if (kt + 1 >= nk) break;
+                NT5_STEP(s1, s0, kt + 1)
+                if (kt + 2 >= nk) break;
+                NT5_STEP(s2, s1, kt + 2)
+                if (kt + 3 >= nk) break;
+                NT5_STEP(s3, s2, kt + 3)
+            }
+        } else {
+            for (int64_t kt = 0; kt < nk; kt += 2) {
+                NT5_STEP(s0, s1, kt)
+                if (kt + 1 >= nk) break;
+                NT5_STEP(s1, s0, kt + 1)
+            }
         }
 #undef NT5_STEP
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the stages are reused below
     }
     gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
-    float* csr[2];
-    csr[0] = (float*)s0;
-    csr[1] = (float*)s1;
-    static_assert(WGM == 2, "store epilogue: one stage array per row group");
+    lds_f32* csr[2];
+    csr[0] = (lds_f32*)s0;
+    csr[1] = (lds_f32*)s1;
     gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, csr);
 }
-
 
 // ---------------------------------------------------------------- fp32 (VALU)
 constexpr int FB = 64, FK = 16;
@@ -910,12 +928,12 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WGM, int WGN>
+template <int WGM, int WGN, int BKS, int NST>
 hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st) {
     GemmArgs a = make_args(probs, nprob, 256, 256);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN>), dim3(total), dim3(64 * WGM * WGN), 0, st, a);
+    hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN, BKS, NST>), dim3(total), dim3(64 * WGM * WGN), 0, st, a);
     return hipGetLastError();
 }
 
@@ -947,8 +965,10 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
             case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st);
             case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st);
             case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st);
-            case 20: return launch_nt5<2, 4>(probs, nprob, st);
-            case 21: return launch_nt5<2, 2>(probs, nprob, st);
+            case 20: return launch_nt5<2, 4, 32, 4>(probs, nprob, st);
+            case 21: return launch_nt5<2, 2, 32, 4>(probs, nprob, st);
+            case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st);
+            case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st);
             default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
         }
     }

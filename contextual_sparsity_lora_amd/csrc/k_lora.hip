@@ -46,7 +46,7 @@ template <> __device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const floa
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
     *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
 }
 template <> __device__ __forceinline__ void store8<float>(float* p, const float* v) {
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                w[q] = (uint32_t)f32_to_bf16(scale * v[2 * q]) | ((uint32_t)f32_to_bf16(scale * v[2 * q + 1]) << 16);
+                w[q] = pack_bf16x2(scale * v[2 * q], scale * v[2 * q + 1]);
             pb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
         }
 #pragma unroll

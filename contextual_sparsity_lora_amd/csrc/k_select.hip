@@ -70,6 +70,40 @@ __device__ __forceinline__ float silu_sl(float z) {
     return z / den;
 }
 
+// The same exp_sl without branches: the reduction and polynomial run on the
+// input clamped to [-104, 89] (the identity wherever their value is used) and
+// the special cases are selected afterwards, so a wave never splits.
+__device__ __forceinline__ float exp_sl_nb(float z) {
+    const float zc = __builtin_fminf(__builtin_fmaxf(z, -104.0f), 89.0f);
+    const float LOG2E = __uint_as_float(0x3FB8AA3Bu);
+    const float LN2_HI = __uint_as_float(0x3F317000u);
+    const float LN2_LO = __uint_as_float(0x3805FDF4u);
+    float t = zc * LOG2E;
+    float n = __builtin_rintf(t);
+    float r = __builtin_fmaf(-n, LN2_HI, zc);
+    r = __builtin_fmaf(-n, LN2_LO, r);
+    float p = __uint_as_float(0x39500D01u);
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3AB60B61u));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3C088889u));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3D2AAAABu));
+    p = __builtin_fmaf(p, r, __uint_as_float(0x3E2AAAABu));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    int ni = (int)n;
+    int a = ni >> 1;
+    int b = ni - a;
+    float v = (p * pow2i(a)) * pow2i(b);
+    v = z >= 89.0f ? __builtin_huge_valf() : v;
+    v = z <= -104.0f ? 0.0f : v;
+    return __builtin_isnan(z) ? z : v;
+}
+
+__device__ __forceinline__ float silu_sl_nb(float z) {
+    const float den = 1.0f + exp_sl_nb(-z);
+    return z / den;
+}
+
 __device__ __forceinline__ uint32_t score_key(float s) {
     return __builtin_isnan(s) ? 0x7FC00000u : __float_as_uint(s);
 }
@@ -128,85 +162,158 @@ __global__ __launch_bounds__(1024) void token_split_kernel(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------- stage 1
-// One wave per pair of context tokens; lane l owns the chains i = l (mod 64).
-// W_A is read in its math layout [D, kt] so a lane loads 4 j-values at once.
+// Stage 1, second form: a block of 4 waves takes S1T context tokens and 32
+// columns of W_A (8 per wave); lane l owns chain l of every (token, column)
+// pair it holds (S1T x 8 = 64 pairs).  The 64 chains of each pair then go
+// through LDS (pair-major rows, pitch 68 floats) and lane p folds pair p with
+// the pairwise tree.
+constexpr int S1T = 8, S1J = 8;
+
 template <bool BF16>
-__global__ __launch_bounds__(256) void stage1_kernel(const void* __restrict__ xv, int64_t ldx,
-                                                     const int32_t* __restrict__ rows, int64_t Tc,
-                                                     int64_t D, const float* __restrict__ WA,
-                                                     int64_t kt, float* __restrict__ xa) {
-    constexpr int TPW = 2;   // tokens per wave
-    constexpr int JC = 32;   // j-chunk held in registers
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int64_t wave = (int64_t)blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE;
-    const int64_t m0 = wave * TPW;
-    if (m0 >= Tc) return;
-    int64_t rowoff[TPW];
-    bool rv[TPW];
+__global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ xv, int64_t ldx,
+                                                      const int32_t* __restrict__ rows, int64_t Tc,
+                                                      int64_t D, const float* __restrict__ WA,
+                                                      int64_t kt, float* __restrict__ xa) {
+    __shared__ __attribute__((aligned(16))) float red[4][S1T * S1J][68];
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
+    const int64_t m0 = (int64_t)blockIdx.x * S1T;
+    const int64_t j0 = (int64_t)blockIdx.y * 32 + w * S1J;
+    // rows past Tc read a valid row (the last one) and are zeroed after the load,
+    // so every load is unconditional and the loads of an iteration overlap
+    int64_t rowoff[S1T];
+    bool tv[S1T];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        rv[t] = m0 + t < Tc;
-        rowoff[t] = rv[t] ? (int64_t)rows[m0 + t] * ldx : 0;
+    for (int t = 0; t < S1T; ++t) {
+        tv[t] = m0 + t < Tc;
+        rowoff[t] = (int64_t)rows[tv[t] ? m0 + t : Tc - 1] * ldx;
     }
-    for (int64_t jc = 0; jc < kt; jc += JC) {
-        const int jn = (int)((kt - jc) < JC ? (kt - jc) : JC);
-        float acc[TPW][JC];
+    const bool wvec = (kt % 4 == 0) && (j0 + S1J <= kt) && (((uintptr_t)WA & 15) == 0);
+    float acc[S1T][S1J];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < S1T; ++t)
 #pragma unroll
-            for (int j = 0; j < JC; ++j) acc[t][j] = 0.0f;
-        for (int64_t i = lane; i < D; i += WAVE) {
-            float xs[TPW];
+        for (int j = 0; j < S1J; ++j) acc[t][j] = 0.0f;
+#pragma unroll 2
+    for (int64_t i = lane; i < D; i += WAVE) {
+        float xs[S1T];
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                if (BF16) xs[t] = bf16_to_f32(((const bf16_t*)xv)[rowoff[t] + i]);
-                else xs[t] = ((const float*)xv)[rowoff[t] + i];
-            }
-            const float* wr = WA + i * kt + jc;
-            if (jn == JC && (kt % 4) == 0) {
+        for (int t = 0; t < S1T; ++t) {
+            const float v = BF16 ? bf16_to_f32(((const bf16_t*)xv)[rowoff[t] + i])
+                                 : ((const float*)xv)[rowoff[t] + i];
+            xs[t] = tv[t] ? v : 0.0f;
+        }
+        float wv[S1J];
+        const float* wr = WA + i * kt + j0;
+        if (wvec) {
+            const float4 a = *(const float4*)wr, b = *(const float4*)(wr + 4);
+            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
+            wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+        } else {
 #pragma unroll
-                for (int j4 = 0; j4 < JC; j4 += 4) {
-                    float4 w = *(const float4*)(wr + j4);
-#pragma unroll
-                    for (int t = 0; t < TPW; ++t) {
-                        acc[t][j4 + 0] = __builtin_fmaf(xs[t], w.x, acc[t][j4 + 0]);
-                        acc[t][j4 + 1] = __builtin_fmaf(xs[t], w.y, acc[t][j4 + 1]);
-                        acc[t][j4 + 2] = __builtin_fmaf(xs[t], w.z, acc[t][j4 + 2]);
-                        acc[t][j4 + 3] = __builtin_fmaf(xs[t], w.w, acc[t][j4 + 3]);
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < JC; ++j) {
-                    if (j < jn) {
-                        float w = wr[j];
-#pragma unroll
-                        for (int t = 0; t < TPW; ++t) acc[t][j] = __builtin_fmaf(xs[t], w, acc[t][j]);
-                    }
-                }
+            for (int j = 0; j < S1J; ++j) {
+                const float v = wr[j0 + j < kt ? j : 0];
+                wv[j] = j0 + j < kt ? v : 0.0f;
             }
         }
-        // pairwise tree over the 64 chains: p[l] = p[l] + p[l + w]
 #pragma unroll
-        for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < S1T; ++t)
 #pragma unroll
-            for (int j = 0; j < JC; ++j) {
-                float v = acc[t][j];
+            for (int j = 0; j < S1J; ++j) acc[t][j] = __builtin_fmaf(xs[t], wv[j], acc[t][j]);
+    }
 #pragma unroll
-                for (int w = 32; w >= 1; w >>= 1) {
-                    float o = __shfl_down(v, w, WAVE);
-                    v = v + o;
-                }
-                acc[t][j] = v;
-            }
-        if (lane == 0) {
+    for (int t = 0; t < S1T; ++t)
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
-                if (rv[t])
+        for (int j = 0; j < S1J; ++j) red[w][t * S1J + j][lane] = acc[t][j];
+    __syncthreads();
+    {
+        const int pr = lane;                      // pair: token pr / S1J, column pr % S1J
+        float v[64];
 #pragma unroll
-                    for (int j = 0; j < JC; ++j)
-                        if (j < jn) xa[(m0 + t) * kt + jc + j] = acc[t][j];
+        for (int l = 0; l < 64; l += 4) {
+            const float4 q = *(const float4*)&red[w][pr][l];
+            v[l] = q.x; v[l + 1] = q.y; v[l + 2] = q.z; v[l + 3] = q.w;
         }
+#pragma unroll
+        for (int s2 = 32; s2 >= 1; s2 >>= 1)
+#pragma unroll
+            for (int l = 0; l < s2; ++l) v[l] = v[l] + v[l + s2];
+        const int64_t m = m0 + pr / S1J, j = j0 + pr % S1J;
+        if (m < Tc && j < kt) xa[m * kt + j] = v[0];
+    }
+}
+
+// Stage 2 + criterion, second form (SwiGLU or L2 with K = 16 estimator
+// columns): 16 waves over 64 channels; wave w owns the token chains
+// 4w .. 4w+3.  The columns of xa the criterion reads are staged in LDS 64
+// tokens at a time (double-buffered, one barrier per chunk) and read back as
+// broadcasts; SiLU runs without branches.
+template <int CRIT>
+__global__ __launch_bounds__(1024) void ssq16_kernel(const float* __restrict__ xa, int64_t ld,
+                                                     int64_t Tc, int64_t off0,
+                                                     const float* __restrict__ WB0, int64_t off1,
+                                                     const float* __restrict__ WB1, int64_t C,
+                                                     float* __restrict__ ssq) {
+    constexpr int K = 16;
+    constexpr int NCOL = CRIT == 1 ? 2 * K : K;
+    __shared__ __attribute__((aligned(16))) float xs[2][64][NCOL];
+    __shared__ float chains[64 * 64];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t c = (int64_t)blockIdx.x * WAVE + lane;
+    const int64_t cc = c < C ? c : C - 1;
+    float wg[K], wu[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        wg[j] = WB0[(int64_t)j * C + cc];
+        wu[j] = CRIT == 1 ? WB1[(int64_t)j * C + cc] : 0.0f;
+    }
+    auto stage = [&](int buf, int64_t mb) {
+        for (int q = tid; q < 64 * NCOL; q += 1024) {
+            const int r = q / NCOL, k = q % NCOL;
+            const int64_t m = mb + r;
+            const int64_t col = k < K ? off0 + k : off1 + (k - K);
+            xs[buf][r][k] = m < Tc ? xa[m * ld + col] : 0.0f;
+        }
+    };
+    float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int64_t nchunk = (Tc + 63) / 64;
+    if (nchunk > 0) stage(0, 0);
+    __syncthreads();
+    for (int64_t ch = 0; ch < nchunk; ++ch) {
+        const int buf = (int)(ch & 1);
+        if (ch + 1 < nchunk) stage(buf ^ 1, (ch + 1) * 64);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = 4 * w + q;
+            const int64_t m = ch * 64 + r;
+            if (m >= Tc) continue;
+            const float* row = &xs[buf][r][0];
+            float g = 0.0f;
+#pragma unroll
+            for (int j = 0; j < K; ++j) g = __builtin_fmaf(row[j], wg[j], g);
+            float v = g;
+            if (CRIT == 1) {
+                float u = 0.0f;
+#pragma unroll
+                for (int j = 0; j < K; ++j) u = __builtin_fmaf(row[K + j], wu[j], u);
+                v = silu_sl_nb(g) * u;
+            }
+            p[q] = __builtin_fmaf(v, v, p[q]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) chains[(4 * w + q) * 64 + lane] = p[q];
+    __syncthreads();
+    if (w == 0) {
+        float v[64];
+#pragma unroll
+        for (int l = 0; l < 64; ++l) v[l] = chains[l * 64 + lane];
+#pragma unroll
+        for (int s2 = 32; s2 >= 1; s2 >>= 1)
+#pragma unroll
+            for (int l = 0; l < s2; ++l) v[l] = v[l] + v[l + s2];
+        if (c < C) ssq[c] = v[0];
     }
 }
 
@@ -455,14 +562,11 @@ hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int
 hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* rows, int64_t Tc,
                          int64_t D, const float* WA, int64_t kt, float* xa, hipStream_t st) {
     if (Tc <= 0) return hipSuccess;
-    const int64_t waves = ceil_div(Tc, 2);
-    const int64_t blocks = ceil_div(waves, 4);
+    const dim3 grid((unsigned)ceil_div(Tc, S1T), (unsigned)ceil_div(kt, 32));
     if (bf16)
-        hipLaunchKernelGGL(stage1_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx,
-                           rows, Tc, D, WA, kt, xa);
+        hipLaunchKernelGGL(stage1b_kernel<true>, grid, dim3(256), 0, st, x, ldx, rows, Tc, D, WA, kt, xa);
     else
-        hipLaunchKernelGGL(stage1_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, x, ldx,
-                           rows, Tc, D, WA, kt, xa);
+        hipLaunchKernelGGL(stage1b_kernel<false>, grid, dim3(256), 0, st, x, ldx, rows, Tc, D, WA, kt, xa);
     return hipGetLastError();
 }
 
@@ -474,13 +578,16 @@ hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t
 #define SSQ_LAUNCH(CR, KK)                                                                       \
     hipLaunchKernelGGL((ssq_kernel<CR, KK>), grid, block, 0, st, xa, ld, Tc, off0, WB0, off1, WB1, \
                        kr, C, ssq)
-    if (crit == 0) {
+    if (k == 16) {
+        if (crit == 0)
+            hipLaunchKernelGGL(ssq16_kernel<0>, grid, dim3(1024), 0, st, xa, ld, Tc, off0, WB0, off1, WB1, C, ssq);
+        else
+            hipLaunchKernelGGL(ssq16_kernel<1>, grid, dim3(1024), 0, st, xa, ld, Tc, off0, WB0, off1, WB1, C, ssq);
+    } else if (crit == 0) {
         if (k == 8) SSQ_LAUNCH(0, 8);
-        else if (k == 16) SSQ_LAUNCH(0, 16);
         else SSQ_LAUNCH(0, 0);
     } else {
         if (k == 8) SSQ_LAUNCH(1, 8);
-        else if (k == 16) SSQ_LAUNCH(1, 16);
         else SSQ_LAUNCH(1, 0);
     }
 #undef SSQ_LAUNCH

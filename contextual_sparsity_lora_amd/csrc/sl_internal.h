@@ -32,12 +32,15 @@ struct sl_handle {
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
-// round to nearest even (NaN kept quiet)
+// round to nearest even (the gfx950 conversion instruction, v_cvt_pk_bf16_f32)
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+    return __builtin_bit_cast(bf16_t, (__bf16)f);
+}
+// two values rounded to bf16 in one instruction: lo in bits 0-15, hi in 16-31
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t h = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // ---------------------------------------------------------------- launchers
