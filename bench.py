@@ -29,7 +29,46 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_nt_ffn_llama3_8b_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "contextual_sparsity_lora_amd", "csrc", f)
+                  for f in ("k_gemm.hip", "sl_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the dominant GEMM kernel from the committed
+    rocprofv3 counter summary, or None when that summary is missing or was
+    taken on a different version of the kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic:"):
+            for kv in line[len("traffic:"):].split():
+                k, _, v = kv.partition("=")
+                vals[k] = v
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def build_block(inp, cfg, dense):
@@ -132,9 +171,12 @@ def main():
     dn, dms, dfl, dby = ops.timing_query(0, dom)
     if dom.startswith("gemm"):
         achieved = dfl / (dms * 1e-3) / 1e12
+        tr = measured_traffic()
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": round(tr) if tr is not None else None,
+                "algorithmic_bytes_per_launch": round(dby / dn),
                 "launches": dn, "avg_launch_ms": round(dms / dn, 4)}
     else:
         achieved = dby / (dms * 1e-3) / 1e9
@@ -180,6 +222,12 @@ def main():
         "cpu_baseline": None,
     }
     out.update(extra)
+    if args.calibrate_copy:
+        src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg)
         print(f"[bench] cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s", file=sys.stderr,
