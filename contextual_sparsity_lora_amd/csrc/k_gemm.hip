@@ -263,15 +263,16 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
             const int64_t n = n0 + c8;
             if (m >= M || n >= N) continue;
             const lds_f32* src = csr[r / 32] + (r % 32) * LDC + c8;
-            const float4 v0 = *(const __attribute__((address_space(3))) float4*)src;
-            const float4 v1 = *(const __attribute__((address_space(3))) float4*)(src + 4);
-            float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            typedef float f32x4n __attribute__((ext_vector_type(4)));
+            const f32x4n v0 = *(const __attribute__((address_space(3))) f32x4n*)src;
+            const f32x4n v1 = *(const __attribute__((address_space(3))) f32x4n*)(src + 4);
+            float v[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
             const bool full = n + 8 <= N;
             if (P.f32out) {                       // split-K partial: raw fp32, unmapped
                 float* dst = (float*)P.C + m * P.ldc + n;
                 if (full && (P.ldc % 4 == 0) && (((uintptr_t)P.C & 15) == 0)) {
-                    *(float4*)dst = v0;
-                    *(float4*)(dst + 4) = v1;
+                    *(float4*)dst = make_float4(v[0], v[1], v[2], v[3]);
+                    *(float4*)(dst + 4) = make_float4(v[4], v[5], v[6], v[7]);
                 } else {
                     for (int q2 = 0; q2 < 8; ++q2)
                         if (n + q2 < N) dst[q2] = v[q2];

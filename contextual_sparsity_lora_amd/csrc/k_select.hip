@@ -549,9 +549,23 @@ __global__ void stack_index_kernel(const int32_t* __restrict__ idx, int64_t n, i
     out[p] = (int32_t)(idx[q] + b * C);
 }
 
+__global__ void offset_index_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t offset,
+                                    int32_t* __restrict__ out) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < n) out[p] = (int32_t)(idx[p] + offset);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
+hipError_t launch_offset_index(const int32_t* idx, int64_t n, int64_t offset, int32_t* out,
+                               hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(offset_index_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, idx, n,
+                       offset, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int64_t Tc,
                               int32_t* out, int64_t To, int* flag, hipStream_t st) {
     hipLaunchKernelGGL(token_split_kernel, dim3(1), dim3(1024), 0, st, roles, T, ctx, Tc, out, To,

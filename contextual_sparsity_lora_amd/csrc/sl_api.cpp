@@ -411,6 +411,16 @@ sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
     return hip_check(h, launch_stack_index(idx, n, C, copies, idx_out, h->stream), "stack_index");
 }
 
+sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t offset,
+                          int64_t C_max, int32_t* idx_out) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, n >= 0 && offset >= 0 && C_max >= 0 && offset + C_max <= INT32_MAX, "bad sizes");
+    if (n == 0) return SL_OK;
+    SL_REQUIRE(h, idx && idx_out, "NULL pointer");
+    DeviceGuard g(h->device);
+    return hip_check(h, launch_offset_index(idx, n, offset, idx_out, h->stream), "offset_index");
+}
+
 // ---------------------------------------------------------------- a6/a7
 static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem* p, int np) {
     Timed tm(h, dt == SL_BF16 ? (nn ? K_GEMM_NN : K_GEMM_NT) : K_GEMM_F32, gemm_flops(p, np),

@@ -88,6 +88,8 @@ hipError_t launch_qk_combine(const float* ssqQ, const float* ssqK, int64_t H_kv,
 hipError_t launch_topk(const float* scores, int64_t C, int64_t n, int32_t* idx, hipStream_t st);
 hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64_t d,
                              int32_t* out, hipStream_t st);
+hipError_t launch_offset_index(const int32_t* idx, int64_t n, int64_t offset, int32_t* out,
+                              hipStream_t st);
 hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t copies,
                               int32_t* out, hipStream_t st);
 // out[m, q] = in[rows[m], cols[q]] for q < ncols, 0 for ncols <= q < npad

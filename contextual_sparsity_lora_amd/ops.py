@@ -158,6 +158,13 @@ def stack_index(idx, C, copies, idx_out):
     _check(h, st, "sl_stack_index")
 
 
+def offset_index(idx, offset, C_max, idx_out):
+    """idx_out[q] = idx[q] + offset (idx_out may be a slice of a larger list)."""
+    h = handle(_dev(idx))
+    st = _lib.load().sl_offset_index(h, _ptr(idx), idx.numel(), int(offset), int(C_max), _ptr(idx_out))
+    _check(h, st, "sl_offset_index")
+
+
 def _lora_args(lora):
     """lora = (P fp32 [T, >= r], Bm [C, >= r], r, scale) or None."""
     if lora is None:

@@ -196,6 +196,17 @@ sl_status sl_expand_gqa(sl_handle* h, const int32_t* idx_kv, int64_t n, int64_t 
 sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
                          int64_t copies, int32_t* idx_out);
 
+/* Channel numbers of one projection inside a stack of projections with their
+ * own selections (q | k | v in one stacked product, PG §3.4 "QK projection
+ * sparsity" and "VO projection sparsity"): idx_out[q] = idx[q] + offset, the
+ * offset being the number of rows stacked above this projection.  idx_out
+ * device int32[n] (may be a slice of a larger index list); n = 0 is a no-op;
+ * SL_ERR_INVALID if offset < 0 or a shifted value could exceed INT32_MAX
+ * (checked as offset + C_max with C_max = max_channel + 1 supplied by the
+ * caller). */
+sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t offset,
+                          int64_t C_max, int32_t* idx_out);
+
 /* ---------------------------------------------------------------- a6/a7: main forward */
 
 /* Sparse main-branch forward (PG §3.4 Algorithm 1 steps 4-5 and "Token
