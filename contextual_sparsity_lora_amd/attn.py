@@ -1,0 +1,149 @@
+"""The contextually-sparse q/k/v/o projections of one attention layer (GQA
+allowed) with dense LoRA on all four: forward and backward of the frozen main
+branch as a sequence of library calls.
+
+Pages ("SparseLoRA: Accelerating LLM Fine-Tuning with Contextual Sparsity"),
+paper-graph summary: §3.4 "QK projection sparsity" (channels scored by the
+product of the query and key norms over context tokens; q and k keep the same
+channels), "VO projection sparsity" (channels scored by the norm of the
+values; v keeps them as outputs and o as inputs), Algorithm 1 (estimate,
+score, keep the top ceil(r C), sliced products, dense LoRA), "Token
+Sensitivity" (output tokens dense).  Under grouped-query attention the
+selection is made in key/value channel space and each kept channel carries its
+group's query heads (the query-norm term sums the group's heads).
+
+Layout in device memory (allocated once, reused every step):
+  W_qkv  [Cq + 2 Ckv, D]  q rows, then k rows, then v rows (nn.Linear layout)
+  W_qkvT [D, Cq + 2 Ckv]  its transposed copy (backward products)
+  W_o    [D, Cq], Wt_o [Cq, D]
+  A_qkv  [3r, D]; B_bd [Cq + 2 Ckv, 3r] block diagonal (q, k, v blocks), so one
+         rank-3r term serves the stacked product
+  WA     [D, 3k] estimator W_A of q, k, v side by side (fp32); WB_* [k, C*]
+  qkv    [T, Cq + 2 Ckv]  q | k | v (main + LoRA); o [T, D]
+Everything below is marshalling: each step is one C-ABI call.
+"""
+import torch
+
+from . import ops
+from .ffn import keep_count
+
+
+class SparseAttnProj:
+    def __init__(self, W_q, W_k, W_v, W_o, A_q, B_q, A_k, B_k, A_v, B_v, A_o, B_o, WA_qkv,
+                 WB_q, WB_k, WB_v, scale, n_kv_heads, head_dim, qk_sparsity=(1, 2),
+                 vo_sparsity=(1, 2), dense=False):
+        dev = W_q.device
+        self.dtype = W_q.dtype
+        self.Cq, self.D = W_q.shape
+        self.Ckv = W_k.shape[0]
+        self.d = head_dim
+        self.n_rep = self.Cq // self.Ckv
+        assert self.Cq == self.n_rep * self.Ckv and self.Ckv == n_kv_heads * head_dim
+        self.r = A_q.shape[0]
+        self.k = WB_q.shape[0]
+        self.scale = float(scale)
+        self.dense = dense
+        self.n_qk = self.Ckv if dense else keep_count(self.Ckv, *qk_sparsity)
+        self.n_vo = self.Ckv if dense else keep_count(self.Ckv, *vo_sparsity)
+        Cq, Ckv, r = self.Cq, self.Ckv, self.r
+        self.Cs = Cq + 2 * Ckv
+        self.W_qkv = torch.cat([W_q, W_k, W_v], 0).contiguous()
+        self.W_qkvT = torch.empty(self.D, self.Cs, dtype=self.dtype, device=dev)
+        ops.transpose(self.W_qkv, self.W_qkvT)
+        self.W_o = W_o.contiguous()
+        self.Wt_o = torch.empty(Cq, self.D, dtype=self.dtype, device=dev)
+        ops.transpose(self.W_o, self.Wt_o)
+        self.A_qkv = torch.cat([A_q, A_k, A_v], 0).contiguous()
+        self.B_bd = torch.zeros(self.Cs, 3 * r, dtype=self.dtype, device=dev)
+        self.B_bd[:Cq, :r] = B_q
+        self.B_bd[Cq:Cq + Ckv, r:2 * r] = B_k
+        self.B_bd[Cq + Ckv:, 2 * r:] = B_v
+        self.A_o, self.B_o = A_o.contiguous(), B_o.contiguous()
+        self.A_qkvT = torch.empty(self.D, 3 * r, dtype=self.dtype, device=dev)
+        self.A_oT = torch.empty(Cq, r, dtype=self.dtype, device=dev)
+        self.WA = WA_qkv.contiguous()                  # [D, 3k] fp32
+        self.WB_q, self.WB_k, self.WB_v = (w.contiguous() for w in (WB_q, WB_k, WB_v))
+        self._T = None
+
+    def _alloc(self, T, T_c, T_o, dev):
+        if self._T == (T, T_c, T_o):
+            return
+        Cq, Ckv, r, k, dt, D = self.Cq, self.Ckv, self.r, self.k, self.dtype, self.D
+        e = lambda *s, **kw: torch.empty(*s, device=dev, **kw)
+        i32, f32 = torch.int32, torch.float32
+        self.ctx_rows, self.out_rows = e(T_c, dtype=i32), e(T_o, dtype=i32)
+        self.xa = e(T_c, 3 * k, dtype=f32)
+        self.scores = e(Ckv, dtype=f32)
+        self.idx_qk, self.idx_vo = e(self.n_qk, dtype=i32), e(self.n_vo, dtype=i32)
+        self.idx_q = e(self.n_qk * self.n_rep, dtype=i32)
+        self.idx_o = e(self.n_vo * self.n_rep, dtype=i32)
+        self.idx_qkv = e(self.n_qk * self.n_rep + self.n_qk + self.n_vo, dtype=i32)
+        if self.dense:
+            torch.arange(self.Cs, out=self.idx_qkv)
+            torch.arange(Cq, out=self.idx_o)
+        self.qkv = e(T, self.Cs, dtype=dt)
+        self.o = e(T, D, dtype=dt)
+        self.xl_qkv = e(T, 3 * r, dtype=f32)
+        self.xl_o = e(T, r, dtype=f32)
+        self.dx = e(T, D, dtype=dt)
+        self.dx_o = e(T, Cq, dtype=dt)
+        self.dA_qkv = e(3 * r, D, dtype=f32)
+        self.dA_q, self.dA_k, self.dA_v = self.dA_qkv[:r], self.dA_qkv[r:2 * r], self.dA_qkv[2 * r:]
+        self.dB_q, self.dB_k, self.dB_v = e(Cq, r, dtype=f32), e(Ckv, r, dtype=f32), e(Ckv, r, dtype=f32)
+        self.dA_o, self.dB_o = e(r, Cq, dtype=f32), e(D, r, dtype=f32)
+        self.gB_qkv, self.gB_o = e(T, 3 * r, dtype=f32), e(T, r, dtype=f32)
+        self._T = (T, T_c, T_o)
+
+    def select(self):
+        """QK and VO selections from the estimator on the context tokens, their
+        GQA expansions and the stacked q|k|v channel list."""
+        k, Ckv, Cq = self.k, self.Ckv, self.Cq
+        ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
+        ops.score_select("qk", self.xa, self.WB_q, self.WB_k, self.n_qk, self.idx_qk,
+                         scores=self.scores, off0=0, off1=k, C=Ckv, n_rep=self.n_rep,
+                         head_dim=self.d)
+        ops.score_select("l2", self.xa, self.WB_v, None, self.n_vo, self.idx_vo, scores=self.scores,
+                         off0=2 * k)
+        ops.expand_gqa(self.idx_qk, self.n_rep, self.d, self.idx_q)
+        ops.expand_gqa(self.idx_vo, self.n_rep, self.d, self.idx_o)
+        nq = self.idx_q.numel()
+        ops.offset_index(self.idx_q, 0, Cq, self.idx_qkv[:nq])
+        ops.offset_index(self.idx_qk, Cq, Ckv, self.idx_qkv[nq:nq + self.n_qk])
+        ops.offset_index(self.idx_vo, Cq + Ckv, Ckv, self.idx_qkv[nq + self.n_qk:])
+
+    def forward(self, x, x_o, roles, T_c):
+        T = x.shape[0]
+        r = self.r
+        self._alloc(T, T_c, T - T_c, x.device)
+        self.x, self.x_o = x, x_o
+        ops.token_split(roles, self.ctx_rows, self.out_rows)
+        if not self.dense:
+            self.select()
+        ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
+        ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
+                              self.qkv, lora=(self.xl_qkv, self.B_bd, 3 * r, self.scale))
+        ops.lora_fwd_bwd(ops.LORA_XL, x_o, self.A_o, None, self.scale, self.xl_o)
+        ops.sparse_linear_fwd("in", x_o, self.W_o, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
+                              self.o, lora=(self.xl_o, self.B_o, r, self.scale))
+        return self.qkv, self.o
+
+    def backward(self, dqkv, dy_o):
+        """dqkv [T, Cq + 2 Ckv]: gradients of q | k | v; dy_o [T, D]."""
+        Cq, Ckv, r, s = self.Cq, self.Ckv, self.r, self.scale
+        # q|k|v: gB and dA through the block-diagonal B, dB per projection
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA, self.x, None, self.B_bd, s, None, dy=dqkv,
+                         dA=self.dA_qkv, gB=self.gB_qkv, D_in=self.D)
+        parts = ((self.dB_q, 0, Cq), (self.dB_k, Cq, Cq + Ckv), (self.dB_v, Cq + Ckv, self.Cs))
+        for i, (dB, c0, c1) in enumerate(parts):
+            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_qkv[:, i * r:(i + 1) * r],
+                             dy=dqkv[:, c0:c1], dB=dB, r=r, D_in=self.D)
+        ops.transpose(self.A_qkv, self.A_qkvT)
+        ops.sparse_linear_bwd("out", dqkv, self.W_qkv, self.W_qkvT, self.ctx_rows, self.out_rows,
+                              self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s))
+        # o: gB, dA, dB; then dx_o (input side: kept channels only) with the LoRA term fused
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.x_o, None, self.B_o, s,
+                         self.xl_o, dy=dy_o, dA=self.dA_o, dB=self.dB_o, gB=self.gB_o, D_in=Cq)
+        ops.transpose(self.A_o, self.A_oT)
+        ops.sparse_linear_bwd("in", dy_o, None, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
+                              self.dx_o, lora=(self.gB_o, self.A_oT, r, s))
+        return self.dx, self.dx_o

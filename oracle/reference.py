@@ -174,6 +174,53 @@ def ffn_block_bwd(inp, fwd, idx, dy=None):
                 dB_up=dB_u, dA_down=dA_d, dB_down=dB_d)
 
 
+def attn_proj_indices(idx_qk, idx_vo, n_rep, head_dim):
+    """Per-projection channel selections of the q/k/v/o projections from the two
+    key/value-space selections (paper-graph summary §3.4 "QK projection
+    sparsity": q and k keep the same channels, here the key channels and their
+    query-head expansion under GQA; "VO projection sparsity": v keeps the
+    selected value channels and o the same channels on its input side, which
+    runs over the query heads).  Returns dict q, k, v (output side) and o
+    (input side)."""
+    return {"q": expand_gqa(idx_qk, n_rep, head_dim), "k": np.asarray(idx_qk, np.int32),
+            "v": np.asarray(idx_vo, np.int32), "o": expand_gqa(idx_vo, n_rep, head_dim)}
+
+
+def attn_proj_fwd(inp, idx_qk, idx_vo, n_rep, head_dim):
+    """Forward of the sparse q, k, v (output side, input x) and o (input side,
+    input x_o) projections with dense LoRA on all four (Algorithm 1 steps 4-6,
+    "Token Sensitivity": output tokens dense)."""
+    x, xo, roles, s = inp["x"], inp["x_o"], inp["roles"], inp["scale"]
+    sel = attn_proj_indices(idx_qk, idx_vo, n_rep, head_dim)
+    out = {}
+    for p in "qkv":
+        xl, lp = lora_fwd(x, inp["A_" + p], inp["B_" + p], s)
+        out[p] = sparse_linear_fwd("out", x, inp["W_" + p], roles, sel[p]) + lp
+        out["xl_" + p] = xl
+    xl, lo = lora_fwd(xo, inp["A_o"], inp["B_o"], s)
+    out["o"] = sparse_linear_fwd("in", xo, inp["W_o"], roles, sel["o"]) + lo
+    out["xl_o"] = xl
+    return out
+
+
+def attn_proj_bwd(inp, fwd, idx_qk, idx_vo, n_rep, head_dim):
+    """Backward of ``attn_proj_fwd`` for upstream gradients dy_q, dy_k, dy_v,
+    dy_o: dx (sum over q, k, v), dx_o, and the LoRA gradients of all four."""
+    x, xo, roles, s = inp["x"], inp["x_o"], inp["roles"], inp["scale"]
+    sel = attn_proj_indices(idx_qk, idx_vo, n_rep, head_dim)
+    res = {}
+    dx = np.zeros(np.shape(x), f64)
+    for p in "qkv":
+        dy = inp["dy_" + p]
+        dxl, dA, dB = lora_bwd(x, fwd["xl_" + p], dy, inp["A_" + p], inp["B_" + p], s)
+        dx = dx + sparse_linear_bwd("out", dy, inp["W_" + p], roles, sel[p]) + dxl
+        res["dA_" + p], res["dB_" + p] = dA, dB
+    dxl, dA, dB = lora_bwd(xo, fwd["xl_o"], inp["dy_o"], inp["A_o"], inp["B_o"], s)
+    res["dx_o"] = sparse_linear_bwd("in", inp["dy_o"], inp["W_o"], roles, sel["o"]) + dxl
+    res["dA_o"], res["dB_o"], res["dx"] = dA, dB, dx
+    return res
+
+
 def max_abs_rel(got, ref):
     """max |got - ref| / max(max |ref|, 1e-30), per tensor."""
     got, ref = np.asarray(got, f64), np.asarray(ref, f64)

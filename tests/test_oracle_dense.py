@@ -221,3 +221,75 @@ def test_full_rank_factors_reconstruct(rng):
     W = rng.standard_normal((30, 20)).astype(np.float32)
     WA_t, WB = svd_factor_pair(W, 20)
     assert np.allclose(WA_t.T.astype(np.float64) @ WB, W.T, atol=1e-5)
+
+
+def _attn_small(rng, Hq=4, Hkv=2, d=3, D=10, T=14, r=2):
+    roles = np.zeros(T, np.uint8)
+    roles[T - 4:] = 1
+    Cq, Ckv = Hq * d, Hkv * d
+    inp = {"x": rng.standard_normal((T, D)), "x_o": rng.standard_normal((T, Cq)), "roles": roles,
+           "scale": 2.0, "W_q": rng.standard_normal((Cq, D)), "W_k": rng.standard_normal((Ckv, D)),
+           "W_v": rng.standard_normal((Ckv, D)), "W_o": rng.standard_normal((D, Cq))}
+    for p, (cin, cout) in {"q": (D, Cq), "k": (D, Ckv), "v": (D, Ckv), "o": (Cq, D)}.items():
+        inp["A_" + p] = rng.standard_normal((r, cin))
+        inp["B_" + p] = rng.standard_normal((cout, r))
+    for p, c in {"q": Cq, "k": Ckv, "v": Ckv, "o": D}.items():
+        inp["dy_" + p] = rng.standard_normal((T, c))
+    idx_qk = np.sort(rng.choice(Ckv, 3, replace=False)).astype(np.int32)
+    idx_vo = np.sort(rng.choice(Ckv, 4, replace=False)).astype(np.int32)
+    return inp, idx_qk, idx_vo, Hq // Hkv, d
+
+
+def test_attn_projections_match_autograd_with_gqa_masks(rng):
+    """q/k/v/o composition against torch autograd on masks built another way:
+    the query-head keep mask is the key mask repeated over each group's heads
+    (repeat_interleave), not the index arithmetic of expand_gqa."""
+    inp, idx_qk, idx_vo, n_rep, d = _attn_small(rng)
+    fwd = ref.attn_proj_fwd(inp, idx_qk, idx_vo, n_rep, d)
+    bwd = ref.attn_proj_bwd(inp, fwd, idx_qk, idx_vo, n_rep, d)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
+    lin = torch.nn.functional.linear
+    s = inp["scale"]
+    ctx = torch.tensor(inp["roles"] == 0)[:, None]
+    Ckv = inp["W_k"].shape[0]
+
+    def kv_keep(idx):
+        m = torch.zeros(Ckv, dtype=torch.float64)
+        m[torch.tensor(idx, dtype=torch.long)] = 1.0
+        return m
+
+    def q_keep(idx):
+        return kv_keep(idx).view(-1, d).repeat_interleave(n_rep, dim=0).reshape(-1)
+
+    masks = {"q": q_keep(idx_qk), "k": kv_keep(idx_qk), "v": kv_keep(idx_vo)}
+    outs = {}
+    for p in "qkv":
+        y = lin(t["x"], t["W_" + p])
+        y = torch.where(ctx, y * masks[p], y) + s * lin(lin(t["x"], t["A_" + p]), t["B_" + p])
+        outs[p] = y
+        assert np.allclose(y.detach().numpy(), fwd[p], rtol=1e-12, atol=1e-12), p
+    mo = q_keep(idx_vo)
+    xo = torch.where(ctx, t["x_o"] * mo, t["x_o"])
+    o = lin(xo, t["W_o"]) + s * lin(lin(t["x_o"], t["A_o"]), t["B_o"])
+    assert np.allclose(o.detach().numpy(), fwd["o"], rtol=1e-12, atol=1e-12)
+    loss = sum((outs[p] * t["dy_" + p]).sum() for p in "qkv") + (o * t["dy_o"]).sum()
+    loss.backward()
+    assert np.allclose(t["x"].grad.numpy(), bwd["dx"], rtol=1e-10, atol=1e-12)
+    assert np.allclose(t["x_o"].grad.numpy(), bwd["dx_o"], rtol=1e-10, atol=1e-12)
+    for p in "qkvo":
+        assert np.allclose(t["A_" + p].grad.numpy(), bwd["dA_" + p], rtol=1e-10, atol=1e-12), p
+        assert np.allclose(t["B_" + p].grad.numpy(), bwd["dB_" + p], rtol=1e-10, atol=1e-12), p
+
+
+def test_attn_projections_all_kept_are_dense(rng):
+    inp, _, _, n_rep, d = _attn_small(rng)
+    Ckv = inp["W_k"].shape[0]
+    allk = np.arange(Ckv, dtype=np.int32)
+    fwd = ref.attn_proj_fwd(inp, allk, allk, n_rep, d)
+    s = inp["scale"]
+    for p in "qkv":
+        dense = inp["x"] @ inp["W_" + p].T + s * (inp["x"] @ inp["A_" + p].T) @ inp["B_" + p].T
+        assert np.allclose(fwd[p], dense, rtol=1e-12, atol=1e-12)
+    dense_o = inp["x_o"] @ inp["W_o"].T + s * (inp["x_o"] @ inp["A_o"].T) @ inp["B_o"].T
+    assert np.allclose(fwd["o"], dense_o, rtol=1e-12, atol=1e-12)
