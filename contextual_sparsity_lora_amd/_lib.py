@@ -50,6 +50,14 @@ SIGNATURES = {
     "sl_swiglu_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
                             _vp, _i64]),
     "sl_transpose": (_st, [_vp, _int, _vp, _i64, _i64, _i64, _vp, _i64]),
+    "sl_rmsnorm_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _f, _vp, _i64, _vp, _i64,
+                             _vp]),
+    "sl_rmsnorm_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),
+    "sl_add": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),
+    "sl_attention_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64,
+                               _i64, _vp, _i64, _vp]),
+    "sl_attention_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                               _i64, _i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]),
 }
 
 _lib = None

@@ -111,26 +111,49 @@ class SparseAttnProj:
         ops.offset_index(self.idx_qk, Cq, Ckv, self.idx_qkv[nq:nq + self.n_qk])
         ops.offset_index(self.idx_vo, Cq + Ckv, Ckv, self.idx_qkv[nq + self.n_qk:])
 
-    def forward(self, x, x_o, roles, T_c):
+    def forward_qkv(self, x, roles, T_c):
+        """Token split, selection and the stacked q|k|v product (main + LoRA)."""
         T = x.shape[0]
         r = self.r
         self._alloc(T, T_c, T - T_c, x.device)
-        self.x, self.x_o = x, x_o
+        self.x = x
         ops.token_split(roles, self.ctx_rows, self.out_rows)
         if not self.dense:
             self.select()
         ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
         ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
                               self.qkv, lora=(self.xl_qkv, self.B_bd, 3 * r, self.scale))
+        return self.qkv
+
+    def forward_o(self, x_o):
+        """The o projection (input side: kept channels only on context rows)."""
+        r = self.r
+        self.x_o = x_o
         ops.lora_fwd_bwd(ops.LORA_XL, x_o, self.A_o, None, self.scale, self.xl_o)
         ops.sparse_linear_fwd("in", x_o, self.W_o, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
                               self.o, lora=(self.xl_o, self.B_o, r, self.scale))
+        return self.o
+
+    def forward(self, x, x_o, roles, T_c):
+        self.forward_qkv(x, roles, T_c)
+        self.forward_o(x_o)
         return self.qkv, self.o
 
-    def backward(self, dqkv, dy_o):
-        """dqkv [T, Cq + 2 Ckv]: gradients of q | k | v; dy_o [T, D]."""
+    def backward_o(self, dy_o):
+        """o: LoRA gB, dA, dB; then dx_o (input side: kept channels only) with
+        the LoRA term fused."""
+        r, s = self.r, self.scale
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.x_o, None, self.B_o, s,
+                         self.xl_o, dy=dy_o, dA=self.dA_o, dB=self.dB_o, gB=self.gB_o, D_in=self.Cq)
+        ops.transpose(self.A_o, self.A_oT)
+        ops.sparse_linear_bwd("in", dy_o, None, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
+                              self.dx_o, lora=(self.gB_o, self.A_oT, r, s))
+        return self.dx_o
+
+    def backward_qkv(self, dqkv):
+        """dqkv [T, Cq + 2 Ckv]: gradients of q | k | v.  gB and dA through the
+        block-diagonal B, dB per projection, then dx with the LoRA term fused."""
         Cq, Ckv, r, s = self.Cq, self.Ckv, self.r, self.scale
-        # q|k|v: gB and dA through the block-diagonal B, dB per projection
         ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA, self.x, None, self.B_bd, s, None, dy=dqkv,
                          dA=self.dA_qkv, gB=self.gB_qkv, D_in=self.D)
         parts = ((self.dB_q, 0, Cq), (self.dB_k, Cq, Cq + Ckv), (self.dB_v, Cq + Ckv, self.Cs))
@@ -140,10 +163,9 @@ class SparseAttnProj:
         ops.transpose(self.A_qkv, self.A_qkvT)
         ops.sparse_linear_bwd("out", dqkv, self.W_qkv, self.W_qkvT, self.ctx_rows, self.out_rows,
                               self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s))
-        # o: gB, dA, dB; then dx_o (input side: kept channels only) with the LoRA term fused
-        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.x_o, None, self.B_o, s,
-                         self.xl_o, dy=dy_o, dA=self.dA_o, dB=self.dB_o, gB=self.gB_o, D_in=Cq)
-        ops.transpose(self.A_o, self.A_oT)
-        ops.sparse_linear_bwd("in", dy_o, None, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
-                              self.dx_o, lora=(self.gB_o, self.A_oT, r, s))
+        return self.dx
+
+    def backward(self, dqkv, dy_o):
+        self.backward_o(dy_o)
+        self.backward_qkv(dqkv)
         return self.dx, self.dx_o

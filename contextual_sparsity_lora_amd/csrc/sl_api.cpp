@@ -91,10 +91,10 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 const char* const kClassNames[] = {"gemm_bf16_nt", "gemm_bf16_nn", "gemm_f32",   "estimate",
                                    "score",        "topk",         "lora",       "swiglu",
                                    "gather",       "fill",         "token_split", "index",
-                                   "splitk_reduce"};
+                                   "splitk_reduce", "norm",        "attention"};
 constexpr int kNumClasses = sizeof(kClassNames) / sizeof(kClassNames[0]);
 enum { K_GEMM_NT, K_GEMM_NN, K_GEMM_F32, K_EST, K_SCORE, K_TOPK, K_LORA, K_SWIGLU, K_GATHER,
-       K_FILL, K_SPLIT, K_INDEX, K_REDUCE };
+       K_FILL, K_SPLIT, K_INDEX, K_REDUCE, K_NORM, K_ATTN };
 
 hipEvent_t take_event(sl_handle* h) {
     if (!h->event_pool.empty()) {
@@ -802,6 +802,115 @@ sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi, i
     DeviceGuard gd(h->device);
     return hip_check(h, launch_transpose(dt == SL_BF16, in, ldi, rows, cols, out, ldo, h->stream),
                      "transpose");
+}
+
+// ---------------------------------------------------------------- a14: layer glue
+sl_status sl_rmsnorm_fwd(sl_handle* h, sl_dtype dt, const void* x, int64_t ldx, const void* res,
+                         int64_t ldres, int64_t T, int64_t D, float eps, void* hsum, int64_t ldh,
+                         void* y, int64_t ldy, float* rstd) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, T >= 0 && T <= 2147483647LL && D >= 1 && eps >= 0.0f, "bad sizes");
+    if (T == 0) return SL_OK;
+    SL_CHECK(check_matrix(h, x, ldx, D, dt, "x"));
+    SL_CHECK(check_matrix(h, y, ldy, D, dt, "y"));
+    if (res) SL_CHECK(check_matrix(h, res, ldres, D, dt, "res"));
+    if (hsum) {
+        SL_REQUIRE(h, res != nullptr, "hsum needs res");
+        SL_CHECK(check_matrix(h, hsum, ldh, D, dt, "hsum"));
+    }
+    SL_REQUIRE(h, rstd != nullptr, "rstd is NULL");
+    DeviceGuard gd(h->device);
+    Timed tm(h, K_NORM, 0, (res ? 3.0 : 2.0) * T * D * esize(dt));
+    return hip_check(h, launch_rmsnorm_fwd(dt == SL_BF16, x, ldx, res, ldres, T, D, eps, hsum, ldh, y,
+                                           ldy, rstd, h->stream), "rmsnorm_fwd");
+}
+
+sl_status sl_rmsnorm_bwd(sl_handle* h, sl_dtype dt, const void* x, int64_t ldx, const float* rstd,
+                         const void* dy, int64_t lddy, const void* dres, int64_t lddres, int64_t T,
+                         int64_t D, void* dx, int64_t lddx) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, T >= 0 && T <= 2147483647LL && D >= 1, "bad sizes");
+    if (T == 0) return SL_OK;
+    SL_CHECK(check_matrix(h, x, ldx, D, dt, "x"));
+    SL_CHECK(check_matrix(h, dy, lddy, D, dt, "dy"));
+    SL_CHECK(check_matrix(h, dx, lddx, D, dt, "dx"));
+    if (dres) SL_CHECK(check_matrix(h, dres, lddres, D, dt, "dres"));
+    SL_REQUIRE(h, rstd != nullptr, "rstd is NULL");
+    DeviceGuard gd(h->device);
+    Timed tm(h, K_NORM, 0, (dres ? 4.0 : 3.0) * T * D * esize(dt));
+    return hip_check(h, launch_rmsnorm_bwd(dt == SL_BF16, x, ldx, rstd, dy, lddy, dres, lddres, T, D,
+                                           dx, lddx, h->stream), "rmsnorm_bwd");
+}
+
+sl_status sl_add(sl_handle* h, sl_dtype dt, const void* a, int64_t lda, const void* b, int64_t ldb,
+                 int64_t T, int64_t D, void* out, int64_t ldo) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, T >= 0 && T <= 65535 && D >= 1, "bad sizes");
+    if (T == 0) return SL_OK;
+    SL_CHECK(check_matrix(h, a, lda, D, dt, "a"));
+    SL_CHECK(check_matrix(h, b, ldb, D, dt, "b"));
+    SL_CHECK(check_matrix(h, out, ldo, D, dt, "out"));
+    DeviceGuard gd(h->device);
+    Timed tm(h, K_NORM, 0, 3.0 * T * D * esize(dt));
+    return hip_check(h, launch_add(dt == SL_BF16, a, lda, b, ldb, T, D, out, ldo, h->stream), "add");
+}
+
+static sl_status check_attn(sl_handle* h, int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd) {
+    SL_REQUIRE(h, B >= 0 && S >= 0 && B <= 65535 && S <= 2147483647LL / 32, "bad sizes");
+    SL_REQUIRE(h, H >= 1 && Hkv >= 1 && H % Hkv == 0 && H <= 65535, "n_heads must be a multiple of n_kv_heads");
+    SL_REQUIRE(h, hd == 32 || hd == 64 || hd == 128, "head_dim must be 32, 64 or 128");
+    return SL_OK;
+}
+
+sl_status sl_attention_fwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq, const void* k,
+                           int64_t ldk, const void* v, int64_t ldv, int64_t batch, int64_t seq,
+                           int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, void* o,
+                           int64_t ldo, float* lse) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_CHECK(check_attn(h, batch, seq, n_heads, n_kv_heads, head_dim));
+    if (batch == 0 || seq == 0) return SL_OK;
+    SL_CHECK(check_matrix(h, q, ldq, n_heads * head_dim, dt, "q"));
+    SL_CHECK(check_matrix(h, k, ldk, n_kv_heads * head_dim, dt, "k"));
+    SL_CHECK(check_matrix(h, v, ldv, n_kv_heads * head_dim, dt, "v"));
+    SL_CHECK(check_matrix(h, o, ldo, n_heads * head_dim, dt, "o"));
+    SL_REQUIRE(h, lse != nullptr, "lse is NULL");
+    DeviceGuard gd(h->device);
+    const double pairs = (double)batch * n_heads * seq * (seq + 1) / 2.0;
+    Timed tm(h, K_ATTN, 4.0 * pairs * head_dim, 0);
+    return hip_check(h, launch_attn_fwd(dt == SL_BF16, q, ldq, k, ldk, v, ldv, batch, seq, n_heads,
+                                        n_kv_heads, head_dim, o, ldo, lse, h->stream), "attention_fwd");
+}
+
+sl_status sl_attention_bwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq, const void* k,
+                           int64_t ldk, const void* v, int64_t ldv, const void* o, int64_t ldo,
+                           const void* dout, int64_t lddout, const float* lse, int64_t batch,
+                           int64_t seq, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                           void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv, int64_t lddv) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_CHECK(check_attn(h, batch, seq, n_heads, n_kv_heads, head_dim));
+    if (batch == 0 || seq == 0) return SL_OK;
+    const int64_t Cq = n_heads * head_dim, Ckv = n_kv_heads * head_dim;
+    SL_CHECK(check_matrix(h, q, ldq, Cq, dt, "q"));
+    SL_CHECK(check_matrix(h, k, ldk, Ckv, dt, "k"));
+    SL_CHECK(check_matrix(h, v, ldv, Ckv, dt, "v"));
+    SL_CHECK(check_matrix(h, o, ldo, Cq, dt, "o"));
+    SL_CHECK(check_matrix(h, dout, lddout, Cq, dt, "dout"));
+    SL_CHECK(check_matrix(h, dq, lddq, Cq, dt, "dq"));
+    SL_CHECK(check_matrix(h, dk, lddk, Ckv, dt, "dk"));
+    SL_CHECK(check_matrix(h, dv, lddv, Ckv, dt, "dv"));
+    SL_REQUIRE(h, lse != nullptr, "lse is NULL");
+    DeviceGuard gd(h->device);
+    SL_CHECK(ensure_ws(h, round_up((size_t)(batch * n_heads * seq) * 4, 256)));
+    const double pairs = (double)batch * n_heads * seq * (seq + 1) / 2.0;
+    Timed tm(h, K_ATTN, 10.0 * pairs * head_dim, 0);
+    return hip_check(h, launch_attn_bwd(dt == SL_BF16, q, ldq, k, ldk, v, ldv, o, ldo, dout, lddout,
+                                        lse, (float*)h->ws, batch, seq, n_heads, n_kv_heads, head_dim,
+                                        dq, lddq, dk, lddk, dv, lddv, h->stream), "attention_bwd");
 }
 
 }  // extern "C"

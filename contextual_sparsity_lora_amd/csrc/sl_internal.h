@@ -123,6 +123,22 @@ hipError_t launch_outer_accum(bool bf16, const float* P, int64_t ldp, int64_t T,
                               const void* Q, int64_t ldq, int64_t Ncols, float scale,
                               float* out, int64_t so_j, int64_t so_c, float* ws, size_t ws_floats,
                               hipStream_t st);
+hipError_t launch_rmsnorm_fwd(bool bf16, const void* x, int64_t ldx, const void* res, int64_t ldr,
+                              int64_t T, int64_t D, float eps, void* hout, int64_t ldh, void* y,
+                              int64_t ldy, float* rstd, hipStream_t st);
+hipError_t launch_rmsnorm_bwd(bool bf16, const void* x, int64_t ldx, const float* rstd, const void* dy,
+                              int64_t lddy, const void* dres, int64_t lddr, int64_t T, int64_t D,
+                              void* dx, int64_t lddx, hipStream_t st);
+hipError_t launch_add(bool bf16, const void* a, int64_t lda, const void* b, int64_t ldb, int64_t T,
+                      int64_t D, void* out, int64_t ldo, hipStream_t st);
+hipError_t launch_attn_fwd(bool bf16, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                           const void* v, int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv,
+                           int64_t hd, void* o, int64_t ldo, float* lse, hipStream_t st);
+hipError_t launch_attn_bwd(bool bf16, const void* q, int64_t ldq, const void* k, int64_t ldk,
+                           const void* v, int64_t ldv, const void* o, int64_t ldo, const void* dO,
+                           int64_t lddo, const float* lse, float* delta, int64_t B, int64_t S,
+                           int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq, void* dk,
+                           int64_t lddk, void* dv, int64_t lddv, hipStream_t st);
 hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,
                             void* out, int64_t ldo, hipStream_t st);
 hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* u, int64_t ldu,

@@ -257,3 +257,46 @@ def transpose(inp, out):
     rows, cols = inp.shape
     st = _lib.load().sl_transpose(h, _dt(inp), _ptr(inp), _ld(inp), rows, cols, _ptr(out), _ld(out))
     _check(h, st, "sl_transpose")
+
+
+def rmsnorm_fwd(x, y, rstd, res=None, hsum=None, eps=1e-5):
+    """y = hsum / sqrt(mean(hsum^2) + eps) with hsum = x (+ res; stored to hsum)."""
+    h = handle(_dev(x))
+    T, D = x.shape
+    ld = lambda v: _ld(v) if v is not None else 0
+    st = _lib.load().sl_rmsnorm_fwd(h, _dt(x), _ptr(x), _ld(x), _ptr(res), ld(res), T, D, float(eps),
+                                    _ptr(hsum), ld(hsum), _ptr(y), _ld(y), _ptr(rstd))
+    _check(h, st, "sl_rmsnorm_fwd")
+
+
+def rmsnorm_bwd(x, rstd, dy, dx, dres=None):
+    h = handle(_dev(x))
+    T, D = x.shape
+    st = _lib.load().sl_rmsnorm_bwd(h, _dt(x), _ptr(x), _ld(x), _ptr(rstd), _ptr(dy), _ld(dy),
+                                    _ptr(dres), _ld(dres) if dres is not None else 0, T, D, _ptr(dx),
+                                    _ld(dx))
+    _check(h, st, "sl_rmsnorm_bwd")
+
+
+def add(a, b, out):
+    h = handle(_dev(a))
+    T, D = a.shape
+    st = _lib.load().sl_add(h, _dt(a), _ptr(a), _ld(a), _ptr(b), _ld(b), T, D, _ptr(out), _ld(out))
+    _check(h, st, "sl_add")
+
+
+def attention_fwd(q, k, v, batch, seq, n_heads, n_kv_heads, head_dim, o, lse):
+    h = handle(_dev(q))
+    st = _lib.load().sl_attention_fwd(h, _dt(q), _ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v),
+                                      batch, seq, n_heads, n_kv_heads, head_dim, _ptr(o), _ld(o),
+                                      _ptr(lse))
+    _check(h, st, "sl_attention_fwd")
+
+
+def attention_bwd(q, k, v, o, dout, lse, batch, seq, n_heads, n_kv_heads, head_dim, dq, dk, dv):
+    h = handle(_dev(q))
+    st = _lib.load().sl_attention_bwd(h, _dt(q), _ptr(q), _ld(q), _ptr(k), _ld(k), _ptr(v), _ld(v),
+                                      _ptr(o), _ld(o), _ptr(dout), _ld(dout), _ptr(lse), batch, seq,
+                                      n_heads, n_kv_heads, head_dim, _ptr(dq), _ld(dq), _ptr(dk),
+                                      _ld(dk), _ptr(dv), _ld(dv))
+    _check(h, st, "sl_attention_bwd")

@@ -310,6 +310,48 @@ sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
 sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi,
                        int64_t rows, int64_t cols, void* out, int64_t ldo);
 
+/* ---------------------------------------------------------------- a14: decoder-layer glue
+ * Support steps between the sparse linears of a decoder layer (the pages'
+ * LLaMA layers; topology here: pre-norm, residual adds, plain causal softmax
+ * attention with scale 1/sqrt(d), no position encoding, grouped-query heads).
+ * fp32 arithmetic; dt storage. */
+
+/* RMSNorm with unit weight: hsum = x + res (res optional; when hsum != NULL
+ * the sum is stored there, rounded to dt, and the norm reads the stored
+ * value), rstd[t] = 1 / sqrt(mean_j hsum[t, j]^2 + eps) (fp32 [T], caller
+ * owned), y = hsum * rstd.  All matrices [T, D] with leading dimensions. */
+sl_status sl_rmsnorm_fwd(sl_handle* h, sl_dtype dt, const void* x, int64_t ldx, const void* res,
+                         int64_t ldres, int64_t T, int64_t D, float eps, void* hsum, int64_t ldh,
+                         void* y, int64_t ldy, float* rstd);
+/* Gradient of sl_rmsnorm_fwd with respect to its normalised input x (the
+ * stored hsum when a residual was fused): dx = rstd dy - rstd^3 x (dy . x) / D,
+ * plus dres when dres != NULL (the residual branch's gradient). */
+sl_status sl_rmsnorm_bwd(sl_handle* h, sl_dtype dt, const void* x, int64_t ldx, const float* rstd,
+                         const void* dy, int64_t lddy, const void* dres, int64_t lddres, int64_t T,
+                         int64_t D, void* dx, int64_t lddx);
+/* out = a + b, [T, D] (residual adds); out may alias a or b. */
+sl_status sl_add(sl_handle* h, sl_dtype dt, const void* a, int64_t lda, const void* b, int64_t ldb,
+                 int64_t T, int64_t D, void* out, int64_t ldo);
+/* Causal softmax attention per sequence and query head.  q [batch*seq,
+ * n_heads*head_dim], k, v [batch*seq, n_kv_heads*head_dim], rows sequence-
+ * major; query head h reads key/value head h / (n_heads / n_kv_heads).
+ * o [batch*seq, n_heads*head_dim]; lse fp32 [batch, n_heads, seq] receives
+ * the log of each softmax denominator (with its max) for the backward pass.
+ * head_dim 32, 64 or 128; n_heads a multiple of n_kv_heads. */
+sl_status sl_attention_fwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq, const void* k,
+                           int64_t ldk, const void* v, int64_t ldv, int64_t batch, int64_t seq,
+                           int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, void* o,
+                           int64_t ldo, float* lse);
+/* Gradients of sl_attention_fwd for upstream dout (softmax probabilities
+ * recomputed from lse): dq, and dk, dv summed over the query heads that read
+ * each key/value head.  Uses batch*n_heads*seq*4 bytes of the handle's
+ * workspace. */
+sl_status sl_attention_bwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq, const void* k,
+                           int64_t ldk, const void* v, int64_t ldv, const void* o, int64_t ldo,
+                           const void* dout, int64_t lddout, const float* lse, int64_t batch,
+                           int64_t seq, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
+                           void* dq, int64_t lddq, void* dk, int64_t lddk, void* dv, int64_t lddv);
+
 #ifdef __cplusplus
 }
 #endif

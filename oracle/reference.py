@@ -221,6 +221,72 @@ def attn_proj_bwd(inp, fwd, idx_qk, idx_vo, n_rep, head_dim):
     return res
 
 
+def rmsnorm_fwd(x, eps=1e-5):
+    """Pre-norm with unit weight: y = x / sqrt(mean_j x_j^2 + eps) per row
+    (decoder layer topology, reading R16).  Returns (y, rstd)."""
+    x = np.asarray(x, f64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
+    return x * r[:, None], r
+
+
+def rmsnorm_bwd(x, rstd, dy):
+    """Gradient of ``rmsnorm_fwd``: dx = r dy - r^3 x (sum_j dy_j x_j) / D."""
+    x, dy = np.asarray(x, f64), np.asarray(dy, f64)
+    r = np.asarray(rstd, f64)[:, None]
+    D = x.shape[1]
+    return r * dy - (r ** 3) * x * np.sum(dy * x, axis=1, keepdims=True) / D
+
+
+def _heads(a, t0, S, H, d):
+    return np.asarray(a[t0:t0 + S], f64).reshape(S, H, d).transpose(1, 0, 2)
+
+
+def attention_fwd(q, k, v, batch, seq, n_heads, n_kv_heads, head_dim):
+    """Plain causal softmax attention per sequence and query head: scale
+    1/sqrt(d), no position encoding; query head h reads key/value head
+    h // (n_heads / n_kv_heads).  q [T, H d], k, v [T, H_kv d], rows are
+    sequence-major.  Returns o [T, H d]."""
+    n_rep, d = n_heads // n_kv_heads, head_dim
+    o = np.zeros((batch * seq, n_heads * d), f64)
+    mask = np.tril(np.ones((seq, seq), bool))
+    for b in range(batch):
+        t0 = b * seq
+        Q, K, V = _heads(q, t0, seq, n_heads, d), _heads(k, t0, seq, n_kv_heads, d), _heads(v, t0, seq, n_kv_heads, d)
+        for h in range(n_heads):
+            s = (Q[h] @ K[h // n_rep].T) / np.sqrt(d)
+            s = np.where(mask, s, -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            o[t0:t0 + seq, h * d:(h + 1) * d] = p @ V[h // n_rep]
+    return o
+
+
+def attention_bwd(q, k, v, do, batch, seq, n_heads, n_kv_heads, head_dim):
+    """Gradients of ``attention_fwd`` for upstream do: (dq, dk, dv); the
+    gradients of a key/value head sum over the query heads that read it."""
+    n_rep, d = n_heads // n_kv_heads, head_dim
+    T = batch * seq
+    dq = np.zeros((T, n_heads * d), f64)
+    dk = np.zeros((T, n_kv_heads * d), f64)
+    dv = np.zeros((T, n_kv_heads * d), f64)
+    mask = np.tril(np.ones((seq, seq), bool))
+    for b in range(batch):
+        t0 = b * seq
+        Q, K, V = _heads(q, t0, seq, n_heads, d), _heads(k, t0, seq, n_kv_heads, d), _heads(v, t0, seq, n_kv_heads, d)
+        dO = _heads(do, t0, seq, n_heads, d)
+        for h in range(n_heads):
+            g = h // n_rep
+            s = np.where(mask, (Q[h] @ K[g].T) / np.sqrt(d), -np.inf)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = dO[h] @ V[g].T
+            ds = p * (dp - np.sum(dp * p, axis=1, keepdims=True)) / np.sqrt(d)
+            dq[t0:t0 + seq, h * d:(h + 1) * d] = ds @ K[g]
+            dk[t0:t0 + seq, g * d:(g + 1) * d] += ds.T @ Q[h]
+            dv[t0:t0 + seq, g * d:(g + 1) * d] += p.T @ dO[h]
+    return dq, dk, dv
+
+
 def max_abs_rel(got, ref):
     """max |got - ref| / max(max |ref|, 1e-30), per tensor."""
     got, ref = np.asarray(got, f64), np.asarray(ref, f64)

@@ -293,3 +293,39 @@ def test_attn_projections_all_kept_are_dense(rng):
         assert np.allclose(fwd[p], dense, rtol=1e-12, atol=1e-12)
     dense_o = inp["x_o"] @ inp["W_o"].T + s * (inp["x_o"] @ inp["A_o"].T) @ inp["B_o"].T
     assert np.allclose(fwd["o"], dense_o, rtol=1e-12, atol=1e-12)
+
+
+def test_rmsnorm_matches_library_and_autograd(rng):
+    x = rng.standard_normal((7, 24)) * 3.0
+    dy = rng.standard_normal((7, 24))
+    y, r = ref.rmsnorm_fwd(x, eps=1e-5)
+    xt = torch.tensor(x, requires_grad=True)
+    yt = torch.nn.functional.rms_norm(xt, (24,), eps=1e-5)
+    assert np.allclose(y, yt.detach().numpy(), rtol=1e-13, atol=1e-13)
+    (yt * torch.tensor(dy)).sum().backward()
+    assert np.allclose(ref.rmsnorm_bwd(x, r, dy), xt.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (6, 2)])
+def test_attention_matches_sdpa_and_autograd(rng, Hq, Hkv):
+    """Causal softmax attention against torch's scaled_dot_product_attention in
+    fp64 with key/value heads repeated over each group (repeat_interleave)."""
+    B, S, d = 2, 9, 5
+    T = B * S
+    q = rng.standard_normal((T, Hq * d))
+    k = rng.standard_normal((T, Hkv * d))
+    v = rng.standard_normal((T, Hkv * d))
+    do = rng.standard_normal((T, Hq * d))
+    o = ref.attention_fwd(q, k, v, B, S, Hq, Hkv, d)
+    dq, dk, dv = ref.attention_bwd(q, k, v, do, B, S, Hq, Hkv, d)
+    qt, kt, vt = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    sh = lambda a, H: a.view(B, S, H, d).transpose(1, 2)
+    kk = sh(kt, Hkv).repeat_interleave(Hq // Hkv, dim=1)
+    vv = sh(vt, Hkv).repeat_interleave(Hq // Hkv, dim=1)
+    ot = torch.nn.functional.scaled_dot_product_attention(sh(qt, Hq), kk, vv, is_causal=True)
+    ot = ot.transpose(1, 2).reshape(T, Hq * d)
+    assert np.allclose(o, ot.detach().numpy(), rtol=1e-12, atol=1e-12)
+    (ot * torch.tensor(do)).sum().backward()
+    assert np.allclose(dq, qt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dk, kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(dv, vt.grad.numpy(), rtol=1e-10, atol=1e-12)

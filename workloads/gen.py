@@ -3,7 +3,7 @@
 Recipe (the same for every configuration):
   * numpy ``Generator(PCG64)``; one child stream per tensor, spawned from
     ``SeedSequence(cfg.seed)`` in the fixed order of ``_FFN_ORDER`` /
-    ``_ATTN_ORDER``;
+    ``_ATTN_ORDER`` / ``_LAYER_ORDER``;
   * frozen weights and LoRA factors ~ N(0, 0.02^2), rounded to the
     configuration's dtype (bf16 round-to-nearest-even, or fp32);
   * linear inputs: N(0, 1) per element, then each row scaled to unit RMS
@@ -25,6 +25,9 @@ _FFN_ORDER = ["x", "W_gate", "W_up", "W_down", "A_gate", "B_gate", "A_up", "B_up
               "A_down", "B_down", "dy"]
 _ATTN_ORDER = ["x", "W_q", "W_k", "W_v", "W_o", "A_q", "B_q", "A_k", "B_k", "A_v", "B_v",
                "A_o", "B_o", "x_o", "dy_q", "dy_k", "dy_v", "dy_o"]
+_LAYER_ORDER = ["x", "W_q", "W_k", "W_v", "W_o", "W_gate", "W_up", "W_down",
+                "A_q", "B_q", "A_k", "B_k", "A_v", "B_v", "A_o", "B_o",
+                "A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down", "dy"]
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -165,5 +168,32 @@ def make_attn_inputs(cfg: Config, with_factors: bool = True) -> dict:
         fa = {p: svd_factor_pair(out["W_" + p], k) for p in ("q", "k", "v")}
         out["WA_t_qkv"] = np.ascontiguousarray(np.concatenate([fa[p][0] for p in "qkv"], axis=0))
         for p in "qkv":
+            out["WB_" + p] = fa[p][1]
+    return out
+
+
+def make_layer_inputs(cfg: Config, with_factors: bool = True, seed: int = None) -> dict:
+    """Inputs of one decoder layer: attention projections (GQA when
+    n_kv_heads < n_q_heads) and a SwiGLU FFN, LoRA on all seven linears, the
+    layer input x and the upstream gradient dy.  ``seed`` overrides
+    ``cfg.seed`` (one seed per layer of a stack)."""
+    D, F, r, T, dt = cfg.hidden, cfg.inter, cfg.lora_rank, cfg.tokens, cfg.dtype
+    Cq, Ckv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    g = _streams(cfg.seed if seed is None else seed, _LAYER_ORDER)
+    shapes = {"W_q": (Cq, D), "W_k": (Ckv, D), "W_v": (Ckv, D), "W_o": (D, Cq),
+              "W_gate": (F, D), "W_up": (F, D), "W_down": (D, F)}
+    out = {"x": _rms_rows(g["x"], (T, D), dt), "roles": roles_for(cfg), "scale": cfg.lora_scale,
+           "dy": _normal(g["dy"], (T, D), 1.0, dt)}
+    for name, shp in shapes.items():
+        out[name] = _normal(g[name], shp, 0.02, dt)
+        p = name[2:]
+        out["A_" + p] = _normal(g["A_" + p], (r, shp[1]), 0.02, dt)
+        out["B_" + p] = _normal(g["B_" + p], (shp[0], r), 0.02, dt)
+    if with_factors:
+        k = cfg.est_rank
+        fa = {p: svd_factor_pair(out["W_" + p], k) for p in ("q", "k", "v", "gate", "up")}
+        out["WA_t_qkv"] = np.ascontiguousarray(np.concatenate([fa[p][0] for p in "qkv"], axis=0))
+        out["WA_t_gu"] = np.ascontiguousarray(np.concatenate([fa["gate"][0], fa["up"][0]], axis=0))
+        for p in ("q", "k", "v", "gate", "up"):
             out["WB_" + p] = fa[p][1]
     return out
