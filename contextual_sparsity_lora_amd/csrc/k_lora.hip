@@ -881,7 +881,7 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
                                  int64_t ldb, int64_t r, float scale, const int32_t* idx,
                                  int64_t n, uint32_t* mask, int beta, hipStream_t st) {
     if (nrows <= 0 || C <= 0) return hipSuccess;
-    if (r < 1 || r > 64) return hipErrorInvalidValue;
+    if (r < 1 || r > 128) return hipErrorInvalidValue;
     if (beta) {
         hipLaunchKernelGGL(select_mask_kernel, dim3((unsigned)ceil_div(ceil_div(C, 32), 256)),
                            dim3(256), 0, st, idx, n, C, mask);
@@ -891,7 +891,8 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
     hipLaunchKernelGGL((lora_fill_rows_kernel<RR>), grid, dim3(256), 0, st, (bf16_t*)y, ldy, rows, \
                        nrows, C, P, ldp, (const bf16_t*)B, ldb, r, scale, (const uint32_t*)mask, beta)
     if (r <= 32) FILL(32);
-    else FILL(64);
+    else if (r <= 64) FILL(64);
+    else FILL(128);
 #undef FILL
     return hipGetLastError();
 }

@@ -445,7 +445,7 @@ struct LoraEpi {
 
 sl_status check_lora(sl_handle* h, const LoraEpi& l, int64_t T, int64_t Nout, sl_dtype dt) {
     if (!l.P) return SL_OK;
-    SL_REQUIRE(h, l.r >= 1 && l.r <= 64, "lora_r must be in [1, 64]");
+    SL_REQUIRE(h, l.r >= 1 && l.r <= 128, "lora_r must be in [1, 128]");
     SL_REQUIRE(h, l.ldP >= l.r && l.ldB >= l.r, "LoRA leading dimension < lora_r");
     SL_REQUIRE(h, l.B != nullptr, "lora_B is NULL");
     (void)T; (void)Nout; (void)dt;
@@ -684,7 +684,8 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
     const int all = SL_LORA_XL | SL_LORA_ADD | SL_LORA_GB | SL_LORA_DA | SL_LORA_DB | SL_LORA_DX;
     SL_REQUIRE(h, (mode & ~all) == 0 && mode != 0, "bad mode");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
-    SL_REQUIRE(h, r >= 1 && r <= 64, "r must be in [1, 64]");
+    SL_REQUIRE(h, r >= 1 && r <= 128, "r must be in [1, 128]");
+    SL_REQUIRE(h, r <= 64 || !(mode & (SL_LORA_ADD | SL_LORA_DX)), "r > 64 with ADD or DX");
     SL_REQUIRE(h, T >= 0 && T <= 65535 * 32 && D_in >= 1 && D_out >= 1, "bad sizes");
     const bool bf = dt == SL_BF16;
     const bool gb = mode & SL_LORA_GB, da = mode & SL_LORA_DA, db = mode & SL_LORA_DB,
@@ -712,14 +713,21 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
                       (gb ? es * T * D_out + 4.0 * T * r : 0) + (da ? es * T * D_in : 0) +
                       (db ? es * T * D_out : 0) + (dxm ? 2 * es * T * D_in : 0);
     Timed tm(h, K_LORA, fl, by);
+    // ranks above 64 run as column chunks of at most 64 (the columns of xl,
+    // gB, the rows of dA and the columns of dB are independent of each other)
+    const int64_t RC = 64;
+    const int64_t rc_max = r < RC ? r : RC;
     if (mode & SL_LORA_XL) {
         float* xw = nullptr;   // split-K partials (bf16)
         if (bf) {
-            SL_CHECK(ensure_ws(h, round_up(lora_xl_ws_floats(T, D_in, r) * 4, 256)));
+            SL_CHECK(ensure_ws(h, round_up(lora_xl_ws_floats(T, D_in, rc_max) * 4, 256)));
             xw = (float*)h->ws;
         }
-        SL_HIP(h, launch_lora_xl(bf, x, ldx, T, D_in, A, D_in, r, xl, ldxl, xw, h->stream),
-               "lora_xl");
+        for (int64_t c0 = 0; c0 < r; c0 += RC) {
+            const int64_t rc = (r - c0) < RC ? (r - c0) : RC;
+            SL_HIP(h, launch_lora_xl(bf, x, ldx, T, D_in, (const char*)A + c0 * D_in * esize(dt), D_in,
+                                     rc, xl + c0, ldxl, xw, h->stream), "lora_xl");
+        }
     }
     if (mode & SL_LORA_ADD)
         SL_HIP(h, launch_lora_add(bf, xl, ldxl, T, r, B, r, 1, D_out, scale, y, ldy, h->stream),
@@ -732,7 +740,7 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         const size_t gb_bytes = round_up((size_t)(T > 0 ? T : 1) * r * 4, 256);
         const int64_t ncol = D_in > D_out ? D_in : D_out;
         size_t part_floats = (size_t)(nch * r * ncol);
-        const size_t xl_floats = bf ? lora_xl_ws_floats(T, D_out, r) : 0;
+        const size_t xl_floats = bf ? lora_xl_ws_floats(T, D_out, rc_max) : 0;
         if (part_floats < xl_floats) part_floats = xl_floats;
         SL_CHECK(ensure_ws(h, bt_bytes + gb_bytes + part_floats * 4));
         char* ws = (char*)h->ws;
@@ -740,17 +748,20 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         float* gB = gB_io ? gB_io : (float*)(ws + bt_bytes);
         const int64_t ldg = gB_io ? ldgB : r;
         float* part = (float*)(ws + bt_bytes + gb_bytes);
-        if (gb) {
-            SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
-            SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, Bt, ldbt, r, gB, ldg, bf ? part : nullptr,
-                                     h->stream), "lora_gB");
+        if (gb) SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
+        for (int64_t c0 = 0; c0 < r; c0 += RC) {
+            const int64_t rc = (r - c0) < RC ? (r - c0) : RC;
+            if (gb)
+                SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, (const char*)Bt + c0 * ldbt * esize(dt),
+                                         ldbt, rc, gB + c0, ldg, bf ? part : nullptr, h->stream),
+                       "lora_gB");
+            if (da)
+                SL_HIP(h, launch_outer_accum(bf, gB + c0, ldg, T, rc, x, ldx, D_in, scale, dA + c0 * D_in,
+                                             D_in, 1, part, part_floats, h->stream), "lora_dA");
+            if (db)
+                SL_HIP(h, launch_outer_accum(bf, xl + c0, ldxl, T, rc, dy, lddy, D_out, scale, dB + c0, 1,
+                                             r, part, part_floats, h->stream), "lora_dB");
         }
-        if (da)
-            SL_HIP(h, launch_outer_accum(bf, gB, ldg, T, r, x, ldx, D_in, scale, dA, D_in, 1, part,
-                                         part_floats, h->stream), "lora_dA");
-        if (db)
-            SL_HIP(h, launch_outer_accum(bf, xl, ldxl, T, r, dy, lddy, D_out, scale, dB, 1, r, part,
-                                         part_floats, h->stream), "lora_dB");
         if (dxm)
             SL_HIP(h, launch_lora_add(bf, gB, ldg, T, r, A, 1, D_in, D_in, scale, dx, lddx, h->stream),
                    "lora_dx");

@@ -31,8 +31,8 @@ class SparseDecoderLayer:
     @classmethod
     def from_arrays(cls, d, f32, cfg, qk_sparsity, vo_sparsity, ffn_sparsity, dense=False):
         """Build from device tensors d[...] (dtype of the layer) and fp32 factor
-        tensors f32[...] as produced by the layer input recipe."""
-        import numpy as np  # noqa: F401  (kept local: marshalling helper only)
+        tensors f32[...]: WA_qkv [D, 3k], WA_gu [D, 2k] (estimator W_A factors
+        side by side) and WB_q, WB_k, WB_v, WB_gate, WB_up."""
         attn = SparseAttnProj(d["W_q"], d["W_k"], d["W_v"], d["W_o"], d["A_q"], d["B_q"], d["A_k"],
                               d["B_k"], d["A_v"], d["B_v"], d["A_o"], d["B_o"], f32["WA_qkv"],
                               f32["WB_q"], f32["WB_k"], f32["WB_v"], cfg.lora_scale, cfg.n_kv_heads,

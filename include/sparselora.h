@@ -221,7 +221,7 @@ sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t o
  * on every row and every output channel, accumulated in fp32 before the one
  * rounding of y; the unselected channels of context rows (side OUT) then hold
  * this term instead of 0.  lora_P: device fp32 [T, ld_lora_P] (xl = x A^T);
- * lora_B: device (dt) [D_out, ld_lora_B] (the LoRA B).  1 <= lora_r <= 64.
+ * lora_B: device (dt) [D_out, ld_lora_B] (the LoRA B).  1 <= lora_r <= 128.
  *   x   device [T, ldx] (dt), channels of side IN are its columns
  *   W   device (dt) [D_out, ldw >= D_in], nn.Linear layout
  *   Wt  device (dt) [D_in, ldwt >= D_out], W transposed; read only for side IN
@@ -286,8 +286,9 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
  *   SL_LORA_DX:  dx += scale gB A                  (dt [T, lddx]); leave it out
  *                and pass gB to sl_sparse_linear_bwd to fuse that term there
  * Modes combine; the steps run in the order listed.  Pointers not used by the
- * mode may be NULL.  1 <= r <= 64.  dA / dB are deterministic (fixed-order
- * token reduction). */
+ * mode may be NULL.  1 <= r <= 128 (r <= 64 with ADD or DX; ranks above 64
+ * run as column chunks of 64).  dA / dB are deterministic (fixed-order token
+ * reduction). */
 sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt,
                           const void* x, int64_t ldx, int64_t T, int64_t D_in, int64_t D_out,
                           const void* A, const void* B, int64_t r, float scale,

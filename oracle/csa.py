@@ -157,3 +157,22 @@ def select(scores, n):
     cnt = lib().orc_select(_p(s), C, n, _p(idx, _ip))
     assert cnt == n
     return idx[:n].copy()
+
+
+def select_ffn(x, ctx_rows, WA_t_gu, WB_gate, WB_up, n):
+    """FFN group selection: estimator on the context rows of the group input,
+    SwiGLU-L2 scores, top-n (paper-graph summary §3.4, Algorithm 1 steps 1-3)."""
+    k = WB_gate.shape[0]
+    xa = stage1(x, ctx_rows, WA_t_gu)
+    return select(ssq_swiglu(xa, WB_gate, WB_up, 0, k), n)
+
+
+def select_attn(x, ctx_rows, WA_t_qkv, WB_q, WB_k, WB_v, n_kv_heads, n_rep, head_dim, n_qk, n_vo):
+    """Attention group selections (QK criterion, VO criterion) from one
+    estimator pass over the context rows of the group input."""
+    k = WB_q.shape[0]
+    xa = stage1(x, ctx_rows, WA_t_qkv)
+    sq, sk = ssq_l2(xa, WB_q, off=0), ssq_l2(xa, WB_k, off=k)
+    idx_qk = select(qk_combine(sq, sk, n_kv_heads, n_rep, head_dim), n_qk)
+    idx_vo = select(ssq_l2(xa, WB_v, off=2 * k), n_vo)
+    return idx_qk, idx_vo

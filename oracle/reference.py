@@ -223,7 +223,9 @@ def attn_proj_bwd(inp, fwd, idx_qk, idx_vo, n_rep, head_dim):
 
 def rmsnorm_fwd(x, eps=1e-5):
     """Pre-norm with unit weight: y = x / sqrt(mean_j x_j^2 + eps) per row
-    (decoder layer topology, reading R16).  Returns (y, rstd)."""
+    (the pages leave the layer topology around the linears open; the LLaMA
+    layers they fine-tune are pre-norm, taken here with unit weight and
+    eps = 1e-5).  Returns (y, rstd)."""
     x = np.asarray(x, f64)
     r = 1.0 / np.sqrt(np.mean(x * x, axis=1) + eps)
     return x * r[:, None], r
@@ -285,6 +287,63 @@ def attention_bwd(q, k, v, do, batch, seq, n_heads, n_kv_heads, head_dim):
             dk[t0:t0 + seq, g * d:(g + 1) * d] += ds.T @ Q[h]
             dv[t0:t0 + seq, g * d:(g + 1) * d] += p.T @ dO[h]
     return dq, dk, dv
+
+
+def decoder_layer_fwd(inp, dims, idx_qk, idx_vo, idx_ffn, eps=1e-5):
+    """Forward of one decoder layer whose seven linears are sparse (pre-norm
+    LLaMA topology, unit-weight RMSNorm, causal softmax attention without
+    position encoding; paper-graph summary §3.4: q/k/v/o by the QK and VO
+    criteria, gate/up/down by the FFN criterion, output tokens dense, LoRA
+    dense everywhere):
+        n1 = rmsnorm(x); q, k, v = sparse(n1); a = attention(q, k, v)
+        o = sparse_o(a); h1 = x + o; n2 = rmsnorm(h1); y = h1 + ffn(n2)
+    dims = (batch, seq, n_heads, n_kv_heads, head_dim).  The selections are
+    inputs: the estimator reads n1 (attention group) and n2 (FFN group)."""
+    B, S, H, Hkv, d = dims
+    n_rep = H // Hkv
+    x, roles, s = np.asarray(inp["x"], f64), inp["roles"], inp["scale"]
+    sel = attn_proj_indices(idx_qk, idx_vo, n_rep, d)
+    f = {}
+    f["n1"], f["rstd1"] = rmsnorm_fwd(x, eps)
+    for p in "qkv":
+        f["xl_" + p], lp = lora_fwd(f["n1"], inp["A_" + p], inp["B_" + p], s)
+        f[p] = sparse_linear_fwd("out", f["n1"], inp["W_" + p], roles, sel[p]) + lp
+    f["a"] = attention_fwd(f["q"], f["k"], f["v"], B, S, H, Hkv, d)
+    f["xl_o"], lo = lora_fwd(f["a"], inp["A_o"], inp["B_o"], s)
+    f["o"] = sparse_linear_fwd("in", f["a"], inp["W_o"], roles, sel["o"]) + lo
+    f["h1"] = x + f["o"]
+    f["n2"], f["rstd2"] = rmsnorm_fwd(f["h1"], eps)
+    ffn = ffn_block_fwd(dict(inp, x=f["n2"]), idx_ffn)
+    f.update({k + "_ffn" if k in ("y",) else k: v for k, v in ffn.items()})
+    f["y"] = f["h1"] + ffn["y"]
+    return f
+
+
+def decoder_layer_bwd(inp, fwd, dims, idx_qk, idx_vo, idx_ffn, dy=None):
+    """Backward of ``decoder_layer_fwd`` for upstream dy (default inp["dy"]):
+    the gradients of every intermediate, dx, and the LoRA gradients of the
+    seven linears (§3.2: dense LoRA gradients, no frozen-weight gradient)."""
+    B, S, H, Hkv, d = dims
+    n_rep = H // Hkv
+    roles, s = inp["roles"], inp["scale"]
+    dy = np.asarray(inp["dy"] if dy is None else dy, f64)
+    sel = attn_proj_indices(idx_qk, idx_vo, n_rep, d)
+    g = {}
+    fb = ffn_block_bwd(dict(inp, x=fwd["n2"]), fwd, idx_ffn, dy=dy)
+    g.update({k: v for k, v in fb.items() if k != "dx"})
+    g["dn2"] = fb["dx"]
+    g["dh1"] = rmsnorm_bwd(fwd["h1"], fwd["rstd2"], g["dn2"]) + dy
+    dal, g["dA_o"], g["dB_o"] = lora_bwd(fwd["a"], fwd["xl_o"], g["dh1"], inp["A_o"], inp["B_o"], s)
+    g["da"] = sparse_linear_bwd("in", g["dh1"], inp["W_o"], roles, sel["o"]) + dal
+    g["dq"], g["dk"], g["dv"] = attention_bwd(fwd["q"], fwd["k"], fwd["v"], g["da"], B, S, H, Hkv, d)
+    dn1 = np.zeros_like(fwd["n1"])
+    for p in "qkv":
+        dxl, g["dA_" + p], g["dB_" + p] = lora_bwd(fwd["n1"], fwd["xl_" + p], g["d" + p],
+                                                   inp["A_" + p], inp["B_" + p], s)
+        dn1 = dn1 + sparse_linear_bwd("out", g["d" + p], inp["W_" + p], roles, sel[p]) + dxl
+    g["dn1"] = dn1
+    g["dx"] = rmsnorm_bwd(inp["x"], fwd["rstd1"], dn1) + g["dh1"]
+    return g
 
 
 def max_abs_rel(got, ref):

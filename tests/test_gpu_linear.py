@@ -147,7 +147,34 @@ def test_lora_fwd_bwd(dtype, T, Din, Dout, r, rng):
     assert mar(host(dx), dx0 + dx_r) <= tol
 
 
-@pytest.mark.parametrize("dtype,r", [("f32", 8), ("bf16", 16), ("bf16", 32)])
+@pytest.mark.parametrize("dtype,T,Din,Dout,r", [("bf16", 700, 520, 1000, 96), ("f32", 90, 136, 200, 128),
+                                                ("bf16", 4096, 256, 392, 128)])
+def test_lora_high_rank_column_chunks(dtype, T, Din, Dout, r, rng):
+    """Ranks above 64 (a stacked q|k|v LoRA of rank 32 per projection has 96):
+    xl, gB, dA and dB run as independent column chunks of 64."""
+    ops = _ops()
+    print(f"[lora] high rank {dtype} T={T} r={r}", flush=True)
+    s = 2.0
+    x = round_dtype(rng.standard_normal((T, Din)), dtype)
+    A = round_dtype(rng.standard_normal((r, Din)) * 0.02, dtype)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.02, dtype)
+    dy = round_dtype(rng.standard_normal((T, Dout)), dtype)
+    xd, Ad, Bd = to_dev(x, dtype), to_dev(A, dtype), to_dev(Bm, dtype)
+    xl = torch.empty(T, r, dtype=torch.float32, device=DEV)
+    ops.lora_fwd_bwd(ops.LORA_XL, xd, Ad, None, s, xl)
+    assert mar(host(xl), x.astype(np.float64) @ A.T.astype(np.float64)) <= 1e-5
+    gB = torch.empty(T, r, dtype=torch.float32, device=DEV)
+    dA = torch.empty(r, Din, dtype=torch.float32, device=DEV)
+    dB = torch.empty(Dout, r, dtype=torch.float32, device=DEV)
+    ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, xd, None, Bd, s, xl, dy=to_dev(dy, dtype),
+                     dA=dA, dB=dB, gB=gB, D_in=Din)
+    _, dA_r, dB_r = ref.lora_bwd(x, host(xl), dy, A, Bm, s)
+    assert mar(host(gB), dy.astype(np.float64) @ Bm.astype(np.float64)) <= 1e-5
+    assert mar(host(dA), dA_r) <= 1e-4
+    assert mar(host(dB), dB_r) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype,r", [("f32", 8), ("bf16", 16), ("bf16", 32), ("bf16", 96), ("f32", 72)])
 def test_fused_lora_term(dtype, r, rng):
     """The LoRA term fused into the main-branch product equals main + s xl B^T,
     and unselected context channels carry the LoRA term alone."""
@@ -193,7 +220,7 @@ def test_fused_lora_term(dtype, r, rng):
     assert mar(host(dx2), ref.sparse_linear_bwd("out", dy2, W, roles, idx) + lora_i) <= tol
 
 
-@pytest.mark.parametrize("r,Dout", [(16, 1000), (32, 1003), (64, 136)])
+@pytest.mark.parametrize("r,Dout", [(16, 1000), (32, 1003), (64, 136), (96, 520), (128, 264)])
 def test_fused_lora_term_accumulates(r, Dout, rng):
     """beta = 1 with the LoRA term: every channel of every row gains exactly one
     copy of the rank-r term (unselected context channels from the rank-r fill,

@@ -329,3 +329,88 @@ def test_attention_matches_sdpa_and_autograd(rng, Hq, Hkv):
     assert np.allclose(dq, qt.grad.numpy(), rtol=1e-10, atol=1e-12)
     assert np.allclose(dk, kt.grad.numpy(), rtol=1e-10, atol=1e-12)
     assert np.allclose(dv, vt.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def _layer_small(rng, B=2, S=7, Hq=4, Hkv=2, d=3, D=10, F=14, r=2):
+    T = B * S
+    roles = np.zeros(T, np.uint8)
+    for b in range(B):
+        roles[b * S + S - 2:(b + 1) * S] = 1
+    Cq, Ckv = Hq * d, Hkv * d
+    shapes = {"q": (Cq, D), "k": (Ckv, D), "v": (Ckv, D), "o": (D, Cq), "gate": (F, D),
+              "up": (F, D), "down": (D, F)}
+    inp = {"x": rng.standard_normal((T, D)) * 2.0, "dy": rng.standard_normal((T, D)),
+           "roles": roles, "scale": 2.0}
+    for p, (cout, cin) in shapes.items():
+        inp["W_" + p] = rng.standard_normal((cout, cin)) * 0.5
+        inp["A_" + p] = rng.standard_normal((r, cin)) * 0.5
+        inp["B_" + p] = rng.standard_normal((cout, r)) * 0.5
+    idx_qk = np.sort(rng.choice(Ckv, 3, replace=False)).astype(np.int32)
+    idx_vo = np.sort(rng.choice(Ckv, 4, replace=False)).astype(np.int32)
+    idx_f = np.sort(rng.choice(F, 6, replace=False)).astype(np.int32)
+    return inp, (B, S, Hq, Hkv, d), idx_qk, idx_vo, idx_f
+
+
+def test_decoder_layer_matches_autograd(rng):
+    """The layer composition against a torch build of the same layer: library
+    RMSNorm, SDPA with key/value heads repeated over each group, keep masks
+    formed from the selections by scatter and repeat_interleave, and autograd
+    for every gradient."""
+    inp, dims, idx_qk, idx_vo, idx_f = _layer_small(rng)
+    B, S, Hq, Hkv, d = dims
+    T, D = inp["x"].shape
+    fwd = ref.decoder_layer_fwd(inp, dims, idx_qk, idx_vo, idx_f)
+    bwd = ref.decoder_layer_bwd(inp, fwd, dims, idx_qk, idx_vo, idx_f)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
+    lin, s = torch.nn.functional.linear, inp["scale"]
+    ctx = torch.tensor(inp["roles"] == 0)[:, None]
+
+    def keep(n, idx):
+        m = torch.zeros(n, dtype=torch.float64)
+        m[torch.tensor(idx, dtype=torch.long)] = 1.0
+        return m
+
+    rep = lambda m: m.view(-1, d).repeat_interleave(Hq // Hkv, dim=0).reshape(-1)
+    mk_qk, mk_vo = keep(Hkv * d, idx_qk), keep(Hkv * d, idx_vo)
+    lora = lambda z, p: s * lin(lin(z, t["A_" + p]), t["B_" + p])
+    out_sparse = lambda z, p, m: torch.where(ctx, lin(z, t["W_" + p]) * m, lin(z, t["W_" + p])) + lora(z, p)
+    in_sparse = lambda z, p, m: lin(torch.where(ctx, z * m, z), t["W_" + p]) + lora(z, p)
+    n1 = torch.nn.functional.rms_norm(t["x"], (D,), eps=1e-5)
+    q, k, v = out_sparse(n1, "q", rep(mk_qk)), out_sparse(n1, "k", mk_qk), out_sparse(n1, "v", mk_vo)
+    sh = lambda a, H: a.view(B, S, H, d).transpose(1, 2)
+    a = torch.nn.functional.scaled_dot_product_attention(
+        sh(q, Hq), sh(k, Hkv).repeat_interleave(Hq // Hkv, dim=1),
+        sh(v, Hkv).repeat_interleave(Hq // Hkv, dim=1), is_causal=True).transpose(1, 2).reshape(T, -1)
+    h1 = t["x"] + in_sparse(a, "o", rep(mk_vo))
+    n2 = torch.nn.functional.rms_norm(h1, (D,), eps=1e-5)
+    mf = keep(inp["W_gate"].shape[0], idx_f)
+    h = torch.nn.functional.silu(out_sparse(n2, "gate", mf)) * out_sparse(n2, "up", mf)
+    y = h1 + in_sparse(h, "down", mf)
+    for name, val in (("a", a), ("h1", h1), ("h", h), ("y", y)):
+        assert np.allclose(val.detach().numpy(), fwd[name], rtol=1e-11, atol=1e-11), name
+    (y * t["dy"]).sum().backward()
+    assert np.allclose(t["x"].grad.numpy(), bwd["dx"], rtol=1e-9, atol=1e-10)
+    for p in ("q", "k", "v", "o", "gate", "up", "down"):
+        assert np.allclose(t["A_" + p].grad.numpy(), bwd["dA_" + p], rtol=1e-9, atol=1e-10), p
+        assert np.allclose(t["B_" + p].grad.numpy(), bwd["dB_" + p], rtol=1e-9, atol=1e-10), p
+
+
+def test_decoder_layer_all_kept_zero_lora_is_plain_layer(rng):
+    """Every channel kept and B = 0: the layer reduces to the plain dense
+    pre-norm layer (residual + attention + SwiGLU), whatever the roles."""
+    inp, dims, *_ = _layer_small(rng)
+    B, S, Hq, Hkv, d = dims
+    for p in ("q", "k", "v", "o", "gate", "up", "down"):
+        inp["B_" + p] = np.zeros_like(inp["B_" + p])
+    allkv = np.arange(Hkv * d, dtype=np.int32)
+    allf = np.arange(inp["W_gate"].shape[0], dtype=np.int32)
+    fwd = ref.decoder_layer_fwd(inp, dims, allkv, allkv, allf)
+    x = inp["x"]
+    n1 = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-5)
+    a = ref.attention_fwd(n1 @ inp["W_q"].T, n1 @ inp["W_k"].T, n1 @ inp["W_v"].T, B, S, Hq, Hkv, d)
+    h1 = x + a @ inp["W_o"].T
+    n2 = h1 / np.sqrt(np.mean(h1 * h1, axis=1, keepdims=True) + 1e-5)
+    g, u = n2 @ inp["W_gate"].T, n2 @ inp["W_up"].T
+    y = h1 + (g / (1.0 + np.exp(-g)) * u) @ inp["W_down"].T
+    assert np.allclose(fwd["y"], y, rtol=1e-12, atol=1e-12)
