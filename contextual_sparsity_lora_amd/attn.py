@@ -40,7 +40,7 @@ class SparseAttnProj:
         self.n_rep = self.Cq // self.Ckv
         assert self.Cq == self.n_rep * self.Ckv and self.Ckv == n_kv_heads * head_dim
         self.r = A_q.shape[0]
-        self.k = WB_q.shape[0]
+        self.k = WB_q.shape[0] if WB_q is not None else 0   # estimator factors: None when dense
         self.scale = float(scale)
         self.dense = dense
         self.n_qk = self.Ckv if dense else keep_count(self.Ckv, *qk_sparsity)
@@ -61,8 +61,10 @@ class SparseAttnProj:
         self.A_o, self.B_o = A_o.contiguous(), B_o.contiguous()
         self.A_qkvT = torch.empty(self.D, 3 * r, dtype=self.dtype, device=dev)
         self.A_oT = torch.empty(Cq, r, dtype=self.dtype, device=dev)
-        self.WA = WA_qkv.contiguous()                  # [D, 3k] fp32
-        self.WB_q, self.WB_k, self.WB_v = (w.contiguous() for w in (WB_q, WB_k, WB_v))
+        cont = lambda w: w.contiguous() if w is not None else None
+        self.WA = cont(WA_qkv)                         # [D, 3k] fp32
+        self.WB_q, self.WB_k, self.WB_v = (cont(w) for w in (WB_q, WB_k, WB_v))
+        assert dense or self.k > 0, "the estimator factors are required unless dense"
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):

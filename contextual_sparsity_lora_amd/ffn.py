@@ -43,7 +43,7 @@ class SparseFFN:
         self.dtype = W_gate.dtype
         self.F, self.D = W_gate.shape
         self.r = A_gate.shape[0]
-        self.k = WB_gate.shape[0]
+        self.k = WB_gate.shape[0] if WB_gate is not None else 0   # factors: None when dense
         self.scale = float(scale)
         # dense=True: the library's dense path at the same shape (every channel
         # kept, no estimator, same LoRA) -- the baseline the sparse block is
@@ -64,8 +64,10 @@ class SparseFFN:
         self.A_down, self.B_down = A_down.contiguous(), B_down.contiguous()
         self.A_guT = torch.empty(self.D, 2 * r, dtype=self.dtype, device=dev)
         self.A_dT = torch.empty(self.F, r, dtype=self.dtype, device=dev)
-        self.WA = WA_gu.contiguous()                 # [D, 2k] fp32
-        self.WB_gate, self.WB_up = WB_gate.contiguous(), WB_up.contiguous()
+        cont = lambda w: w.contiguous() if w is not None else None
+        self.WA = cont(WA_gu)                        # [D, 2k] fp32
+        self.WB_gate, self.WB_up = cont(WB_gate), cont(WB_up)
+        assert dense or self.k > 0, "the estimator factors are required unless dense"
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):

@@ -32,15 +32,17 @@ class SparseDecoderLayer:
     def from_arrays(cls, d, f32, cfg, qk_sparsity, vo_sparsity, ffn_sparsity, dense=False):
         """Build from device tensors d[...] (dtype of the layer) and fp32 factor
         tensors f32[...]: WA_qkv [D, 3k], WA_gu [D, 2k] (estimator W_A factors
-        side by side) and WB_q, WB_k, WB_v, WB_gate, WB_up."""
+        side by side) and WB_q, WB_k, WB_v, WB_gate, WB_up (may be absent when
+        dense)."""
+        f32 = dict(f32)
         attn = SparseAttnProj(d["W_q"], d["W_k"], d["W_v"], d["W_o"], d["A_q"], d["B_q"], d["A_k"],
-                              d["B_k"], d["A_v"], d["B_v"], d["A_o"], d["B_o"], f32["WA_qkv"],
-                              f32["WB_q"], f32["WB_k"], f32["WB_v"], cfg.lora_scale, cfg.n_kv_heads,
+                              d["B_k"], d["A_v"], d["B_v"], d["A_o"], d["B_o"], f32.get("WA_qkv"),
+                              f32.get("WB_q"), f32.get("WB_k"), f32.get("WB_v"), cfg.lora_scale, cfg.n_kv_heads,
                               cfg.head_dim, qk_sparsity=qk_sparsity, vo_sparsity=vo_sparsity,
                               dense=dense)
         ffn = SparseFFN(d["W_gate"], d["W_up"], d["W_down"], d["A_gate"], d["B_gate"], d["A_up"],
-                        d["B_up"], d["A_down"], d["B_down"], f32["WA_gu"], f32["WB_gate"],
-                        f32["WB_up"], cfg.lora_scale, sparsity=ffn_sparsity, dense=dense)
+                        d["B_up"], d["A_down"], d["B_down"], f32.get("WA_gu"), f32.get("WB_gate"),
+                        f32.get("WB_up"), cfg.lora_scale, sparsity=ffn_sparsity, dense=dense)
         return cls(attn, ffn, cfg.batch, cfg.seq, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim)
 
     def _alloc(self, T, D, dev, dt):

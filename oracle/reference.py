@@ -346,6 +346,35 @@ def decoder_layer_bwd(inp, fwd, dims, idx_qk, idx_vo, idx_ffn, dy=None):
     return g
 
 
+def decoder_stack_fwd(layers, x, roles, scale, dims, sels, eps=1e-5):
+    """Forward of a stack of decoder layers: layer l reads the output of layer
+    l - 1 (the first reads x); each layer has its own weights and its own
+    selections sels[l] = (idx_qk, idx_vo, idx_ffn).  Returns the per-layer
+    forward records; the stack output is the last record's "y"."""
+    fwds, h = [], np.asarray(x, f64)
+    for lw, sel in zip(layers, sels):
+        f = decoder_layer_fwd(dict(lw, x=h, roles=roles, scale=scale), dims, *sel, eps=eps)
+        fwds.append(f)
+        h = f["y"]
+    return fwds
+
+
+def decoder_stack_bwd(layers, x, roles, scale, fwds, dy, dims, sels):
+    """Backward of ``decoder_stack_fwd`` for upstream dy at the top: the
+    gradient leaving layer l is the upstream gradient of layer l - 1.  Returns
+    the per-layer backward records (index = layer); the stack input gradient is
+    record 0's "dx"."""
+    n = len(layers)
+    bwds = [None] * n
+    g = np.asarray(dy, f64)
+    for l in range(n - 1, -1, -1):
+        xin = x if l == 0 else fwds[l - 1]["y"]
+        inp = dict(layers[l], x=xin, roles=roles, scale=scale)
+        bwds[l] = decoder_layer_bwd(inp, fwds[l], dims, *sels[l], dy=g)
+        g = bwds[l]["dx"]
+    return bwds
+
+
 def max_abs_rel(got, ref):
     """max |got - ref| / max(max |ref|, 1e-30), per tensor."""
     got, ref = np.asarray(got, f64), np.asarray(ref, f64)

@@ -21,7 +21,11 @@ def gpu_available():
         return False
 
 
-@pytest.fixture(scope="session")
-def rng():
+@pytest.fixture
+def rng(request):
+    """A generator of its own per test, seeded from the test's id, so that a
+    test's draws do not depend on which tests ran before it."""
+    import zlib
+
     import numpy as np
-    return np.random.default_rng(12345)
+    return np.random.default_rng([12345, zlib.crc32(request.node.nodeid.encode())])

@@ -351,20 +351,15 @@ def _layer_small(rng, B=2, S=7, Hq=4, Hkv=2, d=3, D=10, F=14, r=2):
     return inp, (B, S, Hq, Hkv, d), idx_qk, idx_vo, idx_f
 
 
-def test_decoder_layer_matches_autograd(rng):
-    """The layer composition against a torch build of the same layer: library
-    RMSNorm, SDPA with key/value heads repeated over each group, keep masks
-    formed from the selections by scatter and repeat_interleave, and autograd
-    for every gradient."""
-    inp, dims, idx_qk, idx_vo, idx_f = _layer_small(rng)
+def _torch_layer(t, h, dims, roles, sel, s):
+    """A torch build of one sparse decoder layer: library RMSNorm, SDPA with
+    key/value heads repeated over each group, keep masks formed from the
+    selections by scatter and repeat_interleave (t: the layer's weight tensors)."""
     B, S, Hq, Hkv, d = dims
-    T, D = inp["x"].shape
-    fwd = ref.decoder_layer_fwd(inp, dims, idx_qk, idx_vo, idx_f)
-    bwd = ref.decoder_layer_bwd(inp, fwd, dims, idx_qk, idx_vo, idx_f)
-    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
-         for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
-    lin, s = torch.nn.functional.linear, inp["scale"]
-    ctx = torch.tensor(inp["roles"] == 0)[:, None]
+    idx_qk, idx_vo, idx_f = sel
+    T, D = h.shape
+    lin = torch.nn.functional.linear
+    ctx = torch.tensor(roles == 0)[:, None]
 
     def keep(n, idx):
         m = torch.zeros(n, dtype=torch.float64)
@@ -376,24 +371,64 @@ def test_decoder_layer_matches_autograd(rng):
     lora = lambda z, p: s * lin(lin(z, t["A_" + p]), t["B_" + p])
     out_sparse = lambda z, p, m: torch.where(ctx, lin(z, t["W_" + p]) * m, lin(z, t["W_" + p])) + lora(z, p)
     in_sparse = lambda z, p, m: lin(torch.where(ctx, z * m, z), t["W_" + p]) + lora(z, p)
-    n1 = torch.nn.functional.rms_norm(t["x"], (D,), eps=1e-5)
+    n1 = torch.nn.functional.rms_norm(h, (D,), eps=1e-5)
     q, k, v = out_sparse(n1, "q", rep(mk_qk)), out_sparse(n1, "k", mk_qk), out_sparse(n1, "v", mk_vo)
     sh = lambda a, H: a.view(B, S, H, d).transpose(1, 2)
     a = torch.nn.functional.scaled_dot_product_attention(
         sh(q, Hq), sh(k, Hkv).repeat_interleave(Hq // Hkv, dim=1),
         sh(v, Hkv).repeat_interleave(Hq // Hkv, dim=1), is_causal=True).transpose(1, 2).reshape(T, -1)
-    h1 = t["x"] + in_sparse(a, "o", rep(mk_vo))
+    h1 = h + in_sparse(a, "o", rep(mk_vo))
     n2 = torch.nn.functional.rms_norm(h1, (D,), eps=1e-5)
-    mf = keep(inp["W_gate"].shape[0], idx_f)
-    h = torch.nn.functional.silu(out_sparse(n2, "gate", mf)) * out_sparse(n2, "up", mf)
-    y = h1 + in_sparse(h, "down", mf)
-    for name, val in (("a", a), ("h1", h1), ("h", h), ("y", y)):
+    mf = keep(t["W_gate"].shape[0], idx_f)
+    hh = torch.nn.functional.silu(out_sparse(n2, "gate", mf)) * out_sparse(n2, "up", mf)
+    return {"a": a, "h1": h1, "h": hh, "y": h1 + in_sparse(hh, "down", mf)}
+
+
+_LIN = ("q", "k", "v", "o", "gate", "up", "down")
+
+
+def test_decoder_layer_matches_autograd(rng):
+    """The layer composition against the torch build of the same layer, with
+    autograd for every gradient."""
+    inp, dims, idx_qk, idx_vo, idx_f = _layer_small(rng)
+    fwd = ref.decoder_layer_fwd(inp, dims, idx_qk, idx_vo, idx_f)
+    bwd = ref.decoder_layer_bwd(inp, fwd, dims, idx_qk, idx_vo, idx_f)
+    t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+         for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
+    o = _torch_layer(t, t["x"], dims, inp["roles"], (idx_qk, idx_vo, idx_f), inp["scale"])
+    for name, val in o.items():
         assert np.allclose(val.detach().numpy(), fwd[name], rtol=1e-11, atol=1e-11), name
-    (y * t["dy"]).sum().backward()
+    (o["y"] * t["dy"]).sum().backward()
     assert np.allclose(t["x"].grad.numpy(), bwd["dx"], rtol=1e-9, atol=1e-10)
-    for p in ("q", "k", "v", "o", "gate", "up", "down"):
+    for p in _LIN:
         assert np.allclose(t["A_" + p].grad.numpy(), bwd["dA_" + p], rtol=1e-9, atol=1e-10), p
         assert np.allclose(t["B_" + p].grad.numpy(), bwd["dB_" + p], rtol=1e-9, atol=1e-10), p
+
+
+def test_decoder_stack_matches_autograd(rng):
+    """Three layers with their own weights and selections: the stack
+    composition against the torch build chained by hand, autograd for the
+    input gradient and the LoRA gradients of every layer."""
+    layers, sels = [], []
+    for _ in range(3):
+        inp, dims, *sel = _layer_small(rng)
+        layers.append({k: v for k, v in inp.items() if k[:2] in ("W_", "A_", "B_")})
+        sels.append(tuple(sel))
+    x, dy, roles, s = inp["x"], inp["dy"], inp["roles"], inp["scale"]
+    fwds = ref.decoder_stack_fwd(layers, x, roles, s, dims, sels)
+    bwds = ref.decoder_stack_bwd(layers, x, roles, s, fwds, dy, dims, sels)
+    xt = torch.tensor(x, requires_grad=True)
+    ts = [{k: torch.tensor(v, requires_grad=True) for k, v in lw.items()} for lw in layers]
+    h = xt
+    for l in range(3):
+        h = _torch_layer(ts[l], h, dims, roles, sels[l], s)["y"]
+        assert np.allclose(h.detach().numpy(), fwds[l]["y"], rtol=1e-11, atol=1e-11), l
+    (h * torch.tensor(dy)).sum().backward()
+    assert np.allclose(xt.grad.numpy(), bwds[0]["dx"], rtol=1e-9, atol=1e-10)
+    for l in range(3):
+        for p in _LIN:
+            assert np.allclose(ts[l]["A_" + p].grad.numpy(), bwds[l]["dA_" + p], rtol=1e-9, atol=1e-10)
+            assert np.allclose(ts[l]["B_" + p].grad.numpy(), bwds[l]["dB_" + p], rtol=1e-9, atol=1e-10)
 
 
 def test_decoder_layer_all_kept_zero_lora_is_plain_layer(rng):
@@ -414,3 +449,35 @@ def test_decoder_layer_all_kept_zero_lora_is_plain_layer(rng):
     g, u = n2 @ inp["W_gate"].T, n2 @ inp["W_up"].T
     y = h1 + (g / (1.0 + np.exp(-g)) * u) @ inp["W_down"].T
     assert np.allclose(fwd["y"], y, rtol=1e-12, atol=1e-12)
+
+
+def test_subspace_factors_recover_a_planted_spectrum(rng):
+    """With a clear gap after the k-th singular value, the randomized subspace
+    iteration reaches the exact truncated SVD: same factors as the fp64 SVD."""
+    from workloads.gen import svd_factor_pair_subspace
+    d_in, d_out, k = 96, 200, 6
+    U, _ = np.linalg.qr(rng.standard_normal((d_in, d_in)))
+    V, _ = np.linalg.qr(rng.standard_normal((d_out, d_in)))
+    s = np.concatenate([np.linspace(5.0, 2.0, k), 0.05 * np.ones(d_in - k)])
+    W_lin = ((U * s) @ V.T).T                  # nn.Linear layout [d_out, d_in]
+    WA_t, WB = svd_factor_pair(W_lin, k)
+    RA_t, RB = svd_factor_pair_subspace(W_lin, k, np.random.default_rng(5))
+    assert np.allclose(RA_t, WA_t, atol=2e-4) and np.allclose(RB, WB, atol=2e-4)
+
+
+def test_subspace_factors_near_optimal_on_gaussian(rng):
+    """On an unstructured Gaussian weight the approximate rank-k product's
+    Frobenius error stays within 1% of the Eckart-Young optimum, and the
+    factor shapes and scaling match the exact recipe's."""
+    from workloads.gen import svd_factor_pair_subspace
+    W_lin = rng.standard_normal((300, 128)) * 0.02
+    k = 8
+    WA_t, WB = svd_factor_pair(W_lin, k)
+    RA_t, RB = svd_factor_pair_subspace(W_lin, k, np.random.default_rng(6))
+    assert RA_t.shape == WA_t.shape and RB.shape == WB.shape
+    Wm = W_lin.T
+    e_opt = np.linalg.norm(Wm - WA_t.T.astype(np.float64) @ WB)
+    e_rnd = np.linalg.norm(Wm - RA_t.T.astype(np.float64) @ RB)
+    assert e_opt <= e_rnd <= 1.01 * e_opt
+    # W_A and W_B^T share the singular values: column norms of W_A^T rows equal
+    assert np.allclose(np.linalg.norm(RA_t, axis=1), np.linalg.norm(RB, axis=1), rtol=1e-5)

@@ -32,7 +32,17 @@ _LAYER_ORDER = ["x", "W_q", "W_k", "W_v", "W_o", "W_gate", "W_up", "W_down",
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (round to nearest, ties to even); returns uint16 bits."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if np.isfinite(a).all():
+        # finite bit patterns are at most 0xFF7FFFFF, so adding at most 0x8000
+        # cannot wrap in 32 bits
+        u = a.view(np.uint32)
+        t = (u >> 16) & 1
+        t += 0x7FFF
+        t += u
+        t >>= 16
+        return t.astype(np.uint16)
+    u = a.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return u.astype(np.uint16)
 
@@ -196,4 +206,86 @@ def make_layer_inputs(cfg: Config, with_factors: bool = True, seed: int = None) 
         out["WA_t_gu"] = np.ascontiguousarray(np.concatenate([fa["gate"][0], fa["up"][0]], axis=0))
         for p in ("q", "k", "v", "gate", "up"):
             out["WB_" + p] = fa[p][1]
+    return out
+
+
+# ---------------------------------------------------------------- 32-layer stack
+#
+# The stack has 32 layers of LLaMA3-8B shape (7 weights of up to 14336 x 4096
+# per layer), too many for the exact fp64 SVD above in a test's time.  Its
+# recipe differs in two documented ways:
+#   * each layer's tensors come from child streams of SeedSequence((seed,
+#     layer)) in ``_STACK_LAYER_ORDER`` and are drawn on a thread pool;
+#   * its estimator factors are the rank-k truncated SVD from a seeded
+#     randomized subspace iteration (``svd_factor_pair_subspace``), i.e. an
+#     approximate, not the exact, top-k singular subspace.
+# Stack input x: unit-RMS rows; upstream gradient at the top: N(0, 1) on
+# output rows and 0 on context rows (the loss is taken on output tokens).
+
+_STACK_LAYER_ORDER = _LAYER_ORDER[1:-1] + ["omega_q", "omega_k", "omega_v", "omega_gate", "omega_up"]
+
+
+def svd_factor_pair_subspace(W_lin: np.ndarray, k: int, rng, oversample: int = 16, iters: int = 3):
+    """Rank-k estimator factors from a randomized subspace iteration (Halko,
+    Martinsson and Tropp 2011, Algorithms 4.4 and 5.1) on W = W_lin^T, in fp32:
+    Q spans W Omega refined by ``iters`` power steps with re-orthonormalisation,
+    then the SVD of the small matrix Q^T W.  Same output convention and sign
+    rule as ``svd_factor_pair``."""
+    Wm = np.asarray(W_lin, dtype=np.float32).T          # [D_in, D_out]
+    d_in, d_out = Wm.shape
+    p = min(k + oversample, d_in, d_out)
+    Om = rng.standard_normal((d_out, p), dtype=np.float32)
+    Q, _ = np.linalg.qr(Wm @ Om)
+    for _ in range(iters):
+        Z, _ = np.linalg.qr(Wm.T @ Q)
+        Q, _ = np.linalg.qr(Wm @ Z)
+    Ub, s, Vt = np.linalg.svd((Q.T @ Wm).astype(np.float64), full_matrices=False)
+    U = Q.astype(np.float64) @ Ub[:, :k]
+    s, V = s[:k], Vt[:k].T
+    sign = np.sign(U[np.argmax(np.abs(U), axis=0), np.arange(U.shape[1])])
+    sign[sign == 0] = 1.0
+    U, V = U * sign, V * sign
+    rs = np.sqrt(s)
+    return (np.ascontiguousarray((U * rs).T.astype(np.float32)),
+            np.ascontiguousarray((rs[:, None] * V.T).astype(np.float32)))
+
+
+def make_stack_io(cfg: Config) -> dict:
+    """Stack input x, top-of-stack upstream gradient dy, roles and scale."""
+    D, T, dt = cfg.hidden, cfg.tokens, cfg.dtype
+    g = _streams(cfg.seed, ["x", "dy"])
+    roles = roles_for(cfg)
+    dy = _normal(g["dy"], (T, D), 1.0, dt)
+    dy[roles == 0] = 0.0
+    return {"x": _rms_rows(g["x"], (T, D), dt), "dy": dy, "roles": roles, "scale": cfg.lora_scale}
+
+
+def make_stack_layer(cfg: Config, layer: int, with_factors: bool = True, workers: int = 16) -> dict:
+    """Weights, LoRA factors and estimator factors of one layer of the stack."""
+    from concurrent.futures import ThreadPoolExecutor
+    D, F, r, dt = cfg.hidden, cfg.inter, cfg.lora_rank, cfg.dtype
+    Cq, Ckv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    kids = np.random.SeedSequence((cfg.seed, layer)).spawn(len(_STACK_LAYER_ORDER))
+    g = {n: np.random.Generator(np.random.PCG64(s)) for n, s in zip(_STACK_LAYER_ORDER, kids)}
+    shapes = {"W_q": (Cq, D), "W_k": (Ckv, D), "W_v": (Ckv, D), "W_o": (D, Cq),
+              "W_gate": (F, D), "W_up": (F, D), "W_down": (D, F)}
+    jobs = {}
+    for name, shp in shapes.items():
+        p = name[2:]
+        jobs[name] = shp
+        jobs["A_" + p] = (r, shp[1])
+        jobs["B_" + p] = (shp[0], r)
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = {n: ex.submit(_normal, g[n], shp, 0.02, dt) for n, shp in jobs.items()}
+        out = {n: f.result() for n, f in futs.items()}
+        if with_factors:
+            k = cfg.est_rank
+            ff = {p: ex.submit(svd_factor_pair_subspace, out["W_" + p], k, g["omega_" + p])
+                  for p in ("q", "k", "v", "gate", "up")}
+            fa = {p: f.result() for p, f in ff.items()}
+            out["WA_t_qkv"] = np.ascontiguousarray(np.concatenate([fa[p][0] for p in "qkv"], axis=0))
+            out["WA_t_gu"] = np.ascontiguousarray(np.concatenate([fa["gate"][0], fa["up"][0]], axis=0))
+            for p in ("q", "k", "v", "gate", "up"):
+                out["WB_" + p] = fa[p][1]
+    out["roles"], out["scale"] = roles_for(cfg), cfg.lora_scale
     return out
