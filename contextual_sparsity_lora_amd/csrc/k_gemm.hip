@@ -230,6 +230,9 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
     constexpr int RUNS = PR * (BN / 8);          // 8-column runs per pass
     const int64_t M = P.M, N = P.N;
     const bool vec = P.c_cols == nullptr && (P.ldc % 8 == 0) && (((uintptr_t)P.C & 15) == 0);
+    // mapped column of this thread's column (column-map path), -1 past N
+    int64_t cn_tile = -1;
+    if (P.c_cols && !P.f32out && n0 + tid % BN < N) cn_tile = P.c_cols[n0 + tid % BN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         lds_barrier();                          // LDS free (K loop done / previous pass read)
@@ -242,15 +245,20 @@ __device__ __forceinline__ void gemm_store_lds(const GemmProblem& P, f32x16 (&ac
             }
         lds_barrier();
         if (P.c_cols && !P.f32out) {
-            // mapped columns: one element per lane, consecutive lanes on consecutive
-            // columns of one row (each store instruction covers 64 columns)
-            for (int q = tid; q < PR * BN; q += NTH) {
-                const int r = q / BN, c = q % BN;
+            // mapped columns: each thread keeps one column (its mapped channel is
+            // read once per tile) and walks the pass's rows; the row of a wave is
+            // uniform, so its map entry is one scalar load and each store
+            // instruction covers 64 consecutive columns of one row
+            constexpr int RSTEP = NTH / BN;
+            static_assert(RSTEP >= 1 && NTH % BN == 0, "one column per thread");
+            const int c = tid % BN;
+            if (cn_tile < 0) continue;
+            bf16_t* __restrict__ Ccol = (bf16_t*)P.C + cn_tile;
+            for (int r = __builtin_amdgcn_readfirstlane(tid / BN); r < PR; r += RSTEP) {
                 const int64_t m = m0 + (r / 32) * WTM + 32 * i + (r % 32);
-                const int64_t n = n0 + c;
-                if (m >= M || n >= N) continue;
+                if (m >= M) continue;
                 const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
-                bf16_t* dst = (bf16_t*)P.C + cm * P.ldc + P.c_cols[n];
+                bf16_t* dst = Ccol + cm * P.ldc;
                 float x = csr[r / 32][(r % 32) * LDC + c];
                 if (P.beta) x += bf16_to_f32(*dst);
                 *dst = f32_to_bf16(x);
@@ -653,8 +661,39 @@ __device__ __forceinline__ void nt5_dma(rsrc_t ra, rsrc_t rb, bf16_t* st, int64_
                                                  16, kin ? goff[d] : OOB_OFF, soff, 0, 0);
 }
 
+// Scheduling hints for one step (mask 0x008 MFMA, 0x100 LDS read, 0x020 global
+// read): before the step barrier, the fragment reads of the next K sub-step
+// and the stage loads are spread between the MFMAs of the current one; after
+// it, the reads of the next tile's first sub-step between the last MFMAs.
+template <int NRD, int NMF, int NSUB, int NLD>
+__device__ __forceinline__ void nt5_sched_pre() {
+#pragma unroll
+    for (int q = 0; q < NSUB; ++q) {
+#pragma unroll
+        for (int i = 0; i < NRD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NMF - NRD; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < (NLD + NSUB - 1) / NSUB) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+    }
+}
+template <int NRD, int NMF>
+__device__ __forceinline__ void nt5_sched_post() {
+    constexpr int PER = NMF / NRD;
+#pragma unroll
+    for (int i = 0; i < NRD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);
+    }
+}
+
 template <int WGM, int WGN, int BKS, int NST>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args) {
+    constexpr int GRP = 8;
     constexpr int BM = 256, BN = 256;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
@@ -675,8 +714,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     GemmProblem P;
     int t, tiles_m;
     pick_problem(args, L, P, t, tiles_m);
-    const int64_t m0 = (int64_t)(t % tiles_m) * BM;
-    const int64_t n0 = (int64_t)(t / tiles_m) * BN;
+    // grouped order: GRP tile rows at a time with M fastest inside a group, so
+    // the tiles one XCD runs together form a GRP x (32 / GRP) block of C whose
+    // A and B slices are shared in that XCD's L2
+    const int tiles_n = (int)((P.N + BN - 1) / BN);
+    const int grp = t / (GRP * tiles_n), first_m = grp * GRP;
+    const int gm = (tiles_m - first_m) < GRP ? (tiles_m - first_m) : GRP;
+    const int tg = t - grp * GRP * tiles_n;
+    const int64_t m0 = (int64_t)(first_m + tg % gm) * BM;
+    const int64_t n0 = (int64_t)(tg / gm) * BN;
     const int64_t M = P.M, N = P.N, K = P.K;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -699,9 +745,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
         }
     }
     const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
-    const int64_t nk = (K + BKS - 1) / BKS;
-    const int64_t last = nk > 0 ? nk - 1 : 0;
-    auto dma = [&](bf16_t* st, int64_t kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
+    auto dma = [&](bf16_t* st, int kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
 
     // fragment reads: row R = base + lane % 32 (base a multiple of 32), chunk 2 ks + lane / 32
     const int swz = ((lane & 31) / (8 / CPR)) % CPR;
@@ -716,57 +760,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    auto compute = [&](const bf16_t* st) {
+    // two fragment sets: the reads of sub-step ks + 1 overlap the MFMAs of ks,
+    // and the reads of the next tile's sub-step 0 (after the step barrier) the
+    // MFMAs of the last sub-step
+    constexpr int KS = BKS / 16;
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto rd = [&](const bf16_t* st, int ks, int set) {
+        const int ko = ((2 * ks + (lane >> 5)) ^ swz) * 8;
 #pragma unroll
-        for (int ks = 0; ks < BKS / 16; ++ks) {
-            const int ko = ((2 * ks + (lane >> 5)) ^ swz) * 8;
-            bf16x8 a[FM], b[FN];
+        for (int i = 0; i < FM; ++i) fa[set][i] = *(const bf16x8*)&st[arow + i * 32 * BKS + ko];
 #pragma unroll
-            for (int i = 0; i < FM; ++i) a[i] = *(const bf16x8*)&st[arow + i * 32 * BKS + ko];
+        for (int j = 0; j < FN; ++j) fb[set][j] = *(const bf16x8*)&st[brow + j * 32 * BKS + ko];
+    };
+    auto mm = [&](int set) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) b[j] = *(const bf16x8*)&st[brow + j * 32 * BKS + ko];
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int i = 0; i < FM; ++i)
-#pragma unroll
-                for (int j = 0; j < FN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-        }
+            for (int j = 0; j < FN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     };
 
-    if (K > 0) {
-        constexpr int INFL = (NST - 2) * DPT;     // this wave's loads allowed in flight at a step's end
-        dma(s0, 0);
-        if (NST == 4) {
-            dma(s1, 1 <= last ? 1 : last);
-            dma(s2, 2 <= last ? 2 : last);
-        }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));
-        __builtin_amdgcn_s_barrier();
-#define NT5_STEP(CUR, NXT, T)                                                 \
-        dma(NXT, (T) + NST - 1 <= last ? (T) + NST - 1 : last);               \
-        compute(CUR);                                                         \
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));                          \
-        __builtin_amdgcn_s_barrier();
-        if (NST == 4) {
-            for (int64_t kt = 0; kt < nk; kt += 4) {
-                NT5_STEP(s0, s3, kt)
-                if (kt + 1 >= nk) break;
-                NT5_STEP(s1, s0, kt + 1)
-                if (kt + 2 >= nk) break;
-                NT5_STEP(s2, s1, kt + 2)
-                if (kt + 3 >= nk) break;
-                NT5_STEP(s3, s2, kt + 3)
-            }
-        } else {
-            for (int64_t kt = 0; kt < nk; kt += 2) {
-                NT5_STEP(s0, s1, kt)
-                if (kt + 1 >= nk) break;
-                NT5_STEP(s1, s0, kt + 1)
-            }
-        }
-#undef NT5_STEP
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // the stages are reused below
+    // K steps rounded up to whole stage rotations (no early exit: steps past K
+    // load zeros through the out-of-range offset); K = 0 runs no step
+    const int nk = (int)((K + BKS * NST - 1) / (BKS * NST)) * NST;
+    constexpr int INFL = (NST - 2) * DPT;         // this wave's loads allowed in flight at a step's end
+    dma(s0, 0);
+    if (NST == 4) {
+        dma(s1, 1);
+        dma(s2, 2);
     }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));
+    __builtin_amdgcn_s_barrier();
+    rd(s0, 0, 0);
+#define NT5_STEP(CUR, NXTL, NXTC, T)                                          \
+    dma(NXTL, (T) + NST - 1);                                                 \
+    for (int ks = 0; ks < KS - 1; ++ks) {                                     \
+        rd(CUR, ks + 1, (ks + 1) & 1);                                        \
+        mm(ks & 1);                                                           \
+    }                                                                         \
+    nt5_sched_pre<FM + FN, FM * FN, KS - 1, DPT>();                           \
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(INFL));                              \
+    __builtin_amdgcn_s_barrier();                                             \
+    rd(NXTC, 0, KS & 1);                                                      \
+    mm((KS - 1) & 1);                                                         \
+    nt5_sched_post<FM + FN, FM * FN>();
+    if (NST == 4) {
+        for (int kt = 0; kt < nk; kt += 4) {
+            NT5_STEP(s0, s3, s1, kt)
+            NT5_STEP(s1, s0, s2, kt + 1)
+            NT5_STEP(s2, s1, s3, kt + 2)
+            NT5_STEP(s3, s2, s0, kt + 3)
+        }
+    } else {
+        for (int kt = 0; kt < nk; kt += 2) {
+            NT5_STEP(s0, s1, s1, kt)
+            NT5_STEP(s1, s0, s0, kt + 1)
+        }
+    }
+#undef NT5_STEP
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));     // the stages are reused below
     gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
     lds_f32* csr[2];
     csr[0] = (lds_f32*)s0;

@@ -67,6 +67,10 @@ class SparseFFN:
         cont = lambda w: w.contiguous() if w is not None else None
         self.WA = cont(WA_gu)                        # [D, 2k] fp32
         self.WB_gate, self.WB_up = cont(WB_gate), cont(WB_up)
+        # a second stream (default priority) for the LoRA reductions that nothing
+        # later in the block reads, so they overlap the main-branch products
+        self.side = torch.cuda.Stream(device=dev)
+        self._ev = [torch.cuda.Event() for _ in range(4)]
         assert dense or self.k > 0, "the estimator factors are required unless dense"
         self._T = None
 
@@ -106,6 +110,14 @@ class SparseFFN:
         F, r = self.F, self.r
         self._alloc(T, T_c, T - T_c, x.device)
         self.x = x
+        main = torch.cuda.current_stream(x.device)
+        # LoRA down-projection of the block input on the side stream, while the
+        # estimator, scoring and selection run on the main stream
+        self._ev[0].record(main)
+        self.side.wait_event(self._ev[0])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
+            self._ev[1].record(self.side)
         ops.token_split(roles, self.ctx_rows, self.out_rows)
         if not self.dense:
             # estimator on context tokens, SwiGLU-L2 criterion, top-n (shared by gate/up/down)
@@ -113,10 +125,9 @@ class SparseFFN:
             ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
                              scores=self.scores, off0=0, off1=self.k)
             ops.stack_index(self.idx, F, 2, self.idx2)
-        # LoRA down-projection of the block input, then the gate|up main branch
-        # (dense output rows, gathered channels for context rows) with the
-        # LoRA term fused into the same accumulators
-        ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
+        main.wait_event(self._ev[1])
+        # the gate|up main branch (dense output rows, gathered channels for
+        # context rows) with the LoRA term fused into the same accumulators
         ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
                               lora=(self.xl_gu, self.B_bd, 2 * r, self.scale))
         g, u = self.gu[:, :F], self.gu[:, F:]
@@ -129,23 +140,39 @@ class SparseFFN:
 
     def backward(self, dy):
         F, D, r, s = self.F, self.D, self.r, self.scale
-        # down: LoRA gB, dA, dB; then dh with the LoRA input-gradient term fused
-        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.h, None, self.B_down, s,
-                         self.xl_dn, dy=dy, dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F)
+        main = torch.cuda.current_stream(dy.device)
+        # down: LoRA gB (main stream: the dh product reads it); dA and dB on the
+        # side stream, overlapping the dh product
+        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_down, s, None, dy=dy, gB=self.gB_dn,
+                         D_in=F, r=r)
+        self._ev[0].record(main)
+        self.side.wait_event(self._ev[0])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.h, None, None, s, self.xl_dn, dy=dy,
+                             dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
         ops.transpose(self.A_down, self.A_dT)
         ops.sparse_linear_bwd("in", dy, None, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx,
                               self.dh, lora=(self.gB_dn, self.A_dT, r, s))
         g, u = self.gu[:, :F], self.gu[:, F:]
         dg, du = self.dgu[:, :F], self.dgu[:, F:]
         ops.swiglu_bwd(self.dh, g, u, dg, du)
-        # gate|up: gB and dA for both through the block-diagonal B, dB per projection
-        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA, self.x, None, self.B_bd, s, None, dy=self.dgu,
-                         dA=self.dA_gu, gB=self.gB_gu, D_in=D)
-        ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,
-                         dB=self.dB_gate, r=r, D_in=D)
-        ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
-                         dB=self.dB_up, r=r, D_in=D)
+        # gate|up: gB for both through the block-diagonal B (main stream); dA
+        # and the per-projection dB on the side stream, overlapping the dx product
+        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_bd, s, None, dy=self.dgu, gB=self.gB_gu,
+                         D_in=D, r=2 * r)
+        self._ev[1].record(main)
+        self.side.wait_event(self._ev[1])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=self.dgu, dA=self.dA_gu,
+                             gB=self.gB_gu, D_in=D, r=2 * r)
+            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,
+                             dB=self.dB_gate, r=r, D_in=D)
+            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
+                             dB=self.dB_up, r=r, D_in=D)
+            self._ev[2].record(self.side)
         ops.transpose(self.A_gu, self.A_guT)
         ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
                               self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s))
+        # the block's gradients are complete when both streams are
+        main.wait_event(self._ev[2])
         return self.dx

@@ -30,17 +30,26 @@ def _dev(t: torch.Tensor) -> int:
 
 
 def handle(device: int):
-    """Per-device library handle, bound to torch's current stream at each call."""
+    """Library handle for torch's current stream of the device: one handle (and
+    one workspace) per (device, stream), so calls enqueued on different streams
+    never share scratch memory."""
     L = _lib.load()
-    h = _handles.get(device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    key = (device, stream)
+    h = _handles.get(key)
     if h is None:
         p = ctypes.c_void_p()
         st = L.sl_create(ctypes.byref(p), device)
         if st != 0:
             raise SLError(f"sl_create({device}) failed: {L.sl_status_str(st).decode()}")
-        h = _handles[device] = p
-    L.sl_set_stream(h, ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream))
+        h = _handles[key] = p
+        L.sl_set_stream(h, ctypes.c_void_p(stream))
     return h
+
+
+def _device_handles(device: int):
+    handle(device)
+    return [h for (d, _), h in _handles.items() if d == device]
 
 
 def _check(h, st, what):
@@ -76,18 +85,18 @@ def _vec(t):
 
 
 def sync(device: int = 0):
-    h = handle(device)
-    _check(h, _lib.load().sl_sync(h), "sl_sync")
+    for h in _device_handles(device):
+        _check(h, _lib.load().sl_sync(h), "sl_sync")
 
 
 def timing_enable(device: int, enable: bool):
-    h = handle(device)
-    _check(h, _lib.load().sl_timing_enable(h, int(enable)), "sl_timing_enable")
+    for h in _device_handles(device):
+        _check(h, _lib.load().sl_timing_enable(h, int(enable)), "sl_timing_enable")
 
 
 def timing_reset(device: int):
-    h = handle(device)
-    _check(h, _lib.load().sl_timing_reset(h), "sl_timing_reset")
+    for h in _device_handles(device):
+        _check(h, _lib.load().sl_timing_reset(h), "sl_timing_reset")
 
 
 def timing_classes():
@@ -102,14 +111,20 @@ def timing_classes():
 
 
 def timing_query(device: int, kernel_class: str):
-    """(launches, total_ms, flops, bytes) recorded for one kernel class."""
-    h = handle(device)
-    n = ctypes.c_int64()
-    ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
-    st = _lib.load().sl_timing_query(h, kernel_class.encode(), ctypes.byref(n), ctypes.byref(ms),
-                                     ctypes.byref(fl), ctypes.byref(by))
-    _check(h, st, "sl_timing_query")
-    return n.value, ms.value, fl.value, by.value
+    """(launches, total_ms, flops, bytes) recorded for one kernel class, summed
+    over the device's handles (streams)."""
+    tot = [0, 0.0, 0.0, 0.0]
+    for h in _device_handles(device):
+        n = ctypes.c_int64()
+        ms, fl, by = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+        st = _lib.load().sl_timing_query(h, kernel_class.encode(), ctypes.byref(n), ctypes.byref(ms),
+                                         ctypes.byref(fl), ctypes.byref(by))
+        _check(h, st, "sl_timing_query")
+        tot[0] += n.value
+        tot[1] += ms.value
+        tot[2] += fl.value
+        tot[3] += by.value
+    return tuple(tot)
 
 
 def token_split(roles, ctx_rows, out_rows):
