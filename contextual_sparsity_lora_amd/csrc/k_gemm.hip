@@ -40,7 +40,27 @@ struct GemmArgs {
     int first[MAXP + 1];   // first tile of each problem (prefix sums)
     int tiles_m[MAXP];
     int nprob;
+    int grp;               // tile rows per group of the tile order
+    // split tail: tiles [dp, total) each run as sks K-chunks whose fp32
+    // partial tiles go to skws (in the accumulator layout); a second launch
+    // sums them and runs the epilogue.  sks = 0: every tile whole.
+    int dp;
+    int sks;
+    float* skws;
 };
+
+// Tile order inside a problem: groups of `grp` tile rows, M fastest inside a
+// group, so the tiles that one XCD runs together (a contiguous run of ids)
+// form a grp-row block of C whose A and B slices that XCD's L2 shares.
+__device__ __forceinline__ void tile_origin(int t, int tiles_m, int64_t N, int BM, int BN, int grp,
+                                            int64_t& m0, int64_t& n0) {
+    const int tiles_n = (int)((N + BN - 1) / BN);
+    const int g = t / (grp * tiles_n), first_m = g * grp;
+    const int gm = (tiles_m - first_m) < grp ? (tiles_m - first_m) : grp;
+    const int tg = t - g * grp * tiles_n;
+    m0 = (int64_t)(first_m + tg % gm) * BM;
+    n0 = (int64_t)(tg / gm) * BN;
+}
 
 __device__ __forceinline__ void pick_problem(const GemmArgs& args, int L, GemmProblem& P, int& t,
                                              int& tiles_m) {
@@ -507,7 +527,7 @@ __device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
 }
 
 
-template <int BM, int BN, int WGM, int WGN, int NSET>
+template <int BM, int BN, int WGM, int WGN, int NSET, bool PART = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) {
     constexpr int NTH = 64 * WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -518,12 +538,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
     bf16_t* As = smem;
     bf16_t* Bs = smem + 2 * BM * LDK;
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    // PART: block u is K-chunk u % sks of tail tile dp + u / sks (the quotients
+    // are formed on the vector unit; they are block-uniform); else whole tiles
+    constexpr bool part = PART;
+    const int u = part ? (int)blockIdx.x : 0;
+    const int sk1 = args.sks > 1 ? args.sks : 1;
+    const int L = part ? __builtin_amdgcn_readfirstlane(args.dp + u / sk1) : xcd_remap(blockIdx.x, gridDim.x);
+    const int q = part ? __builtin_amdgcn_readfirstlane(u % sk1) : 0;
     GemmProblem P;
     int t, tiles_m;
     pick_problem(args, L, P, t, tiles_m);
-    const int64_t m0 = (int64_t)(t % tiles_m) * BM;
-    const int64_t n0 = (int64_t)(t / tiles_m) * BN;
+    int64_t m0, n0;
+    tile_origin(t, tiles_m, P.N, BM, BN, args.grp, m0, n0);
     const int64_t M = P.M, N = P.N, K = P.K;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid % WGM, wn = wid / WGM;
@@ -541,9 +567,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
         boff[c] = n < N ? (uint32_t)(((P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb + kc8) * 2) : OOB_OFF;
     }
     const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
-    const int64_t nk = (K + BK - 1) / BK;
+    // K steps [kb, kb + nk): the whole K, or chunk q of sks
+    const int64_t nk_all = (K + BK - 1) / BK;
+    int64_t kb = 0, nk = nk_all;
+    if (part) {
+        const int64_t kc = (nk_all + args.sks - 1) / args.sks;
+        kb = q * kc;
+        nk = nk_all - kb < kc ? nk_all - kb : kc;
+        if (nk < 0) nk = 0;
+    }
 
-    auto load = [&](uint4 (&sa)[ACH], uint4 (&sb)[BCH], int64_t kt) {
+    auto load = [&](uint4 (&sa)[ACH], uint4 (&sb)[BCH], int64_t kt0) {
+        const int64_t kt = kb + kt0;
         const uint32_t soff = (uint32_t)(kt * BK * 2);
         const bool kin = kt * BK + kc8 < K;   // whole 8-element chunk inside K (K % 8 == 0)
 #pragma unroll
@@ -623,6 +658,63 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
             lds_barrier();
         }
     }
+    if (part) {
+        // raw fp32 partial in the accumulator layout: 16-byte runs
+        // acc[i][j][4g .. 4g+3] of each lane, a 1 KB row of lanes per store
+        // (buffer stores: one lane offset, the run offset in a scalar)
+        const rsrc_t rw = make_rsrc(args.skws + (size_t)u * BM * BN + (size_t)wid * FM * FN * 16 * 64);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint4 d = make_uint4(__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                                               __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3]));
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, d),
+                                                           rw, lane * 16, ((i * FN + j) * 4 + g) * 1024, 0);
+                }
+        return;
+    }
+    gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
+    gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, (float*)smem);
+}
+
+// Split tail, second launch: tile dp + blockIdx.x sums its sks partials in
+// chunk order (deterministic), then runs the same epilogue as a whole tile.
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_fixup_kernel(GemmArgs args) {
+    constexpr int WTM = BM / WGM, WTN = BN / WGN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    const int L = args.dp + (int)blockIdx.x;
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, L, P, t, tiles_m);
+    int64_t m0, n0;
+    tile_origin(t, tiles_m, P.N, BM, BN, args.grp, m0, n0);
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int wm = wid % WGM, wn = wid / WGM;
+    f32x16 acc[FM][FN];
+    const float* __restrict__ w0 = args.skws + (size_t)blockIdx.x * args.sks * BM * BN +
+                                   (size_t)wid * FM * FN * 16 * 64;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float* w = w0 + ((i * FN + j) * 4 + g) * 256 + lane * 4;
+                float4 v = *(const float4*)w;
+                for (int c = 1; c < args.sks; ++c) {
+                    const float4 x = *(const float4*)(w + (size_t)c * BM * BN);
+                    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
+                }
+                acc[i][j][4 * g] = v.x;
+                acc[i][j][4 * g + 1] = v.y;
+                acc[i][j][4 * g + 2] = v.z;
+                acc[i][j][4 * g + 3] = v.w;
+            }
     gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
     gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, (float*)smem);
 }
@@ -693,7 +785,6 @@ __device__ __forceinline__ void nt5_sched_post() {
 
 template <int WGM, int WGN, int BKS, int NST>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args) {
-    constexpr int GRP = 8;
     constexpr int BM = 256, BN = 256;
     constexpr int NW = WGM * WGN;
     constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
@@ -714,15 +805,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     GemmProblem P;
     int t, tiles_m;
     pick_problem(args, L, P, t, tiles_m);
-    // grouped order: GRP tile rows at a time with M fastest inside a group, so
-    // the tiles one XCD runs together form a GRP x (32 / GRP) block of C whose
-    // A and B slices are shared in that XCD's L2
-    const int tiles_n = (int)((P.N + BN - 1) / BN);
-    const int grp = t / (GRP * tiles_n), first_m = grp * GRP;
-    const int gm = (tiles_m - first_m) < GRP ? (tiles_m - first_m) : GRP;
-    const int tg = t - grp * GRP * tiles_n;
-    const int64_t m0 = (int64_t)(first_m + tg % gm) * BM;
-    const int64_t n0 = (int64_t)(tg / gm) * BN;
+    int64_t m0, n0;
+    tile_origin(t, tiles_m, P.N, BM, BN, args.grp, m0, n0);
     const int64_t M = P.M, N = P.N, K = P.K;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -898,6 +982,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
 GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn) {
     GemmArgs a = {};
     a.nprob = nprob;
+    // SL_GEMM_GRP overrides the tile-row group of the tile order (tuning sweeps)
+    const char* ge = getenv("SL_GEMM_GRP");
+    const int grp_env = ge ? atoi(ge) : 0;
+    a.grp = grp_env > 0 ? grp_env : 8;
     a.first[0] = 0;
     for (int i = 0; i < MAXP; ++i) {
         if (i < nprob) {
@@ -911,6 +999,9 @@ GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn) {
             a.first[i + 1] = a.first[i];
         }
     }
+    a.dp = a.first[MAXP];   // every tile whole unless a launcher plans a split tail
+    a.sks = 0;
+    a.skws = nullptr;
     return a;
 }
 
@@ -963,8 +1054,33 @@ __global__ void splitk_reduce_kernel(const float* __restrict__ part, int64_t S, 
 
 namespace {
 
+// Split-tail plan for a launch of `total` 256 x 256 tiles on ncu compute
+// units: the last (total mod ncu) tiles would run as a partial round; split
+// each into s K-chunks (s = ncu / rem, at most 8, each chunk at least 4 K
+// steps) so that the chunks fill one round.  Returns s (0: no split) and the
+// number of whole tiles.
+int split_tail_plan(const GemmArgs& a, int ncu, int& dp) {
+    const int total = a.first[MAXP];
+    dp = total;
+    if (ncu <= 0 || total <= 0) return 0;
+    const int rem = total % ncu;
+    if (rem == 0) return 0;
+    int sks = ncu / rem;
+    if (sks > 8) sks = 8;
+    // every tail tile must have K steps for sks chunks of >= 4 steps
+    for (int i = 0; i < a.nprob; ++i) {
+        if (a.first[i + 1] <= total - rem) continue;      // no tail tile in problem i
+        const int64_t nk = (a.p[i].K + BK - 1) / BK;
+        while (sks >= 2 && nk < 4 * sks) --sks;
+    }
+    if (sks < 2) return 0;
+    dp = total - rem;
+    return sks;
+}
+
 template <int BM, int BN, int WGM, int WGN, int NSET>
-hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
+hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
+                         size_t skws_floats, int ncu) {
     GemmArgs a = make_args(probs, nprob, BM, BN);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
@@ -972,12 +1088,31 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st) {
     const size_t lds = (size_t)2 * (BM + BN) * LDK * sizeof(bf16_t);
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_nt_kernel<BM, BN, WGM, WGN, NSET>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
+        const void* fns[3] = {(const void*)gemm_nt_kernel<BM, BN, WGM, WGN, NSET, false>,
+                              (const void*)gemm_nt_kernel<BM, BN, WGM, WGN, NSET, true>,
+                              (const void*)gemm_nt_fixup_kernel<BM, BN, WGM, WGN>};
+        for (const void* f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET>), dim3(total), dim3(64 * WGM * WGN), lds, st, a);
+    int dp = total;
+    int sks = (BM == 256 && BN == 256 && skws) ? split_tail_plan(a, ncu, dp) : 0;
+    if (sks && (size_t)(total - dp) * sks * BM * BN > skws_floats) sks = 0, dp = total;
+    a.dp = dp;
+    a.sks = sks;
+    a.skws = skws;
+    // whole tiles (complete rounds), then the tail's K-chunks, then their sums
+    if (dp > 0)
+        hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET, false>), dim3(dp), dim3(64 * WGM * WGN), lds,
+                           st, a);
+    if (sks) {
+        hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET, true>), dim3((total - dp) * sks),
+                           dim3(64 * WGM * WGN), lds, st, a);
+        hipLaunchKernelGGL((gemm_nt_fixup_kernel<BM, BN, WGM, WGN>), dim3(total - dp), dim3(64 * WGM * WGN), lds,
+                           st, a);
+    }
     return hipGetLastError();
 }
 
@@ -1007,22 +1142,30 @@ bool nt_v3_ok(const GemmProblem* probs, int nprob) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st) {
+size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu) {
+    GemmArgs a = make_args(probs, nprob, 256, 256);
+    int dp;
+    const int sks = split_tail_plan(a, ncu, dp);
+    return sks ? (size_t)(a.first[MAXP] - dp) * sks * 256 * 256 : 0;
+}
+
+hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
+                            size_t skws_floats, int ncu) {
     // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
     const char* env = getenv("SL_GEMM_CFG");
     int cfg = env ? atoi(env) : 10;
     if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {
         switch (cfg) {
-            case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
-            case 12: return launch_nt_cfg<256, 256, 2, 4, 1>(probs, nprob, st);
-            case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st);
-            case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st);
-            case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st);
+            case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
+            case 12: return launch_nt_cfg<256, 256, 2, 4, 1>(probs, nprob, st, nullptr, 0, ncu);
+            case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu);
+            case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu);
+            case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st, nullptr, 0, ncu);
             case 20: return launch_nt5<2, 4, 32, 4>(probs, nprob, st);
             case 21: return launch_nt5<2, 2, 32, 4>(probs, nprob, st);
             case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st);
             case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st);
-            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st);
+            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
         }
     }
     if (cfg >= 10) cfg = 2;

@@ -213,6 +213,7 @@ sl_status sl_destroy(sl_handle* h) {
     DeviceGuard g(h->device);
     (void)hipStreamSynchronize(h->stream);
     if (h->ws) (void)hipFree(h->ws);
+    if (h->gws) (void)hipFree(h->gws);
     if (h->dev_flags) (void)hipFree(h->dev_flags);
     for (auto& t : h->timed) {
         (void)hipEventDestroy(t.start);
@@ -423,9 +424,35 @@ sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t o
 
 // ---------------------------------------------------------------- a6/a7
 static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem* p, int np) {
+    float* skws = nullptr;
+    size_t skf = 0;
+    // SL_GEMM_SPLIT=0 turns the split tail off (tuning comparisons)
+    const char* split_env = getenv("SL_GEMM_SPLIT");
+    const bool split_on = !(split_env && split_env[0] == '0');
+    if (dt == SL_BF16 && !nn && split_on) {
+        // scratch for the split tail (partial tiles of the last, partial round)
+        skf = gemm_split_tail_floats(p, np, h->num_cu);
+        if (skf && skf * 4 > h->gws_bytes) {
+            const size_t want = skf * 4 + (skf >> 1) + 4096;
+            if (h->gws) {
+                SL_HIP(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+                SL_HIP(h, hipFree(h->gws), "hipFree");
+                h->gws = nullptr;
+                h->gws_bytes = 0;
+            }
+            if (hipMalloc(&h->gws, want) != hipSuccess) {
+                (void)hipGetLastError();
+                h->gws = nullptr;          // no scratch: the launch runs every tile whole
+            } else {
+                h->gws_bytes = want;
+            }
+        }
+        if (h->gws) skws = (float*)h->gws;
+        skf = h->gws_bytes / 4;
+    }
     Timed tm(h, dt == SL_BF16 ? (nn ? K_GEMM_NN : K_GEMM_NT) : K_GEMM_F32, gemm_flops(p, np),
              gemm_bytes(p, np, esize(dt)));
-    hipError_t e = dt == SL_BF16 ? launch_gemm_bf16(nn, p, np, h->stream)
+    hipError_t e = dt == SL_BF16 ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu)
                                  : launch_gemm_f32(nn, p, np, h->stream);
     return hip_check(h, e, "gemm");
 }

@@ -23,6 +23,8 @@ struct sl_handle {
     hipStream_t stream = nullptr;
     void* ws = nullptr;          // workspace (device)
     size_t ws_bytes = 0;
+    void* gws = nullptr;         // GEMM split-tail partial tiles (device)
+    size_t gws_bytes = 0;
     int* dev_flags = nullptr;    // device error flags (token split count mismatch, ...)
     int num_cu = 256;
     std::string err;
@@ -64,7 +66,12 @@ struct GemmProblem {
 };
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
-hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
+// skws: fp32 scratch for the split tail of the default NT configuration (the
+// partial round's tiles run as K-chunks); nullptr or too small: no split
+hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st,
+                            float* skws = nullptr, size_t skws_floats = 0, int ncu = 256);
+// floats of scratch the split tail of these problems wants (0: none)
+size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu);
 // rank-r term only (K = 0 problem), bf16 output
 // y[rows[m], c] (+)= scale * P[rows[m], :] . B[c, :] over all C channels (bf16 y,
 // fp32 P, bf16 B [C, r]); beta = 0 writes every channel, beta = 1 only the

@@ -245,3 +245,44 @@ def test_fused_lora_term_accumulates(r, Dout, rng):
     assert mar(host(y), want) <= TOL["bf16"]
     drop = np.setdiff1d(np.arange(Dout), idx)
     assert mar(host(y)[np.ix_(ctx, drop)], (y0 + lora)[np.ix_(ctx, drop)]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("side", ["out", "in"])
+def test_split_tail_chunks(side, rng):
+    """A launch whose tiles do not fill the compute units runs its last partial
+    round as K-chunks summed by a second launch (long K, few tiles): the result
+    matches the oracle with the LoRA term, rows mapped, and two runs agree bit
+    for bit (the chunk sums have a fixed order)."""
+    ops = _ops()
+    roles = _roles(2, 320, 64)
+    T, Din, Dout, r, s = 640, 3072, 1100, 16, 2.0
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    print(f"[split-tail] side={side} T={T} K={Din if side == 'out' else Dout}", flush=True)
+    if side == "out":
+        idx = np.sort(rng.choice(Dout, 700, replace=False)).astype(np.int32)
+        Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+        runs = []
+        for _ in range(2):
+            y = empty_pad(T, Dout, "bf16")
+            ops.sparse_linear_fwd("out", dev_pad(x, "bf16"), dev_pad(W, "bf16"), None, c_d, o_d,
+                                  to_dev(idx, None), y, lora=(to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s))
+            runs.append(host(y))
+        want = ref.sparse_linear_fwd("out", x, W, roles, idx) + s * (P.astype(np.float64) @ Bm.T)
+    else:
+        # input side over a long K: dense output rows and gathered context rows
+        Wi = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+        idx = np.sort(rng.choice(Din, 2000, replace=False)).astype(np.int32)
+        Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+        runs = []
+        for _ in range(2):
+            y = empty_pad(T, Dout, "bf16")
+            ops.sparse_linear_fwd("in", dev_pad(x, "bf16"), dev_pad(Wi, "bf16"),
+                                  dev_pad(np.ascontiguousarray(Wi.T), "bf16"), c_d, o_d, to_dev(idx, None), y,
+                                  lora=(to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s))
+            runs.append(host(y))
+        want = ref.sparse_linear_fwd("in", x, Wi, roles, idx) + s * (P.astype(np.float64) @ Bm.T)
+    assert np.array_equal(runs[0], runs[1])
+    assert mar(runs[0], want) <= TOL["bf16"]
