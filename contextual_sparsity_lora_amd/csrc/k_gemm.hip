@@ -571,15 +571,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
     const int64_t nk_all = (K + BK - 1) / BK;
     int64_t kb = 0, nk = nk_all;
     if (part) {
-        const int64_t kc = (nk_all + args.sks - 1) / args.sks;
-        kb = q * kc;
+        // (vector-unit quotient, block-uniform: keep it in scalars so the
+        // buffer loads' offsets stay scalar)
+        const int kc = __builtin_amdgcn_readfirstlane((int)((nk_all + args.sks - 1) / args.sks));
+        kb = (int64_t)q * kc;
         nk = nk_all - kb < kc ? nk_all - kb : kc;
         if (nk < 0) nk = 0;
     }
 
     auto load = [&](uint4 (&sa)[ACH], uint4 (&sb)[BCH], int64_t kt0) {
-        const int64_t kt = kb + kt0;
-        const uint32_t soff = (uint32_t)(kt * BK * 2);
+        // the step index is block-uniform: keep the K offset a scalar operand
+        const int kt = __builtin_amdgcn_readfirstlane((int)(kb + kt0));
+        const uint32_t soff = (uint32_t)kt * (BK * 2);
         const bool kin = kt * BK + kc8 < K;   // whole 8-element chunk inside K (K % 8 == 0)
 #pragma unroll
         for (int c = 0; c < ACH; ++c) sa[c] = bload16(ra, kin ? aoff[c] : OOB_OFF, soff);
@@ -662,7 +665,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
         // raw fp32 partial in the accumulator layout: 16-byte runs
         // acc[i][j][4g .. 4g+3] of each lane, a 1 KB row of lanes per store
         // (buffer stores: one lane offset, the run offset in a scalar)
-        const rsrc_t rw = make_rsrc(args.skws + (size_t)u * BM * BN + (size_t)wid * FM * FN * 16 * 64);
+        const int wid_s = __builtin_amdgcn_readfirstlane(wid);   // (a scalar resource base)
+        const rsrc_t rw = make_rsrc(args.skws + (size_t)u * BM * BN + (size_t)wid_s * FM * FN * 16 * 64);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
