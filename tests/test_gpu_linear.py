@@ -286,3 +286,30 @@ def test_split_tail_chunks(side, rng):
         want = ref.sparse_linear_fwd("in", x, Wi, roles, idx) + s * (P.astype(np.float64) @ Bm.T)
     assert np.array_equal(runs[0], runs[1])
     assert mar(runs[0], want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,F", [("bf16", 704), ("f32", 700), ("bf16", 701), ("f32", 702)])
+def test_swiglu_on_gate_up_slices(dtype, F, rng):
+    """SwiGLU forward and backward on the gate and up halves of one stacked
+    buffer.  Rows must start on 16-byte boundaries (the kernels move 8
+    channels at once): widths that break this are refused before any launch."""
+    ops = _ops()
+    T = 37
+    gu = round_dtype(rng.standard_normal((T, 2 * F)) * 2.0, dtype)
+    dh = round_dtype(rng.standard_normal((T, F)), dtype)
+    gud = to_dev(gu, dtype)
+    h = torch.empty(T, F, dtype=tdt(dtype), device=DEV)
+    dgu = torch.empty(T, 2 * F, dtype=tdt(dtype), device=DEV)
+    esize = 2 if dtype == "bf16" else 4
+    if (F * esize) % 16:
+        with pytest.raises(ops.SLError):
+            ops.swiglu_fwd(gud[:, :F], gud[:, F:], h)
+        with pytest.raises(ops.SLError):
+            ops.swiglu_bwd(to_dev(dh, dtype), gud[:, :F], gud[:, F:], dgu[:, :F], dgu[:, F:])
+        return
+    ops.swiglu_fwd(gud[:, :F], gud[:, F:], h)
+    ops.swiglu_bwd(to_dev(dh, dtype), gud[:, :F], gud[:, F:], dgu[:, :F], dgu[:, F:])
+    g, u = gu[:, :F], gu[:, F:]
+    assert mar(host(h), ref.swiglu_fwd(g, u)) <= TOL[dtype]
+    dg_r, du_r = ref.swiglu_bwd(dh, g, u)
+    assert mar(host(dgu)[:, :F], dg_r) <= TOL[dtype] and mar(host(dgu)[:, F:], du_r) <= TOL[dtype]
