@@ -30,6 +30,7 @@ SIGNATURES = {
     "sl_timing_query": (_st, [_vp, ctypes.c_char_p, ctypes.POINTER(_i64),
                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                               ctypes.POINTER(ctypes.c_double)]),
+    "sl_timing_only": (_st, [_vp, ctypes.c_char_p]),
     "sl_timing_class_name": (ctypes.c_char_p, [_int]),
     "sl_token_split": (_st, [_vp, _vp, _i64, _vp, _i64, _vp, _i64]),
     "sl_svd_estimate": (_st, [_vp, _vp, _int, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
@@ -40,10 +41,13 @@ SIGNATURES = {
     "sl_offset_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_sparse_linear_fwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
-                                   _vp, _i64, _vp, _i64, _i64, _f]),
+                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _int]),
     "sl_sparse_linear_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
-                                   _vp, _i64, _vp, _i64, _i64, _f]),
+                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _int]),
+    "sl_weight_slice": (_st, [_vp, _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64]),
+    "sl_lora_fill_unselected": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64,
+                                      _i64, _f, _vp, _i64]),
     "sl_lora_fwd_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _i64, _f,
                               _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64]),
     "sl_swiglu_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),

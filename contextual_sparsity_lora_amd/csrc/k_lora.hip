@@ -274,7 +274,9 @@ __global__ __launch_bounds__(256) void lora_add_kernel(const float* __restrict__
 // y[rows[m], c] (+)= s * sum_j P[rows[m], j] B[c, j] for every channel c of the
 // given rows; with beta = 0 every channel is written (the main product of the
 // selected channels is launched afterwards and overwrites them), with beta = 1
-// only channels whose bit in `mask` is clear are updated.
+// only channels whose bit in `mask` is clear are updated (accumulated), with
+// beta = 2 only those are written (so the product of the selected channels may
+// run at the same time: the two write disjoint elements).
 // bf16 matrix cores (v_mfma_f32_16x16x32_bf16), channel as M, row as N, rank as
 // K: s P is rounded to bf16 as a bf16 LoRA product rounds its down-projection,
 // accumulation is fp32.  Row slot m of MFMA (g, e) is channel
@@ -363,13 +365,13 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
                 v[4 + i] = acc[1][i];
             }
             bf16_t* dst = y + row * ldy + c;
-            if (!beta && aligned && c + 8 <= C) {
-                store8<bf16_t>(dst, v);
+            const uint32_t bits = beta ? ((mask[c >> 5] >> (c & 31)) & 0xffu) : 0u;   // c % 8 == 0: one word
+            if (beta != 1 && bits == 0u && aligned && c + 8 <= C) {
+                store8<bf16_t>(dst, v);           // every channel of the run is written
             } else {
-                const uint32_t bits = beta ? (mask[c >> 5] >> (c & 31)) : 0u;   // c % 8 == 0: one word
                 for (int q = 0; q < 8; ++q) {
                     if (c + q >= C || ((bits >> q) & 1u)) continue;
-                    dst[q] = f32_to_bf16(v[q] + (beta ? bf16_to_f32(dst[q]) : 0.0f));
+                    dst[q] = f32_to_bf16(v[q] + (beta == 1 ? bf16_to_f32(dst[q]) : 0.0f));
                 }
             }
         }

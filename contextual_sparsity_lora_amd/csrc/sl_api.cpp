@@ -117,7 +117,7 @@ struct Timed {
     hipEvent_t a = nullptr, b = nullptr;
     Timed(sl_handle* h_, int cls_, double flops_, double bytes_)
         : h(h_), cls(cls_), flops(flops_), bytes(bytes_) {
-        if (!h->timing) return;
+        if (!h->timing || (h->timing_cls >= 0 && h->timing_cls != cls)) return;
         a = take_event(h);
         b = take_event(h);
         if (a && b) (void)hipEventRecord(a, h->stream);
@@ -254,6 +254,18 @@ const char* sl_last_error(const sl_handle* h) { return h ? h->err.c_str() : "nul
 sl_status sl_timing_enable(sl_handle* h, int enable) {
     if (!h) return SL_ERR_INVALID;
     h->timing = enable != 0;
+    return SL_OK;
+}
+
+sl_status sl_timing_only(sl_handle* h, const char* kernel_class) {
+    if (!h) return SL_ERR_INVALID;
+    int cls = -1;
+    if (kernel_class && *kernel_class) {
+        for (int i = 0; i < kNumClasses; ++i)
+            if (std::string(kClassNames[i]) == kernel_class) cls = i;
+        SL_REQUIRE(h, cls >= 0, "unknown kernel class '%s'", kernel_class);
+    }
+    h->timing_cls = cls;
     return SL_OK;
 }
 
@@ -507,7 +519,7 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
                      int64_t Kdim, const void* Wc, int64_t ldw, int64_t C,
                      const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
                      const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
-                     const LoraEpi& l) {
+                     const LoraEpi& l, int flags = 0) {
     if (n == C || T_c == 0) {
         GemmProblem p = problem(X, ldx, nullptr, Wc, ldw, nullptr, Z, ldz, nullptr, nullptr, T, C,
                                 Kdim, beta, l, T, C);
@@ -519,7 +531,10 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
     p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
                    C);
     const int np = 2;
-    if (l.P && dt == SL_BF16) {
+    if (flags & SL_NO_FILL) {
+        // the caller writes the unselected channels of context rows itself
+        // (sl_lora_fill_unselected), possibly while this product runs
+    } else if (l.P && dt == SL_BF16) {
         // rank-r term of the unselected channels of context rows: written for
         // every channel (beta = 0: the product below then overwrites the
         // selected ones) or, when accumulating, for the unselected ones only
@@ -562,7 +577,7 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
                     const void* Wd, int64_t ldwd, const void* Wc, int64_t ldwc, int64_t Nout,
                     const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
                     const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
-                    const LoraEpi& l) {
+                    const LoraEpi& l, const void* w_slice = nullptr, int64_t ld_w_slice = 0) {
     if (n == C || T_c == 0) {
         GemmProblem p = problem(X, ldx, nullptr, Wd, ldwd, nullptr, Z, ldz, nullptr, nullptr, T, Nout,
                                 C, beta, l, T, Nout);
@@ -590,16 +605,23 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
     const size_t part_bytes = S > 1 ? round_up((size_t)(S * T_o * Nout) * 4, 256) : 0;
     SL_CHECK(ensure_ws(h, xc_bytes + ws_bytes + part_bytes));
     void* xc = h->ws;
-    void* wsl = (char*)h->ws + xc_bytes;
+    const void* wsl = (char*)h->ws + xc_bytes;
+    int64_t ldwsl = ldn;
     float* part = (float*)((char*)h->ws + xc_bytes + ws_bytes);
     if (n > 0) {
-        Timed tm(h, K_GATHER, 0, 2.0 * (T_c + Nout) * n * esize(dt));
+        Timed tm(h, K_GATHER, 0, 2.0 * (T_c + (w_slice ? 0 : Nout)) * n * esize(dt));
         // both compacted operands are zero-padded to ldn columns, so the
-        // context product may contract over K = ldn (a multiple of 8)
+        // context product may contract over K = ldn (a multiple of 8); a weight
+        // slice built beforehand (sl_weight_slice) is used as given
         SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, ldn, xc, ldn,
                                      h->stream), "gather_cols");
-        SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, wsl, ldn,
-                                       h->stream), "gather_rows_t");
+        if (w_slice) {
+            wsl = w_slice;
+            ldwsl = ld_w_slice;
+        } else {
+            SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, (void*)wsl, ldn,
+                                           h->stream), "gather_rows_t");
+        }
     }
     GemmProblem p[5];
     int np = 0;
@@ -621,7 +643,7 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
         }
     }
     // n > 0: contract over the zero-padded width ldn; n == 0: an empty sum
-    p[np++] = problem(xc, ldn, nullptr, wsl, ldn, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
+    p[np++] = problem(xc, ldn, nullptr, wsl, ldwsl, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
                       n > 0 ? ldn : 0, beta, l, T_c, Nout);
     p[np - 1].k_alg = n;
     SL_CHECK(run_gemm(h, dt, false, p, np));
@@ -643,13 +665,19 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
                                const int32_t* out_rows, int64_t T_o, const int32_t* idx,
                                int64_t n, void* y, int64_t ldy, int beta, const float* lora_P,
                                int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
-                               int64_t lora_r, float lora_scale) {
+                               int64_t lora_r, float lora_scale, const void* w_slice,
+                               int64_t ld_w_slice, int flags) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
+    SL_REQUIRE(h, (flags & ~SL_NO_FILL) == 0, "bad flags");
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
+    if (w_slice) {
+        SL_REQUIRE(h, side == SL_SIDE_IN, "w_slice applies to side IN");
+        SL_CHECK(check_matrix(h, w_slice, ld_w_slice, (n + 7) / 8 * 8, dt, "w_slice"));
+    }
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
     const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
@@ -663,9 +691,9 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     DeviceGuard g(h->device);
     if (side == SL_SIDE_OUT)
         return out_sparse(h, dt, x, ldx, T, D_in, W, ldw, D_out, ctx_rows, T_c, out_rows, T_o, idx,
-                          n, y, ldy, beta, l);
+                          n, y, ldy, beta, l, flags);
     return in_sparse(h, dt, x, ldx, T, D_in, W, ldw, Wt, ldwt, D_out, ctx_rows, T_c, out_rows, T_o,
-                     idx, n, y, ldy, beta, l);
+                     idx, n, y, ldy, beta, l, w_slice, ld_w_slice);
 }
 
 // ---------------------------------------------------------------- a10/a11
@@ -675,13 +703,19 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
                                const int32_t* out_rows, int64_t T_o, const int32_t* idx,
                                int64_t n, void* dx, int64_t lddx, int beta, const float* lora_P,
                                int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
-                               int64_t lora_r, float lora_scale) {
+                               int64_t lora_r, float lora_scale, const void* w_slice,
+                               int64_t ld_w_slice, int flags) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
+    SL_REQUIRE(h, (flags & ~SL_NO_FILL) == 0, "bad flags");
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
+    if (w_slice) {
+        SL_REQUIRE(h, side == SL_SIDE_OUT, "w_slice applies to side OUT");
+        SL_CHECK(check_matrix(h, w_slice, ld_w_slice, (n + 7) / 8 * 8, dt, "w_slice"));
+    }
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
     const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
@@ -695,10 +729,44 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     DeviceGuard g(h->device);
     if (side == SL_SIDE_IN)   // dx = dy W: context rows produce the selected channels only
         return out_sparse(h, dt, dy, lddy, T, D_out, Wt, ldwt, D_in, ctx_rows, T_c, out_rows, T_o,
-                          idx, n, dx, lddx, beta, l);
+                          idx, n, dx, lddx, beta, l, flags);
     // side OUT: context rows contract over the selected output channels only
     return in_sparse(h, dt, dy, lddy, T, D_out, Wt, ldwt, W, ldw, D_in, ctx_rows, T_c, out_rows,
-                     T_o, idx, n, dx, lddx, beta, l);
+                     T_o, idx, n, dx, lddx, beta, l, w_slice, ld_w_slice);
+}
+
+sl_status sl_weight_slice(sl_handle* h, sl_dtype dt, const void* Wc, int64_t ldwc, int64_t C,
+                          const int32_t* idx, int64_t n, int64_t Nout, void* out, int64_t ld_out) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, C >= 1 && Nout >= 1 && n >= 1 && n <= C, "bad sizes");
+    SL_REQUIRE(h, idx != nullptr, "idx is NULL");
+    SL_CHECK(check_matrix(h, Wc, ldwc, Nout, dt, "Wc"));
+    const int64_t ldn = (n + 7) / 8 * 8;
+    SL_CHECK(check_matrix(h, out, ld_out, ldn, dt, "out"));
+    DeviceGuard g(h->device);
+    Timed tm(h, K_GATHER, 0, 2.0 * Nout * n * esize(dt));
+    return hip_check(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, out, ld_out,
+                                             h->stream), "weight_slice");
+}
+
+sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ldy, const int32_t* ctx_rows,
+                                  int64_t T_c, int64_t C, const float* lora_P, int64_t ld_lora_P,
+                                  const void* lora_B, int64_t ld_lora_B, int64_t lora_r, float lora_scale,
+                                  const int32_t* idx, int64_t n) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16, "bf16 only");
+    SL_REQUIRE(h, T_c >= 0 && C >= 1 && n >= 0 && n <= C, "bad sizes");
+    SL_REQUIRE(h, lora_r >= 1 && lora_r <= 128 && ld_lora_P >= lora_r && ld_lora_B >= lora_r, "bad rank");
+    if (T_c == 0 || n == C) return SL_OK;
+    SL_REQUIRE(h, ctx_rows && lora_P && lora_B && (n == 0 || idx), "NULL pointer");
+    SL_CHECK(check_matrix(h, y, ldy, C, dt, "y"));
+    DeviceGuard g(h->device);
+    SL_CHECK(ensure_ws(h, round_up((size_t)ceil_div(C, 32) * 4, 256)));
+    Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * lora_r, (double)T_c * (C - n) * esize(dt));
+    return hip_check(h, launch_lora_fill_rows(y, ldy, ctx_rows, T_c, C, lora_P, ld_lora_P, lora_B, ld_lora_B,
+                                              lora_r, lora_scale, idx, n, (uint32_t*)h->ws, 2, h->stream),
+                     "lora_fill_unselected");
 }
 
 // ---------------------------------------------------------------- a8/a12
@@ -708,7 +776,8 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
                           const void* dy, int64_t lddy, void* dx, int64_t lddx, float* dA,
                           float* dB, float* gB_io, int64_t ldgB) {
     if (!h) return SL_ERR_INVALID;
-    const int all = SL_LORA_XL | SL_LORA_ADD | SL_LORA_GB | SL_LORA_DA | SL_LORA_DB | SL_LORA_DX;
+    const int all = SL_LORA_XL | SL_LORA_ADD | SL_LORA_GB | SL_LORA_DA | SL_LORA_DB | SL_LORA_DX |
+                    SL_LORA_BT;
     SL_REQUIRE(h, (mode & ~all) == 0 && mode != 0, "bad mode");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, r >= 1 && r <= 128, "r must be in [1, 128]");
@@ -722,6 +791,9 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
     if (mode & (SL_LORA_XL | SL_LORA_DA)) SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
     if (mode & (SL_LORA_XL | SL_LORA_DX)) SL_CHECK(check_matrix(h, A, D_in, D_in, dt, "A"));
     if (mode & (SL_LORA_ADD | SL_LORA_GB)) SL_REQUIRE(h, B != nullptr, "B is NULL");
+    const bool bt_given = mode & SL_LORA_BT;   // B passed as B^T [r, ceil8(D_out)]
+    SL_REQUIRE(h, !bt_given || !(mode & SL_LORA_ADD), "SL_LORA_BT with SL_LORA_ADD");
+    if (bt_given && (mode & SL_LORA_GB)) SL_REQUIRE(h, aligned16(B), "B^T is not 16-byte aligned");
     if (mode & SL_LORA_ADD) SL_CHECK(check_matrix(h, y, ldy, D_out, dt, "y"));
     if (gb || db) SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
     if (da) SL_REQUIRE(h, dA != nullptr, "dA is NULL");
@@ -744,9 +816,18 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
     // gB, the rows of dA and the columns of dB are independent of each other)
     const int64_t RC = 64;
     const int64_t rc_max = r < RC ? r : RC;
+    // x A^T-type products: the split-K form (more blocks, a reduction launch)
+    // pays off only for long rows; SL_LORA_XL_SPLIT=0/1 forces a form (tuning)
+    const char* xs_env = getenv("SL_LORA_XL_SPLIT");
+    auto xl_split_for = [&](int64_t Dk) {
+        if (xs_env) return xs_env[0] != '0';
+        return Dk > 16384;
+    };
+    const bool xl_split = xl_split_for(D_in);
+    const bool gb_split = xl_split_for(D_out);
     if (mode & SL_LORA_XL) {
         float* xw = nullptr;   // split-K partials (bf16)
-        if (bf) {
+        if (bf && xl_split) {
             SL_CHECK(ensure_ws(h, round_up(lora_xl_ws_floats(T, D_in, rc_max) * 4, 256)));
             xw = (float*)h->ws;
         }
@@ -775,12 +856,14 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
         float* gB = gB_io ? gB_io : (float*)(ws + bt_bytes);
         const int64_t ldg = gB_io ? ldgB : r;
         float* part = (float*)(ws + bt_bytes + gb_bytes);
-        if (gb) SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
+        const void* Bt_use = Bt;
+        if (gb && bt_given) Bt_use = B;
+        else if (gb) SL_HIP(h, launch_transpose(bf, B, r, D_out, r, Bt, ldbt, h->stream), "transpose");
         for (int64_t c0 = 0; c0 < r; c0 += RC) {
             const int64_t rc = (r - c0) < RC ? (r - c0) : RC;
             if (gb)
-                SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, (const char*)Bt + c0 * ldbt * esize(dt),
-                                         ldbt, rc, gB + c0, ldg, bf ? part : nullptr, h->stream),
+                SL_HIP(h, launch_lora_xl(bf, dy, lddy, T, D_out, (const char*)Bt_use + c0 * ldbt * esize(dt),
+                                         ldbt, rc, gB + c0, ldg, (bf && gb_split) ? part : nullptr, h->stream),
                        "lora_gB");
             if (da)
                 SL_HIP(h, launch_outer_accum(bf, gB + c0, ldg, T, rc, x, ldx, D_in, scale, dA + c0 * D_in,

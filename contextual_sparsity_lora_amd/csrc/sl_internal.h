@@ -18,6 +18,7 @@ struct sl_timed_launch {
 struct sl_handle {
     int device = 0;
     bool timing = false;                  // record events around the main launches
+    int timing_cls = -1;                  // only launches of this class (-1: all)
     std::vector<sl_timed_launch> timed;   // launches recorded since timing was enabled
     std::vector<hipEvent_t> event_pool;
     hipStream_t stream = nullptr;

@@ -15,7 +15,7 @@ from . import _lib
 SL_F32, SL_BF16 = 0, 1
 CRIT = {"l2": 0, "swiglu": 1, "qk": 2}
 SIDE = {"out": 0, "in": 1}
-LORA_XL, LORA_ADD, LORA_GB, LORA_DA, LORA_DB, LORA_DX = 1, 2, 4, 8, 16, 32
+LORA_XL, LORA_ADD, LORA_GB, LORA_DA, LORA_DB, LORA_DX, LORA_BT = 1, 2, 4, 8, 16, 32, 64
 LORA_BWD = LORA_GB | LORA_DA | LORA_DB | LORA_DX
 
 _handles = {}
@@ -92,6 +92,12 @@ def sync(device: int = 0):
 def timing_enable(device: int, enable: bool):
     for h in _device_handles(device):
         _check(h, _lib.load().sl_timing_enable(h, int(enable)), "sl_timing_enable")
+
+
+def timing_only(device: int, kernel_class=None):
+    """Record only launches of kernel_class (None: every class)."""
+    for h in _device_handles(device):
+        _check(h, _lib.load().sl_timing_only(h, (kernel_class or "").encode()), "sl_timing_only")
 
 
 def timing_reset(device: int):
@@ -188,10 +194,16 @@ def _lora_args(lora):
     return (_ptr(P), _ld(P), _ptr(Bm), _ld(Bm), int(r), float(scale))
 
 
-def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=None):
+NO_FILL = 1
+
+
+def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=None,
+                      w_slice=None, flags=0):
     """W: frozen weight [D_out, D_in] (nn.Linear layout); Wt: its transposed
     copy [D_in, D_out] (read for side "in" only; may be None for side "out").
-    lora = (xl, B, r, scale) fuses y += scale * xl B^T into the same pass."""
+    lora = (xl, B, r, scale) fuses y += scale * xl B^T into the same pass.
+    w_slice: weight_slice(Wt, idx) built beforehand (side "in"); flags:
+    NO_FILL leaves the unselected context channels (side "out") unwritten."""
     h = handle(_dev(x))
     T, D_in = x.shape
     D_out = W.shape[0]
@@ -200,14 +212,18 @@ def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=N
                                           _ptr(W), _ld(W), _ptr(Wt), _ld(Wt) if Wt is not None else 0,
                                           D_out, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
                                           out_rows.numel(), _ptr(idx), n, _ptr(y), _ld(y), int(beta),
-                                          *_lora_args(lora))
+                                          *_lora_args(lora), _ptr(w_slice),
+                                          _ld(w_slice) if w_slice is not None else 0, int(flags))
     _check(h, st, "sl_sparse_linear_fwd")
 
 
-def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora=None):
+def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora=None,
+                      w_slice=None, flags=0):
     """Input gradient of sparse_linear_fwd.  Wt [D_in, D_out] is read by every
     product; W [D_out, D_in] only for side "out" (may be None for side "in").
-    lora = (gB, A^T, r, scale) fuses dx += scale * gB A into the same pass."""
+    lora = (gB, A^T, r, scale) fuses dx += scale * gB A into the same pass.
+    w_slice: weight_slice(W, idx) built beforehand (side "out"); flags as for
+    the forward (NO_FILL applies to side "in")."""
     h = handle(_dev(dy))
     T, D_out = dy.shape
     D_in = Wt.shape[0]
@@ -216,8 +232,29 @@ def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora
                                           _ptr(W), _ld(W) if W is not None else 0, _ptr(Wt), _ld(Wt),
                                           D_in, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
                                           out_rows.numel(), _ptr(idx), n, _ptr(dx), _ld(dx),
-                                          int(beta), *_lora_args(lora))
+                                          int(beta), *_lora_args(lora), _ptr(w_slice),
+                                          _ld(w_slice) if w_slice is not None else 0, int(flags))
     _check(h, st, "sl_sparse_linear_bwd")
+
+
+def weight_slice(Wc, idx, out):
+    """out[o, j] = Wc[idx[j], o] (zero columns up to ceil8(n)); Wc bf16 [C, Nout],
+    out bf16 [Nout, >= ceil8(n)]."""
+    h = handle(_dev(Wc))
+    C, Nout = Wc.shape
+    st = _lib.load().sl_weight_slice(h, _dt(Wc), _ptr(Wc), _ld(Wc), C, _ptr(idx), idx.numel(), Nout,
+                                     _ptr(out), _ld(out))
+    _check(h, st, "sl_weight_slice")
+
+
+def lora_fill_unselected(y, ctx_rows, lora, idx):
+    """Write the dense LoRA term alone into the unselected channels of context
+    rows of y (bf16 [T, C]); lora = (P, B, r, scale) as for sparse_linear_fwd."""
+    h = handle(_dev(y))
+    C = y.shape[1]
+    st = _lib.load().sl_lora_fill_unselected(h, _dt(y), _ptr(y), _ld(y), _ptr(ctx_rows), ctx_rows.numel(),
+                                             C, *_lora_args(lora), _ptr(idx), idx.numel())
+    _check(h, st, "sl_lora_fill_unselected")
 
 
 def lora_fwd_bwd(mode, x, A, B, scale, xl, y=None, dy=None, dx=None, dA=None, dB=None,

@@ -68,6 +68,13 @@ typedef enum {
     SL_SIDE_IN = 1    /* input channels (down, o); W is the copy [D_in, D_out]    */
 } sl_side;
 
+/* sl_sparse_linear_fwd / _bwd flag bits. */
+enum {
+    SL_NO_FILL = 1    /* side-OUT-shaped products: leave the unselected channels of
+                         context rows unwritten (the caller writes them itself,
+                         e.g. with sl_lora_fill_unselected on another stream) */
+};
+
 /* sl_lora_fwd_bwd mode bits. */
 enum {
     SL_LORA_XL = 1,   /* forward: xl = x A^T                                      */
@@ -76,6 +83,7 @@ enum {
     SL_LORA_DA = 8,   /* backward: dA = scale gB^T x                              */
     SL_LORA_DB = 16,  /* backward: dB = scale dy^T xl                             */
     SL_LORA_DX = 32,  /* backward: dx += scale gB A                               */
+    SL_LORA_BT = 64,  /* with GB: B is passed transposed, B^T [r, ceil8(D_out)]   */
     SL_LORA_BWD = 60  /* all four backward steps                                  */
 };
 
@@ -108,6 +116,11 @@ const char* sl_version(void);
  * work (flops, and HBM bytes as if every operand element were read once and
  * every result written once).  Enabling does not clear earlier records. */
 sl_status sl_timing_enable(sl_handle* h, int enable);
+/* Record only the launches of one kernel class from now on (NULL or "": every
+ * class, the default).  Each record adds two event markers to the stream,
+ * which cost time between launches; timing one class keeps that cost off the
+ * other launches.  Unknown class: SL_ERR_INVALID. */
+sl_status sl_timing_only(sl_handle* h, const char* kernel_class);
 /* Drop all records (waits for the stream first). */
 sl_status sl_timing_reset(sl_handle* h);
 /* Totals over the records of one kernel class: number of launches, summed
@@ -229,6 +242,12 @@ sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t o
  *   ctx_rows/out_rows  device int32 row lists (sl_token_split)
  *   idx device int32[n], ascending, in [0, C), C = D_out (OUT) or D_in (IN)
  *   y   device [T, ldy] (dt) out
+ *   w_slice  optional (side IN only): the context-row weight slice built
+ *       beforehand by sl_weight_slice from Wt and the same idx, dt
+ *       [D_out, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
+ *   flags  0 or SL_NO_FILL (side OUT: the unselected channels of context rows
+ *       are left unwritten; with lora_P they must be written by
+ *       sl_lora_fill_unselected, without it the caller zeroes them)
  * dt = SL_BF16 (MFMA path) or SL_F32. */
 sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* x, int64_t ldx, int64_t T, int64_t D_in,
@@ -240,7 +259,8 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                void* y, int64_t ldy, int beta,
                                const float* lora_P, int64_t ld_lora_P,
                                const void* lora_B, int64_t ld_lora_B,
-                               int64_t lora_r, float lora_scale);
+                               int64_t lora_r, float lora_scale,
+                               const void* w_slice, int64_t ld_w_slice, int flags);
 
 /* ---------------------------------------------------------------- a10/a11: main backward */
 
@@ -258,7 +278,11 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
  *   dx[t, i] += lora_scale * sum_j lora_P[t, j] * lora_B[i, j]
  * with lora_P = gB = dy B (fp32 [T, ld], from sl_lora_fwd_bwd) and
  * lora_B = A^T (dt [D_in, ld]); unselected context channels (side IN) then
- * hold this term instead of 0. */
+ * hold this term instead of 0.
+ *   w_slice  optional (side OUT only): sl_weight_slice of W with the same idx,
+ *       dt [D_in, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
+ *   flags  0 or SL_NO_FILL (side IN: unselected context channels left
+ *       unwritten, as for the forward) */
 sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* dy, int64_t lddy, int64_t T, int64_t D_out,
                                const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
@@ -269,7 +293,34 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                void* dx, int64_t lddx, int beta,
                                const float* lora_P, int64_t ld_lora_P,
                                const void* lora_B, int64_t ld_lora_B,
-                               int64_t lora_r, float lora_scale);
+                               int64_t lora_r, float lora_scale,
+                               const void* w_slice, int64_t ld_w_slice, int flags);
+
+/* Context-row weight slice of a sparse product, built ahead of the product
+ * (e.g. on another stream right after the selection) so the product itself
+ * only gathers the activations (PG §3.4 Algorithm 1 step 5, the sliced
+ * matmul; the slice is its weight operand):
+ *   out[o, j] = Wc[idx[j], o] for j < n,  out[o, j] = 0 for n <= j < ceil8(n)
+ * for o < Nout.  Wc device (dt) [C, ldwc >= Nout] (channel-major: Wt for a
+ * forward side IN product, W for a backward side OUT product); idx device
+ * int32[n] ascending in [0, C), 1 <= n; out device (dt) [Nout, ld_out >=
+ * ceil8(n)].  dt = SL_BF16 or SL_F32. */
+sl_status sl_weight_slice(sl_handle* h, sl_dtype dt, const void* Wc, int64_t ldwc, int64_t C,
+                          const int32_t* idx, int64_t n, int64_t Nout, void* out,
+                          int64_t ld_out);
+
+/* The unselected channels of context rows of a side-OUT-shaped sparse product
+ * run with SL_NO_FILL: for t in ctx_rows and c not in idx,
+ *   y[t, c] = bf16(lora_scale * sum_{j < lora_r} lora_P[t, j] * lora_B[c, j])
+ * (the dense LoRA term alone, as the fused product would write them); the
+ * selected channels are not touched, so this may run on another stream
+ * concurrently with the product.  y bf16 [T, ldy >= C]; lora_P fp32 [T,
+ * ld_lora_P]; lora_B bf16 [C, ld_lora_B]; 1 <= lora_r <= 128.  bf16 only. */
+sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ldy,
+                                  const int32_t* ctx_rows, int64_t T_c, int64_t C,
+                                  const float* lora_P, int64_t ld_lora_P, const void* lora_B,
+                                  int64_t ld_lora_B, int64_t lora_r, float lora_scale,
+                                  const int32_t* idx, int64_t n);
 
 /* ---------------------------------------------------------------- a8/a12: dense LoRA */
 
@@ -286,7 +337,10 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
  *   SL_LORA_DX:  dx += scale gB A                  (dt [T, lddx]); leave it out
  *                and pass gB to sl_sparse_linear_bwd to fuse that term there
  * Modes combine; the steps run in the order listed.  Pointers not used by the
- * mode may be NULL.  1 <= r <= 128 (r <= 64 with ADD or DX; ranks above 64
+ * mode may be NULL.  SL_LORA_BT: B holds B^T, row-major [r, ld] with ld = D_out
+ * rounded up to a multiple of 8 (a caller that keeps the transposed copy
+ * saves the per-call transpose; not with ADD).
+ * 1 <= r <= 128 (r <= 64 with ADD or DX; ranks above 64
  * run as column chunks of 64).  dA / dB are deterministic (fixed-order token
  * reduction). */
 sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt,

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from oracle import reference as ref
-from tests.gpu_util import DEV, TOL, dev_pad, empty_pad, host, mar, need_lib, tdt, to_dev
+from tests.gpu_util import DEV, TOL, bits, dev_pad, empty_pad, host, mar, need_lib, tdt, to_dev
 from workloads.gen import round_dtype
 
 pytestmark = pytest.mark.gpu
@@ -313,3 +313,135 @@ def test_swiglu_on_gate_up_slices(dtype, F, rng):
     assert mar(host(h), ref.swiglu_fwd(g, u)) <= TOL[dtype]
     dg_r, du_r = ref.swiglu_bwd(dh, g, u)
     assert mar(host(dgu)[:, :F], dg_r) <= TOL[dtype] and mar(host(dgu)[:, F:], du_r) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("r", [16, 96])
+def test_no_fill_with_concurrent_fill_and_prebuilt_slices(r, rng):
+    """The split form of a product equals the one-call form bit for bit: with
+    NO_FILL the product leaves the unselected context channels as they were,
+    lora_fill_unselected (run on another stream at the same time) writes
+    exactly those, and a weight slice built beforehand by weight_slice replaces
+    the one the product would gather itself."""
+    ops = _ops()
+    roles = _roles(2, 300, 70)
+    T, Din, Dout, s = 600, 520, 1000, 2.0
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    print(f"[split-form] r={r}", flush=True)
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    Bo = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+    Bi = round_dtype(rng.standard_normal((Din, r)) * 0.3, "bf16")
+    idx_o = np.sort(rng.choice(Dout, 333, replace=False)).astype(np.int32)
+    idx_i = np.sort(rng.choice(Din, 181, replace=False)).astype(np.int32)
+    xd, Wd, Wtd = dev_pad(x, "bf16"), dev_pad(W, "bf16"), dev_pad(np.ascontiguousarray(W.T), "bf16")
+    Pd, Bod, Bid = to_dev(P, "f32"), dev_pad(Bo, "bf16"), dev_pad(Bi, "bf16")
+    io_d, ii_d = to_dev(idx_o, None), to_dev(idx_i, None)
+    dy = round_dtype(rng.standard_normal((T, Dout)), "bf16")
+    dyd = dev_pad(dy, "bf16")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    drop_o = np.setdiff1d(np.arange(Dout), idx_o)
+    drop_i = np.setdiff1d(np.arange(Din), idx_i)
+
+    def split_out(fn, y, C, idx_d, lora):
+        # product with NO_FILL on the main stream, fill of the rest on the side
+        ev.record(main)
+        side.wait_event(ev)
+        with torch.cuda.stream(side):
+            ops.lora_fill_unselected(y, c_d, lora, idx_d)
+        fn(y)
+        main.wait_stream(side)
+        torch.cuda.synchronize()
+
+    # forward, side "out"
+    lora_o = (Pd, Bod, r, s)
+    y1 = empty_pad(T, Dout, "bf16")
+    ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, lora=lora_o)
+    y2 = empty_pad(T, Dout, "bf16", fill=7.0)
+    ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y2, lora=lora_o, flags=ops.NO_FILL)
+    torch.cuda.synchronize()
+    assert np.all(host(y2)[np.ix_(ctx, drop_o)] == 7.0)     # left unwritten
+    y3 = empty_pad(T, Dout, "bf16", fill=7.0)
+    split_out(lambda y: ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y, lora=lora_o,
+                                              flags=ops.NO_FILL), y3, Dout, io_d, lora_o)
+    assert np.array_equal(bits(host(y1)), bits(host(y3)))
+    lora = s * (P.astype(np.float64) @ Bo.T.astype(np.float64))
+    assert mar(host(y3), ref.sparse_linear_fwd("out", x, W, roles, idx_o) + lora) <= TOL["bf16"]
+    # weight_slice: exact copy of the selected rows of the channel-major weight,
+    # zero columns up to the next multiple of 8
+    ldn = (len(idx_o) + 7) // 8 * 8
+    wsl = torch.full((Din, ldn + 8), 5.0, dtype=torch.bfloat16, device=DEV)
+    ops.weight_slice(Wd, io_d, wsl)
+    torch.cuda.synchronize()
+    got = host(wsl)
+    assert np.array_equal(got[:, :len(idx_o)], W[idx_o].T.astype(np.float32))
+    assert np.all(got[:, len(idx_o):ldn] == 0.0) and np.all(got[:, ldn:] == 5.0)
+    # backward, side "out" (contracts over the selected output channels): the
+    # slice of W built beforehand
+    lora_b = (Pd, Bid, r, s)
+    d1 = empty_pad(T, Din, "bf16")
+    ops.sparse_linear_bwd("out", dyd, Wd, Wtd, c_d, o_d, io_d, d1, lora=lora_b)
+    d2 = empty_pad(T, Din, "bf16")
+    ops.sparse_linear_bwd("out", dyd, Wd, Wtd, c_d, o_d, io_d, d2, lora=lora_b, w_slice=wsl[:, :ldn])
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(d1)), bits(host(d2)))
+    # forward, side "in" with a slice of Wt (the transposed copy) built beforehand
+    xi = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    xid = dev_pad(xi, "bf16")
+    ldi = (len(idx_i) + 7) // 8 * 8
+    wsl_i = torch.empty(Dout, ldi, dtype=torch.bfloat16, device=DEV)
+    ops.weight_slice(Wtd, ii_d, wsl_i)
+    yi1, yi2 = empty_pad(T, Dout, "bf16"), empty_pad(T, Dout, "bf16")
+    ops.sparse_linear_fwd("in", xid, Wd, Wtd, c_d, o_d, ii_d, yi1, lora=lora_o)
+    ops.sparse_linear_fwd("in", xid, Wd, Wtd, c_d, o_d, ii_d, yi2, lora=lora_o, w_slice=wsl_i)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(yi1)), bits(host(yi2)))
+    # backward, side "in" (produces the selected input channels): NO_FILL and
+    # the fill of the unselected ones on the side stream
+    dx1 = empty_pad(T, Din, "bf16")
+    ops.sparse_linear_bwd("in", dyd, None, Wtd, c_d, o_d, ii_d, dx1, lora=lora_b)
+    dx2 = empty_pad(T, Din, "bf16", fill=7.0)
+    split_out(lambda d: ops.sparse_linear_bwd("in", dyd, None, Wtd, c_d, o_d, ii_d, d, lora=lora_b,
+                                              flags=ops.NO_FILL), dx2, Din, ii_d, lora_b)
+    assert np.array_equal(bits(host(dx1)), bits(host(dx2)))
+    lb = s * (P.astype(np.float64) @ Bi.T.astype(np.float64))
+    assert mar(host(dx2)[np.ix_(ctx, drop_i)], lb[np.ix_(ctx, drop_i)]) <= TOL["bf16"]
+    # refused before any launch: a slice on the side that builds none, bad flags,
+    # a slice narrower than ceil8(n), fp32 fills
+    with pytest.raises(ops.SLError):
+        ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, w_slice=wsl)
+    with pytest.raises(ops.SLError):
+        ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, flags=2)
+    with pytest.raises(ops.SLError):
+        ops.sparse_linear_fwd("in", xid, Wd, Wtd, c_d, o_d, ii_d, yi1,
+                              w_slice=torch.empty(Dout, ldi - 8, dtype=torch.bfloat16, device=DEV))
+    with pytest.raises(ops.SLError):
+        ops.lora_fill_unselected(empty_pad(T, Dout, "f32"), c_d, lora_o, io_d)
+
+
+@pytest.mark.parametrize("D_out,r", [(1000, 16), (28672 // 8, 32), (203, 96)])
+def test_lora_gb_with_transposed_b(D_out, r, rng):
+    """gB = dy B from B^T kept by the caller (LORA_BT, rows padded to a multiple
+    of 8) equals the product from B itself bit for bit, and the oracle."""
+    ops = _ops()
+    T, s = 300, 2.0
+    print(f"[lora-bt] D_out={D_out} r={r}", flush=True)
+    Bm = round_dtype(rng.standard_normal((D_out, r)) * 0.05, "bf16")
+    dy = round_dtype(rng.standard_normal((T, D_out)), "bf16")
+    dyd, Bd = dev_pad(dy, "bf16"), to_dev(Bm, "bf16")
+    ld = (D_out + 7) // 8 * 8
+    Bt = torch.zeros(r, ld, dtype=torch.bfloat16, device=DEV)
+    ops.transpose(Bd, Bt[:, :D_out])
+    g1 = torch.empty(T, r, dtype=torch.float32, device=DEV)
+    g2 = torch.empty(T, r, dtype=torch.float32, device=DEV)
+    ops.lora_fwd_bwd(ops.LORA_GB, None, None, Bd, s, None, dy=dyd, gB=g1, D_in=64, r=r)
+    ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, Bt, s, None, dy=dyd, gB=g2, D_in=64,
+                     D_out=D_out, r=r)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(host(g1)), bits(host(g2)))
+    assert mar(host(g2), dy.astype(np.float64) @ Bm.astype(np.float64)) <= 1e-5
+    with pytest.raises(ops.SLError):       # B^T cannot serve the forward add
+        ops.lora_fwd_bwd(ops.LORA_ADD | ops.LORA_BT, None, None, Bt, s, g1,
+                         y=empty_pad(T, D_out, "bf16"), D_out=D_out, r=r)
