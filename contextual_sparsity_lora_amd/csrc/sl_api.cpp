@@ -520,17 +520,23 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
                      const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
                      const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
                      const LoraEpi& l, int flags = 0) {
-    if (n == C || T_c == 0) {
+    const bool only_out = flags & SL_ONLY_OUT_ROWS, only_ctx = flags & SL_ONLY_CTX_ROWS;
+    if (only_out && T_o == 0) return SL_OK;
+    if (only_ctx && T_c == 0) return SL_OK;
+    if (T_c == 0 || (n == C && !only_out && !only_ctx)) {
         GemmProblem p = problem(X, ldx, nullptr, Wc, ldw, nullptr, Z, ldz, nullptr, nullptr, T, C,
                                 Kdim, beta, l, T, C);
         return run_gemm(h, dt, false, &p, 1);
     }
     GemmProblem p[2];
-    p[0] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim, beta,
-                   l, T, C);
-    p[1] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
-                   C);
-    const int np = 2;
+    int np = 0;
+    // output rows: every channel (they do not depend on the selection)
+    if (!only_ctx)
+        p[np++] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim,
+                          beta, l, T, C);
+    if (only_out) return run_gemm(h, dt, false, p, np);
+    p[np++] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
+                      C);
     if (flags & SL_NO_FILL) {
         // the caller writes the unselected channels of context rows itself
         // (sl_lora_fill_unselected), possibly while this product runs
@@ -671,7 +677,11 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
-    SL_REQUIRE(h, (flags & ~SL_NO_FILL) == 0, "bad flags");
+    SL_REQUIRE(h, (flags & ~(SL_NO_FILL | SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) == 0 &&
+                      (flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) != (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS),
+               "bad flags");
+    SL_REQUIRE(h, side == SL_SIDE_OUT || !(flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)),
+               "row-subset flags apply to side OUT");
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     if (w_slice) {
@@ -709,7 +719,11 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
-    SL_REQUIRE(h, (flags & ~SL_NO_FILL) == 0, "bad flags");
+    SL_REQUIRE(h, (flags & ~(SL_NO_FILL | SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) == 0 &&
+                      (flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) != (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS),
+               "bad flags");
+    SL_REQUIRE(h, side == SL_SIDE_IN || !(flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)),
+               "row-subset flags apply to side IN");
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     if (w_slice) {

@@ -111,14 +111,22 @@ class SparseFFN:
         self._alloc(T, T_c, T - T_c, x.device)
         self.x = x
         main = torch.cuda.current_stream(x.device)
-        # LoRA down-projection of the block input on the side stream, while the
-        # estimator, scoring and selection run on the main stream
+        ops.token_split(roles, self.ctx_rows, self.out_rows)
+        # side stream: the LoRA down-projection of the block input, then the
+        # gate|up product of the output rows (dense over every channel, so it
+        # does not wait for the selection) -- both overlap the estimator,
+        # scoring and selection on the main stream, whose small launches leave
+        # most compute units idle
         self._ev[0].record(main)
         self.side.wait_event(self._ev[0])
+        lora = (self.xl_gu, self.B_bd, 2 * r, self.scale)
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
             self._ev[1].record(self.side)
-        ops.token_split(roles, self.ctx_rows, self.out_rows)
+            if not self.dense:
+                ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
+                                      self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
+            self._ev[3].record(self.side)
         if not self.dense:
             # estimator on context tokens, SwiGLU-L2 criterion, top-n (shared by gate/up/down)
             ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
@@ -126,10 +134,11 @@ class SparseFFN:
                              scores=self.scores, off0=0, off1=self.k)
             ops.stack_index(self.idx, F, 2, self.idx2)
         main.wait_event(self._ev[1])
-        # the gate|up main branch (dense output rows, gathered channels for
-        # context rows) with the LoRA term fused into the same accumulators
+        # the gate|up main branch of the context rows (gathered channels; every
+        # row when dense) with the LoRA term fused into the same accumulators
         ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
-                              lora=(self.xl_gu, self.B_bd, 2 * r, self.scale))
+                              lora=lora, flags=0 if self.dense else ops.ONLY_CTX_ROWS)
+        main.wait_event(self._ev[3])
         g, u = self.gu[:, :F], self.gu[:, F:]
         ops.swiglu_fwd(g, u, self.h)
         # down main branch: input channels = the same selection; LoRA fused

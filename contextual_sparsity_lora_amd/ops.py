@@ -195,6 +195,8 @@ def _lora_args(lora):
 
 
 NO_FILL = 1
+ONLY_OUT_ROWS = 2
+ONLY_CTX_ROWS = 4
 
 
 def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=None,

@@ -70,9 +70,15 @@ typedef enum {
 
 /* sl_sparse_linear_fwd / _bwd flag bits. */
 enum {
-    SL_NO_FILL = 1    /* side-OUT-shaped products: leave the unselected channels of
-                         context rows unwritten (the caller writes them itself,
-                         e.g. with sl_lora_fill_unselected on another stream) */
+    SL_NO_FILL = 1,       /* side-OUT-shaped products: leave the unselected channels
+                             of context rows unwritten (the caller writes them
+                             itself, e.g. with sl_lora_fill_unselected) */
+    SL_ONLY_OUT_ROWS = 2, /* side-OUT-shaped products: compute the output rows only
+                             (dense over every channel; idx is not read, so the
+                             selection may still be in the making on another
+                             stream); context rows untouched */
+    SL_ONLY_CTX_ROWS = 4  /* the complement: context rows only (selected channels,
+                             and the unselected ones unless SL_NO_FILL) */
 };
 
 /* sl_lora_fwd_bwd mode bits. */
@@ -245,9 +251,12 @@ sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t o
  *   w_slice  optional (side IN only): the context-row weight slice built
  *       beforehand by sl_weight_slice from Wt and the same idx, dt
  *       [D_out, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
- *   flags  0 or SL_NO_FILL (side OUT: the unselected channels of context rows
+ *   flags  SL_NO_FILL (side OUT: the unselected channels of context rows
  *       are left unwritten; with lora_P they must be written by
- *       sl_lora_fill_unselected, without it the caller zeroes them)
+ *       sl_lora_fill_unselected, without it the caller zeroes them), and at
+ *       most one of SL_ONLY_OUT_ROWS / SL_ONLY_CTX_ROWS (side OUT: one of the
+ *       two row sets per call; the two calls together compute what one call
+ *       without them computes, up to the order of fp32 accumulation)
  * dt = SL_BF16 (MFMA path) or SL_F32. */
 sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* x, int64_t ldx, int64_t T, int64_t D_in,
@@ -281,8 +290,8 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
  * hold this term instead of 0.
  *   w_slice  optional (side OUT only): sl_weight_slice of W with the same idx,
  *       dt [D_in, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
- *   flags  0 or SL_NO_FILL (side IN: unselected context channels left
- *       unwritten, as for the forward) */
+ *   flags  as for the forward, with side IN in place of side OUT
+ *       (SL_NO_FILL, SL_ONLY_OUT_ROWS, SL_ONLY_CTX_ROWS) */
 sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* dy, int64_t lddy, int64_t T, int64_t D_out,
                                const void* W, int64_t ldw, const void* Wt, int64_t ldwt,

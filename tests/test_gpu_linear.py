@@ -413,7 +413,7 @@ def test_no_fill_with_concurrent_fill_and_prebuilt_slices(r, rng):
     with pytest.raises(ops.SLError):
         ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, w_slice=wsl)
     with pytest.raises(ops.SLError):
-        ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, flags=2)
+        ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, io_d, y1, flags=8)
     with pytest.raises(ops.SLError):
         ops.sparse_linear_fwd("in", xid, Wd, Wtd, c_d, o_d, ii_d, yi1,
                               w_slice=torch.empty(Dout, ldi - 8, dtype=torch.bfloat16, device=DEV))
@@ -445,3 +445,53 @@ def test_lora_gb_with_transposed_b(D_out, r, rng):
     with pytest.raises(ops.SLError):       # B^T cannot serve the forward add
         ops.lora_fwd_bwd(ops.LORA_ADD | ops.LORA_BT, None, None, Bt, s, g1,
                          y=empty_pad(T, D_out, "bf16"), D_out=D_out, r=r)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_row_subset_calls(direction, rng):
+    """ONLY_OUT_ROWS and ONLY_CTX_ROWS split a side-OUT-shaped product (forward
+    side "out", backward side "in") into its two row sets: each call writes its
+    rows only, the out-row call reads no selection (a garbage index list), and
+    the two together match the oracle.  Row-subset flags on the other shape are
+    refused."""
+    ops = _ops()
+    roles = _roles(2, 300, 70)
+    T, Din, Dout, r, s = 600, 520, 1000, 16, 2.0
+    ctx, out, c_d, o_d = _lists(ops, roles)
+    print(f"[row-subset] {direction}", flush=True)
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+    idx = np.sort(rng.choice(Dout, 333, replace=False)).astype(np.int32)
+    lora = (to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s)
+    Wd, Wtd = dev_pad(W, "bf16"), dev_pad(np.ascontiguousarray(W.T), "bf16")
+    garbage = torch.full((len(idx),), 1 << 30, dtype=torch.int32, device=DEV)
+    y = empty_pad(T, Dout, "bf16", fill=7.0)
+    lterm = s * (P.astype(np.float64) @ Bm.T.astype(np.float64))
+    if direction == "fwd":
+        xd = dev_pad(x, "bf16")
+        call = lambda ix, f: ops.sparse_linear_fwd("out", xd, Wd, None, c_d, o_d, ix, y, lora=lora, flags=f)
+        want = ref.sparse_linear_fwd("out", x, W, roles, idx) + lterm
+    else:
+        # backward of a side "in" product whose weight is W^T [Din, Dout]: dy has Din columns
+        Wi = np.ascontiguousarray(W.T)                       # [D_out', D_in'] = [Din, Dout]
+        dyd = dev_pad(x, "bf16")
+        call = lambda ix, f: ops.sparse_linear_bwd("in", dyd, None, Wd, c_d, o_d, ix, y, lora=lora, flags=f)
+        want = ref.sparse_linear_bwd("in", x, Wi, roles, idx) + lterm
+    call(garbage, ops.ONLY_OUT_ROWS)
+    torch.cuda.synchronize()
+    got = host(y)
+    assert np.all(got[ctx] == 7.0)                      # context rows untouched
+    assert mar(got[out], want[out]) <= TOL["bf16"]
+    call(to_dev(idx, None), ops.ONLY_CTX_ROWS)
+    torch.cuda.synchronize()
+    got2 = host(y)
+    assert np.array_equal(got2[out], got[out])          # output rows untouched
+    assert mar(got2, want) <= TOL["bf16"]
+    with pytest.raises(ops.SLError):
+        call(to_dev(idx, None), ops.ONLY_OUT_ROWS | ops.ONLY_CTX_ROWS)
+    with pytest.raises(ops.SLError):
+        ops.sparse_linear_fwd("in", dev_pad(x[:, :Din], "bf16"), Wd, Wtd, c_d, o_d,
+                              to_dev(np.arange(10, dtype=np.int32), None), empty_pad(T, Dout, "bf16"),
+                              flags=ops.ONLY_OUT_ROWS)
