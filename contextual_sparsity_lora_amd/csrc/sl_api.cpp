@@ -102,8 +102,11 @@ hipEvent_t take_event(sl_handle* h) {
         h->event_pool.pop_back();
         return e;
     }
+    // timing only: no system-scope fence when the event is recorded (the
+    // stream is synchronised before any elapsed time is read), so the markers
+    // do not add cache write-back and invalidation between the timed launches
     hipEvent_t e = nullptr;
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipGetLastError();
         return nullptr;
     }
