@@ -205,6 +205,10 @@ def main():
              "per_class_note": f"separate instrumented pass of {psteps} steps "
                                f"({pms:.3f} ms/step with events around every launch)"}
     if not args.no_dense:
+        import types
+        from contextual_sparsity_lora_amd import fidelity
+        # the sparse block's LoRA gradients of its last step (same inputs every step)
+        sparse_grads = types.SimpleNamespace(**{k: v.clone() for k, v in fidelity.lora_grads(blk).items()})
         del blk
         torch.cuda.empty_cache()
         dblk, x, roles, dy = build_block(inp, cfg, dense=True)
@@ -212,6 +216,13 @@ def main():
         extra["dense_ms_per_step"] = round(dms_step, 4)
         extra["speedup_vs_dense"] = round(dms_step / ms, 3)
         print(f"[bench] dense step {dms_step:.3f} ms", file=sys.stderr, flush=True)
+        # gradient fidelity: cosine between the sparse and the dense block's
+        # LoRA gradients on the same synthetic inputs (random weights: a
+        # measurement of the tool, not a result about the method)
+        extra["grad_fidelity"] = {k: round(v, 6) for k, v in
+                                  fidelity.block_fidelity(sparse_grads, dblk).items()}
+        print(f"[bench] LoRA gradient cosines sparse vs dense: {extra['grad_fidelity']}",
+              file=sys.stderr, flush=True)
         del dblk
     out = {
         "metric": "sparse-LoRA linear fwd+bwd tokens/s and MFMA util at LLaMA3-8B FFN shape, 1 GPU",

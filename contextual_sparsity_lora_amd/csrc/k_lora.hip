@@ -899,6 +899,61 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- dot statistics
+// (a.b, a.a, b.b) over n fp32 values in fp64 (each product exact), in a fixed
+// order: thread i of block g sums elements g*256 + i + k*DOT_G*256, k = 0, 1,
+// ...; a block combines its 256 thread sums by a pairwise tree in LDS, and a
+// second launch combines the DOT_G block sums by the same tree.
+constexpr int DOT_G = 256;
+
+__device__ __forceinline__ void tree3(double (*s)[256], int tid) {
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (tid < w) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) s[j][tid] += s[j][tid + w];
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void dot_stats_partial_kernel(const float* __restrict__ a,
+                                                                const float* __restrict__ b,
+                                                                int64_t n, double* __restrict__ part) {
+    __shared__ double s[3][256];
+    const int tid = threadIdx.x;
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + tid; i < n; i += (int64_t)DOT_G * 256) {
+        const double x = a[i], y = b[i];
+        ab = __builtin_fma(x, y, ab);
+        aa = __builtin_fma(x, x, aa);
+        bb = __builtin_fma(y, y, bb);
+    }
+    s[0][tid] = ab;
+    s[1][tid] = aa;
+    s[2][tid] = bb;
+    __syncthreads();
+    tree3(s, tid);
+    if (tid < 3) part[(int64_t)blockIdx.x * 3 + tid] = s[tid][0];
+}
+
+__global__ __launch_bounds__(256) void dot_stats_final_kernel(const double* __restrict__ part,
+                                                              double* __restrict__ out) {
+    __shared__ double s[3][256];
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) s[j][tid] = part[tid * 3 + j];
+    __syncthreads();
+    tree3(s, tid);
+    if (tid < 3) out[tid] = s[tid][0];
+}
+
+hipError_t launch_dot_stats(const float* a, const float* b, int64_t n, double* part, double* out,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(dot_stats_partial_kernel, dim3(DOT_G), dim3(256), 0, st, a, b, n, part);
+    hipLaunchKernelGGL(dot_stats_final_kernel, dim3(1), dim3(256), 0, st, part, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,
                             void* out, int64_t ldo, hipStream_t st) {
     if (rows <= 0 || cols <= 0) return hipSuccess;

@@ -942,6 +942,17 @@ sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi, i
                      "transpose");
 }
 
+sl_status sl_dot_stats(sl_handle* h, const float* a, const float* b, int64_t n, double* out) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, n >= 0, "bad size");
+    SL_REQUIRE(h, out != nullptr && (n == 0 || (a && b)), "NULL pointer");
+    SL_REQUIRE(h, ((uintptr_t)a & 3) == 0 && ((uintptr_t)b & 3) == 0 && ((uintptr_t)out & 7) == 0,
+               "misaligned pointer");
+    DeviceGuard gd(h->device);
+    SL_CHECK(ensure_ws(h, 256 * 3 * sizeof(double)));
+    return hip_check(h, launch_dot_stats(a, b, n, (double*)h->ws, out, h->stream), "dot_stats");
+}
+
 // ---------------------------------------------------------------- a14: layer glue
 sl_status sl_rmsnorm_fwd(sl_handle* h, sl_dtype dt, const void* x, int64_t ldx, const void* res,
                          int64_t ldres, int64_t T, int64_t D, float eps, void* hsum, int64_t ldh,

@@ -147,6 +147,9 @@ hipError_t launch_attn_bwd(bool bf16, const void* q, int64_t ldq, const void* k,
                            int64_t lddo, const float* lse, float* delta, int64_t B, int64_t S,
                            int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq, void* dk,
                            int64_t lddk, void* dv, int64_t lddv, hipStream_t st);
+// (a.b, a.a, b.b) in fp64 over n fp32 values, fixed order; part holds 256 x 3 doubles
+hipError_t launch_dot_stats(const float* a, const float* b, int64_t n, double* part, double* out,
+                            hipStream_t st);
 hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,
                             void* out, int64_t ldo, hipStream_t st);
 hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* u, int64_t ldu,

@@ -306,6 +306,16 @@ def swiglu_bwd(dh, g, u, dg, du):
     _check(h, st, "sl_swiglu_bwd")
 
 
+def dot_stats(a, b, out):
+    """out (fp64 [3] on the device) = (a.b, a.a, b.b) over the fp32 elements of
+    two contiguous tensors of the same size."""
+    assert a.is_contiguous() and b.is_contiguous() and a.numel() == b.numel()
+    assert a.dtype == torch.float32 and b.dtype == torch.float32 and out.dtype == torch.float64
+    h = handle(_dev(a))
+    st = _lib.load().sl_dot_stats(h, _ptr(a), _ptr(b), a.numel(), _ptr(out))
+    _check(h, st, "sl_dot_stats")
+
+
 def transpose(inp, out):
     h = handle(_dev(inp))
     rows, cols = inp.shape

@@ -331,6 +331,19 @@ sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ld
                                   int64_t ld_lora_B, int64_t lora_r, float lora_scale,
                                   const int32_t* idx, int64_t n);
 
+/* ---------------------------------------------------------------- gradient fidelity */
+
+/* Dot statistics of two fp32 vectors, for the cosine between a sparse and a
+ * dense gradient of the same LoRA adapter (paper-graph summary, "Follow-Up
+ * Research This Work Enables": gradient cosine similarity as a fidelity
+ * measure of training sparsity):
+ *   out[0] = sum a[i] b[i],  out[1] = sum a[i]^2,  out[2] = sum b[i]^2
+ * over i < n, in fp64 with every product exact and a fixed summation order
+ * (the result does not depend on timing).  a, b device fp32 [n] (4-byte
+ * aligned, contiguous); out device fp64 [3] (8-byte aligned).  n = 0 gives
+ * zeros. */
+sl_status sl_dot_stats(sl_handle* h, const float* a, const float* b, int64_t n, double* out);
+
 /* ---------------------------------------------------------------- a8/a12: dense LoRA */
 
 /* Dense LoRA branch on every token and channel (PG §3.4 Algorithm 1 step 6:

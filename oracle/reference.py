@@ -386,3 +386,27 @@ def estimator_cost_ratio(k, d_in, d_out):
     """Estimator cost relative to the dense product: k (D_in + D_out) / (D_in D_out)
     (paper-graph summary §3.4, SVD estimator "Cost analysis")."""
     return Fraction(k * (d_in + d_out), d_in * d_out)
+
+
+def grad_cosine(a, b):
+    """cos(a, b) = a.b / (|a| |b|) over all elements, fp64; nan when either
+    vector is zero.  Paper-graph summary, "Follow-Up Research This Work
+    Enables": the cosine between the dense and the sparse gradient update of
+    the LoRA adapters measures gradient fidelity under training sparsity."""
+    a, b = np.asarray(a, f64).ravel(), np.asarray(b, f64).ravel()
+    na, nb = float(np.sqrt(np.dot(a, a))), float(np.sqrt(np.dot(b, b)))
+    return float(np.dot(a, b) / (na * nb)) if na > 0.0 and nb > 0.0 else float("nan")
+
+
+LORA_GRADS_FFN = ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")
+
+
+def ffn_grad_fidelity(inp, idx):
+    """Per LoRA gradient of the FFN block: the cosine between the gradient with
+    the selection idx and the gradient of the dense block (every channel kept)
+    on the same inputs."""
+    F = np.asarray(inp["W_gate"]).shape[0]
+    everything = np.arange(F)
+    fs, fd = ffn_block_fwd(inp, idx), ffn_block_fwd(inp, everything)
+    bs, bd = ffn_block_bwd(inp, fs, idx), ffn_block_bwd(inp, fd, everything)
+    return {k: grad_cosine(bs[k], bd[k]) for k in LORA_GRADS_FFN}

@@ -481,3 +481,49 @@ def test_subspace_factors_near_optimal_on_gaussian(rng):
     assert e_opt <= e_rnd <= 1.01 * e_opt
     # W_A and W_B^T share the singular values: column norms of W_A^T rows equal
     assert np.allclose(np.linalg.norm(RA_t, axis=1), np.linalg.norm(RB, axis=1), rtol=1e-5)
+
+
+def test_grad_cosine_closed_forms(rng):
+    """cos of (1, 2, 2) and (2, 1, 2) is 8/9; a vector with a positive multiple
+    of itself gives 1, with a negative one -1; orthogonal vectors give 0; a
+    zero vector gives nan; shape does not matter (all elements count)."""
+    assert ref.grad_cosine([1, 2, 2], [2, 1, 2]) == pytest.approx(8 / 9, abs=1e-15)
+    a = rng.standard_normal((7, 5))
+    assert ref.grad_cosine(a, 3.0 * a) == pytest.approx(1.0, abs=1e-15)
+    assert ref.grad_cosine(a, -0.5 * a) == pytest.approx(-1.0, abs=1e-15)
+    b = rng.standard_normal((7, 5))
+    b_orth = b - (np.sum(a * b) / np.sum(a * a)) * a
+    assert abs(ref.grad_cosine(a, b_orth)) < 1e-14
+    assert np.isnan(ref.grad_cosine(np.zeros(3), [1, 2, 3]))
+    assert ref.grad_cosine(a, b) == pytest.approx(ref.grad_cosine(a.ravel(), b.T.T.ravel()), abs=0)
+
+
+def test_ffn_grad_fidelity_matches_autograd_cosines(rng):
+    """The per-adapter cosines between the sparse and the dense FFN block's
+    LoRA gradients equal torch's cosine_similarity of autograd gradients of the
+    masked and the unmasked block; with every channel kept they are 1."""
+    cfg, inp, idx = _ffn_small(rng)
+    fid = ref.ffn_grad_fidelity(inp, idx)
+    T = cfg.tokens
+    s = inp["scale"]
+    lin = torch.nn.functional.linear
+
+    def grads(mask):
+        M = torch.tensor(mask)
+        t = {k: torch.tensor(v, dtype=torch.float64, requires_grad=True)
+             for k, v in inp.items() if isinstance(v, np.ndarray) and k != "roles"}
+        g = lin(t["x"], t["W_gate"]) * M + s * lin(lin(t["x"], t["A_gate"]), t["B_gate"])
+        u = lin(t["x"], t["W_up"]) * M + s * lin(lin(t["x"], t["A_up"]), t["B_up"])
+        h = torch.nn.functional.silu(g) * u
+        y = lin(h * M, t["W_down"]) + s * lin(lin(h, t["A_down"]), t["B_down"])
+        (y * t["dy"]).sum().backward()
+        return {p: t[p].grad.reshape(-1) for p in ("A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down")}
+
+    gs = grads(ref.keep_mask(T, cfg.inter, inp["roles"], idx))
+    gd = grads(np.ones((T, cfg.inter)))
+    for p in gs:
+        want = float(torch.nn.functional.cosine_similarity(gs[p], gd[p], dim=0))
+        assert fid["d" + p] == pytest.approx(want, abs=1e-12), p
+    assert min(fid.values()) < 1.0 - 1e-6          # the selection changes some gradient
+    full = ref.ffn_grad_fidelity(inp, np.arange(cfg.inter))
+    assert all(v == pytest.approx(1.0, abs=1e-14) for v in full.values())
