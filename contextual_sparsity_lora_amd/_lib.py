@@ -36,6 +36,10 @@ SIGNATURES = {
     "sl_svd_estimate": (_st, [_vp, _vp, _int, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "sl_score_select": (_st, [_vp, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                               _i64, _i64, _i64, _vp, _vp]),
+    "sl_select_top": (_st, [_vp, _vp, _i64, _i64, _vp]),
+    "sl_random_scores": (_st, [_vp, ctypes.c_uint64, _i64, _vp]),
+    "sl_dense_scores": (_st, [_vp, _int, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),
+    "sl_select_heads": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_expand_gqa": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_stack_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_offset_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),

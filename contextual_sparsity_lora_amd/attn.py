@@ -31,7 +31,7 @@ from .ffn import keep_count
 class SparseAttnProj:
     def __init__(self, W_q, W_k, W_v, W_o, A_q, B_q, A_k, B_k, A_v, B_v, A_o, B_o, WA_qkv,
                  WB_q, WB_k, WB_v, scale, n_kv_heads, head_dim, qk_sparsity=(1, 2),
-                 vo_sparsity=(1, 2), dense=False):
+                 vo_sparsity=(1, 2), dense=False, criterion="svd", seed=0):
         dev = W_q.device
         self.dtype = W_q.dtype
         self.Cq, self.D = W_q.shape
@@ -43,7 +43,20 @@ class SparseAttnProj:
         self.k = WB_q.shape[0] if WB_q is not None else 0   # estimator factors: None when dense
         self.scale = float(scale)
         self.dense = dense
+        # criterion ablations (paper-graph summary, Tables 7 and 10): "svd" the
+        # rank-k estimate (the method); "oracle" the QK and VO criteria on the
+        # exact q, k, v outputs of the frozen weights; "random" uniformly random
+        # channel sets (library draws, seed + call number); "head" the QK
+        # selection made per key/value head (the estimate's channel scores
+        # summed per head, whole heads kept; VO stays per channel)
+        assert criterion in ("svd", "oracle", "random", "head"), criterion
+        self.criterion = criterion
+        self.seed, self.calls, self.last_seed = int(seed), 0, None
+        self.n_kv_heads = n_kv_heads
         self.n_qk = self.Ckv if dense else keep_count(self.Ckv, *qk_sparsity)
+        if criterion == "head" and not dense:
+            self.heads_keep = keep_count(n_kv_heads, *qk_sparsity)
+            self.n_qk = self.heads_keep * head_dim
         self.n_vo = self.Ckv if dense else keep_count(self.Ckv, *vo_sparsity)
         Cq, Ckv, r = self.Cq, self.Ckv, self.r
         self.Cs = Cq + 2 * Ckv
@@ -64,7 +77,7 @@ class SparseAttnProj:
         cont = lambda w: w.contiguous() if w is not None else None
         self.WA = cont(WA_qkv)                         # [D, 3k] fp32
         self.WB_q, self.WB_k, self.WB_v = (cont(w) for w in (WB_q, WB_k, WB_v))
-        assert dense or self.k > 0, "the estimator factors are required unless dense"
+        assert dense or criterion in ("oracle", "random") or self.k > 0, "the estimator factors are required"
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):
@@ -76,6 +89,8 @@ class SparseAttnProj:
         self.ctx_rows, self.out_rows = e(T_c, dtype=i32), e(T_o, dtype=i32)
         self.xa = e(T_c, 3 * k, dtype=f32)
         self.scores = e(Ckv, dtype=f32)
+        self.scores_vo = e(Ckv, dtype=f32)
+        self.idx_all = torch.arange(self.Cs, dtype=i32, device=dev) if self.criterion == "oracle" else None
         self.idx_qk, self.idx_vo = e(self.n_qk, dtype=i32), e(self.n_vo, dtype=i32)
         self.idx_q = e(self.n_qk * self.n_rep, dtype=i32)
         self.idx_o = e(self.n_vo * self.n_rep, dtype=i32)
@@ -100,12 +115,35 @@ class SparseAttnProj:
         """QK and VO selections from the estimator on the context tokens, their
         GQA expansions and the stacked q|k|v channel list."""
         k, Ckv, Cq = self.k, self.Ckv, self.Cq
-        ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
-        ops.score_select("qk", self.xa, self.WB_q, self.WB_k, self.n_qk, self.idx_qk,
-                         scores=self.scores, off0=0, off1=k, C=Ckv, n_rep=self.n_rep,
-                         head_dim=self.d)
-        ops.score_select("l2", self.xa, self.WB_v, None, self.n_vo, self.idx_vo, scores=self.scores,
-                         off0=2 * k)
+        crit = self.criterion
+        if crit in ("svd", "head"):
+            ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
+            ops.score_select("qk", self.xa, self.WB_q, self.WB_k, 0 if crit == "head" else self.n_qk,
+                             self.idx_qk, scores=self.scores, off0=0, off1=k, C=Ckv, n_rep=self.n_rep,
+                             head_dim=self.d)
+            if crit == "head":
+                ops.select_heads(self.scores, self.n_kv_heads, self.d, self.heads_keep, self.idx_qk)
+            ops.score_select("l2", self.xa, self.WB_v, None, self.n_vo, self.idx_vo,
+                             scores=self.scores_vo, off0=2 * k)
+        elif crit == "oracle":
+            # exact q|k|v outputs of the frozen weights (no LoRA) in qkv, which
+            # the product then overwrites
+            ops.sparse_linear_fwd("out", self.x, self.W_qkv, None, self.ctx_rows, self.out_rows,
+                                  self.idx_all, self.qkv)
+            q, kk, v = self.qkv[:, :Cq], self.qkv[:, Cq:Cq + Ckv], self.qkv[:, Cq + Ckv:]
+            ops.dense_scores("qk", q, kk, self.ctx_rows, self.scores, C=Ckv, n_rep=self.n_rep,
+                             head_dim=self.d)
+            ops.select_top(self.scores, self.n_qk, self.idx_qk)
+            ops.dense_scores("l2", v, None, self.ctx_rows, self.scores_vo)
+            ops.select_top(self.scores_vo, self.n_vo, self.idx_vo)
+        else:
+            # two independent draws: QK from seed', VO from seed' + 2^32
+            self.last_seed = self.seed + self.calls
+            ops.random_scores(self.last_seed, self.scores)
+            ops.select_top(self.scores, self.n_qk, self.idx_qk)
+            ops.random_scores(self.last_seed + (1 << 32), self.scores_vo)
+            ops.select_top(self.scores_vo, self.n_vo, self.idx_vo)
+        self.calls += 1
         ops.expand_gqa(self.idx_qk, self.n_rep, self.d, self.idx_q)
         ops.expand_gqa(self.idx_vo, self.n_rep, self.d, self.idx_o)
         nq = self.idx_q.numel()

@@ -555,6 +555,96 @@ __global__ void offset_index_kernel(const int32_t* __restrict__ idx, int64_t n, 
     if (p < n) out[p] = (int32_t)(idx[p] + offset);
 }
 
+// ---------------------------------------------------------------- criterion variants
+template <typename T> __device__ __forceinline__ float ldv(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ldv<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ldv<bf16_t>(const bf16_t* p, int64_t i) {
+    return bf16_to_f32(p[i]);
+}
+
+// Dense ("oracle") criterion: the same metric on exact outputs instead of the
+// estimate, ssq[c] = R64 over listed rows m of (v[m, c], v[m, c]) with
+// v = Y0 (L2) or silu(Y0) * Y1 (FFN).  Block = 4 waves; chain l = 4 by + w
+// (64 chains, by = blockIdx.y < 16) takes rows m = l, l + 64, ...; a lane owns
+// 8 consecutive channels.  The 64 chain sums go to part[l][c]; the second
+// kernel runs the R64 pairwise tree per channel.
+template <typename T, int CRIT>
+__global__ __launch_bounds__(256) void dense_chain_kernel(const T* __restrict__ Y0, int64_t ld0,
+                                                          const T* __restrict__ Y1, int64_t ld1,
+                                                          const int32_t* __restrict__ rows,
+                                                          int64_t Tc, int64_t C,
+                                                          float* __restrict__ part) {
+    const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x >> 6;
+    const int l = (int)blockIdx.y * 4 + w;
+    const int64_t c0 = ((int64_t)blockIdx.x * WAVE + lane) * 8;
+    if (c0 >= C) return;
+    const int nc = (C - c0) < 8 ? (int)(C - c0) : 8;
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = 0.0f;
+    for (int64_t m = l; m < Tc; m += 64) {
+        const int64_t t = rows[m];
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float y = 0.0f;
+            if (e < nc) {
+                y = ldv<T>(Y0, t * ld0 + c0 + e);
+                if (CRIT == 1) y = silu_sl_nb(y) * ldv<T>(Y1, t * ld1 + c0 + e);
+            }
+            v[e] = y;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_fmaf(v[e], v[e], p[e]);
+    }
+    for (int e = 0; e < nc; ++e) part[(int64_t)l * C + c0 + e] = p[e];
+}
+
+__global__ void r64_tree_kernel(const float* __restrict__ part, int64_t C, float* __restrict__ ssq) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    float v[64];
+#pragma unroll
+    for (int l = 0; l < 64; ++l) v[l] = part[(int64_t)l * C + c];
+#pragma unroll
+    for (int s2 = 32; s2 >= 1; s2 >>= 1)
+#pragma unroll
+        for (int l = 0; l < s2; ++l) v[l] = v[l] + v[l + s2];
+    ssq[c] = v[0];
+}
+
+// Random selection scores from a counter-based generator: score[c] is the top
+// 24 bits of the (c + 1)-th output of SplitMix64 (Steele, Lea and Flood, 2014)
+// started at state `seed`, scaled by 2^-24 (a uniform value in [0, 1), exact in
+// fp32).  Output c needs only the counter c, so every channel is independent.
+__global__ void random_scores_kernel(uint64_t seed, int64_t C, float* __restrict__ sc) {
+    const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= C) return;
+    uint64_t z = seed + (uint64_t)(c + 1) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    sc[c] = (float)(uint32_t)(z >> 40) * 0x1p-24f;
+}
+
+// Head-level selection: hs[g] = sum over j < d of score[g d + j] (fp32, j
+// ascending from +0); the kept heads (top-n over hs) expand to their channels.
+__global__ void head_score_kernel(const float* __restrict__ sc, int64_t H, int64_t d,
+                                  float* __restrict__ hs) {
+    const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= H) return;
+    float s = 0.0f;
+    for (int64_t j = 0; j < d; ++j) s = s + sc[g * d + j];
+    hs[g] = s;
+}
+
+__global__ void head_expand_kernel(const int32_t* __restrict__ heads, int64_t nh, int64_t d,
+                                   int32_t* __restrict__ idx) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= nh * d) return;
+    idx[p] = (int32_t)(heads[p / d] * d + p % d);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
@@ -635,5 +725,42 @@ hipError_t launch_stack_index(const int32_t* idx, int64_t n, int64_t C, int64_t 
     if (n <= 0 || copies <= 0) return hipSuccess;
     hipLaunchKernelGGL(stack_index_kernel, dim3((unsigned)ceil_div(n * copies, 256)), dim3(256), 0,
                        st, idx, n, C, copies, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_ssq(int crit, bool bf16, const void* Y0, int64_t ld0, const void* Y1, int64_t ld1,
+                            const int32_t* rows, int64_t Tc, int64_t C, float* part, float* ssq,
+                            hipStream_t st) {
+    if (C <= 0) return hipSuccess;
+    const dim3 grid((unsigned)ceil_div(C, WAVE * 8), 16);
+#define DCH(TT, CR)                                                                                   \
+    hipLaunchKernelGGL((dense_chain_kernel<TT, CR>), grid, dim3(256), 0, st, (const TT*)Y0, ld0,     \
+                       (const TT*)Y1, ld1, rows, Tc, C, part)
+    if (bf16) {
+        if (crit == 1) DCH(bf16_t, 1); else DCH(bf16_t, 0);
+    } else {
+        if (crit == 1) DCH(float, 1); else DCH(float, 0);
+    }
+#undef DCH
+    // rows past Tc leave chains at +0: every chain slot of every channel is written
+    hipLaunchKernelGGL(r64_tree_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, st, part, C, ssq);
+    return hipGetLastError();
+}
+
+hipError_t launch_head_select(const float* scores, int64_t H, int64_t d, int64_t nh, float* hs,
+                              int32_t* heads, int32_t* idx, hipStream_t st) {
+    if (nh <= 0) return hipSuccess;
+    hipLaunchKernelGGL(head_score_kernel, dim3((unsigned)ceil_div(H, 256)), dim3(256), 0, st, scores, H,
+                       d, hs);
+    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(1024), 0, st, hs, H, nh, heads);
+    hipLaunchKernelGGL(head_expand_kernel, dim3((unsigned)ceil_div(nh * d, 256)), dim3(256), 0, st, heads,
+                       nh, d, idx);
+    return hipGetLastError();
+}
+
+hipError_t launch_random_scores(uint64_t seed, int64_t C, float* scores, hipStream_t st) {
+    if (C <= 0) return hipSuccess;
+    hipLaunchKernelGGL(random_scores_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, st, seed, C,
+                       scores);
     return hipGetLastError();
 }

@@ -405,6 +405,85 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     return hip_check(h, e, "score_select");
 }
 
+// ---------------------------------------------------------------- criterion variants
+sl_status sl_select_top(sl_handle* h, const float* scores, int64_t C, int64_t n_keep, int32_t* idx) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, C >= 1 && C <= INT32_MAX, "C out of range");
+    SL_REQUIRE(h, n_keep >= 0 && n_keep <= C, "n_keep must be in [0, C]");
+    if (n_keep == 0) return SL_OK;
+    SL_REQUIRE(h, scores && idx, "NULL pointer");
+    DeviceGuard g(h->device);
+    Timed tm(h, K_TOPK, 0, 4.0 * C + 4.0 * n_keep);
+    return hip_check(h, launch_topk(scores, C, n_keep, idx, h->stream), "select_top");
+}
+
+sl_status sl_random_scores(sl_handle* h, uint64_t seed, int64_t C, float* scores) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, C >= 0 && C <= INT32_MAX, "C out of range");
+    if (C == 0) return SL_OK;
+    SL_REQUIRE(h, scores != nullptr, "NULL pointer");
+    DeviceGuard g(h->device);
+    Timed tm(h, K_SCORE, 0, 4.0 * C);
+    return hip_check(h, launch_random_scores(seed, C, scores, h->stream), "random_scores");
+}
+
+sl_status sl_dense_scores(sl_handle* h, sl_criterion crit, sl_dtype dt, const void* Y0, int64_t ld0,
+                          const void* Y1, int64_t ld1, const int32_t* rows, int64_t T_c, int64_t C,
+                          int64_t n_rep, int64_t head_dim, float* scores) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, crit == SL_CRIT_L2 || crit == SL_CRIT_SWIGLU_L2 || crit == SL_CRIT_QK,
+               "bad criterion");
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, C >= 1 && C <= INT32_MAX && T_c >= 0, "bad sizes");
+    SL_REQUIRE(h, scores != nullptr && (T_c == 0 || rows != nullptr), "NULL pointer");
+    const int64_t Cq = crit == SL_CRIT_QK ? C * n_rep : 0;
+    if (crit == SL_CRIT_QK)
+        SL_REQUIRE(h, n_rep >= 1 && head_dim >= 1 && C % head_dim == 0, "bad QK grouping");
+    if (T_c > 0) {
+        SL_REQUIRE(h, Y0 != nullptr && (crit == SL_CRIT_L2 || Y1 != nullptr), "NULL pointer");
+        SL_REQUIRE(h, ld0 >= (crit == SL_CRIT_QK ? Cq : C), "ld0 too small");
+        if (crit != SL_CRIT_L2) SL_REQUIRE(h, ld1 >= C, "ld1 too small");
+    }
+    DeviceGuard g(h->device);
+    const int64_t Cmax = crit == SL_CRIT_QK ? Cq : C;
+    const size_t part_bytes = round_up((size_t)64 * Cmax * 4, 256);
+    const size_t qk_bytes = crit == SL_CRIT_QK ? round_up((size_t)Cq * 4, 256) + round_up((size_t)C * 4, 256) : 0;
+    SL_CHECK(ensure_ws(h, part_bytes + qk_bytes));
+    float* part = (float*)h->ws;
+    const bool bf = dt == SL_BF16;
+    const double es = (double)esize(dt);
+    Timed tm(h, K_SCORE, (crit == SL_CRIT_QK ? 2.0 * (Cq + C) : 2.0 * C) * T_c,
+             es * T_c * (crit == SL_CRIT_L2 ? C : (crit == SL_CRIT_QK ? Cq + C : 2.0 * C)) + 4.0 * C);
+    hipError_t e;
+    if (crit == SL_CRIT_QK) {
+        float* sq = (float*)((char*)h->ws + part_bytes);
+        float* sk = (float*)((char*)h->ws + part_bytes + round_up((size_t)Cq * 4, 256));
+        e = launch_dense_ssq(0, bf, Y0, ld0, nullptr, 0, rows, T_c, Cq, part, sq, h->stream);
+        if (e == hipSuccess) e = launch_dense_ssq(0, bf, Y1, ld1, nullptr, 0, rows, T_c, C, part, sk, h->stream);
+        if (e == hipSuccess) e = launch_qk_combine(sq, sk, C / head_dim, n_rep, head_dim, scores, h->stream);
+    } else {
+        e = launch_dense_ssq(crit == SL_CRIT_SWIGLU_L2 ? 1 : 0, bf, Y0, ld0, Y1, ld1, rows, T_c, C, part,
+                             scores, h->stream);
+    }
+    return hip_check(h, e, "dense_scores");
+}
+
+sl_status sl_select_heads(sl_handle* h, const float* scores, int64_t n_heads, int64_t head_dim,
+                          int64_t heads_keep, int32_t* idx) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, n_heads >= 1 && head_dim >= 1 && n_heads * head_dim <= INT32_MAX, "bad sizes");
+    SL_REQUIRE(h, heads_keep >= 0 && heads_keep <= n_heads, "heads_keep must be in [0, n_heads]");
+    if (heads_keep == 0) return SL_OK;
+    SL_REQUIRE(h, scores && idx, "NULL pointer");
+    DeviceGuard g(h->device);
+    SL_CHECK(ensure_ws(h, round_up((size_t)n_heads * 4, 256) * 2));
+    float* hs = (float*)h->ws;
+    int32_t* heads = (int32_t*)((char*)h->ws + round_up((size_t)n_heads * 4, 256));
+    Timed tm(h, K_TOPK, (double)n_heads * head_dim, 4.0 * n_heads * head_dim + 4.0 * heads_keep * head_dim);
+    return hip_check(h, launch_head_select(scores, n_heads, head_dim, heads_keep, hs, heads, idx, h->stream),
+                     "select_heads");
+}
+
 // ---------------------------------------------------------------- a5
 sl_status sl_expand_gqa(sl_handle* h, const int32_t* idx_kv, int64_t n, int64_t n_rep,
                         int64_t head_dim, int32_t* idx_q) {

@@ -94,6 +94,16 @@ hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t
 hipError_t launch_qk_combine(const float* ssqQ, const float* ssqK, int64_t H_kv, int64_t n_rep,
                              int64_t d, float* score, hipStream_t st);
 hipError_t launch_topk(const float* scores, int64_t C, int64_t n, int32_t* idx, hipStream_t st);
+// dense criterion: ssq[c] = R64 over rows of v^2, v = Y0 (crit 0) or silu(Y0) * Y1
+// (crit 1); part holds 64 * C floats
+hipError_t launch_dense_ssq(int crit, bool bf16, const void* Y0, int64_t ld0, const void* Y1, int64_t ld1,
+                            const int32_t* rows, int64_t Tc, int64_t C, float* part, float* ssq,
+                            hipStream_t st);
+// random selection scores: SplitMix64 output c + 1 from state seed, top 24 bits / 2^24
+hipError_t launch_random_scores(uint64_t seed, int64_t C, float* scores, hipStream_t st);
+// head-level selection: hs [H], heads [nh] scratch; idx [nh * d] out
+hipError_t launch_head_select(const float* scores, int64_t H, int64_t d, int64_t nh, float* hs,
+                              int32_t* heads, int32_t* idx, hipStream_t st);
 hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64_t d,
                              int32_t* out, hipStream_t st);
 hipError_t launch_offset_index(const int32_t* idx, int64_t n, int64_t offset, int32_t* out,

@@ -37,8 +37,11 @@ def keep_count(C: int, num: int, den: int) -> int:
 
 
 class SparseFFN:
+    CRITERIA = ("svd", "oracle", "random")
+
     def __init__(self, W_gate, W_up, W_down, A_gate, B_gate, A_up, B_up, A_down, B_down,
-                 WA_gu, WB_gate, WB_up, scale, sparsity=(7, 10), dense=False):
+                 WA_gu, WB_gate, WB_up, scale, sparsity=(7, 10), dense=False, criterion="svd",
+                 seed=0):
         dev = W_gate.device
         self.dtype = W_gate.dtype
         self.F, self.D = W_gate.shape
@@ -49,6 +52,13 @@ class SparseFFN:
         # kept, no estimator, same LoRA) -- the baseline the sparse block is
         # compared with.
         self.dense = dense
+        # criterion ablations (paper-graph summary, Table 7 and Table 10):
+        # "svd" the rank-k estimate (the method), "oracle" the same SwiGLU-L2
+        # criterion on the exact gate/up outputs of the frozen weights, "random"
+        # a uniformly random channel set (library draws, seed + call number)
+        assert criterion in self.CRITERIA, criterion
+        self.criterion = criterion
+        self.seed, self.calls, self.last_seed = int(seed), 0, None
         self.n = self.F if dense else keep_count(self.F, *sparsity)
         self.W_gu = torch.cat([W_gate, W_up], 0).contiguous()
         self.W_guT = torch.empty(self.D, 2 * self.F, dtype=self.dtype, device=dev)
@@ -71,7 +81,7 @@ class SparseFFN:
         # later in the block reads, so they overlap the main-branch products
         self.side = torch.cuda.Stream(device=dev)
         self._ev = [torch.cuda.Event() for _ in range(4)]
-        assert dense or self.k > 0, "the estimator factors are required unless dense"
+        assert dense or criterion != "svd" or self.k > 0, "the estimator factors are required"
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):
@@ -88,6 +98,7 @@ class SparseFFN:
         if self.dense:
             torch.arange(self.F, out=self.idx)
             torch.arange(2 * self.F, out=self.idx2)
+        self.idx_all = torch.arange(2 * F, dtype=torch.int32, device=dev) if self.criterion == "oracle" else None
         self.gu = e(T, 2 * F, dtype=dt)
         self.h = e(T, F, dtype=dt)
         self.y = e(T, D, dtype=dt)
@@ -112,32 +123,30 @@ class SparseFFN:
         self.x = x
         main = torch.cuda.current_stream(x.device)
         ops.token_split(roles, self.ctx_rows, self.out_rows)
-        # side stream: the LoRA down-projection of the block input, then the
-        # gate|up product of the output rows (dense over every channel, so it
-        # does not wait for the selection) -- both overlap the estimator,
-        # scoring and selection on the main stream, whose small launches leave
-        # most compute units idle
+        # side stream: the LoRA down-projection of the block input, then (with
+        # the estimator) the gate|up product of the output rows (dense over
+        # every channel, so it does not wait for the selection) -- both overlap
+        # the estimator, scoring and selection on the main stream, whose small
+        # launches leave most compute units idle
+        overlap = not self.dense and self.criterion == "svd"
         self._ev[0].record(main)
         self.side.wait_event(self._ev[0])
         lora = (self.xl_gu, self.B_bd, 2 * r, self.scale)
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
             self._ev[1].record(self.side)
-            if not self.dense:
+            if overlap:
                 ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
                                       self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
             self._ev[3].record(self.side)
         if not self.dense:
-            # estimator on context tokens, SwiGLU-L2 criterion, top-n (shared by gate/up/down)
-            ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
-            ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
-                             scores=self.scores, off0=0, off1=self.k)
-            ops.stack_index(self.idx, F, 2, self.idx2)
+            self._select(x)
         main.wait_event(self._ev[1])
         # the gate|up main branch of the context rows (gathered channels; every
-        # row when dense) with the LoRA term fused into the same accumulators
+        # row when dense or not overlapped) with the LoRA term fused into the
+        # same accumulators
         ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
-                              lora=lora, flags=0 if self.dense else ops.ONLY_CTX_ROWS)
+                              lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
         main.wait_event(self._ev[3])
         g, u = self.gu[:, :F], self.gu[:, F:]
         ops.swiglu_fwd(g, u, self.h)
@@ -146,6 +155,28 @@ class SparseFFN:
         ops.sparse_linear_fwd("in", self.h, self.W_dn, self.Wt_dn, self.ctx_rows, self.out_rows,
                               self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale))
         return self.y
+
+    def _select(self, x):
+        """The shared gate/up/down selection idx (and its stacked form idx2)."""
+        F = self.F
+        if self.criterion == "svd":
+            # estimator on context tokens, SwiGLU-L2 criterion, top-n
+            ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
+            ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
+                             scores=self.scores, off0=0, off1=self.k)
+        elif self.criterion == "oracle":
+            # exact gate|up outputs of the frozen weights (no LoRA) in gu, which
+            # the product below then overwrites
+            ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx_all,
+                                  self.gu)
+            ops.dense_scores("swiglu", self.gu[:, :F], self.gu[:, F:], self.ctx_rows, self.scores)
+            ops.select_top(self.scores, self.n, self.idx)
+        else:
+            self.last_seed = self.seed + self.calls
+            ops.random_scores(self.last_seed, self.scores)
+            ops.select_top(self.scores, self.n, self.idx)
+        self.calls += 1
+        ops.stack_index(self.idx, F, 2, self.idx2)
 
     def backward(self, dy):
         F, D, r, s = self.F, self.D, self.r, self.scale

@@ -167,6 +167,41 @@ def score_select(crit, xa, WB0, WB1, n_keep, idx, scores=None, off0=0, off1=None
     _check(h, st, "sl_score_select")
 
 
+def select_top(scores, n_keep, idx):
+    """idx = the n_keep channels with the largest scores (ties: lower index), ascending."""
+    h = handle(_dev(scores))
+    st = _lib.load().sl_select_top(h, _ptr(scores), scores.numel(), int(n_keep), _ptr(idx))
+    _check(h, st, "sl_select_top")
+
+
+def random_scores(seed, scores):
+    """scores (fp32 [C]) = the library's counter-based uniform draws for seed."""
+    h = handle(_dev(scores))
+    st = _lib.load().sl_random_scores(h, ctypes.c_uint64(int(seed) & ((1 << 64) - 1)), scores.numel(),
+                                      _ptr(scores))
+    _check(h, st, "sl_random_scores")
+
+
+def dense_scores(crit, Y0, Y1, rows, scores, C=None, n_rep=1, head_dim=1):
+    """Criterion on exact outputs: Y0 (and Y1) are [T, *] views of the dense
+    main-branch outputs; rows the context rows; scores fp32 [C] out."""
+    h = handle(_dev(Y0))
+    if C is None:
+        C = Y1.shape[1] if crit in ("qk", "swiglu") else Y0.shape[1]
+    st = _lib.load().sl_dense_scores(h, CRIT[crit], _dt(Y0), _ptr(Y0), _ld(Y0), _ptr(Y1),
+                                     _ld(Y1) if Y1 is not None else 0, _ptr(rows), rows.numel(), C,
+                                     n_rep, head_dim, _ptr(scores))
+    _check(h, st, "sl_dense_scores")
+
+
+def select_heads(scores, n_heads, head_dim, heads_keep, idx):
+    """Keep the heads_keep heads with the largest summed channel score; idx
+    [heads_keep * head_dim] lists their channels ascending."""
+    h = handle(_dev(scores))
+    st = _lib.load().sl_select_heads(h, _ptr(scores), n_heads, head_dim, int(heads_keep), _ptr(idx))
+    _check(h, st, "sl_select_heads")
+
+
 def expand_gqa(idx_kv, n_rep, head_dim, idx_q):
     h = handle(_dev(idx_kv))
     st = _lib.load().sl_expand_gqa(h, _ptr(idx_kv), idx_kv.numel(), n_rep, head_dim, _ptr(idx_q))

@@ -199,6 +199,57 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
                           const float* WB1, int64_t k, int64_t C, int64_t n_rep,
                           int64_t head_dim, int64_t n_keep, float* scores, int32_t* idx);
 
+/* ---------------------------------------------------------------- criterion variants */
+
+/* Top-n of given scores, the selection rule of sl_score_select (largest score
+ * bit patterns, NaN above +inf, ties to the lower index, idx ascending).  With
+ * scores drawn at random by the caller this is the pages' random-selection
+ * ablation (paper-graph summary, "Ablation Studies and Robustness Checks",
+ * pruning criteria, Table 10); with sl_dense_scores it selects by the exact
+ * ("oracle") criterion.  scores device fp32 [C]; idx device int32 [n_keep]
+ * out; 0 <= n_keep <= C. */
+sl_status sl_select_top(sl_handle* h, const float* scores, int64_t C, int64_t n_keep, int32_t* idx);
+
+/* Scores for the random-selection ablation, from a counter-based generator:
+ * scores[c] = (z_{c+1} >> 40) * 2^-24, where z_i is the i-th output of
+ * SplitMix64 (Steele, Lea and Flood, 2014: state += 0x9E3779B97F4A7C15;
+ * z = state; z = (z ^ z >> 30) * 0xBF58476D1CE4E5B9; z = (z ^ z >> 27) *
+ * 0x94D049BB133111EB; z ^= z >> 31) started at state `seed`.  Uniform in
+ * [0, 1), exact in fp32; with sl_select_top it keeps a uniformly random
+ * channel subset (the caller varies the seed per step and layer).
+ * scores device fp32 [C] out. */
+sl_status sl_random_scores(sl_handle* h, uint64_t seed, int64_t C, float* scores);
+
+/* The channel criteria of sl_score_select evaluated on exact outputs instead
+ * of the rank-k estimate (paper-graph summary §3.4, "Oracle Sparse Neuron
+ * Selection Criteria": the oracle row of Table 7; these need the dense
+ * outputs, which is what the estimator avoids):
+ *   SL_CRIT_L2:        v = Y0[t, c]
+ *   SL_CRIT_SWIGLU_L2: v = silu(Y0[t, c]) * Y1[t, c]  (Y0 = gate, Y1 = up;
+ *                      silu with the library's fixed fp32 exp)
+ *   ssq[c] = R64 over m < T_c of (v, v) at t = rows[m] (the order of
+ *            sl_score_select: 64 chains m mod 64, then the pairwise tree)
+ *   SL_CRIT_QK: Y0 = Q [*, C n_rep], Y1 = K [*, C]; scores[g d + j] =
+ *            (sum over the group's query heads of ssq_Q) * ssq_K[g d + j]
+ *   otherwise scores = ssq.
+ * Y0/Y1 device (dt) with leading dimensions ld0/ld1 (the main-branch outputs
+ * x W^T of the frozen weight); rows device int32 [T_c] (context rows);
+ * scores device fp32 [C] out.  T_c = 0 gives zeros. */
+sl_status sl_dense_scores(sl_handle* h, sl_criterion crit, sl_dtype dt, const void* Y0, int64_t ld0,
+                          const void* Y1, int64_t ld1, const int32_t* rows, int64_t T_c, int64_t C,
+                          int64_t n_rep, int64_t head_dim, float* scores);
+
+/* Head-level selection, the coarser alternative the pages weigh against
+ * channel-level QK sparsity (paper-graph summary §3.4, "Why not head-level
+ * pruning for QK?"; Table 10): head score hs[g] = sum over j < head_dim of
+ * scores[g head_dim + j] (fp32, j ascending from +0); the heads_keep heads
+ * with the largest hs (rule of sl_select_top) keep all their channels:
+ * idx[i head_dim + j] = head_i head_dim + j, heads ascending.
+ * scores device fp32 [n_heads head_dim]; idx device int32 [heads_keep
+ * head_dim] out. */
+sl_status sl_select_heads(sl_handle* h, const float* scores, int64_t n_heads, int64_t head_dim,
+                          int64_t heads_keep, int32_t* idx);
+
 /* ---------------------------------------------------------------- a5: index propagation */
 
 /* Key/value-space selection -> query-space (or o-input) selection under

@@ -176,3 +176,67 @@ def select_attn(x, ctx_rows, WA_t_qkv, WB_q, WB_k, WB_v, n_kv_heads, n_rep, head
     idx_qk = select(qk_combine(sq, sk, n_kv_heads, n_rep, head_dim), n_qk)
     idx_vo = select(ssq_l2(xa, WB_v, off=2 * k), n_vo)
     return idx_qk, idx_vo
+
+
+# ---------------------------------------------------------------- criterion variants
+# Paper-graph summary §3.4 "Oracle Sparse Neuron Selection Criteria" (the
+# criteria on exact outputs, the oracle row of Table 7), "Why not head-level
+# pruning for QK?" and the pruning-criterion ablation of Table 10 (random,
+# head-level).
+
+
+def dense_ssq(crit, Y0, Y1, rows):
+    """Criterion on exact outputs: v = Y0[rows] ("l2") or
+    silu_sl(Y0[rows]) * Y1[rows] ("swiglu", one fp32 rounding of the product);
+    ssq[c] = R64 over the listed rows of (v[:, c], v[:, c])."""
+    rows = np.asarray(rows, np.int64)
+    v = _f32(np.asarray(Y0, np.float32)[rows])
+    if crit == "swiglu":
+        v = _f32(silu_sl(v) * np.asarray(Y1, np.float32)[rows])
+    T_c, C = v.shape
+    out = np.zeros(C, np.float32)
+    for c in range(C):
+        col = np.ascontiguousarray(v[:, c])
+        out[c] = np.float32(lib().orc_r64(_p(col), 1, _p(col), 1, T_c))
+    return out
+
+
+def dense_scores(crit, Y0, Y1, rows, n_kv_heads=1, n_rep=1, head_dim=1):
+    """Scores of the exact ("oracle") criterion: L2 and SwiGLU-L2 as dense_ssq;
+    QK from Q = Y0 and K = Y1 through qk_combine."""
+    if crit == "qk":
+        return qk_combine(dense_ssq("l2", Y0, None, rows), dense_ssq("l2", Y1, None, rows),
+                          n_kv_heads, n_rep, head_dim)
+    return dense_ssq(crit, Y0, Y1, rows)
+
+
+def head_scores(scores, n_heads, head_dim):
+    """hs[g] = sum over j < head_dim of scores[g head_dim + j], fp32 adds with j
+    ascending from +0."""
+    s = _f32(scores).reshape(n_heads, head_dim)
+    hs = np.zeros(n_heads, np.float32)
+    for j in range(head_dim):
+        hs = (hs + s[:, j]).astype(np.float32)
+    return hs
+
+
+def select_heads(scores, n_heads, head_dim, heads_keep):
+    """Head-level selection: the heads_keep heads with the largest head score
+    (rule of ``select``) keep every channel; channels ascending."""
+    heads = select(head_scores(scores, n_heads, head_dim), heads_keep)
+    return (heads[:, None] * head_dim + np.arange(head_dim)[None, :]).reshape(-1).astype(np.int32)
+
+
+_GAMMA = np.uint64(0x9E3779B97F4A7C15)
+
+
+def random_scores(seed, C):
+    """Uniform scores for the random-selection ablation: score[c] = top 24 bits
+    of the (c + 1)-th SplitMix64 output from state ``seed`` (Steele, Lea and
+    Flood, 2014), times 2^-24."""
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed) + np.arange(1, C + 1, dtype=np.uint64) * _GAMMA
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+        z = z ^ (z >> np.uint64(31))
+    return ((z >> np.uint64(40)).astype(np.float64) * 2.0 ** -24).astype(np.float32)
