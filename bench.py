@@ -29,6 +29,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-ablations", action="store_true",
+                    help="skip the step times with the random and the exact-output criteria")
+    ap.add_argument("--no-schedule", action="store_true",
+                    help="skip the whole-training-step run with the dense-then-sparse schedule")
+    ap.add_argument("--schedule-steps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -71,7 +76,7 @@ def measured_traffic():
         return None
 
 
-def build_block(inp, cfg, dense):
+def build_block(inp, cfg, dense, criterion="svd"):
     import numpy as np
     import torch
     from contextual_sparsity_lora_amd.ffn import SparseFFN
@@ -82,7 +87,7 @@ def build_block(inp, cfg, dense):
                     t["B_up"], t["A_down"], t["B_down"],
                     torch.from_numpy(np.ascontiguousarray(inp["WA_t_gu"].T)).to(dev),
                     torch.from_numpy(inp["WB_gate"]).to(dev), torch.from_numpy(inp["WB_up"]).to(dev),
-                    inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense)
+                    inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense, criterion=criterion)
     roles = torch.from_numpy(inp["roles"]).to(dev)
     return blk, t["x"], roles, t["dy"]
 
@@ -112,6 +117,56 @@ def time_steps(blk, x, roles, dy, T_c, steps, warmup, ops, record=False, only=No
         ops.timing_enable(0, False)
         ops.timing_only(0, None)
     return start.elapsed_time(stop) / steps
+
+
+def training_schedule(inp, cfg, ops, steps, dense_frac=0.1, vocab=32000):
+    """Whole training steps (block forward, LM-head logits of the output rows,
+    cross-entropy, backward, AdamW on LoRA) over `steps` steps: once with the
+    first ceil(dense_frac steps) dense and the rest sparse, once all dense.
+    Returns the timings, the sparse-phase speedup s and the bound
+    1 / (p + (1 - p) / s) on the overall speedup."""
+    import math
+    import numpy as np
+    import torch
+    from contextual_sparsity_lora_amd.train import LoRATrainer
+    dev = "cuda:0"
+    rng = np.random.default_rng(cfg.seed + 77)
+    bf = torch.bfloat16
+    W_head = (torch.from_numpy(rng.standard_normal((vocab, cfg.hidden)).astype(np.float32)) * 0.02).to(bf).to(dev)
+    # a synthetic stream of two batches (hidden states and next-token labels)
+    xs = [torch.from_numpy(inp["x"]).to(bf).to(dev),
+          torch.from_numpy(rng.standard_normal((cfg.tokens, cfg.hidden)).astype(np.float32)).to(bf).to(dev)]
+    labels = [torch.from_numpy(rng.integers(0, vocab, size=cfg.tokens).astype(np.int32)).to(dev) for _ in xs]
+    roles = torch.from_numpy(inp["roles"]).to(dev)
+
+    def run(frac, n, record=None):
+        blk, _, _, _ = build_block(inp, cfg, dense=False)
+        tr = LoRATrainer(blk, W_head, total_steps=n, dense_frac=frac)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for t in range(n):
+            tr.step(xs[t % 2], labels[t % 2], roles, cfg.ctx_tokens)
+            ev[t + 1].record()
+        torch.cuda.synchronize()
+        ms = [ev[t].elapsed_time(ev[t + 1]) for t in range(n)]
+        del tr, blk
+        torch.cuda.empty_cache()
+        return ms
+
+    run(0.5, 4)                                   # warm-up: every kernel of both phases
+    sched = run(dense_frac, steps)
+    dense = run(1.0, steps)
+    nd = math.ceil(dense_frac * steps)
+    d_step = float(np.median(dense))
+    s_step = float(np.median(sched[nd:]))
+    s = d_step / s_step
+    return {"steps": steps, "dense_frac": dense_frac, "dense_steps": nd, "vocab": vocab,
+            "lr_schedule": "cosine, 4% warm-up", "optimizer": "AdamW on LoRA (fp32 masters)",
+            "dense_step_ms": round(d_step, 4), "sparse_step_ms": round(s_step, 4),
+            "scheduled_total_ms": round(sum(sched), 3), "dense_total_ms": round(sum(dense), 3),
+            "sparse_phase_speedup": round(s, 4), "overall_speedup": round(sum(dense) / sum(sched), 4),
+            "bound": round(1.0 / (dense_frac + (1.0 - dense_frac) / s), 4)}
 
 
 def cpu_baseline(inp, cfg):
@@ -247,6 +302,24 @@ def main():
         "cpu_baseline": None,
     }
     out.update(extra)
+    if not args.no_schedule:
+        extra["training_schedule"] = training_schedule(inp, cfg, ops, args.schedule_steps)
+        print(f"[bench] training schedule: {extra['training_schedule']}", file=sys.stderr, flush=True)
+    if not args.no_ablations:
+        # the same step with the selection made at random (no estimator: the
+        # difference is the estimator's cost) and by the exact-output criterion
+        # (dense gate|up outputs first: what the estimator avoids)
+        # (all three timed alike, without events)
+        crit_ms = {}
+        for crit in ("svd", "random", "oracle"):
+            ablk, x, roles, dy = build_block(inp, cfg, dense=False, criterion=crit)
+            crit_ms[crit] = round(time_steps(ablk, x, roles, dy, cfg.ctx_tokens, args.steps,
+                                             args.warmup, ops), 4)
+            del ablk
+            torch.cuda.empty_cache()
+        extra["criterion_ms_per_step"] = crit_ms
+        extra["estimator_overhead_vs_random"] = round(crit_ms["svd"] / crit_ms["random"] - 1.0, 4)
+        print(f"[bench] step ms by criterion: {crit_ms}", file=sys.stderr, flush=True)
     if args.calibrate_copy:
         src = torch.empty(128 * 1024 * 1024, dtype=torch.bfloat16, device="cuda:0")
         dst = torch.empty_like(src)

@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <new>
 
+#include <cmath>
+
 #include "sl_internal.h"
 
 namespace {
@@ -1030,6 +1032,58 @@ sl_status sl_dot_stats(sl_handle* h, const float* a, const float* b, int64_t n, 
     DeviceGuard gd(h->device);
     SL_CHECK(ensure_ws(h, 256 * 3 * sizeof(double)));
     return hip_check(h, launch_dot_stats(a, b, n, (double*)h->ws, out, h->stream), "dot_stats");
+}
+
+// ---------------------------------------------------------------- training step
+sl_status sl_token_ce(sl_handle* h, sl_dtype dt, const void* logits, int64_t ld, const int32_t* rows,
+                      int64_t n_rows, const int32_t* labels, int64_t V, float scale, void* dlogits,
+                      int64_t ld_d, double* loss) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, n_rows >= 0 && n_rows <= INT32_MAX && V >= 1, "bad sizes");
+    SL_REQUIRE(h, loss != nullptr && ((uintptr_t)loss & 7) == 0, "loss is NULL or misaligned");
+    DeviceGuard g(h->device);
+    if (n_rows > 0) {
+        SL_REQUIRE(h, logits && rows && labels && dlogits, "NULL pointer");
+        SL_REQUIRE(h, ld >= V && ld_d >= V, "leading dimension below V");
+    }
+    SL_CHECK(ensure_ws(h, round_up((size_t)(n_rows > 0 ? n_rows : 1) * 4, 256)));
+    Timed tm(h, K_REDUCE, 4.0 * n_rows * V, (double)esize(dt) * 2.0 * n_rows * V);
+    return hip_check(h, launch_ce_rows(dt == SL_BF16, logits, ld, rows, n_rows, labels, V, scale, dlogits,
+                                       ld_d, (float*)h->ws, loss, h->stream), "token_ce");
+}
+
+sl_status sl_adamw_step(sl_handle* h, const sl_adamw_tensor* tensors, int n, float lr, float beta1,
+                        float beta2, float eps, float weight_decay, int64_t step) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, n >= 0 && n <= SL_ADAMW_MAXT, "at most %d tensors per call", SL_ADAMW_MAXT);
+    SL_REQUIRE(h, step >= 1, "step counts from 1");
+    SL_REQUIRE(h, beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps > 0.f, "bad hyperparameters");
+    if (n == 0) return SL_OK;
+    SL_REQUIRE(h, tensors != nullptr, "tensors is NULL");
+    AdamwArgs a{};
+    int64_t blocks = 0;
+    for (int i = 0; i < n; ++i) {
+        const sl_adamw_tensor& t = tensors[i];
+        SL_REQUIRE(h, t.rows >= 0 && t.cols >= 0, "tensor %d: bad shape", i);
+        SL_REQUIRE(h, t.param && t.grad && t.m && t.v, "tensor %d: NULL pointer", i);
+        SL_REQUIRE(h, !t.out || t.ld_out >= t.cols, "tensor %d: ld_out < cols", i);
+        SL_REQUIRE(h, t.out_dtype == SL_BF16 || t.out_dtype == SL_F32, "tensor %d: bad out_dtype", i);
+        a.t[i] = AdamwTensor{t.param, t.grad, t.m, t.v, t.out, t.ld_out, t.out_dtype == SL_F32 ? 1 : 0,
+                             t.rows, t.cols, blocks};
+        blocks += ceil_div(t.rows * t.cols, 256);
+    }
+    a.n = n;
+    a.lr = lr;
+    a.b1 = beta1;
+    a.b2 = beta2;
+    a.eps = eps;
+    a.wd = weight_decay;
+    a.bc1 = (float)(1.0 - std::pow((double)beta1, (double)step));
+    a.bc2 = (float)(1.0 - std::pow((double)beta2, (double)step));
+    DeviceGuard g(h->device);
+    Timed tm(h, K_LORA, 0, 20.0 * 256 * blocks);
+    return hip_check(h, launch_adamw(a, blocks, h->stream), "adamw");
 }
 
 // ---------------------------------------------------------------- a14: layer glue

@@ -158,6 +158,28 @@ hipError_t launch_attn_bwd(bool bf16, const void* q, int64_t ldq, const void* k,
                            int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq, void* dk,
                            int64_t lddk, void* dv, int64_t lddv, hipStream_t st);
 // (a.b, a.a, b.b) in fp64 over n fp32 values, fixed order; part holds 256 x 3 doubles
+// ---------------------------------------------------------------- training step
+constexpr int SL_ADAMW_MAXT = 16;
+struct AdamwTensor {
+    float* p;            // fp32 master [rows * cols]
+    const float* g;      // gradient [rows * cols]
+    float* m;
+    float* v;
+    void* out;           // compute copy written after the update (may be null), [rows, ld_out]
+    int64_t ld_out;
+    int out_f32;         // the copy is fp32 (else bf16)
+    int64_t rows, cols;
+    int64_t first_block; // first 256-element block of this tensor in the launch
+};
+struct AdamwArgs {
+    AdamwTensor t[SL_ADAMW_MAXT];
+    int n;
+    float lr, b1, b2, eps, wd, bc1, bc2;
+};
+hipError_t launch_adamw(const AdamwArgs& a, int64_t blocks, hipStream_t st);
+hipError_t launch_ce_rows(bool bf16, const void* L, int64_t ldl, const int32_t* rows, int64_t nrows,
+                          const int32_t* labels, int64_t V, float scale, void* dL, int64_t lddl,
+                          float* loss_rows, double* loss_sum, hipStream_t st);
 hipError_t launch_dot_stats(const float* a, const float* b, int64_t n, double* part, double* out,
                             hipStream_t st);
 hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,

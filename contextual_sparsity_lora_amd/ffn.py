@@ -59,7 +59,8 @@ class SparseFFN:
         assert criterion in self.CRITERIA, criterion
         self.criterion = criterion
         self.seed, self.calls, self.last_seed = int(seed), 0, None
-        self.n = self.F if dense else keep_count(self.F, *sparsity)
+        self.n_sparse = keep_count(self.F, *sparsity)
+        self.n = self.F if dense else self.n_sparse
         self.W_gu = torch.cat([W_gate, W_up], 0).contiguous()
         self.W_guT = torch.empty(self.D, 2 * self.F, dtype=self.dtype, device=dev)
         ops.transpose(self.W_gu, self.W_guT)
@@ -83,6 +84,27 @@ class SparseFFN:
         self._ev = [torch.cuda.Event() for _ in range(4)]
         assert dense or criterion != "svd" or self.k > 0, "the estimator factors are required"
         self._T = None
+
+    def set_dense(self, dense: bool):
+        """Switch between the dense path (every channel kept, no selection) and
+        the sparse path at the block's sparsity -- the two phases of a
+        progressive schedule (paper-graph summary, "Step Sensitivity and
+        Progressive Sparse Fine-Tuning").  Takes effect at the next forward."""
+        dense = bool(dense)
+        if dense == self.dense:
+            return
+        assert dense or self.criterion != "svd" or self.k > 0, "the estimator factors are required"
+        self.dense = dense
+        self.n = self.F if dense else self.n_sparse
+        self._T = None
+
+    def lora_params(self):
+        """(name, bf16 view the products read, name of the fp32 gradient) per
+        LoRA tensor; the views point into the stacked copies."""
+        r, F = self.r, self.F
+        return [("A_gate", self.A_gu[:r], "dA_gate"), ("A_up", self.A_gu[r:], "dA_up"),
+                ("B_gate", self.B_bd[:F, :r], "dB_gate"), ("B_up", self.B_bd[F:, r:], "dB_up"),
+                ("A_down", self.A_down, "dA_down"), ("B_down", self.B_down, "dB_down")]
 
     def _alloc(self, T, T_c, T_o, dev):
         if self._T == (T, T_c, T_o):
@@ -128,7 +150,7 @@ class SparseFFN:
         # every channel, so it does not wait for the selection) -- both overlap
         # the estimator, scoring and selection on the main stream, whose small
         # launches leave most compute units idle
-        overlap = not self.dense and self.criterion == "svd"
+        overlap = not self.dense and self.criterion != "oracle"   # "oracle" scores in gu first
         self._ev[0].record(main)
         self.side.wait_event(self._ev[0])
         lora = (self.xl_gu, self.B_bd, 2 * r, self.scale)

@@ -341,6 +341,46 @@ def swiglu_bwd(dh, g, u, dg, du):
     _check(h, st, "sl_swiglu_bwd")
 
 
+def token_ce(logits, rows, labels, dlogits, loss, scale=None):
+    """Softmax cross-entropy of logits [T, V] on the listed rows against
+    labels[row]; dlogits = scale (softmax - onehot) on those rows; loss (fp64
+    [1] on the device) = scale * sum of row losses (scale default 1/len(rows))."""
+    h = handle(_dev(logits))
+    n = rows.numel()
+    if scale is None:
+        scale = 1.0 / max(n, 1)
+    st = _lib.load().sl_token_ce(h, _dt(logits), _ptr(logits), _ld(logits), _ptr(rows), n, _ptr(labels),
+                                 logits.shape[1], float(scale), _ptr(dlogits), _ld(dlogits), _ptr(loss))
+    _check(h, st, "sl_token_ce")
+
+
+class AdamwTensor(ctypes.Structure):
+    _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("ld_out", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("out_dtype", ctypes.c_int)]
+
+
+def adamw_step(groups, lr, step, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0):
+    """groups: list of (param fp32, grad fp32, m, v, out view (bf16 or fp32) or
+    None), param/grad/m/v contiguous of one shape [rows, cols] (or 1-d)."""
+    if not groups:
+        return
+    h = handle(_dev(groups[0][0]))
+    arr = (AdamwTensor * len(groups))()
+    for i, (p, g, m, v, out) in enumerate(groups):
+        assert all(t.is_contiguous() and t.dtype == torch.float32 and t.shape == p.shape for t in (p, g, m, v))
+        rows, cols = (p.shape[0], p.shape[1]) if p.dim() == 2 else (1, p.numel())
+        if out is not None:
+            assert tuple(out.shape) == (rows, cols) and (out.stride(1) == 1 or cols == 1)
+        arr[i] = AdamwTensor(p.data_ptr(), g.data_ptr(), m.data_ptr(), v.data_ptr(),
+                             out.data_ptr() if out is not None else None,
+                             out.stride(0) if out is not None else 0, rows, cols,
+                             _dt(out) if out is not None else 0)
+    st = _lib.load().sl_adamw_step(h, arr, len(groups), float(lr), float(beta1), float(beta2), float(eps),
+                                   float(weight_decay), int(step))
+    _check(h, st, "sl_adamw_step")
+
+
 def dot_stats(a, b, out):
     """out (fp64 [3] on the device) = (a.b, a.a, b.b) over the fp32 elements of
     two contiguous tensors of the same size."""

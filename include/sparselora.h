@@ -382,6 +382,46 @@ sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ld
                                   int64_t ld_lora_B, int64_t lora_r, float lora_scale,
                                   const int32_t* idx, int64_t n);
 
+/* ---------------------------------------------------------------- training step */
+
+/* Token loss on the listed rows (paper-graph summary, "Putting It All
+ * Together": the loss is computed only on output token positions, the
+ * standard autoregressive loss): for m < n_rows, t = rows[m], z =
+ * logits[t, 0:V], y = labels[t] (0 <= y < V),
+ *   row loss   = logsumexp(z) - z[y]                       (fp32, max-shifted)
+ *   dlogits[t, c] = scale * (softmax(z)[c] - [c == y])     (dt)
+ *   *loss      = scale * sum of the row losses             (fp64, fixed order)
+ * scale = 1 / n_rows gives the mean loss and its gradient.  Rows not listed
+ * are not touched.  logits, dlogits device (dt) [*, ld >= V]; rows device
+ * int32 [n_rows]; labels device int32 [*] (indexed by row); loss device fp64
+ * [1] out.  dt = SL_BF16 or SL_F32. */
+sl_status sl_token_ce(sl_handle* h, sl_dtype dt, const void* logits, int64_t ld, const int32_t* rows,
+                      int64_t n_rows, const int32_t* labels, int64_t V, float scale, void* dlogits,
+                      int64_t ld_d, double* loss);
+
+/* One AdamW step (decoupled weight decay) on up to 16 tensors (paper-graph
+ * summary, "Putting It All Together": only the LoRA parameters are updated),
+ * elementwise in fp32:
+ *   p = p * (1 - lr wd);  m = b1 m + (1 - b1) g;  v = b2 v + (1 - b2) g^2
+ *   p = p - lr * (m / bc1) / (sqrt(v / bc2) + eps),  bc_i = 1 - b_i^step
+ * then, if out is set, out[r, c] = p[r cols + c] rounded to out_dtype (the
+ * copy the sparse products read).  param/grad/m/v: device fp32 [rows * cols],
+ * contiguous; out: device (out_dtype) [rows, ld_out >= cols] or NULL.  step >= 1
+ * (the number of this update); lr is the caller's scheduled rate. */
+typedef struct {
+    float* param;
+    const float* grad;
+    float* m;
+    float* v;
+    void* out;
+    int64_t ld_out;
+    int64_t rows;
+    int64_t cols;
+    sl_dtype out_dtype;
+} sl_adamw_tensor;
+sl_status sl_adamw_step(sl_handle* h, const sl_adamw_tensor* tensors, int n, float lr, float beta1,
+                        float beta2, float eps, float weight_decay, int64_t step);
+
 /* ---------------------------------------------------------------- gradient fidelity */
 
 /* Dot statistics of two fp32 vectors, for the cosine between a sparse and a

@@ -410,3 +410,93 @@ def ffn_grad_fidelity(inp, idx):
     fs, fd = ffn_block_fwd(inp, idx), ffn_block_fwd(inp, everything)
     bs, bd = ffn_block_bwd(inp, fs, idx), ffn_block_bwd(inp, fd, everything)
     return {k: grad_cosine(bs[k], bd[k]) for k in LORA_GRADS_FFN}
+
+
+# ---------------------------------------------------------------- training steps
+# Paper-graph summary, "Step Sensitivity and Progressive Sparse Fine-Tuning"
+# (dense for the first p of the steps, then sparse), "Interaction with the
+# learning rate schedule" (cosine with a 4 % warm-up), "Putting It All
+# Together" (loss on output positions only, the autoregressive loss; only the
+# LoRA parameters are updated).
+
+
+def round_to(a, dtype):
+    """Values rounded to the compute dtype ("f64" keeps them, "f32" to binary32,
+    "bf16" to bfloat16 with round-to-nearest-even), returned as float64."""
+    a = np.asarray(a, f64)
+    if dtype == "f64":
+        return a.copy()
+    f = a.astype(np.float32)
+    if dtype == "f32":
+        return f.astype(f64)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(f64)
+
+
+def token_ce(logits, labels):
+    """Mean softmax cross-entropy of the rows of logits [n, V] against integer
+    labels [n], and its gradient with respect to the logits."""
+    z = np.asarray(logits, f64)
+    n = z.shape[0]
+    if n == 0:
+        return 0.0, np.zeros_like(z)
+    zmax = z.max(axis=1, keepdims=True)
+    lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
+    rows = np.arange(n)
+    loss = float(np.mean(lse - z[rows, labels]))
+    p = np.exp(z - lse[:, None])
+    p[rows, labels] -= 1.0
+    return loss, p / n
+
+
+def adamw(p, g, m, v, step, lr, b1=0.9, b2=0.999, eps=1e-8, wd=0.0):
+    """One AdamW update (decoupled weight decay), textbook form."""
+    p = np.asarray(p, f64) * (1.0 - lr * wd)
+    m = b1 * m + (1.0 - b1) * g
+    v = b2 * v + (1.0 - b2) * g * g
+    mh, vh = m / (1.0 - b1 ** step), v / (1.0 - b2 ** step)
+    return p - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+def lr_schedule(step, total, peak, warmup_ratio=0.04):
+    """Rate of 0-based step: linear from 0 over the warm-up steps
+    (ceil(warmup_ratio total)), then half a cosine period down to 0 at `total`."""
+    w = int(np.ceil(warmup_ratio * total))
+    if step < w:
+        return peak * step / w
+    return peak * 0.5 * (1.0 + np.cos(np.pi * (step - w) / max(1, total - w)))
+
+
+LORA_FFN = ("A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down")
+
+
+def ffn_train(inp, W_head, xs, labels, total, n_dense, select, dtype, lr, warmup_ratio=0.04,
+              b1=0.9, b2=0.999, eps=1e-8, wd=0.0):
+    """len(xs) training steps of the FFN block with a frozen LM head W_head
+    [V, D]: step t runs dense (every channel) when t < n_dense, else with the
+    selection select(x_t); logits of the output rows, mean cross-entropy
+    against their labels, backward, AdamW on the six LoRA tensors (masters in
+    float64, the forward and backward use them rounded to `dtype`).  Returns
+    the per-step losses and the final masters."""
+    F = np.asarray(inp["W_gate"]).shape[0]
+    master = {k: np.asarray(inp[k], f64).copy() for k in LORA_FFN}
+    mom = {k: np.zeros_like(master[k]) for k in LORA_FFN}
+    vel = {k: np.zeros_like(master[k]) for k in LORA_FFN}
+    ctx, out = token_lists(inp["roles"])
+    Wh = np.asarray(W_head, f64)
+    losses = []
+    for t, (x, lab) in enumerate(zip(xs, labels)):
+        d = dict(inp, x=np.asarray(x, f64), **{k: round_to(master[k], dtype) for k in LORA_FFN})
+        idx = np.arange(F) if t < n_dense else select(x)
+        fw = ffn_block_fwd(d, idx)
+        loss, dlog = token_ce(fw["y"][out] @ Wh.T, np.asarray(lab)[out])
+        dy = np.zeros_like(fw["y"])
+        dy[out] = dlog @ Wh
+        bw = ffn_block_bwd(d, fw, idx, dy)
+        rate = lr_schedule(t, total, lr, warmup_ratio)
+        for k in LORA_FFN:
+            master[k], mom[k], vel[k] = adamw(master[k], bw["d" + k], mom[k], vel[k], t + 1, rate, b1, b2,
+                                              eps, wd)
+        losses.append(loss)
+    return losses, master

@@ -1,0 +1,125 @@
+"""GPU parity of whole training steps with the progressive schedule (dense
+first steps, then sparse): losses per step and the LoRA masters after the last
+update against the oracle's training steps; the token loss and the AdamW
+update on their own."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa, reference as ref
+from tests.gpu_util import DEV, TOL, dev_pad, empty_pad, host, host_i, mar, need_lib, to_dev
+from workloads.configs import CONFIGS, scaled
+from workloads.gen import make_ffn_inputs, round_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    return ops
+
+
+@pytest.mark.parametrize("dtype,n,V", [("f32", 37, 97), ("bf16", 300, 1000), ("bf16", 0, 10)])
+def test_token_ce(dtype, n, V, rng):
+    ops = _ops()
+    T = 400
+    z = round_dtype(rng.standard_normal((T, V)) * 4, dtype)
+    rows = np.sort(rng.choice(T, n, replace=False)).astype(np.int32)
+    lab = rng.integers(0, V, size=T).astype(np.int32)
+    dz = empty_pad(T, V, dtype, fill=7.0)
+    loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    ops.token_ce(dev_pad(z, dtype), to_dev(rows, None), to_dev(lab, None), dz, loss)
+    torch.cuda.synchronize()
+    want_loss, want_dz = ref.token_ce(z[rows], lab[rows])
+    assert abs(float(loss.item()) - want_loss) <= (1e-5 if dtype == "f32" else 1e-3) * max(1.0, abs(want_loss))
+    got = host(dz)
+    if n:
+        assert mar(got[rows], want_dz) <= TOL[dtype]
+    others = np.setdiff1d(np.arange(T), rows)
+    assert np.all(got[others] == 7.0)
+
+
+def test_adamw_step_matches_oracle(rng):
+    ops = _ops()
+    shapes = [(16, 520), (1400, 16), (1, 7), (33, 1)]
+    ps = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+    P = [to_dev(p, "f32") for p in ps]
+    M = [torch.zeros_like(p) for p in P]
+    Vv = [torch.zeros_like(p) for p in P]
+    outs = [torch.empty(s[0], s[1] + 3, dtype=torch.bfloat16, device=DEV)[:, :s[1]] for s in shapes]
+    ref_p, ref_m, ref_v = [p.astype(np.float64) for p in ps], [0.0] * 4, [0.0] * 4
+    for step in range(1, 4):
+        gs = [rng.standard_normal(s).astype(np.float32) for s in shapes]
+        G = [to_dev(g, "f32") for g in gs]
+        ops.adamw_step([(P[i], G[i], M[i], Vv[i], outs[i]) for i in range(4)], 1e-2, step, 0.9, 0.999,
+                       1e-8, 0.05)
+        for i in range(4):
+            ref_p[i], ref_m[i], ref_v[i] = ref.adamw(ref_p[i], gs[i].astype(np.float64), ref_m[i], ref_v[i],
+                                                     step, 1e-2, 0.9, 0.999, 1e-8, 0.05)
+    torch.cuda.synchronize()
+    for i in range(4):
+        assert mar(host(P[i]), ref_p[i]) <= 1e-5
+        assert np.array_equal(host(outs[i]), ref.round_to(host(P[i]), "bf16").astype(np.float32))
+
+
+def _train(cfg, steps, n_dense, V, lr, seed=11):
+    from contextual_sparsity_lora_amd.ffn import SparseFFN
+    from contextual_sparsity_lora_amd.train import LoRATrainer
+    inp = make_ffn_inputs(cfg)
+    rng = np.random.default_rng(seed)
+    dt = cfg.dtype
+    W_head = round_dtype(rng.standard_normal((V, cfg.hidden)) * 0.05, dt)
+    xs = [round_dtype(rng.standard_normal((cfg.tokens, cfg.hidden)), dt) for _ in range(steps)]
+    labels = [rng.integers(0, V, size=cfg.tokens).astype(np.int32) for _ in range(steps)]
+    d = {k: to_dev(v, dt) for k, v in inp.items()
+         if k in ("W_gate", "W_up", "W_down", "A_gate", "B_gate", "A_up", "B_up", "A_down", "B_down")}
+    blk = SparseFFN(d["W_gate"], d["W_up"], d["W_down"], d["A_gate"], d["B_gate"], d["A_up"], d["B_up"],
+                    d["A_down"], d["B_down"], to_dev(np.ascontiguousarray(inp["WA_t_gu"].T), "f32"),
+                    to_dev(inp["WB_gate"], "f32"), to_dev(inp["WB_up"], "f32"), inp["scale"],
+                    sparsity=cfg.ffn_sparsity)
+    # eps well above the gradients' rounding noise: near-zero gradient entries
+    # then move the masters smoothly instead of by +-lr (Adam's first steps
+    # are sign-like when eps is negligible)
+    tr = LoRATrainer(blk, to_dev(W_head, dt), total_steps=steps, dense_frac=n_dense / steps, lr=lr,
+                     eps=1e-3, weight_decay=0.01)
+    assert tr.n_dense == n_dense
+    roles = to_dev(inp["roles"], None)
+    losses, sels = [], []
+    for t in range(steps):
+        loss = tr.step(to_dev(xs[t], dt), to_dev(labels[t], None), roles, cfg.ctx_tokens)
+        losses.append(float(loss.item()))
+        sels.append(None if blk.dense else host_i(blk.idx).copy())
+    torch.cuda.synchronize()
+    return inp, W_head, xs, labels, tr, losses, sels
+
+
+@pytest.mark.parametrize("case", ["f32", "bf16"])
+def test_training_steps_with_schedule(case):
+    """4 steps, the first dense: the selection of every sparse step is the
+    oracle's (bit-exact), losses and the final masters within tolerance."""
+    need_lib()
+    if case == "f32":
+        cfg, V, lr = CONFIGS[1], 97, 1e-2
+    else:
+        cfg, V, lr = scaled(CONFIGS[2], batch=2, seq=160, out_per_seq=40, hidden=520, inter=1400), 1000, 1e-2
+    print(f"[train] {case}", flush=True)
+    steps, n_dense = 4, 1
+    inp, W_head, xs, labels, tr, losses, sels = _train(cfg, steps, n_dense, V, lr)
+    ctx, _ = ref.token_lists(inp["roles"])
+    n = ref.n_keep(cfg.inter, *cfg.ffn_sparsity)
+
+    def select(x):
+        return csa.select_ffn(x, ctx, inp["WA_t_gu"], inp["WB_gate"], inp["WB_up"], n)
+
+    for t in range(n_dense, steps):
+        assert np.array_equal(sels[t], select(xs[t])), t
+    want_losses, master = ref.ffn_train(inp, W_head, xs, labels, total=steps, n_dense=n_dense, select=select,
+                                        dtype=cfg.dtype, lr=lr, eps=1e-3, wd=0.01)
+    tol = TOL[cfg.dtype]
+    assert np.allclose(losses, want_losses, rtol=tol, atol=0.0), (losses, want_losses)
+    got = tr.masters()
+    for k in ref.LORA_FFN:
+        # the updates themselves (master - initial), not only the masters
+        init = inp[k].astype(np.float64)
+        assert mar(host(got[k]) - init, master[k] - init) <= max(tol, 1e-3), k
