@@ -34,6 +34,8 @@ def parse():
     ap.add_argument("--no-schedule", action="store_true",
                     help="skip the whole-training-step run with the dense-then-sparse schedule")
     ap.add_argument("--schedule-steps", type=int, default=20)
+    ap.add_argument("--no-factors", action="store_true",
+                    help="skip timing the on-GPU estimator factor preparation")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -302,6 +304,28 @@ def main():
         "cpu_baseline": None,
     }
     out.update(extra)
+    if not args.no_factors:
+        # the offline step: rank-16 factors of gate and up (randomized subspace
+        # iteration, 3 power steps, 16 extra columns) from the bf16 weights
+        import numpy as np
+        F, D, k = cfg.inter, cfg.hidden, cfg.est_rank
+        W = torch.from_numpy(np.concatenate([inp["W_gate"], inp["W_up"]])).to(torch.bfloat16).to("cuda:0")
+        Wt = torch.empty(D, 2 * F, dtype=torch.bfloat16, device="cuda:0")
+        ops.transpose(W, Wt)
+        WA_t = torch.empty(k, D, dtype=torch.float32, device="cuda:0")
+        WB = torch.empty(k, F, dtype=torch.float32, device="cuda:0")
+        ops.svd_factors(W[:F], Wt[:, :F], k, WA_t, WB)          # warm-up
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for half in range(2):
+            ops.svd_factors(W[half * F:(half + 1) * F], Wt[:, half * F:(half + 1) * F], k, WA_t, WB, seed=half)
+        e1.record()
+        torch.cuda.synchronize()
+        extra["factor_prep_ms_per_matrix"] = round(e0.elapsed_time(e1) / 2, 3)
+        print(f"[bench] factor preparation {extra['factor_prep_ms_per_matrix']} ms per {F}x{D} matrix",
+              file=sys.stderr, flush=True)
+        del W, Wt
     if not args.no_schedule:
         extra["training_schedule"] = training_schedule(inp, cfg, ops, args.schedule_steps)
         print(f"[bench] training schedule: {extra['training_schedule']}", file=sys.stderr, flush=True)

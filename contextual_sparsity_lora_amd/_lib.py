@@ -57,6 +57,8 @@ SIGNATURES = {
     "sl_swiglu_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),
     "sl_swiglu_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
                             _vp, _i64]),
+    "sl_svd_factors": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_uint64,
+                             _vp, _vp]),
     "sl_token_ce": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f, _vp, _i64, _vp]),
     "sl_adamw_step": (_st, [_vp, _vp, _int, _f, _f, _f, _f, _f, _i64]),
     "sl_dot_stats": (_st, [_vp, _vp, _vp, _i64, _vp]),

@@ -1023,6 +1023,23 @@ sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi, i
                      "transpose");
 }
 
+sl_status sl_svd_factors(sl_handle* h, sl_dtype dt, const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
+                         int64_t D_out, int64_t D_in, int64_t k, int64_t oversample, int64_t iters,
+                         uint64_t seed, float* WA_t, float* WB) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    SL_REQUIRE(h, D_out >= 1 && D_in >= 1 && k >= 1 && oversample >= 0 && iters >= 0 && iters <= 16,
+               "bad sizes");
+    const int64_t p = k + oversample;
+    SL_REQUIRE(h, p <= 64 && p <= D_in && p <= D_out, "k + oversample must be <= 64 and <= min(D_in, D_out)");
+    SL_REQUIRE(h, W && Wt && WA_t && WB, "NULL pointer");
+    SL_REQUIRE(h, ldw >= D_in && ldwt >= D_out, "bad leading dimension");
+    DeviceGuard g(h->device);
+    SL_CHECK(ensure_ws(h, svd_factors_ws_bytes(D_out, D_in, (int)p)));
+    return hip_check(h, launch_svd_factors(dt == SL_BF16, W, ldw, Wt, ldwt, D_out, D_in, (int)k, (int)p, (int)iters,
+                                           seed, WA_t, WB, h->ws, h->stream), "svd_factors");
+}
+
 sl_status sl_dot_stats(sl_handle* h, const float* a, const float* b, int64_t n, double* out) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, n >= 0, "bad size");

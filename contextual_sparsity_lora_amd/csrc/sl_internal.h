@@ -180,6 +180,11 @@ hipError_t launch_adamw(const AdamwArgs& a, int64_t blocks, hipStream_t st);
 hipError_t launch_ce_rows(bool bf16, const void* L, int64_t ldl, const int32_t* rows, int64_t nrows,
                           const int32_t* labels, int64_t V, float scale, void* dL, int64_t lddl,
                           float* loss_rows, double* loss_sum, hipStream_t st);
+// rank-k factors by randomized subspace iteration (p = k + oversample <= 64)
+size_t svd_factors_ws_bytes(int64_t D_out, int64_t D_in, int p);
+hipError_t launch_svd_factors(bool bf16, const void* W, int64_t ldw, const void* Wt, int64_t ldwt, int64_t D_out,
+                              int64_t D_in, int k, int p, int iters, uint64_t seed, float* WA_t, float* WB,
+                              void* ws, hipStream_t st);
 hipError_t launch_dot_stats(const float* a, const float* b, int64_t n, double* part, double* out,
                             hipStream_t st);
 hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows, int64_t cols,

@@ -341,6 +341,17 @@ def swiglu_bwd(dh, g, u, dg, du):
     _check(h, st, "sl_swiglu_bwd")
 
 
+def svd_factors(W, Wt, k, WA_t, WB, oversample=16, iters=3, seed=0):
+    """Rank-k estimator factors of W [D_out, D_in] (with its transposed copy Wt)
+    into WA_t fp32 [k, D_in] and WB fp32 [k, D_out]."""
+    h = handle(_dev(W))
+    D_out, D_in = W.shape
+    st = _lib.load().sl_svd_factors(h, _dt(W), _ptr(W), _ld(W), _ptr(Wt), _ld(Wt), D_out, D_in, int(k),
+                                    int(oversample), int(iters), ctypes.c_uint64(int(seed) & ((1 << 64) - 1)),
+                                    _ptr(WA_t), _ptr(WB))
+    _check(h, st, "sl_svd_factors")
+
+
 def token_ce(logits, rows, labels, dlogits, loss, scale=None):
     """Softmax cross-entropy of logits [T, V] on the listed rows against
     labels[row]; dlogits = scale (softmax - onehot) on those rows; loss (fp64

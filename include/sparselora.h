@@ -382,6 +382,29 @@ sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ld
                                   int64_t ld_lora_B, int64_t lora_r, float lora_scale,
                                   const int32_t* idx, int64_t n);
 
+/* ---------------------------------------------------------------- estimator factors */
+
+/* Rank-k estimator factors of a frozen weight, computed on the GPU (the
+ * offline step of paper-graph summary §3.4 "SVD Sparsity Estimator": W_A =
+ * U_k sqrt(S_k), W_B = sqrt(S_k) V_k^T from the truncated SVD of W = W_lin^T
+ * [D_in, D_out]).  Randomized subspace iteration (Halko, Martinsson and
+ * Tropp, 2011): Omega [D_out, p] standard normal from a counter-based
+ * generator (SplitMix64 uniforms, Box-Muller) seeded by `seed`, p = k +
+ * oversample; Q = orth(W Omega); `iters` power steps Z = orth(W^T Q), Q =
+ * orth(W Z) (orth = CholeskyQR2); then the SVD of Q^T W through the
+ * eigen-decomposition of its Gram matrix (Jacobi, fp64).  Each singular pair
+ * is signed so that the largest-magnitude entry of its left vector is
+ * positive.  The result approaches the truncated SVD as iters grows (exactly
+ * on a planted spectrum with a gap at k).
+ *   W  device (dt) [D_out, ldw >= D_in] (nn.Linear layout); Wt its transposed
+ *      copy [D_in, ldwt >= D_out]
+ *   WA_t device fp32 [k, D_in] out (W_A transposed: the layout sl_svd_estimate
+ *      reads after a transpose to [D_in, k]); WB device fp32 [k, D_out] out
+ * 1 <= k, k + oversample <= 64 and <= min(D_in, D_out); iters <= 16. */
+sl_status sl_svd_factors(sl_handle* h, sl_dtype dt, const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
+                         int64_t D_out, int64_t D_in, int64_t k, int64_t oversample, int64_t iters,
+                         uint64_t seed, float* WA_t, float* WB);
+
 /* ---------------------------------------------------------------- training step */
 
 /* Token loss on the listed rows (paper-graph summary, "Putting It All

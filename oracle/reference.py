@@ -500,3 +500,19 @@ def ffn_train(inp, W_head, xs, labels, total, n_dense, select, dtype, lr, warmup
                                               eps, wd)
         losses.append(loss)
     return losses, master
+
+
+def svd_factors(W_lin, k):
+    """Rank-k estimator factors of a weight in nn.Linear layout [D_out, D_in]
+    (paper-graph summary §3.4 "SVD Sparsity Estimator": with W = W_lin^T =
+    U diag(s) V^T, W_A = U_k diag(sqrt(s_k)), W_B = diag(sqrt(s_k)) V_k^T, so
+    x W ~ (x W_A) W_B).  Each singular pair is signed so that the
+    largest-magnitude entry of its left vector is positive (the first such
+    entry on ties).  Returns (W_A^T [k, D_in], W_B [k, D_out]) in float64."""
+    W = np.asarray(W_lin, f64).T
+    U, s, Vt = np.linalg.svd(W, full_matrices=False)
+    U, s, V = U[:, :k], s[:k], Vt[:k].T
+    sign = np.sign(U[np.argmax(np.abs(U), axis=0), np.arange(k)])
+    sign[sign == 0] = 1.0
+    rs = np.sqrt(s)
+    return (U * sign * rs).T, (rs[:, None] * (V * sign).T)

@@ -1,0 +1,78 @@
+"""GPU estimator factors (randomized subspace iteration) against the oracle's
+truncated SVD: a planted spectrum with a gap is recovered entry by entry, a
+flat Gaussian spectrum is approximated within a few percent of the optimal
+rank-k error, and the estimator driven by the GPU factors selects exactly
+what the oracle selects with those factors."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import csa, reference as ref
+from tests.gpu_util import DEV, host, host_i, need_lib, to_dev
+from workloads.gen import round_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _factors(W_lin, dtype, k, iters=3, oversample=16, seed=1):
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    D_out, D_in = W_lin.shape
+    W = to_dev(W_lin, dtype)
+    Wt = to_dev(np.ascontiguousarray(W_lin.T), dtype)
+    WA_t = torch.empty(k, D_in, dtype=torch.float32, device=DEV)
+    WB = torch.empty(k, D_out, dtype=torch.float32, device=DEV)
+    ops.svd_factors(W, Wt, k, WA_t, WB, oversample=oversample, iters=iters, seed=seed)
+    torch.cuda.synchronize()
+    return host(WA_t), host(WB)
+
+
+@pytest.mark.parametrize("dtype,D_out,D_in", [("f32", 700, 256), ("bf16", 1400, 520), ("bf16", 520, 1400)])
+def test_planted_spectrum(dtype, D_out, D_in, rng):
+    k, n = 16, 48
+    print(f"[factors] planted {dtype} {D_out}x{D_in}", flush=True)
+    U0, _ = np.linalg.qr(rng.standard_normal((D_in, n)))
+    V0, _ = np.linalg.qr(rng.standard_normal((D_out, n)))
+    s0 = 0.7 ** np.arange(n)
+    W_lin = round_dtype(((U0 * s0) @ V0.T).T, dtype)
+    WA_t, WB = _factors(W_lin, dtype, k)
+    want_A, want_B = ref.svd_factors(W_lin, k)     # exact SVD of the (rounded) weight
+    assert np.max(np.abs(WA_t - want_A)) <= 2e-4 * np.max(np.abs(want_A))
+    assert np.max(np.abs(WB - want_B)) <= 2e-4 * np.max(np.abs(want_B))
+
+
+def test_gaussian_weight_near_optimal(rng):
+    D_out, D_in, k = 1400, 520, 16
+    print("[factors] gaussian", flush=True)
+    W_lin = round_dtype(rng.standard_normal((D_out, D_in)) * 0.02, "bf16")
+    WA_t, WB = _factors(W_lin, "bf16", k, iters=3)
+    W = W_lin.T.astype(np.float64)
+    A, B = ref.svd_factors(W_lin, k)
+    best = np.linalg.norm(W - A.T @ B)
+    got = np.linalg.norm(W - WA_t.T.astype(np.float64) @ WB.astype(np.float64))
+    assert best <= got <= 1.01 * best, (got / best)
+    # the factors keep their convention: the left vectors' largest entries are positive
+    for row in WA_t:
+        assert row[np.argmax(np.abs(row))] > 0
+
+
+def test_estimator_with_gpu_factors_selects_like_the_oracle(rng):
+    """FFN estimator on GPU-made factors: the selection equals the oracle's
+    selection from the same factor values (bit for bit)."""
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    T_c, D, F, k, n = 300, 520, 1400, 16, 420
+    Wg = round_dtype(rng.standard_normal((F, D)) * 0.02, "bf16")
+    Wu = round_dtype(rng.standard_normal((F, D)) * 0.02, "bf16")
+    Ag, Bg = _factors(Wg, "bf16", k)
+    Au, Bu = _factors(Wu, "bf16", k)
+    x = round_dtype(rng.standard_normal((T_c + 40, D)), "bf16")
+    ctx = np.sort(rng.choice(T_c + 40, T_c, replace=False)).astype(np.int32)
+    WA_t = np.concatenate([Ag, Au])                  # [2k, D]
+    xa = torch.empty(T_c, 2 * k, dtype=torch.float32, device=DEV)
+    ops.svd_estimate(to_dev(x, "bf16"), to_dev(ctx, None), to_dev(np.ascontiguousarray(WA_t.T), "f32"), xa)
+    idx = torch.empty(n, dtype=torch.int32, device=DEV)
+    ops.score_select("swiglu", xa, to_dev(Bg, "f32"), to_dev(Bu, "f32"), n, idx, off0=0, off1=k)
+    torch.cuda.synchronize()
+    want = csa.select_ffn(x, ctx, WA_t, Bg, Bu, n)
+    assert np.array_equal(host_i(idx), want)
