@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--schedule-steps", type=int, default=20)
     ap.add_argument("--no-factors", action="store_true",
                     help="skip timing the on-GPU estimator factor preparation")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the sparse/dense step times of the other workloads (projections, "
+                         "layer, 32-layer stack, fp32 block)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -169,6 +172,114 @@ def training_schedule(inp, cfg, ops, steps, dense_frac=0.1, vocab=32000):
             "scheduled_total_ms": round(sum(sched), 3), "dense_total_ms": round(sum(dense), 3),
             "sparse_phase_speedup": round(s, 4), "overall_speedup": round(sum(dense) / sum(sched), 4),
             "bound": round(1.0 / (dense_frac + (1.0 - dense_frac) / s), 4)}
+
+
+def _rand_layer_arrays(cfg, gen, dev):
+    """Device weights of one decoder layer, N(0, 0.02^2) in bf16, and fp32
+    estimator factors N(0, 1/rows), drawn from a seeded torch generator (step
+    times do not depend on the values; parity tests use the oracle's inputs)."""
+    import torch
+    D, F, r, k = cfg.hidden, cfg.inter, cfg.lora_rank, cfg.est_rank
+    Cq, Ckv = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    w = lambda *sh: (torch.randn(*sh, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    f = lambda *sh: torch.randn(*sh, generator=gen, device=dev) / sh[0] ** 0.5
+    d = {"W_q": w(Cq, D), "W_k": w(Ckv, D), "W_v": w(Ckv, D), "W_o": w(D, Cq)}
+    for p, co, ci in (("q", Cq, D), ("k", Ckv, D), ("v", Ckv, D), ("o", D, Cq)):
+        d["A_" + p], d["B_" + p] = w(r, ci), w(co, r)
+    if F:
+        d.update({"W_gate": w(F, D), "W_up": w(F, D), "W_down": w(D, F)})
+        for p, co, ci in (("gate", F, D), ("up", F, D), ("down", D, F)):
+            d["A_" + p], d["B_" + p] = w(r, ci), w(co, r)
+    f32 = {"WA_qkv": f(D, 3 * k), "WB_q": f(k, Cq), "WB_k": f(k, Ckv), "WB_v": f(k, Ckv)}
+    if F:
+        f32.update({"WA_gu": f(D, 2 * k), "WB_gate": f(k, F), "WB_up": f(k, F)})
+    return d, f32
+
+
+def other_configs(steps=3):
+    """fwd+bwd step times, sparse and dense (every channel kept, same LoRA), of
+    the other workloads: the fp32 FFN block (config 1), the LLaMA3-8B q/k/v/o
+    projections (config 3), one LLaMA2-13B decoder layer (config 4) and the
+    32-layer LLaMA3-8B stack with its per-layer sparsity ramp (config 5)."""
+    import torch
+    from contextual_sparsity_lora_amd.attn import SparseAttnProj
+    from contextual_sparsity_lora_amd.layer import SparseDecoderLayer
+    from contextual_sparsity_lora_amd.stack import SparseStack
+    from workloads.configs import CONFIGS
+    from workloads.gen import make_ffn_inputs, roles_for
+    dev = "cuda:0"
+
+    def timed(step, n):
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    out = {}
+    # config 1: the fp32 FFN block
+    cfg = CONFIGS[1]
+    inp = make_ffn_inputs(cfg)
+    ms = {}
+    for dense in (False, True):
+        import numpy as np
+        from contextual_sparsity_lora_amd.ffn import SparseFFN
+        t = {k: torch.from_numpy(v).to(dev) for k, v in inp.items() if isinstance(v, np.ndarray)
+             and k.startswith(("x", "W_", "A_", "B_", "dy"))}
+        blk = SparseFFN(t["W_gate"], t["W_up"], t["W_down"], t["A_gate"], t["B_gate"], t["A_up"], t["B_up"],
+                        t["A_down"], t["B_down"], torch.from_numpy(np.ascontiguousarray(inp["WA_t_gu"].T)).to(dev),
+                        t["WB_gate"] if "WB_gate" in t else torch.from_numpy(inp["WB_gate"]).to(dev),
+                        torch.from_numpy(inp["WB_up"]).to(dev), inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense)
+        roles = torch.from_numpy(inp["roles"]).to(dev)
+        ms[dense] = timed(lambda: (blk.forward(t["x"], roles, cfg.ctx_tokens), blk.backward(t["dy"])), 20)
+    out["1"] = {"workload": cfg.name, "tokens": cfg.tokens, "sparse_ms": round(ms[False], 4),
+                "dense_ms": round(ms[True], 4), "speedup": round(ms[True] / ms[False], 3)}
+    gen = torch.Generator(device=dev)
+    for cid in (3, 4, 5):
+        cfg = CONFIGS[cid]
+        roles = torch.from_numpy(roles_for(cfg)).to(dev)
+        T, D = cfg.tokens, cfg.hidden
+        ms = {}
+        for dense in (False, True):
+            gen.manual_seed(cfg.seed)
+            x = (torch.randn(T, D, generator=gen, device=dev)).to(torch.bfloat16)
+            dy = torch.randn(T, D, generator=gen, device=dev).to(torch.bfloat16)
+            if cid == 3:
+                d, f32 = _rand_layer_arrays(cfg, gen, dev)
+                blk = SparseAttnProj(d["W_q"], d["W_k"], d["W_v"], d["W_o"], d["A_q"], d["B_q"], d["A_k"], d["B_k"],
+                                     d["A_v"], d["B_v"], d["A_o"], d["B_o"], f32["WA_qkv"], f32["WB_q"], f32["WB_k"],
+                                     f32["WB_v"], cfg.lora_scale, cfg.n_kv_heads, cfg.head_dim,
+                                     qk_sparsity=cfg.qk_sparsity, vo_sparsity=cfg.vo_sparsity, dense=dense)
+                Cs = blk.Cs
+                xo = torch.randn(T, blk.Cq, generator=gen, device=dev).to(torch.bfloat16)
+                dqkv = torch.randn(T, Cs, generator=gen, device=dev).to(torch.bfloat16)
+                step = lambda: (blk.forward(x, xo, roles, cfg.ctx_tokens), blk.backward(dqkv, dy[:, :D]))
+            elif cid == 4:
+                d, f32 = _rand_layer_arrays(cfg, gen, dev)
+                blk = SparseDecoderLayer.from_arrays(d, f32, cfg, cfg.qk_sparsity, cfg.vo_sparsity,
+                                                     cfg.ffn_sparsity, dense=dense)
+                step = lambda: (blk.forward(x, roles, cfg.ctx_tokens), blk.backward(dy))
+            else:
+                arrays, sps = [], []
+                for layer in range(cfg.n_layers):
+                    arrays.append(_rand_layer_arrays(cfg, gen, dev))
+                    sps.append((0, 1) if dense else cfg.layer_sparsity(layer))
+                blk = SparseStack.build(cfg, arrays, sps)
+                del arrays
+                step = lambda: (blk.forward(x, roles, cfg.ctx_tokens), blk.backward(dy))
+            ms[dense] = timed(step, steps)
+            del blk, step
+            torch.cuda.empty_cache()
+        out[str(cid)] = {"workload": cfg.name, "tokens": T, "sparse_ms": round(ms[False], 3),
+                         "dense_ms": round(ms[True], 3), "speedup": round(ms[True] / ms[False], 3),
+                         "sparse_tokens_per_s": round(T / (ms[False] * 1e-3), 1)}
+        print(f"[bench] config {cid} ({cfg.name}): sparse {ms[False]:.3f} ms, dense {ms[True]:.3f} ms",
+              file=sys.stderr, flush=True)
+    return out
 
 
 def cpu_baseline(inp, cfg):
@@ -326,6 +437,8 @@ def main():
         print(f"[bench] factor preparation {extra['factor_prep_ms_per_matrix']} ms per {F}x{D} matrix",
               file=sys.stderr, flush=True)
         del W, Wt
+    if not args.no_configs:
+        extra["other_configs"] = other_configs()
     if not args.no_schedule:
         extra["training_schedule"] = training_schedule(inp, cfg, ops, args.schedule_steps)
         print(f"[bench] training schedule: {extra['training_schedule']}", file=sys.stderr, flush=True)

@@ -78,6 +78,11 @@ class SparseAttnProj:
         self.WA = cont(WA_qkv)                         # [D, 3k] fp32
         self.WB_q, self.WB_k, self.WB_v = (cont(w) for w in (WB_q, WB_k, WB_v))
         assert dense or criterion in ("oracle", "random") or self.k > 0, "the estimator factors are required"
+        # a second stream (default priority): the q|k|v product of the output
+        # rows and the LoRA down-projection overlap the selection; the LoRA
+        # reductions nothing later reads overlap the backward products
+        self.side = torch.cuda.Stream(device=dev)
+        self._ev = [torch.cuda.Event() for _ in range(6)]
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):
@@ -111,13 +116,15 @@ class SparseAttnProj:
         self.gB_qkv, self.gB_o = e(T, 3 * r, dtype=f32), e(T, r, dtype=f32)
         self._T = (T, T_c, T_o)
 
-    def select(self):
+    def select(self, estimated=False):
         """QK and VO selections from the estimator on the context tokens, their
-        GQA expansions and the stacked q|k|v channel list."""
+        GQA expansions and the stacked q|k|v channel list (estimated: xa is
+        already computed)."""
         k, Ckv, Cq = self.k, self.Ckv, self.Cq
         crit = self.criterion
         if crit in ("svd", "head"):
-            ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
+            if not estimated:
+                ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
             ops.score_select("qk", self.xa, self.WB_q, self.WB_k, 0 if crit == "head" else self.n_qk,
                              self.idx_qk, scores=self.scores, off0=0, off1=k, C=Ckv, n_rep=self.n_rep,
                              head_dim=self.d)
@@ -157,12 +164,31 @@ class SparseAttnProj:
         r = self.r
         self._alloc(T, T_c, T - T_c, x.device)
         self.x = x
+        main, ev = torch.cuda.current_stream(x.device), self._ev
         ops.token_split(roles, self.ctx_rows, self.out_rows)
+        # side stream: x A^T, then (unless the selection itself writes qkv) the
+        # q|k|v product of the output rows, which does not read the selection
+        overlap = not self.dense and self.criterion != "oracle"
+        lora = (self.xl_qkv, self.B_bd, 3 * r, self.scale)
+        ev[0].record(main)
+        if not self.dense and self.criterion in ("svd", "head"):
+            # the estimator's first product goes first, so the GPU has work
+            # while the host issues the side-stream calls
+            ops.svd_estimate(self.x, self.ctx_rows, self.WA, self.xa)
+        self.side.wait_event(ev[0])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
+            ev[1].record(self.side)
+            if overlap:
+                ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
+                                      self.qkv, lora=lora, flags=ops.ONLY_OUT_ROWS)
+            ev[2].record(self.side)
         if not self.dense:
-            self.select()
-        ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
+            self.select(estimated=True)
+        main.wait_event(ev[1])
         ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
-                              self.qkv, lora=(self.xl_qkv, self.B_bd, 3 * r, self.scale))
+                              self.qkv, lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
+        main.wait_event(ev[2])
         return self.qkv
 
     def forward_o(self, x_o):
@@ -183,26 +209,45 @@ class SparseAttnProj:
         """o: LoRA gB, dA, dB; then dx_o (input side: kept channels only) with
         the LoRA term fused."""
         r, s = self.r, self.scale
-        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA | ops.LORA_DB, self.x_o, None, self.B_o, s,
-                         self.xl_o, dy=dy_o, dA=self.dA_o, dB=self.dB_o, gB=self.gB_o, D_in=self.Cq)
+        main, ev = torch.cuda.current_stream(dy_o.device), self._ev
+        # gB on the main stream (the dx_o product reads it); dA, dB on the side stream
+        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_o, s, None, dy=dy_o, gB=self.gB_o, D_in=self.Cq)
+        ev[3].record(main)
         ops.transpose(self.A_o, self.A_oT)
         ops.sparse_linear_bwd("in", dy_o, None, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
                               self.dx_o, lora=(self.gB_o, self.A_oT, r, s))
+        # (issued after the main-stream product, so the host's time on these
+        # calls overlaps that product instead of delaying it)
+        self.side.wait_event(ev[3])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.x_o, None, None, s, self.xl_o, dy=dy_o,
+                             dA=self.dA_o, dB=self.dB_o, gB=self.gB_o, D_in=self.Cq, r=r)
         return self.dx_o
 
     def backward_qkv(self, dqkv):
         """dqkv [T, Cq + 2 Ckv]: gradients of q | k | v.  gB and dA through the
         block-diagonal B, dB per projection, then dx with the LoRA term fused."""
         Cq, Ckv, r, s = self.Cq, self.Ckv, self.r, self.scale
-        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_DA, self.x, None, self.B_bd, s, None, dy=dqkv,
-                         dA=self.dA_qkv, gB=self.gB_qkv, D_in=self.D)
-        parts = ((self.dB_q, 0, Cq), (self.dB_k, Cq, Cq + Ckv), (self.dB_v, Cq + Ckv, self.Cs))
-        for i, (dB, c0, c1) in enumerate(parts):
-            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_qkv[:, i * r:(i + 1) * r],
-                             dy=dqkv[:, c0:c1], dB=dB, r=r, D_in=self.D)
+        main, ev = torch.cuda.current_stream(dqkv.device), self._ev
+        # gB through the block-diagonal B on the main stream; dA and the
+        # per-projection dB on the side stream, next to the dx product
+        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_bd, s, None, dy=dqkv, gB=self.gB_qkv,
+                         D_in=self.D, r=3 * r)
+        ev[4].record(main)
         ops.transpose(self.A_qkv, self.A_qkvT)
         ops.sparse_linear_bwd("out", dqkv, self.W_qkv, self.W_qkvT, self.ctx_rows, self.out_rows,
                               self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s))
+        self.side.wait_event(ev[4])
+        with torch.cuda.stream(self.side):
+            ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=dqkv, dA=self.dA_qkv,
+                             gB=self.gB_qkv, D_in=self.D, r=3 * r)
+            parts = ((self.dB_q, 0, Cq), (self.dB_k, Cq, Cq + Ckv), (self.dB_v, Cq + Ckv, self.Cs))
+            for i, (dB, c0, c1) in enumerate(parts):
+                ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_qkv[:, i * r:(i + 1) * r],
+                                 dy=dqkv[:, c0:c1], dB=dB, r=r, D_in=self.D)
+            ev[5].record(self.side)
+        # the projections' gradients are complete when both streams are
+        main.wait_event(ev[5])
         return self.dx
 
     def backward(self, dqkv, dy_o):

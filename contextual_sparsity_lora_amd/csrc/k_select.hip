@@ -162,12 +162,13 @@ __global__ __launch_bounds__(1024) void token_split_kernel(const uint8_t* __rest
 }
 
 // ---------------------------------------------------------------- stage 1
-// Stage 1, second form: a block of 4 waves takes S1T context tokens and 32
-// columns of W_A (8 per wave); lane l owns chain l of every (token, column)
-// pair it holds (S1T x 8 = 64 pairs).  The 64 chains of each pair then go
-// through LDS (pair-major rows, pitch 68 floats) and lane p folds pair p with
-// the pairwise tree.
-constexpr int S1T = 8, S1J = 8;
+// Stage 1, second form: a block of 4 waves takes S1T context tokens and
+// 4 S1J columns of W_A (S1J per wave); lane l owns chain l of every (token,
+// column) pair it holds (S1T x S1J = 64 pairs).  The 64 chains of each pair
+// then go through LDS (pair-major rows, pitch 68 floats) and lane p folds pair
+// p with the pairwise tree.  16 tokens per block keep the W_A rows a block
+// streams (D x 16 floats) shared by 16 tokens.
+constexpr int S1T = 16, S1J = 4;
 
 template <bool BF16>
 __global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ xv, int64_t ldx,
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ x
     __shared__ __attribute__((aligned(16))) float red[4][S1T * S1J][68];
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
     const int64_t m0 = (int64_t)blockIdx.x * S1T;
-    const int64_t j0 = (int64_t)blockIdx.y * 32 + w * S1J;
+    const int64_t j0 = (int64_t)blockIdx.y * (4 * S1J) + w * S1J;
     // rows past Tc read a valid row (the last one) and are zeroed after the load,
     // so every load is unconditional and the loads of an iteration overlap
     int64_t rowoff[S1T];
@@ -205,9 +206,11 @@ __global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ x
         float wv[S1J];
         const float* wr = WA + i * kt + j0;
         if (wvec) {
-            const float4 a = *(const float4*)wr, b = *(const float4*)(wr + 4);
-            wv[0] = a.x; wv[1] = a.y; wv[2] = a.z; wv[3] = a.w;
-            wv[4] = b.x; wv[5] = b.y; wv[6] = b.z; wv[7] = b.w;
+#pragma unroll
+            for (int q = 0; q < S1J; q += 4) {
+                const float4 a = *(const float4*)(wr + q);
+                wv[q] = a.x; wv[q + 1] = a.y; wv[q + 2] = a.z; wv[q + 3] = a.w;
+            }
         } else {
 #pragma unroll
             for (int j = 0; j < S1J; ++j) {
@@ -315,6 +318,48 @@ __global__ __launch_bounds__(1024) void ssq16_kernel(const float* __restrict__ x
             for (int l = 0; l < s2; ++l) v[l] = v[l] + v[l + s2];
         if (c < C) ssq[c] = v[0];
     }
+}
+
+// Stage 2 + criterion for few channels (k = 16): the 64 token chains of a
+// channel are spread over 16 blocks (4 waves, one chain per wave), so a
+// launch over C channels has 16 ceil(C / 64) blocks instead of ceil(C / 64).
+// Chain l = 4 blockIdx.y + w takes tokens m = l, l + 64, ... in order with the
+// same fused chain and criterion as ssq16_kernel; its sum goes to part[l, c]
+// and r64_tree_kernel applies the pairwise tree (the same result bit for bit).
+template <int CRIT>
+__global__ __launch_bounds__(256) void ssq16_chain_kernel(const float* __restrict__ xa, int64_t ld,
+                                                          int64_t Tc, int64_t off0,
+                                                          const float* __restrict__ WB0, int64_t off1,
+                                                          const float* __restrict__ WB1, int64_t C,
+                                                          float* __restrict__ part) {
+    constexpr int K = 16;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = (int)blockIdx.y * 4 + w;
+    const int64_t c = (int64_t)blockIdx.x * WAVE + lane;
+    const int64_t cc = c < C ? c : C - 1;
+    float wg[K], wu[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        wg[j] = WB0[(int64_t)j * C + cc];
+        wu[j] = CRIT == 1 ? WB1[(int64_t)j * C + cc] : 0.0f;
+    }
+    float p = 0.0f;
+    for (int64_t m = l; m < Tc; m += 64) {
+        const float* row = xa + m * ld;
+        float g = 0.0f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) g = __builtin_fmaf(row[off0 + j], wg[j], g);
+        float v = g;
+        if (CRIT == 1) {
+            float u = 0.0f;
+#pragma unroll
+            for (int j = 0; j < K; ++j) u = __builtin_fmaf(row[off1 + j], wu[j], u);
+            v = silu_sl_nb(g) * u;
+        }
+        p = __builtin_fmaf(v, v, p);
+    }
+    if (c < C) part[(int64_t)l * C + c] = p;
 }
 
 // ---------------------------------------------------------------- stage 2 + criterion
@@ -666,7 +711,7 @@ hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int
 hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* rows, int64_t Tc,
                          int64_t D, const float* WA, int64_t kt, float* xa, hipStream_t st) {
     if (Tc <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(Tc, S1T), (unsigned)ceil_div(kt, 32));
+    const dim3 grid((unsigned)ceil_div(Tc, S1T), (unsigned)ceil_div(kt, 4 * S1J));
     if (bf16)
         hipLaunchKernelGGL(stage1b_kernel<true>, grid, dim3(256), 0, st, x, ldx, rows, Tc, D, WA, kt, xa);
     else
@@ -676,8 +721,17 @@ hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* r
 
 hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t off0,
                       const float* WB0, int64_t off1, const float* WB1, int64_t k, int64_t C,
-                      float* ssq, hipStream_t st) {
+                      float* ssq, hipStream_t st, float* part) {
     const dim3 grid((unsigned)ceil_div(C, 64)), block(512);
+    if (k == 16 && part && C < SSQ_SPLIT_C) {
+        const dim3 g2((unsigned)ceil_div(C, 64), 16);
+        if (crit == 0)
+            hipLaunchKernelGGL(ssq16_chain_kernel<0>, g2, dim3(256), 0, st, xa, ld, Tc, off0, WB0, off1, WB1, C, part);
+        else
+            hipLaunchKernelGGL(ssq16_chain_kernel<1>, g2, dim3(256), 0, st, xa, ld, Tc, off0, WB0, off1, WB1, C, part);
+        hipLaunchKernelGGL(r64_tree_kernel, dim3((unsigned)ceil_div(C, 256)), dim3(256), 0, st, part, C, ssq);
+        return hipGetLastError();
+    }
     const int kr = (int)k;
 #define SSQ_LAUNCH(CR, KK)                                                                       \
     hipLaunchKernelGGL((ssq_kernel<CR, KK>), grid, block, 0, st, xa, ld, Tc, off0, WB0, off1, WB1, \

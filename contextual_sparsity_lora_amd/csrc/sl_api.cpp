@@ -377,8 +377,15 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     const int64_t Cq = crit == SL_CRIT_QK ? C * n_rep : 0;
     if (!scores) need += round_up((size_t)C * 4, 256);
     if (crit == SL_CRIT_QK) need += round_up((size_t)Cq * 4, 256) + round_up((size_t)C * 4, 256);
+    // chain partials of the split scoring form (few channels, k = 16)
+    const int64_t Cmax = crit == SL_CRIT_QK ? Cq : C;
+    const bool split = k == 16 && (C < SSQ_SPLIT_C || Cq < SSQ_SPLIT_C);
+    const size_t part_bytes = split ? round_up((size_t)64 * (Cmax < SSQ_SPLIT_C ? Cmax : C) * 4, 256) : 0;
+    need += part_bytes;
     SL_CHECK(ensure_ws(h, need));
     char* ws = (char*)h->ws;
+    float* part = split ? (float*)ws : nullptr;
+    ws += part_bytes;
     float* sc = scores;
     if (!sc) {
         sc = (float*)ws;
@@ -392,12 +399,15 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     if (crit == SL_CRIT_QK) {
         float* sq = (float*)ws;
         float* sk = (float*)(ws + round_up((size_t)Cq * 4, 256));
-        e = launch_ssq(0, xa, ld_xa, T_c, off0, WB0, 0, nullptr, k, Cq, sq, h->stream);
-        if (e == hipSuccess) e = launch_ssq(0, xa, ld_xa, T_c, off1, WB1, 0, nullptr, k, C, sk, h->stream);
+        e = launch_ssq(0, xa, ld_xa, T_c, off0, WB0, 0, nullptr, k, Cq, sq, h->stream,
+                       Cq < SSQ_SPLIT_C ? part : nullptr);
+        if (e == hipSuccess)
+            e = launch_ssq(0, xa, ld_xa, T_c, off1, WB1, 0, nullptr, k, C, sk, h->stream,
+                           C < SSQ_SPLIT_C ? part : nullptr);
         if (e == hipSuccess) e = launch_qk_combine(sq, sk, C / head_dim, n_rep, head_dim, sc, h->stream);
     } else {
         e = launch_ssq(crit == SL_CRIT_SWIGLU_L2 ? 1 : 0, xa, ld_xa, T_c, off0, WB0, off1, WB1, k,
-                       C, sc, h->stream);
+                       C, sc, h->stream, C < SSQ_SPLIT_C ? part : nullptr);
     }
     }
     if (e == hipSuccess) {

@@ -208,13 +208,15 @@ class SparseFFN:
         ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_down, s, None, dy=dy, gB=self.gB_dn,
                          D_in=F, r=r)
         self._ev[0].record(main)
+        ops.transpose(self.A_down, self.A_dT)
+        ops.sparse_linear_bwd("in", dy, None, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx,
+                              self.dh, lora=(self.gB_dn, self.A_dT, r, s))
+        # (issued after the main-stream product: the host's time on these calls
+        # overlaps that product)
         self.side.wait_event(self._ev[0])
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.h, None, None, s, self.xl_dn, dy=dy,
                              dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
-        ops.transpose(self.A_down, self.A_dT)
-        ops.sparse_linear_bwd("in", dy, None, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx,
-                              self.dh, lora=(self.gB_dn, self.A_dT, r, s))
         g, u = self.gu[:, :F], self.gu[:, F:]
         dg, du = self.dgu[:, :F], self.dgu[:, F:]
         ops.swiglu_bwd(self.dh, g, u, dg, du)
@@ -223,6 +225,9 @@ class SparseFFN:
         ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_bd, s, None, dy=self.dgu, gB=self.gB_gu,
                          D_in=D, r=2 * r)
         self._ev[1].record(main)
+        ops.transpose(self.A_gu, self.A_guT)
+        ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
+                              self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s))
         self.side.wait_event(self._ev[1])
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=self.dgu, dA=self.dA_gu,
@@ -232,9 +237,6 @@ class SparseFFN:
             ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
                              dB=self.dB_up, r=r, D_in=D)
             self._ev[2].record(self.side)
-        ops.transpose(self.A_gu, self.A_guT)
-        ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
-                              self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s))
         # the block's gradients are complete when both streams are
         main.wait_event(self._ev[2])
         return self.dx
