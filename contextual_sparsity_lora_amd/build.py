@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsparselora.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sl_api.cpp", "k_select.hip", "k_gemm.hip", "k_lora.hip", "k_layer.hip", "k_train.hip", "k_factor.hip"]
+SOURCES = ["sl_api.cpp", "k_select.hip", "k_gemm.hip", "k_lora.hip", "k_layer.hip", "k_train.hip", "k_factor.hip", "k_attn.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
          "-fno-gpu-flush-denormals-to-zero", "-fhip-fp32-correctly-rounded-divide-sqrt",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

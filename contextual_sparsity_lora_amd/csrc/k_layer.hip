@@ -388,10 +388,19 @@ hipError_t launch_add(bool bf16, const void* a, int64_t lda, const void* b, int6
         default: return hipErrorInvalidValue;                    \
     }
 
+// matrix-core attention (k_attn.hip): bf16, head dimension 32 / 64 / 128, 16-byte rows
+bool attn_mfma_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                  int64_t ldv, const void* o, int64_t ldo);
+hipError_t launch_attn_fwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* o,
+                                int64_t ldo, float* lse, hipStream_t st);
+
 hipError_t launch_attn_fwd(bool bf16, const void* q, int64_t ldq, const void* k, int64_t ldk,
                            const void* v, int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv,
                            int64_t hd, void* o, int64_t ldo, float* lse, hipStream_t st) {
     if (B <= 0 || S <= 0) return hipSuccess;
+    if (bf16 && attn_mfma_ok(hd, q, ldq, k, ldk, v, ldv, o, ldo))
+        return launch_attn_fwd_mfma(q, ldq, k, ldk, v, ldv, B, S, H, Hkv, hd, o, ldo, lse, st);
     const dim3 grid((unsigned)ceil_div(S, AQ), (unsigned)H, (unsigned)B);
     const int64_t n_rep = H / Hkv;
     SL_DISPATCH_HD(hd, SL_DISPATCH_T(bf16, hipLaunchKernelGGL((attn_fwd_kernel<TT, HDV>), grid, dim3(256), 0,
