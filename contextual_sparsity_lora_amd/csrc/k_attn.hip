@@ -152,6 +152,161 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(const bf16_t* __rest
     if (grp == 0) lse[(b * H + h) * S + qn] = m + logf(l);
 }
 
+// ---------------------------------------------------------------- backward
+// With P = exp(s / sqrt(d) - lse) recomputed per tile and
+// dS = P (dP - delta) / sqrt(d), delta[q] = sum_c dO[q, c] O[q, c]:
+//   dQ = dS K, dK = dS^T Q, dV = P^T dO, dP = dO V^T.
+
+// dQ: block = (64 queries, head h, sequence b), heaviest query blocks first.
+// Per step of 32 keys: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T fragments in
+// registers), dS^T in registers, dQ^T += K^T dS^T.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
+    const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
+    const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
+    const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
+    bf16_t* __restrict__ dq, int64_t lddq) {
+    constexpr int NC = HD / 32, NU = HD / 16;
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[FK][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Kt[HD][FK + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Vs[FK][HD + 8];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
+    const int64_t b = blockIdx.z, h = blockIdx.y, g = h / n_rep, t0 = b * S;
+    const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * FQ, qn = q0 + 16 * w + cn;
+    const bool qv = qn < S;
+    const float scale = 1.0f / sqrtf((float)HD);
+    bf16x8 qf[NC], gf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int64_t off = t0 + (qv ? qn : 0);
+        qf[c] = __builtin_bit_cast(bf16x8, gload16(q + off * ldq + h * HD + 32 * c + 8 * grp, qv));
+        gf[c] = __builtin_bit_cast(bf16x8, gload16(dO + off * lddo + h * HD + 32 * c + 8 * grp, qv));
+    }
+    const float L = qv ? lse[(b * H + h) * S + qn] : 0.0f;
+    const float Dl = qv ? delta[(b * H + h) * S + qn] : 0.0f;
+    f32x4 acc[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int64_t kend = q0 + FQ < S ? q0 + FQ : S;
+    for (int64_t k0 = 0; k0 < kend; k0 += FK) {
+        __syncthreads();
+        stage<HD, true, true>(k, ldk, t0, k0, S, g * HD, Ks, Kt);
+        stage<HD, true, false>(v, ldv, t0, k0, S, g * HD, Vs, nullptr);
+        __syncthreads();
+        f32x4 st[2], dp[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                st[t] = mfma16(*(const bf16x8*)&Ks[16 * t + cn][32 * c + 8 * grp], qf[c], st[t]);
+                dp[t] = mfma16(*(const bf16x8*)&Vs[16 * t + cn][32 * c + 8 * grp], gf[c], dp[t]);
+            }
+        }
+        float ds[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t key = k0 + 16 * t + 4 * grp + i;
+                const float p = (qv && key <= qn && key < S) ? expf(st[t][i] * scale - L) : 0.0f;
+                ds[4 * t + i] = p * (dp[t][i] - Dl) * scale;
+            }
+        const bf16x8 db = pack8(ds);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+            acc[u] = mfma16(lds_pair4(Kt[16 * u + cn], 4 * grp, 16 + 4 * grp), db, acc[u]);
+    }
+    if (!qv) return;
+    bf16_t* op = dq + (t0 + qn) * lddq + h * HD + 4 * grp;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+        *(uint2*)(op + 16 * u) = make_uint2(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]));
+}
+
+// dK, dV: block = (64 keys, key/value head g, sequence b); loops over the
+// group's query heads and the query steps of 32 at or after the keys.  S and
+// dP are computed untransposed (S = Q K^T, dP = dO V^T with K^T, V^T fragments
+// in registers), so a lane's four C entries belong to one key; then
+// dV^T += dO^T P and dK^T += Q^T dS.
+template <int HD>
+__global__ __launch_bounds__(256) void attn_bwd_kv_mfma_kernel(
+    const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
+    const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
+    const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
+    bf16_t* __restrict__ dk, int64_t lddk, bf16_t* __restrict__ dv, int64_t lddv) {
+    constexpr int NC = HD / 32, NU = HD / 16;
+    __shared__ __attribute__((aligned(16))) bf16_t Qs[FK][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Qt[HD][FK + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Gs[FK][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Gt[HD][FK + 8];
+    __shared__ float Ls[FK], Ds[FK];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
+    const int64_t b = blockIdx.z, g = blockIdx.y, t0 = b * S;
+    const int64_t k0 = (int64_t)blockIdx.x * FQ, kn = k0 + 16 * w + cn;
+    const bool kv = kn < S;
+    const float scale = 1.0f / sqrtf((float)HD);
+    bf16x8 kf[NC], vf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int64_t off = t0 + (kv ? kn : 0);
+        kf[c] = __builtin_bit_cast(bf16x8, gload16(k + off * ldk + g * HD + 32 * c + 8 * grp, kv));
+        vf[c] = __builtin_bit_cast(bf16x8, gload16(v + off * ldv + g * HD + 32 * c + 8 * grp, kv));
+    }
+    f32x4 dka[NU], dva[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) dka[u] = dva[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int64_t hr = 0; hr < n_rep; ++hr) {
+        const int64_t h = g * n_rep + hr;
+        for (int64_t i0 = k0; i0 < S; i0 += FK) {
+            __syncthreads();
+            stage<HD, true, true>(q, ldq, t0, i0, S, h * HD, Qs, Qt);
+            stage<HD, true, true>(dO, lddo, t0, i0, S, h * HD, Gs, Gt);
+            if (threadIdx.x < FK) {
+                const int64_t qi = i0 + threadIdx.x;
+                Ls[threadIdx.x] = qi < S ? lse[(b * H + h) * S + qi] : 0.0f;
+                Ds[threadIdx.x] = qi < S ? delta[(b * H + h) * S + qi] : 0.0f;
+            }
+            __syncthreads();
+            f32x4 st[2], dp[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    st[t] = mfma16(*(const bf16x8*)&Qs[16 * t + cn][32 * c + 8 * grp], kf[c], st[t]);
+                    dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][32 * c + 8 * grp], vf[c], dp[t]);
+                }
+            }
+            float p[8], ds[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int j = 16 * t + 4 * grp + i;
+                    const int64_t qi = i0 + j;
+                    const float pv = (kv && qi < S && kn <= qi) ? expf(st[t][i] * scale - Ls[j]) : 0.0f;
+                    p[4 * t + i] = pv;
+                    ds[4 * t + i] = pv * (dp[t][i] - Ds[j]) * scale;
+                }
+            const bf16x8 pb = pack8(p), db = pack8(ds);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                dva[u] = mfma16(lds_pair4(Gt[16 * u + cn], 4 * grp, 16 + 4 * grp), pb, dva[u]);
+                dka[u] = mfma16(lds_pair4(Qt[16 * u + cn], 4 * grp, 16 + 4 * grp), db, dka[u]);
+            }
+        }
+    }
+    if (!kv) return;
+    bf16_t* kp = dk + (t0 + kn) * lddk + g * HD + 4 * grp;
+    bf16_t* vp = dv + (t0 + kn) * lddv + g * HD + 4 * grp;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+        *(uint2*)(kp + 16 * u) = make_uint2(pack_bf16x2(dka[u][0], dka[u][1]), pack_bf16x2(dka[u][2], dka[u][3]));
+        *(uint2*)(vp + 16 * u) = make_uint2(pack_bf16x2(dva[u][0], dva[u][1]), pack_bf16x2(dva[u][2], dva[u][3]));
+    }
+}
+
 }  // namespace
 
 bool attn_mfma_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
@@ -175,5 +330,37 @@ hipError_t launch_attn_fwd_mfma(const void* q, int64_t ldq, const void* k, int64
     else if (hd == 128) AF(128);
     else return hipErrorInvalidValue;
 #undef AF
+    return hipGetLastError();
+}
+
+
+bool attn_mfma_bwd_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                      int64_t ldv, const void* dO, int64_t lddo, const void* dq, int64_t lddq, const void* dk,
+                      int64_t lddk, const void* dv, int64_t lddv) {
+    const auto a8 = [](const void* p, int64_t ld) { return ((uintptr_t)p & 7) == 0 && ld % 4 == 0; };
+    return attn_mfma_ok(hd, q, ldq, k, ldk, v, ldv, dq, lddq) && ((uintptr_t)dO & 15) == 0 && lddo % 8 == 0 &&
+           a8(dk, lddk) && a8(dv, lddv);
+}
+
+hipError_t launch_attn_bwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                int64_t ldv, const void* dO, int64_t lddo, const float* lse, const float* delta,
+                                int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq,
+                                void* dk, int64_t lddk, void* dv, int64_t lddv, hipStream_t st) {
+    if (B <= 0 || S <= 0) return hipSuccess;
+    const dim3 gq((unsigned)ceil_div(S, FQ), (unsigned)H, (unsigned)B);
+    const dim3 gk((unsigned)ceil_div(S, FQ), (unsigned)Hkv, (unsigned)B);
+    const int64_t n_rep = H / Hkv;
+#define AB(HDV)                                                                                               \
+    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<HDV>), gk, dim3(256), 0, st, (const bf16_t*)q, ldq,             \
+                       (const bf16_t*)k, ldk, (const bf16_t*)v, ldv, (const bf16_t*)dO, lddo, lse, delta, S, H, \
+                       n_rep, (bf16_t*)dk, lddk, (bf16_t*)dv, lddv);                                            \
+    hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<HDV>), gq, dim3(256), 0, st, (const bf16_t*)q, ldq,              \
+                       (const bf16_t*)k, ldk, (const bf16_t*)v, ldv, (const bf16_t*)dO, lddo, lse, delta, S, H, \
+                       n_rep, (bf16_t*)dq, lddq)
+    if (hd == 32) { AB(32); }
+    else if (hd == 64) { AB(64); }
+    else if (hd == 128) { AB(128); }
+    else return hipErrorInvalidValue;
+#undef AB
     return hipGetLastError();
 }

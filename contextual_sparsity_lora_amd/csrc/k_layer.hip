@@ -394,6 +394,13 @@ bool attn_mfma_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int64_t
 hipError_t launch_attn_fwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                                 int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* o,
                                 int64_t ldo, float* lse, hipStream_t st);
+bool attn_mfma_bwd_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                      int64_t ldv, const void* dO, int64_t lddo, const void* dq, int64_t lddq, const void* dk,
+                      int64_t lddk, const void* dv, int64_t lddv);
+hipError_t launch_attn_bwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
+                                int64_t ldv, const void* dO, int64_t lddo, const float* lse, const float* delta,
+                                int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq,
+                                void* dk, int64_t lddk, void* dv, int64_t lddv, hipStream_t st);
 
 hipError_t launch_attn_fwd(bool bf16, const void* q, int64_t ldq, const void* k, int64_t ldk,
                            const void* v, int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv,
@@ -419,6 +426,14 @@ hipError_t launch_attn_bwd(bool bf16, const void* q, int64_t ldq, const void* k,
     const int64_t n_rep = H / Hkv;
     const dim3 gq((unsigned)ceil_div(S, AQ), (unsigned)H, (unsigned)B);
     const dim3 gk((unsigned)ceil_div(S, AQ), (unsigned)Hkv, (unsigned)B);
+    if (bf16 && attn_mfma_bwd_ok(hd, q, ldq, k, ldk, v, ldv, dO, lddo, dq, lddq, dk, lddk, dv, lddv)) {
+        SL_DISPATCH_HD(hd, hipLaunchKernelGGL((attn_delta_kernel<bf16_t, HDV>), gq, dim3(256), 0, st,
+                                              (const bf16_t*)o, ldo, (const bf16_t*)dO, lddo, S, H, delta);)
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return launch_attn_bwd_mfma(q, ldq, k, ldk, v, ldv, dO, lddo, lse, delta, B, S, H, Hkv, hd, dq, lddq, dk,
+                                    lddk, dv, lddv, st);
+    }
     SL_DISPATCH_HD(hd, SL_DISPATCH_T(bf16,
         hipLaunchKernelGGL((attn_delta_kernel<TT, HDV>), gq, dim3(256), 0, st, (const TT*)o, ldo,
                            (const TT*)dO, lddo, S, H, delta);

@@ -65,6 +65,12 @@ def test_attention_core(case, rng):
                       d, dq, dk, dv)
     torch.cuda.synchronize()
     dq_r, dk_r, dv_r = ref.attention_bwd(q, k, v, do, B, S, H, Hkv, d)
-    assert mar(host(dq), dq_r) <= tol
-    assert mar(host(dk), dk_r) <= tol
+    if S == 1:
+        # one visible key: softmax is 1, dS = P (dP - delta) = 0, so dQ and dK
+        # are exactly zero and only rounding of dP against delta remains
+        assert np.max(np.abs(host(dq))) <= 1e-3 and np.max(np.abs(host(dk))) <= 1e-3
+        assert np.all(dq_r == 0) and np.all(dk_r == 0)
+    else:
+        assert mar(host(dq), dq_r) <= tol
+        assert mar(host(dk), dk_r) <= tol
     assert mar(host(dv), dv_r) <= tol
