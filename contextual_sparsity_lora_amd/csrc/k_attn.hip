@@ -24,8 +24,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int FQ = 64;   // queries (or keys) per block: 4 waves x 16
-constexpr int FK = 32;   // keys (or queries) per inner step
+constexpr int FQ = 64;   // backward: queries (or keys) per block, 4 waves x 16
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -48,108 +47,191 @@ __device__ __forceinline__ uint4 gload16(const bf16_t* p, bool ok) {
     return ok ? *(const uint4*)p : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Stage FK rows (row r = r0 + j of the sequence) of a [*, ld] matrix slice at
-// column c0: plain (rows x HD, pitch HD + 8) and/or transposed (HD x FK, pitch
-// FK + 8).
-template <int HD, bool PLAIN, bool TRANS>
-__device__ __forceinline__ void stage(const bf16_t* __restrict__ src, int64_t ld, int64_t t0, int64_t r0,
-                                      int64_t S, int64_t c0, bf16_t (*pl)[HD + 8], bf16_t (*tr)[FK + 8]) {
-    for (int e = threadIdx.x; e < FK * HD / 8; e += 256) {
-        const int j = e / (HD / 8), c8 = (e % (HD / 8)) * 8;
-        const int64_t r = r0 + j;
-        const uint4 v = gload16(src + (t0 + r) * ld + c0 + c8, r < S);
-        if (PLAIN) *(uint4*)&pl[j][c8] = v;
-        if (TRANS) {
-            const bf16_t* vb = (const bf16_t*)&v;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// A tile of FR sequence rows (r0 .. r0 + FR - 1; rows at or past S read as 0)
+// by HD columns of a [*, ld] slice at column c0, fetched into registers so the
+// loads of the next step are in flight while the current one is multiplied.
+// Unit e < FR / 4 * HD / 8 holds rows 4 (e % (FR / 4)) .. + 3 of the 8-column
+// chunk e / (FR / 4): its transposed store is eight 8-byte runs of 4 rows.
+template <int HD, int FR>
+struct Tile {
+    static constexpr int NQ = FR / 4, NE = NQ * HD / 8, PER = (NE + 255) / 256;
+    uint4 r[PER][4];
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ src, int64_t ld, int64_t t0, int64_t r0,
+                                         int64_t S, int64_t c0) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) tr[c8 + q][j] = vb[q];
+        for (int p = 0; p < PER; ++p) {
+            const int e = threadIdx.x + 256 * p;
+            if (NE % 256 != 0 && e >= NE) continue;
+            const int rq = e % NQ, ci = e / NQ;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = r0 + 4 * rq + i;
+                r[p][i] = gload16(src + (t0 + (row < S ? row : 0)) * ld + c0 + 8 * ci, row < S);
+            }
         }
     }
-}
+    __device__ __forceinline__ void store_plain(bf16_t (*pl)[HD + 8]) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = threadIdx.x + 256 * p;
+            if (NE % 256 != 0 && e >= NE) continue;
+            const int rq = e % NQ, ci = e / NQ;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(uint4*)&pl[4 * rq + i][8 * ci] = r[p][i];
+        }
+    }
+    template <int TP>
+    __device__ __forceinline__ void store_trans(bf16_t (*tr)[TP]) const {
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int e = threadIdx.x + 256 * p;
+            if (NE % 256 != 0 && e >= NE) continue;
+            const int rq = e % NQ, ci = e / NQ;
+            const u32x4 x0 = __builtin_bit_cast(u32x4, r[p][0]), x1 = __builtin_bit_cast(u32x4, r[p][1]);
+            const u32x4 x2 = __builtin_bit_cast(u32x4, r[p][2]), x3 = __builtin_bit_cast(u32x4, r[p][3]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                // column 8 ci + 2 w: low halves; column 8 ci + 2 w + 1: high halves
+                const uint2 lo = make_uint2((x0[w] & 0xffffu) | (x1[w] << 16), (x2[w] & 0xffffu) | (x3[w] << 16));
+                const uint2 hi = make_uint2((x0[w] >> 16) | (x1[w] & 0xffff0000u), (x2[w] >> 16) | (x3[w] & 0xffff0000u));
+                *(uint2*)&tr[8 * ci + 2 * w][4 * rq] = lo;
+                *(uint2*)&tr[8 * ci + 2 * w + 1][4 * rq] = hi;
+            }
+        }
+    }
+};
+
+constexpr int F2Q = 128;       // forward: queries per block, 4 waves x 32
+constexpr int F2K = 64;        // keys (forward, dQ) or queries (dK, dV) per step
+// transposed-tile pitch (elements): 8-byte aligned rows, banks balanced for the
+// 4-row stores above
+constexpr int TP64 = F2K + 8;
 
 // ---------------------------------------------------------------- forward
-// Block = (64 queries, head h, sequence b); wave w owns queries q0 + 16 w ..
-// + 15, lane l query q0 + 16 w + (l % 16).  Per step of 32 keys: S^T (2 tiles
-// x HD/32 chunks), online softmax, O^T += V^T P^T (HD/16 tiles).
+// Block = (128 queries, head h, sequence b), heaviest (latest) query blocks
+// first; wave w owns queries q0 + 32 w .. + 31 as two 16-query column tiles,
+// lane l queries q0 + 32 w + 16 qt + (l % 16).  Per step of 64 keys (K plain,
+// V transposed, double-buffered in LDS, the next step's loads in flight):
+// S^T (4 key tiles x 2 query tiles x HD/32 chunks), online softmax,
+// O^T += V^T P^T (2 key halves x HD/16 tiles per query tile).  A wave skips
+// the steps whose keys all lie after its queries.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(const bf16_t* __restrict__ q, int64_t ldq,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_mfma_kernel(const bf16_t* __restrict__ q, int64_t ldq,
                                                             const bf16_t* __restrict__ k, int64_t ldk,
                                                             const bf16_t* __restrict__ v, int64_t ldv,
                                                             int64_t S, int64_t H, int64_t n_rep,
                                                             bf16_t* __restrict__ o, int64_t ldo,
                                                             float* __restrict__ lse) {
     constexpr int NC = HD / 32, NU = HD / 16;
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[FK][HD + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Vt[HD][FK + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[2][F2K][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Vt[2][HD][TP64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / n_rep, t0 = b * S;
-    const int64_t q0 = (int64_t)blockIdx.x * FQ, qn = q0 + 16 * w + cn;
+    const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * F2Q, qw = q0 + 32 * w;
     const float scale = 1.0f / sqrtf((float)HD);
-    bf16x8 qf[NC];
+    bf16x8 qf[2][NC];
+    int64_t qn[2];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-        qf[c] = __builtin_bit_cast(bf16x8, gload16(q + (t0 + (qn < S ? qn : 0)) * ldq + h * HD + 32 * c + 8 * grp,
-                                                   qn < S));
-    f32x4 acc[NU];
+    for (int qt = 0; qt < 2; ++qt) {
+        qn[qt] = qw + 16 * qt + cn;
+        const bool ok = qn[qt] < S;
 #pragma unroll
-    for (int u = 0; u < NU; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, lsum = 0.0f;
-    const int64_t kend = q0 + FQ < S ? q0 + FQ : S;
-    for (int64_t k0 = 0; k0 < kend; k0 += FK) {
-        __syncthreads();
-        stage<HD, true, false>(k, ldk, t0, k0, S, g * HD, Ks, nullptr);
-        stage<HD, false, true>(v, ldv, t0, k0, S, g * HD, nullptr, Vt);
-        __syncthreads();
-        f32x4 st[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+        for (int c = 0; c < NC; ++c)
+            qf[qt][c] = __builtin_bit_cast(
+                bf16x8, gload16(q + (t0 + (ok ? qn[qt] : 0)) * ldq + h * HD + 32 * c + 8 * grp, ok));
+    }
+    f32x4 acc[2][NU];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+    for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
-                st[t] = mfma16(*(const bf16x8*)&Ks[16 * t + cn][32 * c + 8 * grp], qf[c], st[t]);
-        float p[8], mloc = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t key = k0 + 16 * t + 4 * grp + i;
-                const float s = (key <= qn && key < S) ? st[t][i] * scale : -INFINITY;
-                p[4 * t + i] = s;
-                mloc = fmaxf(mloc, s);
-            }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-        const float mnew = fmaxf(m, mloc);
-        const float mu = mnew == -INFINITY ? 0.0f : mnew;     // no visible key yet: everything stays 0
-        const float corr = expf(m - mu);
-        float ps = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            p[e] = expf(p[e] - mu);
-            ps += p[e];
+        for (int u = 0; u < NU; ++u) acc[qt][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    float m[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.0f, 0.0f};
+    const int64_t kend = q0 + F2Q < S ? q0 + F2Q : S;
+    const int nsteps = (int)((kend + F2K - 1) / F2K);
+    Tile<HD, F2K> tk, tv;
+    tk.load(k, ldk, t0, 0, S, g * HD);
+    tv.load(v, ldv, t0, 0, S, g * HD);
+    tk.store_plain(Ks[0]);
+    tv.store_trans(Vt[0]);
+    __syncthreads();
+    for (int s = 0; s < nsteps; ++s) {
+        const int buf = s & 1;
+        const int64_t k0 = (int64_t)s * F2K;
+        if (s + 1 < nsteps) {
+            tk.load(k, ldk, t0, k0 + F2K, S, g * HD);
+            tv.load(v, ldv, t0, k0 + F2K, S, g * HD);
         }
-        lsum = lsum * corr + ps;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+            if (k0 > qw + 16 * qt + 15 || qw + 16 * qt >= S) continue;   // wave-uniform: nothing visible
+            f32x4 st[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                st[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    st[t] = mfma16(*(const bf16x8*)&Ks[buf][16 * t + cn][32 * c + 8 * grp], qf[qt][c], st[t]);
+            }
+            float p[16], mloc = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t key = k0 + 16 * t + 4 * grp + i;
+                    const float sv = (key <= qn[qt] && key < S) ? st[t][i] * scale : -INFINITY;
+                    p[4 * t + i] = sv;
+                    mloc = fmaxf(mloc, sv);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float mnew = fmaxf(m[qt], mloc);
+            const float mu = mnew == -INFINITY ? 0.0f : mnew;   // no visible key yet: everything stays 0
+            const float corr = expf(m[qt] - mu);
+            float ps = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                p[e] = expf(p[e] - mu);
+                ps += p[e];
+            }
+            lsum[qt] = lsum[qt] * corr + ps;
+            m[qt] = mnew;
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[qt][u][i] *= corr;
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk) {
+                float ph[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ph[e] = p[8 * hk + e];
+                const bf16x8 pb = pack8(ph);
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+                    acc[qt][u] = mfma16(lds_pair4(&Vt[buf][16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), pb,
+                                        acc[qt][u]);
+            }
+        }
+        if (s + 1 < nsteps) {
+            tk.store_plain(Ks[buf ^ 1]);
+            tv.store_trans(Vt[buf ^ 1]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+        float l = lsum[qt] + __shfl_xor(lsum[qt], 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        if (qn[qt] >= S) continue;
+        const float inv = 1.0f / l;
+        bf16_t* op = o + (t0 + qn[qt]) * ldo + h * HD + 4 * grp;
 #pragma unroll
         for (int u = 0; u < NU; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[u][i] *= corr;
-        const bf16x8 pb = pack8(p);
-#pragma unroll
-        for (int u = 0; u < NU; ++u)
-            acc[u] = mfma16(lds_pair4(Vt[16 * u + cn], 4 * grp, 16 + 4 * grp), pb, acc[u]);
-        m = mnew;
+            *(uint2*)(op + 16 * u) = make_uint2(pack_bf16x2(acc[qt][u][0] * inv, acc[qt][u][1] * inv),
+                                                pack_bf16x2(acc[qt][u][2] * inv, acc[qt][u][3] * inv));
+        if (grp == 0) lse[(b * H + h) * S + qn[qt]] = m[qt] + logf(l);
     }
-    float l = lsum + __shfl_xor(lsum, 16, 64);
-    l += __shfl_xor(l, 32, 64);
-    if (qn >= S) return;
-    const float inv = 1.0f / l;
-    bf16_t* op = o + (t0 + qn) * ldo + h * HD + 4 * grp;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-        const uint2 pk = make_uint2(pack_bf16x2(acc[u][0] * inv, acc[u][1] * inv),
-                                    pack_bf16x2(acc[u][2] * inv, acc[u][3] * inv));
-        *(uint2*)(op + 16 * u) = pk;
-    }
-    if (grp == 0) lse[(b * H + h) * S + qn] = m + logf(l);
 }
 
 // ---------------------------------------------------------------- backward
@@ -157,22 +239,24 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma_kernel(const bf16_t* __rest
 // dS = P (dP - delta) / sqrt(d), delta[q] = sum_c dO[q, c] O[q, c]:
 //   dQ = dS K, dK = dS^T Q, dV = P^T dO, dP = dO V^T.
 
-// dQ: block = (64 queries, head h, sequence b), heaviest query blocks first.
-// Per step of 32 keys: S^T = K Q^T and dP^T = V dO^T (Q^T, dO^T fragments in
-// registers), dS^T in registers, dQ^T += K^T dS^T.
+// dQ: block = (64 queries, head h, sequence b), heaviest query blocks first;
+// wave w owns queries q0 + 16 w .. + 15.  Per step of 64 keys (K plain and
+// transposed, V plain; the next step's loads in flight): S^T = K Q^T and
+// dP^T = V dO^T (Q^T, dO^T fragments in registers), dS^T in registers,
+// dQ^T += K^T dS^T.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
     const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
     const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
     const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
     bf16_t* __restrict__ dq, int64_t lddq) {
-    constexpr int NC = HD / 32, NU = HD / 16;
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[FK][HD + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Kt[HD][FK + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Vs[FK][HD + 8];
+    constexpr int NC = HD / 32, NU = HD / 16, NT = F2K / 16;
+    __shared__ __attribute__((aligned(16))) bf16_t Ks[F2K][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Kt[HD][TP64];
+    __shared__ __attribute__((aligned(16))) bf16_t Vs[F2K][HD + 8];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / n_rep, t0 = b * S;
-    const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * FQ, qn = q0 + 16 * w + cn;
+    const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * FQ, qw = q0 + 16 * w, qn = qw + cn;
     const bool qv = qn < S;
     const float scale = 1.0f / sqrtf((float)HD);
     bf16x8 qf[NC], gf[NC];
@@ -188,14 +272,23 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
 #pragma unroll
     for (int u = 0; u < NU; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const int64_t kend = q0 + FQ < S ? q0 + FQ : S;
-    for (int64_t k0 = 0; k0 < kend; k0 += FK) {
+    Tile<HD, F2K> tk, tv;
+    tk.load(k, ldk, t0, 0, S, g * HD);
+    tv.load(v, ldv, t0, 0, S, g * HD);
+    for (int64_t k0 = 0; k0 < kend; k0 += F2K) {
         __syncthreads();
-        stage<HD, true, true>(k, ldk, t0, k0, S, g * HD, Ks, Kt);
-        stage<HD, true, false>(v, ldv, t0, k0, S, g * HD, Vs, nullptr);
+        tk.store_plain(Ks);
+        tk.store_trans(Kt);
+        tv.store_plain(Vs);
         __syncthreads();
-        f32x4 st[2], dp[2];
+        if (k0 + F2K < kend) {
+            tk.load(k, ldk, t0, k0 + F2K, S, g * HD);
+            tv.load(v, ldv, t0, k0 + F2K, S, g * HD);
+        }
+        if (k0 > qw + 15 || qw >= S) continue;   // wave-uniform: no visible key
+        f32x4 st[NT], dp[NT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < NT; ++t) {
             st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
@@ -203,19 +296,25 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
                 dp[t] = mfma16(*(const bf16x8*)&Vs[16 * t + cn][32 * c + 8 * grp], gf[c], dp[t]);
             }
         }
-        float ds[8];
+        float ds[4 * NT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int64_t key = k0 + 16 * t + 4 * grp + i;
                 const float p = (qv && key <= qn && key < S) ? expf(st[t][i] * scale - L) : 0.0f;
                 ds[4 * t + i] = p * (dp[t][i] - Dl) * scale;
             }
-        const bf16x8 db = pack8(ds);
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-            acc[u] = mfma16(lds_pair4(Kt[16 * u + cn], 4 * grp, 16 + 4 * grp), db, acc[u]);
+        for (int hk = 0; hk < NT / 2; ++hk) {
+            float dh[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dh[e] = ds[8 * hk + e];
+            const bf16x8 db = pack8(dh);
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                acc[u] = mfma16(lds_pair4(&Kt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), db, acc[u]);
+        }
     }
     if (!qv) return;
     bf16_t* op = dq + (t0 + qn) * lddq + h * HD + 4 * grp;
@@ -224,26 +323,27 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
         *(uint2*)(op + 16 * u) = make_uint2(pack_bf16x2(acc[u][0], acc[u][1]), pack_bf16x2(acc[u][2], acc[u][3]));
 }
 
-// dK, dV: block = (64 keys, key/value head g, sequence b); loops over the
-// group's query heads and the query steps of 32 at or after the keys.  S and
-// dP are computed untransposed (S = Q K^T, dP = dO V^T with K^T, V^T fragments
-// in registers), so a lane's four C entries belong to one key; then
-// dV^T += dO^T P and dK^T += Q^T dS.
+// dK, dV: block = (64 keys, key/value head g, sequence b); wave w owns keys
+// k0 + 16 w .. + 15.  Steps run over the group's query heads and, per head,
+// the 64-query runs at or after the keys (Q and dO plain and transposed; the
+// next step's loads in flight).  S and dP are computed untransposed
+// (S = Q K^T, dP = dO V^T with K^T, V^T fragments in registers), so a lane's
+// four C entries belong to one key; then dV^T += dO^T P and dK^T += Q^T dS.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_kv_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_kv_mfma_kernel(
     const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
     const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
     const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
     bf16_t* __restrict__ dk, int64_t lddk, bf16_t* __restrict__ dv, int64_t lddv) {
-    constexpr int NC = HD / 32, NU = HD / 16;
-    __shared__ __attribute__((aligned(16))) bf16_t Qs[FK][HD + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Qt[HD][FK + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Gs[FK][HD + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t Gt[HD][FK + 8];
-    __shared__ float Ls[FK], Ds[FK];
+    constexpr int NC = HD / 32, NU = HD / 16, NT = F2K / 16;
+    __shared__ __attribute__((aligned(16))) bf16_t Qs[F2K][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Qt[HD][TP64];
+    __shared__ __attribute__((aligned(16))) bf16_t Gs[F2K][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Gt[HD][TP64];
+    __shared__ float Ls[F2K], Ds[F2K];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
     const int64_t b = blockIdx.z, g = blockIdx.y, t0 = b * S;
-    const int64_t k0 = (int64_t)blockIdx.x * FQ, kn = k0 + 16 * w + cn;
+    const int64_t k0 = (int64_t)blockIdx.x * FQ, kw = k0 + 16 * w, kn = kw + cn;
     const bool kv = kn < S;
     const float scale = 1.0f / sqrtf((float)HD);
     bf16x8 kf[NC], vf[NC];
@@ -256,44 +356,60 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_mfma_kernel(
     f32x4 dka[NU], dva[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) dka[u] = dva[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int64_t hr = 0; hr < n_rep; ++hr) {
-        const int64_t h = g * n_rep + hr;
-        for (int64_t i0 = k0; i0 < S; i0 += FK) {
-            __syncthreads();
-            stage<HD, true, true>(q, ldq, t0, i0, S, h * HD, Qs, Qt);
-            stage<HD, true, true>(dO, lddo, t0, i0, S, h * HD, Gs, Gt);
-            if (threadIdx.x < FK) {
-                const int64_t qi = i0 + threadIdx.x;
-                Ls[threadIdx.x] = qi < S ? lse[(b * H + h) * S + qi] : 0.0f;
-                Ds[threadIdx.x] = qi < S ? delta[(b * H + h) * S + qi] : 0.0f;
-            }
-            __syncthreads();
-            f32x4 st[2], dp[2];
+    // steps (query head hr, queries i0 .. i0 + 63), i0 from k0 to S, flattened
+    const int64_t nsi = (S - k0 + F2K - 1) / F2K, nst = nsi * n_rep;
+    Tile<HD, F2K> tq, tg;
+    float lr = 0.0f, dr = 0.0f;
+    auto fetch = [&](int64_t sidx) {
+        const int64_t h = g * n_rep + sidx / nsi, i0 = k0 + (sidx % nsi) * F2K;
+        tq.load(q, ldq, t0, i0, S, h * HD);
+        tg.load(dO, lddo, t0, i0, S, h * HD);
+        if (threadIdx.x < F2K) {
+            const int64_t qi = i0 + threadIdx.x;
+            lr = qi < S ? lse[(b * H + h) * S + qi] : 0.0f;
+            dr = qi < S ? delta[(b * H + h) * S + qi] : 0.0f;
+        }
+    };
+    fetch(0);
+    for (int64_t sidx = 0; sidx < nst; ++sidx) {
+        const int64_t i0 = k0 + (sidx % nsi) * F2K;
+        __syncthreads();
+        tq.store_plain(Qs);
+        tq.store_trans(Qt);
+        tg.store_plain(Gs);
+        tg.store_trans(Gt);
+        if (threadIdx.x < F2K) Ls[threadIdx.x] = lr, Ds[threadIdx.x] = dr;
+        __syncthreads();
+        if (sidx + 1 < nst) fetch(sidx + 1);
+        if (i0 + F2K - 1 < kw || kw >= S) continue;   // wave-uniform: every query precedes the wave's keys
+        f32x4 st[NT], dp[NT];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t) {
+            st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-                    st[t] = mfma16(*(const bf16x8*)&Qs[16 * t + cn][32 * c + 8 * grp], kf[c], st[t]);
-                    dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][32 * c + 8 * grp], vf[c], dp[t]);
-                }
+            for (int c = 0; c < NC; ++c) {
+                st[t] = mfma16(*(const bf16x8*)&Qs[16 * t + cn][32 * c + 8 * grp], kf[c], st[t]);
+                dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][32 * c + 8 * grp], vf[c], dp[t]);
             }
+        }
+#pragma unroll
+        for (int hk = 0; hk < NT / 2; ++hk) {
             float p[8], ds[8];
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int j = 16 * t + 4 * grp + i;
+                    const int t = 2 * hk + tt, j = 16 * t + 4 * grp + i;
                     const int64_t qi = i0 + j;
                     const float pv = (kv && qi < S && kn <= qi) ? expf(st[t][i] * scale - Ls[j]) : 0.0f;
-                    p[4 * t + i] = pv;
-                    ds[4 * t + i] = pv * (dp[t][i] - Ds[j]) * scale;
+                    p[4 * tt + i] = pv;
+                    ds[4 * tt + i] = pv * (dp[t][i] - Ds[j]) * scale;
                 }
             const bf16x8 pb = pack8(p), db = pack8(ds);
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                dva[u] = mfma16(lds_pair4(Gt[16 * u + cn], 4 * grp, 16 + 4 * grp), pb, dva[u]);
-                dka[u] = mfma16(lds_pair4(Qt[16 * u + cn], 4 * grp, 16 + 4 * grp), db, dka[u]);
+                dva[u] = mfma16(lds_pair4(&Gt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), pb, dva[u]);
+                dka[u] = mfma16(lds_pair4(&Qt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), db, dka[u]);
             }
         }
     }
@@ -320,7 +436,7 @@ hipError_t launch_attn_fwd_mfma(const void* q, int64_t ldq, const void* k, int64
                                 int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* o,
                                 int64_t ldo, float* lse, hipStream_t st) {
     if (B <= 0 || S <= 0) return hipSuccess;
-    const dim3 grid((unsigned)ceil_div(S, FQ), (unsigned)H, (unsigned)B);
+    const dim3 grid((unsigned)ceil_div(S, F2Q), (unsigned)H, (unsigned)B);
     const int64_t n_rep = H / Hkv;
 #define AF(HDV)                                                                                      \
     hipLaunchKernelGGL((attn_fwd_mfma_kernel<HDV>), grid, dim3(256), 0, st, (const bf16_t*)q, ldq,      \
