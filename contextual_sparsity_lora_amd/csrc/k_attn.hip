@@ -49,6 +49,12 @@ __device__ __forceinline__ uint4 gload16(const bf16_t* p, bool ok) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Plain tiles keep row r's 16-byte chunk c at chunk c ^ ((r >> 4) & 3): the 16
+// lanes of a quarter-wave store rows 4 apart (16 banks apart at a 68-word
+// pitch), which the swizzle spreads over all 64 banks; a product reads one
+// 16-row tile t at a time, where the swizzle is the fixed xor by t.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 4) & 3); }
+
 // A tile of FR sequence rows (r0 .. r0 + FR - 1; rows at or past S read as 0)
 // by HD columns of a [*, ld] slice at column c0, fetched into registers so the
 // loads of the next step are in flight while the current one is multiplied.
@@ -79,7 +85,7 @@ struct Tile {
             if (NE % 256 != 0 && e >= NE) continue;
             const int rq = e % NQ, ci = e / NQ;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *(uint4*)&pl[4 * rq + i][8 * ci] = r[p][i];
+            for (int i = 0; i < 4; ++i) *(uint4*)&pl[4 * rq + i][8 * swz(4 * rq + i, ci)] = r[p][i];
         }
     }
     template <int TP>
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 st[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < NC; ++c)
-                    st[t] = mfma16(*(const bf16x8*)&Ks[buf][16 * t + cn][32 * c + 8 * grp], qf[qt][c], st[t]);
+                    st[t] = mfma16(*(const bf16x8*)&Ks[buf][16 * t + cn][8 * ((4 * c + grp) ^ t)], qf[qt][c], st[t]);
             }
             float p[16], mloc = -INFINITY;
 #pragma unroll
@@ -292,8 +298,8 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
             st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                st[t] = mfma16(*(const bf16x8*)&Ks[16 * t + cn][32 * c + 8 * grp], qf[c], st[t]);
-                dp[t] = mfma16(*(const bf16x8*)&Vs[16 * t + cn][32 * c + 8 * grp], gf[c], dp[t]);
+                st[t] = mfma16(*(const bf16x8*)&Ks[16 * t + cn][8 * ((4 * c + grp) ^ t)], qf[c], st[t]);
+                dp[t] = mfma16(*(const bf16x8*)&Vs[16 * t + cn][8 * ((4 * c + grp) ^ t)], gf[c], dp[t]);
             }
         }
         float ds[4 * NT];
@@ -388,8 +394,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                st[t] = mfma16(*(const bf16x8*)&Qs[16 * t + cn][32 * c + 8 * grp], kf[c], st[t]);
-                dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][32 * c + 8 * grp], vf[c], dp[t]);
+                st[t] = mfma16(*(const bf16x8*)&Qs[16 * t + cn][8 * ((4 * c + grp) ^ t)], kf[c], st[t]);
+                dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][8 * ((4 * c + grp) ^ t)], vf[c], dp[t]);
             }
         }
 #pragma unroll
