@@ -81,7 +81,7 @@ class SparseFFN:
         # a second stream (default priority) for the LoRA reductions that nothing
         # later in the block reads, so they overlap the main-branch products
         self.side = torch.cuda.Stream(device=dev)
-        self._ev = [torch.cuda.Event() for _ in range(4)]
+        self._ev = [torch.cuda.Event() for _ in range(5)]
         assert dense or criterion != "svd" or self.k > 0, "the estimator factors are required"
         self._T = None
 
@@ -136,6 +136,11 @@ class SparseFFN:
         self.dA_down, self.dB_down = e(r, F, dtype=f32), e(D, r, dtype=f32)
         self.gB_gu = e(T, 2 * r, dtype=f32)
         self.gB_dn = e(T, r, dtype=f32)
+        # K-gathered weight slices of the selection (bf16 only): down's input
+        # channels for the forward, gate|up's rows for the backward
+        c8 = lambda n: (n + 7) // 8 * 8
+        self.ws_dn = e(D, c8(self.n), dtype=dt) if dt == torch.bfloat16 else None
+        self.ws_gu = e(D, c8(2 * self.n), dtype=dt) if dt == torch.bfloat16 else None
         self._T = (T, T_c, T_o)
 
     def forward(self, x, roles, T_c):
@@ -160,9 +165,19 @@ class SparseFFN:
             if overlap:
                 ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
                                       self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
-            self._ev[3].record(self.side)
         if not self.dense:
             self._select(x)
+        # the weight slices need only the selection: built on the second stream
+        # while the main stream runs the context rows' gate|up product
+        self._slices = overlap and self.ws_dn is not None
+        if self._slices:
+            self._ev[4].record(main)
+            self.side.wait_event(self._ev[4])
+        with torch.cuda.stream(self.side):
+            if self._slices:
+                ops.weight_slice(self.Wt_dn, self.idx, self.ws_dn)
+                ops.weight_slice(self.W_gu, self.idx2, self.ws_gu)
+            self._ev[3].record(self.side)
         main.wait_event(self._ev[1])
         # the gate|up main branch of the context rows (gathered channels; every
         # row when dense or not overlapped) with the LoRA term fused into the
@@ -175,7 +190,8 @@ class SparseFFN:
         # down main branch: input channels = the same selection; LoRA fused
         ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
         ops.sparse_linear_fwd("in", self.h, self.W_dn, self.Wt_dn, self.ctx_rows, self.out_rows,
-                              self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale))
+                              self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale),
+                              w_slice=self.ws_dn if self._slices else None)
         return self.y
 
     def _select(self, x):
@@ -227,7 +243,8 @@ class SparseFFN:
         self._ev[1].record(main)
         ops.transpose(self.A_gu, self.A_guT)
         ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
-                              self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s))
+                              self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s),
+                              w_slice=self.ws_gu if self._slices else None)
         self.side.wait_event(self._ev[1])
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=self.dgu, dA=self.dA_gu,
