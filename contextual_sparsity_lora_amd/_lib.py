@@ -43,6 +43,7 @@ SIGNATURES = {
     "sl_expand_gqa": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_stack_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
     "sl_offset_index": (_st, [_vp, _vp, _i64, _i64, _i64, _vp]),
+    "sl_qkv_index": (_st, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
     "sl_sparse_linear_fwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
                                    _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _int]),

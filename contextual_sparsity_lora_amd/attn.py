@@ -82,7 +82,7 @@ class SparseAttnProj:
         # rows and the LoRA down-projection overlap the selection; the LoRA
         # reductions nothing later reads overlap the backward products
         self.side = torch.cuda.Stream(device=dev)
-        self._ev = [torch.cuda.Event() for _ in range(6)]
+        self._ev = [torch.cuda.Event() for _ in range(7)]
         self._T = None
 
     def _alloc(self, T, T_c, T_o, dev):
@@ -114,6 +114,13 @@ class SparseAttnProj:
         self.dB_q, self.dB_k, self.dB_v = e(Cq, r, dtype=f32), e(Ckv, r, dtype=f32), e(Ckv, r, dtype=f32)
         self.dA_o, self.dB_o = e(r, Cq, dtype=f32), e(D, r, dtype=f32)
         self.gB_qkv, self.gB_o = e(T, 3 * r, dtype=f32), e(T, r, dtype=f32)
+        # K-gathered weight slices of the selection (bf16 only): o's input
+        # channels for the forward, q|k|v's rows for the backward's dx product
+        c8 = lambda n: (n + 7) // 8 * 8
+        bf = dt == torch.bfloat16
+        self.ws_o = e(D, c8(self.n_vo * self.n_rep), dtype=dt) if bf else None
+        self.ws_qkv = e(D, c8(self.idx_qkv.numel()), dtype=dt) if bf else None
+        self._slices = False
         self._T = (T, T_c, T_o)
 
     def select(self, estimated=False):
@@ -151,12 +158,8 @@ class SparseAttnProj:
             ops.random_scores(self.last_seed + (1 << 32), self.scores_vo)
             ops.select_top(self.scores_vo, self.n_vo, self.idx_vo)
         self.calls += 1
-        ops.expand_gqa(self.idx_qk, self.n_rep, self.d, self.idx_q)
-        ops.expand_gqa(self.idx_vo, self.n_rep, self.d, self.idx_o)
-        nq = self.idx_q.numel()
-        ops.offset_index(self.idx_q, 0, Cq, self.idx_qkv[:nq])
-        ops.offset_index(self.idx_qk, Cq, Ckv, self.idx_qkv[nq:nq + self.n_qk])
-        ops.offset_index(self.idx_vo, Cq + Ckv, Ckv, self.idx_qkv[nq + self.n_qk:])
+        ops.qkv_index(self.idx_qk, self.idx_vo, self.n_kv_heads, self.n_rep, self.d, self.idx_q, self.idx_o,
+                      self.idx_qkv)
 
     def forward_qkv(self, x, roles, T_c):
         """Token split, selection and the stacked q|k|v product (main + LoRA)."""
@@ -182,9 +185,19 @@ class SparseAttnProj:
             if overlap:
                 ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
                                       self.qkv, lora=lora, flags=ops.ONLY_OUT_ROWS)
-            ev[2].record(self.side)
         if not self.dense:
             self.select(estimated=True)
+        # the weight slices need only the selection: built on the second stream
+        # while the main stream runs the context rows' q|k|v product
+        self._slices = overlap and self.ws_o is not None
+        if self._slices:
+            ev[6].record(main)
+            self.side.wait_event(ev[6])
+        with torch.cuda.stream(self.side):
+            if self._slices:
+                ops.weight_slice(self.Wt_o, self.idx_o, self.ws_o)
+                ops.weight_slice(self.W_qkv, self.idx_qkv, self.ws_qkv)
+            ev[2].record(self.side)
         main.wait_event(ev[1])
         ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
                               self.qkv, lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
@@ -197,7 +210,8 @@ class SparseAttnProj:
         self.x_o = x_o
         ops.lora_fwd_bwd(ops.LORA_XL, x_o, self.A_o, None, self.scale, self.xl_o)
         ops.sparse_linear_fwd("in", x_o, self.W_o, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
-                              self.o, lora=(self.xl_o, self.B_o, r, self.scale))
+                              self.o, lora=(self.xl_o, self.B_o, r, self.scale),
+                              w_slice=self.ws_o if self._slices else None)
         return self.o
 
     def forward(self, x, x_o, roles, T_c):
@@ -236,7 +250,8 @@ class SparseAttnProj:
         ev[4].record(main)
         ops.transpose(self.A_qkv, self.A_qkvT)
         ops.sparse_linear_bwd("out", dqkv, self.W_qkv, self.W_qkvT, self.ctx_rows, self.out_rows,
-                              self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s))
+                              self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s),
+                              w_slice=self.ws_qkv if self._slices else None)
         self.side.wait_event(ev[4])
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=dqkv, dA=self.dA_qkv,

@@ -600,6 +600,35 @@ __global__ void offset_index_kernel(const int32_t* __restrict__ idx, int64_t n, 
     if (p < n) out[p] = (int32_t)(idx[p] + offset);
 }
 
+// q|k|v index lists of one attention block in one launch: thread p < n_qk
+// expands QK key/value channel idx_qk[p] to its n_rep query channels (idx_q)
+// and writes its key row idx_qk[p] + Cq; thread n_qk + p' does the same for
+// VO channel idx_vo[p'] (idx_o, value row idx_vo[p'] + Cq + Ckv).  The stacked
+// list is [idx_q | idx_qk + Cq | idx_vo + Cq + Ckv].
+__global__ void qkv_index_kernel(const int32_t* __restrict__ idx_qk, int64_t n_qk,
+                                 const int32_t* __restrict__ idx_vo, int64_t n_vo, int64_t n_rep, int64_t d,
+                                 int64_t Cq, int64_t Ckv, int32_t* __restrict__ idx_q,
+                                 int32_t* __restrict__ idx_o, int32_t* __restrict__ idx_qkv) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n_qk + n_vo) return;
+    const bool qk = p < n_qk;
+    const int32_t* idx = qk ? idx_qk : idx_vo;
+    const int64_t n = qk ? n_qk : n_vo, i = qk ? p : p - n_qk;
+    int32_t* ex = qk ? idx_q : idx_o;
+    const int64_t e = idx[i], g = e / d, j = e % d;
+    const int64_t sg = lower_bound_i32(idx, n, g * d);
+    const int64_t cg = lower_bound_i32(idx, n, (g + 1) * d) - sg;
+    for (int64_t r = 0; r < n_rep; ++r) {
+        const int64_t pos = sg * n_rep + r * cg + (i - sg);
+        const int32_t v = (int32_t)((g * n_rep + r) * d + j);
+        ex[pos] = v;
+        if (qk) idx_qkv[pos] = v;
+    }
+    const int64_t nq = n_qk * n_rep;
+    if (qk) idx_qkv[nq + i] = (int32_t)(e + Cq);
+    else idx_qkv[nq + n_qk + i] = (int32_t)(e + Cq + Ckv);
+}
+
 // ---------------------------------------------------------------- criterion variants
 template <typename T> __device__ __forceinline__ float ldv(const T* p, int64_t i);
 template <> __device__ __forceinline__ float ldv<float>(const float* p, int64_t i) { return p[i]; }
@@ -771,6 +800,15 @@ hipError_t launch_expand_gqa(const int32_t* idx, int64_t n, int64_t n_rep, int64
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(expand_gqa_kernel, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, st, idx,
                        n, n_rep, d, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_index(const int32_t* idx_qk, int64_t n_qk, const int32_t* idx_vo, int64_t n_vo,
+                            int64_t n_rep, int64_t d, int64_t Cq, int64_t Ckv, int32_t* idx_q, int32_t* idx_o,
+                            int32_t* idx_qkv, hipStream_t st) {
+    if (n_qk + n_vo <= 0) return hipSuccess;
+    hipLaunchKernelGGL(qkv_index_kernel, dim3((unsigned)ceil_div(n_qk + n_vo, 256)), dim3(256), 0, st, idx_qk,
+                       n_qk, idx_vo, n_vo, n_rep, d, Cq, Ckv, idx_q, idx_o, idx_qkv);
     return hipGetLastError();
 }
 

@@ -175,6 +175,11 @@ sl_status check_rows(sl_handle* h, const int32_t* ctx, int64_t Tc, const int32_t
 
 }  // namespace
 
+// (k_select.hip)
+hipError_t launch_qkv_index(const int32_t* idx_qk, int64_t n_qk, const int32_t* idx_vo, int64_t n_vo,
+                            int64_t n_rep, int64_t d, int64_t Cq, int64_t Ckv, int32_t* idx_q, int32_t* idx_o,
+                            int32_t* idx_qkv, hipStream_t st);
+
 extern "C" {
 
 const char* sl_version(void) { return "sparselora-gfx950 0.1"; }
@@ -526,6 +531,22 @@ sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t o
     SL_REQUIRE(h, idx && idx_out, "NULL pointer");
     DeviceGuard g(h->device);
     return hip_check(h, launch_offset_index(idx, n, offset, idx_out, h->stream), "offset_index");
+}
+
+sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const int32_t* idx_vo, int64_t n_vo,
+                       int64_t n_kv_heads, int64_t n_rep, int64_t head_dim, int32_t* idx_q, int32_t* idx_o,
+                       int32_t* idx_qkv) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, n_kv_heads >= 1 && n_rep >= 1 && head_dim >= 1, "bad sizes");
+    const int64_t Ckv = n_kv_heads * head_dim, Cq = Ckv * n_rep;
+    SL_REQUIRE(h, n_qk >= 0 && n_vo >= 0 && n_qk <= Ckv && n_vo <= Ckv && Cq + 2 * Ckv <= INT32_MAX,
+               "bad sizes");
+    if (n_qk + n_vo == 0) return SL_OK;
+    SL_REQUIRE(h, idx_qkv && (n_qk == 0 || (idx_qk && idx_q)) && (n_vo == 0 || (idx_vo && idx_o)),
+               "NULL pointer");
+    DeviceGuard g(h->device);
+    return hip_check(h, launch_qkv_index(idx_qk, n_qk, idx_vo, n_vo, n_rep, head_dim, Cq, Ckv, idx_q, idx_o,
+                                         idx_qkv, h->stream), "qkv_index");
 }
 
 // ---------------------------------------------------------------- a6/a7

@@ -221,6 +221,15 @@ def offset_index(idx, offset, C_max, idx_out):
     _check(h, st, "sl_offset_index")
 
 
+def qkv_index(idx_qk, idx_vo, n_kv_heads, n_rep, head_dim, idx_q, idx_o, idx_qkv):
+    """idx_q, idx_o: GQA expansions of idx_qk, idx_vo; idx_qkv: the stacked
+    q|k|v channel list [idx_q | idx_qk + Cq | idx_vo + Cq + Ckv]."""
+    h = handle(_dev(idx_qkv))
+    st = _lib.load().sl_qkv_index(h, _ptr(idx_qk), idx_qk.numel(), _ptr(idx_vo), idx_vo.numel(), n_kv_heads,
+                                  n_rep, head_dim, _ptr(idx_q), _ptr(idx_o), _ptr(idx_qkv))
+    _check(h, st, "sl_qkv_index")
+
+
 def _lora_args(lora):
     """lora = (P fp32 [T, >= r], Bm [C, >= r], r, scale) or None."""
     if lora is None:

@@ -277,6 +277,21 @@ sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
 sl_status sl_offset_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t offset,
                           int64_t C_max, int32_t* idx_out);
 
+/* The three index lists of one attention block's q|k|v and o products in one
+ * call (PG §3.4 "QK projection sparsity" and "VO projection sparsity": a
+ * selection in key/value channel space serves every query head of its group):
+ *   idx_q   = sl_expand_gqa(idx_qk)                    int32[n_qk * n_rep]
+ *   idx_o   = sl_expand_gqa(idx_vo)                    int32[n_vo * n_rep]
+ *   idx_qkv = [idx_q | idx_qk + Cq | idx_vo + Cq + Ckv] int32[n_qk * n_rep + n_qk + n_vo]
+ * with Ckv = n_kv_heads * head_dim, Cq = n_rep * Ckv.  idx_qk, idx_vo: device
+ * int32, ascending, values < Ckv; every output list is ascending and device
+ * memory the caller owns.  n_qk = n_vo = 0 is a no-op; SL_ERR_INVALID for bad
+ * sizes (n > Ckv, Cq + 2 Ckv > INT32_MAX) or NULL pointers of a non-empty
+ * part. */
+sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const int32_t* idx_vo, int64_t n_vo,
+                       int64_t n_kv_heads, int64_t n_rep, int64_t head_dim, int32_t* idx_q, int32_t* idx_o,
+                       int32_t* idx_qkv);
+
 /* ---------------------------------------------------------------- a6/a7: main forward */
 
 /* Sparse main-branch forward (PG §3.4 Algorithm 1 steps 4-5 and "Token

@@ -158,3 +158,26 @@ def test_estimator_bf16_and_f32_inputs_ragged(rng):
             xa = torch.empty(len(rows), kt, dtype=torch.float32, device=DEV)
             ops.svd_estimate(to_dev(x, dtype), to_dev(rows, None), to_dev(np.ascontiguousarray(WA_t.T), "f32"), xa)
             assert np.array_equal(bits(host(xa)), bits(csa.stage1(x, rows, WA_t)))
+
+
+@pytest.mark.parametrize("n_kv,n_rep,d,fq,fv", [(8, 4, 128, 0.5, 0.5), (2, 1, 64, 1.0, 0.25), (4, 2, 32, 0.3, 0.0),
+                                                (1, 8, 16, 0.0, 1.0)])
+def test_qkv_index(n_kv, n_rep, d, fq, fv, rng):
+    """One-call q|k|v index lists: GQA expansions and the stacked list, bit-exact
+    against the oracle's expansion and the stacking offsets."""
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    Ckv = n_kv * d
+    Cq = n_rep * Ckv
+    n_qk, n_vo = int(round(fq * Ckv)), int(round(fv * Ckv))
+    iqk = np.sort(rng.choice(Ckv, n_qk, replace=False)).astype(np.int32)
+    ivo = np.sort(rng.choice(Ckv, n_vo, replace=False)).astype(np.int32)
+    dev = lambda a: torch.from_numpy(a).to(DEV)
+    iq = torch.full((n_qk * n_rep,), -1, dtype=torch.int32, device=DEV)
+    io = torch.full((n_vo * n_rep,), -1, dtype=torch.int32, device=DEV)
+    iqkv = torch.full((n_qk * n_rep + n_qk + n_vo,), -1, dtype=torch.int32, device=DEV)
+    ops.qkv_index(dev(iqk), dev(ivo), n_kv, n_rep, d, iq, io, iqkv)
+    eq, eo = ref.expand_gqa(iqk, n_rep, d), ref.expand_gqa(ivo, n_rep, d)
+    assert np.array_equal(host_i(iq), eq)
+    assert np.array_equal(host_i(io), eo)
+    assert np.array_equal(host_i(iqkv), np.concatenate([eq, iqk + Cq, ivo + Cq + Ckv]))
