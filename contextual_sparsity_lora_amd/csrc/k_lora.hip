@@ -292,6 +292,7 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
     const float* __restrict__ P, int64_t ldp, const bf16_t* __restrict__ B, int64_t ldb, int64_t r,
     float scale, const uint32_t* __restrict__ mask, int beta) {
     constexpr int KS = (R + 31) / 32;     // 32-wide rank steps
+    __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int64_t c0 = (int64_t)blockIdx.x * 128;
     const int64_t t0 = ((int64_t)blockIdx.y * 4 + wid) * FTW;
@@ -348,6 +349,10 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
                 w[q] = pack_bf16x2(scale * v[2 * q], scale * v[2 * q + 1]);
             pb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
         }
+        // whole 128-channel block written without a mask: the 16 x 128 tile
+        // goes through this wave's LDS rows so each output row leaves as 256
+        // contiguous bytes (16 lanes x 16 B) instead of four 64-byte pieces
+        const bool whole = beta == 0 && aligned && c0 + 128 <= C;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             f32x4 acc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
@@ -357,13 +362,20 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
                 for (int e = 0; e < 2; ++e)
                     acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][g][e], pb[ks], acc[e], 0, 0, 0);
             const int64_t c = cl + 32 * g;
-            if (!mv || c >= C) continue;
             float v[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 v[i] = acc[0][i];
                 v[4 + i] = acc[1][i];
             }
+            if (whole) {
+                uint32_t w[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+                *(uint4*)&tile[wid][lane & 15][8 * (lane >> 4) + 32 * g] = make_uint4(w[0], w[1], w[2], w[3]);
+                continue;
+            }
+            if (!mv || c >= C) continue;
             bf16_t* dst = y + row * ldy + c;
             const uint32_t bits = beta ? ((mask[c >> 5] >> (c & 31)) & 0xffu) : 0u;   // c % 8 == 0: one word
             if (beta != 1 && bits == 0u && aligned && c + 8 <= C) {
@@ -374,6 +386,23 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
                     dst[q] = f32_to_bf16(v[q] + (beta == 1 ? bf16_to_f32(dst[q]) : 0.0f));
                 }
             }
+        }
+        if (whole) {
+            // (this wave's own LDS rows: in-order LDS access within the wave)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rr = 4 * j + (lane >> 4);               // tile row: lane rr holds its row number
+                const int64_t orow = __shfl(row, rr, 64);
+                const int ov = __shfl((int)mv, rr, 64);
+                const uint4 d = *(const uint4*)&tile[wid][rr][8 * (lane & 15)];
+                if (ov) *(uint4*)(y + orow * ldy + c0 + 8 * (lane & 15)) = d;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 }
