@@ -74,6 +74,11 @@ class SparseAttnProj:
         self.A_o, self.B_o = A_o.contiguous(), B_o.contiguous()
         self.A_qkvT = torch.empty(self.D, 3 * r, dtype=self.dtype, device=dev)
         self.A_oT = torch.empty(Cq, r, dtype=self.dtype, device=dev)
+        # transposed B copies for the backward's gB steps (rows padded to a
+        # multiple of 8), refreshed with the A transposes in every forward
+        c8 = lambda n: (n + 7) // 8 * 8
+        self.B_bdT = torch.empty(3 * r, c8(self.Cs), dtype=self.dtype, device=dev)
+        self.B_oT = torch.empty(r, c8(self.D), dtype=self.dtype, device=dev)
         cont = lambda w: w.contiguous() if w is not None else None
         self.WA = cont(WA_qkv)                         # [D, 3k] fp32
         self.WB_q, self.WB_k, self.WB_v = (cont(w) for w in (WB_q, WB_k, WB_v))
@@ -182,6 +187,11 @@ class SparseAttnProj:
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
             ev[1].record(self.side)
+            # the backward's transposed LoRA factors (off the main stream)
+            ops.transpose(self.A_qkv, self.A_qkvT)
+            ops.transpose(self.A_o, self.A_oT)
+            ops.transpose(self.B_bd, self.B_bdT[:, :self.Cs])
+            ops.transpose(self.B_o, self.B_oT[:, :self.D])
             if overlap:
                 ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
                                       self.qkv, lora=lora, flags=ops.ONLY_OUT_ROWS)
@@ -225,9 +235,9 @@ class SparseAttnProj:
         r, s = self.r, self.scale
         main, ev = torch.cuda.current_stream(dy_o.device), self._ev
         # gB on the main stream (the dx_o product reads it); dA, dB on the side stream
-        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_o, s, None, dy=dy_o, gB=self.gB_o, D_in=self.Cq)
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_oT, s, None, dy=dy_o, gB=self.gB_o,
+                         D_in=self.Cq, D_out=self.D, r=r)
         ev[3].record(main)
-        ops.transpose(self.A_o, self.A_oT)
         ops.sparse_linear_bwd("in", dy_o, None, self.Wt_o, self.ctx_rows, self.out_rows, self.idx_o,
                               self.dx_o, lora=(self.gB_o, self.A_oT, r, s))
         # (issued after the main-stream product, so the host's time on these
@@ -245,10 +255,9 @@ class SparseAttnProj:
         main, ev = torch.cuda.current_stream(dqkv.device), self._ev
         # gB through the block-diagonal B on the main stream; dA and the
         # per-projection dB on the side stream, next to the dx product
-        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_bd, s, None, dy=dqkv, gB=self.gB_qkv,
-                         D_in=self.D, r=3 * r)
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_bdT, s, None, dy=dqkv, gB=self.gB_qkv,
+                         D_in=self.D, D_out=self.Cs, r=3 * r)
         ev[4].record(main)
-        ops.transpose(self.A_qkv, self.A_qkvT)
         ops.sparse_linear_bwd("out", dqkv, self.W_qkv, self.W_qkvT, self.ctx_rows, self.out_rows,
                               self.idx_qkv, self.dx, lora=(self.gB_qkv, self.A_qkvT, 3 * r, s),
                               w_slice=self.ws_qkv if self._slices else None)

@@ -75,6 +75,11 @@ class SparseFFN:
         self.A_down, self.B_down = A_down.contiguous(), B_down.contiguous()
         self.A_guT = torch.empty(self.D, 2 * r, dtype=self.dtype, device=dev)
         self.A_dT = torch.empty(self.F, r, dtype=self.dtype, device=dev)
+        # transposed B copies for the backward's gB step (rows padded to a
+        # multiple of 8), refreshed with the A transposes in every forward
+        c8 = lambda n: (n + 7) // 8 * 8
+        self.B_dnT = torch.empty(r, c8(self.D), dtype=self.dtype, device=dev)
+        self.B_bdT = torch.empty(2 * r, c8(2 * self.F), dtype=self.dtype, device=dev)
         cont = lambda w: w.contiguous() if w is not None else None
         self.WA = cont(WA_gu)                        # [D, 2k] fp32
         self.WB_gate, self.WB_up = cont(WB_gate), cont(WB_up)
@@ -162,6 +167,11 @@ class SparseFFN:
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
             self._ev[1].record(self.side)
+            # the backward's transposed LoRA factors (off the main stream)
+            ops.transpose(self.A_down, self.A_dT)
+            ops.transpose(self.A_gu, self.A_guT)
+            ops.transpose(self.B_down, self.B_dnT[:, :self.D])
+            ops.transpose(self.B_bd, self.B_bdT[:, :2 * F])
             if overlap:
                 ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
                                       self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
@@ -221,10 +231,9 @@ class SparseFFN:
         main = torch.cuda.current_stream(dy.device)
         # down: LoRA gB (main stream: the dh product reads it); dA and dB on the
         # side stream, overlapping the dh product
-        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_down, s, None, dy=dy, gB=self.gB_dn,
-                         D_in=F, r=r)
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_dnT, s, None, dy=dy, gB=self.gB_dn,
+                         D_in=F, D_out=D, r=r)
         self._ev[0].record(main)
-        ops.transpose(self.A_down, self.A_dT)
         ops.sparse_linear_bwd("in", dy, None, self.Wt_dn, self.ctx_rows, self.out_rows, self.idx,
                               self.dh, lora=(self.gB_dn, self.A_dT, r, s))
         # (issued after the main-stream product: the host's time on these calls
@@ -238,10 +247,9 @@ class SparseFFN:
         ops.swiglu_bwd(self.dh, g, u, dg, du)
         # gate|up: gB for both through the block-diagonal B (main stream); dA
         # and the per-projection dB on the side stream, overlapping the dx product
-        ops.lora_fwd_bwd(ops.LORA_GB, None, None, self.B_bd, s, None, dy=self.dgu, gB=self.gB_gu,
-                         D_in=D, r=2 * r)
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_bdT, s, None, dy=self.dgu,
+                         gB=self.gB_gu, D_in=D, D_out=2 * F, r=2 * r)
         self._ev[1].record(main)
-        ops.transpose(self.A_gu, self.A_guT)
         ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
                               self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s),
                               w_slice=self.ws_gu if self._slices else None)
