@@ -74,3 +74,18 @@ def test_attention_core(case, rng):
         assert mar(host(dq), dq_r) <= tol
         assert mar(host(dk), dk_r) <= tol
     assert mar(host(dv), dv_r) <= tol
+
+
+def test_attention_rejects_unaligned_rows():
+    """Rows that are not 16-byte aligned (q, k, v one column into a stacked
+    buffer) are refused with an error before any launch."""
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    B, S, H, Hkv, d = 1, 16, 2, 2, 32
+    T, Cq, Ckv = B * S, H * d, Hkv * d
+    buf = torch.zeros(T, 1 + Cq + 2 * Ckv, dtype=torch.bfloat16, device=DEV)
+    qd, kd, vd = buf[:, 1:1 + Cq], buf[:, 1 + Cq:1 + Cq + Ckv], buf[:, 1 + Cq + Ckv:]
+    o = torch.empty(T, Cq, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B * H * S, dtype=torch.float32, device=DEV)
+    with pytest.raises(ops.SLError):
+        ops.attention_fwd(qd, kd, vd, B, S, H, Hkv, d, o, lse)
