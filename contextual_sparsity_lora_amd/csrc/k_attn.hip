@@ -245,84 +245,51 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // dS = P (dP - delta) / sqrt(d), delta[q] = sum_c dO[q, c] O[q, c]:
 //   dQ = dS K, dK = dS^T Q, dV = P^T dO, dP = dO V^T.
 
-// dQ: block = (64 queries, head h, sequence b), heaviest query blocks first;
-// wave w owns queries q0 + 16 w .. + 15.  Per step of 64 keys (K plain and
-// transposed, V plain; the next step's loads in flight): S^T = K Q^T and
-// dP^T = V dO^T (Q^T, dO^T fragments in registers), dS^T in registers,
-// dQ^T += K^T dS^T.
+// dQ = dS K from the dS tiles the dK/dV kernel stored (bf16, the values its
+// own products used): block = (64 queries, head h, sequence b), heaviest query
+// blocks first; wave w owns queries q0 + 16 w .. + 15.  Per step of 64 keys,
+// K and the dS tile [keys][queries] are staged transposed (the next step's
+// loads in flight) and dQ^T += K^T dS^T.  dS rows are padded to a multiple of
+// 64 queries; entries above the diagonal of a diagonal tile hold 0.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(
-    const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
-    const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
-    const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
-    bf16_t* __restrict__ dq, int64_t lddq) {
-    constexpr int NC = HD / 32, NU = HD / 16, NT = F2K / 16;
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[F2K][HD + 8];
+__global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(const bf16_t* __restrict__ k, int64_t ldk,
+                                                              const bf16_t* __restrict__ dS, int64_t S,
+                                                              int64_t Sp, int64_t H, int64_t n_rep,
+                                                              bf16_t* __restrict__ dq, int64_t lddq) {
+    constexpr int NU = HD / 16;
     __shared__ __attribute__((aligned(16))) bf16_t Kt[HD][TP64];
-    __shared__ __attribute__((aligned(16))) bf16_t Vs[F2K][HD + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t Dt[FQ][TP64];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / n_rep, t0 = b * S;
     const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * FQ, qw = q0 + 16 * w, qn = qw + cn;
-    const bool qv = qn < S;
-    const float scale = 1.0f / sqrtf((float)HD);
-    bf16x8 qf[NC], gf[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int64_t off = t0 + (qv ? qn : 0);
-        qf[c] = __builtin_bit_cast(bf16x8, gload16(q + off * ldq + h * HD + 32 * c + 8 * grp, qv));
-        gf[c] = __builtin_bit_cast(bf16x8, gload16(dO + off * lddo + h * HD + 32 * c + 8 * grp, qv));
-    }
-    const float L = qv ? lse[(b * H + h) * S + qn] : 0.0f;
-    const float Dl = qv ? delta[(b * H + h) * S + qn] : 0.0f;
+    const bf16_t* dsh = dS + (b * H + h) * S * Sp;
     f32x4 acc[NU];
 #pragma unroll
     for (int u = 0; u < NU; ++u) acc[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
     const int64_t kend = q0 + FQ < S ? q0 + FQ : S;
-    Tile<HD, F2K> tk, tv;
+    Tile<HD, F2K> tk;
+    Tile<FQ, F2K> td;   // rows: keys; columns: this block's queries
     tk.load(k, ldk, t0, 0, S, g * HD);
-    tv.load(v, ldv, t0, 0, S, g * HD);
+    td.load(dsh, Sp, 0, 0, S, q0);
     for (int64_t k0 = 0; k0 < kend; k0 += F2K) {
         __syncthreads();
-        tk.store_plain(Ks);
         tk.store_trans(Kt);
-        tv.store_plain(Vs);
+        td.store_trans(Dt);
         __syncthreads();
         if (k0 + F2K < kend) {
             tk.load(k, ldk, t0, k0 + F2K, S, g * HD);
-            tv.load(v, ldv, t0, k0 + F2K, S, g * HD);
+            td.load(dsh, Sp, 0, k0 + F2K, S, q0);
         }
         if (k0 > qw + 15 || qw >= S) continue;   // wave-uniform: no visible key
-        f32x4 st[NT], dp[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            st[t] = dp[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                st[t] = mfma16(*(const bf16x8*)&Ks[16 * t + cn][8 * ((4 * c + grp) ^ t)], qf[c], st[t]);
-                dp[t] = mfma16(*(const bf16x8*)&Vs[16 * t + cn][8 * ((4 * c + grp) ^ t)], gf[c], dp[t]);
-            }
-        }
-        float ds[4 * NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t key = k0 + 16 * t + 4 * grp + i;
-                const float p = (qv && key <= qn && key < S) ? expf(st[t][i] * scale - L) : 0.0f;
-                ds[4 * t + i] = p * (dp[t][i] - Dl) * scale;
-            }
-#pragma unroll
-        for (int hk = 0; hk < NT / 2; ++hk) {
-            float dh[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dh[e] = ds[8 * hk + e];
-            const bf16x8 db = pack8(dh);
+        for (int hk = 0; hk < F2K / 32; ++hk) {
+            const bf16x8 db = lds_pair4(&Dt[16 * w + cn][32 * hk], 4 * grp, 16 + 4 * grp);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
                 acc[u] = mfma16(lds_pair4(&Kt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), db, acc[u]);
         }
     }
-    if (!qv) return;
+    if (qn >= S) return;
     bf16_t* op = dq + (t0 + qn) * lddq + h * HD + 4 * grp;
 #pragma unroll
     for (int u = 0; u < NU; ++u)
@@ -340,7 +307,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const bf16_t* __restrict__ q, int64_t ldq, const bf16_t* __restrict__ k, int64_t ldk,
     const bf16_t* __restrict__ v, int64_t ldv, const bf16_t* __restrict__ dO, int64_t lddo,
     const float* __restrict__ lse, const float* __restrict__ delta, int64_t S, int64_t H, int64_t n_rep,
-    bf16_t* __restrict__ dk, int64_t lddk, bf16_t* __restrict__ dv, int64_t lddv) {
+    bf16_t* __restrict__ dk, int64_t lddk, bf16_t* __restrict__ dv, int64_t lddv, bf16_t* __restrict__ dS,
+    int64_t Sp) {
     constexpr int NC = HD / 32, NU = HD / 16, NT = F2K / 16;
     __shared__ __attribute__((aligned(16))) bf16_t Qs[F2K][HD + 8];
     __shared__ __attribute__((aligned(16))) bf16_t Qt[HD][TP64];
@@ -412,6 +380,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                     ds[4 * tt + i] = pv * (dp[t][i] - Ds[j]) * scale;
                 }
             const bf16x8 pb = pack8(p), db = pack8(ds);
+            if (kv) {
+                // dS[b, h][key][query]: the 4 consecutive queries of each 16-query tile
+                const uint4 dw = __builtin_bit_cast(uint4, db);
+                bf16_t* dr = dS + ((b * H + g * n_rep + sidx / nsi) * S + kn) * Sp + i0 + 32 * hk + 4 * grp;
+                *(uint2*)dr = make_uint2(dw.x, dw.y);
+                *(uint2*)(dr + 16) = make_uint2(dw.z, dw.w);
+            }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
                 dva[u] = mfma16(lds_pair4(&Gt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), pb, dva[u]);
@@ -464,21 +439,24 @@ bool attn_mfma_bwd_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int
            a8(dk, lddk) && a8(dv, lddv);
 }
 
+size_t attn_bwd_ds_bytes(int64_t B, int64_t S, int64_t H) {
+    return (size_t)B * H * S * (size_t)(ceil_div(S, FQ) * FQ) * sizeof(bf16_t);
+}
+
 hipError_t launch_attn_bwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                                 int64_t ldv, const void* dO, int64_t lddo, const float* lse, const float* delta,
                                 int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq,
-                                void* dk, int64_t lddk, void* dv, int64_t lddv, hipStream_t st) {
+                                void* dk, int64_t lddk, void* dv, int64_t lddv, void* ds, hipStream_t st) {
     if (B <= 0 || S <= 0) return hipSuccess;
     const dim3 gq((unsigned)ceil_div(S, FQ), (unsigned)H, (unsigned)B);
     const dim3 gk((unsigned)ceil_div(S, FQ), (unsigned)Hkv, (unsigned)B);
-    const int64_t n_rep = H / Hkv;
+    const int64_t n_rep = H / Hkv, Sp = ceil_div(S, FQ) * FQ;
 #define AB(HDV)                                                                                               \
     hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<HDV>), gk, dim3(256), 0, st, (const bf16_t*)q, ldq,             \
                        (const bf16_t*)k, ldk, (const bf16_t*)v, ldv, (const bf16_t*)dO, lddo, lse, delta, S, H, \
-                       n_rep, (bf16_t*)dk, lddk, (bf16_t*)dv, lddv);                                            \
-    hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<HDV>), gq, dim3(256), 0, st, (const bf16_t*)q, ldq,              \
-                       (const bf16_t*)k, ldk, (const bf16_t*)v, ldv, (const bf16_t*)dO, lddo, lse, delta, S, H, \
-                       n_rep, (bf16_t*)dq, lddq)
+                       n_rep, (bf16_t*)dk, lddk, (bf16_t*)dv, lddv, (bf16_t*)ds, Sp);                          \
+    hipLaunchKernelGGL((attn_bwd_q_mfma_kernel<HDV>), gq, dim3(256), 0, st, (const bf16_t*)k, ldk,              \
+                       (const bf16_t*)ds, S, Sp, H, n_rep, (bf16_t*)dq, lddq)
     if (hd == 32) { AB(32); }
     else if (hd == 64) { AB(64); }
     else if (hd == 128) { AB(128); }

@@ -400,7 +400,7 @@ bool attn_mfma_bwd_ok(int64_t hd, const void* q, int64_t ldq, const void* k, int
 hipError_t launch_attn_bwd_mfma(const void* q, int64_t ldq, const void* k, int64_t ldk, const void* v,
                                 int64_t ldv, const void* dO, int64_t lddo, const float* lse, const float* delta,
                                 int64_t B, int64_t S, int64_t H, int64_t Hkv, int64_t hd, void* dq, int64_t lddq,
-                                void* dk, int64_t lddk, void* dv, int64_t lddv, hipStream_t st);
+                                void* dk, int64_t lddk, void* dv, int64_t lddv, void* ds, hipStream_t st);
 
 hipError_t launch_attn_fwd(bool bf16, const void* q, int64_t ldq, const void* k, int64_t ldk,
                            const void* v, int64_t ldv, int64_t B, int64_t S, int64_t H, int64_t Hkv,
@@ -431,8 +431,11 @@ hipError_t launch_attn_bwd(bool bf16, const void* q, int64_t ldq, const void* k,
                                               (const bf16_t*)o, ldo, (const bf16_t*)dO, lddo, S, H, delta);)
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        // the caller's workspace holds delta, then (at the next 256-byte
+        // boundary) the bf16 dS tiles of the matrix-core backward
+        void* ds = (char*)delta + (((size_t)(B * H * S) * sizeof(float) + 255) / 256) * 256;
         return launch_attn_bwd_mfma(q, ldq, k, ldk, v, ldv, dO, lddo, lse, delta, B, S, H, Hkv, hd, dq, lddq, dk,
-                                    lddk, dv, lddv, st);
+                                    lddk, dv, lddv, ds, st);
     }
     SL_DISPATCH_HD(hd, SL_DISPATCH_T(bf16,
         hipLaunchKernelGGL((attn_delta_kernel<TT, HDV>), gq, dim3(256), 0, st, (const TT*)o, ldo,

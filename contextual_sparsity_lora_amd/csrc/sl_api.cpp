@@ -175,6 +175,9 @@ sl_status check_rows(sl_handle* h, const int32_t* ctx, int64_t Tc, const int32_t
 
 }  // namespace
 
+// (k_attn.hip) bytes of the bf16 dS tiles the matrix-core attention backward keeps
+size_t attn_bwd_ds_bytes(int64_t B, int64_t S, int64_t H);
+
 // (k_select.hip)
 hipError_t launch_qkv_index(const int32_t* idx_qk, int64_t n_qk, const int32_t* idx_vo, int64_t n_vo,
                             int64_t n_rep, int64_t d, int64_t Cq, int64_t Ckv, int32_t* idx_q, int32_t* idx_o,
@@ -1235,7 +1238,9 @@ sl_status sl_attention_bwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq
     SL_CHECK(check_matrix(h, dv, lddv, Ckv, dt, "dv"));
     SL_REQUIRE(h, lse != nullptr, "lse is NULL");
     DeviceGuard gd(h->device);
-    SL_CHECK(ensure_ws(h, round_up((size_t)(batch * n_heads * seq) * 4, 256)));
+    // delta (fp32 per query row), then for bf16 the dS tiles of the backward
+    SL_CHECK(ensure_ws(h, round_up((size_t)(batch * n_heads * seq) * 4, 256) +
+                              (dt == SL_BF16 ? attn_bwd_ds_bytes(batch, seq, n_heads) : 0)));
     const double pairs = (double)batch * n_heads * seq * (seq + 1) / 2.0;
     Timed tm(h, K_ATTN, 10.0 * pairs * head_dim, 0);
     return hip_check(h, launch_attn_bwd(dt == SL_BF16, q, ldq, k, ldk, v, ldv, o, ldo, dout, lddout,
