@@ -169,55 +169,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             tk.load(k, ldk, t0, k0 + F2K, S, g * HD);
             tv.load(v, ldv, t0, k0 + F2K, S, g * HD);
         }
+        // wave-uniform: which of the two query tiles see a key of this step
+        bool vis[2];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            if (k0 > qw + 16 * qt + 15 || qw + 16 * qt >= S) continue;   // wave-uniform: nothing visible
-            f32x4 st[4];
+        for (int qt = 0; qt < 2; ++qt) vis[qt] = !(k0 > qw + 16 * qt + 15 || qw + 16 * qt >= S);
+        if (vis[0] || vis[1]) {
+            // S^T for both query tiles, each K fragment read from LDS once
+            f32x4 st[2][4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                st[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                st[0][t] = st[1][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < NC; ++c)
-                    st[t] = mfma16(*(const bf16x8*)&Ks[buf][16 * t + cn][8 * ((4 * c + grp) ^ t)], qf[qt][c], st[t]);
-            }
-            float p[16], mloc = -INFINITY;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t key = k0 + 16 * t + 4 * grp + i;
-                    const float sv = (key <= qn[qt] && key < S) ? st[t][i] * scale : -INFINITY;
-                    p[4 * t + i] = sv;
-                    mloc = fmaxf(mloc, sv);
+                for (int c = 0; c < NC; ++c) {
+                    const bf16x8 kf = *(const bf16x8*)&Ks[buf][16 * t + cn][8 * ((4 * c + grp) ^ t)];
+                    st[0][t] = mfma16(kf, qf[0][c], st[0][t]);
+                    st[1][t] = mfma16(kf, qf[1][c], st[1][t]);
                 }
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float mnew = fmaxf(m[qt], mloc);
-            const float mu = mnew == -INFINITY ? 0.0f : mnew;   // no visible key yet: everything stays 0
-            const float corr = expf(m[qt] - mu);
-            float ps = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                p[e] = expf(p[e] - mu);
-                ps += p[e];
             }
-            lsum[qt] = lsum[qt] * corr + ps;
-            m[qt] = mnew;
+            bf16x8 pb[2][2];
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
+            for (int qt = 0; qt < 2; ++qt) {
+                float p[16], mloc = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[qt][u][i] *= corr;
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int hk = 0; hk < 2; ++hk) {
-                float ph[8];
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t key = k0 + 16 * t + 4 * grp + i;
+                        const float sv = (key <= qn[qt] && key < S) ? st[qt][t][i] * scale : -INFINITY;
+                        p[4 * t + i] = sv;
+                        mloc = fmaxf(mloc, sv);
+                    }
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+                mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+                const float mnew = fmaxf(m[qt], mloc);
+                const float mu = mnew == -INFINITY ? 0.0f : mnew;   // no visible key yet: everything stays 0
+                const float corr = expf(m[qt] - mu);
+                float ps = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ph[e] = p[8 * hk + e];
-                const bf16x8 pb = pack8(ph);
+                for (int e = 0; e < 16; ++e) {
+                    p[e] = expf(p[e] - mu);
+                    ps += p[e];
+                }
+                lsum[qt] = lsum[qt] * corr + ps;
+                m[qt] = mnew;
 #pragma unroll
                 for (int u = 0; u < NU; ++u)
-                    acc[qt][u] = mfma16(lds_pair4(&Vt[buf][16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), pb,
-                                        acc[qt][u]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[qt][u][i] *= corr;
+#pragma unroll
+                for (int hk = 0; hk < 2; ++hk) {
+                    float ph[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ph[e] = p[8 * hk + e];
+                    pb[qt][hk] = pack8(ph);
+                }
             }
+            // O^T += V^T P^T for both query tiles, each V^T fragment read once
+            // (a tile with no visible key has P = 0 and corr = 1: unchanged)
+#pragma unroll
+            for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    const bf16x8 vf = lds_pair4(&Vt[buf][16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp);
+                    acc[0][u] = mfma16(vf, pb[0][hk], acc[0][u]);
+                    acc[1][u] = mfma16(vf, pb[1][hk], acc[1][u]);
+                }
         }
         if (s + 1 < nsteps) {
             tk.store_plain(Ks[buf ^ 1]);
