@@ -260,6 +260,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 // With P = exp(s / sqrt(d) - lse) recomputed per tile and
 // dS = P (dP - delta) / sqrt(d), delta[q] = sum_c dO[q, c] O[q, c]:
 //   dQ = dS K, dK = dS^T Q, dV = P^T dO, dP = dO V^T.
+// The dK/dV kernel (launched first) recomputes S and dP once per tile, and
+// stores the bf16 dS it multiplies; the dQ kernel then needs one product per
+// tile.  (This file's forward and backward kernels are reached for bf16; the
+// fp32 path has kernels of its own.)
 
 // dQ = dS K from the dS tiles the dK/dV kernel stored (bf16, the values its
 // own products used): block = (64 queries, head h, sequence b), heaviest query
