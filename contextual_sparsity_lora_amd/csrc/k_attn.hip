@@ -136,7 +136,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, grp = lane >> 4, cn = lane & 15;
     const int64_t b = blockIdx.z, h = blockIdx.y, g = h / n_rep, t0 = b * S;
     const int64_t q0 = (int64_t)(gridDim.x - 1 - blockIdx.x) * F2Q, qw = q0 + 32 * w;
-    const float scale = 1.0f / sqrtf((float)HD);
+    // scores in base-2 units (log2 e folded into the scale): the softmax's
+    // exponentials are single v_exp_f32 instructions
+    const float sl2 = 1.4426950408889634f / sqrtf((float)HD);
     bf16x8 qf[2][NC];
     int64_t qn[2];
 #pragma unroll
@@ -190,12 +192,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 float p[16], mloc = -INFINITY;
+                // wave-uniform: every key of the step precedes the tile's first
+                // query and lies inside the sequence, so nothing is masked
+                const bool whole = k0 + F2K - 1 <= qw + 16 * qt && k0 + F2K <= S;
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int64_t key = k0 + 16 * t + 4 * grp + i;
-                        const float sv = (key <= qn[qt] && key < S) ? st[qt][t][i] * scale : -INFINITY;
+                        const float sv = (whole || (key <= qn[qt] && key < S)) ? st[qt][t][i] * sl2 : -INFINITY;
                         p[4 * t + i] = sv;
                         mloc = fmaxf(mloc, sv);
                     }
@@ -203,11 +208,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
                 const float mnew = fmaxf(m[qt], mloc);
                 const float mu = mnew == -INFINITY ? 0.0f : mnew;   // no visible key yet: everything stays 0
-                const float corr = expf(m[qt] - mu);
+                const float corr = __builtin_amdgcn_exp2f(m[qt] - mu);
                 float ps = 0.0f;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    p[e] = expf(p[e] - mu);
+                    p[e] = __builtin_amdgcn_exp2f(p[e] - mu);
                     ps += p[e];
                 }
                 lsum[qt] = lsum[qt] * corr + ps;
@@ -252,7 +257,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         for (int u = 0; u < NU; ++u)
             *(uint2*)(op + 16 * u) = make_uint2(pack_bf16x2(acc[qt][u][0] * inv, acc[qt][u][1] * inv),
                                                 pack_bf16x2(acc[qt][u][2] * inv, acc[qt][u][3] * inv));
-        if (grp == 0) lse[(b * H + h) * S + qn[qt]] = m[qt] + logf(l);
+        // natural-log units for the backward: (m + log2 l) ln 2
+        if (grp == 0) lse[(b * H + h) * S + qn[qt]] = (m[qt] + log2f(l)) * 0.6931471805599453f;
     }
 }
 
@@ -339,7 +345,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int64_t b = blockIdx.z, g = blockIdx.y, t0 = b * S;
     const int64_t k0 = (int64_t)blockIdx.x * FQ, kw = k0 + 16 * w, kn = kw + cn;
     const bool kv = kn < S;
-    const float scale = 1.0f / sqrtf((float)HD);
+    const float scale = 1.0f / sqrtf((float)HD), sl2 = 1.4426950408889634f * scale;
     bf16x8 kf[NC], vf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -360,7 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         tg.load(dO, lddo, t0, i0, S, h * HD);
         if (threadIdx.x < F2K) {
             const int64_t qi = i0 + threadIdx.x;
-            lr = qi < S ? lse[(b * H + h) * S + qi] : 0.0f;
+            lr = qi < S ? lse[(b * H + h) * S + qi] * 1.4426950408889634f : 0.0f;   // base 2
             dr = qi < S ? delta[(b * H + h) * S + qi] : 0.0f;
         }
     };
@@ -386,6 +392,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 dp[t] = mfma16(*(const bf16x8*)&Gs[16 * t + cn][8 * ((4 * c + grp) ^ t)], vf[c], dp[t]);
             }
         }
+        // wave-uniform: every query of the step follows the wave's keys and
+        // both lie inside the sequence, so nothing is masked
+        const bool whole = i0 >= kw + 15 && i0 + F2K <= S && kw + 16 <= S;
 #pragma unroll
         for (int hk = 0; hk < NT / 2; ++hk) {
             float p[8], ds[8];
@@ -395,7 +404,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
                 for (int i = 0; i < 4; ++i) {
                     const int t = 2 * hk + tt, j = 16 * t + 4 * grp + i;
                     const int64_t qi = i0 + j;
-                    const float pv = (kv && qi < S && kn <= qi) ? expf(st[t][i] * scale - Ls[j]) : 0.0f;
+                    const float pv = (whole || (kv && qi < S && kn <= qi))
+                                         ? __builtin_amdgcn_exp2f(st[t][i] * sl2 - Ls[j]) : 0.0f;
                     p[4 * tt + i] = pv;
                     ds[4 * tt + i] = pv * (dp[t][i] - Ds[j]) * scale;
                 }
