@@ -550,8 +550,11 @@ sl_status sl_attention_fwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq
                            int64_t ldo, float* lse);
 /* Gradients of sl_attention_fwd for upstream dout (softmax probabilities
  * recomputed from lse): dq, and dk, dv summed over the query heads that read
- * each key/value head.  Uses batch*n_heads*seq*4 bytes of the handle's
- * workspace. */
+ * each key/value head.  Uses the handle's workspace: batch*n_heads*seq*4
+ * bytes (per-row softmax terms) rounded up to 256, plus for bf16
+ * batch*n_heads*seq*ceil64(seq)*2 bytes (the dS tiles handed from the dK/dV
+ * pass to the dQ pass; 1 GiB at batch 4, 32 heads, seq 2048) -- reserve that
+ * much with sl_reserve_workspace to keep the call allocation-free. */
 sl_status sl_attention_bwd(sl_handle* h, sl_dtype dt, const void* q, int64_t ldq, const void* k,
                            int64_t ldk, const void* v, int64_t ldv, const void* o, int64_t ldo,
                            const void* dout, int64_t lddout, const float* lse, int64_t batch,
