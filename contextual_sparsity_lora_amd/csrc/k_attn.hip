@@ -37,10 +37,15 @@ __device__ __forceinline__ bf16x8 pack8(const float (&v)[8]) {
     return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
 }
 
-// 8 bf16 of one LDS row: two 4-element runs (the relabelled K index)
-__device__ __forceinline__ bf16x8 lds_pair4(const bf16_t* row, int a0, int a1) {
-    const uint2 x = *(const uint2*)(row + a0), y = *(const uint2*)(row + a1);
-    return __builtin_bit_cast(bf16x8, make_uint4(x.x, x.y, y.x, y.y));
+// Transposed tiles keep each 32-row half in the products' relabelled K order:
+// row quad q (rows 4 q .. 4 q + 3) of a half sits at column 8 (q % 4) +
+// 4 (q / 4), so lane group g's eight K entries (rows 4 g .. + 3 and
+// 16 + 4 g .. + 3) are one contiguous 16-byte run at column 8 g.
+__device__ __forceinline__ int kpos(int rq) { return 32 * (rq >> 3) + 8 * (rq & 3) + 4 * ((rq >> 2) & 1); }
+
+// the relabelled 8 K entries of lane group g in half hk of a transposed row
+__device__ __forceinline__ bf16x8 lds_k8(const bf16_t* row, int hk, int g) {
+    return *(const bf16x8*)(row + 32 * hk + 8 * g);
 }
 
 __device__ __forceinline__ uint4 gload16(const bf16_t* p, bool ok) {
@@ -102,8 +107,8 @@ struct Tile {
                 // column 8 ci + 2 w: low halves; column 8 ci + 2 w + 1: high halves
                 const uint2 lo = make_uint2((x0[w] & 0xffffu) | (x1[w] << 16), (x2[w] & 0xffffu) | (x3[w] << 16));
                 const uint2 hi = make_uint2((x0[w] >> 16) | (x1[w] & 0xffff0000u), (x2[w] >> 16) | (x3[w] & 0xffff0000u));
-                *(uint2*)&tr[8 * ci + 2 * w][4 * rq] = lo;
-                *(uint2*)&tr[8 * ci + 2 * w + 1][4 * rq] = hi;
+                *(uint2*)&tr[8 * ci + 2 * w][kpos(rq)] = lo;
+                *(uint2*)&tr[8 * ci + 2 * w + 1][kpos(rq)] = hi;
             }
         }
     }
@@ -235,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
                 for (int u = 0; u < NU; ++u) {
-                    const bf16x8 vf = lds_pair4(&Vt[buf][16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp);
+                    const bf16x8 vf = lds_k8(Vt[buf][16 * u + cn], hk, grp);
                     acc[0][u] = mfma16(vf, pb[0][hk], acc[0][u]);
                     acc[1][u] = mfma16(vf, pb[1][hk], acc[1][u]);
                 }
@@ -309,10 +314,10 @@ __global__ __launch_bounds__(256) void attn_bwd_q_mfma_kernel(const bf16_t* __re
         if (k0 > qw + 15 || qw >= S) continue;   // wave-uniform: no visible key
 #pragma unroll
         for (int hk = 0; hk < F2K / 32; ++hk) {
-            const bf16x8 db = lds_pair4(&Dt[16 * w + cn][32 * hk], 4 * grp, 16 + 4 * grp);
+            const bf16x8 db = lds_k8(Dt[16 * w + cn], hk, grp);
 #pragma unroll
             for (int u = 0; u < NU; ++u)
-                acc[u] = mfma16(lds_pair4(&Kt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), db, acc[u]);
+                acc[u] = mfma16(lds_k8(Kt[16 * u + cn], hk, grp), db, acc[u]);
         }
     }
     if (qn >= S) return;
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
 #pragma unroll
             for (int u = 0; u < NU; ++u) {
-                dva[u] = mfma16(lds_pair4(&Gt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), pb, dva[u]);
-                dka[u] = mfma16(lds_pair4(&Qt[16 * u + cn][32 * hk], 4 * grp, 16 + 4 * grp), db, dka[u]);
+                dva[u] = mfma16(lds_k8(Gt[16 * u + cn], hk, grp), pb, dva[u]);
+                dka[u] = mfma16(lds_k8(Qt[16 * u + cn], hk, grp), db, dka[u]);
             }
         }
     }
