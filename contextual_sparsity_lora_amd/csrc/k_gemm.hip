@@ -136,7 +136,8 @@ __device__ __forceinline__ void gemm_lora_term(const GemmProblem& P, f32x16 (&ac
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int64_t n = n0 + wn * WTN + j * 32 + (lane & 31);
-            const int64_t cn = n < N ? (P.c_cols ? (int64_t)P.c_cols[n] : n) : -1;
+            const int32_t* lmap = P.l_cols ? P.l_cols : P.c_cols;
+            const int64_t cn = n < N ? (lmap ? (int64_t)lmap[n] : n) : -1;
             bcol[j] = cn >= 0 ? lB + cn * P.ldlB : nullptr;
         }
         for (int kk = 0; kk < lr; kk += 16) {
@@ -730,9 +731,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_fixup_kernel(GemmArgs 
 // B rows 256-511) of BKS bf16, i.e. CPR 16-byte chunks per row.  One load
 // instruction of a wave fills a 1 KB slab with lane i at byte 16 i, so lane i
 // fetches row i / CPR of the slab and the k-chunk that the row swizzle puts at
-// position i % CPR: chunk c of row R sits at position c ^ ((R / (8 / CPR)) % CPR),
-// which keeps the MFMA fragment reads (8 lanes = 8 consecutive rows, same chunk)
-// free of bank conflicts.  The stages are separate LDS arrays and the K loop is
+// position i % CPR: chunk c of row R sits at position c ^ ((R / (16 / CPR)) % CPR),
+// so that 16 consecutive rows (the lanes one LDS cycle of a 16-byte fragment
+// read serves) hit 16 different 16-byte bank groups of the 256-byte bank row.  The stages are separate LDS arrays and the K loop is
 // unrolled by NST so that every read names its stage.  Step t issues the loads
 // of tile t + NST - 1 into the stage of tile t - 1, multiplies tile t, waits
 // for this wave's loads of tile t + 1 and ends with the one barrier of the step
@@ -787,7 +788,7 @@ __device__ __forceinline__ void nt5_sched_post() {
     }
 }
 
-template <int WGM, int WGN, int BKS, int NST>
+template <int WGM, int WGN, int BKS, int NST, bool PART = false>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args) {
     constexpr int BM = 256, BN = 256;
     constexpr int NW = WGM * WGN;
@@ -805,7 +806,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     __shared__ __attribute__((aligned(16))) bf16_t s2[NST == 4 ? SZ : 8];
     __shared__ __attribute__((aligned(16))) bf16_t s3[NST == 4 ? SZ : 8];
 
-    const int L = xcd_remap(blockIdx.x, gridDim.x);
+    // PART: block u is K-chunk u % sks of tail tile dp + u / sks (split tail,
+    // as in the v3 kernel); else whole tiles
+    const int u = PART ? (int)blockIdx.x : 0;
+    const int sk1 = args.sks > 1 ? args.sks : 1;
+    const int L = PART ? __builtin_amdgcn_readfirstlane(args.dp + u / sk1) : xcd_remap(blockIdx.x, gridDim.x);
+    const int qch = PART ? __builtin_amdgcn_readfirstlane(u % sk1) : 0;
     GemmProblem P;
     int t, tiles_m;
     pick_problem(args, L, P, t, tiles_m);
@@ -818,7 +824,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
 
     // loads: slab q = wid + NW d holds rows (1024 / (2 BKS)) q ..; lane i: row i / CPR of it
     constexpr int SR = 1024 / (2 * BKS);         // rows per slab
-    const int ck = (lane % CPR) ^ (((lane / CPR) / (8 / CPR)) % CPR);   // k-chunk this lane fetches
+    // k-chunk this lane fetches: (stage row / (16 / CPR)) mod CPR does not depend
+    // on the slab's d (the slabs of one wave are NW apart, 16 NW / (16 / CPR) rows)
+    const int ck = (lane % CPR) ^ (((SR * wid + lane / CPR) / (16 / CPR)) % CPR);
     uint32_t goff[DPT];
 #pragma unroll
     for (int d = 0; d < DPT; ++d) {
@@ -833,10 +841,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
         }
     }
     const rsrc_t ra = make_rsrc(P.A), rb = make_rsrc(P.B);
-    auto dma = [&](bf16_t* st, int kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kt, K, ck, wid, goff); };
+    // K steps of this block: [kb, kb + nk), nk a whole number of stage rotations
+    // (steps past K load zeros); a PART chunk covers kc steps of the tile
+    const int nk_all = (int)((K + BKS - 1) / BKS);
+    int kb = 0, nk = (nk_all + NST - 1) / NST * NST;
+    if (PART) {
+        const int kc = __builtin_amdgcn_readfirstlane(((nk_all + sk1 - 1) / sk1 + NST - 1) / NST * NST);
+        kb = qch * kc;
+        const int rest = nk_all - kb;
+        nk = rest <= 0 ? 0 : (rest < kc ? (rest + NST - 1) / NST * NST : kc);
+    }
+    auto dma = [&](bf16_t* st, int kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kb + kt, K, ck, wid, goff); };
 
     // fragment reads: row R = base + lane % 32 (base a multiple of 32), chunk 2 ks + lane / 32
-    const int swz = ((lane & 31) / (8 / CPR)) % CPR;
+    const int swz = ((lane & 31) / (16 / CPR)) % CPR;
     const int arow = (wm * WTM + (lane & 31)) * BKS;
     const int brow = (256 + wn * WTN + (lane & 31)) * BKS;
 
@@ -868,9 +886,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
     };
 
-    // K steps rounded up to whole stage rotations (no early exit: steps past K
-    // load zeros through the out-of-range offset); K = 0 runs no step
-    const int nk = (int)((K + BKS * NST - 1) / (BKS * NST)) * NST;
     constexpr int INFL = (NST - 2) * DPT;         // this wave's loads allowed in flight at a step's end
     dma(s0, 0);
     if (NST == 4) {
@@ -907,6 +922,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     }
 #undef NT5_STEP
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));     // the stages are reused below
+    if (PART) {
+        // raw fp32 partial in the accumulator layout (as the v3 kernel's tail chunks)
+        const rsrc_t rw = make_rsrc(args.skws + (size_t)u * BM * BN + (size_t)wid * FM * FN * 16 * 64);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const uint4 d = make_uint4(__float_as_uint(acc[i][j][4 * g]), __float_as_uint(acc[i][j][4 * g + 1]),
+                                               __float_as_uint(acc[i][j][4 * g + 2]), __float_as_uint(acc[i][j][4 * g + 3]));
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned int, d),
+                                                           rw, lane * 16, ((i * FN + j) * 4 + g) * 1024, 0);
+                }
+        return;
+    }
     gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
     lds_f32* csr[2];
     csr[0] = (lds_f32*)s0;
@@ -1121,11 +1152,34 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, fl
 }
 
 template <int WGM, int WGN, int BKS, int NST>
-hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st) {
+hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st, float* skws = nullptr,
+                      size_t skws_floats = 0, int ncu = 256) {
     GemmArgs a = make_args(probs, nprob, 256, 256);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
-    hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN, BKS, NST>), dim3(total), dim3(64 * WGM * WGN), 0, st, a);
+    // fixup launch: its store epilogue uses WGM row groups of 32 x (BN + 4) fp32
+    const size_t fix_lds = (size_t)WGM * 32 * (256 + 4) * sizeof(float);
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_nt_fixup_kernel<256, 256, WGM, WGN>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)fix_lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    int dp = total;
+    int sks = skws ? split_tail_plan(a, ncu, dp) : 0;
+    if (sks && (size_t)(total - dp) * sks * 256 * 256 > skws_floats) sks = 0, dp = total;
+    a.dp = dp;
+    a.sks = sks;
+    a.skws = skws;
+    if (dp > 0)
+        hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN, BKS, NST, false>), dim3(dp), dim3(64 * WGM * WGN), 0, st, a);
+    if (sks) {
+        hipLaunchKernelGGL((gemm_nt5_kernel<WGM, WGN, BKS, NST, true>), dim3((total - dp) * sks),
+                           dim3(64 * WGM * WGN), 0, st, a);
+        hipLaunchKernelGGL((gemm_nt_fixup_kernel<256, 256, WGM, WGN>), dim3(total - dp), dim3(64 * WGM * WGN),
+                           fix_lds, st, a);
+    }
     return hipGetLastError();
 }
 
@@ -1157,7 +1211,7 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
                             size_t skws_floats, int ncu) {
     // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
     const char* env = getenv("SL_GEMM_CFG");
-    int cfg = env ? atoi(env) : 10;
+    int cfg = env ? atoi(env) : 31;
     if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {
         switch (cfg) {
             case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
@@ -1167,9 +1221,11 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
             case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st, nullptr, 0, ncu);
             case 20: return launch_nt5<2, 4, 32, 4>(probs, nprob, st);
             case 21: return launch_nt5<2, 2, 32, 4>(probs, nprob, st);
+            case 31: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, skws, skws_floats, ncu);
+            case 33: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, skws, skws_floats, ncu);
             case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st);
             case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st);
-            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
+            default: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, skws, skws_floats, ncu);
         }
     }
     if (cfg >= 10) cfg = 2;

@@ -407,6 +407,155 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
     }
 }
 
+// ---------------------------------------------------------------- merge of a compact product
+// y[rows[m], c] = Yc[m, j] for the selected channels c = idx[j] (the context
+// rows' product stored compactly, one row per listed row, one column per
+// selected channel), and s * P[rows[m], :] . B[c, :] (0 without a rank-r term)
+// for every other channel.  Same tiling and matrix-core rank-r product as the
+// fill above; the wave's 16 x 128 tile goes to its LDS rows, the selected
+// channels of the 128-channel block (idx[j0 .. j1): one contiguous run of each
+// compact row, since idx is ascending) overwrite their slots, and each row
+// leaves as 256 contiguous bytes.  Every element of the listed rows is written
+// exactly once, with 16-byte stores.
+__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* __restrict__ a, int64_t n, int64_t v) {
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (a[mid] < v) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+template <int R>
+__global__ __launch_bounds__(256) void lora_merge_rows_kernel(
+    bf16_t* __restrict__ y, int64_t ldy, const int32_t* __restrict__ rows, int64_t nrows, int64_t C,
+    const float* __restrict__ P, int64_t ldp, const bf16_t* __restrict__ B, int64_t ldb, int64_t r,
+    float scale, const bf16_t* __restrict__ Yc, int64_t ldyc, const int32_t* __restrict__ idx, int64_t n) {
+    constexpr int KS = (R + 31) / 32;     // 32-wide rank steps
+    __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int64_t c0 = (int64_t)blockIdx.x * 128;
+    const int64_t t0 = ((int64_t)blockIdx.y * 4 + wid) * FTW;
+    const int kl = 8 * (lane >> 4);
+    const bool lora = P != nullptr;
+    const bool bvec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
+    const bool pvec = (ldp % 4 == 0) && (((uintptr_t)P & 15) == 0);
+    bf16x8 wa[KS][4][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int m = lane & 15;
+                const int64_t c = c0 + 32 * g + 8 * (m >> 2) + 4 * e + (m & 3);
+                const int k = 32 * ks + kl;
+                uint4 u = make_uint4(0u, 0u, 0u, 0u);
+                if (lora && c < C) {
+                    const bf16_t* br = B + c * ldb;
+                    if (bvec && k + 8 <= r) {
+                        u = *(const uint4*)(br + k);
+                    } else {
+                        uint32_t w[4] = {0u, 0u, 0u, 0u};
+                        for (int q = 0; q < 8; ++q)
+                            if (k + q < r) w[q >> 1] |= (uint32_t)br[k + q] << ((q & 1) * 16);
+                        u = make_uint4(w[0], w[1], w[2], w[3]);
+                    }
+                }
+                wa[ks][g][e] = __builtin_bit_cast(bf16x8, u);
+            }
+    // the block's selected channels: idx[j0 .. j1), at most 128 of them; lane
+    // holds entries j0 + lane and j0 + 64 + lane (slot in the block, or -1)
+    const int64_t j0 = lower_bound_i32(idx, n, c0);
+    const int64_t j1 = lower_bound_i32(idx, n, c0 + 128);
+    const int sl0 = j0 + lane < j1 ? (int)(idx[j0 + lane] - c0) : -1;
+    const int sl1 = j0 + 64 + lane < j1 ? (int)(idx[j0 + 64 + lane] - c0) : -1;
+    const bool aligned = (ldy % 8 == 0) && (((uintptr_t)y & 15) == 0);
+    const bool whole = aligned && c0 + 128 <= C;
+    for (int64_t tg = t0; tg < t0 + FTW && tg < nrows; tg += 16) {
+        const int64_t m = tg + (lane & 15);
+        const bool mv = m < nrows;
+        const int64_t row = mv ? (int64_t)rows[m] : 0;
+        // the compact values of the 16 rows, loaded ahead of the rank-r products
+        bf16_t cv0[16], cv1[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const bool ok = tg + rr < nrows;
+            const bf16_t* yc = Yc + (tg + rr) * ldyc + j0;
+            cv0[rr] = (ok && sl0 >= 0) ? yc[lane] : (bf16_t)0;
+            cv1[rr] = (ok && sl1 >= 0) ? yc[64 + lane] : (bf16_t)0;
+        }
+        bf16x8 pb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k = 32 * ks + kl;
+            float v[8];
+            if (lora && mv && pvec && k + 8 <= r) {
+                const float* prow = P + row * ldp;
+                const float4 v0 = *(const float4*)(prow + k), v1 = *(const float4*)(prow + k + 4);
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = (lora && mv && k + q < r) ? P[row * ldp + k + q] : 0.0f;
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = pack_bf16x2(scale * v[2 * q], scale * v[2 * q + 1]);
+            pb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 acc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+            if (lora) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e)
+                        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks][g][e], pb[ks], acc[e], 0, 0, 0);
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                w[q] = pack_bf16x2(acc[0][2 * q], acc[0][2 * q + 1]);
+                w[2 + q] = pack_bf16x2(acc[1][2 * q], acc[1][2 * q + 1]);
+            }
+            *(uint4*)&tile[wid][lane & 15][8 * (lane >> 4) + 32 * g] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        // (this wave's own LDS rows: in-order LDS access within the wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // the selected channels from the compact rows
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            if (sl0 >= 0) tile[wid][rr][sl0] = cv0[rr];
+            if (sl1 >= 0) tile[wid][rr][sl1] = cv1[rr];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rr = 4 * j + (lane >> 4);               // tile row: lane rr holds its row number
+            const int64_t orow = __shfl(row, rr, 64);
+            const int ov = __shfl((int)mv, rr, 64);
+            if (!ov) continue;
+            const int64_t c = c0 + 8 * (lane & 15);
+            if (whole) {
+                *(uint4*)(y + orow * ldy + c) = *(const uint4*)&tile[wid][rr][8 * (lane & 15)];
+            } else {
+                for (int q = 0; q < 8; ++q)
+                    if (c + q < C) y[orow * ldy + c + q] = tile[wid][rr][8 * (lane & 15) + q];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
 // mask[w] bit b set <=> channel 32 w + b is in the ascending list idx
 __global__ void select_mask_kernel(const int32_t* __restrict__ idx, int64_t n, int64_t C,
                                    uint32_t* __restrict__ mask) {
@@ -925,6 +1074,23 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
     else if (r <= 64) FILL(64);
     else FILL(128);
 #undef FILL
+    return hipGetLastError();
+}
+
+hipError_t launch_lora_merge_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
+                                  int64_t C, const float* P, int64_t ldp, const void* B,
+                                  int64_t ldb, int64_t r, float scale, const void* Yc,
+                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st) {
+    if (nrows <= 0 || C <= 0) return hipSuccess;
+    if (P && (r < 1 || r > 128)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)ceil_div(C, 128), (unsigned)ceil_div(nrows, 4 * FTW));
+#define MERGE(RR)                                                                                  \
+    hipLaunchKernelGGL((lora_merge_rows_kernel<RR>), grid, dim3(256), 0, st, (bf16_t*)y, ldy, rows, \
+                       nrows, C, P, ldp, (const bf16_t*)B, ldb, P ? r : 0, scale, (const bf16_t*)Yc, ldyc, idx, n)
+    if (!P || r <= 32) MERGE(32);
+    else if (r <= 64) MERGE(64);
+    else MERGE(128);
+#undef MERGE
     return hipGetLastError();
 }
 

@@ -653,6 +653,28 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
         p[np++] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim,
                           beta, l, T, C);
     if (only_out) return run_gemm(h, dt, false, p, np);
+    if (dt == SL_BF16 && !beta && !(flags & SL_NO_FILL)) {
+        // context rows: the product of the selected channels is stored compactly
+        // ([T_c, n], whole 16-byte rows), then one pass writes every channel of
+        // those rows: the compact values at the selected channels, the rank-r
+        // term (or 0) at the others
+        const int64_t ldn = n > 0 ? (n + 7) / 8 * 8 : 8;
+        SL_CHECK(ensure_ws(h, round_up((size_t)(T_c * ldn) * 2, 256)));
+        void* yc = h->ws;
+        if (n > 0) {
+            GemmProblem pc = problem(X, ldx, ctx_rows, Wc, ldw, idx, yc, ldn, nullptr, nullptr, T_c, n, Kdim, 0,
+                                     l, T, C);
+            pc.l_rows = ctx_rows;
+            pc.l_cols = idx;
+            p[np++] = pc;
+            SL_CHECK(run_gemm(h, dt, false, p, np));
+        } else if (np) {
+            SL_CHECK(run_gemm(h, dt, false, p, np));
+        }
+        Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C + n) * 2);
+        return hip_check(h, launch_lora_merge_rows(Z, ldz, ctx_rows, T_c, C, l.P, l.ldP, l.B, l.ldB, l.r, l.scale,
+                                                   yc, ldn, idx, n, h->stream), "lora_merge");
+    }
     p[np++] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
                       C);
     if (flags & SL_NO_FILL) {

@@ -64,6 +64,7 @@ struct GemmProblem {
     const int32_t* l_rows;  // rank-r row map (token rows) when C rows are unmapped partials
     int64_t a_nrows, b_nrows;  // heights of the A / B matrices (0: unknown)
     int64_t k_alg;             // contraction length counted as work (0: K; K may include zero padding)
+    const int32_t* l_cols;     // rank-r column map (rows of lB) when C columns are stored unmapped
 };
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
@@ -81,6 +82,13 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
                                  int64_t C, const float* P, int64_t ldp, const void* B,
                                  int64_t ldb, int64_t r, float scale, const int32_t* idx,
                                  int64_t n, uint32_t* mask, int beta, hipStream_t st);
+// y[rows[m], c] = Yc[m, j] for the selected channels c = idx[j] (a product
+// stored compactly, [nrows, >= n] bf16), and scale * P[rows[m], :] . B[c, :]
+// (0 when P is null) for every other channel of the row; bf16 y and B
+hipError_t launch_lora_merge_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
+                                  int64_t C, const float* P, int64_t ldp, const void* B,
+                                  int64_t ldb, int64_t r, float scale, const void* Yc,
+                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st);
 // fp32 version (VALU), same semantics.
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 
