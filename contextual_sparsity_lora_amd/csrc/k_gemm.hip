@@ -745,7 +745,7 @@ __host__ __device__ constexpr uint16_t vmcnt_imm(int n) {
 
 template <int BKS, int NW, int DPT>
 __device__ __forceinline__ void nt5_dma(rsrc_t ra, rsrc_t rb, bf16_t* st, int64_t kt, int64_t K, int ck,
-                                        int wid, const uint32_t (&goff)[DPT]) {
+                                        int wid, const uint32_t* goff) {
     const uint32_t soff = (uint32_t)(kt * BKS * 2);
     const bool kin = kt * BKS + ck * 8 < K;
 #pragma unroll
@@ -846,12 +846,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
     const int nk_all = (int)((K + BKS - 1) / BKS);
     int kb = 0, nk = (nk_all + NST - 1) / NST * NST;
     if (PART) {
-        const int kc = __builtin_amdgcn_readfirstlane(((nk_all + sk1 - 1) / sk1 + NST - 1) / NST * NST);
+        const int kc = ((nk_all + sk1 - 1) / sk1 + NST - 1) / NST * NST;
         kb = qch * kc;
         const int rest = nk_all - kb;
         nk = rest <= 0 ? 0 : (rest < kc ? (rest + NST - 1) / NST * NST : kc);
     }
-    auto dma = [&](bf16_t* st, int kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kb + kt, K, ck, wid, goff); };
+    const int64_t kb64 = kb;
+    auto dma = [&](bf16_t* st, int kt) { nt5_dma<BKS, NW, DPT>(ra, rb, st, kb64 + kt, K, ck, wid, goff); };
 
     // fragment reads: row R = base + lane % 32 (base a multiple of 32), chunk 2 ks + lane / 32
     const int swz = ((lane & 31) / (16 / CPR)) % CPR;
@@ -1211,7 +1212,7 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
                             size_t skws_floats, int ncu) {
     // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
     const char* env = getenv("SL_GEMM_CFG");
-    int cfg = env ? atoi(env) : 31;
+    int cfg = env ? atoi(env) : 10;
     if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {
         switch (cfg) {
             case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
@@ -1225,7 +1226,7 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
             case 33: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, skws, skws_floats, ncu);
             case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st);
             case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st);
-            default: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, skws, skws_floats, ncu);
+            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
         }
     }
     if (cfg >= 10) cfg = 2;
