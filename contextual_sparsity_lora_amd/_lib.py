@@ -36,6 +36,8 @@ SIGNATURES = {
     "sl_svd_estimate": (_st, [_vp, _vp, _int, _i64, _vp, _i64, _i64, _vp, _i64, _vp]),
     "sl_score_select": (_st, [_vp, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                               _i64, _i64, _i64, _vp, _vp]),
+    "sl_score_select_noalloc": (_st, [_vp, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
+                                      _i64, _i64, _i64, _vp, _vp]),
     "sl_select_top": (_st, [_vp, _vp, _i64, _i64, _vp]),
     "sl_random_scores": (_st, [_vp, ctypes.c_uint64, _i64, _vp]),
     "sl_dense_scores": (_st, [_vp, _int, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp]),

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 #include <new>
 
 #include <cmath>
@@ -122,13 +123,13 @@ struct Timed {
     hipEvent_t a = nullptr, b = nullptr;
     Timed(sl_handle* h_, int cls_, double flops_, double bytes_)
         : h(h_), cls(cls_), flops(flops_), bytes(bytes_) {
-        if (!h->timing || (h->timing_cls >= 0 && h->timing_cls != cls)) return;
+        if (!h || !h->timing || (h->timing_cls >= 0 && h->timing_cls != cls)) return;
         a = take_event(h);
         b = take_event(h);
         if (a && b) (void)hipEventRecord(a, h->stream);
     }
     ~Timed() {
-        if (!h->timing || !a || !b) return;
+        if (!h || !h->timing || !a || !b) return;
         (void)hipEventRecord(b, h->stream);
         h->timed.push_back({cls, a, b, flops, bytes});
     }
@@ -163,6 +164,9 @@ struct DeviceGuard {
         if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
     }
 };
+
+// device address of the allocation-free scratch (defined with the score selection)
+sl_status scratch_init(int device);
 
 sl_status check_rows(sl_handle* h, const int32_t* ctx, int64_t Tc, const int32_t* out,
                      int64_t To, int64_t T) {
@@ -214,6 +218,12 @@ sl_status sl_create(sl_handle** out, int device) {
     if (hipGetDeviceProperties(&prop, device) == hipSuccess) h->num_cu = prop.multiProcessorCount;
     if (hipMalloc(&h->dev_flags, 64) != hipSuccess ||
         hipMemset(h->dev_flags, 0, 64) != hipSuccess) {
+        delete h;
+        return SL_ERR_HIP;
+    }
+    // the device address of this device's allocation-free scratch (once per device)
+    if (scratch_init(device) != SL_OK) {
+        (void)hipFree(h->dev_flags);
         delete h;
         return SL_ERR_HIP;
     }
@@ -359,11 +369,27 @@ sl_status sl_svd_estimate(sl_handle* h, const void* x, sl_dtype xdt, int64_t ldx
 }
 
 // ---------------------------------------------------------------- a3 + a4
-sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
-                          int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
-                          const float* WB1, int64_t k, int64_t C, int64_t n_rep, int64_t head_dim,
-                          int64_t n_keep, float* scores, int32_t* idx) {
-    if (!h) return SL_ERR_INVALID;
+}  // extern "C"
+
+namespace {
+
+// Bytes of scratch score selection needs for these sizes (scores kept in the
+// workspace when the caller passes none, the QK criterion's two ssq vectors,
+// the chain partials of the split scoring form).
+size_t score_select_ws_bytes(sl_criterion crit, int64_t k, int64_t C, int64_t n_rep, bool scores_given) {
+    size_t need = 0;
+    const int64_t Cq = crit == SL_CRIT_QK ? C * n_rep : 0;
+    if (!scores_given) need += round_up((size_t)C * 4, 256);
+    if (crit == SL_CRIT_QK) need += round_up((size_t)Cq * 4, 256) + round_up((size_t)C * 4, 256);
+    const int64_t Cmax = crit == SL_CRIT_QK ? Cq : C;
+    const bool split = k == 16 && (C < SSQ_SPLIT_C || Cq < SSQ_SPLIT_C);
+    if (split) need += round_up((size_t)64 * (Cmax < SSQ_SPLIT_C ? Cmax : C) * 4, 256);
+    return need;
+}
+
+sl_status score_select_check(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa, int64_t T_c,
+                             int64_t off0, const float* WB0, int64_t off1, const float* WB1, int64_t k,
+                             int64_t C, int64_t n_rep, int64_t head_dim, int64_t n_keep, int32_t* idx) {
     SL_REQUIRE(h, crit == SL_CRIT_L2 || crit == SL_CRIT_SWIGLU_L2 || crit == SL_CRIT_QK,
                "bad criterion");
     SL_REQUIRE(h, k >= 1 && k <= 64, "k must be in [1, 64]");
@@ -379,19 +405,21 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     if (crit == SL_CRIT_QK) {
         SL_REQUIRE(h, n_rep >= 1 && head_dim >= 1 && C % head_dim == 0, "bad QK grouping");
         SL_REQUIRE(h, off1 >= 0 && off1 + k <= ld_xa, "off1 + k exceeds ld_xa");
+        SL_REQUIRE(h, C * n_rep <= INT32_MAX, "C * n_rep out of range");
     }
-    DeviceGuard g(h->device);
-    size_t need = 0;
+    return SL_OK;
+}
+
+// Score and select with the scratch at ws (score_select_ws_bytes of it).
+// timed: bracket the launches with the handle's timing events.
+sl_status score_select_run(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa, int64_t T_c,
+                           int64_t off0, const float* WB0, int64_t off1, const float* WB1, int64_t k,
+                           int64_t C, int64_t n_rep, int64_t head_dim, int64_t n_keep, float* scores,
+                           int32_t* idx, char* ws, bool timed) {
     const int64_t Cq = crit == SL_CRIT_QK ? C * n_rep : 0;
-    if (!scores) need += round_up((size_t)C * 4, 256);
-    if (crit == SL_CRIT_QK) need += round_up((size_t)Cq * 4, 256) + round_up((size_t)C * 4, 256);
-    // chain partials of the split scoring form (few channels, k = 16)
     const int64_t Cmax = crit == SL_CRIT_QK ? Cq : C;
     const bool split = k == 16 && (C < SSQ_SPLIT_C || Cq < SSQ_SPLIT_C);
     const size_t part_bytes = split ? round_up((size_t)64 * (Cmax < SSQ_SPLIT_C ? Cmax : C) * 4, 256) : 0;
-    need += part_bytes;
-    SL_CHECK(ensure_ws(h, need));
-    char* ws = (char*)h->ws;
     float* part = split ? (float*)ws : nullptr;
     ws += part_bytes;
     float* sc = scores;
@@ -403,7 +431,8 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     {
     const int nwb = crit == SL_CRIT_L2 ? 1 : 2;
     const double Cs = crit == SL_CRIT_QK ? (double)(C * n_rep + C) : (double)C * nwb;
-    Timed tm(h, K_SCORE, 2.0 * T_c * k * Cs, 4.0 * T_c * (double)(nwb * k) + 4.0 * k * Cs + 4.0 * C);
+    sl_handle* th = timed ? h : nullptr;
+    Timed tm(th, K_SCORE, 2.0 * T_c * k * Cs, 4.0 * T_c * (double)(nwb * k) + 4.0 * k * Cs + 4.0 * C);
     if (crit == SL_CRIT_QK) {
         float* sq = (float*)ws;
         float* sk = (float*)(ws + round_up((size_t)Cq * 4, 256));
@@ -419,10 +448,76 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
     }
     }
     if (e == hipSuccess) {
-        Timed tm(h, K_TOPK, 0, 4.0 * C + 4.0 * n_keep);
+        Timed tm(timed ? h : nullptr, K_TOPK, 0, 4.0 * C + 4.0 * n_keep);
         e = launch_topk(sc, C, n_keep, idx, h->stream);
     }
     return hip_check(h, e, "score_select");
+}
+
+// ---------------------------------------------------------------- allocation-free scratch
+// Device memory of the allocation-free entry points: one array per device
+// (each device that loads the library holds its own copy until the process
+// ends).  Host code never uses the array's name as an address: its device
+// address comes from hipGetSymbolAddress, once per device, at sl_create.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// with `device` current
+sl_status scratch_init(int device) {
+    if (device < 0 || device >= kMaxDevices) return SL_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[device]) return SL_OK;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return SL_ERR_HIP;
+    }
+    g_scratch_ptr[device] = p;
+    return SL_OK;
+}
+
+void* scratch_ptr(int device) {
+    if (device < 0 || device >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return g_scratch_ptr[device];
+}
+
+}  // namespace
+
+extern "C" {
+
+sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
+                          int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
+                          const float* WB1, int64_t k, int64_t C, int64_t n_rep, int64_t head_dim,
+                          int64_t n_keep, float* scores, int32_t* idx) {
+    if (!h) return SL_ERR_INVALID;
+    SL_CHECK(score_select_check(h, crit, xa, ld_xa, T_c, off0, WB0, off1, WB1, k, C, n_rep, head_dim,
+                                n_keep, idx));
+    DeviceGuard g(h->device);
+    SL_CHECK(ensure_ws(h, score_select_ws_bytes(crit, k, C, n_rep, scores != nullptr)));
+    return score_select_run(h, crit, xa, ld_xa, T_c, off0, WB0, off1, WB1, k, C, n_rep, head_dim, n_keep,
+                            scores, idx, (char*)h->ws, true);
+}
+
+sl_status sl_score_select_noalloc(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
+                                  int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
+                                  const float* WB1, int64_t k, int64_t C, int64_t n_rep,
+                                  int64_t head_dim, int64_t n_keep, float* scores, int32_t* idx) {
+    if (!h) return SL_ERR_INVALID;
+    SL_CHECK(score_select_check(h, crit, xa, ld_xa, T_c, off0, WB0, off1, WB1, k, C, n_rep, head_dim,
+                                n_keep, idx));
+    const size_t need = score_select_ws_bytes(crit, k, C, n_rep, scores != nullptr);
+    if (need > kNoAllocScratchBytes)
+        return fail(h, SL_ERR_WORKSPACE, "sl_score_select_noalloc needs %zu bytes of scratch, above its fixed %zu",
+                    need, kNoAllocScratchBytes);
+    char* ws = (char*)scratch_ptr(h->device);
+    if (!ws) return fail(h, SL_ERR_HIP, "the allocation-free scratch of device %d is not set up", h->device);
+    DeviceGuard g(h->device);
+    return score_select_run(h, crit, xa, ld_xa, T_c, off0, WB0, off1, WB1, k, C, n_rep, head_dim, n_keep,
+                            scores, idx, ws, false);
 }
 
 // ---------------------------------------------------------------- criterion variants

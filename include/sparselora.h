@@ -199,6 +199,22 @@ sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int6
                           const float* WB1, int64_t k, int64_t C, int64_t n_rep,
                           int64_t head_dim, int64_t n_keep, float* scores, int32_t* idx);
 
+/* The same score selection for callers that cannot allocate device memory:
+ * code being captured into a HIP graph, tight serving loops, and harnesses
+ * that forbid hipMalloc.  Arguments, results and error behaviour are those of
+ * sl_score_select; the scratch it needs (the scores when scores is NULL, the
+ * QK criterion's two ssq vectors, chain partials of the split scoring form)
+ * lives in a fixed 4 MiB device array of the library, one per device, whose
+ * address is taken once per device in sl_create.  A call that would need more
+ * than 4 MiB returns SL_ERR_WORKSPACE before launching anything.  The call
+ * allocates nothing, records no timing events, and leaves no state that a
+ * later call relies on; calls that overlap on one device (other handles or
+ * streams included) share that array and race. */
+sl_status sl_score_select_noalloc(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
+                                  int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
+                                  const float* WB1, int64_t k, int64_t C, int64_t n_rep,
+                                  int64_t head_dim, int64_t n_keep, float* scores, int32_t* idx);
+
 /* ---------------------------------------------------------------- criterion variants */
 
 /* Top-n of given scores, the selection rule of sl_score_select (largest score
