@@ -417,15 +417,6 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
 // compact row, since idx is ascending) overwrite their slots, and each row
 // leaves as 256 contiguous bytes.  Every element of the listed rows is written
 // exactly once, with 16-byte stores.
-__device__ __forceinline__ int64_t lower_bound_i32(const int32_t* __restrict__ a, int64_t n, int64_t v) {
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi) >> 1;
-        if (a[mid] < v) lo = mid + 1; else hi = mid;
-    }
-    return lo;
-}
-
 template <int R>
 __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
     bf16_t* __restrict__ y, int64_t ldy, const int32_t* __restrict__ rows, int64_t nrows, int64_t C,
@@ -466,8 +457,8 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
             }
     // the block's selected channels: idx[j0 .. j1), at most 128 of them; lane
     // holds entries j0 + lane and j0 + 64 + lane (slot in the block, or -1)
-    const int64_t j0 = lower_bound_i32(idx, n, c0);
-    const int64_t j1 = lower_bound_i32(idx, n, c0 + 128);
+    int64_t j0, j1;
+    wave_lower_bounds(idx, n, c0, c0 + 128, lane, j0, j1);
     const int sl0 = j0 + lane < j1 ? (int)(idx[j0 + lane] - c0) : -1;
     const int sl1 = j0 + 64 + lane < j1 ? (int)(idx[j0 + 64 + lane] - c0) : -1;
     const bool aligned = (ldy % 8 == 0) && (((uintptr_t)y & 15) == 0);
@@ -757,12 +748,12 @@ __global__ void swiglu_fwd_kernel(const T* __restrict__ g, int64_t ldg, const T*
         load8<T>(g + t * ldg + c0, gv);
         load8<T>(u + t * ldu + c0, uv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) hv[e] = gv[e] / (1.0f + expf(-gv[e])) * uv[e];
+        for (int e = 0; e < 8; ++e) hv[e] = gv[e] * sigmoid_hw(gv[e]) * uv[e];
         store8<T>(h + t * ldh + c0, hv);
     } else {
         for (int64_t c = c0; c < F; ++c) {
             const float a = ld<T>(g, t * ldg + c), b = ld<T>(u, t * ldu + c);
-            st<T>(h, t * ldh + c, a / (1.0f + expf(-a)) * b);
+            st<T>(h, t * ldh + c, a * sigmoid_hw(a) * b);
         }
     }
 }
@@ -782,7 +773,7 @@ __global__ void swiglu_bwd_kernel(const T* __restrict__ dh, int64_t lddh, const 
         load8<T>(u + t * ldu + c0, uv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float sg = 1.0f / (1.0f + expf(-gv[e]));
+            const float sg = sigmoid_hw(gv[e]);
             a[e] = d[e] * uv[e] * (sg * (1.0f + gv[e] * (1.0f - sg)));
             b[e] = d[e] * (gv[e] * sg);
         }
@@ -792,7 +783,7 @@ __global__ void swiglu_bwd_kernel(const T* __restrict__ dh, int64_t lddh, const 
         for (int64_t c = c0; c < F; ++c) {
             const float d = ld<T>(dh, t * lddh + c), gv = ld<T>(g, t * ldg + c),
                         uv = ld<T>(u, t * ldu + c);
-            const float sg = 1.0f / (1.0f + expf(-gv));
+            const float sg = sigmoid_hw(gv);
             st<T>(dg, t * lddg + c, d * uv * (sg * (1.0f + gv * (1.0f - sg))));
             st<T>(du, t * lddu + c, d * (gv * sg));
         }

@@ -46,6 +46,56 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// ---------------------------------------------------------------- SwiGLU activation
+// Logistic sigmoid on the hardware exponential and reciprocal (v_exp_f32,
+// v_rcp_f32, about one ulp each): 1 / (1 + 2^(-z log2 e)).  The activation of
+// the SwiGLU passes; the selection criterion evaluates SiLU with its own fixed
+// exp instead, so that its scores are reproducible bit for bit.
+__device__ __forceinline__ float sigmoid_hw(float z) {
+    return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.44269504088896341f));
+}
+
+// ---------------------------------------------------------------- ascending-list search
+// One round of a wave's search for #{j : a[j] < v} in [lo, hi] (the answer is
+// known to lie there): the 64 lanes probe 64 evenly spaced entries of the range
+// and a ballot keeps the one step that holds the answer.  lo, hi, v uniform.
+__device__ __forceinline__ void wave_lb_round(const int32_t* __restrict__ a, int64_t v, int lane, int64_t& lo,
+                                              int64_t& hi) {
+    const int64_t st = (hi - lo + 63) / 64;
+    const int64_t p = lo + lane * st;
+    const uint64_t m = __ballot(p < hi && a[p] >= v);
+    if (m == 0) {                        // every probe below v: past the last one
+        lo = lo + ((hi - 1 - lo) / st) * st + 1;
+    } else {
+        const int f = __builtin_ctzll(m);
+        if (f == 0) {
+            hi = lo;                     // a[lo] >= v: the answer is lo
+        } else {
+            hi = lo + (int64_t)f * st;   // a[lo + f st] >= v > a[lo + (f - 1) st]
+            lo = lo + (int64_t)(f - 1) * st + 1;
+        }
+    }
+}
+__device__ __forceinline__ int64_t wave_lb_final(const int32_t* __restrict__ a, int64_t v, int lane, int64_t lo,
+                                                 int64_t hi) {
+    const uint64_t m = __ballot(lo + lane < hi && a[lo + lane] >= v);
+    return m ? lo + __builtin_ctzll(m) : hi;
+}
+// j0 = #{j : a[j] < v0} and j1 = #{j : a[j] < v1} over the ascending list
+// a[0..n), by the whole wave: each round narrows a range 64-fold with one
+// dependent load (two rounds for n up to 262144), instead of the ~log2(n)
+// dependent loads of a one-lane binary search.
+__device__ __forceinline__ void wave_lower_bounds(const int32_t* __restrict__ a, int64_t n, int64_t v0, int64_t v1,
+                                                  int lane, int64_t& j0, int64_t& j1) {
+    int64_t lo0 = 0, hi0 = n, lo1 = 0, hi1 = n;
+    while (hi0 - lo0 > 64 || hi1 - lo1 > 64) {
+        if (hi0 - lo0 > 64) wave_lb_round(a, v0, lane, lo0, hi0);
+        if (hi1 - lo1 > 64) wave_lb_round(a, v1, lane, lo1, hi1);
+    }
+    j0 = wave_lb_final(a, v0, lane, lo0, hi0);
+    j1 = wave_lb_final(a, v1, lane, lo1, hi1);
+}
+
 // ---------------------------------------------------------------- launchers
 // Every launcher enqueues on `st` and returns hipGetLastError().
 struct GemmProblem {
@@ -204,5 +254,4 @@ hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* 
 hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void* g, int64_t ldg,
                              const void* u, int64_t ldu, int64_t T, int64_t F, void* dg,
                              int64_t lddg, void* du, int64_t lddu, hipStream_t st);
-
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
