@@ -21,6 +21,8 @@ SIGNATURES = {
     "sl_destroy": (_st, [_vp]),
     "sl_set_stream": (_st, [_vp, _vp]),
     "sl_reserve_workspace": (_st, [_vp, ctypes.c_size_t]),
+    "sl_workspace_bytes": (_st, [_vp, ctypes.POINTER(ctypes.c_size_t)]),
+    "sl_set_option": (_st, [_vp, ctypes.c_char_p, _i64]),
     "sl_sync": (_st, [_vp]),
     "sl_last_error": (ctypes.c_char_p, [_vp]),
     "sl_status_str": (ctypes.c_char_p, [_st]),

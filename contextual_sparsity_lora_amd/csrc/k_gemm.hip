@@ -22,8 +22,6 @@
 // accumulators with v_mfma_f32_32x32x2_f32 (fp32 operands), cm / cn being the
 // mapped output row / channel.  A problem with K = 0 carries only this term
 // (the unselected channels of context rows).
-#include <cstdlib>
-
 #include "sl_internal.h"
 
 namespace {
@@ -1015,13 +1013,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
     }
 }
 
-GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn) {
+GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn, int grp = 8) {
     GemmArgs a = {};
     a.nprob = nprob;
-    // SL_GEMM_GRP overrides the tile-row group of the tile order (tuning sweeps)
-    const char* ge = getenv("SL_GEMM_GRP");
-    const int grp_env = ge ? atoi(ge) : 0;
-    a.grp = grp_env > 0 ? grp_env : 8;
+    a.grp = grp > 0 ? grp : 8;     // tile rows per group of the tile order
     a.first[0] = 0;
     for (int i = 0; i < MAXP; ++i) {
         if (i < nprob) {
@@ -1116,8 +1111,8 @@ int split_tail_plan(const GemmArgs& a, int ncu, int& dp) {
 
 template <int BM, int BN, int WGM, int WGN, int NSET>
 hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
-                         size_t skws_floats, int ncu) {
-    GemmArgs a = make_args(probs, nprob, BM, BN);
+                         size_t skws_floats, int ncu, int grp) {
+    GemmArgs a = make_args(probs, nprob, BM, BN, grp);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
     // staging buffers; the store epilogue reuses them (always needed)
@@ -1153,9 +1148,9 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, fl
 }
 
 template <int WGM, int WGN, int BKS, int NST>
-hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st, float* skws = nullptr,
+hipError_t launch_nt5(const GemmProblem* probs, int nprob, hipStream_t st, int grp, float* skws = nullptr,
                       size_t skws_floats = 0, int ncu = 256) {
-    GemmArgs a = make_args(probs, nprob, 256, 256);
+    GemmArgs a = make_args(probs, nprob, 256, 256, grp);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
     // fixup launch: its store epilogue uses WGM row groups of 32 x (BN + 4) fp32
@@ -1201,32 +1196,32 @@ bool nt_v3_ok(const GemmProblem* probs, int nprob) {
 
 }  // namespace
 
-size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu) {
-    GemmArgs a = make_args(probs, nprob, 256, 256);
+size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu, const sl_tuning& tune) {
+    GemmArgs a = make_args(probs, nprob, 256, 256, tune.gemm_grp);
     int dp;
     const int sks = split_tail_plan(a, ncu, dp);
     return sks ? (size_t)(a.first[MAXP] - dp) * sks * 256 * 256 : 0;
 }
 
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
-                            size_t skws_floats, int ncu) {
-    // SL_GEMM_CFG selects a tile configuration by number (tuning sweeps only)
-    const char* env = getenv("SL_GEMM_CFG");
-    int cfg = env ? atoi(env) : 10;
+                            size_t skws_floats, int ncu, const sl_tuning& tune) {
+    // tune.gemm_cfg selects a tile configuration by number (tuning sweeps)
+    int cfg = tune.gemm_cfg;
+    const int grp = tune.gemm_grp;
     if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {
         switch (cfg) {
-            case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
-            case 12: return launch_nt_cfg<256, 256, 2, 4, 1>(probs, nprob, st, nullptr, 0, ncu);
-            case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu);
-            case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu);
-            case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st, nullptr, 0, ncu);
-            case 20: return launch_nt5<2, 4, 32, 4>(probs, nprob, st);
-            case 21: return launch_nt5<2, 2, 32, 4>(probs, nprob, st);
-            case 31: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, skws, skws_floats, ncu);
-            case 33: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, skws, skws_floats, ncu);
-            case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st);
-            case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st);
-            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu);
+            case 11: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu, grp);
+            case 12: return launch_nt_cfg<256, 256, 2, 4, 1>(probs, nprob, st, nullptr, 0, ncu, grp);
+            case 13: return launch_nt_cfg<256, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu, grp);
+            case 14: return launch_nt_cfg<128, 128, 2, 2, 2>(probs, nprob, st, nullptr, 0, ncu, grp);
+            case 15: return launch_nt_cfg<256, 256, 2, 2, 1>(probs, nprob, st, nullptr, 0, ncu, grp);
+            case 20: return launch_nt5<2, 4, 32, 4>(probs, nprob, st, grp);
+            case 21: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, grp);
+            case 31: return launch_nt5<2, 2, 32, 4>(probs, nprob, st, grp, skws, skws_floats, ncu);
+            case 33: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, grp, skws, skws_floats, ncu);
+            case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st, grp);
+            case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, grp);
+            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu, grp);
         }
     }
     if (cfg >= 10) cfg = 2;

@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <cstdio>
 #include <mutex>
+#include <vector>
 #include <new>
 
 #include <cmath>
@@ -69,6 +70,9 @@ sl_status check_matrix(sl_handle* h, const void* p, int64_t ld, int64_t cols, sl
 
 sl_status ensure_ws(sl_handle* h, size_t bytes) {
     if (bytes <= h->ws_bytes) return SL_OK;
+    if (h->ws_fixed)
+        return fail(h, SL_ERR_WORKSPACE, "the call needs %zu bytes of workspace, above the fixed %zu", bytes,
+                    h->ws_bytes);
     size_t want = bytes + (bytes >> 3) + 4096;
     if (h->ws) {
         SL_HIP(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
@@ -87,6 +91,31 @@ sl_status ensure_ws(sl_handle* h, size_t bytes) {
 }
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Debug mode (SL_DEBUG=1, or sl_set_option "debug"): before launching, copy a
+// caller's index list to the host (after synchronising the stream) and check
+// that it is strictly ascending with every entry in [0, bound).  Off by
+// default: the hot path never synchronises.
+sl_status debug_check_list(sl_handle* h, const int32_t* list, int64_t n, int64_t bound, const char* name) {
+    if (!h->debug || n <= 0 || !list) return SL_OK;
+    std::vector<int32_t> v((size_t)n);
+    SL_HIP(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
+    SL_HIP(h, hipMemcpy(v.data(), list, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost), "hipMemcpy");
+    for (int64_t i = 0; i < n; ++i) {
+        if (v[(size_t)i] < 0 || v[(size_t)i] >= bound)
+            return fail(h, SL_ERR_INVALID, "%s[%lld] = %d is outside [0, %lld)", name, (long long)i, v[(size_t)i],
+                        (long long)bound);
+        if (i > 0 && v[(size_t)i] <= v[(size_t)i - 1])
+            return fail(h, SL_ERR_INVALID, "%s is not strictly ascending at %lld (%d after %d)", name, (long long)i,
+                        v[(size_t)i], v[(size_t)i - 1]);
+    }
+    return SL_OK;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* e = getenv(name);
+    return (e && *e) ? atoi(e) : dflt;
+}
 
 // ---------------------------------------------------------------- measurement
 // Kernel classes whose launches are bracketed by HIP events on the handle's
@@ -213,6 +242,15 @@ sl_status sl_create(sl_handle** out, int device) {
     sl_handle* h = new (std::nothrow) sl_handle();
     if (!h) return SL_ERR_WORKSPACE;
     h->device = device;
+    // tuning knobs and debug mode: read once per handle
+    h->tune.gemm_cfg = env_int("SL_GEMM_CFG", h->tune.gemm_cfg);
+    h->tune.gemm_grp = env_int("SL_GEMM_GRP", h->tune.gemm_grp);
+    h->tune.gemm_split = env_int("SL_GEMM_SPLIT", h->tune.gemm_split);
+    h->tune.splitk_max = env_int("SL_SPLITK_MAX", h->tune.splitk_max);
+    h->tune.lora_xl_split = env_int("SL_LORA_XL_SPLIT", h->tune.lora_xl_split);
+    if (h->tune.gemm_grp < 1 || h->tune.gemm_grp > 64) h->tune.gemm_grp = 8;
+    if (h->tune.splitk_max < 1 || h->tune.splitk_max > 16) h->tune.splitk_max = 4;
+    h->debug = env_int("SL_DEBUG", 0) != 0;
     DeviceGuard g(device);
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, device) == hipSuccess) h->num_cu = prop.multiProcessorCount;
@@ -257,6 +295,32 @@ sl_status sl_reserve_workspace(sl_handle* h, size_t bytes) {
     if (!h) return SL_ERR_INVALID;
     DeviceGuard g(h->device);
     return ensure_ws(h, bytes);
+}
+
+sl_status sl_set_option(sl_handle* h, const char* name, int64_t value) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, name != nullptr, "option name is NULL");
+    const std::string n(name);
+    if (n == "gemm_cfg") h->tune.gemm_cfg = (int)value;
+    else if (n == "gemm_grp") {
+        SL_REQUIRE(h, value >= 1 && value <= 64, "gemm_grp must be in [1, 64]");
+        h->tune.gemm_grp = (int)value;
+    } else if (n == "gemm_split") h->tune.gemm_split = (int)value;
+    else if (n == "splitk_max") {
+        SL_REQUIRE(h, value >= 1 && value <= 16, "splitk_max must be in [1, 16]");
+        h->tune.splitk_max = (int)value;
+    }
+    else if (n == "lora_xl_split") h->tune.lora_xl_split = (int)value;
+    else if (n == "workspace_fixed") h->ws_fixed = value != 0;
+    else if (n == "debug") h->debug = value != 0;
+    else return fail(h, SL_ERR_INVALID, "unknown option '%s'", name);
+    return SL_OK;
+}
+
+sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes) {
+    if (!h || !bytes) return SL_ERR_INVALID;
+    *bytes = h->ws_bytes + h->gws_bytes;
+    return SL_OK;
 }
 
 sl_status sl_sync(sl_handle* h) {
@@ -607,6 +671,7 @@ sl_status sl_expand_gqa(sl_handle* h, const int32_t* idx_kv, int64_t n, int64_t 
     if (n == 0) return SL_OK;
     SL_REQUIRE(h, idx_kv && idx_q, "NULL pointer");
     DeviceGuard g(h->device);
+    SL_CHECK(debug_check_list(h, idx_kv, n, INT32_MAX, "idx_kv"));
     return hip_check(h, launch_expand_gqa(idx_kv, n, n_rep, head_dim, idx_q, h->stream),
                      "expand_gqa");
 }
@@ -618,6 +683,7 @@ sl_status sl_stack_index(sl_handle* h, const int32_t* idx, int64_t n, int64_t C,
     if (n == 0) return SL_OK;
     SL_REQUIRE(h, idx && idx_out, "NULL pointer");
     DeviceGuard g(h->device);
+    SL_CHECK(debug_check_list(h, idx, n, C, "idx"));
     return hip_check(h, launch_stack_index(idx, n, C, copies, idx_out, h->stream), "stack_index");
 }
 
@@ -643,6 +709,8 @@ sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const 
     SL_REQUIRE(h, idx_qkv && (n_qk == 0 || (idx_qk && idx_q)) && (n_vo == 0 || (idx_vo && idx_o)),
                "NULL pointer");
     DeviceGuard g(h->device);
+    SL_CHECK(debug_check_list(h, idx_qk, n_qk, Ckv, "idx_qk"));
+    SL_CHECK(debug_check_list(h, idx_vo, n_vo, Ckv, "idx_vo"));
     return hip_check(h, launch_qkv_index(idx_qk, n_qk, idx_vo, n_vo, n_rep, head_dim, Cq, Ckv, idx_q, idx_o,
                                          idx_qkv, h->stream), "qkv_index");
 }
@@ -651,13 +719,13 @@ sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const 
 static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem* p, int np) {
     float* skws = nullptr;
     size_t skf = 0;
-    // SL_GEMM_SPLIT=0 turns the split tail off (tuning comparisons)
-    const char* split_env = getenv("SL_GEMM_SPLIT");
-    const bool split_on = !(split_env && split_env[0] == '0');
+    // tune.gemm_split = 0 turns the split tail off (tuning comparisons)
+    const bool split_on = h->tune.gemm_split != 0;
     if (dt == SL_BF16 && !nn && split_on) {
-        // scratch for the split tail (partial tiles of the last, partial round)
-        skf = gemm_split_tail_floats(p, np, h->num_cu);
-        if (skf && skf * 4 > h->gws_bytes) {
+        // scratch for the split tail (partial tiles of the last, partial round);
+        // with a fixed workspace a launch it does not fit runs every tile whole
+        skf = gemm_split_tail_floats(p, np, h->num_cu, h->tune);
+        if (skf && skf * 4 > h->gws_bytes && !h->ws_fixed) {
             const size_t want = skf * 4 + (skf >> 1) + 4096;
             if (h->gws) {
                 SL_HIP(h, hipStreamSynchronize(h->stream), "hipStreamSynchronize");
@@ -677,7 +745,7 @@ static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem*
     }
     Timed tm(h, dt == SL_BF16 ? (nn ? K_GEMM_NN : K_GEMM_NT) : K_GEMM_F32, gemm_flops(p, np),
              gemm_bytes(p, np, esize(dt)));
-    hipError_t e = dt == SL_BF16 ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu)
+    hipError_t e = dt == SL_BF16 ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu, h->tune)
                                  : launch_gemm_f32(nn, p, np, h->stream);
     return hip_check(h, e, "gemm");
 }
@@ -830,8 +898,7 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
     // part may be split along K (fp32 partials + one ordered reduction) so the
     // tiles of the launch carry similar work.  SL_SPLITK_MAX caps the split
     // (tuning sweeps; default 4).
-    const char* env = getenv("SL_SPLITK_MAX");
-    const int64_t smax = env ? atoll(env) : 4;
+    const int64_t smax = h->tune.splitk_max;
     int64_t S = 1, Ks = C;
     if (dt == SL_BF16 && T_o > 0 && n > 0 && smax > 1) {
         S = (C + n / 2) / n;
@@ -928,6 +995,9 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
     SL_CHECK(check_lora(h, l, T, D_out, dt));
     if (T == 0) return SL_OK;
+    SL_CHECK(debug_check_list(h, idx, n, C, "idx"));
+    SL_CHECK(debug_check_list(h, ctx_rows, T_c, T, "ctx_rows"));
+    SL_CHECK(debug_check_list(h, out_rows, T_o, T, "out_rows"));
     SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
     SL_CHECK(check_matrix(h, y, ldy, D_out, dt, "y"));
     SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
@@ -970,6 +1040,9 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     const LoraEpi l = {lora_P, ld_lora_P, lora_B, ld_lora_B, lora_r, lora_scale};
     SL_CHECK(check_lora(h, l, T, D_in, dt));
     if (T == 0) return SL_OK;
+    SL_CHECK(debug_check_list(h, idx, n, C, "idx"));
+    SL_CHECK(debug_check_list(h, ctx_rows, T_c, T, "ctx_rows"));
+    SL_CHECK(debug_check_list(h, out_rows, T_o, T, "out_rows"));
     SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
     SL_CHECK(check_matrix(h, dx, lddx, D_in, dt, "dx"));
     SL_CHECK(check_matrix(h, Wt, ldwt, D_out, dt, "Wt"));
@@ -994,6 +1067,7 @@ sl_status sl_weight_slice(sl_handle* h, sl_dtype dt, const void* Wc, int64_t ldw
     const int64_t ldn = (n + 7) / 8 * 8;
     SL_CHECK(check_matrix(h, out, ld_out, ldn, dt, "out"));
     DeviceGuard g(h->device);
+    SL_CHECK(debug_check_list(h, idx, n, C, "idx"));
     Timed tm(h, K_GATHER, 0, 2.0 * Nout * n * esize(dt));
     return hip_check(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, out, ld_out,
                                              h->stream), "weight_slice");
@@ -1011,6 +1085,7 @@ sl_status sl_lora_fill_unselected(sl_handle* h, sl_dtype dt, void* y, int64_t ld
     SL_REQUIRE(h, ctx_rows && lora_P && lora_B && (n == 0 || idx), "NULL pointer");
     SL_CHECK(check_matrix(h, y, ldy, C, dt, "y"));
     DeviceGuard g(h->device);
+    SL_CHECK(debug_check_list(h, idx, n, C, "idx"));
     SL_CHECK(ensure_ws(h, round_up((size_t)ceil_div(C, 32) * 4, 256)));
     Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * lora_r, (double)T_c * (C - n) * esize(dt));
     return hip_check(h, launch_lora_fill_rows(y, ldy, ctx_rows, T_c, C, lora_P, ld_lora_P, lora_B, ld_lora_B,
@@ -1066,10 +1141,9 @@ sl_status sl_lora_fwd_bwd(sl_handle* h, int mode, sl_dtype dt, const void* x, in
     const int64_t RC = 64;
     const int64_t rc_max = r < RC ? r : RC;
     // x A^T-type products: the split-K form (more blocks, a reduction launch)
-    // pays off only for long rows; SL_LORA_XL_SPLIT=0/1 forces a form (tuning)
-    const char* xs_env = getenv("SL_LORA_XL_SPLIT");
+    // pays off only for long rows; tune.lora_xl_split = 0/1 forces a form
     auto xl_split_for = [&](int64_t Dk) {
-        if (xs_env) return xs_env[0] != '0';
+        if (h->tune.lora_xl_split >= 0) return h->tune.lora_xl_split != 0;
         return Dk > 16384;
     };
     const bool xl_split = xl_split_for(D_in);

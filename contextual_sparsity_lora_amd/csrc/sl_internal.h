@@ -15,8 +15,21 @@ struct sl_timed_launch {
     double flops, bytes;     // algorithmic work of this launch
 };
 
+// Tuning knobs of the launchers, read from the environment once per handle
+// (sl_create) and settable with sl_set_option.
+struct sl_tuning {
+    int gemm_cfg = 10;        // SL_GEMM_CFG: tile configuration of the bf16 NT GEMM
+    int gemm_grp = 8;         // SL_GEMM_GRP: tile rows per group of the GEMM tile order
+    int gemm_split = 1;       // SL_GEMM_SPLIT: split the last partial round into K-chunks
+    int splitk_max = 4;       // SL_SPLITK_MAX: largest split-K of dense output rows
+    int lora_xl_split = -1;   // SL_LORA_XL_SPLIT: x A^T split-K form (-1: by row length)
+};
+
 struct sl_handle {
     int device = 0;
+    sl_tuning tune;
+    bool ws_fixed = false;    // workspace growth is an error (sl_set_option "workspace_fixed")
+    bool debug = false;       // SL_DEBUG: host checks of index lists (synchronises)
     bool timing = false;                  // record events around the main launches
     int timing_cls = -1;                  // only launches of this class (-1: all)
     std::vector<sl_timed_launch> timed;   // launches recorded since timing was enabled
@@ -121,9 +134,9 @@ struct GemmProblem {
 // skws: fp32 scratch for the split tail of the default NT configuration (the
 // partial round's tiles run as K-chunks); nullptr or too small: no split
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st,
-                            float* skws = nullptr, size_t skws_floats = 0, int ncu = 256);
+                            float* skws, size_t skws_floats, int ncu, const sl_tuning& tune);
 // floats of scratch the split tail of these problems wants (0: none)
-size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu);
+size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu, const sl_tuning& tune);
 // rank-r term only (K = 0 problem), bf16 output
 // y[rows[m], c] (+)= scale * P[rows[m], :] . B[c, :] over all C channels (bf16 y,
 // fp32 P, bf16 B [C, r]); beta = 0 writes every channel, beta = 1 only the

@@ -88,6 +88,11 @@ class SparseFFN:
         self.side = torch.cuda.Stream(device=dev)
         self._ev = [torch.cuda.Event() for _ in range(5)]
         assert dense or criterion != "svd" or self.k > 0, "the estimator factors are required"
+        # stream plan: the gate|up product of the output rows on the second
+        # stream during the selection, and the LoRA gradient reductions on the
+        # second stream next to the backward products
+        self.overlap_out_rows = True
+        self.side_lora_grads = True
         self._T = None
 
     def set_dense(self, dense: bool):
@@ -160,7 +165,8 @@ class SparseFFN:
         # every channel, so it does not wait for the selection) -- both overlap
         # the estimator, scoring and selection on the main stream, whose small
         # launches leave most compute units idle
-        overlap = not self.dense and self.criterion != "oracle"   # "oracle" scores in gu first
+        overlap = (self.overlap_out_rows and not self.dense
+                   and self.criterion != "oracle")   # "oracle" scores in gu first
         self._ev[0].record(main)
         self.side.wait_event(self._ev[0])
         lora = (self.xl_gu, self.B_bd, 2 * r, self.scale)
@@ -239,7 +245,7 @@ class SparseFFN:
         # (issued after the main-stream product: the host's time on these calls
         # overlaps that product)
         self.side.wait_event(self._ev[0])
-        with torch.cuda.stream(self.side):
+        with torch.cuda.stream(self.side if self.side_lora_grads else main):
             ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.h, None, None, s, self.xl_dn, dy=dy,
                              dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
         g, u = self.gu[:, :F], self.gu[:, F:]
@@ -254,7 +260,7 @@ class SparseFFN:
                               self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s),
                               w_slice=self.ws_gu if self._slices else None)
         self.side.wait_event(self._ev[1])
-        with torch.cuda.stream(self.side):
+        with torch.cuda.stream(self.side if self.side_lora_grads else main):
             ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=self.dgu, dA=self.dA_gu,
                              gB=self.gB_gu, D_in=D, r=2 * r)
             ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,

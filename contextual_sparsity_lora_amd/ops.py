@@ -89,6 +89,27 @@ def sync(device: int = 0):
         _check(h, _lib.load().sl_sync(h), "sl_sync")
 
 
+def set_option(device: int, name: str, value: int):
+    """sl_set_option on every handle of the device (its streams)."""
+    for h in _device_handles(device):
+        _check(h, _lib.load().sl_set_option(h, name.encode(), int(value)), "sl_set_option")
+
+
+def fix_workspaces(device: int = 0):
+    """After a first step has sized them: the device's handles grow their
+    workspaces no more (a call needing more fails instead of allocating)."""
+    set_option(device, "workspace_fixed", 1)
+
+
+def workspace_bytes(device: int = 0) -> int:
+    tot = 0
+    for h in _device_handles(device):
+        b = ctypes.c_size_t()
+        _check(h, _lib.load().sl_workspace_bytes(h, ctypes.byref(b)), "sl_workspace_bytes")
+        tot += b.value
+    return tot
+
+
 def timing_enable(device: int, enable: bool):
     for h in _device_handles(device):
         _check(h, _lib.load().sl_timing_enable(h, int(enable)), "sl_timing_enable")

@@ -104,6 +104,29 @@ sl_status sl_destroy(sl_handle* h);
 sl_status sl_set_stream(sl_handle* h, void* hip_stream);
 /* Ensure the internal workspace holds at least `bytes` (allocates now). */
 sl_status sl_reserve_workspace(sl_handle* h, size_t bytes);
+/* Bytes of device memory the handle's workspaces hold now (the internal
+ * workspace plus the GEMM's split-tail scratch). */
+sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
+/* Handle options (integers):
+ *   "workspace_fixed"  1: no call grows the workspace any more -- a call that
+ *                      would need more returns SL_ERR_WORKSPACE before
+ *                      launching, and a GEMM whose split tail does not fit the
+ *                      scratch runs every tile whole.  For steady-state steps
+ *                      after a first step has sized the workspace: no
+ *                      allocation, free or synchronisation happens in them.
+ *   "debug"            1: before launching, calls that take index lists
+ *                      (selections, row lists) copy them to the host after a
+ *                      stream synchronisation and return SL_ERR_INVALID unless
+ *                      they are strictly ascending and in range (also set by
+ *                      the environment variable SL_DEBUG=1 at sl_create).
+ *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "lora_xl_split"
+ *                      launch tuning of the GEMM and LoRA kernels (tile
+ *                      configuration, tile-order group, split tail on/off,
+ *                      largest split-K, x A^T split form); read from the
+ *                      environment variables of the same names in upper case
+ *                      with an SL_ prefix at sl_create.
+ * Unknown names return SL_ERR_INVALID. */
+sl_status sl_set_option(sl_handle* h, const char* name, int64_t value);
 /* Wait for the handle's stream; reports asynchronous HIP errors. */
 sl_status sl_sync(sl_handle* h);
 /* Human-readable text of the last error on this handle ("" if none). */

@@ -451,7 +451,7 @@ def test_lora_gb_with_transposed_b(D_out, r, rng):
 def test_row_subset_calls(direction, rng):
     """ONLY_OUT_ROWS and ONLY_CTX_ROWS split a side-OUT-shaped product (forward
     side "out", backward side "in") into its two row sets: each call writes its
-    rows only, the out-row call reads no selection (a garbage index list), and
+    rows only, the out-row call does not use the selection (it is given a wrong one), and
     the two together match the oracle.  Row-subset flags on the other shape are
     refused."""
     ops = _ops()
@@ -466,7 +466,9 @@ def test_row_subset_calls(direction, rng):
     idx = np.sort(rng.choice(Dout, 333, replace=False)).astype(np.int32)
     lora = (to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s)
     Wd, Wtd = dev_pad(W, "bf16"), dev_pad(np.ascontiguousarray(W.T), "bf16")
-    garbage = torch.full((len(idx),), 1 << 30, dtype=torch.int32, device=DEV)
+    # valid but wrong: the first channels of the complement, ascending and in range
+    wrong = np.setdiff1d(np.arange(Dout, dtype=np.int32), idx)[:len(idx)]
+    wrong_d = to_dev(wrong, None)
     y = empty_pad(T, Dout, "bf16", fill=7.0)
     lterm = s * (P.astype(np.float64) @ Bm.T.astype(np.float64))
     if direction == "fwd":
@@ -479,7 +481,7 @@ def test_row_subset_calls(direction, rng):
         dyd = dev_pad(x, "bf16")
         call = lambda ix, f: ops.sparse_linear_bwd("in", dyd, None, Wd, c_d, o_d, ix, y, lora=lora, flags=f)
         want = ref.sparse_linear_bwd("in", x, Wi, roles, idx) + lterm
-    call(garbage, ops.ONLY_OUT_ROWS)
+    call(wrong_d, ops.ONLY_OUT_ROWS)
     torch.cuda.synchronize()
     got = host(y)
     assert np.all(got[ctx] == 7.0)                      # context rows untouched

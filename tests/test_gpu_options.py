@@ -1,0 +1,90 @@
+"""Handle options on the GPU: debug mode's host check of index lists, and a
+fixed workspace that refuses to grow."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import reference as ref
+from tests.gpu_util import TOL, dev_pad, empty_pad, host, mar, need_lib, to_dev
+from workloads.gen import round_dtype
+
+pytestmark = pytest.mark.gpu
+
+
+def _ops():
+    need_lib()
+    from contextual_sparsity_lora_amd import ops
+    return ops
+
+
+def _problem(rng, T, T_c, Din, Dout, n):
+    roles = np.zeros(T, dtype=np.uint8)
+    roles[T_c:] = 1
+    ctx, out = ref.token_lists(roles)
+    x = round_dtype(rng.standard_normal((T, Din)), "bf16")
+    W = round_dtype(rng.standard_normal((Dout, Din)) * 0.05, "bf16")
+    idx = np.sort(rng.choice(Dout, n, replace=False)).astype(np.int32)
+    return roles, to_dev(ctx, None), to_dev(out, None), x, W, idx
+
+
+def test_debug_rejects_bad_lists_before_launch(rng):
+    """With "debug" on, an index list out of range or not strictly ascending
+    is refused on the host before anything is launched; a valid one runs."""
+    ops = _ops()
+    roles, c, o, x, W, idx = _problem(rng, 300, 200, 256, 512, 100)
+    print("[options] debug lists", flush=True)
+    xd, Wd = dev_pad(x, "bf16"), dev_pad(W, "bf16")
+    y = empty_pad(x.shape[0], W.shape[0], "bf16", fill=3.0)
+    oob, neg = idx.copy(), idx.copy()
+    oob[-1] = W.shape[0]
+    neg[0] = -1
+    bad = [oob, neg, idx[::-1].copy(), np.concatenate([idx[:50], idx[49:99]])]
+    ops.set_option(0, "debug", 1)
+    try:
+        for b in bad:
+            with pytest.raises(ops.SLError, match="idx"):
+                ops.sparse_linear_fwd("out", xd, Wd, None, c, o, to_dev(b.astype(np.int32), None), y)
+        torch.cuda.synchronize()
+        assert np.all(host(y) == 3.0)   # nothing was launched
+        ops.sparse_linear_fwd("out", xd, Wd, None, c, o, to_dev(idx, None), y)
+        torch.cuda.synchronize()
+        assert mar(host(y), ref.sparse_linear_fwd("out", x, W, roles, idx)) <= TOL["bf16"]
+    finally:
+        ops.set_option(0, "debug", 0)
+
+
+def test_fixed_workspace_refuses_growth(rng):
+    """On a handle of its own (a new stream): a first call sizes the
+    workspace; with "workspace_fixed" on the same call runs and a call needing
+    more is refused without allocating; with it off again that call runs."""
+    ops = _ops()
+    print("[options] fixed workspace", flush=True)
+    small = _problem(rng, 300, 200, 256, 512, 100)
+    large = _problem(rng, 1200, 1000, 256, 2048, 1500)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        dev = [(r, c, o, x, W, i, dev_pad(x, "bf16"), dev_pad(W, "bf16"),
+                empty_pad(x.shape[0], W.shape[0], "bf16")) for r, c, o, x, W, i in (small, large)]
+
+        def call(k):
+            r, c, o, x, W, i, xd, Wd, y = dev[k]
+            ops.sparse_linear_fwd("out", xd, Wd, None, c, o, to_dev(i, None), y)
+
+        call(0)
+        st.synchronize()
+        held = ops.workspace_bytes(0)
+        ops.set_option(0, "workspace_fixed", 1)
+        try:
+            call(0)
+            with pytest.raises(ops.SLError, match="workspace"):
+                call(1)
+            st.synchronize()
+            assert ops.workspace_bytes(0) == held
+        finally:
+            ops.set_option(0, "workspace_fixed", 0)
+        call(1)
+        st.synchronize()
+        assert ops.workspace_bytes(0) > held
+        for k in (0, 1):
+            r, c, o, x, W, i, xd, Wd, y = dev[k]
+            assert mar(host(y), ref.sparse_linear_fwd("out", x, W, r, i)) <= TOL["bf16"]
