@@ -3,9 +3,10 @@
 // AdamW update of the LoRA parameters.
 //
 // Pages (all titled "SparseLoRA: Accelerating LLM Fine-Tuning with Contextual
-// Sparsity"): paper-graph summary, "Putting It All Together": the loss is
-// computed on output token positions only (the standard autoregressive loss),
-// and only the LoRA parameters A and B are updated; "Interaction with the
+// Sparsity"): paper-graph summary, "Putting It All Together": the training
+// objective counts the target (output) positions alone, as in ordinary
+// next-token fine-tuning, and the adapters' A and B are the only trained
+// parameters; "Interaction with the
 // learning rate schedule": cosine schedule with a 4 % warm-up (the rate is the
 // caller's scalar per step).
 #include "sl_internal.h"
@@ -37,6 +38,8 @@ __device__ __forceinline__ float block_tree(float v, float* sh, Op op) {
 // Row m of the listed rows: t = rows[m], logits z = L[t, 0:V], label y = labels[t].
 //   loss[m] = logsumexp(z) - z[y]   (fp32, max-shifted)
 //   dL[t, c] = scale * (softmax(z)[c] - [c == y])
+// A label outside [0, V) (an ignore index such as -100) marks the row as
+// ignored: loss[m] = 0 and dL[t, :] = 0; z is then not read at all.
 // Thread i takes columns i, i + CE_T, ... (fixed order), then the block tree.
 template <typename T>
 __global__ __launch_bounds__(CE_T) void ce_rows_kernel(const T* __restrict__ L, int64_t ldl_,
@@ -48,6 +51,13 @@ __global__ __launch_bounds__(CE_T) void ce_rows_kernel(const T* __restrict__ L, 
     const int64_t t = rows[blockIdx.x];
     const T* z = L + t * ldl_;
     const int tid = threadIdx.x;
+    const int64_t y = labels[t];
+    T* d = dL + t * lddl;
+    if (y < 0 || y >= V) {   // ignored row (uniform across the block)
+        if (tid == 0) loss[blockIdx.x] = 0.0f;
+        for (int64_t c = tid; c < V; c += CE_T) stl(d, c, 0.0f);
+        return;
+    }
     float mx = -__builtin_huge_valf();
     for (int64_t c = tid; c < V; c += CE_T) mx = fmaxf(mx, ldl(z, c));
     mx = block_tree(mx, sh, [](float a, float b) { return fmaxf(a, b); });
@@ -55,9 +65,7 @@ __global__ __launch_bounds__(CE_T) void ce_rows_kernel(const T* __restrict__ L, 
     for (int64_t c = tid; c < V; c += CE_T) s += expf(ldl(z, c) - mx);
     s = block_tree(s, sh, [](float a, float b) { return a + b; });
     const float lse = mx + logf(s);
-    const int64_t y = labels[t];
     if (tid == 0) loss[blockIdx.x] = lse - ldl(z, y);
-    T* d = dL + t * lddl;
     for (int64_t c = tid; c < V; c += CE_T) {
         const float p = expf(ldl(z, c) - lse);
         stl(d, c, scale * (p - (c == y ? 1.0f : 0.0f)));

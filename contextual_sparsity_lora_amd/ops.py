@@ -385,7 +385,9 @@ def svd_factors(W, Wt, k, WA_t, WB, oversample=16, iters=3, seed=0):
 def token_ce(logits, rows, labels, dlogits, loss, scale=None):
     """Softmax cross-entropy of logits [T, V] on the listed rows against
     labels[row]; dlogits = scale (softmax - onehot) on those rows; loss (fp64
-    [1] on the device) = scale * sum of row losses (scale default 1/len(rows))."""
+    [1] on the device) = scale * sum of row losses (scale default 1/len(rows)).
+    A row whose label is outside [0, V) is ignored (zero loss, zero gradient);
+    pass scale = 1 / (rows with a label in range) for the mean over the rest."""
     h = handle(_dev(logits))
     n = rows.numel()
     if scale is None:

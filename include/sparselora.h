@@ -462,14 +462,16 @@ sl_status sl_svd_factors(sl_handle* h, sl_dtype dt, const void* W, int64_t ldw, 
 /* ---------------------------------------------------------------- training step */
 
 /* Token loss on the listed rows (paper-graph summary, "Putting It All
- * Together": the loss is computed only on output token positions, the
- * standard autoregressive loss): for m < n_rows, t = rows[m], z =
- * logits[t, 0:V], y = labels[t] (0 <= y < V),
+ * Together": only the target positions enter the objective, as in ordinary
+ * next-token fine-tuning): for m < n_rows, t = rows[m], z = logits[t, 0:V],
+ * y = labels[t],
  *   row loss   = logsumexp(z) - z[y]                       (fp32, max-shifted)
  *   dlogits[t, c] = scale * (softmax(z)[c] - [c == y])     (dt)
  *   *loss      = scale * sum of the row losses             (fp64, fixed order)
- * scale = 1 / n_rows gives the mean loss and its gradient.  Rows not listed
- * are not touched.  logits, dlogits device (dt) [*, ld >= V]; rows device
+ * A label outside [0, V) (an ignore index such as -100) marks its row as
+ * ignored: row loss 0 and dlogits[t, :] = 0.  scale = 1 / (number of rows
+ * with a label in range) gives the mean loss and its gradient.  Rows not
+ * listed are not touched.  logits, dlogits device (dt) [*, ld >= V]; rows device
  * int32 [n_rows]; labels device int32 [*] (indexed by row); loss device fp64
  * [1] out.  dt = SL_BF16 or SL_F32. */
 sl_status sl_token_ce(sl_handle* h, sl_dtype dt, const void* logits, int64_t ld, const int32_t* rows,

@@ -436,18 +436,25 @@ def round_to(a, dtype):
 
 def token_ce(logits, labels):
     """Mean softmax cross-entropy of the rows of logits [n, V] against integer
-    labels [n], and its gradient with respect to the logits."""
+    labels [n], and its gradient with respect to the logits.  A label outside
+    [0, V) (an ignore index such as -100) marks a position that is not a
+    target: it adds nothing to the loss, has a zero gradient row, and is not
+    counted in the mean."""
     z = np.asarray(logits, f64)
-    n = z.shape[0]
-    if n == 0:
+    labels = np.asarray(labels).astype(np.int64)
+    n, V = z.shape
+    keep = (labels >= 0) & (labels < V)
+    nv = int(keep.sum())
+    if nv == 0:
         return 0.0, np.zeros_like(z)
     zmax = z.max(axis=1, keepdims=True)
     lse = zmax[:, 0] + np.log(np.exp(z - zmax).sum(axis=1))
-    rows = np.arange(n)
-    loss = float(np.mean(lse - z[rows, labels]))
+    rows = np.nonzero(keep)[0]
+    loss = float(np.sum(lse[rows] - z[rows, labels[rows]]) / nv)
     p = np.exp(z - lse[:, None])
-    p[rows, labels] -= 1.0
-    return loss, p / n
+    p[rows, labels[rows]] -= 1.0
+    p[~keep] = 0.0
+    return loss, p / nv
 
 
 def adamw(p, g, m, v, step, lr, b1=0.9, b2=0.999, eps=1e-8, wd=0.0):

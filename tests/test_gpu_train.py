@@ -40,6 +40,31 @@ def test_token_ce(dtype, n, V, rng):
     assert np.all(got[others] == 7.0)
 
 
+def test_token_ce_ignored_labels(rng):
+    """Rows whose label lies outside [0, V) (-100, V, a large value) get a zero
+    loss and a zero gradient row; with scale = 1 / (rows with a label in
+    range) the loss and gradient are the oracle's ignore-index mean."""
+    ops = _ops()
+    T, V = 200, 300
+    z = round_dtype(rng.standard_normal((T, V)) * 4, "bf16")
+    rows = np.sort(rng.choice(T, 90, replace=False)).astype(np.int32)
+    lab = rng.integers(0, V, size=T).astype(np.int32)
+    bad = rows[::7]
+    lab[bad] = np.resize(np.array([-100, V, 1 << 30, -1], np.int32), len(bad))
+    nv = int(np.sum((lab[rows] >= 0) & (lab[rows] < V)))
+    dz = empty_pad(T, V, "bf16", fill=7.0)
+    loss = torch.zeros(1, dtype=torch.float64, device=DEV)
+    print("[train] token loss with ignored labels", flush=True)
+    ops.token_ce(dev_pad(z, "bf16"), to_dev(rows, None), to_dev(lab, None), dz, loss, scale=1.0 / nv)
+    torch.cuda.synchronize()
+    want_loss, want_dz = ref.token_ce(z[rows], lab[rows])
+    assert abs(float(loss.item()) - want_loss) <= 1e-3 * max(1.0, abs(want_loss))
+    got = host(dz)
+    assert np.all(got[bad] == 0.0)
+    assert mar(got[rows], want_dz) <= TOL["bf16"]
+    assert np.all(got[np.setdiff1d(np.arange(T), rows)] == 7.0)
+
+
 def test_adamw_step_matches_oracle(rng):
     ops = _ops()
     shapes = [(16, 520), (1400, 16), (1, 7), (33, 1)]

@@ -25,6 +25,24 @@ def test_token_ce_matches_torch(rng):
     assert ref.token_ce(np.zeros((0, 5)), np.zeros(0, int))[0] == 0.0
 
 
+def test_token_ce_ignored_labels_match_torch(rng):
+    """Positions whose label is the ignore index -100 drop out of the loss, its
+    mean and its gradient, as torch's cross_entropy(ignore_index=-100) does."""
+    z = rng.standard_normal((12, 23)) * 3
+    y = rng.integers(0, 23, size=12)
+    y[[0, 5, 6, 11]] = -100
+    loss, dz = ref.token_ce(z, y)
+    zt = torch.tensor(z, requires_grad=True)
+    lt = torch.nn.functional.cross_entropy(zt, torch.tensor(y), ignore_index=-100)
+    lt.backward()
+    assert loss == pytest.approx(float(lt.detach()), abs=1e-13)
+    assert np.allclose(dz, zt.grad.numpy(), atol=1e-15, rtol=1e-12)
+    assert np.all(dz[[0, 5, 6, 11]] == 0.0)
+    # every label ignored: zero loss, zero gradient
+    l0, d0 = ref.token_ce(z[:3], np.array([-100, 23, 99]))
+    assert l0 == 0.0 and np.all(d0 == 0.0)
+
+
 def test_adamw_matches_torch(rng):
     p0 = rng.standard_normal((4, 6))
     pt = torch.tensor(p0, requires_grad=True)
