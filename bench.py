@@ -39,6 +39,10 @@ def parse():
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the sparse/dense step times of the other workloads (projections, "
                          "layer, 32-layer stack, fp32 block)")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="issue every launch of the block on one stream (clean per-kernel times "
+                         "for profiles; the default overlaps LoRA reductions and the output-row "
+                         "product on a second stream)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -81,7 +85,7 @@ def measured_traffic():
         return None
 
 
-def build_block(inp, cfg, dense, criterion="svd"):
+def build_block(inp, cfg, dense, criterion="svd", single_stream=False):
     import numpy as np
     import torch
     from contextual_sparsity_lora_amd.ffn import SparseFFN
@@ -92,7 +96,8 @@ def build_block(inp, cfg, dense, criterion="svd"):
                     t["B_up"], t["A_down"], t["B_down"],
                     torch.from_numpy(np.ascontiguousarray(inp["WA_t_gu"].T)).to(dev),
                     torch.from_numpy(inp["WB_gate"]).to(dev), torch.from_numpy(inp["WB_up"]).to(dev),
-                    inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense, criterion=criterion)
+                    inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense, criterion=criterion,
+                    single_stream=single_stream)
     roles = torch.from_numpy(inp["roles"]).to(dev)
     return blk, t["x"], roles, t["dy"]
 
@@ -340,7 +345,7 @@ def main():
     t0 = time.perf_counter()
     inp = make_ffn_inputs(cfg)
     print(f"[bench] inputs ready in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
-    blk, x, roles, dy = build_block(inp, cfg, dense=False)
+    blk, x, roles, dy = build_block(inp, cfg, dense=False, single_stream=args.single_stream)
     T = cfg.tokens
     # per-class breakdown from a short instrumented pass of its own: events
     # around every launch add time between launches, so the timed pass below
@@ -394,7 +399,7 @@ def main():
         sparse_grads = types.SimpleNamespace(**{k: v.clone() for k, v in fidelity.lora_grads(blk).items()})
         del blk
         torch.cuda.empty_cache()
-        dblk, x, roles, dy = build_block(inp, cfg, dense=True)
+        dblk, x, roles, dy = build_block(inp, cfg, dense=True, single_stream=args.single_stream)
         dms_step = time_steps(dblk, x, roles, dy, cfg.ctx_tokens, args.steps, args.warmup, ops)
         extra["dense_ms_per_step"] = round(dms_step, 4)
         extra["speedup_vs_dense"] = round(dms_step / ms, 3)
@@ -425,7 +430,7 @@ def main():
                    "output_tokens_per_seq": cfg.out_per_seq, "lora_rank": cfg.lora_rank,
                    "estimator_rank": cfg.est_rank, "ffn_sparsity": "7/10",
                    "kept_channels": blk_n(cfg), "global_batch": cfg.batch, "seq_len": cfg.seq,
-                   "parallelism": "single-gpu"},
+                   "parallelism": "single-gpu", "streams": 1 if args.single_stream else 2},
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -790,6 +790,243 @@ __global__ void swiglu_bwd_kernel(const T* __restrict__ dh, int64_t lddh, const 
     }
 }
 
+// ---------------------------------------------------------------- SwiGLU with the LoRA reductions
+// The SwiGLU passes also form the LoRA reductions that read the same tensors,
+// so each tensor is read once (bf16, 16-byte rows, F % 8 == 0).  The
+// reductions run on the matrix cores in fp32 (v_mfma_f32_16x16x4_f32): the
+// bf16 values and the fp32 factors enter exactly and accumulate in fp32; a
+// fixed-order sum over the blocks' partials follows (deterministic).
+
+__device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        f[2 * q] = __uint_as_float(w[q] << 16);
+        f[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+    }
+}
+
+// Forward: h = silu(g) u (as swiglu_fwd) and the row partials of
+// xl[t, j] = sum_c h[t, c] A[j, c] from the stored (bf16) h.  A block of 4
+// waves shares 16 rows; wave w takes SFW columns from its block's start, 128
+// at a time.  Loads and stores go 4 rows at a time with 16 lanes on each
+// row's 256 bytes (lane l: row 4 s + l / 16, columns 8 (l % 16) + e); h then
+// passes through the wave's LDS tile to the matrix-core layout (lane l: row
+// l % 16, columns 32 s + 8 (l / 16) + e).  MFMA (s, e): A[m][k] = h[t0 + m][32 s
+// + 8 k + e], B[k][n] = A_lora[n][same column]; D[m][n] gathers the row's sum
+// over the wave's columns.  The waves' sums meet in LDS in wave order; the
+// block writes part[blockIdx.x][t][j].
+constexpr int SFW = 512;
+
+template <int NR>
+__global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
+    const bf16_t* __restrict__ g, int64_t ldg, const bf16_t* __restrict__ u, int64_t ldu, int64_t Tn, int64_t F,
+    bf16_t* __restrict__ h, int64_t ldh, const bf16_t* __restrict__ A, int64_t lda, int64_t r,
+    float* __restrict__ part) {
+    constexpr int RW = 16 * NR;
+    __shared__ float red[4][16][RW + 1];
+    __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rr = lane & 15, kq = lane >> 4;       // matrix-core layout
+    const int cg = lane & 15, rs = lane >> 4;       // load layout
+    const int64_t t0 = (int64_t)blockIdx.y * 16;
+    const int64_t cw = (int64_t)blockIdx.x * (4 * SFW) + (int64_t)wid * SFW;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    f32x4 acc[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) acc[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int64_t cs = cw; cs < cw + SFW && cs < F; cs += 128) {
+        uint4 gv[4], uv[4], av[4][NR];
+        const int64_t cl = cs + 8 * cg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int64_t t = t0 + 4 * s + rs;
+            const bool ok = t < Tn && cl < F;
+            gv[s] = ok ? *(const uint4*)(g + t * ldg + cl) : zero;
+            uv[s] = ok ? *(const uint4*)(u + t * ldu + cl) : zero;
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const int64_t j = 16 * k + rr, c = cs + 32 * s + 8 * kq;
+                av[s][k] = (c < F && j < r) ? *(const uint4*)(A + j * lda + c) : zero;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float gf[8], uf[8];
+            unpack_bf16x8(gv[s], gf);
+            unpack_bf16x8(uv[s], uf);
+            uint32_t w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float h0 = gf[2 * q] * sigmoid_hw(gf[2 * q]) * uf[2 * q];
+                const float h1 = gf[2 * q + 1] * sigmoid_hw(gf[2 * q + 1]) * uf[2 * q + 1];
+                w[q] = pack_bf16x2(h0, h1);
+            }
+            const uint4 hv = make_uint4(w[0], w[1], w[2], w[3]);
+            const int64_t t = t0 + 4 * s + rs;
+            if (t < Tn && cl < F) *(uint4*)(h + t * ldh + cl) = hv;
+            *(uint4*)&tile[wid][4 * s + rs][8 * cg] = hv;   // rows past T / columns past F: zeros
+        }
+        // (this wave's own LDS rows: in-order LDS access within the wave)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float hb[8];
+            unpack_bf16x8(*(const uint4*)&tile[wid][rr][32 * s + 8 * kq], hb);
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                float af[8];
+                unpack_bf16x8(av[s][k], af);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], af[e], acc[k], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // lane holds D[4 (l / 16) + i][l % 16]: row t0 + 4 kq + i, rank 16 k + rr
+#pragma unroll
+    for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wid][4 * kq + i][16 * k + rr] = acc[k][i];
+    __syncthreads();
+    for (int q = threadIdx.x; q < 16 * RW; q += 256) {
+        const int row = q / RW, j = q % RW;
+        const float v = ((red[0][row][j] + red[1][row][j]) + red[2][row][j]) + red[3][row][j];
+        if (t0 + row < Tn) part[((int64_t)blockIdx.x * Tn + t0 + row) * RW + j] = v;
+    }
+}
+
+// Backward: dg, du as swiglu_bwd, plus the token reductions over the same
+// tiles: P0[c][j] = sum_t h[t, c] Y0[t, j] (h = silu(g) u recomputed exactly
+// as the forward stored it), P1[c][j] = sum_t dg[t, c] Y1[t, j], P2[c][j] =
+// sum_t du[t, c] Y2[t, j] (dg, du as stored).  A block of 4 waves covers 512
+// columns (wave: 128; lane l: the 8 columns 8 (l % 16) + e of row t0 + l / 16,
+// so a row's 256 bytes leave as one run) and the rows of one chunk, 4 at a
+// time.  MFMA (e): A[m][k] = X[t0 + k][cw + 8 m + e], B[k][n] = Y[t0 + k][n];
+// D accumulates over the chunk; each chunk writes part[p][chunk][c][j].
+template <int NR>
+__global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
+    const bf16_t* __restrict__ dh, int64_t lddh, const bf16_t* __restrict__ g, int64_t ldg,
+    const bf16_t* __restrict__ u, int64_t ldu, int64_t Tn, int64_t F, bf16_t* __restrict__ dg, int64_t lddg,
+    bf16_t* __restrict__ du, int64_t lddu, const float* __restrict__ Y0, int64_t ldy0,
+    const float* __restrict__ Y1, int64_t ldy1, const float* __restrict__ Y2, int64_t ldy2, int64_t r,
+    int64_t rows_per_chunk, float* __restrict__ part) {
+    constexpr int RW = 16 * NR;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int cg = lane & 15, rs = lane >> 4;
+    const int64_t cw = (int64_t)blockIdx.x * 512 + (int64_t)wid * 128;
+    const int64_t c = cw + 8 * cg;
+    const bool cv = c < F;
+    const int64_t tb = (int64_t)blockIdx.y * rows_per_chunk;
+    const int64_t te = (Tn - tb) < rows_per_chunk ? Tn : tb + rows_per_chunk;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    f32x4 acc[3][NR][8];
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[p][k][e] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    constexpr int U = 1;   // 4-row slabs per load batch (2 measured slower: the extra registers halve occupancy)
+    for (int64_t tu = tb; tu < te; tu += 4 * U) {
+        uint4 vd[U], vg[U], vu[U];
+        float y0[U][NR], y1[U][NR], y2[U][NR];
+#pragma unroll
+        for (int sl = 0; sl < U; ++sl) {
+            const int64_t t = tu + 4 * sl + rs;
+            const bool tv = t < te;
+            const bool ok = cv && tv;
+            vd[sl] = ok ? *(const uint4*)(dh + t * lddh + c) : zero;
+            vg[sl] = ok ? *(const uint4*)(g + t * ldg + c) : zero;
+            vu[sl] = ok ? *(const uint4*)(u + t * ldu + c) : zero;
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                const int64_t j = 16 * k + cg;
+                const bool yv = tv && j < r;
+                y0[sl][k] = yv ? Y0[t * ldy0 + j] : 0.0f;
+                y1[sl][k] = yv ? Y1[t * ldy1 + j] : 0.0f;
+                y2[sl][k] = yv ? Y2[t * ldy2 + j] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < U; ++sl) {
+            const int64_t t = tu + 4 * sl + rs;
+            const bool ok = cv && t < te;
+            float d[8], gf[8], uf[8];
+            unpack_bf16x8(vd[sl], d);
+            unpack_bf16x8(vg[sl], gf);
+            unpack_bf16x8(vu[sl], uf);
+            uint32_t wa[4], wb[4], wh[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float a2[2], b2[2], h2[2];
+#pragma unroll
+                for (int o = 0; o < 2; ++o) {
+                    const int e = 2 * q + o;
+                    const float sg = sigmoid_hw(gf[e]);
+                    a2[o] = d[e] * uf[e] * (sg * (1.0f + gf[e] * (1.0f - sg)));
+                    b2[o] = d[e] * (gf[e] * sg);
+                    h2[o] = gf[e] * sg * uf[e];
+                }
+                wa[q] = pack_bf16x2(a2[0], a2[1]);
+                wb[q] = pack_bf16x2(b2[0], b2[1]);
+                wh[q] = pack_bf16x2(h2[0], h2[1]);
+            }
+            const uint4 va = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+            const uint4 vb = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+            if (ok) {
+                *(uint4*)(dg + t * lddg + c) = va;
+                *(uint4*)(du + t * lddu + c) = vb;
+            }
+            float hb[8], ab[8], bb[8];
+            unpack_bf16x8(make_uint4(wh[0], wh[1], wh[2], wh[3]), hb);
+            unpack_bf16x8(va, ab);
+            unpack_bf16x8(vb, bb);
+#pragma unroll
+            for (int k = 0; k < NR; ++k)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    acc[0][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], y0[sl][k], acc[0][k][e], 0, 0, 0);
+                    acc[1][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[e], y1[sl][k], acc[1][k][e], 0, 0, 0);
+                    acc[2][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(bb[e], y2[sl][k], acc[2][k][e], 0, 0, 0);
+                }
+        }
+    }
+    // lane holds D[4 (l / 16) + i][l % 16] of MFMA e: column cw + 8 (4 rs + i) + e, rank 16 k + cg
+    const int64_t nch = gridDim.y;
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t col = cw + 8 * (4 * rs + i) + e;
+                    const int64_t j = 16 * k + cg;
+                    if (col < F && j < r)
+                        part[(((int64_t)p * nch + blockIdx.y) * F + col) * RW + j] = acc[p][k][e][i];
+                }
+}
+
+// out[a soa + j soj] = scale * sum over ch = 0.. of part[(ch A + a) RW + j]
+// (ascending ch), j < r: the ordered sum of the fused kernels' partials.
+__global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict__ part, int64_t nch, int64_t Adim,
+                                                       int RW, int64_t r, float scale, float* __restrict__ out,
+                                                       int64_t soa, int64_t soj) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= Adim * r) return;
+    const int64_t a = q / r, j = q % r;
+    float s = 0.0f;
+    for (int64_t ch = 0; ch < nch; ++ch) s += part[(ch * Adim + a) * RW + j];
+    out[a * soa + j * soj] = scale * s;
+}
+
 // out[m, q..q+7] = in[rows[m], cols[q..q+7]]: gathered loads, one vector store.
 template <typename T>
 __global__ void gather_cols_kernel(const T* __restrict__ in, int64_t ldi,
@@ -1234,5 +1471,65 @@ hipError_t launch_gather_rows_t(bool bf16, const void* src, int64_t lds, const i
     else
         hipLaunchKernelGGL(gather_rows_t_kernel<float>, grid, dim3(256), 0, st, (const float*)src,
                            lds, idx, n, npad, Dd, (float*)out, ldo);
+    return hipGetLastError();
+}
+
+size_t swiglu_fwd_lora_ws_floats(int64_t T, int64_t F, int64_t r) {
+    const int64_t RW = r <= 16 ? 16 : 32;
+    return (size_t)(ceil_div(F, 4 * SFW) * T * RW);
+}
+
+hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t T, int64_t F,
+                                  void* h, int64_t ldh, const void* A, int64_t lda, int64_t r, float* xl,
+                                  int64_t ldxl, float* part, hipStream_t st) {
+    if (T <= 0 || F <= 0) return hipSuccess;
+    const int64_t ncb = ceil_div(F, 4 * SFW);
+    const dim3 grid((unsigned)ncb, (unsigned)ceil_div(T, 16));
+    const int RW = r <= 16 ? 16 : 32;
+    if (r <= 16)
+        hipLaunchKernelGGL(swiglu_fwd_lora_kernel<1>, grid, dim3(256), 0, st, (const bf16_t*)g, ldg,
+                           (const bf16_t*)u, ldu, T, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
+    else
+        hipLaunchKernelGGL(swiglu_fwd_lora_kernel<2>, grid, dim3(256), 0, st, (const bf16_t*)g, ldg,
+                           (const bf16_t*)u, ldu, T, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
+    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0, st, part, ncb, T, RW,
+                       r, 1.0f, xl, ldxl, (int64_t)1);
+    return hipGetLastError();
+}
+
+size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk) {
+    const int64_t RW = r <= 16 ? 16 : 32;
+    return (size_t)(3 * ceil_div(T, rows_per_chunk) * F * RW);
+}
+
+hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, int64_t ldg, const void* u,
+                                  int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
+                                  int64_t lddu, const float* Y0, int64_t ldy0, const float* Y1, int64_t ldy1,
+                                  const float* Y2, int64_t ldy2, int64_t r, float scale, float* dA, float* dB1,
+                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st) {
+    if (F <= 0) return hipSuccess;
+    // T = 0: no partials; the sums below write zero gradients
+    const int64_t nch = T > 0 ? ceil_div(T, rows_per_chunk) : 0;
+    const dim3 grid((unsigned)ceil_div(F, 512), (unsigned)nch);
+    const int RW = r <= 16 ? 16 : 32;
+#define SBL(NRR)                                                                                               \
+    hipLaunchKernelGGL((swiglu_bwd_lora_kernel<NRR>), grid, dim3(256), 0, st, (const bf16_t*)dh, lddh,          \
+                       (const bf16_t*)g, ldg, (const bf16_t*)u, ldu, T, F, (bf16_t*)dg, lddg, (bf16_t*)du, lddu, \
+                       Y0, ldy0, Y1, ldy1, Y2, ldy2, r, rows_per_chunk, part)
+    if (T <= 0) {
+    } else if (r <= 16) {
+        SBL(1);
+    } else {
+        SBL(2);
+    }
+#undef SBL
+    const dim3 rg((unsigned)ceil_div(F * r, 256));
+    const size_t pstride = (size_t)nch * F * RW;
+    // dA [r, F] (row j, column c); dB [F, r]
+    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part, nch, F, RW, r, scale, dA, (int64_t)1, F);
+    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + pstride, nch, F, RW, r, scale, dB1, r,
+                       (int64_t)1);
+    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + 2 * pstride, nch, F, RW, r, scale, dB2, r,
+                       (int64_t)1);
     return hipGetLastError();
 }

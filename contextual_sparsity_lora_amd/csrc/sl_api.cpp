@@ -248,6 +248,8 @@ sl_status sl_create(sl_handle** out, int device) {
     h->tune.gemm_split = env_int("SL_GEMM_SPLIT", h->tune.gemm_split);
     h->tune.splitk_max = env_int("SL_SPLITK_MAX", h->tune.splitk_max);
     h->tune.lora_xl_split = env_int("SL_LORA_XL_SPLIT", h->tune.lora_xl_split);
+    h->tune.swiglu_rows = env_int("SL_SWIGLU_ROWS", h->tune.swiglu_rows);
+    if (h->tune.swiglu_rows < 4 || h->tune.swiglu_rows % 4 != 0) h->tune.swiglu_rows = 256;
     if (h->tune.gemm_grp < 1 || h->tune.gemm_grp > 64) h->tune.gemm_grp = 8;
     if (h->tune.splitk_max < 1 || h->tune.splitk_max > 16) h->tune.splitk_max = 4;
     h->debug = env_int("SL_DEBUG", 0) != 0;
@@ -311,6 +313,10 @@ sl_status sl_set_option(sl_handle* h, const char* name, int64_t value) {
         h->tune.splitk_max = (int)value;
     }
     else if (n == "lora_xl_split") h->tune.lora_xl_split = (int)value;
+    else if (n == "swiglu_rows") {
+        SL_REQUIRE(h, value >= 4 && value <= 65536 && value % 4 == 0, "swiglu_rows must be a multiple of 4 in [4, 65536]");
+        h->tune.swiglu_rows = (int)value;
+    }
     else if (n == "workspace_fixed") h->ws_fixed = value != 0;
     else if (n == "debug") h->debug = value != 0;
     else return fail(h, SL_ERR_INVALID, "unknown option '%s'", name);
@@ -1234,6 +1240,57 @@ sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
     Timed tm(h, K_SWIGLU, 0, 5.0 * T * F * esize(dt));
     return hip_check(h, launch_swiglu_bwd(dt == SL_BF16, dh, lddh, g, ldg, u, ldu, T, F, dg, lddg,
                                           du, lddu, h->stream), "swiglu_bwd");
+}
+
+sl_status sl_swiglu_fwd_lora(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg, const void* u, int64_t ldu,
+                             int64_t T, int64_t F, void* hout, int64_t ldh, const void* A, int64_t lda, int64_t r,
+                             float* xl, int64_t ldxl) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    if (dt != SL_BF16) return fail(h, SL_ERR_UNSUPPORTED, "the fused SwiGLU + LoRA pass is bf16 only");
+    SL_REQUIRE(h, T >= 0 && T <= 65535 * 16 && F >= 1 && F % 8 == 0, "bad sizes (F must be a multiple of 8)");
+    SL_REQUIRE(h, r >= 1 && r <= 32, "r must be in [1, 32]");
+    if (T == 0) return SL_OK;
+    SL_CHECK(check_matrix(h, g, ldg, F, dt, "g"));
+    SL_CHECK(check_matrix(h, u, ldu, F, dt, "u"));
+    SL_CHECK(check_matrix(h, hout, ldh, F, dt, "h"));
+    SL_CHECK(check_matrix(h, A, lda, F, dt, "A"));
+    SL_REQUIRE(h, xl != nullptr && ldxl >= r, "xl is NULL or ldxl < r");
+    SL_CHECK(ensure_ws(h, round_up(swiglu_fwd_lora_ws_floats(T, F, r) * 4, 256)));
+    DeviceGuard gd(h->device);
+    Timed tm(h, K_SWIGLU, 2.0 * T * F * r, 3.0 * T * F * 2 + 2.0 * r * F + 4.0 * T * r);
+    return hip_check(h, launch_swiglu_fwd_lora(g, ldg, u, ldu, T, F, hout, ldh, A, lda, r, xl, ldxl,
+                                               (float*)h->ws, h->stream), "swiglu_fwd_lora");
+}
+
+sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh, const void* g, int64_t ldg,
+                             const void* u, int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
+                             int64_t lddu, const float* gB, int64_t ldgB, const float* xl_g, int64_t ldxlg,
+                             const float* xl_u, int64_t ldxlu, int64_t r, float scale, float* dA, float* dB_g,
+                             float* dB_u) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    if (dt != SL_BF16) return fail(h, SL_ERR_UNSUPPORTED, "the fused SwiGLU + LoRA pass is bf16 only");
+    SL_REQUIRE(h, T >= 0 && T <= 65535 * 4 && F >= 1 && F % 8 == 0, "bad sizes (F must be a multiple of 8)");
+    SL_REQUIRE(h, r >= 1 && r <= 32, "r must be in [1, 32]");
+    SL_REQUIRE(h, dA && dB_g && dB_u, "dA, dB_g or dB_u is NULL");
+    if (T > 0) {
+        SL_CHECK(check_matrix(h, dh, lddh, F, dt, "dh"));
+        SL_CHECK(check_matrix(h, g, ldg, F, dt, "g"));
+        SL_CHECK(check_matrix(h, u, ldu, F, dt, "u"));
+        SL_CHECK(check_matrix(h, dg, lddg, F, dt, "dg"));
+        SL_CHECK(check_matrix(h, du, lddu, F, dt, "du"));
+        SL_REQUIRE(h, gB && xl_g && xl_u && ldgB >= r && ldxlg >= r && ldxlu >= r,
+                   "gB / xl_g / xl_u NULL or leading dimension < r");
+    }
+    const int64_t rpc = h->tune.swiglu_rows;
+    DeviceGuard gd(h->device);
+    // T = 0: no rows to read; the sums write zero gradients
+    if (T > 0) SL_CHECK(ensure_ws(h, round_up(swiglu_bwd_lora_ws_floats(T, F, r, rpc) * 4, 256)));
+    Timed tm(h, K_SWIGLU, 3.0 * 2.0 * T * F * r, 5.0 * T * F * 2 + 3.0 * 4 * T * r + 3.0 * 4 * r * F);
+    return hip_check(h, launch_swiglu_bwd_lora(dh, lddh, g, ldg, u, ldu, T, F, dg, lddg, du, lddu, gB, ldgB, xl_g,
+                                               ldxlg, xl_u, ldxlu, r, scale, dA, dB_g, dB_u, rpc,
+                                               T > 0 ? (float*)h->ws : nullptr, h->stream), "swiglu_bwd_lora");
 }
 
 sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi, int64_t rows,

@@ -23,6 +23,7 @@ struct sl_tuning {
     int gemm_split = 1;       // SL_GEMM_SPLIT: split the last partial round into K-chunks
     int splitk_max = 4;       // SL_SPLITK_MAX: largest split-K of dense output rows
     int lora_xl_split = -1;   // SL_LORA_XL_SPLIT: x A^T split-K form (-1: by row length)
+    int swiglu_rows = 256;    // SL_SWIGLU_ROWS: rows per partial of the fused SwiGLU backward
 };
 
 struct sl_handle {
@@ -264,6 +265,17 @@ hipError_t launch_transpose(bool bf16, const void* in, int64_t ldi, int64_t rows
                             void* out, int64_t ldo, hipStream_t st);
 hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* u, int64_t ldu,
                              int64_t T, int64_t F, void* h, int64_t ldh, hipStream_t st);
+// SwiGLU with the LoRA reductions reading the same tensors (bf16, r <= 32).
+size_t swiglu_fwd_lora_ws_floats(int64_t T, int64_t F, int64_t r);
+hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t T, int64_t F,
+                                  void* h, int64_t ldh, const void* A, int64_t lda, int64_t r, float* xl,
+                                  int64_t ldxl, float* part, hipStream_t st);
+size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk);
+hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, int64_t ldg, const void* u,
+                                  int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
+                                  int64_t lddu, const float* Y0, int64_t ldy0, const float* Y1, int64_t ldy1,
+                                  const float* Y2, int64_t ldy2, int64_t r, float scale, float* dA, float* dB1,
+                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st);
 hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void* g, int64_t ldg,
                              const void* u, int64_t ldu, int64_t T, int64_t F, void* dg,
                              int64_t lddg, void* du, int64_t lddu, hipStream_t st);

@@ -41,7 +41,7 @@ class SparseFFN:
 
     def __init__(self, W_gate, W_up, W_down, A_gate, B_gate, A_up, B_up, A_down, B_down,
                  WA_gu, WB_gate, WB_up, scale, sparsity=(7, 10), dense=False, criterion="svd",
-                 seed=0):
+                 seed=0, single_stream=False):
         dev = W_gate.device
         self.dtype = W_gate.dtype
         self.F, self.D = W_gate.shape
@@ -84,8 +84,10 @@ class SparseFFN:
         self.WA = cont(WA_gu)                        # [D, 2k] fp32
         self.WB_gate, self.WB_up = cont(WB_gate), cont(WB_up)
         # a second stream (default priority) for the LoRA reductions that nothing
-        # later in the block reads, so they overlap the main-branch products
-        self.side = torch.cuda.Stream(device=dev)
+        # later in the block reads, so they overlap the main-branch products;
+        # single_stream=True issues everything on the caller's stream in the
+        # same order (each kernel then runs alone: clean per-kernel times)
+        self.side = torch.cuda.current_stream(dev) if single_stream else torch.cuda.Stream(device=dev)
         self._ev = [torch.cuda.Event() for _ in range(5)]
         assert dense or criterion != "svd" or self.k > 0, "the estimator factors are required"
         # stream plan: the gate|up product of the output rows on the second
@@ -93,6 +95,10 @@ class SparseFFN:
         # second stream next to the backward products
         self.overlap_out_rows = True
         self.side_lora_grads = True
+        # bf16 blocks run the SwiGLU passes fused with the LoRA reductions that
+        # read the same tensors (h A_down^T forward; dA_down, dB_gate, dB_up
+        # backward), so h, dh, g, u, dg and du are each read once
+        self.fused_swiglu_lora = (self.dtype == torch.bfloat16 and self.r <= 32 and self.F % 8 == 0)
         self._T = None
 
     def set_dense(self, dense: bool):
@@ -202,9 +208,12 @@ class SparseFFN:
                               lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
         main.wait_event(self._ev[3])
         g, u = self.gu[:, :F], self.gu[:, F:]
-        ops.swiglu_fwd(g, u, self.h)
+        if self.fused_swiglu_lora:
+            ops.swiglu_fwd_lora(g, u, self.h, self.A_down, self.xl_dn)
+        else:
+            ops.swiglu_fwd(g, u, self.h)
+            ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
         # down main branch: input channels = the same selection; LoRA fused
-        ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
         ops.sparse_linear_fwd("in", self.h, self.W_dn, self.Wt_dn, self.ctx_rows, self.out_rows,
                               self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale),
                               w_slice=self.ws_dn if self._slices else None)
@@ -245,12 +254,21 @@ class SparseFFN:
         # (issued after the main-stream product: the host's time on these calls
         # overlaps that product)
         self.side.wait_event(self._ev[0])
+        fused = self.fused_swiglu_lora
         with torch.cuda.stream(self.side if self.side_lora_grads else main):
-            ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.h, None, None, s, self.xl_dn, dy=dy,
-                             dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
+            if fused:   # dA_down comes with the SwiGLU backward below
+                ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_dn, dy=dy, dB=self.dB_down,
+                                 D_in=F, r=r)
+            else:
+                ops.lora_fwd_bwd(ops.LORA_DA | ops.LORA_DB, self.h, None, None, s, self.xl_dn, dy=dy,
+                                 dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
         g, u = self.gu[:, :F], self.gu[:, F:]
         dg, du = self.dgu[:, :F], self.dgu[:, F:]
-        ops.swiglu_bwd(self.dh, g, u, dg, du)
+        if fused:
+            ops.swiglu_bwd_lora(self.dh, g, u, dg, du, self.gB_dn, self.xl_gu[:, :r], self.xl_gu[:, r:], s,
+                                self.dA_down, self.dB_gate, self.dB_up)
+        else:
+            ops.swiglu_bwd(self.dh, g, u, dg, du)
         # gate|up: gB for both through the block-diagonal B (main stream); dA
         # and the per-projection dB on the side stream, overlapping the dx product
         ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_bdT, s, None, dy=self.dgu,
@@ -263,10 +281,11 @@ class SparseFFN:
         with torch.cuda.stream(self.side if self.side_lora_grads else main):
             ops.lora_fwd_bwd(ops.LORA_DA, self.x, None, None, s, None, dy=self.dgu, dA=self.dA_gu,
                              gB=self.gB_gu, D_in=D, r=2 * r)
-            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,
-                             dB=self.dB_gate, r=r, D_in=D)
-            ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
-                             dB=self.dB_up, r=r, D_in=D)
+            if not fused:
+                ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, :r], dy=dg,
+                                 dB=self.dB_gate, r=r, D_in=D)
+                ops.lora_fwd_bwd(ops.LORA_DB, None, None, None, s, self.xl_gu[:, r:], dy=du,
+                                 dB=self.dB_up, r=r, D_in=D)
             self._ev[2].record(self.side)
         # the block's gradients are complete when both streams are
         main.wait_event(self._ev[2])

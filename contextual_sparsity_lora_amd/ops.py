@@ -371,6 +371,29 @@ def swiglu_bwd(dh, g, u, dg, du):
     _check(h, st, "sl_swiglu_bwd")
 
 
+def swiglu_fwd_lora(g, u, hout, A, xl):
+    """hout = silu(g) u and xl = hout A^T (fp32 [T, r]) in one pass over g, u
+    (bf16; A [r, F])."""
+    h = handle(_dev(g))
+    T, F = g.shape
+    st = _lib.load().sl_swiglu_fwd_lora(h, _dt(g), _ptr(g), _ld(g), _ptr(u), _ld(u), T, F, _ptr(hout), _ld(hout),
+                                        _ptr(A), _ld(A), A.shape[0], _ptr(xl), _ld(xl))
+    _check(h, st, "sl_swiglu_fwd_lora")
+
+
+def swiglu_bwd_lora(dh, g, u, dg, du, gB, xl_g, xl_u, scale, dA, dB_g, dB_u):
+    """dg, du as swiglu_bwd, with dA = scale gB^T h ([r, F]), dB_g = scale
+    dg^T xl_g and dB_u = scale du^T xl_u ([F, r]) from the same pass (bf16)."""
+    h = handle(_dev(g))
+    T, F = g.shape
+    r = gB.shape[1]
+    st = _lib.load().sl_swiglu_bwd_lora(h, _dt(g), _ptr(dh), _ld(dh), _ptr(g), _ld(g), _ptr(u), _ld(u), T, F,
+                                        _ptr(dg), _ld(dg), _ptr(du), _ld(du), _ptr(gB), _ld(gB), _ptr(xl_g),
+                                        _ld(xl_g), _ptr(xl_u), _ld(xl_u), r, float(scale), _ptr(dA), _ptr(dB_g),
+                                        _ptr(dB_u))
+    _check(h, st, "sl_swiglu_bwd_lora")
+
+
 def svd_factors(W, Wt, k, WA_t, WB, oversample=16, iters=3, seed=0):
     """Rank-k estimator factors of W [D_out, D_in] (with its transposed copy Wt)
     into WA_t fp32 [k, D_in] and WB fp32 [k, D_out]."""

@@ -119,10 +119,11 @@ sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
  *                      stream synchronisation and return SL_ERR_INVALID unless
  *                      they are strictly ascending and in range (also set by
  *                      the environment variable SL_DEBUG=1 at sl_create).
- *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "lora_xl_split"
- *                      launch tuning of the GEMM and LoRA kernels (tile
+ *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "lora_xl_split",
+ *   "swiglu_rows"      launch tuning of the GEMM and LoRA kernels (tile
  *                      configuration, tile-order group, split tail on/off,
- *                      largest split-K, x A^T split form); read from the
+ *                      largest split-K, x A^T split form, rows per partial of
+ *                      the fused SwiGLU backward); read from the
  *                      environment variables of the same names in upper case
  *                      with an SL_ prefix at sl_create.
  * Unknown names return SL_ERR_INVALID. */
@@ -553,6 +554,41 @@ sl_status sl_swiglu_fwd(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg,
 sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
                         const void* g, int64_t ldg, const void* u, int64_t ldu,
                         int64_t T, int64_t F, void* dg, int64_t lddg, void* du, int64_t lddu);
+/* SwiGLU forward fused with the LoRA down-projection of the down projection
+ * (PG §3.4 "FFN structure"; Algorithm 1 step 6: the LoRA branch is dense, so
+ * its input is the whole hidden state h):
+ *   h = silu(g) * u                  (exactly as sl_swiglu_fwd, stored in dt)
+ *   xl[t, j] = sum_c h[t, c] A[j, c] (fp32, from the stored h; as SL_LORA_XL)
+ * so h is read once.  A [r, lda >= F] (dt) is the down projection's LoRA A;
+ * xl fp32 [T, ldxl >= r] out.  bf16 only (SL_ERR_UNSUPPORTED otherwise),
+ * F % 8 == 0, 1 <= r <= 32.  xl's sum is a fixed-order reduction over column
+ * blocks (deterministic). */
+sl_status sl_swiglu_fwd_lora(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg,
+                             const void* u, int64_t ldu, int64_t T, int64_t F,
+                             void* hout, int64_t ldh, const void* A, int64_t lda, int64_t r,
+                             float* xl, int64_t ldxl);
+/* SwiGLU backward fused with the three LoRA gradient reductions that read the
+ * same tensors (PG §3.2 "Information flow during a backward pass": the LoRA
+ * gradients are computed in full; §3.4 "FFN structure"):
+ *   dg, du                     exactly as sl_swiglu_bwd (stored in dt)
+ *   dA[j, c]   = scale * sum_t gB[t, j] h[t, c]     (h = silu(g) u recomputed
+ *                                                     exactly as the forward
+ *                                                     stored it; the down
+ *                                                     projection's dA)
+ *   dB_g[c, j] = scale * sum_t dg[t, c] xl_g[t, j]  (gate's dB, from stored dg)
+ *   dB_u[c, j] = scale * sum_t du[t, c] xl_u[t, j]  (up's dB, from stored du)
+ * so dh, g and u are read once and dg, du are not read back.  gB fp32 [T,
+ * ldgB] (the down projection's dy B_down), xl_g / xl_u fp32 [T, ld >= r] (the
+ * gate and up x A^T); dA fp32 [r, F], dB_g / dB_u fp32 [F, r] (contiguous,
+ * out, the layouts of SL_LORA_DA / SL_LORA_DB).  bf16 only, F % 8 == 0,
+ * 1 <= r <= 32; the token sums are fixed-order reductions over row chunks
+ * (deterministic). */
+sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
+                             const void* g, int64_t ldg, const void* u, int64_t ldu,
+                             int64_t T, int64_t F, void* dg, int64_t lddg, void* du, int64_t lddu,
+                             const float* gB, int64_t ldgB, const float* xl_g, int64_t ldxlg,
+                             const float* xl_u, int64_t ldxlu, int64_t r, float scale,
+                             float* dA, float* dB_g, float* dB_u);
 /* out[j, i] = in[i, j]; in [rows, ldi], out [cols, ldo] (dt). */
 sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi,
                        int64_t rows, int64_t cols, void* out, int64_t ldo);
