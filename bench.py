@@ -20,6 +20,10 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+# fp32 vector arithmetic without packed (two-wide) fp32 instructions, which
+# this library does not use: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x
+# 2.4 GHz
+PEAK_F32_VALU_TFLOPS = 78.6
 
 
 def parse():
@@ -296,12 +300,16 @@ def other_configs(steps=3):
     return out
 
 
-def cpu_baseline(inp, cfg, min_s=10.0):
+def cpu_baseline(inp, cfg, min_s=10.0, threads=None):
     """The CPU oracle on whole sequences of the workload (512 tokens each: 384
     context, 128 output), one after another until at least `min_s` seconds have
     passed or the batch is done: per sequence, selection over its context
-    tokens (fp32 C) + masked-dense fp64 forward and backward."""
-    import numpy as np
+    tokens (fp32 C) + masked-dense fp64 forward and backward.  threads: cap on
+    the BLAS threads (None: as configured)."""
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=threads):
+            return cpu_baseline(inp, cfg, min_s, None)
     from oracle import csa, reference as ref
     try:
         from threadpoolctl import threadpool_info
@@ -383,6 +391,30 @@ def main():
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                 "traffic": None, "launches": dn, "avg_launch_ms": round(dms / dn, 4)}
+    # the same per-class pass with every launch on one stream (each kernel
+    # alone on the GPU: clean per-kernel times), and the selection chain's
+    # kernels against their bounds
+    side = blk.side
+    blk.side = torch.cuda.current_stream()
+    sms = time_steps(blk, x, roles, dy, cfg.ctx_tokens, psteps, 1, ops, record=True)
+    blk.side = side
+    per_class_1s = {}
+    for c in ops.timing_classes():
+        n, tms, fl, by = ops.timing_query(0, c)
+        if n:
+            sec = tms * 1e-3
+            per_class_1s[c] = {"launches_per_step": n / psteps, "ms_per_step": round(tms / psteps, 4),
+                               "gbs": round(by / sec / 1e9, 1), "hbm_frac": round(by / sec / 1e9 / PEAK_HBM_GBS, 4),
+                               "tflops": round(fl / sec / 1e12, 2)}
+    ops.timing_reset(0)
+    selection = {}
+    for c in ("estimate", "score", "topk"):
+        if c in per_class_1s:
+            v = dict(per_class_1s[c])
+            v["valu_frac"] = round(v["tflops"] / PEAK_F32_VALU_TFLOPS, 4)
+            selection[c] = v
+    print(f"[bench] single-stream instrumented step {sms:.3f} ms; selection: {selection}", file=sys.stderr,
+          flush=True)
     gemm_fl = sum(v["gflop_per_step"] for c, v in per_class.items() if c.startswith("gemm"))
     gemm_ms = sum(v["ms_per_step"] for c, v in per_class.items() if c.startswith("gemm"))
     step_gf = sum(v["gflop_per_step"] for v in per_class.values())
@@ -391,7 +423,13 @@ def main():
              "mfma_util_gemm": round(gemm_fl / gemm_ms / PEAK_BF16_TFLOPS, 4) if gemm_ms else None,
              "step_tflops": round(step_gf / ms, 2), "per_class": per_class,
              "per_class_note": f"separate instrumented pass of {psteps} steps "
-                               f"({pms:.3f} ms/step with events around every launch)"}
+                               f"({pms:.3f} ms/step with events around every launch)",
+             "per_class_single_stream": per_class_1s,
+             "per_class_single_stream_note": f"{psteps} steps with every launch on one stream "
+                                             f"({sms:.3f} ms/step with events around every launch)",
+             "selection_chain": selection,
+             "selection_chain_note": "single-stream pass; gbs/hbm_frac against 8 TB/s, tflops/valu_frac "
+                                     "against the 78.6 TF/s fp32 vector peak without packed fp32"}
     if not args.no_dense:
         import types
         from contextual_sparsity_lora_amd import fidelity
@@ -485,8 +523,13 @@ def main():
     out.update(extra)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, cfg)
-        print(f"[bench] cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s", file=sys.stderr,
-              flush=True)
+        out["cpu_baseline"]["affinity_cpus"] = len(os.sched_getaffinity(0))
+        # one core: one sequence (its oracle work alone takes tens of seconds)
+        one = cpu_baseline(inp, cfg, min_s=1.0, threads=1)
+        out["cpu_baseline"]["single_core"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+        print(f"[bench] cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s "
+              f"({out['cpu_baseline']['cores']} threads), {one['value']:.1f} tokens/s on one core",
+              file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

@@ -390,13 +390,30 @@ __device__ __forceinline__ float crit_value(const float* __restrict__ row, int64
     }
 }
 
+// Any rank k (the estimator up to full rank): the factor columns are read
+// from memory inside the chain instead of living in registers; the same
+// fma chain over j ascending from +0.
+template <int CRIT>
+__device__ __forceinline__ float crit_value_mem(const float* __restrict__ row, int64_t off0, int64_t off1,
+                                                const float* __restrict__ WB0, const float* __restrict__ WB1,
+                                                int64_t C, int64_t c, int krt) {
+    float g = 0.0f;
+    for (int j = 0; j < krt; ++j) g = __builtin_fmaf(row[off0 + j], WB0[(int64_t)j * C + c], g);
+    if (CRIT == 0) return g;
+    float u = 0.0f;
+    for (int j = 0; j < krt; ++j) u = __builtin_fmaf(row[off1 + j], WB1[(int64_t)j * C + c], u);
+    return silu_sl(g) * u;
+}
+
+// K > 0: that rank, factor columns in registers; K = 0: rank krt <= 64 in
+// registers; K = -1: rank krt of any size, factor columns read in the chain.
 template <int CRIT, int K>
 __global__ __launch_bounds__(512) void ssq_kernel(const float* __restrict__ xa, int64_t ld,
                                                   int64_t Tc, int64_t off0,
                                                   const float* __restrict__ WB0, int64_t off1,
                                                   const float* __restrict__ WB1, int krt,
                                                   int64_t C, float* __restrict__ ssq) {
-    constexpr int KR = K > 0 ? K : 64;
+    constexpr int KR = K > 0 ? K : (K == 0 ? 64 : 1);
     __shared__ float chains[64 * 64];
     const int lane = threadIdx.x & (WAVE - 1);
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -404,10 +421,12 @@ __global__ __launch_bounds__(512) void ssq_kernel(const float* __restrict__ xa, 
     const int64_t cc = c < C ? c : C - 1;
     const int kk = K > 0 ? K : krt;
     float wg[KR], wu[KR];
+    if constexpr (K >= 0) {
 #pragma unroll
-    for (int j = 0; j < KR; ++j) {
-        wg[j] = (j < kk) ? WB0[(int64_t)j * C + cc] : 0.0f;
-        wu[j] = (CRIT == 1 && j < kk) ? WB1[(int64_t)j * C + cc] : 0.0f;
+        for (int j = 0; j < KR; ++j) {
+            wg[j] = (j < kk) ? WB0[(int64_t)j * C + cc] : 0.0f;
+            wu[j] = (CRIT == 1 && j < kk) ? WB1[(int64_t)j * C + cc] : 0.0f;
+        }
     }
     float p[8];
 #pragma unroll
@@ -418,7 +437,9 @@ __global__ __launch_bounds__(512) void ssq_kernel(const float* __restrict__ xa, 
             const int64_t m = mb + 8 * w + q;
             if (m < Tc) {
                 const float* row = xa + m * ld;
-                float v = crit_value<CRIT, K>(row, off0, off1, wg, wu, kk);
+                float v;
+                if constexpr (K >= 0) v = crit_value<CRIT, K>(row, off0, off1, wg, wu, kk);
+                else v = crit_value_mem<CRIT>(row, off0, off1, WB0, WB1, C, cc, kk);
                 p[q] = __builtin_fmaf(v, v, p[q]);
             }
         }
@@ -772,10 +793,12 @@ hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t
             hipLaunchKernelGGL(ssq16_kernel<1>, grid, dim3(1024), 0, st, xa, ld, Tc, off0, WB0, off1, WB1, C, ssq);
     } else if (crit == 0) {
         if (k == 8) SSQ_LAUNCH(0, 8);
-        else SSQ_LAUNCH(0, 0);
+        else if (k <= 64) SSQ_LAUNCH(0, 0);
+        else SSQ_LAUNCH(0, -1);
     } else {
         if (k == 8) SSQ_LAUNCH(1, 8);
-        else SSQ_LAUNCH(1, 0);
+        else if (k <= 64) SSQ_LAUNCH(1, 0);
+        else SSQ_LAUNCH(1, -1);
     }
 #undef SSQ_LAUNCH
     return hipGetLastError();

@@ -426,7 +426,7 @@ sl_status sl_svd_estimate(sl_handle* h, const void* x, sl_dtype xdt, int64_t ldx
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, xdt == SL_BF16 || xdt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T_c >= 0 && D_in >= 1, "bad sizes");
-    SL_REQUIRE(h, k_tot >= 1 && k_tot <= 128, "k_tot must be in [1, 128]");
+    SL_REQUIRE(h, k_tot >= 1 && k_tot <= 65535 * 16, "k_tot must be in [1, 65535 * 16]");
     if (T_c == 0) return SL_OK;
     SL_REQUIRE(h, x && ctx_rows && WA && xa, "NULL pointer");
     SL_REQUIRE(h, ldx >= D_in, "ldx < D_in");
@@ -462,7 +462,7 @@ sl_status score_select_check(sl_handle* h, sl_criterion crit, const float* xa, i
                              int64_t C, int64_t n_rep, int64_t head_dim, int64_t n_keep, int32_t* idx) {
     SL_REQUIRE(h, crit == SL_CRIT_L2 || crit == SL_CRIT_SWIGLU_L2 || crit == SL_CRIT_QK,
                "bad criterion");
-    SL_REQUIRE(h, k >= 1 && k <= 64, "k must be in [1, 64]");
+    SL_REQUIRE(h, k >= 1 && k <= 65536, "k must be in [1, 65536]");
     SL_REQUIRE(h, C >= 1 && C <= INT32_MAX, "C out of range");
     SL_REQUIRE(h, n_keep >= 0 && n_keep <= C, "n_keep must be in [0, C]");
     SL_REQUIRE(h, T_c >= 0, "T_c < 0");

@@ -188,7 +188,8 @@ sl_status sl_token_split(sl_handle* h, const uint8_t* roles, int64_t T,
  *            W_A[i, :]); factors of projections that share the input are
  *            placed side by side (gate|up: 2k columns; q|k|v: 3k)
  *   xa       device fp32 [T_c, k_tot] out
- * Constraints: 1 <= k_tot <= 128, D_in >= 1.  T_c = 0 is a no-op. */
+ * Constraints: 1 <= k_tot <= 65535 * 16 (any rank up to the full one), D_in >= 1.
+ * T_c = 0 is a no-op. */
 sl_status sl_svd_estimate(sl_handle* h, const void* x, sl_dtype xdt, int64_t ldx,
                           const int32_t* ctx_rows, int64_t T_c, int64_t D_in,
                           const float* WA, int64_t k_tot, float* xa);
@@ -216,8 +217,10 @@ sl_status sl_svd_estimate(sl_handle* h, const void* x, sl_dtype xdt, int64_t ldx
  *   WB0/WB1 device fp32 [k, *] row-major (WB1 unused, may be NULL, for L2)
  *   scores  device fp32 [C] out, or NULL (then kept in the workspace)
  *   idx     device int32[n_keep] out
- * Constraints: 1 <= k <= 64; 0 <= n_keep <= C; n_rep >= 1 and head_dim >= 1
- * for QK (ignored otherwise).  T_c = 0 gives all-zero scores. */
+ * Constraints: 1 <= k <= 65536 (ranks above 64 read the factor columns
+ * inside the chain: the same arithmetic, more memory traffic);
+ * 0 <= n_keep <= C; n_rep >= 1 and head_dim >= 1 for QK (ignored
+ * otherwise).  T_c = 0 gives all-zero scores. */
 sl_status sl_score_select(sl_handle* h, sl_criterion crit, const float* xa, int64_t ld_xa,
                           int64_t T_c, int64_t off0, const float* WB0, int64_t off1,
                           const float* WB1, int64_t k, int64_t C, int64_t n_rep,

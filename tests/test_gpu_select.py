@@ -181,3 +181,40 @@ def test_qkv_index(n_kv, n_rep, d, fq, fv, rng):
     assert np.array_equal(host_i(iq), eq)
     assert np.array_equal(host_i(io), eo)
     assert np.array_equal(host_i(iqkv), np.concatenate([eq, iqk + Cq, ivo + Cq + Ckv]))
+
+
+def test_full_rank_estimator_bit_exact_and_matches_exact_criterion():
+    """The estimator at full rank (k = D = 256 at the fp32 FFN shape; W_A has
+    2k = 512 columns): the library's stage-1 products, SwiGLU-L2 scores and
+    selection equal the oracle's bit for bit, and the scores follow the exact
+    (dense-output) criterion within fp32 rounding, so the selection is the
+    exact criterion's wherever its n-th and (n+1)-th scores are apart."""
+    import dataclasses
+    from tests.test_oracle_score import _margin_ok, _top_set
+    ops = _ops()
+    cfg = dataclasses.replace(CONFIGS[1], est_rank=CONFIGS[1].hidden)
+    inp = make_ffn_inputs(cfg)
+    k = cfg.est_rank
+    print(f"[select] config 1 at full rank k={k}", flush=True)
+    ctx, out, c_d, o_d = _split(ops, inp["roles"])
+    x = to_dev(inp["x"], cfg.dtype)
+    WA = to_dev(np.ascontiguousarray(inp["WA_t_gu"].T), "f32")
+    xa = torch.empty(len(ctx), 2 * k, dtype=torch.float32, device=DEV)
+    ops.svd_estimate(x, c_d, WA, xa)
+    xa_ref = csa.stage1(inp["x"], ctx, inp["WA_t_gu"])
+    assert np.array_equal(bits(host(xa)), bits(xa_ref))
+    n = ref.n_keep(cfg.inter, *cfg.ffn_sparsity)
+    sc = torch.empty(cfg.inter, dtype=torch.float32, device=DEV)
+    idx = torch.empty(n, dtype=torch.int32, device=DEV)
+    ops.score_select("swiglu", xa, to_dev(inp["WB_gate"], "f32"), to_dev(inp["WB_up"], "f32"), n, idx,
+                     scores=sc, off0=0, off1=k)
+    sc_ref = csa.ssq_swiglu(xa_ref, inp["WB_gate"], inp["WB_up"])
+    got = host(sc)
+    assert np.array_equal(bits(got), bits(sc_ref))
+    assert np.array_equal(host_i(idx), csa.select(sc_ref, n))
+    xc = inp["x"][ctx].astype(np.float64)
+    h = ref.silu(xc @ inp["W_gate"].T.astype(np.float64)) * (xc @ inp["W_up"].T.astype(np.float64))
+    s64 = np.sum(h * h, axis=0)
+    assert np.allclose(got, s64, rtol=1e-3, atol=0)
+    if _margin_ok(s64, n, 1e-3):
+        assert np.array_equal(host_i(idx), _top_set(s64, n))
