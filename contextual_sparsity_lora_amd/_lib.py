@@ -50,10 +50,10 @@ SIGNATURES = {
     "sl_qkv_index": (_st, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp]),
     "sl_sparse_linear_fwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
-                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _int]),
+                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _vp, _i64, _int]),
     "sl_sparse_linear_bwd": (_st, [_vp, _int, _int, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
                                    _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _int,
-                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _int]),
+                                   _vp, _i64, _vp, _i64, _i64, _f, _vp, _i64, _vp, _i64, _int]),
     "sl_weight_slice": (_st, [_vp, _int, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64]),
     "sl_lora_fill_unselected": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64,
                                       _i64, _f, _vp, _i64]),
@@ -62,8 +62,10 @@ SIGNATURES = {
     "sl_swiglu_fwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64]),
     "sl_swiglu_bwd": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64,
                             _vp, _i64]),
-    "sl_swiglu_fwd_lora": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64,
-                                 _vp, _i64]),
+    "sl_swiglu_fwd_lora": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                 _i64, _vp, _i64]),
+    "sl_swiglu_fwd_ctx": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                _i64, _f, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
     "sl_swiglu_bwd_lora": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
                                  _vp, _i64, _vp, _i64, _vp, _i64, _i64, _f, _vp, _vp, _vp]),
     "sl_svd_factors": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_uint64,

@@ -15,6 +15,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Orders this wave's LDS accesses across its lanes (a tile written by some
+// lanes and read by others).  LDS only: the wave's outstanding global loads
+// and stores are not waited for.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
 template <typename T> __device__ __forceinline__ float ld(const T* p, int64_t i);
 template <> __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
 template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p, int64_t i) {
@@ -389,9 +398,7 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
         }
         if (whole) {
             // (this wave's own LDS rows: in-order LDS access within the wave)
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rr = 4 * j + (lane >> 4);               // tile row: lane rr holds its row number
@@ -400,9 +407,7 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
                 const uint4 d = *(const uint4*)&tile[wid][rr][8 * (lane & 15)];
                 if (ov) *(uint4*)(y + orow * ldy + c0 + 8 * (lane & 15)) = d;
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            wave_lds_sync();
         }
     }
 }
@@ -515,18 +520,14 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
             *(uint4*)&tile[wid][lane & 15][8 * (lane >> 4) + 32 * g] = make_uint4(w[0], w[1], w[2], w[3]);
         }
         // (this wave's own LDS rows: in-order LDS access within the wave)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
         // the selected channels from the compact rows
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             if (sl0 >= 0) tile[wid][rr][sl0] = cv0[rr];
             if (sl1 >= 0) tile[wid][rr][sl1] = cv1[rr];
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int rr = 4 * j + (lane >> 4);               // tile row: lane rr holds its row number
@@ -541,9 +542,7 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
                     if (c + q < C) y[orow * ldy + c + q] = tile[wid][rr][8 * (lane & 15) + q];
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
     }
 }
 
@@ -807,7 +806,8 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 v, float* f) {
 }
 
 // Forward: h = silu(g) u (as swiglu_fwd) and the row partials of
-// xl[t, j] = sum_c h[t, c] A[j, c] from the stored (bf16) h.  A block of 4
+// xl[t, j] = sum_c h[t, c] A[j, c] from the stored (bf16) h, over rows t =
+// rows[m] (or m) for m < Tn; partials are indexed by m.  A block of 4
 // waves shares 16 rows; wave w takes SFW columns from its block's start, 128
 // at a time.  Loads and stores go 4 rows at a time with 16 lanes on each
 // row's 256 bytes (lane l: row 4 s + l / 16, columns 8 (l % 16) + e); h then
@@ -820,9 +820,9 @@ constexpr int SFW = 512;
 
 template <int NR>
 __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
-    const bf16_t* __restrict__ g, int64_t ldg, const bf16_t* __restrict__ u, int64_t ldu, int64_t Tn, int64_t F,
-    bf16_t* __restrict__ h, int64_t ldh, const bf16_t* __restrict__ A, int64_t lda, int64_t r,
-    float* __restrict__ part) {
+    const bf16_t* __restrict__ g, int64_t ldg, const bf16_t* __restrict__ u, int64_t ldu,
+    const int32_t* __restrict__ rows, int64_t Tn, int64_t F, bf16_t* __restrict__ h, int64_t ldh,
+    const bf16_t* __restrict__ A, int64_t lda, int64_t r, float* __restrict__ part) {
     constexpr int RW = 16 * NR;
     __shared__ float red[4][16][RW + 1];
     __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
@@ -840,8 +840,9 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
         const int64_t cl = cs + 8 * cg;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int64_t t = t0 + 4 * s + rs;
-            const bool ok = t < Tn && cl < F;
+            const int64_t m = t0 + 4 * s + rs;
+            const bool ok = m < Tn && cl < F;
+            const int64_t t = (rows && m < Tn) ? (int64_t)rows[m] : m;
             gv[s] = ok ? *(const uint4*)(g + t * ldg + cl) : zero;
             uv[s] = ok ? *(const uint4*)(u + t * ldu + cl) : zero;
 #pragma unroll
@@ -863,14 +864,12 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
                 w[q] = pack_bf16x2(h0, h1);
             }
             const uint4 hv = make_uint4(w[0], w[1], w[2], w[3]);
-            const int64_t t = t0 + 4 * s + rs;
-            if (t < Tn && cl < F) *(uint4*)(h + t * ldh + cl) = hv;
+            const int64_t m = t0 + 4 * s + rs;
+            if (m < Tn && cl < F) *(uint4*)(h + ((rows ? (int64_t)rows[m] : m) * ldh) + cl) = hv;
             *(uint4*)&tile[wid][4 * s + rs][8 * cg] = hv;   // rows past T / columns past F: zeros
         }
         // (this wave's own LDS rows: in-order LDS access within the wave)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             float hb[8];
@@ -884,9 +883,7 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
                     acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], af[e], acc[k], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
     }
     // lane holds D[4 (l / 16) + i][l % 16]: row t0 + 4 kq + i, rank 16 k + rr
 #pragma unroll
@@ -1014,17 +1011,293 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
                 }
 }
 
-// out[a soa + j soj] = scale * sum over ch = 0.. of part[(ch A + a) RW + j]
-// (ascending ch), j < r: the ordered sum of the fused kernels' partials.
+// out[a' soa + j soj] = scale * sum over ch = 0.. of part[(ch A + a) RW + j]
+// (ascending ch), j < r, a' = amap[a] (or a): the ordered sum of the fused
+// kernels' partials.
 __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict__ part, int64_t nch, int64_t Adim,
                                                        int RW, int64_t r, float scale, float* __restrict__ out,
-                                                       int64_t soa, int64_t soj) {
+                                                       int64_t soa, int64_t soj, const int32_t* __restrict__ amap) {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (q >= Adim * r) return;
     const int64_t a = q / r, j = q % r;
     float s = 0.0f;
     for (int64_t ch = 0; ch < nch; ++ch) s += part[(ch * Adim + a) * RW + j];
-    out[a * soa + j * soj] = scale * s;
+    const int64_t ao = amap ? (int64_t)amap[a] : a;   // output row of partial row a
+    out[ao * soa + j * soj] = scale * s;
+}
+
+// ---------------------------------------------------------------- forward SwiGLU of context rows from their compact product
+// For the listed (context) rows t = rows[m] and every channel c < F:
+//   g = Yc[m, j]     if c = idx[j] (selected), else s P[t, :] . B[c, :]
+//   u = Yc[m, n + j] if c = idx[j],            else s P[t, :] . B[F + c, :]
+// exactly as the merge of the gate|up compact product forms them (the
+// rank-r values on the matrix cores from s P rounded to bf16, one bf16
+// rounding), stored to gu[t, c] and gu[t, F + c]; then h = silu(g) u (bf16,
+// as swiglu_fwd) goes to the compact hc[m, j] = h[t, idx[j]] (columns n ..
+// npad zero), optionally to hf[t, :] (the whole row), and into the row sums
+// xl[t, :] = sum over every c of h[t, c] A[:, c] (fp32 matrix cores, row
+// partials per 512 channels, a fixed-order sum follows).  Block = 4 waves on 64 rows (four 16-row tiles) and 512
+// channels, wave w on 128 of them; the tiles pass through the wave's LDS
+// rows between the matrix-core layout (lane l: row l % 16, 8 channels at
+// 32 g + 8 (l / 16)) and the row-store layout (lane l: row 4 q + l / 16, 8
+// channels at 8 (l % 16)).
+constexpr int SCR = 64;   // rows per block
+
+template <int R, int NR>
+__global__ __launch_bounds__(256) void swiglu_fwd_ctx_kernel(
+    bf16_t* __restrict__ gu, int64_t ldgu, const int32_t* __restrict__ rows, int64_t nrows, int64_t F,
+    const float* __restrict__ P, int64_t ldp, const bf16_t* __restrict__ B, int64_t ldb, int64_t r2, float scale,
+    const bf16_t* __restrict__ Yc, int64_t ldyc, const int32_t* __restrict__ idx, int64_t n,
+    bf16_t* __restrict__ hc, int64_t ldhc, int64_t npad, const bf16_t* __restrict__ A, int64_t lda, int64_t r,
+    bf16_t* __restrict__ hf, int64_t ldhf, float* __restrict__ part) {
+    constexpr int KS = (R + 31) / 32;
+    constexpr int RW = 16 * NR;
+    __shared__ __attribute__((aligned(16))) bf16_t tg[4][16][128 + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t tu[4][16][128 + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t cb[4][16][136];   // compact values of the wave's run
+    __shared__ float red[4][SCR][RW + 1];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rr = lane & 15, kq = lane >> 4;
+    const int64_t c0 = (int64_t)blockIdx.x * 512 + (int64_t)wid * 128;
+    const int64_t mb = (int64_t)blockIdx.y * SCR;
+    const int kl = 8 * kq;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    // the rank-r factor rows of this wave's gate and up channels (slot order
+    // of the matrix-core layout), and A's columns for the row sums
+    bf16x8 wg[KS][4][2], wu[KS][4][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int64_t c = c0 + 32 * g + 8 * (rr >> 2) + 4 * e + (rr & 3);
+                const int k = 32 * ks + kl;
+                uint4 a = zero, b = zero;
+                if (c < F && k < r2) {
+                    if (k + 8 <= r2) {
+                        a = *(const uint4*)(B + c * ldb + k);
+                        b = *(const uint4*)(B + (F + c) * ldb + k);
+                    } else {
+                        uint32_t wa[4] = {0u, 0u, 0u, 0u}, wb[4] = {0u, 0u, 0u, 0u};
+                        for (int q = 0; q < 8; ++q)
+                            if (k + q < r2) {
+                                wa[q >> 1] |= (uint32_t)B[c * ldb + k + q] << ((q & 1) * 16);
+                                wb[q >> 1] |= (uint32_t)B[(F + c) * ldb + k + q] << ((q & 1) * 16);
+                            }
+                        a = make_uint4(wa[0], wa[1], wa[2], wa[3]);
+                        b = make_uint4(wb[0], wb[1], wb[2], wb[3]);
+                    }
+                }
+                wg[ks][g][e] = __builtin_bit_cast(bf16x8, a);
+                wu[ks][g][e] = __builtin_bit_cast(bf16x8, b);
+            }
+    uint4 av[4][NR];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const int64_t j = 16 * k + rr, c = c0 + 32 * s + kl;
+            av[s][k] = (c < F && j < r) ? *(const uint4*)(A + j * lda + c) : zero;
+        }
+    // this wave's selected channels: idx[j0 .. j1) (at most 128); lane holds
+    // entries j0 + lane and j0 + 64 + lane (slot in the wave's block, or -1)
+    int64_t j0, j1;
+    wave_lower_bounds(idx, n, c0, c0 + 128, lane, j0, j1);
+    const int sl0 = j0 + lane < j1 ? (int)(idx[j0 + lane] - c0) : -1;
+    const int sl1 = j0 + 64 + lane < j1 ? (int)(idx[j0 + 64 + lane] - c0) : -1;
+    // the compact values of a row arrive as 16-byte chunks (lane l: chunk
+    // l % 16 of row 4 s + l / 16, and chunk 16 + l % 16 when the run needs a
+    // 17th), aligned from jbg (gate, compact positions j) or jbu (up, n + j);
+    // they pass through the wave's LDS rows, from which lane l moves compact
+    // value j0 + l (and j0 + 64 + l) to its slot sl0 (sl1) of the tile
+    const int cq = lane & 15;
+    const int64_t jbg = j0 & ~(int64_t)7, jbu = (n + j0) & ~(int64_t)7;
+    const bool two = (j1 - jbg > 128) || (n + j1 - jbu > 128);   // a 17th chunk (wave-uniform)
+    const bool run64 = j1 - j0 > 64;                                 // wave-uniform
+    const bool ldg0 = jbg + 8 * cq < j1, ldu0 = jbu + 8 * cq < n + j1;
+    const bool ldg1 = two && jbg + 8 * (cq + 16) < j1, ldu1 = two && jbu + 8 * (cq + 16) < n + j1;
+    const int og = (int)(j0 - jbg), ou = (int)(n + j0 - jbu);      // run start within the LDS rows
+    f32x4 acc[SCR / 16][NR];
+#pragma unroll
+    for (int q = 0; q < SCR / 16; ++q)
+#pragma unroll
+        for (int k = 0; k < NR; ++k) acc[q][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < SCR / 16; ++q) {
+        const int64_t m0 = mb + 16 * q;
+        if (m0 >= nrows) break;   // uniform across the block
+        const int64_t m = m0 + rr;
+        const bool mv = m < nrows;
+        const int64_t row = mv ? (int64_t)rows[m] : 0;
+        // the compact values of the 16 rows, loaded ahead (16-byte chunks)
+        uint4 cg[4], cu[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const int64_t mr = m0 + 4 * s4 + kq;
+            const bool ok = mr < nrows;
+            const bf16_t* yr = Yc + mr * ldyc;
+            cg[s4] = (ok && ldg0) ? *(const uint4*)(yr + jbg + 8 * cq) : zero;
+            cu[s4] = (ok && ldu0) ? *(const uint4*)(yr + jbu + 8 * cq) : zero;
+        }
+        bf16x8 pb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k = 32 * ks + kl;
+            float v[8];
+            if (mv && k + 8 <= r2 && (ldp & 3) == 0) {
+                const float4 v0 = *(const float4*)(P + row * ldp + k), v1 = *(const float4*)(P + row * ldp + k + 4);
+                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
+                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = (mv && k + e < r2) ? P[row * ldp + k + e] : 0.0f;
+            }
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(scale * v[2 * e], scale * v[2 * e + 1]);
+            pb[ks] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            f32x4 ag[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+            f32x4 au[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    ag[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wg[ks][g][e], pb[ks], ag[e], 0, 0, 0);
+                    au[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wu[ks][g][e], pb[ks], au[e], 0, 0, 0);
+                }
+            uint32_t w0[4], w1[4];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                w0[e] = pack_bf16x2(ag[0][2 * e], ag[0][2 * e + 1]);
+                w0[2 + e] = pack_bf16x2(ag[1][2 * e], ag[1][2 * e + 1]);
+                w1[e] = pack_bf16x2(au[0][2 * e], au[0][2 * e + 1]);
+                w1[2 + e] = pack_bf16x2(au[1][2 * e], au[1][2 * e + 1]);
+            }
+            *(uint4*)&tg[wid][rr][kl + 32 * g] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+            *(uint4*)&tu[wid][rr][kl + 32 * g] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+        }
+        // (this wave's own LDS rows: in-order LDS access within the wave)
+        wave_lds_sync();
+        // gate: the compact chunks to the LDS rows, then each run value to its slot
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) *(uint4*)&cb[wid][4 * s4 + kq][8 * cq] = cg[s4];
+        if (two && cq == 0) {   // chunk 16 (lanes 0, 16, 32, 48: one per row)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int64_t mr = m0 + 4 * s4 + kq;
+                *(uint4*)&cb[wid][4 * s4 + kq][128] =
+                    (mr < nrows && ldg1) ? *(const uint4*)(Yc + mr * ldyc + jbg + 128) : zero;
+            }
+        }
+        wave_lds_sync();
+        if (sl0 >= 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tg[wid][i][sl0] = cb[wid][i][og + lane];
+        }
+        if (run64 && sl1 >= 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tg[wid][i][sl1] = cb[wid][i][og + 64 + lane];
+        }
+        wave_lds_sync();
+        // up: the same through the same LDS rows
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) *(uint4*)&cb[wid][4 * s4 + kq][8 * cq] = cu[s4];
+        if (two && cq == 0) {   // chunk 16 (lanes 0, 16, 32, 48: one per row)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int64_t mr = m0 + 4 * s4 + kq;
+                *(uint4*)&cb[wid][4 * s4 + kq][128] =
+                    (mr < nrows && ldu1) ? *(const uint4*)(Yc + mr * ldyc + jbu + 128) : zero;
+            }
+        }
+        wave_lds_sync();
+        if (sl0 >= 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tu[wid][i][sl0] = cb[wid][i][ou + lane];
+        }
+        if (run64 && sl1 >= 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tu[wid][i][sl1] = cb[wid][i][ou + 64 + lane];
+        }
+        wave_lds_sync();
+        // whole rows of g and u to gu; h into the g tile (each element is
+        // read and rewritten by the same lane)
+        const int64_t cs = c0 + 8 * rr;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int tr = 4 * jj + kq;
+            const int64_t orow = __shfl(row, tr, 64);
+            const int ov = __shfl((int)mv, tr, 64);
+            const uint4 gv = *(const uint4*)&tg[wid][tr][8 * rr];
+            const uint4 uv = *(const uint4*)&tu[wid][tr][8 * rr];
+            if (ov && cs < F) {
+                *(uint4*)(gu + orow * ldgu + cs) = gv;
+                *(uint4*)(gu + orow * ldgu + F + cs) = uv;
+            }
+            float gf[8], uf[8];
+            unpack_bf16x8(gv, gf);
+            unpack_bf16x8(uv, uf);
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float h0 = gf[2 * e] * sigmoid_hw(gf[2 * e]) * uf[2 * e];
+                const float h1 = gf[2 * e + 1] * sigmoid_hw(gf[2 * e + 1]) * uf[2 * e + 1];
+                w[e] = pack_bf16x2(h0, h1);
+            }
+            const uint4 hv = make_uint4(w[0], w[1], w[2], w[3]);
+            *(uint4*)&tg[wid][tr][8 * rr] = hv;
+            if (hf && ov && cs < F) *(uint4*)(hf + orow * ldhf + cs) = hv;   // optional full rows of h
+        }
+        wave_lds_sync();
+        // the selected channels of h to the compact rows
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (m0 + i >= nrows) break;
+            bf16_t* hr = hc + (m0 + i) * ldhc + j0;
+            if (sl0 >= 0) hr[lane] = tg[wid][i][sl0];
+            if (sl1 >= 0) hr[64 + lane] = tg[wid][i][sl1];
+        }
+        // row sums of h A^T: MFMA (s, e) with A[m][k] = h[m][32 s + 8 k + e]
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float hb[8];
+            unpack_bf16x8(*(const uint4*)&tg[wid][rr][32 * s + kl], hb);
+#pragma unroll
+            for (int k = 0; k < NR; ++k) {
+                float af[8];
+                unpack_bf16x8(av[s][k], af);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[q][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], af[e], acc[q][k], 0, 0, 0);
+            }
+        }
+        wave_lds_sync();
+    }
+    // zero padding of the compact rows (columns n .. npad)
+    if (blockIdx.x == 0 && wid == 0 && npad > n) {
+        const int64_t w = npad - n;
+        for (int64_t q = lane; q < SCR * w; q += 64) {
+            const int64_t m = mb + q / w;
+            if (m < nrows) hc[m * ldhc + n + q % w] = (bf16_t)0;
+        }
+    }
+    // lane holds D[4 (l / 16) + i][l % 16] of tile q: row m0 + 4 kq + i, rank 16 k + rr
+#pragma unroll
+    for (int q = 0; q < SCR / 16; ++q)
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wid][16 * q + 4 * kq + i][16 * k + rr] = acc[q][k][i];
+    __syncthreads();
+    for (int q = threadIdx.x; q < SCR * RW; q += 256) {
+        const int row = q / RW, j = q % RW;
+        const float v = ((red[0][row][j] + red[1][row][j]) + red[2][row][j]) + red[3][row][j];
+        if (mb + row < nrows) part[((int64_t)blockIdx.x * nrows + mb + row) * RW + j] = v;
+    }
 }
 
 // out[m, q..q+7] = in[rows[m], cols[q..q+7]]: gathered loads, one vector store.
@@ -1479,21 +1752,21 @@ size_t swiglu_fwd_lora_ws_floats(int64_t T, int64_t F, int64_t r) {
     return (size_t)(ceil_div(F, 4 * SFW) * T * RW);
 }
 
-hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t T, int64_t F,
-                                  void* h, int64_t ldh, const void* A, int64_t lda, int64_t r, float* xl,
-                                  int64_t ldxl, float* part, hipStream_t st) {
-    if (T <= 0 || F <= 0) return hipSuccess;
+hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, const int32_t* rows,
+                                  int64_t nr, int64_t F, void* h, int64_t ldh, const void* A, int64_t lda, int64_t r,
+                                  float* xl, int64_t ldxl, float* part, hipStream_t st) {
+    if (nr <= 0 || F <= 0) return hipSuccess;
     const int64_t ncb = ceil_div(F, 4 * SFW);
-    const dim3 grid((unsigned)ncb, (unsigned)ceil_div(T, 16));
+    const dim3 grid((unsigned)ncb, (unsigned)ceil_div(nr, 16));
     const int RW = r <= 16 ? 16 : 32;
     if (r <= 16)
         hipLaunchKernelGGL(swiglu_fwd_lora_kernel<1>, grid, dim3(256), 0, st, (const bf16_t*)g, ldg,
-                           (const bf16_t*)u, ldu, T, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
+                           (const bf16_t*)u, ldu, rows, nr, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
     else
         hipLaunchKernelGGL(swiglu_fwd_lora_kernel<2>, grid, dim3(256), 0, st, (const bf16_t*)g, ldg,
-                           (const bf16_t*)u, ldu, T, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
-    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0, st, part, ncb, T, RW,
-                       r, 1.0f, xl, ldxl, (int64_t)1);
+                           (const bf16_t*)u, ldu, rows, nr, F, (bf16_t*)h, ldh, (const bf16_t*)A, lda, r, part);
+    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)ceil_div(nr * r, 256)), dim3(256), 0, st, part, ncb, nr, RW,
+                       r, 1.0f, xl, ldxl, (int64_t)1, rows);
     return hipGetLastError();
 }
 
@@ -1526,10 +1799,43 @@ hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, i
     const dim3 rg((unsigned)ceil_div(F * r, 256));
     const size_t pstride = (size_t)nch * F * RW;
     // dA [r, F] (row j, column c); dB [F, r]
-    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part, nch, F, RW, r, scale, dA, (int64_t)1, F);
+    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part, nch, F, RW, r, scale, dA, (int64_t)1, F,
+                       (const int32_t*)nullptr);
     hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + pstride, nch, F, RW, r, scale, dB1, r,
-                       (int64_t)1);
+                       (int64_t)1, (const int32_t*)nullptr);
     hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + 2 * pstride, nch, F, RW, r, scale, dB2, r,
-                       (int64_t)1);
+                       (int64_t)1, (const int32_t*)nullptr);
+    return hipGetLastError();
+}
+
+size_t swiglu_fwd_ctx_ws_floats(int64_t nrows, int64_t F, int64_t r) {
+    const int64_t RW = r <= 16 ? 16 : 32;
+    return (size_t)(ceil_div(F, 512) * nrows * RW);
+}
+
+hipError_t launch_swiglu_fwd_ctx(void* gu, int64_t ldgu, const int32_t* rows, int64_t nrows, int64_t F,
+                                 const float* P, int64_t ldp, const void* B, int64_t ldb, int64_t r2, float scale,
+                                 const void* Yc, int64_t ldyc, const int32_t* idx, int64_t n, void* hc, int64_t ldhc,
+                                 int64_t npad, const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
+                                 void* hf, int64_t ldhf, float* part, hipStream_t st) {
+    if (nrows <= 0 || F <= 0) return hipSuccess;
+    if (r2 > 64 || r > 32) return hipErrorInvalidValue;
+    const int64_t ncb = ceil_div(F, 512);
+    const dim3 grid((unsigned)ncb, (unsigned)ceil_div(nrows, SCR));
+    const int RW = r <= 16 ? 16 : 32;
+#define SFC(RR, NRR)                                                                                          \
+    hipLaunchKernelGGL((swiglu_fwd_ctx_kernel<RR, NRR>), grid, dim3(256), 0, st, (bf16_t*)gu, ldgu, rows, nrows, \
+                       F, P, ldp, (const bf16_t*)B, ldb, r2, scale, (const bf16_t*)Yc, ldyc, idx, n, (bf16_t*)hc,  \
+                       ldhc, npad, (const bf16_t*)A, lda, r, (bf16_t*)hf, ldhf, part)
+    if (r2 <= 32) {
+        if (r <= 16) SFC(32, 1);
+        else SFC(32, 2);
+    } else {
+        if (r <= 16) SFC(64, 1);
+        else SFC(64, 2);
+    }
+#undef SFC
+    hipLaunchKernelGGL(chunk_sum_kernel, dim3((unsigned)ceil_div(nrows * r, 256)), dim3(256), 0, st, part, ncb,
+                       nrows, RW, r, 1.0f, xl, ldxl, (int64_t)1, rows);
     return hipGetLastError();
 }

@@ -797,6 +797,19 @@ GemmProblem problem(const void* A, int64_t lda, const int32_t* a_rows, const voi
     return p;
 }
 
+// Flag bits of the sparse products.  row_side: the call's side is the one
+// whose products are side-OUT-shaped (fwd OUT, bwd IN), where the row-subset
+// and compact-output flags apply.
+sl_status check_flags(sl_handle* h, int flags, bool row_side) {
+    const int rows2 = SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS;
+    SL_REQUIRE(h, (flags & ~(SL_NO_FILL | rows2 | SL_CTX_COMPACT)) == 0 && (flags & rows2) != rows2, "bad flags");
+    SL_REQUIRE(h, row_side || !(flags & (rows2 | SL_CTX_COMPACT)),
+               "row-subset and compact flags apply to side-OUT-shaped products (fwd OUT, bwd IN)");
+    SL_REQUIRE(h, !(flags & SL_CTX_COMPACT) || (flags & SL_ONLY_CTX_ROWS),
+               "SL_CTX_COMPACT needs SL_ONLY_CTX_ROWS");
+    return SL_OK;
+}
+
 // Output-channel-sparse product (context rows keep only the selected output
 // channels): fwd side OUT and bwd side IN share this shape.
 //   Z[t, :] = X[t, :] Wc^T  over all channels for output rows,
@@ -822,6 +835,15 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
         p[np++] = problem(X, ldx, out_rows, Wc, ldw, nullptr, Z, ldz, out_rows, nullptr, T_o, C, Kdim,
                           beta, l, T, C);
     if (only_out) return run_gemm(h, dt, false, p, np);
+    if (flags & SL_CTX_COMPACT) {
+        // the context rows' product of the selected channels, stored compactly
+        // in Z (row m, column j), the rank-r term of those channels included
+        if (n == 0) return SL_OK;
+        GemmProblem pc = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, nullptr, nullptr, T_c, n, Kdim, 0, l, T, C);
+        pc.l_rows = ctx_rows;
+        pc.l_cols = idx;
+        return run_gemm(h, dt, false, &pc, 1);
+    }
     if (dt == SL_BF16 && !beta && !(flags & SL_NO_FILL)) {
         // context rows: the product of the selected channels is stored compactly
         // ([T_c, n], whole 16-byte rows), then one pass writes every channel of
@@ -892,7 +914,8 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
                     const void* Wd, int64_t ldwd, const void* Wc, int64_t ldwc, int64_t Nout,
                     const int32_t* ctx_rows, int64_t T_c, const int32_t* out_rows, int64_t T_o,
                     const int32_t* idx, int64_t n, void* Z, int64_t ldz, int beta,
-                    const LoraEpi& l, const void* w_slice = nullptr, int64_t ld_w_slice = 0) {
+                    const LoraEpi& l, const void* w_slice = nullptr, int64_t ld_w_slice = 0,
+                    const void* x_slice = nullptr, int64_t ld_x_slice = 0) {
     if (n == C || T_c == 0) {
         GemmProblem p = problem(X, ldx, nullptr, Wd, ldwd, nullptr, Z, ldz, nullptr, nullptr, T, Nout,
                                 C, beta, l, T, Nout);
@@ -914,28 +937,31 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
             S = ceil_div(C, Ks);
         }
     }
-    const size_t xc_bytes = round_up((size_t)(T_c * ldn) * esize(dt), 256);
-    const size_t ws_bytes = round_up((size_t)(Nout * ldn) * esize(dt), 256);
+    const size_t xc_bytes = x_slice ? 0 : round_up((size_t)(T_c * ldn) * esize(dt), 256);
+    const size_t ws_bytes = w_slice ? 0 : round_up((size_t)(Nout * ldn) * esize(dt), 256);
     const size_t part_bytes = S > 1 ? round_up((size_t)(S * T_o * Nout) * 4, 256) : 0;
     SL_CHECK(ensure_ws(h, xc_bytes + ws_bytes + part_bytes));
-    void* xc = h->ws;
+    const void* xc = x_slice ? x_slice : h->ws;
+    const int64_t ldxc = x_slice ? ld_x_slice : ldn;
     const void* wsl = (char*)h->ws + xc_bytes;
     int64_t ldwsl = ldn;
     float* part = (float*)((char*)h->ws + xc_bytes + ws_bytes);
-    if (n > 0) {
-        Timed tm(h, K_GATHER, 0, 2.0 * (T_c + (w_slice ? 0 : Nout)) * n * esize(dt));
+    if (w_slice) {
+        wsl = w_slice;
+        ldwsl = ld_w_slice;
+    }
+    if (n > 0 && !(x_slice && w_slice)) {
+        Timed tm(h, K_GATHER, 0, 2.0 * ((x_slice ? 0 : T_c) + (w_slice ? 0 : Nout)) * n * esize(dt));
         // both compacted operands are zero-padded to ldn columns, so the
         // context product may contract over K = ldn (a multiple of 8); a weight
-        // slice built beforehand (sl_weight_slice) is used as given
-        SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, ldn, xc, ldn,
-                                     h->stream), "gather_cols");
-        if (w_slice) {
-            wsl = w_slice;
-            ldwsl = ld_w_slice;
-        } else {
+        // slice built beforehand (sl_weight_slice) and compact activations
+        // written by their producer are used as given
+        if (!x_slice)
+            SL_HIP(h, launch_gather_cols(dt == SL_BF16, X, ldx, ctx_rows, T_c, idx, n, ldn, (void*)xc, ldn,
+                                         h->stream), "gather_cols");
+        if (!w_slice)
             SL_HIP(h, launch_gather_rows_t(dt == SL_BF16, Wc, ldwc, idx, n, ldn, Nout, (void*)wsl, ldn,
                                            h->stream), "gather_rows_t");
-        }
     }
     GemmProblem p[5];
     int np = 0;
@@ -957,7 +983,7 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
         }
     }
     // n > 0: contract over the zero-padded width ldn; n == 0: an empty sum
-    p[np++] = problem(xc, ldn, nullptr, wsl, ldwsl, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
+    p[np++] = problem(xc, ldxc, nullptr, wsl, ldwsl, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
                       n > 0 ? ldn : 0, beta, l, T_c, Nout);
     p[np - 1].k_alg = n;
     SL_CHECK(run_gemm(h, dt, false, p, np));
@@ -980,21 +1006,21 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
                                int64_t n, void* y, int64_t ldy, int beta, const float* lora_P,
                                int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
                                int64_t lora_r, float lora_scale, const void* w_slice,
-                               int64_t ld_w_slice, int flags) {
+                               int64_t ld_w_slice, const void* x_slice, int64_t ld_x_slice, int flags) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
-    SL_REQUIRE(h, (flags & ~(SL_NO_FILL | SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) == 0 &&
-                      (flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) != (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS),
-               "bad flags");
-    SL_REQUIRE(h, side == SL_SIDE_OUT || !(flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)),
-               "row-subset flags apply to side OUT");
+    SL_CHECK(check_flags(h, flags, side == SL_SIDE_OUT));
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     if (w_slice) {
         SL_REQUIRE(h, side == SL_SIDE_IN, "w_slice applies to side IN");
         SL_CHECK(check_matrix(h, w_slice, ld_w_slice, (n + 7) / 8 * 8, dt, "w_slice"));
+    }
+    if (x_slice) {
+        SL_REQUIRE(h, side == SL_SIDE_IN, "x_slice applies to side IN");
+        SL_CHECK(check_matrix(h, x_slice, ld_x_slice, (n + 7) / 8 * 8, dt, "x_slice"));
     }
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
@@ -1005,16 +1031,16 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     SL_CHECK(debug_check_list(h, ctx_rows, T_c, T, "ctx_rows"));
     SL_CHECK(debug_check_list(h, out_rows, T_o, T, "out_rows"));
     SL_CHECK(check_matrix(h, x, ldx, D_in, dt, "x"));
-    SL_CHECK(check_matrix(h, y, ldy, D_out, dt, "y"));
+    SL_CHECK(check_matrix(h, y, ldy, (flags & SL_CTX_COMPACT) ? (n > 0 ? n : 1) : D_out, dt, "y"));
     SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
-    const bool need_t = side == SL_SIDE_IN && n < C && T_c > 0;
+    const bool need_t = side == SL_SIDE_IN && n < C && T_c > 0 && !w_slice;
     if (need_t) SL_CHECK(check_matrix(h, Wt, ldwt, D_out, dt, "Wt"));
     DeviceGuard g(h->device);
     if (side == SL_SIDE_OUT)
         return out_sparse(h, dt, x, ldx, T, D_in, W, ldw, D_out, ctx_rows, T_c, out_rows, T_o, idx,
                           n, y, ldy, beta, l, flags);
     return in_sparse(h, dt, x, ldx, T, D_in, W, ldw, Wt, ldwt, D_out, ctx_rows, T_c, out_rows, T_o,
-                     idx, n, y, ldy, beta, l, w_slice, ld_w_slice);
+                     idx, n, y, ldy, beta, l, w_slice, ld_w_slice, x_slice, ld_x_slice);
 }
 
 // ---------------------------------------------------------------- a10/a11
@@ -1025,21 +1051,21 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
                                int64_t n, void* dx, int64_t lddx, int beta, const float* lora_P,
                                int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B,
                                int64_t lora_r, float lora_scale, const void* w_slice,
-                               int64_t ld_w_slice, int flags) {
+                               int64_t ld_w_slice, const void* x_slice, int64_t ld_x_slice, int flags) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, side == SL_SIDE_OUT || side == SL_SIDE_IN, "bad side");
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     SL_REQUIRE(h, T >= 0 && T <= 65535 && D_in >= 1 && D_out >= 1, "bad sizes");
-    SL_REQUIRE(h, (flags & ~(SL_NO_FILL | SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) == 0 &&
-                      (flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)) != (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS),
-               "bad flags");
-    SL_REQUIRE(h, side == SL_SIDE_IN || !(flags & (SL_ONLY_OUT_ROWS | SL_ONLY_CTX_ROWS)),
-               "row-subset flags apply to side IN");
+    SL_CHECK(check_flags(h, flags, side == SL_SIDE_IN));
     SL_CHECK(check_rows(h, ctx_rows, T_c, out_rows, T_o, T));
     const int64_t C = side == SL_SIDE_OUT ? D_out : D_in;
     if (w_slice) {
         SL_REQUIRE(h, side == SL_SIDE_OUT, "w_slice applies to side OUT");
         SL_CHECK(check_matrix(h, w_slice, ld_w_slice, (n + 7) / 8 * 8, dt, "w_slice"));
+    }
+    if (x_slice) {
+        SL_REQUIRE(h, side == SL_SIDE_OUT, "x_slice applies to side OUT");
+        SL_CHECK(check_matrix(h, x_slice, ld_x_slice, (n + 7) / 8 * 8, dt, "x_slice"));
     }
     SL_REQUIRE(h, n >= 0 && n <= C, "n must be in [0, C]");
     SL_REQUIRE(h, n == 0 || idx != nullptr, "idx is NULL");
@@ -1050,9 +1076,9 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
     SL_CHECK(debug_check_list(h, ctx_rows, T_c, T, "ctx_rows"));
     SL_CHECK(debug_check_list(h, out_rows, T_o, T, "out_rows"));
     SL_CHECK(check_matrix(h, dy, lddy, D_out, dt, "dy"));
-    SL_CHECK(check_matrix(h, dx, lddx, D_in, dt, "dx"));
+    SL_CHECK(check_matrix(h, dx, lddx, (flags & SL_CTX_COMPACT) ? (n > 0 ? n : 1) : D_in, dt, "dx"));
     SL_CHECK(check_matrix(h, Wt, ldwt, D_out, dt, "Wt"));
-    const bool need_w = side == SL_SIDE_OUT && n < C && T_c > 0;
+    const bool need_w = side == SL_SIDE_OUT && n < C && T_c > 0 && !w_slice;
     if (need_w) SL_CHECK(check_matrix(h, W, ldw, D_in, dt, "W"));
     DeviceGuard g(h->device);
     if (side == SL_SIDE_IN)   // dx = dy W: context rows produce the selected channels only
@@ -1060,7 +1086,7 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt, const vo
                           idx, n, dx, lddx, beta, l, flags);
     // side OUT: context rows contract over the selected output channels only
     return in_sparse(h, dt, dy, lddy, T, D_out, Wt, ldwt, W, ldw, D_in, ctx_rows, T_c, out_rows,
-                     T_o, idx, n, dx, lddx, beta, l, w_slice, ld_w_slice);
+                     T_o, idx, n, dx, lddx, beta, l, w_slice, ld_w_slice, x_slice, ld_x_slice);
 }
 
 sl_status sl_weight_slice(sl_handle* h, sl_dtype dt, const void* Wc, int64_t ldwc, int64_t C,
@@ -1243,24 +1269,61 @@ sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
 }
 
 sl_status sl_swiglu_fwd_lora(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg, const void* u, int64_t ldu,
-                             int64_t T, int64_t F, void* hout, int64_t ldh, const void* A, int64_t lda, int64_t r,
-                             float* xl, int64_t ldxl) {
+                             int64_t T, int64_t F, const int32_t* rows, int64_t n_rows, void* hout, int64_t ldh,
+                             const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     if (dt != SL_BF16) return fail(h, SL_ERR_UNSUPPORTED, "the fused SwiGLU + LoRA pass is bf16 only");
     SL_REQUIRE(h, T >= 0 && T <= 65535 * 16 && F >= 1 && F % 8 == 0, "bad sizes (F must be a multiple of 8)");
     SL_REQUIRE(h, r >= 1 && r <= 32, "r must be in [1, 32]");
-    if (T == 0) return SL_OK;
+    SL_REQUIRE(h, !rows || (n_rows >= 0 && n_rows <= T), "n_rows must be in [0, T]");
+    const int64_t nr = rows ? n_rows : T;
+    if (nr == 0) return SL_OK;
     SL_CHECK(check_matrix(h, g, ldg, F, dt, "g"));
     SL_CHECK(check_matrix(h, u, ldu, F, dt, "u"));
     SL_CHECK(check_matrix(h, hout, ldh, F, dt, "h"));
     SL_CHECK(check_matrix(h, A, lda, F, dt, "A"));
     SL_REQUIRE(h, xl != nullptr && ldxl >= r, "xl is NULL or ldxl < r");
-    SL_CHECK(ensure_ws(h, round_up(swiglu_fwd_lora_ws_floats(T, F, r) * 4, 256)));
+    if (rows) SL_CHECK(debug_check_list(h, rows, nr, T, "rows"));
+    SL_CHECK(ensure_ws(h, round_up(swiglu_fwd_lora_ws_floats(nr, F, r) * 4, 256)));
     DeviceGuard gd(h->device);
-    Timed tm(h, K_SWIGLU, 2.0 * T * F * r, 3.0 * T * F * 2 + 2.0 * r * F + 4.0 * T * r);
-    return hip_check(h, launch_swiglu_fwd_lora(g, ldg, u, ldu, T, F, hout, ldh, A, lda, r, xl, ldxl,
+    Timed tm(h, K_SWIGLU, 2.0 * nr * F * r, 3.0 * nr * F * 2 + 2.0 * r * F + 4.0 * nr * r);
+    return hip_check(h, launch_swiglu_fwd_lora(g, ldg, u, ldu, rows, nr, F, hout, ldh, A, lda, r, xl, ldxl,
                                                (float*)h->ws, h->stream), "swiglu_fwd_lora");
+}
+
+sl_status sl_swiglu_fwd_ctx(sl_handle* h, sl_dtype dt, const void* Yc, int64_t ldyc, const int32_t* ctx_rows,
+                            int64_t T_c, int64_t T, int64_t F, const int32_t* idx, int64_t n, const float* lora_P,
+                            int64_t ld_lora_P, const void* lora_B, int64_t ld_lora_B, int64_t lora_r,
+                            float lora_scale, void* gu, int64_t ldgu, void* hc, int64_t ldhc, const void* A,
+                            int64_t lda, int64_t r, float* xl, int64_t ldxl, void* h_rows, int64_t ld_h_rows) {
+    if (!h) return SL_ERR_INVALID;
+    SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
+    if (dt != SL_BF16) return fail(h, SL_ERR_UNSUPPORTED, "the fused context-row SwiGLU pass is bf16 only");
+    SL_REQUIRE(h, T >= 0 && T <= 65535 * 64 && T_c >= 0 && T_c <= T, "bad sizes");
+    SL_REQUIRE(h, F >= 1 && F % 8 == 0, "F must be a positive multiple of 8");
+    SL_REQUIRE(h, n >= 0 && n <= F, "n must be in [0, F]");
+    SL_REQUIRE(h, lora_r >= 1 && lora_r <= 64 && r >= 1 && r <= 32, "lora_r must be in [1, 64] and r in [1, 32]");
+    if (T_c == 0) return SL_OK;
+    SL_REQUIRE(h, ctx_rows != nullptr && (n == 0 || idx != nullptr), "ctx_rows or idx is NULL");
+    SL_REQUIRE(h, lora_P != nullptr && ld_lora_P >= lora_r, "lora_P is NULL or ld_lora_P < lora_r");
+    SL_REQUIRE(h, xl != nullptr && ldxl >= r, "xl is NULL or ldxl < r");
+    if (n > 0) SL_CHECK(check_matrix(h, Yc, ldyc, 2 * n, dt, "Yc"));
+    SL_CHECK(check_matrix(h, lora_B, ld_lora_B, lora_r, dt, "lora_B"));
+    SL_CHECK(check_matrix(h, gu, ldgu, 2 * F, dt, "gu"));
+    SL_CHECK(check_matrix(h, hc, ldhc, (n + 7) / 8 * 8 > 0 ? (n + 7) / 8 * 8 : 8, dt, "hc"));
+    SL_CHECK(check_matrix(h, A, lda, F, dt, "A"));
+    if (h_rows) SL_CHECK(check_matrix(h, h_rows, ld_h_rows, F, dt, "h_rows"));
+    SL_CHECK(debug_check_list(h, idx, n, F, "idx"));
+    SL_CHECK(debug_check_list(h, ctx_rows, T_c, T, "ctx_rows"));
+    SL_CHECK(ensure_ws(h, round_up(swiglu_fwd_ctx_ws_floats(T_c, F, r) * 4, 256)));
+    DeviceGuard gd(h->device);
+    Timed tm(h, K_SWIGLU, 2.0 * T_c * F * (r + 2 * lora_r),
+             2.0 * T_c * (2.0 * n + 2.0 * F + n) + 4.0 * T_c * (lora_r + r) + 2.0 * F * (2 * lora_r + r));
+    return hip_check(h, launch_swiglu_fwd_ctx(gu, ldgu, ctx_rows, T_c, F, lora_P, ld_lora_P, lora_B, ld_lora_B,
+                                              lora_r, lora_scale, Yc, ldyc, idx, n, hc, ldhc, (n + 7) / 8 * 8, A,
+                                              lda, r, xl, ldxl, h_rows, ld_h_rows, (float*)h->ws, h->stream),
+                     "swiglu_fwd_ctx");
 }
 
 sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh, const void* g, int64_t ldg,

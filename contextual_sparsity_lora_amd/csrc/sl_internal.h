@@ -267,9 +267,17 @@ hipError_t launch_swiglu_fwd(bool bf16, const void* g, int64_t ldg, const void* 
                              int64_t T, int64_t F, void* h, int64_t ldh, hipStream_t st);
 // SwiGLU with the LoRA reductions reading the same tensors (bf16, r <= 32).
 size_t swiglu_fwd_lora_ws_floats(int64_t T, int64_t F, int64_t r);
-hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, int64_t T, int64_t F,
-                                  void* h, int64_t ldh, const void* A, int64_t lda, int64_t r, float* xl,
-                                  int64_t ldxl, float* part, hipStream_t st);
+hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int64_t ldu, const int32_t* rows,
+                                  int64_t nr, int64_t F, void* h, int64_t ldh, const void* A, int64_t lda, int64_t r,
+                                  float* xl, int64_t ldxl, float* part, hipStream_t st);
+// Context rows from their compact gate|up product: merged gu rows, compact h,
+// and the rows of h A^T (bf16, 2r <= 64, r <= 32).
+size_t swiglu_fwd_ctx_ws_floats(int64_t nrows, int64_t F, int64_t r);
+hipError_t launch_swiglu_fwd_ctx(void* gu, int64_t ldgu, const int32_t* rows, int64_t nrows, int64_t F,
+                                 const float* P, int64_t ldp, const void* B, int64_t ldb, int64_t r2, float scale,
+                                 const void* Yc, int64_t ldyc, const int32_t* idx, int64_t n, void* hc, int64_t ldhc,
+                                 int64_t npad, const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
+                                 void* hf, int64_t ldhf, float* part, hipStream_t st);
 size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk);
 hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, int64_t ldg, const void* u,
                                   int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,

@@ -99,6 +99,14 @@ class SparseFFN:
         # read the same tensors (h A_down^T forward; dA_down, dB_gate, dB_up
         # backward), so h, dh, g, u, dg and du are each read once
         self.fused_swiglu_lora = (self.dtype == torch.bfloat16 and self.r <= 32 and self.F % 8 == 0)
+        # compact_ctx (sparse bf16 forward): the context rows' gate|up product
+        # stays compact and one pass forms their merged gate|up rows (kept for
+        # the backward), the compact h the down product reads, and their
+        # h A_down^T; h itself is then written for the output rows only
+        # (keep_h: for the context rows too, as a check of that pass).  Off by
+        # default: measured slower than merge + fused SwiGLU + gather so far.
+        self.compact_ctx = False
+        self.keep_h = False
         self._T = None
 
     def set_dense(self, dense: bool):
@@ -157,6 +165,9 @@ class SparseFFN:
         c8 = lambda n: (n + 7) // 8 * 8
         self.ws_dn = e(D, c8(self.n), dtype=dt) if dt == torch.bfloat16 else None
         self.ws_gu = e(D, c8(2 * self.n), dtype=dt) if dt == torch.bfloat16 else None
+        # compact context-row operands: gate|up product [T_c, 2n], h [T_c, n]
+        self.yc_gu = e(T_c, c8(2 * self.n), dtype=dt) if dt == torch.bfloat16 else None
+        self.hc = e(T_c, c8(self.n), dtype=dt) if dt == torch.bfloat16 else None
         self._T = (T, T_c, T_o)
 
     def forward(self, x, roles, T_c):
@@ -201,22 +212,35 @@ class SparseFFN:
                 ops.weight_slice(self.W_gu, self.idx2, self.ws_gu)
             self._ev[3].record(self.side)
         main.wait_event(self._ev[1])
-        # the gate|up main branch of the context rows (gathered channels; every
-        # row when dense or not overlapped) with the LoRA term fused into the
-        # same accumulators
-        ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
-                              lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
-        main.wait_event(self._ev[3])
         g, u = self.gu[:, :F], self.gu[:, F:]
-        if self.fused_swiglu_lora:
-            ops.swiglu_fwd_lora(g, u, self.h, self.A_down, self.xl_dn)
+        self._compact = compact = overlap and self.compact_ctx and self._slices
+        if compact:
+            # the context rows' gate|up product over the selected channels,
+            # stored compactly (LoRA term of those channels fused)
+            ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
+                                  self.yc_gu[:, :2 * self.n], lora=lora,
+                                  flags=ops.ONLY_CTX_ROWS | ops.CTX_COMPACT)
+            ops.swiglu_fwd_ctx(self.yc_gu, self.ctx_rows, self.idx, lora, self.gu, self.hc, self.A_down,
+                               self.xl_dn, h_rows=self.h if self.keep_h else None)
+            main.wait_event(self._ev[3])
+            ops.swiglu_fwd_lora(g, u, self.h, self.A_down, self.xl_dn, rows=self.out_rows)
         else:
-            ops.swiglu_fwd(g, u, self.h)
-            ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
+            # the gate|up main branch of the context rows (gathered channels;
+            # every row when dense or not overlapped) with the LoRA term fused
+            # into the same accumulators
+            ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2, self.gu,
+                                  lora=lora, flags=ops.ONLY_CTX_ROWS if overlap else 0)
+            main.wait_event(self._ev[3])
+            if self.fused_swiglu_lora:
+                ops.swiglu_fwd_lora(g, u, self.h, self.A_down, self.xl_dn)
+            else:
+                ops.swiglu_fwd(g, u, self.h)
+                ops.lora_fwd_bwd(ops.LORA_XL, self.h, self.A_down, None, self.scale, self.xl_dn)
         # down main branch: input channels = the same selection; LoRA fused
         ops.sparse_linear_fwd("in", self.h, self.W_dn, self.Wt_dn, self.ctx_rows, self.out_rows,
                               self.idx, self.y, lora=(self.xl_dn, self.B_down, r, self.scale),
-                              w_slice=self.ws_dn if self._slices else None)
+                              w_slice=self.ws_dn if self._slices else None,
+                              x_slice=self.hc if compact else None)
         return self.y
 
     def _select(self, x):

@@ -262,15 +262,19 @@ def _lora_args(lora):
 NO_FILL = 1
 ONLY_OUT_ROWS = 2
 ONLY_CTX_ROWS = 4
+CTX_COMPACT = 8
 
 
 def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=None,
-                      w_slice=None, flags=0):
+                      w_slice=None, flags=0, x_slice=None):
     """W: frozen weight [D_out, D_in] (nn.Linear layout); Wt: its transposed
     copy [D_in, D_out] (read for side "in" only; may be None for side "out").
     lora = (xl, B, r, scale) fuses y += scale * xl B^T into the same pass.
-    w_slice: weight_slice(Wt, idx) built beforehand (side "in"); flags:
-    NO_FILL leaves the unselected context channels (side "out") unwritten."""
+    w_slice: weight_slice(Wt, idx) built beforehand (side "in"); x_slice: the
+    context rows' selected columns of x, compact and zero-padded (side "in");
+    flags: NO_FILL leaves the unselected context channels (side "out")
+    unwritten; CTX_COMPACT | ONLY_CTX_ROWS writes the context rows' product
+    compactly to y [T_c, n]."""
     h = handle(_dev(x))
     T, D_in = x.shape
     D_out = W.shape[0]
@@ -280,12 +284,13 @@ def sparse_linear_fwd(side, x, W, Wt, ctx_rows, out_rows, idx, y, beta=0, lora=N
                                           D_out, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
                                           out_rows.numel(), _ptr(idx), n, _ptr(y), _ld(y), int(beta),
                                           *_lora_args(lora), _ptr(w_slice),
-                                          _ld(w_slice) if w_slice is not None else 0, int(flags))
+                                          _ld(w_slice) if w_slice is not None else 0, _ptr(x_slice),
+                                          _ld(x_slice) if x_slice is not None else 0, int(flags))
     _check(h, st, "sl_sparse_linear_fwd")
 
 
 def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora=None,
-                      w_slice=None, flags=0):
+                      w_slice=None, flags=0, x_slice=None):
     """Input gradient of sparse_linear_fwd.  Wt [D_in, D_out] is read by every
     product; W [D_out, D_in] only for side "out" (may be None for side "in").
     lora = (gB, A^T, r, scale) fuses dx += scale * gB A into the same pass.
@@ -300,7 +305,8 @@ def sparse_linear_bwd(side, dy, W, Wt, ctx_rows, out_rows, idx, dx, beta=0, lora
                                           D_in, _ptr(ctx_rows), ctx_rows.numel(), _ptr(out_rows),
                                           out_rows.numel(), _ptr(idx), n, _ptr(dx), _ld(dx),
                                           int(beta), *_lora_args(lora), _ptr(w_slice),
-                                          _ld(w_slice) if w_slice is not None else 0, int(flags))
+                                          _ld(w_slice) if w_slice is not None else 0, _ptr(x_slice),
+                                          _ld(x_slice) if x_slice is not None else 0, int(flags))
     _check(h, st, "sl_sparse_linear_bwd")
 
 
@@ -371,14 +377,32 @@ def swiglu_bwd(dh, g, u, dg, du):
     _check(h, st, "sl_swiglu_bwd")
 
 
-def swiglu_fwd_lora(g, u, hout, A, xl):
+def swiglu_fwd_lora(g, u, hout, A, xl, rows=None):
     """hout = silu(g) u and xl = hout A^T (fp32 [T, r]) in one pass over g, u
-    (bf16; A [r, F])."""
+    (bf16; A [r, F]); rows: only those rows (int32 device list)."""
     h = handle(_dev(g))
     T, F = g.shape
-    st = _lib.load().sl_swiglu_fwd_lora(h, _dt(g), _ptr(g), _ld(g), _ptr(u), _ld(u), T, F, _ptr(hout), _ld(hout),
+    st = _lib.load().sl_swiglu_fwd_lora(h, _dt(g), _ptr(g), _ld(g), _ptr(u), _ld(u), T, F, _ptr(rows),
+                                        rows.numel() if rows is not None else 0, _ptr(hout), _ld(hout),
                                         _ptr(A), _ld(A), A.shape[0], _ptr(xl), _ld(xl))
     _check(h, st, "sl_swiglu_fwd_lora")
+
+
+def swiglu_fwd_ctx(Yc, ctx_rows, idx, lora, gu, hc, A, xl, h_rows=None):
+    """Context rows of a sparse SwiGLU FFN from the compact gate|up product Yc
+    [T_c, >= 2n]: merged gate|up rows into gu [T, 2F], compact h into hc
+    [T_c, >= ceil8(n)], and xl = h A^T rows (fp32); h_rows [T, F] optionally
+    receives the whole h rows.  lora = (xl_gu, B_bd, 2r, scale) as for the
+    gate|up product."""
+    h = handle(_dev(gu))
+    T, F2 = gu.shape
+    P, B, r2, s = lora
+    n = idx.numel()
+    st = _lib.load().sl_swiglu_fwd_ctx(h, _dt(gu), _ptr(Yc), _ld(Yc), _ptr(ctx_rows), ctx_rows.numel(), T,
+                                       F2 // 2, _ptr(idx), n, _ptr(P), _ld(P), _ptr(B), _ld(B), int(r2), float(s),
+                                       _ptr(gu), _ld(gu), _ptr(hc), _ld(hc), _ptr(A), _ld(A), A.shape[0],
+                                       _ptr(xl), _ld(xl), _ptr(h_rows), _ld(h_rows) if h_rows is not None else 0)
+    _check(h, st, "sl_swiglu_fwd_ctx")
 
 
 def swiglu_bwd_lora(dh, g, u, dg, du, gB, xl_g, xl_u, scale, dA, dB_g, dB_u):

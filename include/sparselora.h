@@ -77,8 +77,14 @@ enum {
                              (dense over every channel; idx is not read, so the
                              selection may still be in the making on another
                              stream); context rows untouched */
-    SL_ONLY_CTX_ROWS = 4  /* the complement: context rows only (selected channels,
+    SL_ONLY_CTX_ROWS = 4, /* the complement: context rows only (selected channels,
                              and the unselected ones unless SL_NO_FILL) */
+    SL_CTX_COMPACT = 8    /* side-OUT-shaped products, with SL_ONLY_CTX_ROWS: the
+                             context rows' product over the selected channels
+                             is stored compactly, y[m, j] for context row m and
+                             selected channel idx[j] (y then has T_c rows and
+                             ldy >= n), the rank-r term included; the
+                             unselected channels are not formed */
 };
 
 /* sl_lora_fwd_bwd mode bits. */
@@ -360,12 +366,18 @@ sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const 
  *   w_slice  optional (side IN only): the context-row weight slice built
  *       beforehand by sl_weight_slice from Wt and the same idx, dt
  *       [D_out, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
+ *   x_slice  optional (side IN only): the context rows' selected input
+ *       channels given compactly, x_slice[m, j] = x[ctx_rows[m], idx[j]],
+ *       dt [T_c, ld_x_slice >= ceil8(n)] with columns n .. ceil8(n) zero (as
+ *       sl_swiglu_fwd_ctx writes it); NULL gathers them from x inside the call
  *   flags  SL_NO_FILL (side OUT: the unselected channels of context rows
  *       are left unwritten; with lora_P they must be written by
  *       sl_lora_fill_unselected, without it the caller zeroes them), and at
  *       most one of SL_ONLY_OUT_ROWS / SL_ONLY_CTX_ROWS (side OUT: one of the
  *       two row sets per call; the two calls together compute what one call
- *       without them computes, up to the order of fp32 accumulation)
+ *       without them computes, up to the order of fp32 accumulation), and
+ *       SL_CTX_COMPACT with SL_ONLY_CTX_ROWS (side OUT, bf16: the compact
+ *       context-row product, see the flag)
  * dt = SL_BF16 (MFMA path) or SL_F32. */
 sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* x, int64_t ldx, int64_t T, int64_t D_in,
@@ -378,7 +390,8 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const float* lora_P, int64_t ld_lora_P,
                                const void* lora_B, int64_t ld_lora_B,
                                int64_t lora_r, float lora_scale,
-                               const void* w_slice, int64_t ld_w_slice, int flags);
+                               const void* w_slice, int64_t ld_w_slice,
+                               const void* x_slice, int64_t ld_x_slice, int flags);
 
 /* ---------------------------------------------------------------- a10/a11: main backward */
 
@@ -399,8 +412,10 @@ sl_status sl_sparse_linear_fwd(sl_handle* h, sl_side side, sl_dtype dt,
  * hold this term instead of 0.
  *   w_slice  optional (side OUT only): sl_weight_slice of W with the same idx,
  *       dt [D_in, ld_w_slice >= ceil8(n)]; NULL builds it inside the call
+ *   x_slice  optional (side OUT only): dy's context rows at the selected
+ *       channels, compact and zero-padded as for the forward; NULL gathers
  *   flags  as for the forward, with side IN in place of side OUT
- *       (SL_NO_FILL, SL_ONLY_OUT_ROWS, SL_ONLY_CTX_ROWS) */
+ *       (SL_NO_FILL, SL_ONLY_OUT_ROWS, SL_ONLY_CTX_ROWS, SL_CTX_COMPACT) */
 sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const void* dy, int64_t lddy, int64_t T, int64_t D_out,
                                const void* W, int64_t ldw, const void* Wt, int64_t ldwt,
@@ -412,7 +427,8 @@ sl_status sl_sparse_linear_bwd(sl_handle* h, sl_side side, sl_dtype dt,
                                const float* lora_P, int64_t ld_lora_P,
                                const void* lora_B, int64_t ld_lora_B,
                                int64_t lora_r, float lora_scale,
-                               const void* w_slice, int64_t ld_w_slice, int flags);
+                               const void* w_slice, int64_t ld_w_slice,
+                               const void* x_slice, int64_t ld_x_slice, int flags);
 
 /* Context-row weight slice of a sparse product, built ahead of the product
  * (e.g. on another stream right after the selection) so the product itself
@@ -562,14 +578,48 @@ sl_status sl_swiglu_bwd(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
  * its input is the whole hidden state h):
  *   h = silu(g) * u                  (exactly as sl_swiglu_fwd, stored in dt)
  *   xl[t, j] = sum_c h[t, c] A[j, c] (fp32, from the stored h; as SL_LORA_XL)
- * so h is read once.  A [r, lda >= F] (dt) is the down projection's LoRA A;
- * xl fp32 [T, ldxl >= r] out.  bf16 only (SL_ERR_UNSUPPORTED otherwise),
+ * so h is read once.  rows: NULL for all T rows, else the n_rows listed rows
+ * (e.g. the output rows of a sparse FFN; each row index < T).  A [r, lda >=
+ * F] (dt) is the down projection's LoRA A; xl fp32 [T, ldxl >= r] out (the
+ * processed rows).  bf16 only (SL_ERR_UNSUPPORTED otherwise),
  * F % 8 == 0, 1 <= r <= 32.  xl's sum is a fixed-order reduction over column
  * blocks (deterministic). */
 sl_status sl_swiglu_fwd_lora(sl_handle* h, sl_dtype dt, const void* g, int64_t ldg,
                              const void* u, int64_t ldu, int64_t T, int64_t F,
+                             const int32_t* rows, int64_t n_rows,
                              void* hout, int64_t ldh, const void* A, int64_t lda, int64_t r,
                              float* xl, int64_t ldxl);
+/* The same pass for the context rows of a sparse SwiGLU FFN, from the compact
+ * gate|up product (PG §3.4 Algorithm 1 steps 5-6 and "FFN structure": the
+ * context rows' gate and up outputs are the selected channels' products, the
+ * dense LoRA term alone at the others; "Token Sensitivity": output rows are
+ * dense and take sl_swiglu_fwd_lora):  for m < T_c, t = ctx_rows[m], c < F,
+ *   g[t, c] = Yc[m, j] if c = idx[j], else lora_scale * P[t, :] . B[c, :]
+ *   u[t, c] = Yc[m, n + j] if c = idx[j], else lora_scale * P[t, :] . B[F + c, :]
+ *     (the rank-r values formed exactly as the SL_LORA fill/merge of a sparse
+ *     product forms them: s P rounded to dt, fp32 accumulation, one rounding),
+ *     stored to gu[t, c] and gu[t, F + c] (the backward reads them);
+ *   h = silu(g) u (exactly as sl_swiglu_fwd), of which only the selected
+ *     channels are stored: hc[m, j] = h[t, idx[j]], columns n .. ceil8(n) of
+ *     hc zero (the x_slice of the down product);
+ *   xl[t, :] = sum over every channel c of h[t, c] A[:, c] (fp32, as
+ *     sl_swiglu_fwd_lora);
+ *   h_rows[t, :] = h[t, :] when h_rows is not NULL (whole rows; a check of
+ *     the pass, not needed by the FFN: the down product reads hc).
+ * Yc: dt [T_c, ldyc >= 2n], the SL_CTX_COMPACT product of the gate|up weight
+ * [2F, D] with the stacked selection (idx, idx + F); P fp32 [T, ld_P] (x A^T
+ * of gate|up), B dt [2F, ld_B] (the block-diagonal gate|up LoRA B, 2r ranks);
+ * gu dt [T, ldgu >= 2F]; hc dt [T_c, ldhc >= ceil8(n)]; A dt [r, lda >= F]
+ * (the down projection's LoRA A); xl fp32 [T, ldxl >= r] (rows t = ctx_rows[m]
+ * written).  bf16 only, F % 8 == 0, lora_r = 2r <= 64, r <= 32. */
+sl_status sl_swiglu_fwd_ctx(sl_handle* h, sl_dtype dt, const void* Yc, int64_t ldyc,
+                            const int32_t* ctx_rows, int64_t T_c, int64_t T, int64_t F,
+                            const int32_t* idx, int64_t n,
+                            const float* lora_P, int64_t ld_lora_P, const void* lora_B,
+                            int64_t ld_lora_B, int64_t lora_r, float lora_scale,
+                            void* gu, int64_t ldgu, void* hc, int64_t ldhc,
+                            const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
+                            void* h_rows, int64_t ld_h_rows);
 /* SwiGLU backward fused with the three LoRA gradient reductions that read the
  * same tensors (PG §3.2 "Information flow during a backward pass": the LoRA
  * gradients are computed in full; §3.4 "FFN structure"):

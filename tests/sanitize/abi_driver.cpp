@@ -81,7 +81,7 @@ int main() {
     auto fwd = [&](sl_side side, sl_dtype dt, const void* x, int64_t ldx, int64_t T, const int32_t* idx,
                    int64_t n, int flags) {
         return sl_sparse_linear_fwd(h, side, dt, x, ldx, T, 64, p, 64, p, 64, 64, ip, T / 2, ip, T - T / 2, idx, n,
-                                    p, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, flags);
+                                    p, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, nullptr, 0, flags);
     };
     expect(h, fwd((sl_side)7, SL_BF16, p, 64, 8, ip, 4, 0), INV, "fwd side");
     expect(h, fwd(SL_SIDE_OUT, (sl_dtype)5, p, 64, 8, ip, 4, 0), INV, "fwd dtype");
@@ -93,11 +93,25 @@ int main() {
     expect(h, fwd(SL_SIDE_OUT, SL_BF16, mis, 64, 8, ip, 4, 0), INV, "fwd x misaligned");
     expect(h, fwd(SL_SIDE_OUT, SL_BF16, p, 68, 8, ip, 4, 0), INV, "fwd ldx not 16-byte rows");
     expect(h, fwd(SL_SIDE_OUT, SL_BF16, p, 64, 8, ip, 4, 1 << 9), INV, "fwd unknown flag");
+    expect(h, fwd(SL_SIDE_OUT, SL_BF16, p, 64, 8, ip, 4, SL_CTX_COMPACT), INV, "fwd compact without ctx-only");
+    expect(h, fwd(SL_SIDE_IN, SL_BF16, p, 64, 8, ip, 4, SL_CTX_COMPACT | SL_ONLY_CTX_ROWS), INV,
+           "fwd compact on side in");
+    expect(h, sl_swiglu_fwd_lora(h, SL_BF16, p, 64, p, 64, 8, 64, ip, 9, p, 64, p, 64, 16, fp, 16), INV,
+           "swiglu_fwd_lora n_rows > T");
+    expect(h, sl_swiglu_fwd_ctx(h, SL_BF16, p, 64, ip, 4, 8, 60, ip, 4, fp, 32, p, 32, 32, 1.0f, p, 128, p, 8, p,
+                                64, 16, fp, 16, nullptr, 0),
+           INV, "swiglu_fwd_ctx F not a multiple of 8");
+    expect(h, sl_swiglu_fwd_ctx(h, SL_BF16, p, 64, ip, 4, 8, 64, ip, 4, fp, 32, p, 32, 80, 1.0f, p, 128, p, 8, p,
+                                64, 16, fp, 16, nullptr, 0),
+           INV, "swiglu_fwd_ctx lora_r above 64");
+    expect(h, sl_swiglu_bwd_lora(h, SL_BF16, p, 64, p, 64, p, 64, 8, 64, p, 64, p, 64, fp, 16, fp, 32, fp, 32, 40,
+                                 1.0f, fp, fp, fp),
+           INV, "swiglu_bwd_lora r above 32");
     expect(h, sl_sparse_linear_bwd(h, SL_SIDE_IN, SL_BF16, p, 64, 8, 64, p, 64, nullptr, 64, 64, ip, 4, ip, 4, ip,
-                                   4, p, 64, 0, fp, 16, p, 16, 200, 1.0f, nullptr, 0, 0),
+                                   4, p, 64, 0, fp, 16, p, 16, 200, 1.0f, nullptr, 0, nullptr, 0, 0),
            INV, "bwd LoRA rank above the limit");
     expect(h, sl_sparse_linear_bwd(h, SL_SIDE_OUT, SL_BF16, p, 64, 8, 64, p, 64, nullptr, 64, 64, ip, 4, ip, 4, ip,
-                                   4, nullptr, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, 0),
+                                   4, nullptr, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, nullptr, 0, 0),
            INV, "bwd dx NULL");
     expect(h, sl_weight_slice(h, SL_BF16, p, 64, 64, ip, 65, 64, p, 72), INV, "weight_slice n > C");
     expect(h, sl_lora_fill_unselected(h, SL_BF16, p, 64, ip, 4, 64, nullptr, 16, p, 16, 16, 1.0f, ip, 4), INV,
@@ -129,7 +143,8 @@ int main() {
     expect(nullptr, sl_set_option(nullptr, "debug", 1), INV, "set_option NULL handle");
     expect(nullptr, sl_select_top(nullptr, fp, 64, 8, ip), INV, "select_top NULL handle");
     expect(nullptr, sl_sparse_linear_fwd(nullptr, SL_SIDE_OUT, SL_BF16, p, 64, 8, 64, p, 64, p, 64, 64, ip, 4, ip, 4,
-                                         ip, 4, p, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, 0),
+                                         ip, 4, p, 64, 0, nullptr, 0, nullptr, 0, 0, 1.0f, nullptr, 0, nullptr, 0,
+                                         0),
            INV, "fwd NULL handle");
 
     std::printf("%d checks, %d failed\n", g_checks, g_fail);

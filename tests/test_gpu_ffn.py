@@ -24,7 +24,7 @@ def _inputs(cid):
     return make_ffn_inputs(CONFIGS[cid])
 
 
-def _run(cid):
+def _run(cid, keep_h=True, compact_ctx=None):
     need_lib()
     from contextual_sparsity_lora_amd.ffn import SparseFFN
     cfg = CONFIGS[cid]
@@ -38,6 +38,9 @@ def _run(cid):
                     to_dev(np.ascontiguousarray(inp["WA_t_gu"].T), "f32"),
                     to_dev(inp["WB_gate"], "f32"), to_dev(inp["WB_up"], "f32"), inp["scale"],
                     sparsity=cfg.ffn_sparsity)
+    blk.keep_h = keep_h      # h of the context rows as well (checked below)
+    if compact_ctx is not None:
+        blk.compact_ctx = compact_ctx
     roles = to_dev(inp["roles"], None)
     y = blk.forward(d["x"], roles, cfg.ctx_tokens)
     dx = blk.backward(d["dy"])
@@ -75,8 +78,12 @@ def test_ffn_block_f32_end_to_end():
 
 
 def test_ffn_block_bf16_full_size():
-    cfg, inp, blk, y, dx = _run(2)
-    print("[ffn] config 2 full size", flush=True)
+    _full_size_checks(compact_ctx=False)
+
+
+def _full_size_checks(compact_ctx):
+    cfg, inp, blk, y, dx = _run(2, compact_ctx=compact_ctx)
+    print(f"[ffn] config 2 full size (compact context rows: {compact_ctx})", flush=True)
     F, r, s = cfg.inter, cfg.lora_rank, inp["scale"]
     tol = TOL["bf16"]
     idx = _selection(cfg, inp)
@@ -124,3 +131,37 @@ def test_ffn_block_bf16_full_size():
     assert mar(host(y)[R], f["y"]) <= tol
     b = ref.ffn_block_bwd(sub, f, idx)
     assert mar(host(dx)[R], b["dx"]) <= tol
+
+
+def test_ffn_block_compact_context_rows():
+    """The compact context-row path stores h of the context rows only
+    compactly (the down product's operand): the same outputs and gradients
+    bit for bit as with the whole rows kept, hc equal to those rows' selected
+    channels (padding columns zero), and the per-op checks of the full-size
+    test hold on it as well."""
+    cfg, inp, blk, y, dx = _run(2, keep_h=True, compact_ctx=True)
+    print("[ffn] config 2 compact context rows", flush=True)
+    if not blk._compact:
+        pytest.skip("the block does not take the compact context-row path here")
+    ctx, _ = ref.token_lists(inp["roles"])
+    n = blk.n
+    idx = host_i(blk.idx)
+    hc = host(blk.hc)
+    h = host(blk.h)
+    assert np.array_equal(hc[:, :n], h[ctx][:, idx])
+    assert np.all(hc[:, n:] == 0.0)
+    ref_out = {k: host(getattr(blk, k)).copy() for k in ("y", "dx", "gu", "dgu", "dA_gate", "dB_gate", "dA_up",
+                                                          "dB_up", "dA_down", "dB_down")}
+    blk.keep_h = False
+    roles = to_dev(inp["roles"], None)
+    d = {k: to_dev(inp[k], cfg.dtype) for k in ("x", "dy")}
+    blk.forward(d["x"], roles, cfg.ctx_tokens)
+    blk.backward(d["dy"])
+    torch.cuda.synchronize()
+    for k, v in ref_out.items():
+        assert np.array_equal(host(getattr(blk, k)), v), k
+
+
+def test_ffn_block_bf16_full_size_compact_path():
+    """The full-size per-op checks on the compact context-row path."""
+    _full_size_checks(compact_ctx=True)

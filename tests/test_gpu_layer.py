@@ -56,6 +56,7 @@ def _run(key):
         f32["WB_" + p] = to_dev(inp["WB_" + p], "f32")
     L = SparseDecoderLayer.from_arrays(d, f32, cfg, cfg.qk_sparsity, cfg.vo_sparsity,
                                        cfg.ffn_sparsity)
+    L.ffn.keep_h = True      # whole rows of the FFN's h, for the checks
     roles = to_dev(inp["roles"], None)
     L.forward(d["x"], roles, cfg.ctx_tokens)
     L.backward(d["dy"])

@@ -55,6 +55,8 @@ def _build_and_run(cfg, ramp, keep_host):
             kept[l] = lw
         print(f"[stack] layer {l} generated and uploaded (sparsity {sp[0]}/{sp[1]})", flush=True)
     stack = SparseStack.build(cfg, arrays, sps)
+    for L in stack.layers:
+        L.ffn.keep_h = True  # whole rows of the FFN's h, for the checks
     del arrays
     roles = to_dev(io["roles"], None)
     stack.forward(to_dev(io["x"], dt), roles, cfg.ctx_tokens)
