@@ -34,7 +34,8 @@ def test_random_scores_bits(seed, C):
     assert np.array_equal(bits(host(s)), bits(csa.random_scores(seed, C)))
 
 
-@pytest.mark.parametrize("C,n", [(1000, 0), (1000, 1), (1000, 333), (1000, 1000), (14336, 4301), (17, 5)])
+@pytest.mark.parametrize("C,n", [(1000, 0), (1000, 1), (1000, 333), (1000, 1000), (14336, 4301), (17, 5),
+                                 (32768, 9000), (40000, 12001)])
 def test_select_top_bits(C, n, rng):
     ops = _ops()
     s = (rng.integers(0, 50, size=C) / 8.0).astype(np.float32)     # heavy ties

@@ -89,7 +89,10 @@ def _full_size_checks(compact_ctx):
     idx = _selection(cfg, inp)
     assert np.array_equal(host_i(blk.idx), idx)
     ctx, out = ref.token_lists(inp["roles"])
-    R = sample_rows(ctx, out, 40)
+    # sampled rows plus every row of whole 256-row M-tiles of the products:
+    # the first and last tiles of the context-row products (the last ones
+    # run as split-tail tiles) and the last tile of the output-row products
+    R = np.unique(np.concatenate([sample_rows(ctx, out, 40), ctx[:256], ctx[-256:], out[-256:]]))
     rr = inp["roles"][R]
     x = inp["x"]
     g_d, u_d = host(blk.gu[:, :F]), host(blk.gu[:, F:])

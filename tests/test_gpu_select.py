@@ -218,3 +218,30 @@ def test_full_rank_estimator_bit_exact_and_matches_exact_criterion():
     assert np.allclose(got, s64, rtol=1e-3, atol=0)
     if _margin_ok(s64, n, 1e-3):
         assert np.array_equal(host_i(idx), _top_set(s64, n))
+
+
+def test_r64_rounding_order_golden_on_gpu():
+    """The estimator's stage-1 reduction on the hand-derived R64 cases (fp32
+    x row = the a terms, W_A column = the b terms): the GPU gives exactly the
+    canonical value of each case."""
+    import json
+    import os
+    ops = _ops()
+    with open(os.path.join(os.path.dirname(__file__), "golden", "r64_order.json")) as f:
+        cases = json.load(f)["cases"]
+    print("[select] R64 rounding-order goldens", flush=True)
+    for case in cases:
+        L = case["L"]
+        a = np.zeros((1, L), np.float32)
+        b = np.zeros((L, 4), np.float32)      # four identical W_A columns
+        for m, av, bv in case["terms"]:
+            a[0, m], b[m, :] = av, bv
+        x = torch.zeros(1, (L + 3) // 4 * 4, dtype=torch.float32, device=DEV)
+        x[:, :L] = torch.from_numpy(a).to(DEV)
+        rows = torch.zeros(1, dtype=torch.int32, device=DEV)
+        xa = torch.empty(1, 4, dtype=torch.float32, device=DEV)
+        ops.svd_estimate(x[:, :L], rows, to_dev(b, "f32"), xa)
+        torch.cuda.synchronize()
+        got = host(xa)[0]
+        want = np.float32(case["r64"])
+        assert np.all(got.view(np.uint32) == want.view(np.uint32)), (case["name"], got, want)

@@ -116,5 +116,7 @@ def test_stack_full_size_sampled_layers():
     R = sample_rows(ctx, out, 16)
     for l in check:
         g, inp, sel = _layer_case(cfg, io, kept[l], stack, l, sps[l])
-        check_ops(cfg, inp, g, sel, R, [(l % cfg.batch, l % cfg.n_kv_heads)], tag=f"stack l{l}")
+        pairs = [(l % cfg.batch, l % cfg.n_kv_heads), ((l + 3) % cfg.batch, (l + 5) % cfg.n_kv_heads),
+                 ((l + 6) % cfg.batch, (l + 2) % cfg.n_kv_heads)]
+        check_ops(cfg, inp, g, sel, R, pairs, tag=f"stack l{l}")
         del g, inp

@@ -236,3 +236,27 @@ def test_scores_are_nonnegative(rng):
     WB = rng.standard_normal((4, 50)).astype(np.float32)
     for s in (csa.ssq_l2(xa, WB), csa.ssq_swiglu(xa, WB, WB)):
         assert np.all(s.view(np.uint32) < 0x80000000)
+
+
+def _r64_golden():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "r64_order.json")
+    with open(path) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _r64_golden(), ids=lambda c: c["name"][:30])
+def test_r64_rounding_order_golden(case):
+    """Hand-derived binary32 results that depend on the reduction's order, the
+    fused multiply-add and the tree's pairing: the oracle's R64 gives exactly
+    the canonical value, which differs from the other orders' values."""
+    L = case["L"]
+    a = np.zeros(L, np.float32)
+    b = np.zeros(L, np.float32)
+    for m, av, bv in case["terms"]:
+        a[m], b[m] = av, bv
+    got = csa.r64(a, b)
+    assert np.float32(got).view(np.uint32) == np.float32(case["r64"]).view(np.uint32)
+    others = [v for k, v in case.items() if k not in ("name", "terms", "L", "derivation", "r64")]
+    assert others and all(np.float32(v) != np.float32(case["r64"]) for v in others)
