@@ -700,24 +700,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_fixup_kernel(GemmArgs 
     const int wm = wid % WGM, wn = wid / WGM;
     f32x16 acc[FM][FN];
     const float* __restrict__ w0 = args.skws + (size_t)blockIdx.x * args.sks * BM * BN +
-                                   (size_t)wid * FM * FN * 16 * 64;
+                                   (size_t)wid * FM * FN * 16 * 64 + lane * 4;
+    // one partial at a time, all of its loads in flight together; each element
+    // is still summed in chunk order
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const float* w = w0 + ((i * FN + j) * 4 + g) * 256 + lane * 4;
-                float4 v = *(const float4*)w;
-                for (int c = 1; c < args.sks; ++c) {
-                    const float4 x = *(const float4*)(w + (size_t)c * BM * BN);
-                    v.x += x.x; v.y += x.y; v.z += x.z; v.w += x.w;
-                }
+                const float4 v = *(const float4*)(w0 + ((i * FN + j) * 4 + g) * 256);
                 acc[i][j][4 * g] = v.x;
                 acc[i][j][4 * g + 1] = v.y;
                 acc[i][j][4 * g + 2] = v.z;
                 acc[i][j][4 * g + 3] = v.w;
             }
+    for (int c = 1; c < args.sks; ++c) {
+        const float* __restrict__ wc = w0 + (size_t)c * BM * BN;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const float4 x = *(const float4*)(wc + ((i * FN + j) * 4 + g) * 256);
+                    acc[i][j][4 * g] += x.x;
+                    acc[i][j][4 * g + 1] += x.y;
+                    acc[i][j][4 * g + 2] += x.z;
+                    acc[i][j][4 * g + 3] += x.w;
+                }
+    }
     gemm_lora_term<FM, FN, WTM, WTN>(P, acc, m0, n0, wm, wn, lane);
     gemm_store_lds<FM, FN, WTM, WTN, WGM, WGN>(P, acc, m0, n0, wm, wn, lane, tid, (float*)smem);
 }
@@ -1205,7 +1217,11 @@ size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu, cons
 
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
                             size_t skws_floats, int ncu, const sl_tuning& tune) {
-    // tune.gemm_cfg selects a tile configuration by number (tuning sweeps)
+    // tune.gemm_cfg selects a tile configuration by number (tuning sweeps).
+    // The default (10, the eight-wave 256 x 256 kernel) was the fastest inside
+    // whole FFN and attention steps at T = 4096 on launches of every size; the
+    // smaller-tile and four-wave kernels win only on a product repeated with
+    // its weights still in the caches.
     int cfg = tune.gemm_cfg;
     const int grp = tune.gemm_grp;
     if (!nn && cfg >= 10 && nt_v3_ok(probs, nprob)) {

@@ -179,15 +179,11 @@ __global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ x
     const int lane = threadIdx.x & (WAVE - 1), w = threadIdx.x / WAVE;
     const int64_t m0 = (int64_t)blockIdx.x * S1T;
     const int64_t j0 = (int64_t)blockIdx.y * (4 * S1J) + w * S1J;
-    // rows past Tc read a valid row (the last one) and are zeroed after the load,
-    // so every load is unconditional and the loads of an iteration overlap
+    // rows past Tc read a valid row (the last one); their sums are never
+    // stored, so every load is unconditional and the loads of an iteration overlap
     int64_t rowoff[S1T];
-    bool tv[S1T];
 #pragma unroll
-    for (int t = 0; t < S1T; ++t) {
-        tv[t] = m0 + t < Tc;
-        rowoff[t] = (int64_t)rows[tv[t] ? m0 + t : Tc - 1] * ldx;
-    }
+    for (int t = 0; t < S1T; ++t) rowoff[t] = (int64_t)rows[m0 + t < Tc ? m0 + t : Tc - 1] * ldx;
     const bool wvec = (kt % 4 == 0) && (j0 + S1J <= kt) && (((uintptr_t)WA & 15) == 0);
     float acc[S1T][S1J];
 #pragma unroll
@@ -199,9 +195,7 @@ __global__ __launch_bounds__(256) void stage1b_kernel(const void* __restrict__ x
         float xs[S1T];
 #pragma unroll
         for (int t = 0; t < S1T; ++t) {
-            const float v = BF16 ? bf16_to_f32(((const bf16_t*)xv)[rowoff[t] + i])
-                                 : ((const float*)xv)[rowoff[t] + i];
-            xs[t] = tv[t] ? v : 0.0f;
+            xs[t] = BF16 ? bf16_to_f32(((const bf16_t*)xv)[rowoff[t] + i]) : ((const float*)xv)[rowoff[t] + i];
         }
         float wv[S1J];
         const float* wr = WA + i * kt + j0;
@@ -344,19 +338,30 @@ __global__ __launch_bounds__(256) void ssq16_chain_kernel(const float* __restric
         wg[j] = WB0[(int64_t)j * C + cc];
         wu[j] = CRIT == 1 ? WB1[(int64_t)j * C + cc] : 0.0f;
     }
-    float p = 0.0f;
-    for (int64_t m = l; m < Tc; m += 64) {
+    // the criterion values of four tokens of the chain are independent: they
+    // are formed together, then folded into the chain in token order
+    auto value = [&](int64_t m) -> float {
         const float* row = xa + m * ld;
         float g = 0.0f;
 #pragma unroll
         for (int j = 0; j < K; ++j) g = __builtin_fmaf(row[off0 + j], wg[j], g);
-        float v = g;
-        if (CRIT == 1) {
-            float u = 0.0f;
+        if (CRIT == 0) return g;
+        float u = 0.0f;
 #pragma unroll
-            for (int j = 0; j < K; ++j) u = __builtin_fmaf(row[off1 + j], wu[j], u);
-            v = silu_sl_nb(g) * u;
-        }
+        for (int j = 0; j < K; ++j) u = __builtin_fmaf(row[off1 + j], wu[j], u);
+        return silu_sl_nb(g) * u;
+    };
+    float p = 0.0f;
+    int64_t m = l;
+    for (; m + 192 < Tc; m += 256) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = value(m + 64 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) p = __builtin_fmaf(v[q], v[q], p);
+    }
+    for (; m < Tc; m += 64) {
+        const float v = value(m);
         p = __builtin_fmaf(v, v, p);
     }
     if (c < C) part[(int64_t)l * C + c] = p;

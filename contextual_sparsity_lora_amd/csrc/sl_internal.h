@@ -22,6 +22,7 @@ struct sl_tuning {
     int gemm_grp = 8;         // SL_GEMM_GRP: tile rows per group of the GEMM tile order
     int gemm_split = 1;       // SL_GEMM_SPLIT: split the last partial round into K-chunks
     int splitk_max = 4;       // SL_SPLITK_MAX: largest split-K of dense output rows
+    int splitk_min = 2;       // SL_SPLITK_MIN: smallest split-K taken (smaller: none)
     int lora_xl_split = -1;   // SL_LORA_XL_SPLIT: x A^T split-K form (-1: by row length)
     int swiglu_rows = 256;    // SL_SWIGLU_ROWS: rows per partial of the fused SwiGLU backward
 };

@@ -125,11 +125,13 @@ sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
  *                      stream synchronisation and return SL_ERR_INVALID unless
  *                      they are strictly ascending and in range (also set by
  *                      the environment variable SL_DEBUG=1 at sl_create).
- *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "lora_xl_split",
- *   "swiglu_rows"      launch tuning of the GEMM and LoRA kernels (tile
+ *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "splitk_min",
+ *   "lora_xl_split", "swiglu_rows"
+ *                      launch tuning of the GEMM and LoRA kernels (tile
  *                      configuration, tile-order group, split tail on/off,
- *                      largest split-K, x A^T split form, rows per partial of
- *                      the fused SwiGLU backward); read from the
+ *                      largest and smallest split-K of the dense output rows
+ *                      of an input-sparse product, x A^T split form, rows per
+ *                      partial of the fused SwiGLU backward); read from the
  *                      environment variables of the same names in upper case
  *                      with an SL_ prefix at sl_create.
  * Unknown names return SL_ERR_INVALID. */

@@ -38,11 +38,23 @@ CASES = [
 ]
 
 
+@pytest.fixture(params=[10, 11, 14, 33], ids=lambda c: f"gemm{c}")
+def gemm_cfg(request):
+    """Each tile configuration of the bf16 product on every case: 10 the
+    default (the eight-wave 256 x 256 kernel), 11 the same kernel named, 14
+    the 128 x 128 one, 33 the four-wave LDS-DMA kernel with split tails.  The
+    option is put back to 10 afterwards."""
+    ops = _ops()
+    ops.set_option(0, "gemm_cfg", request.param)
+    yield request.param
+    ops.set_option(0, "gemm_cfg", 10)
+
+
 @pytest.mark.parametrize("case", CASES)
-def test_sparse_linear_fwd_bwd(case, rng):
+def test_sparse_linear_fwd_bwd(case, gemm_cfg, rng):
     ops = _ops()
     dtype, B, S, O, Din, Dout, keep = case
-    print(f"[linear] {case}", flush=True)
+    print(f"[linear] {case} gemm_cfg={gemm_cfg}", flush=True)
     roles = _roles(B, S, O)
     T = B * S
     ctx, out, c_d, o_d = _lists(ops, roles)
@@ -247,13 +259,23 @@ def test_fused_lora_term_accumulates(r, Dout, rng):
     assert mar(host(y)[np.ix_(ctx, drop)], (y0 + lora)[np.ix_(ctx, drop)]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("cfg", [11, 33])
 @pytest.mark.parametrize("side", ["out", "in"])
-def test_split_tail_chunks(side, rng):
+def test_split_tail_chunks(side, cfg, rng):
     """A launch whose tiles do not fill the compute units runs its last partial
     round as K-chunks summed by a second launch (long K, few tiles): the result
     matches the oracle with the LoRA term, rows mapped, and two runs agree bit
-    for bit (the chunk sums have a fixed order)."""
+    for bit (the chunk sums have a fixed order).  Both 256 x 256 kernels that
+    split their tails are run."""
     ops = _ops()
+    ops.set_option(0, "gemm_cfg", cfg)
+    try:
+        _split_tail_case(ops, side, rng)
+    finally:
+        ops.set_option(0, "gemm_cfg", 10)
+
+
+def _split_tail_case(ops, side, rng):
     roles = _roles(2, 320, 64)
     T, Din, Dout, r, s = 640, 3072, 1100, 16, 2.0
     ctx, out, c_d, o_d = _lists(ops, roles)
