@@ -422,16 +422,17 @@ __global__ __launch_bounds__(256) void lora_fill_rows_kernel(
 // compact row, since idx is ascending) overwrite their slots, and each row
 // leaves as 256 contiguous bytes.  Every element of the listed rows is written
 // exactly once, with 16-byte stores.
-template <int R>
+template <int R, int MTW>
 __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
     bf16_t* __restrict__ y, int64_t ldy, const int32_t* __restrict__ rows, int64_t nrows, int64_t C,
     const float* __restrict__ P, int64_t ldp, const bf16_t* __restrict__ B, int64_t ldb, int64_t r,
     float scale, const bf16_t* __restrict__ Yc, int64_t ldyc, const int32_t* __restrict__ idx, int64_t n) {
     constexpr int KS = (R + 31) / 32;     // 32-wide rank steps
     __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    static_assert(MTW == 16 || MTW == 32 || MTW == 64, "rows per wave");
+    const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t c0 = (int64_t)blockIdx.x * 128;
-    const int64_t t0 = ((int64_t)blockIdx.y * 4 + wid) * FTW;
+    const int64_t t0 = ((int64_t)blockIdx.y * 4 + wid) * MTW;
     const int kl = 8 * (lane >> 4);
     const bool lora = P != nullptr;
     const bool bvec = (ldb % 8 == 0) && (((uintptr_t)B & 15) == 0);
@@ -464,37 +465,59 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
     // holds entries j0 + lane and j0 + 64 + lane (slot in the block, or -1)
     int64_t j0, j1;
     wave_lower_bounds(idx, n, c0, c0 + 128, lane, j0, j1);
-    const int sl0 = j0 + lane < j1 ? (int)(idx[j0 + lane] - c0) : -1;
-    const int sl1 = j0 + 64 + lane < j1 ? (int)(idx[j0 + 64 + lane] - c0) : -1;
+    const bool has0 = j0 + lane < j1, has1 = j0 + 64 + lane < j1;
+    const int sl0 = has0 ? (int)(idx[j0 + lane] - c0) : -1;
+    const int sl1 = has1 ? (int)(idx[j0 + 64 + lane] - c0) : -1;
+    // Branch-free inner loop: every load reads an in-bounds address (rows past
+    // the list read the last listed row, lanes without a selected channel read
+    // the run's first compact value) and the values that must not count are
+    // never stored: tile rows past the list are not written out, and a lane
+    // without a selected channel puts its value in the tile's padding columns.
+    const bool any = j1 > j0, run64 = j1 - j0 > 64;      // wave-uniform
+    const int ds0 = has0 ? sl0 : 128 + (lane & 7), ds1 = has1 ? sl1 : 128 + (lane & 7);
+    const int64_t jc0 = has0 ? j0 + lane : j0, jc1 = has1 ? j0 + 64 + lane : j0;
+    const bool pfast = lora && pvec && r % 8 == 0;        // whole 8-rank runs of P
     const bool aligned = (ldy % 8 == 0) && (((uintptr_t)y & 15) == 0);
     const bool whole = aligned && c0 + 128 <= C;
-    for (int64_t tg = t0; tg < t0 + FTW && tg < nrows; tg += 16) {
+    // the wave's rows (list entries t0 .. t0 + MTW), read once: lane l holds
+    // entry t0 + l (clamped to the list); a 16-row step takes its rows by lane shuffle
+    const int32_t rowv = rows[t0 + (lane % MTW) < nrows ? t0 + (lane % MTW) : nrows - 1];
+    for (int64_t tg = t0; tg < t0 + MTW && tg < nrows; tg += 16) {
         const int64_t m = tg + (lane & 15);
         const bool mv = m < nrows;
-        const int64_t row = mv ? (int64_t)rows[m] : 0;
-        // the compact values of the 16 rows, loaded ahead of the rank-r products
-        bf16_t cv0[16], cv1[16];
+        const int64_t row = (int64_t)__shfl(rowv, (int)(tg - t0) + (lane & 15), 64);
+        // the rank-r operand's loads go out first, then the compact values of
+        // the 16 rows; both are in flight before the first is used
+        float pv[KS][8];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            const bool ok = tg + rr < nrows;
-            const bf16_t* yc = Yc + (tg + rr) * ldyc + j0;
-            cv0[rr] = (ok && sl0 >= 0) ? yc[lane] : (bf16_t)0;
-            cv1[rr] = (ok && sl1 >= 0) ? yc[64 + lane] : (bf16_t)0;
+        for (int ks = 0; ks < KS; ++ks) {
+            const int k = 32 * ks + kl;
+            if (pfast) {
+                const bool kin = k < r;
+                const float* prow = P + row * ldp + (kin ? k : 0);
+                const float4 v0 = *(const float4*)prow, v1 = *(const float4*)(prow + 4);
+                pv[ks][0] = v0.x; pv[ks][1] = v0.y; pv[ks][2] = v0.z; pv[ks][3] = v0.w;
+                pv[ks][4] = v1.x; pv[ks][5] = v1.y; pv[ks][6] = v1.z; pv[ks][7] = v1.w;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) pv[ks][q] = kin ? pv[ks][q] : 0.0f;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) pv[ks][q] = (lora && mv && k + q < r) ? P[row * ldp + k + q] : 0.0f;
+            }
+        }
+        bf16_t cv0[16], cv1[16];
+        if (any) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const bf16_t* yc = Yc + (tg + rr < nrows ? tg + rr : nrows - 1) * ldyc;
+                cv0[rr] = yc[jc0];
+                cv1[rr] = run64 ? yc[jc1] : (bf16_t)0;
+            }
         }
         bf16x8 pb[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int k = 32 * ks + kl;
-            float v[8];
-            if (lora && mv && pvec && k + 8 <= r) {
-                const float* prow = P + row * ldp;
-                const float4 v0 = *(const float4*)(prow + k), v1 = *(const float4*)(prow + k + 4);
-                v[0] = v0.x; v[1] = v0.y; v[2] = v0.z; v[3] = v0.w;
-                v[4] = v1.x; v[5] = v1.y; v[6] = v1.z; v[7] = v1.w;
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) v[q] = (lora && mv && k + q < r) ? P[row * ldp + k + q] : 0.0f;
-            }
+            const float* v = pv[ks];
             uint32_t w[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -522,10 +545,13 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
         // (this wave's own LDS rows: in-order LDS access within the wave)
         wave_lds_sync();
         // the selected channels from the compact rows
+        if (any) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            if (sl0 >= 0) tile[wid][rr][sl0] = cv0[rr];
-            if (sl1 >= 0) tile[wid][rr][sl1] = cv1[rr];
+            for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds0] = cv0[rr];
+        }
+        if (run64) {
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds1] = cv1[rr];
         }
         wave_lds_sync();
 #pragma unroll
@@ -1581,16 +1607,23 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
 hipError_t launch_lora_merge_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
                                   int64_t C, const float* P, int64_t ldp, const void* B,
                                   int64_t ldb, int64_t r, float scale, const void* Yc,
-                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st) {
+                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st,
+                                  int merge_rows) {
     if (nrows <= 0 || C <= 0) return hipSuccess;
     if (P && (r < 1 || r > 128)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)ceil_div(C, 128), (unsigned)ceil_div(nrows, 4 * FTW));
-#define MERGE(RR)                                                                                  \
-    hipLaunchKernelGGL((lora_merge_rows_kernel<RR>), grid, dim3(256), 0, st, (bf16_t*)y, ldy, rows, \
+    const int mtw = merge_rows == 16 || merge_rows == 32 ? merge_rows : 64;
+    const dim3 grid((unsigned)ceil_div(C, 128), (unsigned)ceil_div(nrows, 4 * mtw));
+#define MERGE(RR, TW)                                                                                  \
+    hipLaunchKernelGGL((lora_merge_rows_kernel<RR, TW>), grid, dim3(256), 0, st, (bf16_t*)y, ldy, rows, \
                        nrows, C, P, ldp, (const bf16_t*)B, ldb, P ? r : 0, scale, (const bf16_t*)Yc, ldyc, idx, n)
-    if (!P || r <= 32) MERGE(32);
-    else if (r <= 64) MERGE(64);
-    else MERGE(128);
+#define MERGE_R(TW)                    \
+    if (!P || r <= 32) MERGE(32, TW);  \
+    else if (r <= 64) MERGE(64, TW);   \
+    else MERGE(128, TW);
+    if (mtw == 16) { MERGE_R(16) }
+    else if (mtw == 32) { MERGE_R(32) }
+    else { MERGE_R(64) }
+#undef MERGE_R
 #undef MERGE
     return hipGetLastError();
 }

@@ -248,12 +248,14 @@ sl_status sl_create(sl_handle** out, int device) {
     h->tune.gemm_split = env_int("SL_GEMM_SPLIT", h->tune.gemm_split);
     h->tune.splitk_max = env_int("SL_SPLITK_MAX", h->tune.splitk_max);
     h->tune.splitk_min = env_int("SL_SPLITK_MIN", h->tune.splitk_min);
+    h->tune.merge_rows = env_int("SL_MERGE_ROWS", h->tune.merge_rows);
     h->tune.lora_xl_split = env_int("SL_LORA_XL_SPLIT", h->tune.lora_xl_split);
     h->tune.swiglu_rows = env_int("SL_SWIGLU_ROWS", h->tune.swiglu_rows);
     if (h->tune.swiglu_rows < 4 || h->tune.swiglu_rows % 4 != 0) h->tune.swiglu_rows = 256;
     if (h->tune.gemm_grp < 1 || h->tune.gemm_grp > 64) h->tune.gemm_grp = 8;
     if (h->tune.splitk_max < 1 || h->tune.splitk_max > 16) h->tune.splitk_max = 4;
     if (h->tune.splitk_min < 2 || h->tune.splitk_min > 16) h->tune.splitk_min = 2;
+    if (h->tune.merge_rows != 16 && h->tune.merge_rows != 32) h->tune.merge_rows = 64;
     h->debug = env_int("SL_DEBUG", 0) != 0;
     DeviceGuard g(device);
     hipDeviceProp_t prop;
@@ -316,6 +318,9 @@ sl_status sl_set_option(sl_handle* h, const char* name, int64_t value) {
     } else if (n == "splitk_min") {
         SL_REQUIRE(h, value >= 2 && value <= 16, "splitk_min must be in [2, 16]");
         h->tune.splitk_min = (int)value;
+    } else if (n == "merge_rows") {
+        SL_REQUIRE(h, value == 16 || value == 32 || value == 64, "merge_rows must be 16, 32 or 64");
+        h->tune.merge_rows = (int)value;
     }
     else if (n == "lora_xl_split") h->tune.lora_xl_split = (int)value;
     else if (n == "swiglu_rows") {
@@ -869,7 +874,8 @@ sl_status out_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int6
         }
         Timed tm(h, K_FILL, 2.0 * T_c * (C - n) * l.r, (double)T_c * (C + n) * 2);
         return hip_check(h, launch_lora_merge_rows(Z, ldz, ctx_rows, T_c, C, l.P, l.ldP, l.B, l.ldB, l.r, l.scale,
-                                                   yc, ldn, idx, n, h->stream), "lora_merge");
+                                                   yc, ldn, idx, n, h->stream, h->tune.merge_rows),
+                         "lora_merge");
     }
     p[np++] = problem(X, ldx, ctx_rows, Wc, ldw, idx, Z, ldz, ctx_rows, idx, T_c, n, Kdim, beta, l, T,
                       C);

@@ -23,6 +23,7 @@ struct sl_tuning {
     int gemm_split = 1;       // SL_GEMM_SPLIT: split the last partial round into K-chunks
     int splitk_max = 4;       // SL_SPLITK_MAX: largest split-K of dense output rows
     int splitk_min = 2;       // SL_SPLITK_MIN: smallest split-K taken (smaller: none)
+    int merge_rows = 64;      // SL_MERGE_ROWS: rows per wave of the compact-product merge (16, 32, 64)
     int lora_xl_split = -1;   // SL_LORA_XL_SPLIT: x A^T split-K form (-1: by row length)
     int swiglu_rows = 256;    // SL_SWIGLU_ROWS: rows per partial of the fused SwiGLU backward
 };
@@ -153,7 +154,8 @@ hipError_t launch_lora_fill_rows(void* y, int64_t ldy, const int32_t* rows, int6
 hipError_t launch_lora_merge_rows(void* y, int64_t ldy, const int32_t* rows, int64_t nrows,
                                   int64_t C, const float* P, int64_t ldp, const void* B,
                                   int64_t ldb, int64_t r, float scale, const void* Yc,
-                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st);
+                                  int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st,
+                                  int merge_rows = 64);
 // fp32 version (VALU), same semantics.
 hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
 

@@ -126,12 +126,13 @@ sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
  *                      they are strictly ascending and in range (also set by
  *                      the environment variable SL_DEBUG=1 at sl_create).
  *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "splitk_min",
- *   "lora_xl_split", "swiglu_rows"
+ *   "lora_xl_split", "swiglu_rows", "merge_rows"
  *                      launch tuning of the GEMM and LoRA kernels (tile
  *                      configuration, tile-order group, split tail on/off,
  *                      largest and smallest split-K of the dense output rows
  *                      of an input-sparse product, x A^T split form, rows per
- *                      partial of the fused SwiGLU backward); read from the
+ *                      partial of the fused SwiGLU backward, rows per wave of
+ *                      the merge of a compact product); read from the
  *                      environment variables of the same names in upper case
  *                      with an SL_ prefix at sl_create.
  * Unknown names return SL_ERR_INVALID. */
