@@ -187,14 +187,15 @@ class SparseAttnProj:
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_qkv, None, self.scale, self.xl_qkv)
             ev[1].record(self.side)
-            # the backward's transposed LoRA factors (off the main stream)
+            if overlap:
+                ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
+                                      self.qkv, lora=lora, flags=ops.ONLY_OUT_ROWS)
+            # the backward's transposed LoRA factors (after the product, which
+            # they would otherwise delay)
             ops.transpose(self.A_qkv, self.A_qkvT)
             ops.transpose(self.A_o, self.A_oT)
             ops.transpose(self.B_bd, self.B_bdT[:, :self.Cs])
             ops.transpose(self.B_o, self.B_oT[:, :self.D])
-            if overlap:
-                ops.sparse_linear_fwd("out", x, self.W_qkv, None, self.ctx_rows, self.out_rows, self.idx_qkv,
-                                      self.qkv, lora=lora, flags=ops.ONLY_OUT_ROWS)
         if not self.dense:
             self.select(estimated=True)
         # the weight slices need only the selection: built on the second stream

@@ -185,21 +185,26 @@ class SparseFFN:
         overlap = (self.overlap_out_rows and not self.dense
                    and self.criterion != "oracle")   # "oracle" scores in gu first
         self._ev[0].record(main)
+        if not self.dense and self.criterion == "svd":
+            # the estimator's first product goes out first, so the main stream
+            # has work while the host issues the side stream's calls
+            ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
         self.side.wait_event(self._ev[0])
         lora = (self.xl_gu, self.B_bd, 2 * r, self.scale)
         with torch.cuda.stream(self.side):
             ops.lora_fwd_bwd(ops.LORA_XL, x, self.A_gu, None, self.scale, self.xl_gu)
             self._ev[1].record(self.side)
-            # the backward's transposed LoRA factors (off the main stream)
+            if overlap:
+                ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
+                                      self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
+            # the backward's transposed LoRA factors (after the product, which
+            # they would otherwise delay)
             ops.transpose(self.A_down, self.A_dT)
             ops.transpose(self.A_gu, self.A_guT)
             ops.transpose(self.B_down, self.B_dnT[:, :self.D])
             ops.transpose(self.B_bd, self.B_bdT[:, :2 * F])
-            if overlap:
-                ops.sparse_linear_fwd("out", x, self.W_gu, None, self.ctx_rows, self.out_rows, self.idx2,
-                                      self.gu, lora=lora, flags=ops.ONLY_OUT_ROWS)
         if not self.dense:
-            self._select(x)
+            self._select(x, estimated=self.criterion == "svd")
         # the weight slices need only the selection: built on the second stream
         # while the main stream runs the context rows' gate|up product
         self._slices = overlap and self.ws_dn is not None
@@ -243,12 +248,14 @@ class SparseFFN:
                               x_slice=self.hc if compact else None)
         return self.y
 
-    def _select(self, x):
-        """The shared gate/up/down selection idx (and its stacked form idx2)."""
+    def _select(self, x, estimated=False):
+        """The shared gate/up/down selection idx (and its stacked form idx2);
+        estimated: the estimator's product xa is already computed."""
         F = self.F
         if self.criterion == "svd":
             # estimator on context tokens, SwiGLU-L2 criterion, top-n
-            ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
+            if not estimated:
+                ops.svd_estimate(x, self.ctx_rows, self.WA, self.xa)
             ops.score_select("swiglu", self.xa, self.WB_gate, self.WB_up, self.n, self.idx,
                              scores=self.scores, off0=0, off1=self.k)
         elif self.criterion == "oracle":
