@@ -67,8 +67,7 @@ SIGNATURES = {
     "sl_swiglu_fwd_ctx": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                 _i64, _f, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _vp, _i64]),
     "sl_swiglu_bwd_lora": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
-                                 _vp, _i64, _vp, _i64, _vp, _i64, _i64, _f, _vp, _vp, _vp, _vp, _i64, _vp, _i64,
-                                 _vp, _i64]),
+                                 _vp, _i64, _vp, _i64, _vp, _i64, _i64, _f, _vp, _vp, _vp]),
     "sl_svd_factors": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _i64, ctypes.c_uint64,
                              _vp, _vp]),
     "sl_token_ce": (_st, [_vp, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f, _vp, _i64, _vp]),

@@ -932,25 +932,14 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
 // so a row's 256 bytes leave as one run) and the rows of one chunk, 4 at a
 // time.  MFMA (e): A[m][k] = X[t0 + k][cw + 8 m + e], B[k][n] = Y[t0 + k][n];
 // D accumulates over the chunk; each chunk writes part[p][chunk][c][j].
-// Optionally (partg non-null) also the row sums over the channels of the
-// stored dg, du: G[t][j] = sum_c dg[t, c] Bg[j][c] and G[t][RW + j] = sum_c
-// du[t, c] Bu[j][c] (Bg, Bu rank-major [r, F]).  Each 16-row group passes
-// through the wave's LDS tiles to the matrix-core layout (lane l: row l % 16,
-// channels 32 s + 8 (l / 16) + e) for the bf16 matrix cores; the 4 waves'
-// sums meet in LDS in wave order and the block writes
-// partg[blockIdx.x][t][0 .. 2 RW) for its 512 channels.
 template <int NR>
 __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
     const bf16_t* __restrict__ dh, int64_t lddh, const bf16_t* __restrict__ g, int64_t ldg,
     const bf16_t* __restrict__ u, int64_t ldu, int64_t Tn, int64_t F, bf16_t* __restrict__ dg, int64_t lddg,
     bf16_t* __restrict__ du, int64_t lddu, const float* __restrict__ Y0, int64_t ldy0,
     const float* __restrict__ Y1, int64_t ldy1, const float* __restrict__ Y2, int64_t ldy2, int64_t r,
-    int64_t rows_per_chunk, float* __restrict__ part, const bf16_t* __restrict__ Bg, int64_t ldbg,
-    const bf16_t* __restrict__ Bu, int64_t ldbu, float* __restrict__ partg) {
+    int64_t rows_per_chunk, float* __restrict__ part) {
     constexpr int RW = 16 * NR;
-    __shared__ __attribute__((aligned(16))) bf16_t tgl[4][16][128 + 8];
-    __shared__ __attribute__((aligned(16))) bf16_t tul[4][16][128 + 8];
-    __shared__ float gred[4][16][2 * RW + 1];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int cg = lane & 15, rs = lane >> 4;
     const int64_t cw = (int64_t)blockIdx.x * 512 + (int64_t)wid * 128;
@@ -959,19 +948,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
     const int64_t tb = (int64_t)blockIdx.y * rows_per_chunk;
     const int64_t te = (Tn - tb) < rows_per_chunk ? Tn : tb + rows_per_chunk;
     const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
-    const bool fred = partg != nullptr;                 // block-uniform
-    const int rr = lane & 15, kq = lane >> 4;          // matrix-core layout of the row sums
-    // the wave's factor fragments: rank 16 k + rr, channels cw + 32 s + 8 kq + e
-    uint4 bgf[4][NR], buf[4][NR];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            const int64_t j = 16 * k + rr, cc = cw + 32 * s4 + 8 * kq;
-            const bool bv = fred && j < r && cc < F;
-            bgf[s4][k] = bv ? *(const uint4*)(Bg + j * ldbg + cc) : zero;
-            buf[s4][k] = bv ? *(const uint4*)(Bu + j * ldbu + cc) : zero;
-        }
     f32x4 acc[3][NR][8];
 #pragma unroll
     for (int p = 0; p < 3; ++p)
@@ -1030,11 +1006,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
                 *(uint4*)(dg + t * lddg + c) = va;
                 *(uint4*)(du + t * lddu + c) = vb;
             }
-            if (fred) {   // rows past the chunk or channels past F carry zeros
-                const int gr = (int)((tu + 4 * sl - tb) & 15) + rs;
-                *(uint4*)&tgl[wid][gr][8 * cg] = ok ? va : zero;
-                *(uint4*)&tul[wid][gr][8 * cg] = ok ? vb : zero;
-            }
             float hb[8], ab[8], bb[8];
             unpack_bf16x8(make_uint4(wh[0], wh[1], wh[2], wh[3]), hb);
             unpack_bf16x8(va, ab);
@@ -1047,46 +1018,6 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
                     acc[1][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[e], y1[sl][k], acc[1][k][e], 0, 0, 0);
                     acc[2][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(bb[e], y2[sl][k], acc[2][k][e], 0, 0, 0);
                 }
-        }
-        const int64_t done = tu + 4 * U - tb;              // rows of the chunk staged so far
-        if (fred && ((done & 15) == 0 || tu + 4 * U >= te)) {
-            // the 16-row group [g0, g0 + 16) is complete (or the chunk ends in it)
-            const int64_t g0 = tb + ((done - 1) & ~(int64_t)15);
-            wave_lds_sync();
-            // bf16 matrix cores (both operands are stored bf16 values, so the
-            // products are exact; fp32 accumulation): MFMA s4 takes A[m][k] =
-            // dg[row m][32 s4 + k], B[k][n] = Bg[n][same channel], lane l
-            // supplying row / rank l % 16 and channels 32 s4 + 8 (l / 16) + e
-            f32x4 sg[NR], su[NR];
-#pragma unroll
-            for (int k = 0; k < NR; ++k) sg[k] = su[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-                const bf16x8 xg = __builtin_bit_cast(bf16x8, *(const uint4*)&tgl[wid][rr][32 * s4 + 8 * kq]);
-                const bf16x8 xu = __builtin_bit_cast(bf16x8, *(const uint4*)&tul[wid][rr][32 * s4 + 8 * kq]);
-#pragma unroll
-                for (int k = 0; k < NR; ++k) {
-                    sg[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xg, __builtin_bit_cast(bf16x8, bgf[s4][k]), sg[k],
-                                                                    0, 0, 0);
-                    su[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xu, __builtin_bit_cast(bf16x8, buf[s4][k]), su[k],
-                                                                    0, 0, 0);
-                }
-            }
-            // lane holds D[4 kq + i][rr]: row g0 + 4 kq + i, rank 16 k + rr
-#pragma unroll
-            for (int k = 0; k < NR; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    gred[wid][4 * kq + i][16 * k + rr] = sg[k][i];
-                    gred[wid][4 * kq + i][RW + 16 * k + rr] = su[k][i];
-                }
-            __syncthreads();
-            for (int q = threadIdx.x; q < 16 * 2 * RW; q += 256) {
-                const int row = q / (2 * RW), j = q % (2 * RW);
-                const float v = ((gred[0][row][j] + gred[1][row][j]) + gred[2][row][j]) + gred[3][row][j];
-                if (g0 + row < te) partg[((int64_t)blockIdx.x * Tn + g0 + row) * (2 * RW) + j] = v;
-            }
-            __syncthreads();   // gred and the tiles are reused by the next group
         }
     }
     // lane holds D[4 (l / 16) + i][l % 16] of MFMA e: column cw + 8 (4 rs + i) + e, rank 16 k + cg
@@ -1872,31 +1803,25 @@ hipError_t launch_swiglu_fwd_lora(const void* g, int64_t ldg, const void* u, int
     return hipGetLastError();
 }
 
-size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk, bool row_sums) {
+size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk) {
     const int64_t RW = r <= 16 ? 16 : 32;
-    return (size_t)(3 * ceil_div(T, rows_per_chunk) * F * RW) +
-           (row_sums ? (size_t)(ceil_div(F, 512) * T * 2 * RW) : 0);
+    return (size_t)(3 * ceil_div(T, rows_per_chunk) * F * RW);
 }
 
 hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, int64_t ldg, const void* u,
                                   int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
                                   int64_t lddu, const float* Y0, int64_t ldy0, const float* Y1, int64_t ldy1,
                                   const float* Y2, int64_t ldy2, int64_t r, float scale, float* dA, float* dB1,
-                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st,
-                                  const void* Bg, int64_t ldbg, const void* Bu, int64_t ldbu, float* G, int64_t ldG) {
+                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st) {
     if (F <= 0) return hipSuccess;
     // T = 0: no partials; the sums below write zero gradients
     const int64_t nch = T > 0 ? ceil_div(T, rows_per_chunk) : 0;
-    const int64_t nbx = ceil_div(F, 512);
-    const dim3 grid((unsigned)nbx, (unsigned)nch);
+    const dim3 grid((unsigned)ceil_div(F, 512), (unsigned)nch);
     const int RW = r <= 16 ? 16 : 32;
-    const size_t pstride = (size_t)nch * F * RW;
-    float* partg = (G && T > 0) ? part + 3 * pstride : nullptr;
 #define SBL(NRR)                                                                                               \
     hipLaunchKernelGGL((swiglu_bwd_lora_kernel<NRR>), grid, dim3(256), 0, st, (const bf16_t*)dh, lddh,          \
                        (const bf16_t*)g, ldg, (const bf16_t*)u, ldu, T, F, (bf16_t*)dg, lddg, (bf16_t*)du, lddu, \
-                       Y0, ldy0, Y1, ldy1, Y2, ldy2, r, rows_per_chunk, part, (const bf16_t*)Bg, ldbg,         \
-                       (const bf16_t*)Bu, ldbu, partg)
+                       Y0, ldy0, Y1, ldy1, Y2, ldy2, r, rows_per_chunk, part)
     if (T <= 0) {
     } else if (r <= 16) {
         SBL(1);
@@ -1905,6 +1830,7 @@ hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, i
     }
 #undef SBL
     const dim3 rg((unsigned)ceil_div(F * r, 256));
+    const size_t pstride = (size_t)nch * F * RW;
     // dA [r, F] (row j, column c); dB [F, r]
     hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part, nch, F, RW, r, scale, dA, (int64_t)1, F,
                        (const int32_t*)nullptr);
@@ -1912,15 +1838,6 @@ hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, i
                        (int64_t)1, (const int32_t*)nullptr);
     hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + 2 * pstride, nch, F, RW, r, scale, dB2, r,
                        (int64_t)1, (const int32_t*)nullptr);
-    if (G && T > 0) {
-        // G [T, 2r]: the gate sums in columns [0, r), the up sums in [r, 2r)
-        const dim3 gg((unsigned)ceil_div(T * r, 256));
-        // (unscaled, as SL_LORA_GB: the scale enters where gB is used)
-        hipLaunchKernelGGL(chunk_sum_kernel, gg, dim3(256), 0, st, partg, nbx, T, 2 * RW, r, 1.0f, G, ldG,
-                           (int64_t)1, (const int32_t*)nullptr);
-        hipLaunchKernelGGL(chunk_sum_kernel, gg, dim3(256), 0, st, partg + RW, nbx, T, 2 * RW, r, 1.0f, G + r, ldG,
-                           (int64_t)1, (const int32_t*)nullptr);
-    }
     return hipGetLastError();
 }
 

@@ -1346,8 +1346,7 @@ sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t 
                              const void* u, int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
                              int64_t lddu, const float* gB, int64_t ldgB, const float* xl_g, int64_t ldxlg,
                              const float* xl_u, int64_t ldxlu, int64_t r, float scale, float* dA, float* dB_g,
-                             float* dB_u, const void* Bg_t, int64_t ld_bg, const void* Bu_t, int64_t ld_bu,
-                             float* gB_gu, int64_t ld_gBgu) {
+                             float* dB_u) {
     if (!h) return SL_ERR_INVALID;
     SL_REQUIRE(h, dt == SL_BF16 || dt == SL_F32, "bad dtype");
     if (dt != SL_BF16) return fail(h, SL_ERR_UNSUPPORTED, "the fused SwiGLU + LoRA pass is bf16 only");
@@ -1363,23 +1362,14 @@ sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t 
         SL_REQUIRE(h, gB && xl_g && xl_u && ldgB >= r && ldxlg >= r && ldxlu >= r,
                    "gB / xl_g / xl_u NULL or leading dimension < r");
     }
-    const bool row_sums = gB_gu != nullptr;
-    if (row_sums && T > 0) {
-        SL_REQUIRE(h, Bg_t && Bu_t && ld_gBgu >= 2 * r, "Bg_t / Bu_t NULL or ld_gBgu < 2 r");
-        SL_CHECK(check_matrix(h, Bg_t, ld_bg, F, dt, "Bg_t"));
-        SL_CHECK(check_matrix(h, Bu_t, ld_bu, F, dt, "Bu_t"));
-    }
     const int64_t rpc = h->tune.swiglu_rows;
     DeviceGuard gd(h->device);
-    // T = 0: no rows to read; the sums write zero gradients (and no row sums)
-    if (T > 0) SL_CHECK(ensure_ws(h, round_up(swiglu_bwd_lora_ws_floats(T, F, r, rpc, row_sums) * 4, 256)));
-    Timed tm(h, K_SWIGLU, (row_sums ? 5.0 : 3.0) * 2.0 * T * F * r,
-             5.0 * T * F * 2 + (row_sums ? 5.0 : 3.0) * 4 * T * r + (row_sums ? 5.0 : 3.0) * 4 * r * F);
+    // T = 0: no rows to read; the sums write zero gradients
+    if (T > 0) SL_CHECK(ensure_ws(h, round_up(swiglu_bwd_lora_ws_floats(T, F, r, rpc) * 4, 256)));
+    Timed tm(h, K_SWIGLU, 3.0 * 2.0 * T * F * r, 5.0 * T * F * 2 + 3.0 * 4 * T * r + 3.0 * 4 * r * F);
     return hip_check(h, launch_swiglu_bwd_lora(dh, lddh, g, ldg, u, ldu, T, F, dg, lddg, du, lddu, gB, ldgB, xl_g,
                                                ldxlg, xl_u, ldxlu, r, scale, dA, dB_g, dB_u, rpc,
-                                               T > 0 ? (float*)h->ws : nullptr, h->stream, Bg_t, ld_bg, Bu_t,
-                                               ld_bu, gB_gu, ld_gBgu),
-                     "swiglu_bwd_lora");
+                                               T > 0 ? (float*)h->ws : nullptr, h->stream), "swiglu_bwd_lora");
 }
 
 sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi, int64_t rows,

@@ -281,14 +281,12 @@ hipError_t launch_swiglu_fwd_ctx(void* gu, int64_t ldgu, const int32_t* rows, in
                                  const void* Yc, int64_t ldyc, const int32_t* idx, int64_t n, void* hc, int64_t ldhc,
                                  int64_t npad, const void* A, int64_t lda, int64_t r, float* xl, int64_t ldxl,
                                  void* hf, int64_t ldhf, float* part, hipStream_t st);
-size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk, bool row_sums);
+size_t swiglu_bwd_lora_ws_floats(int64_t T, int64_t F, int64_t r, int64_t rows_per_chunk);
 hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, int64_t ldg, const void* u,
                                   int64_t ldu, int64_t T, int64_t F, void* dg, int64_t lddg, void* du,
                                   int64_t lddu, const float* Y0, int64_t ldy0, const float* Y1, int64_t ldy1,
                                   const float* Y2, int64_t ldy2, int64_t r, float scale, float* dA, float* dB1,
-                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st,
-                                  const void* Bg = nullptr, int64_t ldbg = 0, const void* Bu = nullptr,
-                                  int64_t ldbu = 0, float* G = nullptr, int64_t ldG = 0);
+                                  float* dB2, int64_t rows_per_chunk, float* part, hipStream_t st);
 hipError_t launch_swiglu_bwd(bool bf16, const void* dh, int64_t lddh, const void* g, int64_t ldg,
                              const void* u, int64_t ldu, int64_t T, int64_t F, void* dg,
                              int64_t lddg, void* du, int64_t lddu, hipStream_t st);

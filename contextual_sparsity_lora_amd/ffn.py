@@ -99,9 +99,6 @@ class SparseFFN:
         # read the same tensors (h A_down^T forward; dA_down, dB_gate, dB_up
         # backward), so h, dh, g, u, dg and du are each read once
         self.fused_swiglu_lora = (self.dtype == torch.bfloat16 and self.r <= 32 and self.F % 8 == 0)
-        # with it, the SwiGLU backward also forms the gate|up gB (channel sums
-        # of dg, du through B_gate, B_up) instead of a later pass reading dg, du
-        self.fused_gB = True
         # compact_ctx (sparse bf16 forward): the context rows' gate|up product
         # stays compact and one pass forms their merged gate|up rows (kept for
         # the backward), the compact h the down product reads, and their
@@ -298,22 +295,15 @@ class SparseFFN:
                                  dA=self.dA_down, dB=self.dB_down, gB=self.gB_dn, D_in=F, r=r)
         g, u = self.gu[:, :F], self.gu[:, F:]
         dg, du = self.dgu[:, :F], self.dgu[:, F:]
-        fused_gB = fused and self.fused_gB
         if fused:
-            # (B_bdT holds B_gate^T in rows [0, r) x columns [0, F) and B_up^T in
-            # rows [r, 2r) x columns [F, 2F))
             ops.swiglu_bwd_lora(self.dh, g, u, dg, du, self.gB_dn, self.xl_gu[:, :r], self.xl_gu[:, r:], s,
-                                self.dA_down, self.dB_gate, self.dB_up,
-                                Bg_t=self.B_bdT[:r, :F] if fused_gB else None,
-                                Bu_t=self.B_bdT[r:2 * r, F:2 * F] if fused_gB else None,
-                                gB_gu=self.gB_gu if fused_gB else None)
+                                self.dA_down, self.dB_gate, self.dB_up)
         else:
             ops.swiglu_bwd(self.dh, g, u, dg, du)
-        if not fused_gB:
-            # gate|up: gB for both through the block-diagonal B (main stream)
-            ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_bdT, s, None, dy=self.dgu,
-                             gB=self.gB_gu, D_in=D, D_out=2 * F, r=2 * r)
-        # dA and the per-projection dB on the side stream, overlapping the dx product
+        # gate|up: gB for both through the block-diagonal B (main stream); dA
+        # and the per-projection dB on the side stream, overlapping the dx product
+        ops.lora_fwd_bwd(ops.LORA_GB | ops.LORA_BT, None, None, self.B_bdT, s, None, dy=self.dgu,
+                         gB=self.gB_gu, D_in=D, D_out=2 * F, r=2 * r)
         self._ev[1].record(main)
         ops.sparse_linear_bwd("out", self.dgu, self.W_gu, self.W_guT, self.ctx_rows, self.out_rows,
                               self.idx2, self.dx, lora=(self.gB_gu, self.A_guT, 2 * r, s),

@@ -405,22 +405,16 @@ def swiglu_fwd_ctx(Yc, ctx_rows, idx, lora, gu, hc, A, xl, h_rows=None):
     _check(h, st, "sl_swiglu_fwd_ctx")
 
 
-def swiglu_bwd_lora(dh, g, u, dg, du, gB, xl_g, xl_u, scale, dA, dB_g, dB_u, Bg_t=None, Bu_t=None,
-                    gB_gu=None):
+def swiglu_bwd_lora(dh, g, u, dg, du, gB, xl_g, xl_u, scale, dA, dB_g, dB_u):
     """dg, du as swiglu_bwd, with dA = scale gB^T h ([r, F]), dB_g = scale
-    dg^T xl_g and dB_u = scale du^T xl_u ([F, r]) from the same pass (bf16);
-    with gB_gu ([T, 2r] fp32) also [dg Bg_t^T | du Bu_t^T] (unscaled, as
-    LORA_GB's gB; Bg_t, Bu_t: the B factors transposed, [r, F] bf16)."""
+    dg^T xl_g and dB_u = scale du^T xl_u ([F, r]) from the same pass (bf16)."""
     h = handle(_dev(g))
     T, F = g.shape
     r = gB.shape[1]
-    rs = gB_gu is not None
     st = _lib.load().sl_swiglu_bwd_lora(h, _dt(g), _ptr(dh), _ld(dh), _ptr(g), _ld(g), _ptr(u), _ld(u), T, F,
                                         _ptr(dg), _ld(dg), _ptr(du), _ld(du), _ptr(gB), _ld(gB), _ptr(xl_g),
                                         _ld(xl_g), _ptr(xl_u), _ld(xl_u), r, float(scale), _ptr(dA), _ptr(dB_g),
-                                        _ptr(dB_u), _ptr(Bg_t) if rs else None, _ld(Bg_t) if rs else 0,
-                                        _ptr(Bu_t) if rs else None, _ld(Bu_t) if rs else 0,
-                                        _ptr(gB_gu) if rs else None, _ld(gB_gu) if rs else 0)
+                                        _ptr(dB_u))
     _check(h, st, "sl_swiglu_bwd_lora")
 
 

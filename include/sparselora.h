@@ -638,23 +638,13 @@ sl_status sl_swiglu_fwd_ctx(sl_handle* h, sl_dtype dt, const void* Yc, int64_t l
  * gate and up x A^T); dA fp32 [r, F], dB_g / dB_u fp32 [F, r] (contiguous,
  * out, the layouts of SL_LORA_DA / SL_LORA_DB).  bf16 only, F % 8 == 0,
  * 1 <= r <= 32; the token sums are fixed-order reductions over row chunks
- * (deterministic).
- * Optionally (gB_gu != NULL) also the gate and up projections' gB, the
- * channel sums of the stored dg, du through the LoRA B factors (the gate|up
- * counterpart of SL_LORA_GB, so the backward's dx product and dA reductions
- * have them without reading dg, du back):
- *   gB_gu[t, j]     = sum_c dg[t, c] Bg_t[j, c]   (j < r; unscaled, as
- *   gB_gu[t, r + j] = sum_c du[t, c] Bu_t[j, c]    SL_LORA_GB's gB)
- * Bg_t / Bu_t: B_gate^T / B_up^T, rank-major bf16 [r, ld >= F] with 16-byte
- * rows; gB_gu fp32 [T, ld_gBgu >= 2 r] (out).  The sums are per 512-channel
- * block in a fixed order, then over the blocks in ascending order. */
+ * (deterministic). */
 sl_status sl_swiglu_bwd_lora(sl_handle* h, sl_dtype dt, const void* dh, int64_t lddh,
                              const void* g, int64_t ldg, const void* u, int64_t ldu,
                              int64_t T, int64_t F, void* dg, int64_t lddg, void* du, int64_t lddu,
                              const float* gB, int64_t ldgB, const float* xl_g, int64_t ldxlg,
                              const float* xl_u, int64_t ldxlu, int64_t r, float scale,
-                             float* dA, float* dB_g, float* dB_u, const void* Bg_t, int64_t ld_bg,
-                             const void* Bu_t, int64_t ld_bu, float* gB_gu, int64_t ld_gBgu);
+                             float* dA, float* dB_g, float* dB_u);
 /* out[j, i] = in[i, j]; in [rows, ldi], out [cols, ldo] (dt). */
 sl_status sl_transpose(sl_handle* h, sl_dtype dt, const void* in, int64_t ldi,
                        int64_t rows, int64_t cols, void* out, int64_t ldo);

@@ -56,17 +56,6 @@ def test_swiglu_lora_fwd_bwd(T, F, r, rows, rng):
         dBu = torch.full((F, r), 7.0, dtype=torch.float32, device=DEV)
         ops.swiglu_bwd(dhd, gd, ud, dg1, du1)
         ops.swiglu_bwd_lora(dhd, gd, ud, dg2, du2, gBd, xld[:, :r], xld[:, r:], s, dA, dBg, dBu)
-        # the same pass forming the gate|up gB too (channel sums of the stored
-        # dg, du through B_gate^T, B_up^T): the other outputs do not change
-        Bg = round_dtype(rng.standard_normal((r, F)) * 0.1, "bf16")
-        Bu = round_dtype(rng.standard_normal((r, F)) * 0.1, "bf16")
-        dg3, du3 = empty_pad(T, F, "bf16"), empty_pad(T, F, "bf16")
-        dA3 = torch.full((r, F), 7.0, dtype=torch.float32, device=DEV)
-        dBg3 = torch.full((F, r), 7.0, dtype=torch.float32, device=DEV)
-        dBu3 = torch.full((F, r), 7.0, dtype=torch.float32, device=DEV)
-        G = torch.full((T, 2 * r), 7.0, dtype=torch.float32, device=DEV)
-        ops.swiglu_bwd_lora(dhd, gd, ud, dg3, du3, gBd, xld[:, :r], xld[:, r:], s, dA3, dBg3, dBu3,
-                            Bg_t=dev_pad(Bg, "bf16"), Bu_t=dev_pad(Bu, "bf16"), gB_gu=G)
         torch.cuda.synchronize()
     finally:
         ops.set_option(0, "swiglu_rows", 256)
@@ -79,12 +68,6 @@ def test_swiglu_lora_fwd_bwd(T, F, r, rows, rng):
     assert mar(host(dA), s * (gB.astype(f64).T @ hh.astype(f64))) <= 1e-5
     assert mar(host(dBg), s * (dgh.astype(f64).T @ xl_gu[:, :r].astype(f64))) <= 1e-5
     assert mar(host(dBu), s * (duh.astype(f64).T @ xl_gu[:, r:].astype(f64))) <= 1e-5
-    for a_, b_ in ((dg3, dg2), (du3, du2), (dA3, dA), (dBg3, dBg), (dBu3, dBu)):
-        assert np.array_equal(bits(host(a_)), bits(host(b_)))
-    Gh = host(G)
-    # unscaled, as the LoRA pass's gB (the scale enters where gB is used)
-    assert mar(Gh[:, :r], dgh.astype(f64) @ Bg.T.astype(f64)) <= 1e-5
-    assert mar(Gh[:, r:], duh.astype(f64) @ Bu.T.astype(f64)) <= 1e-5
 
 
 def test_swiglu_lora_bwd_no_rows():
