@@ -227,8 +227,9 @@ def other_configs(steps=3):
     from workloads.gen import make_ffn_inputs, roles_for
     dev = "cuda:0"
 
-    def timed(step, n):
-        step()
+    def timed(step, n, warm=3):
+        for _ in range(warm):
+            step()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -291,7 +292,7 @@ def other_configs(steps=3):
                 step = lambda: (blk.forward(x, roles, cfg.ctx_tokens), blk.backward(dy))
             # (the one-layer workloads take about a millisecond a step: 20 timed
             # steps keep launch jitter out; the 32-layer stack takes the given count)
-            ms[dense] = timed(step, steps if cid == 5 else max(steps, 20))
+            ms[dense] = timed(step, steps if cid == 5 else max(steps, 20), warm=1 if cid == 5 else 3)
             del blk, step
             torch.cuda.empty_cache()
         out[str(cid)] = {"workload": cfg.name, "tokens": T, "sparse_ms": round(ms[False], 3),
