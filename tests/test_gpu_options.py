@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from oracle import reference as ref
-from tests.gpu_util import TOL, dev_pad, empty_pad, host, mar, need_lib, to_dev
+from tests.gpu_util import TOL, bits, dev_pad, empty_pad, host, mar, need_lib, to_dev
 from workloads.gen import round_dtype
 
 pytestmark = pytest.mark.gpu
@@ -88,3 +88,45 @@ def test_fixed_workspace_refuses_growth(rng):
         for k in (0, 1):
             r, c, o, x, W, i, xd, Wd, y = dev[k]
             assert mar(host(y), ref.sparse_linear_fwd("out", x, W, r, i)) <= TOL["bf16"]
+
+
+def test_tuning_options_refuse_bad_values():
+    """The launch-tuning options validate their values; a refused value leaves
+    the handle's setting as it was."""
+    ops = _ops()
+    print("[options] tuning refusals", flush=True)
+    for name, bad in (("merge_rows", 48), ("merge_rows", 0), ("splitk_min", 1), ("splitk_min", 17),
+                      ("splitk_max", 0), ("swiglu_rows", 3)):
+        with pytest.raises(ops.SLError):
+            ops.set_option(0, name, bad)
+    with pytest.raises(ops.SLError):
+        ops.set_option(0, "no_such_option", 1)
+
+
+@pytest.mark.parametrize("rows", [16, 32, 64])
+def test_merge_rows_per_wave(rows, rng):
+    """Every rows-per-wave form of the compact-product merge (the context rows
+    of an output-side bf16 product with its rank-r term) matches the oracle,
+    over a ragged row count and channel blocks with and without selected
+    channels, and the three forms agree bit for bit."""
+    ops = _ops()
+    print(f"[options] merge_rows={rows}", flush=True)
+    T, T_c, Din, Dout, n, r, s = 301, 250, 136, 1000, 300, 16, 2.0
+    roles, c, o, x, W, idx = _problem(rng, T, T_c, Din, Dout, n)
+    idx = idx[idx < 600]                                  # the last channel blocks select nothing
+    P = rng.standard_normal((T, r)).astype(np.float32)
+    Bm = round_dtype(rng.standard_normal((Dout, r)) * 0.3, "bf16")
+    ys = []
+    for v in (rows, 64):
+        y = empty_pad(T, Dout, "bf16", fill=3.0)
+        ops.set_option(0, "merge_rows", v)
+        try:
+            ops.sparse_linear_fwd("out", dev_pad(x, "bf16"), dev_pad(W, "bf16"), None, c, o, to_dev(idx, None), y,
+                                  lora=(to_dev(P, "f32"), dev_pad(Bm, "bf16"), r, s))
+            torch.cuda.synchronize()
+        finally:
+            ops.set_option(0, "merge_rows", 64)
+        ys.append(host(y))
+    want = ref.sparse_linear_fwd("out", x, W, roles, idx) + s * (P.astype(np.float64) @ Bm.T)
+    assert mar(ys[0], want) <= TOL["bf16"]
+    assert np.array_equal(bits(ys[0]), bits(ys[1]))
