@@ -136,6 +136,29 @@ def time_steps(blk, x, roles, dy, T_c, steps, warmup, ops, record=False, only=No
     return start.elapsed_time(stop) / steps
 
 
+def step_distribution(blk, x, roles, dy, T_c, steps, ops):
+    """Per-step times (ms) of `steps` further steps, each bracketed by its own
+    events on the caller's stream (the block joins its second stream before
+    returning, so the end event follows all of the step's work)."""
+    import torch
+    ops.set_option(0, "workspace_fixed", 1)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in ev:
+        a.record()
+        blk.forward(x, roles, T_c)
+        blk.backward(dy)
+        b.record()
+    torch.cuda.synchronize()
+    ops.set_option(0, "workspace_fixed", 0)
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def percentiles(v):
+    import numpy as np
+    return [round(float(q), 4) for q in np.percentile(np.asarray(v), [10, 50, 90])]
+
+
 def training_schedule(inp, cfg, ops, steps, dense_frac=0.1, vocab=32000):
     """Whole training steps (block forward, LM-head logits of the output rows,
     cross-entropy, backward, AdamW on LoRA) over `steps` steps: once with the
@@ -378,6 +401,9 @@ def main():
     # dominant kernel: the class with the most time per step
     dom = max(per_class, key=lambda c: per_class[c]["ms_per_step"])
     ms = time_steps(blk, x, roles, dy, cfg.ctx_tokens, args.steps, 1, ops, record=True, only=dom)
+    # the spread of single steps (each between its own events), beside the
+    # bracketed mean that `value` is computed from
+    step_pct = percentiles(step_distribution(blk, x, roles, dy, cfg.ctx_tokens, args.steps, ops))
     print(f"[bench] sparse step {ms:.3f} ms (events around {dom} only)", file=sys.stderr, flush=True)
     dn, dms, dfl, dby = ops.timing_query(0, dom)
     if dom.startswith("gemm"):
@@ -443,6 +469,8 @@ def main():
         dblk, x, roles, dy = build_block(inp, cfg, dense=True, single_stream=args.single_stream)
         dms_step = time_steps(dblk, x, roles, dy, cfg.ctx_tokens, args.steps, args.warmup, ops)
         extra["dense_ms_per_step"] = round(dms_step, 4)
+        extra["dense_step_ms_p10_p50_p90"] = percentiles(
+            step_distribution(dblk, x, roles, dy, cfg.ctx_tokens, args.steps, ops))
         extra["speedup_vs_dense"] = round(dms_step / ms, 3)
         print(f"[bench] dense step {dms_step:.3f} ms", file=sys.stderr, flush=True)
         # gradient fidelity: cosine between the sparse and the dense block's
@@ -461,6 +489,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "step_ms_p10_p50_p90": step_pct,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
