@@ -19,9 +19,10 @@
 //
 // Optional rank-r term (the dense LoRA branch): before the single rounding of
 // C, lscale * lP[cm, :] . lB[cn, :] is accumulated into the same fp32
-// accumulators with v_mfma_f32_32x32x2_f32 (fp32 operands), cm / cn being the
-// mapped output row / channel.  A problem with K = 0 carries only this term
-// (the unselected channels of context rows).
+// accumulators on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16, with
+// lscale * lP rounded to bf16 as a bf16 LoRA product rounds its
+// down-projection), cm / cn being the mapped output row / channel.  A problem
+// with K = 0 carries only this term (the unselected channels of context rows).
 #include "sl_internal.h"
 
 namespace {
