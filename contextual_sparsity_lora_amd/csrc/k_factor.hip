@@ -110,22 +110,29 @@ __global__ void gram_final_kernel(const double* __restrict__ part, int nb, int p
     G[e] = s;
 }
 
-// Cholesky G = R^T R (R upper, fp64), one thread; a non-positive pivot is
-// floored at 1e-300 so the triangular solve stays finite.
-__global__ void chol_kernel(const double* __restrict__ G, int p, double* __restrict__ R) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    for (int i = 0; i < p * p; ++i) R[i] = 0.0;
+// Cholesky G = R^T R (R upper, fp64); a non-positive pivot is floored at
+// 1e-300 so the triangular solve stays finite.  One wave, R in LDS: column j's
+// entries below the diagonal are independent, so thread i forms R[j][i] with
+// the same sequential sum over l as a one-thread loop would (same values).
+__global__ __launch_bounds__(64) void chol_kernel(const double* __restrict__ G, int p, double* __restrict__ R) {
+    __shared__ double Rs[FK_PMAX * FK_PMAX];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < p * p; e += blockDim.x) Rs[e] = 0.0;
+    __syncthreads();
     for (int j = 0; j < p; ++j) {
         double d = G[j * p + j];
-        for (int l = 0; l < j; ++l) d -= R[l * p + j] * R[l * p + j];
+        for (int l = 0; l < j; ++l) d -= Rs[l * p + j] * Rs[l * p + j];
         d = d > 1e-300 ? sqrt(d) : 1e-150;
-        R[j * p + j] = d;
-        for (int i = j + 1; i < p; ++i) {
+        const int i = tid;
+        if (i == j) Rs[j * p + j] = d;
+        if (i > j && i < p) {
             double s = G[j * p + i];
-            for (int l = 0; l < j; ++l) s -= R[l * p + j] * R[l * p + i];
-            R[j * p + i] = s / d;
+            for (int l = 0; l < j; ++l) s -= Rs[l * p + j] * Rs[l * p + i];
+            Rs[j * p + i] = s / d;
         }
+        __syncthreads();
     }
+    for (int e = tid; e < p * p; e += blockDim.x) R[e] = Rs[e];
 }
 
 // Y[m, :] <- Y[m, :] R^-1 (row-wise forward substitution, fp64).
@@ -141,62 +148,78 @@ __global__ void trsm_rows_kernel(float* __restrict__ Y, int64_t M, int p, const 
     for (int j = 0; j < p; ++j) Y[m * p + j] = (float)x[j];
 }
 
-// Eigen-decomposition of the symmetric G (fp64) by cyclic Jacobi rotations,
-// one thread: Ub columns sorted by descending eigenvalue into lam.
-__global__ void jacobi_kernel(const double* __restrict__ G, int p, double* __restrict__ A,
-                              double* __restrict__ Vm, double* __restrict__ Ub, double* __restrict__ lam) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    for (int i = 0; i < p * p; ++i) {
-        A[i] = G[i];
-        Vm[i] = (i / p == i % p) ? 1.0 : 0.0;
+// Eigen-decomposition of the symmetric G (fp64) by cyclic Jacobi rotations:
+// Ub columns sorted by descending eigenvalue into lam.  One wave with A and V
+// in LDS: the rotations run in the cyclic order, and within a rotation the
+// column update (rows l of columns i, j), then the row update (rows i, j) and
+// V's columns are each independent over l, so thread l applies them to its
+// entries with the same arithmetic as a one-thread loop (same values); the
+// convergence sums stay sequential on thread 0.
+__global__ __launch_bounds__(64) void jacobi_kernel(const double* __restrict__ G, int p, double* __restrict__ Ub,
+                                                    double* __restrict__ lam) {
+    __shared__ double As[FK_PMAX * FK_PMAX];
+    __shared__ double Vs[FK_PMAX * FK_PMAX];
+    __shared__ int s_done;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < p * p; e += blockDim.x) {
+        As[e] = G[e];
+        Vs[e] = (e / p == e % p) ? 1.0 : 0.0;
     }
+    __syncthreads();
     for (int sweep = 0; sweep < 60; ++sweep) {
-        double off = 0.0, tot = 0.0;
-        for (int i = 0; i < p; ++i)
-            for (int j = 0; j < p; ++j) {
-                const double a = A[i * p + j] * A[i * p + j];
-                tot += a;
-                if (i != j) off += a;
-            }
-        if (off <= 1e-30 * tot) break;
+        if (tid == 0) {
+            double off = 0.0, tot = 0.0;
+            for (int i = 0; i < p; ++i)
+                for (int j = 0; j < p; ++j) {
+                    const double a = As[i * p + j] * As[i * p + j];
+                    tot += a;
+                    if (i != j) off += a;
+                }
+            s_done = off <= 1e-30 * tot;
+        }
+        __syncthreads();
+        if (s_done) break;
         for (int i = 0; i < p - 1; ++i)
             for (int j = i + 1; j < p; ++j) {
-                const double aij = A[i * p + j];
-                if (aij == 0.0) continue;
-                const double th = (A[j * p + j] - A[i * p + i]) / (2.0 * aij);
+                const double aij = As[i * p + j];
+                if (aij == 0.0) continue;             // (the same value in every thread)
+                const double th = (As[j * p + j] - As[i * p + i]) / (2.0 * aij);
                 const double t = (th >= 0.0 ? 1.0 : -1.0) / (fabs(th) + sqrt(th * th + 1.0));
                 const double c = 1.0 / sqrt(t * t + 1.0), s = t * c;
-                for (int l = 0; l < p; ++l) {          // A <- J^T A J
-                    const double ali = A[l * p + i], alj = A[l * p + j];
-                    A[l * p + i] = c * ali - s * alj;
-                    A[l * p + j] = s * ali + c * alj;
+                __syncthreads();                       // every thread has read the pivot entries
+                const int l = tid;
+                if (l < p) {                           // A <- J^T A J: columns i, j
+                    const double ali = As[l * p + i], alj = As[l * p + j];
+                    As[l * p + i] = c * ali - s * alj;
+                    As[l * p + j] = s * ali + c * alj;
                 }
-                for (int l = 0; l < p; ++l) {
-                    const double ail = A[i * p + l], ajl = A[j * p + l];
-                    A[i * p + l] = c * ail - s * ajl;
-                    A[j * p + l] = s * ail + c * ajl;
+                __syncthreads();
+                if (l < p) {                           // rows i, j; V <- V J
+                    const double ail = As[i * p + l], ajl = As[j * p + l];
+                    As[i * p + l] = c * ail - s * ajl;
+                    As[j * p + l] = s * ail + c * ajl;
+                    const double vli = Vs[l * p + i], vlj = Vs[l * p + j];
+                    Vs[l * p + i] = c * vli - s * vlj;
+                    Vs[l * p + j] = s * vli + c * vlj;
                 }
-                for (int l = 0; l < p; ++l) {          // V <- V J
-                    const double vli = Vm[l * p + i], vlj = Vm[l * p + j];
-                    Vm[l * p + i] = c * vli - s * vlj;
-                    Vm[l * p + j] = s * vli + c * vlj;
-                }
+                __syncthreads();
             }
     }
+    if (tid != 0) return;
     // selection sort by descending eigenvalue (ties: lower index first)
     int order[FK_PMAX];
     for (int i = 0; i < p; ++i) order[i] = i;
     for (int i = 0; i < p; ++i) {
         int b = i;
         for (int j = i + 1; j < p; ++j)
-            if (A[order[j] * p + order[j]] > A[order[b] * p + order[b]]) b = j;
+            if (As[order[j] * p + order[j]] > As[order[b] * p + order[b]]) b = j;
         const int t = order[i];
         order[i] = order[b];
         order[b] = t;
     }
     for (int j = 0; j < p; ++j) {
-        lam[j] = A[order[j] * p + order[j]];
-        for (int l = 0; l < p; ++l) Ub[l * p + j] = Vm[l * p + order[j]];
+        lam[j] = As[order[j] * p + order[j]];
+        for (int l = 0; l < p; ++l) Ub[l * p + j] = Vs[l * p + order[j]];
     }
 }
 
@@ -277,7 +300,7 @@ size_t svd_factors_ws_bytes(int64_t D_out, int64_t D_in, int p) {
     w.take(sizeof(float) * D_out * FK_PMAX);
     w.take(sizeof(float) * FK_PMAX);
     w.take(sizeof(double) * FK_NB * p * p);
-    for (int i = 0; i < 5; ++i) w.take(sizeof(double) * p * p);
+    for (int i = 0; i < 3; ++i) w.take(sizeof(double) * p * p);
     w.take(sizeof(double) * p);
     return w.off;
 }
@@ -296,8 +319,6 @@ hipError_t launch_svd_factors(bool bf16, const void* W, int64_t ldw, const void*
     double* part = (double*)w.take(sizeof(double) * nb * p * p);
     double* G = (double*)w.take(sizeof(double) * p * p);
     double* R = (double*)w.take(sizeof(double) * p * p);
-    double* A = (double*)w.take(sizeof(double) * p * p);
-    double* Vm = (double*)w.take(sizeof(double) * p * p);
     double* Ub = (double*)w.take(sizeof(double) * p * p);
     double* lam = (double*)w.take(sizeof(double) * p);
     hipError_t e = hipSuccess;
@@ -332,7 +353,7 @@ hipError_t launch_svd_factors(bool bf16, const void* W, int64_t ldw, const void*
     }
     skinny(W, ldw, D_out, D_in, Q, Z);               // Z = W^T Q = (Q^T W)^T
     gram(Z, D_out);                                  // G = Z^T Z
-    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(64), 0, st, G, p, A, Vm, Ub, lam);
+    hipLaunchKernelGGL(jacobi_kernel, dim3(1), dim3(64), 0, st, G, p, Ub, lam);
     hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((D_in + 255) / 256)), dim3(256), 0, st, Q, D_in, p, k, Ub, lam, 0, U);
     hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)((D_out + 255) / 256)), dim3(256), 0, st, Z, D_out, p, k, Ub, lam, 1, V);
     hipLaunchKernelGGL(sign_kernel, dim3((unsigned)k), dim3(256), 0, st, U, D_in, k, sgn);
