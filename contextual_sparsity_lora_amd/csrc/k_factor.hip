@@ -21,9 +21,9 @@
 
 namespace {
 
-constexpr int FK_ROWS = 16;   // rows of A per block in the skinny product
-constexpr int FK_KC = 64;     // K chunk staged in LDS
-constexpr int FK_PMAX = 64;   // max columns p
+constexpr int FK_KC = 32;       // K chunk staged in LDS by the skinny product
+constexpr int FK_PMAX = 64;     // max columns p
+constexpr int FK_BLOCKS = 1024; // blocks a skinny product aims for (row blocks x K splits)
 
 __device__ __forceinline__ float ldf(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float ldf(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
@@ -44,45 +44,73 @@ __global__ void omega_kernel(uint64_t seed, int64_t n, float* __restrict__ om) {
     om[e] = (float)(sqrt(-2.0 * log(u1)) * cos(6.283185307179586 * u2));
 }
 
-// C[M, p] = A[M, K] B[K, p]: A row-major (dt), B, C fp32 row-major (ld = p).
-// Block = 256 threads over FK_ROWS rows; thread t owns row t / 16 and columns
-// (t % 16) + 16 c; K in FK_KC chunks through LDS, sums in K order.
-template <typename T>
+// C[M, p] = A[M, K] B[K, p] over one K span: A row-major (dt), B fp32 row-major
+// (ld = p), out fp32 row-major (ld = p) at out + blockIdx.y * ostride.
+// p is padded to P (16, 32 or 64).  Block = 256 threads = RG row groups x CL
+// column lanes (CL = P / 4); thread (ty, tx) owns the 4 x 4 tile of rows
+// 4 ty .. 4 ty + 3 and columns 4 tx .. 4 tx + 3, so one block covers
+// RB = 4096 / P rows.  Block y sums K in [y kspan, (y + 1) kspan) through LDS in
+// FK_KC chunks: A transposed (a thread's 4 rows are one 16-byte read), B as is
+// (its 4 columns are one 16-byte read), 16 FMAs per pair of reads.
+template <typename T, int P>
 __global__ __launch_bounds__(256) void skinny_kernel(const T* __restrict__ A, int64_t lda, int64_t M,
                                                      int64_t K, const float* __restrict__ B, int p,
-                                                     float* __restrict__ C) {
-    __shared__ float as[FK_ROWS][FK_KC + 1];
-    __shared__ float bs[FK_KC][FK_PMAX];
+                                                     int64_t kspan, float* __restrict__ out, int64_t ostride) {
+    constexpr int CL = P / 4, RB = 4096 / P, AS = RB + 4;
+    __shared__ __align__(16) float at[FK_KC * AS];
+    __shared__ __align__(16) float bs[FK_KC * P];
     const int tid = threadIdx.x;
-    const int64_t m0 = (int64_t)blockIdx.x * FK_ROWS;
-    const int r = tid / 16, cl = tid % 16;
-    float acc[FK_PMAX / 16];
+    const int tx = tid % CL, ty = tid / CL;
+    const int64_t m0 = (int64_t)blockIdx.x * RB;
+    const int64_t kb = (int64_t)blockIdx.y * kspan;
+    const int64_t ke = kb + kspan < K ? kb + kspan : K;
+    float acc[4][4];
 #pragma unroll
-    for (int c = 0; c < FK_PMAX / 16; ++c) acc[c] = 0.0f;
-    for (int64_t k0 = 0; k0 < K; k0 += FK_KC) {
-        for (int q = tid; q < FK_ROWS * FK_KC; q += 256) {
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int64_t k0 = kb; k0 < ke; k0 += FK_KC) {
+        for (int q = tid; q < RB * FK_KC; q += 256) {
             const int rr = q / FK_KC, kk = q % FK_KC;
             const int64_t m = m0 + rr, k = k0 + kk;
-            as[rr][kk] = (m < M && k < K) ? ldf(A, m * lda + k) : 0.0f;
+            at[kk * AS + rr] = (m < M && k < ke) ? ldf(A, m * lda + k) : 0.0f;
         }
-        for (int q = tid; q < FK_KC * FK_PMAX; q += 256) {
-            const int kk = q / FK_PMAX, c = q % FK_PMAX;
+        for (int q = tid; q < FK_KC * P; q += 256) {
+            const int kk = q / P, c = q % P;
             const int64_t k = k0 + kk;
-            bs[kk][c] = (k < K && c < p) ? B[k * p + c] : 0.0f;
+            bs[q] = (k < ke && c < p) ? B[k * p + c] : 0.0f;
         }
         __syncthreads();
+#pragma unroll 8
         for (int kk = 0; kk < FK_KC; ++kk) {
-            const float a = as[r][kk];
+            const float4 av = *(const float4*)&at[kk * AS + 4 * ty];
+            const float4 bv = *(const float4*)&bs[kk * P + 4 * tx];
+            const float a4[4] = {av.x, av.y, av.z, av.w}, b4[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-            for (int c = 0; c < FK_PMAX / 16; ++c) acc[c] = fmaf(a, bs[kk][cl + 16 * c], acc[c]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a4[i], b4[j], acc[i][j]);
         }
         __syncthreads();
     }
-    const int64_t m = m0 + r;
-    if (m < M)
+    float* o = out + (int64_t)blockIdx.y * ostride;
 #pragma unroll
-        for (int c = 0; c < FK_PMAX / 16; ++c)
-            if (cl + 16 * c < p) C[m * p + cl + 16 * c] = acc[c];
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 4 * ty + i;
+        if (m < M)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (4 * tx + j < p) o[m * p + 4 * tx + j] = acc[i][j];
+    }
+}
+
+// C[e] = sum over s of part[s n + e], s in order (the K splits of one product).
+__global__ void skinny_sum_kernel(const float* __restrict__ part, int64_t n, int S, float* __restrict__ C) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= n) return;
+    float v = part[e];
+    for (int s = 1; s < S; ++s) v += part[(int64_t)s * n + e];
+    C[e] = v;
 }
 
 // Partial Gram matrices: block b sums rows [b R, (b+1) R) of Y [M, p] (fp64).
@@ -291,6 +319,35 @@ struct FactorWs {
 
 constexpr int FK_NB = 256;   // Gram partial blocks
 
+// Launch shape of one skinny product C[M, p] = A[M, K] B[K, p]: P = p padded to
+// 16, 32 or 64, RB = 4096 / P rows per block, and K cut into S spans of cps
+// chunks so that row blocks x S reaches about FK_BLOCKS; S > 1 sums the spans'
+// partial products (S M p floats of workspace) afterwards.
+struct SkinnyPlan {
+    int P;
+    int64_t rb, rowblocks, cps, S;
+};
+SkinnyPlan skinny_plan(int64_t M, int64_t K, int p) {
+    SkinnyPlan s;
+    s.P = p <= 16 ? 16 : (p <= 32 ? 32 : 64);
+    s.rb = 4096 / s.P;
+    s.rowblocks = (M + s.rb - 1) / s.rb;
+    const int64_t chunks = (K + FK_KC - 1) / FK_KC;
+    int64_t want = (FK_BLOCKS + s.rowblocks - 1) / s.rowblocks;
+    if (want > chunks) want = chunks;
+    if (want < 1) want = 1;
+    s.cps = (chunks + want - 1) / want;
+    if (s.cps < 1) s.cps = 1;
+    s.S = (chunks + s.cps - 1) / s.cps;
+    if (s.S < 1) s.S = 1;
+    return s;
+}
+int64_t skinny_part_floats(int64_t D_out, int64_t D_in, int p) {
+    const SkinnyPlan a = skinny_plan(D_in, D_out, p), b = skinny_plan(D_out, D_in, p);
+    const int64_t fa = a.S > 1 ? a.S * D_in * p : 0, fb = b.S > 1 ? b.S * D_out * p : 0;
+    return fa > fb ? fa : fb;
+}
+
 size_t svd_factors_ws_bytes(int64_t D_out, int64_t D_in, int p) {
     FactorWs w{nullptr};
     w.take(sizeof(float) * D_out * p);
@@ -302,6 +359,7 @@ size_t svd_factors_ws_bytes(int64_t D_out, int64_t D_in, int p) {
     w.take(sizeof(double) * FK_NB * p * p);
     for (int i = 0; i < 3; ++i) w.take(sizeof(double) * p * p);
     w.take(sizeof(double) * p);
+    w.take(sizeof(float) * skinny_part_floats(D_out, D_in, p));
     return w.off;
 }
 
@@ -321,14 +379,33 @@ hipError_t launch_svd_factors(bool bf16, const void* W, int64_t ldw, const void*
     double* R = (double*)w.take(sizeof(double) * p * p);
     double* Ub = (double*)w.take(sizeof(double) * p * p);
     double* lam = (double*)w.take(sizeof(double) * p);
+    float* spart = (float*)w.take(sizeof(float) * skinny_part_floats(D_out, D_in, p));
     hipError_t e = hipSuccess;
     // C[M, p] = A[M, K] B[K, p]
     auto skinny = [&](const void* Am, int64_t lda, int64_t M, int64_t K, const float* B, float* C) {
-        const dim3 grid((unsigned)((M + FK_ROWS - 1) / FK_ROWS));
-        if (bf16)
-            hipLaunchKernelGGL(skinny_kernel<bf16_t>, grid, dim3(256), 0, st, (const bf16_t*)Am, lda, M, K, B, p, C);
-        else
-            hipLaunchKernelGGL(skinny_kernel<float>, grid, dim3(256), 0, st, (const float*)Am, lda, M, K, B, p, C);
+        const SkinnyPlan pl = skinny_plan(M, K, p);
+        const dim3 grid((unsigned)pl.rowblocks, (unsigned)pl.S);
+        const int64_t kspan = pl.cps * FK_KC;
+        float* o = pl.S > 1 ? spart : C;
+        const int64_t os = M * p;
+#define SL_SKINNY(P_)                                                                                         \
+    if (bf16)                                                                                                 \
+        hipLaunchKernelGGL((skinny_kernel<bf16_t, P_>), grid, dim3(256), 0, st, (const bf16_t*)Am, lda, M, K, B, \
+                           p, kspan, o, os);                                                                  \
+    else                                                                                                      \
+        hipLaunchKernelGGL((skinny_kernel<float, P_>), grid, dim3(256), 0, st, (const float*)Am, lda, M, K, B,  \
+                           p, kspan, o, os);
+        if (pl.P == 16) {
+            SL_SKINNY(16)
+        } else if (pl.P == 32) {
+            SL_SKINNY(32)
+        } else {
+            SL_SKINNY(64)
+        }
+#undef SL_SKINNY
+        if (pl.S > 1)
+            hipLaunchKernelGGL(skinny_sum_kernel, dim3((unsigned)((os + 255) / 256)), dim3(256), 0, st, spart, os,
+                               (int)pl.S, C);
     };
     auto gram = [&](const float* X, int64_t M) {
         const int64_t rpb = (M + nb - 1) / nb;
