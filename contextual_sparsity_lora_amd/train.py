@@ -6,9 +6,9 @@ Pages ("SparseLoRA: Accelerating LLM Fine-Tuning with Contextual Sparsity"),
 paper-graph summary: "Step Sensitivity and Progressive Sparse Fine-Tuning"
 (dense for the first p <= 10 % of steps; the overall speedup is bounded by
 1 / (p + (1 - p) / s)); "Interaction with the learning rate schedule" (cosine
-schedule with a 4 % warm-up); "Putting It All Together" (loss on output token
-positions only, the standard autoregressive loss; only LoRA A and B are
-updated, with the frozen weights untouched).
+schedule with a 4 % warm-up); "Putting It All Together" (next-token
+cross-entropy taken over the output-token positions alone; the adapters' A
+and B are the only trained tensors, the base weights stay frozen).
 
 One step: block forward -> logits of the output rows through a frozen LM head
 W_head [V, D] -> softmax cross-entropy against the labels of those rows (mean
