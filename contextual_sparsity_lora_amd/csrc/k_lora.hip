@@ -955,35 +955,45 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
         for (int k = 0; k < NR; ++k)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[p][k][e] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    constexpr int U = 1;   // 4-row slabs per load batch (2 measured slower: the extra registers halve occupancy)
-    for (int64_t tu = tb; tu < te; tu += 4 * U) {
-        uint4 vd[U], vg[U], vu[U];
-        float y0[U][NR], y1[U][NR], y2[U][NR];
+    // one 4-row slab at a time, the next slab's loads in flight while this
+    // one is processed (its matrix-core work would otherwise sit between a
+    // wave's loads; two waves per SIMD do not cover that)
+    uint4 vd, vg, vu;
+    float y0[NR], y1[NR], y2[NR];
+    auto fetch = [&](int64_t tu) {
+        const int64_t t = tu + rs;
+        const bool tv = t < te;
+        const bool ok = cv && tv;
+        vd = ok ? *(const uint4*)(dh + t * lddh + c) : zero;
+        vg = ok ? *(const uint4*)(g + t * ldg + c) : zero;
+        vu = ok ? *(const uint4*)(u + t * ldu + c) : zero;
 #pragma unroll
-        for (int sl = 0; sl < U; ++sl) {
-            const int64_t t = tu + 4 * sl + rs;
-            const bool tv = t < te;
-            const bool ok = cv && tv;
-            vd[sl] = ok ? *(const uint4*)(dh + t * lddh + c) : zero;
-            vg[sl] = ok ? *(const uint4*)(g + t * ldg + c) : zero;
-            vu[sl] = ok ? *(const uint4*)(u + t * ldu + c) : zero;
-#pragma unroll
-            for (int k = 0; k < NR; ++k) {
-                const int64_t j = 16 * k + cg;
-                const bool yv = tv && j < r;
-                y0[sl][k] = yv ? Y0[t * ldy0 + j] : 0.0f;
-                y1[sl][k] = yv ? Y1[t * ldy1 + j] : 0.0f;
-                y2[sl][k] = yv ? Y2[t * ldy2 + j] : 0.0f;
-            }
+        for (int k = 0; k < NR; ++k) {
+            const int64_t j = 16 * k + cg;
+            const bool yv = tv && j < r;
+            y0[k] = yv ? Y0[t * ldy0 + j] : 0.0f;
+            y1[k] = yv ? Y1[t * ldy1 + j] : 0.0f;
+            y2[k] = yv ? Y2[t * ldy2 + j] : 0.0f;
         }
+    };
+    if (tb < te) fetch(tb);
+    for (int64_t tu = tb; tu < te; tu += 4) {
+        const uint4 cd = vd, cgv = vg, cu = vu;
+        float z0[NR], z1[NR], z2[NR];
 #pragma unroll
-        for (int sl = 0; sl < U; ++sl) {
-            const int64_t t = tu + 4 * sl + rs;
+        for (int k = 0; k < NR; ++k) {
+            z0[k] = y0[k];
+            z1[k] = y1[k];
+            z2[k] = y2[k];
+        }
+        if (tu + 4 < te) fetch(tu + 4);
+        {
+            const int64_t t = tu + rs;
             const bool ok = cv && t < te;
             float d[8], gf[8], uf[8];
-            unpack_bf16x8(vd[sl], d);
-            unpack_bf16x8(vg[sl], gf);
-            unpack_bf16x8(vu[sl], uf);
+            unpack_bf16x8(cd, d);
+            unpack_bf16x8(cgv, gf);
+            unpack_bf16x8(cu, uf);
             uint32_t wa[4], wb[4], wh[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1014,9 +1024,9 @@ __global__ __launch_bounds__(256) void swiglu_bwd_lora_kernel(
             for (int k = 0; k < NR; ++k)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    acc[0][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], y0[sl][k], acc[0][k][e], 0, 0, 0);
-                    acc[1][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[e], y1[sl][k], acc[1][k][e], 0, 0, 0);
-                    acc[2][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(bb[e], y2[sl][k], acc[2][k][e], 0, 0, 0);
+                    acc[0][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(hb[e], z0[k], acc[0][k][e], 0, 0, 0);
+                    acc[1][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(ab[e], z1[k], acc[1][k][e], 0, 0, 0);
+                    acc[2][k][e] = __builtin_amdgcn_mfma_f32_16x16x4f32(bb[e], z2[k], acc[2][k][e], 0, 0, 0);
                 }
         }
     }
