@@ -46,6 +46,10 @@ struct GemmArgs {
     int dp;
     int sks;
     float* skws;
+    // split-K sum run by blocks past the tail sums of the tail-sum launch
+    // (nred of them; 0: none)
+    SplitkRed red;
+    int nred;
 };
 
 // Tile order inside a problem: groups of `grp` tile rows, M fastest inside a
@@ -686,11 +690,47 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_kernel(GemmArgs args) 
 
 // Split tail, second launch: tile dp + blockIdx.x sums its sks partials in
 // chunk order (deterministic), then runs the same epilogue as a whole tile.
+// Blocks past the tail sums: Z[rows[m], n..n+7] = round(sum over s ascending
+// of part[s][m][n..n+7] (+ Z if beta)), each element formed exactly as
+// splitk_reduce_kernel forms it; 8 columns per thread, grid-strided.
+__device__ __forceinline__ void splitk_red_block(const SplitkRed& R, int b, int nb, int tid, int nth) {
+    const int64_t n8 = R.N / 8, items = R.M * n8;
+    for (int64_t i = (int64_t)b * nth + tid; i < items; i += (int64_t)nb * nth) {
+        const int64_t m = i / n8, q = (i - m * n8) * 8;
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        for (int64_t s = 0; s < R.S; ++s) {
+            const float* p = R.part + (s * R.M + m) * R.N + q;
+            const float4 a = *(const float4*)p, c = *(const float4*)(p + 4);
+            v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+            v[4] += c.x; v[5] += c.y; v[6] += c.z; v[7] += c.w;
+        }
+        bf16_t* d = (bf16_t*)R.Z + (R.rows ? (int64_t)R.rows[m] : m) * R.ldz + q;
+        if (R.beta) {
+            const uint4 o = *(const uint4*)d;
+            const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] += bf16_to_f32((bf16_t)((ow[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+        }
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            w[e] = (uint32_t)f32_to_bf16(v[2 * e]) | ((uint32_t)f32_to_bf16(v[2 * e + 1]) << 16);
+        *(uint4*)d = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+}
+
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt_fixup_kernel(GemmArgs args) {
     constexpr int WTM = BM / WGM, WTN = BN / WGN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     extern __shared__ __attribute__((aligned(16))) bf16_t smem[];
+    const int ntail = args.first[MAXP] - args.dp;
+    if ((int)blockIdx.x >= ntail) {   // (block-uniform)
+        splitk_red_block(args.red, (int)blockIdx.x - ntail, args.nred, (int)threadIdx.x, 64 * WGM * WGN);
+        return;
+    }
     const int L = args.dp + (int)blockIdx.x;
     GemmProblem P;
     int t, tiles_m;
@@ -1124,7 +1164,8 @@ int split_tail_plan(const GemmArgs& a, int ncu, int& dp) {
 
 template <int BM, int BN, int WGM, int WGN, int NSET>
 hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
-                         size_t skws_floats, int ncu, int grp) {
+                         size_t skws_floats, int ncu, int grp, const SplitkRed* red = nullptr,
+                         bool* red_done = nullptr) {
     GemmArgs a = make_args(probs, nprob, BM, BN, grp);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
@@ -1147,6 +1188,25 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, fl
     a.dp = dp;
     a.sks = sks;
     a.skws = skws;
+    // a split-K sum given by the caller rides in the tail-sum launch (its
+    // tail tiles leave compute units idle), when its layout allows
+    int nred = 0;
+    // (not when a tail tile belongs to a partial-output problem: its sum
+    // would write the partials the split-K sum reads)
+    bool tail_f32 = false;
+    for (int i = 0; i < a.nprob; ++i)
+        if (a.first[i + 1] > dp && a.p[i].f32out) tail_f32 = true;
+    if (sks && red && !tail_f32 && red->S > 0 && red->M > 0 && red->N > 0 && red->N % 8 == 0 &&
+        red->ldz % 8 == 0 && ((uintptr_t)red->Z & 15) == 0 && ((uintptr_t)red->part & 15) == 0) {
+        const int64_t items = red->M * (red->N / 8);
+        const int64_t want = ceil_div(items, (int64_t)(64 * WGM * WGN));
+        int64_t nb = ncu - (total - dp);
+        if (nb < 32) nb = 32;
+        nred = (int)(nb < want ? nb : want);
+        a.red = *red;
+    }
+    a.nred = nred;
+    if (red_done) *red_done = nred > 0;
     // whole tiles (complete rounds), then the tail's K-chunks, then their sums
     if (dp > 0)
         hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET, false>), dim3(dp), dim3(64 * WGM * WGN), lds,
@@ -1154,8 +1214,8 @@ hipError_t launch_nt_cfg(const GemmProblem* probs, int nprob, hipStream_t st, fl
     if (sks) {
         hipLaunchKernelGGL((gemm_nt_kernel<BM, BN, WGM, WGN, NSET, true>), dim3((total - dp) * sks),
                            dim3(64 * WGM * WGN), lds, st, a);
-        hipLaunchKernelGGL((gemm_nt_fixup_kernel<BM, BN, WGM, WGN>), dim3(total - dp), dim3(64 * WGM * WGN), lds,
-                           st, a);
+        hipLaunchKernelGGL((gemm_nt_fixup_kernel<BM, BN, WGM, WGN>), dim3(total - dp + nred), dim3(64 * WGM * WGN),
+                           lds, st, a);
     }
     return hipGetLastError();
 }
@@ -1217,7 +1277,9 @@ size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu, cons
 }
 
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
-                            size_t skws_floats, int ncu, const sl_tuning& tune) {
+                            size_t skws_floats, int ncu, const sl_tuning& tune, const SplitkRed* red,
+                            bool* red_done) {
+    if (red_done) *red_done = false;
     // tune.gemm_cfg selects a tile configuration by number (tuning sweeps).
     // The default (10, the eight-wave 256 x 256 kernel) was the fastest inside
     // whole FFN and attention steps at T = 4096 on launches of every size; the
@@ -1238,7 +1300,8 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
             case 33: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, grp, skws, skws_floats, ncu);
             case 22: return launch_nt5<2, 4, 64, 2>(probs, nprob, st, grp);
             case 23: return launch_nt5<2, 2, 64, 2>(probs, nprob, st, grp);
-            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu, grp);
+            default: return launch_nt_cfg<256, 256, 2, 4, 2>(probs, nprob, st, skws, skws_floats, ncu, grp, red,
+                                                             red_done);
         }
     }
     if (cfg >= 10) cfg = 2;

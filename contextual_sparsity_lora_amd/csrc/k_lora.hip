@@ -1062,6 +1062,25 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
     out[ao * soa + j * soj] = scale * s;
 }
 
+// The three ordered sums of the fused SwiGLU backward in one launch:
+// blockIdx.y = p sums partial set p (at part + p pstride) into out[p] with
+// strides soa[p], soj[p], exactly as chunk_sum_kernel does.
+struct ChunkSum3 {
+    float* out[3];
+    int64_t soa[3], soj[3];
+};
+__global__ __launch_bounds__(256) void chunk_sum3_kernel(const float* __restrict__ part, int64_t pstride, int64_t nch,
+                                                        int64_t Adim, int RW, int64_t r, float scale, ChunkSum3 o) {
+    const int p = (int)blockIdx.y;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= Adim * r) return;
+    const int64_t a = q / r, j = q % r;
+    const float* __restrict__ pp = part + p * pstride;
+    float s = 0.0f;
+    for (int64_t ch = 0; ch < nch; ++ch) s += pp[(ch * Adim + a) * RW + j];
+    o.out[p][a * o.soa[p] + j * o.soj[p]] = scale * s;
+}
+
 // ---------------------------------------------------------------- forward SwiGLU of context rows from their compact product
 // For the listed (context) rows t = rows[m] and every channel c < F:
 //   g = Yc[m, j]     if c = idx[j] (selected), else s P[t, :] . B[c, :]
@@ -1839,15 +1858,14 @@ hipError_t launch_swiglu_bwd_lora(const void* dh, int64_t lddh, const void* g, i
         SBL(2);
     }
 #undef SBL
-    const dim3 rg((unsigned)ceil_div(F * r, 256));
+    // dA [r, F] (row j, column c); dB [F, r]: the three ordered sums in one launch
     const size_t pstride = (size_t)nch * F * RW;
-    // dA [r, F] (row j, column c); dB [F, r]
-    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part, nch, F, RW, r, scale, dA, (int64_t)1, F,
-                       (const int32_t*)nullptr);
-    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + pstride, nch, F, RW, r, scale, dB1, r,
-                       (int64_t)1, (const int32_t*)nullptr);
-    hipLaunchKernelGGL(chunk_sum_kernel, rg, dim3(256), 0, st, part + 2 * pstride, nch, F, RW, r, scale, dB2, r,
-                       (int64_t)1, (const int32_t*)nullptr);
+    ChunkSum3 o;
+    o.out[0] = dA;  o.soa[0] = 1; o.soj[0] = F;
+    o.out[1] = dB1; o.soa[1] = r; o.soj[1] = 1;
+    o.out[2] = dB2; o.soa[2] = r; o.soj[2] = 1;
+    hipLaunchKernelGGL(chunk_sum3_kernel, dim3((unsigned)ceil_div(F * r, 256), 3), dim3(256), 0, st, part,
+                       (int64_t)pstride, nch, F, RW, r, scale, o);
     return hipGetLastError();
 }
 

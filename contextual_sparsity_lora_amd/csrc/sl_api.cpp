@@ -732,7 +732,9 @@ sl_status sl_qkv_index(sl_handle* h, const int32_t* idx_qk, int64_t n_qk, const 
 }
 
 // ---------------------------------------------------------------- a6/a7
-static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem* p, int np) {
+static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem* p, int np,
+                          const SplitkRed* red = nullptr, bool* red_done = nullptr) {
+    if (red_done) *red_done = false;
     float* skws = nullptr;
     size_t skf = 0;
     // tune.gemm_split = 0 turns the split tail off (tuning comparisons)
@@ -761,8 +763,9 @@ static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem*
     }
     Timed tm(h, dt == SL_BF16 ? (nn ? K_GEMM_NN : K_GEMM_NT) : K_GEMM_F32, gemm_flops(p, np),
              gemm_bytes(p, np, esize(dt)));
-    hipError_t e = dt == SL_BF16 ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu, h->tune)
-                                 : launch_gemm_f32(nn, p, np, h->stream);
+    hipError_t e = dt == SL_BF16
+                       ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu, h->tune, red, red_done)
+                       : launch_gemm_f32(nn, p, np, h->stream);
     return hip_check(h, e, "gemm");
 }
 
@@ -1002,8 +1005,12 @@ sl_status in_sparse(sl_handle* h, sl_dtype dt, const void* X, int64_t ldx, int64
     p[np++] = problem(xc, ldxc, nullptr, wsl, ldwsl, nullptr, Z, ldz, ctx_rows, nullptr, T_c, Nout,
                       n > 0 ? ldn : 0, beta, l, T_c, Nout);
     p[np - 1].k_alg = n;
-    SL_CHECK(run_gemm(h, dt, false, p, np));
-    if (S > 1) {
+    // the ordered sum of the output rows' K-split partials goes with the
+    // product's tail-sum launch when it has one, else it follows as its own
+    const SplitkRed red = {part, S, T_o, Nout, Z, ldz, out_rows, beta};
+    bool red_done = false;
+    SL_CHECK(run_gemm(h, dt, false, p, np, (S > 1 && dt == SL_BF16) ? &red : nullptr, &red_done));
+    if (S > 1 && !red_done) {
         Timed tm(h, K_REDUCE, (double)S * T_o * Nout, (double)(S * 4 + 2 * esize(dt)) * T_o * Nout);
         SL_HIP(h, launch_splitk_reduce(dt == SL_BF16, part, S, T_o, Nout, Z, ldz, out_rows, nullptr,
                                        beta, h->stream), "splitk_reduce");

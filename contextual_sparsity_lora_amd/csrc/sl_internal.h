@@ -132,12 +132,28 @@ struct GemmProblem {
     int64_t k_alg;             // contraction length counted as work (0: K; K may include zero padding)
     const int32_t* l_cols;     // rank-r column map (rows of lB) when C columns are stored unmapped
 };
+// Ordered sum of split-K partials of bf16 output rows:
+//   Z[rows[m], n] = round(sum over s ascending of part[s][m][n] (+ Z if beta))
+// (the arithmetic of launch_splitk_reduce).  A launch with a split tail runs it
+// in its tail-sum launch, next to the tail tiles' sums, on the compute units
+// those leave idle; it needs N % 8 == 0, ldz % 8 == 0 and a 16-byte aligned Z.
+struct SplitkRed {
+    const float* part;
+    int64_t S, M, N;
+    void* Z;
+    int64_t ldz;
+    const int32_t* rows;
+    int beta;
+};
 // bf16 inputs, fp32 accumulate, bf16 output.  nn = false: B is [N, K] ("NT");
 // nn = true: B is [K, N] ("NN").  Up to three problems in one launch.
 // skws: fp32 scratch for the split tail of the default NT configuration (the
-// partial round's tiles run as K-chunks); nullptr or too small: no split
+// partial round's tiles run as K-chunks); nullptr or too small: no split.
+// red (optional): a split-K sum the launch may take over (see SplitkRed);
+// *red_done says whether it did (else the caller launches it afterwards).
 hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStream_t st,
-                            float* skws, size_t skws_floats, int ncu, const sl_tuning& tune);
+                            float* skws, size_t skws_floats, int ncu, const sl_tuning& tune,
+                            const SplitkRed* red = nullptr, bool* red_done = nullptr);
 // floats of scratch the split tail of these problems wants (0: none)
 size_t gemm_split_tail_floats(const GemmProblem* probs, int nprob, int ncu, const sl_tuning& tune);
 // rank-r term only (K = 0 problem), bf16 output

@@ -130,3 +130,40 @@ def test_merge_rows_per_wave(rows, rng):
     want = ref.sparse_linear_fwd("out", x, W, roles, idx) + s * (P.astype(np.float64) @ Bm.T)
     assert mar(ys[0], want) <= TOL["bf16"]
     assert np.array_equal(bits(ys[0]), bits(ys[1]))
+
+
+def test_splitk_sum_in_tail_launch(rng):
+    """An input-side bf16 product whose output rows are split along K (C about
+    3n) and whose last partial round is split into K-chunks: the output rows'
+    ordered partial sum runs in the tail-sum launch.  With the split tail off
+    ("gemm_split" 0) the same sum runs as its own launch after whole tiles:
+    the output rows agree bit for bit (same partials, same order), and both
+    results match the oracle.  Sizes: 48 output-row partial tiles + 224
+    context tiles = 272 tiles, so the 16-tile tail lies in the context rows."""
+    ops = _ops()
+    print("[options] split-K sum in the tail launch", flush=True)
+    T_o, T_c, C, Dout, n = 256, 3584, 1600, 4096, 520
+    T = T_o + T_c
+    roles, c, o, x, W, _ = _problem(rng, T, T_c, C, Dout, n)
+    # an input-side product selects among its C input channels
+    idx = np.sort(rng.choice(C, n, replace=False)).astype(np.int32)
+    assert idx[0] >= 0 and idx[-1] < C and np.all(np.diff(idx) > 0)
+    xd, Wd = dev_pad(x, "bf16"), dev_pad(W, "bf16")
+    Wtd = dev_pad(np.ascontiguousarray(W.T), "bf16")
+    ys = []
+    for split in (1, 0):
+        y = empty_pad(T, Dout, "bf16", fill=3.0)
+        ops.set_option(0, "gemm_split", split)
+        ops.set_option(0, "debug", 1)      # index lists checked on the host before any launch
+        try:
+            ops.sparse_linear_fwd("in", xd, Wd, Wtd, c, o, to_dev(idx, None), y)
+            torch.cuda.synchronize()
+        finally:
+            ops.set_option(0, "gemm_split", 1)
+            ops.set_option(0, "debug", 0)
+        ys.append(host(y))
+    out = np.arange(T_c, T)
+    assert np.array_equal(bits(ys[0][out]), bits(ys[1][out]))
+    want = ref.sparse_linear_fwd("in", x, W, roles, idx)
+    for yv in ys:
+        assert mar(yv, want) <= TOL["bf16"]
