@@ -154,6 +154,28 @@ def step_distribution(blk, x, roles, dy, T_c, steps, ops):
     return [a.elapsed_time(b) for a, b in ev]
 
 
+def graph_step_ms(step, side, steps):
+    """Mean ms per step with the whole step (forward + backward, both streams)
+    replayed from a HIP graph (StepGraph: captured after eager warm-up steps
+    on its own stream); the host issues one replay per step."""
+    import torch
+    from contextual_sparsity_lora_amd.graph import StepGraph
+    g = StepGraph(step, side_streams=(side,))
+    try:
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    finally:
+        g.close()
+
+
 def percentiles(v):
     import numpy as np
     return [round(float(q), 4) for q in np.percentile(np.asarray(v), [10, 50, 90])]
@@ -266,7 +288,7 @@ def other_configs(steps=3):
     # config 1: the fp32 FFN block
     cfg = CONFIGS[1]
     inp = make_ffn_inputs(cfg)
-    ms = {}
+    ms, gms = {}, {}
     for dense in (False, True):
         import numpy as np
         from contextual_sparsity_lora_amd.ffn import SparseFFN
@@ -277,15 +299,19 @@ def other_configs(steps=3):
                         t["WB_gate"] if "WB_gate" in t else torch.from_numpy(inp["WB_gate"]).to(dev),
                         torch.from_numpy(inp["WB_up"]).to(dev), inp["scale"], sparsity=cfg.ffn_sparsity, dense=dense)
         roles = torch.from_numpy(inp["roles"]).to(dev)
-        ms[dense] = timed(lambda: (blk.forward(t["x"], roles, cfg.ctx_tokens), blk.backward(t["dy"])), 20)
+        step1 = lambda: (blk.forward(t["x"], roles, cfg.ctx_tokens), blk.backward(t["dy"]))
+        ms[dense] = timed(step1, 20)
+        gms[dense] = graph_step_ms(step1, blk.side, 20)
     out["1"] = {"workload": cfg.name, "tokens": cfg.tokens, "sparse_ms": round(ms[False], 4),
-                "dense_ms": round(ms[True], 4), "speedup": round(ms[True] / ms[False], 3)}
+                "dense_ms": round(ms[True], 4), "speedup": round(ms[True] / ms[False], 3),
+                "graph_sparse_ms": round(gms[False], 4), "graph_dense_ms": round(gms[True], 4),
+                "graph_speedup": round(gms[True] / gms[False], 3)}
     gen = torch.Generator(device=dev)
     for cid in (3, 4, 5):
         cfg = CONFIGS[cid]
         roles = torch.from_numpy(roles_for(cfg)).to(dev)
         T, D = cfg.tokens, cfg.hidden
-        ms = {}
+        ms, gms = {}, {}
         for dense in (False, True):
             gen.manual_seed(cfg.seed)
             x = (torch.randn(T, D, generator=gen, device=dev)).to(torch.bfloat16)
@@ -316,11 +342,16 @@ def other_configs(steps=3):
             # (the one-layer workloads take about a millisecond a step: 20 timed
             # steps keep launch jitter out; the 32-layer stack takes the given count)
             ms[dense] = timed(step, steps if cid == 5 else max(steps, 20), warm=1 if cid == 5 else 3)
+            if cid == 3:   # one block with one second stream: also replayed from a HIP graph
+                gms[dense] = graph_step_ms(step, blk.side, 20)
             del blk, step
             torch.cuda.empty_cache()
         out[str(cid)] = {"workload": cfg.name, "tokens": T, "sparse_ms": round(ms[False], 3),
                          "dense_ms": round(ms[True], 3), "speedup": round(ms[True] / ms[False], 3),
                          "sparse_tokens_per_s": round(T / (ms[False] * 1e-3), 1)}
+        if gms:
+            out[str(cid)].update({"graph_sparse_ms": round(gms[False], 3), "graph_dense_ms": round(gms[True], 3),
+                                  "graph_speedup": round(gms[True] / gms[False], 3)})
         print(f"[bench] config {cid} ({cfg.name}): sparse {ms[False]:.3f} ms, dense {ms[True]:.3f} ms",
               file=sys.stderr, flush=True)
     return out
@@ -459,6 +490,12 @@ def main():
              "selection_chain": selection,
              "selection_chain_note": "single-stream pass; gbs/hbm_frac against 8 TB/s, tflops/valu_frac "
                                      "against the 78.6 TF/s fp32 vector peak without packed fp32"}
+    graph = {}
+    if not args.single_stream:
+        graph["sparse_ms"] = round(graph_step_ms(lambda: (blk.forward(x, roles, cfg.ctx_tokens), blk.backward(dy)),
+                                                 blk.side, args.steps), 4)
+        print(f"[bench] sparse step replayed from a HIP graph {graph['sparse_ms']:.3f} ms", file=sys.stderr,
+              flush=True)
     if not args.no_dense:
         import types
         from contextual_sparsity_lora_amd import fidelity
@@ -473,6 +510,12 @@ def main():
             step_distribution(dblk, x, roles, dy, cfg.ctx_tokens, args.steps, ops))
         extra["speedup_vs_dense"] = round(dms_step / ms, 3)
         print(f"[bench] dense step {dms_step:.3f} ms", file=sys.stderr, flush=True)
+        if graph:
+            graph["dense_ms"] = round(graph_step_ms(
+                lambda: (dblk.forward(x, roles, cfg.ctx_tokens), dblk.backward(dy)), dblk.side, args.steps), 4)
+            graph["speedup"] = round(graph["dense_ms"] / graph["sparse_ms"], 3)
+            print(f"[bench] dense step replayed from a HIP graph {graph['dense_ms']:.3f} ms", file=sys.stderr,
+                  flush=True)
         # gradient fidelity: cosine between the sparse and the dense block's
         # LoRA gradients on the same synthetic inputs (random weights: a
         # measurement of the tool, not a result about the method)
@@ -481,6 +524,8 @@ def main():
         print(f"[bench] LoRA gradient cosines sparse vs dense: {extra['grad_fidelity']}",
               file=sys.stderr, flush=True)
         del dblk
+    if graph:
+        extra["graph_replay"] = graph
     out = {
         "metric": "sparse-LoRA linear fwd+bwd tokens/s and MFMA util at LLaMA3-8B FFN shape, 1 GPU",
         "value": round(T / (ms * 1e-3), 1),

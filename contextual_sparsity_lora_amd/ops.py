@@ -101,6 +101,13 @@ def fix_workspaces(device: int = 0):
     set_option(device, "workspace_fixed", 1)
 
 
+def set_stream_option(stream, name: str, value: int):
+    """sl_set_option on the one handle of a given stream (created if missing)."""
+    with torch.cuda.stream(stream):
+        h = handle(stream.device.index if stream.device.index is not None else 0)
+    _check(h, _lib.load().sl_set_option(h, name.encode(), int(value)), "sl_set_option")
+
+
 def workspace_bytes(device: int = 0) -> int:
     tot = 0
     for h in _device_handles(device):
