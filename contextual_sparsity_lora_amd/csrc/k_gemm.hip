@@ -1000,69 +1000,132 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_nt5_kernel(GemmArgs args)
 // ---------------------------------------------------------------- fp32 (VALU)
 constexpr int FB = 64, FK = 16;
 
+// Epilogue of the fp32 kernels for element (m, n) of problem P with product
+// value v: the rank-r term, then the store through the row / column maps (or
+// the raw value of a split-K partial problem).
+__device__ __forceinline__ void f32_store(const GemmProblem& P, int64_t m, int64_t n, float v) {
+    float* Cg = (float*)P.C;
+    const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
+    const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
+    if (P.lr > 0) {
+        const int64_t lm = P.l_rows ? (int64_t)P.l_rows[m] : cm;
+        const float* lP = P.lP + lm * P.ldlP;
+        const float* lB = (const float*)P.lB + cn * P.ldlB;
+        float l = 0.0f;
+        for (int k = 0; k < P.lr; ++k) l += lP[k] * lB[k];
+        v += P.lscale * l;
+    }
+    if (P.f32out) {
+        Cg[m * P.ldc + n] = v;
+        return;
+    }
+    float* dst = Cg + cm * P.ldc + cn;
+    *dst = v + (P.beta ? *dst : 0.0f);
+}
+
+// fp32 products on the vector unit: a 64 x 64 output tile per block of 256
+// threads (4 x 4 per thread), K in steps of 16 staged through LDS; the next
+// step's operands are loaded into registers while the current one is
+// multiplied, and the operand rows of the tile are looked up once.  A launch
+// with few tiles against the compute units splits K: with args.sks = S > 1,
+// block b runs K-chunk b mod S of tile b / S and stores its fp32 partial tile
+// to args.skws; gemm_f32_sum_kernel then adds the S chunks of each element in
+// chunk order and runs the epilogue (deterministic).
 template <bool NN>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
     __shared__ float As[FK][FB + 1];
     __shared__ float Bs[FK][FB + 1];
+    const int S = args.sks > 1 ? args.sks : 1;
+    const int L = (int)blockIdx.x / S, q = (int)blockIdx.x % S;
     GemmProblem P;
     int t, tiles_m;
-    pick_problem(args, blockIdx.x, P, t, tiles_m);
+    pick_problem(args, L, P, t, tiles_m);
     const int64_t m0 = (int64_t)(t % tiles_m) * FB, n0 = (int64_t)(t / tiles_m) * FB;
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
     const float* Ag = (const float*)P.A;
     const float* Bg = (const float*)P.B;
+    // load slots: element (kk, r) with kk = tid % 16 (the same for all four
+    // slots of a thread) and r = tid / 16 + 16 c
+    const int kk = tid & 15;
+    int64_t aoff[4], boff[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int64_t m = m0 + ty + 16 * c, n = n0 + ty + 16 * c;
+        aoff[c] = m < P.M ? (P.a_rows ? (int64_t)P.a_rows[m] : m) * P.lda : -1;
+        if (!NN) boff[c] = n < P.N ? (P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb : -1;
+        else boff[c] = n < P.N ? n : -1;
+    }
+    // K steps of this block
+    const int64_t nk_all = (P.K + FK - 1) / FK;
+    const int64_t kc = (nk_all + S - 1) / S;
+    const int64_t kb = (int64_t)q * kc;
+    const int64_t ke = nk_all < kb + kc ? nk_all : kb + kc;
+    float ra[4], rb[4];
+    auto load = [&](int64_t ks) {
+        const int64_t k = ks * FK + kk;
+        const bool kin = k < P.K;
+        int64_t bk = 0;
+        if (NN && kin) bk = (P.b_rows ? (int64_t)P.b_rows[k] : k) * P.ldb;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            ra[c] = (kin && aoff[c] >= 0) ? Ag[aoff[c] + k] : 0.0f;
+            if (!NN) rb[c] = (kin && boff[c] >= 0) ? Bg[boff[c] + k] : 0.0f;
+            else rb[c] = (kin && boff[c] >= 0) ? Bg[bk + boff[c]] : 0.0f;
+        }
+    };
     float acc[4][4] = {};
-    for (int64_t k0 = 0; k0 < P.K; k0 += FK) {
-        for (int q = threadIdx.x; q < FK * FB; q += 256) {
-            const int kk = q % FK, r = q / FK;
-            const int64_t m = m0 + r, k = k0 + kk;
-            float a = 0.0f;
-            if (m < P.M && k < P.K) a = Ag[(P.a_rows ? (int64_t)P.a_rows[m] : m) * P.lda + k];
-            As[kk][r] = a;
-            const int64_t n = n0 + r;
-            float b = 0.0f;
-            if (n < P.N && k < P.K) {
-                if (!NN) b = Bg[(P.b_rows ? (int64_t)P.b_rows[n] : n) * P.ldb + k];
-                else b = Bg[(P.b_rows ? (int64_t)P.b_rows[k] : k) * P.ldb + n];
-            }
-            Bs[kk][r] = b;
+    if (kb < ke) load(kb);
+    for (int64_t ks = kb; ks < ke; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            As[kk][ty + 16 * c] = ra[c];
+            Bs[kk][ty + 16 * c] = rb[c];
         }
         __syncthreads();
+        if (ks + 1 < ke) load(ks + 1);
 #pragma unroll
-        for (int kk = 0; kk < FK; ++kk)
+        for (int k2 = 0; k2 < FK; ++k2)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] += As[kk][ty * 4 + i] * Bs[kk][tx * 4 + j];
+                for (int j = 0; j < 4; ++j) acc[i][j] += As[k2][ty * 4 + i] * Bs[k2][tx * 4 + j];
         __syncthreads();
     }
-    float* Cg = (float*)P.C;
+    if (S > 1) {
+        float* w = args.skws + (size_t)blockIdx.x * FB * FB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(float4*)&w[(ty * 4 + i) * FB + tx * 4] = make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + ty * 4 + i;
         if (m >= P.M) continue;
-        const int64_t cm = P.c_rows ? (int64_t)P.c_rows[m] : m;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t n = n0 + tx * 4 + j;
-            if (n >= P.N) continue;
-            const int64_t cn = P.c_cols ? (int64_t)P.c_cols[n] : n;
-            float v = acc[i][j];
-            if (P.lr > 0) {
-                const int64_t lm = P.l_rows ? (int64_t)P.l_rows[m] : cm;
-                const float* lP = P.lP + lm * P.ldlP;
-                const float* lB = (const float*)P.lB + cn * P.ldlB;
-                float l = 0.0f;
-                for (int k = 0; k < P.lr; ++k) l += lP[k] * lB[k];
-                v += P.lscale * l;
-            }
-            if (P.f32out) {
-                Cg[m * P.ldc + n] = v;
-                continue;
-            }
-            float* dst = Cg + cm * P.ldc + cn;
-            *dst = v + (P.beta ? *dst : 0.0f);
+            if (n < P.N) f32_store(P, m, n, acc[i][j]);
         }
+    }
+}
+
+// Split-K sum of the fp32 kernel: block L adds the S partial tiles of tile L
+// in chunk order, then the epilogue.
+__global__ __launch_bounds__(256) void gemm_f32_sum_kernel(GemmArgs args) {
+    const int S = args.sks;
+    const int L = (int)blockIdx.x;
+    GemmProblem P;
+    int t, tiles_m;
+    pick_problem(args, L, P, t, tiles_m);
+    const int64_t m0 = (int64_t)(t % tiles_m) * FB, n0 = (int64_t)(t / tiles_m) * FB;
+    const float* w = args.skws + (size_t)L * S * FB * FB;
+    for (int e = threadIdx.x; e < FB * FB; e += 256) {
+        const int64_t m = m0 + e / FB, n = n0 + e % FB;
+        if (m >= P.M || n >= P.N) continue;
+        float v = w[e];
+        for (int c = 1; c < S; ++c) v += w[(size_t)c * FB * FB + e];
+        f32_store(P, m, n, v);
     }
 }
 
@@ -1319,12 +1382,44 @@ hipError_t launch_gemm_bf16(bool nn, const GemmProblem* probs, int nprob, hipStr
     }
 }
 
-hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st) {
+namespace {
+// K-chunks per tile of an fp32 launch: a launch of at most half a round of
+// tiles splits K so that its blocks fill about one round (at most 16 chunks,
+// each of at least 4 K steps of the longest problem); 1: no split.
+int f32_split_plan(const GemmArgs& a, int ncu) {
+    const int total = a.first[MAXP];
+    if (ncu <= 0 || total <= 0 || 2 * total > ncu) return 1;
+    int64_t nk = 0;
+    for (int i = 0; i < a.nprob; ++i)
+        if (a.first[i + 1] > a.first[i]) {
+            const int64_t k = (a.p[i].K + FK - 1) / FK;
+            nk = k > nk ? k : nk;
+        }
+    int S = ncu / total;
+    if (S > 16) S = 16;
+    while (S >= 2 && nk < 4 * S) --S;
+    return S >= 2 ? S : 1;
+}
+}  // namespace
+
+size_t gemm_f32_split_floats(const GemmProblem* probs, int nprob, int ncu) {
+    GemmArgs a = make_args(probs, nprob, FB, FB);
+    const int S = f32_split_plan(a, ncu);
+    return S > 1 ? (size_t)a.first[MAXP] * S * FB * FB : 0;
+}
+
+hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st, float* skws,
+                           size_t skws_floats, int ncu) {
     GemmArgs a = make_args(probs, nprob, FB, FB);
     const int total = a.first[MAXP];
     if (total == 0) return hipSuccess;
-    if (nn) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(total), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(total), dim3(256), 0, st, a);
+    int S = skws ? f32_split_plan(a, ncu) : 1;
+    if (S > 1 && (size_t)total * S * FB * FB > skws_floats) S = 1;
+    a.sks = S;
+    a.skws = skws;
+    if (nn) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(total * S), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(total * S), dim3(256), 0, st, a);
+    if (S > 1) hipLaunchKernelGGL(gemm_f32_sum_kernel, dim3(total), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

@@ -219,15 +219,35 @@ __global__ void lora_xl_reduce_kernel(const float* __restrict__ part, int64_t KS
     xl[t * ldxl + j] = s;
 }
 
-__global__ void lora_xl_f32_kernel(const float* __restrict__ x, int64_t ldx, int64_t T, int64_t D,
-                                   const float* __restrict__ A, int64_t lda, int64_t r,
-                                   float* __restrict__ xl, int64_t ldxl) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= T * r) return;
-    const int64_t t = q / r, j = q % r;
-    float s = 0.0f;
-    for (int64_t i = 0; i < D; ++i) s += x[t * ldx + i] * A[j * lda + i];
-    xl[t * ldxl + j] = s;
+// fp32: one wave per row t; lane l sums the columns i = l, l + 64, .. of 16
+// ranks at a time, then the 64 lane sums of each rank are combined by a fixed
+// butterfly (deterministic).
+__global__ __launch_bounds__(256) void lora_xl_f32_kernel(const float* __restrict__ x, int64_t ldx, int64_t T,
+                                                          int64_t D, const float* __restrict__ A, int64_t lda,
+                                                          int64_t r, float* __restrict__ xl, int64_t ldxl) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;   // (wave-uniform)
+    const float* xr = x + t * ldx;
+    for (int64_t j0 = 0; j0 < r; j0 += 16) {
+        float s[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) s[q] = 0.0f;
+        for (int64_t i = lane; i < D; i += 64) {
+            const float xv = xr[i];
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                if (j0 + q < r) s[q] += xv * A[(j0 + q) * lda + i];
+        }
+        float out = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) s[q] += __shfl_xor(s[q], o, 64);
+            if (lane == q) out = s[q];
+        }
+        if (lane < 16 && j0 + lane < r) xl[t * ldxl + j0 + lane] = out;
+    }
 }
 
 // ---------------------------------------------------------------- y += s P Bm^T
@@ -1538,7 +1558,7 @@ hipError_t launch_lora_xl(bool bf16, const void* x, int64_t ldx, int64_t T, int6
         hipLaunchKernelGGL(lora_xl_bf16_kernel, dim3((unsigned)ceil_div(T, 16)), dim3(XW * 64), 0, st,
                            (const bf16_t*)x, ldx, T, D, (const bf16_t*)A, lda, r, xl, ldxl);
     } else {
-        hipLaunchKernelGGL(lora_xl_f32_kernel, dim3((unsigned)ceil_div(T * r, 256)), dim3(256), 0,
+        hipLaunchKernelGGL(lora_xl_f32_kernel, dim3((unsigned)ceil_div(T, 4)), dim3(256), 0,
                            st, (const float*)x, ldx, T, D, (const float*)A, lda, r, xl, ldxl);
     }
     return hipGetLastError();

@@ -739,10 +739,12 @@ static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem*
     size_t skf = 0;
     // tune.gemm_split = 0 turns the split tail off (tuning comparisons)
     const bool split_on = h->tune.gemm_split != 0;
-    if (dt == SL_BF16 && !nn && split_on) {
-        // scratch for the split tail (partial tiles of the last, partial round);
-        // with a fixed workspace a launch it does not fit runs every tile whole
-        skf = gemm_split_tail_floats(p, np, h->num_cu, h->tune);
+    if ((dt == SL_BF16 && !nn && split_on) || (dt == SL_F32 && split_on)) {
+        // scratch for the split tail (bf16: partial tiles of the last, partial
+        // round) or the K split (fp32: launches with few tiles); with a fixed
+        // workspace a launch it does not fit runs every tile whole
+        skf = dt == SL_BF16 ? gemm_split_tail_floats(p, np, h->num_cu, h->tune)
+                            : gemm_f32_split_floats(p, np, h->num_cu);
         if (skf && skf * 4 > h->gws_bytes && !h->ws_fixed) {
             const size_t want = skf * 4 + (skf >> 1) + 4096;
             if (h->gws) {
@@ -765,7 +767,7 @@ static sl_status run_gemm(sl_handle* h, sl_dtype dt, bool nn, const GemmProblem*
              gemm_bytes(p, np, esize(dt)));
     hipError_t e = dt == SL_BF16
                        ? launch_gemm_bf16(nn, p, np, h->stream, skws, skf, h->num_cu, h->tune, red, red_done)
-                       : launch_gemm_f32(nn, p, np, h->stream);
+                       : launch_gemm_f32(nn, p, np, h->stream, skws, skf, h->num_cu);
     return hip_check(h, e, "gemm");
 }
 

@@ -173,7 +173,12 @@ hipError_t launch_lora_merge_rows(void* y, int64_t ldy, const int32_t* rows, int
                                   int64_t ldyc, const int32_t* idx, int64_t n, hipStream_t st,
                                   int merge_rows = 64);
 // fp32 version (VALU), same semantics.
-hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st);
+// fp32 products (vector unit).  skws: fp32 scratch for the K split of launches
+// with few tiles (nullptr or too small: no split); ncu: compute units.
+hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStream_t st,
+                           float* skws = nullptr, size_t skws_floats = 0, int ncu = 0);
+// floats of scratch the K split of these fp32 problems wants (0: none)
+size_t gemm_f32_split_floats(const GemmProblem* probs, int nprob, int ncu);
 
 hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int64_t Tc,
                               int32_t* out, int64_t To, int* flag, hipStream_t st);
