@@ -1110,23 +1110,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs args) {
     }
 }
 
-// Split-K sum of the fp32 kernel: block L adds the S partial tiles of tile L
-// in chunk order, then the epilogue.
+// Split-K sum of the fp32 kernel: 16 blocks per tile (block 16 L + g takes
+// elements 256 g .. 256 g + 255 of tile L, one per thread); a thread loads its
+// S (<= 16) partials together, adds them in chunk order, then the epilogue.
 __global__ __launch_bounds__(256) void gemm_f32_sum_kernel(GemmArgs args) {
     const int S = args.sks;
-    const int L = (int)blockIdx.x;
+    const int L = (int)blockIdx.x / 16;
+    const int e = ((int)blockIdx.x % 16) * 256 + (int)threadIdx.x;
     GemmProblem P;
     int t, tiles_m;
     pick_problem(args, L, P, t, tiles_m);
     const int64_t m0 = (int64_t)(t % tiles_m) * FB, n0 = (int64_t)(t / tiles_m) * FB;
-    const float* w = args.skws + (size_t)L * S * FB * FB;
-    for (int e = threadIdx.x; e < FB * FB; e += 256) {
-        const int64_t m = m0 + e / FB, n = n0 + e % FB;
-        if (m >= P.M || n >= P.N) continue;
-        float v = w[e];
-        for (int c = 1; c < S; ++c) v += w[(size_t)c * FB * FB + e];
-        f32_store(P, m, n, v);
-    }
+    const int64_t m = m0 + e / FB, n = n0 + e % FB;
+    if (m >= P.M || n >= P.N) return;
+    const float* w = args.skws + (size_t)L * S * FB * FB + e;
+    float p[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) p[c] = c < S ? w[(size_t)c * FB * FB] : 0.0f;
+    float v = p[0];
+#pragma unroll
+    for (int c = 1; c < 16; ++c)
+        if (c < S) v += p[c];
+    f32_store(P, m, n, v);
 }
 
 GemmArgs make_args(const GemmProblem* probs, int nprob, int bm, int bn, int grp = 8) {
@@ -1419,7 +1424,7 @@ hipError_t launch_gemm_f32(bool nn, const GemmProblem* probs, int nprob, hipStre
     a.skws = skws;
     if (nn) hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(total * S), dim3(256), 0, st, a);
     else hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(total * S), dim3(256), 0, st, a);
-    if (S > 1) hipLaunchKernelGGL(gemm_f32_sum_kernel, dim3(total), dim3(256), 0, st, a);
+    if (S > 1) hipLaunchKernelGGL(gemm_f32_sum_kernel, dim3(total * 16), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

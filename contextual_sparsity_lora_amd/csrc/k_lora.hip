@@ -220,8 +220,8 @@ __global__ void lora_xl_reduce_kernel(const float* __restrict__ part, int64_t KS
 }
 
 // fp32: one wave per row t; lane l sums the columns i = l, l + 64, .. of 16
-// ranks at a time, then the 64 lane sums of each rank are combined by a fixed
-// butterfly (deterministic).
+// ranks at a time (four columns' loads issued together), then the 64 lane
+// sums of each rank are combined by a fixed butterfly (deterministic).
 __global__ __launch_bounds__(256) void lora_xl_f32_kernel(const float* __restrict__ x, int64_t ldx, int64_t T,
                                                           int64_t D, const float* __restrict__ A, int64_t lda,
                                                           int64_t r, float* __restrict__ xl, int64_t ldxl) {
@@ -233,11 +233,20 @@ __global__ __launch_bounds__(256) void lora_xl_f32_kernel(const float* __restric
         float s[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) s[q] = 0.0f;
-        for (int64_t i = lane; i < D; i += 64) {
-            const float xv = xr[i];
+        for (int64_t i0 = lane; i0 < D; i0 += 256) {
+            float xv[4], av[4][16];
 #pragma unroll
-            for (int q = 0; q < 16; ++q)
-                if (j0 + q < r) s[q] += xv * A[(j0 + q) * lda + i];
+            for (int u = 0; u < 4; ++u) {
+                const int64_t i = i0 + 64 * u;
+                const bool iv = i < D;
+                xv[u] = iv ? xr[i] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 16; ++q) av[u][q] = (iv && j0 + q < r) ? A[(j0 + q) * lda + i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) s[q] += xv[u] * av[u][q];
         }
         float out = 0.0f;
 #pragma unroll
