@@ -264,21 +264,41 @@ __global__ __launch_bounds__(1024) void ssq16_kernel(const float* __restrict__ x
         wg[j] = WB0[(int64_t)j * C + cc];
         wu[j] = CRIT == 1 ? WB1[(int64_t)j * C + cc] : 0.0f;
     }
-    auto stage = [&](int buf, int64_t mb) {
-        for (int q = tid; q < 64 * NCOL; q += 1024) {
+    // staging of a 64-token chunk of xa: each thread's elements are loaded
+    // into registers (fetch) and written to LDS later (put), so the loads of
+    // chunk ch + 1 are in flight while chunk ch is scored
+    constexpr int NSL = (64 * NCOL + 1023) / 1024;
+    float sv[NSL];
+    auto fetch = [&](int64_t mb) {
+#pragma unroll
+        for (int s = 0; s < NSL; ++s) {
+            const int q = tid + 1024 * s;
             const int r = q / NCOL, k = q % NCOL;
             const int64_t m = mb + r;
             const int64_t col = k < K ? off0 + k : off1 + (k - K);
-            xs[buf][r][k] = m < Tc ? xa[m * ld + col] : 0.0f;
+            sv[s] = (q < 64 * NCOL && m < Tc) ? xa[m * ld + col] : 0.0f;
+        }
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int s = 0; s < NSL; ++s) {
+            const int q = tid + 1024 * s;
+            if (q < 64 * NCOL) xs[buf][q / NCOL][q % NCOL] = sv[s];
         }
     };
     float p[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int64_t nchunk = (Tc + 63) / 64;
-    if (nchunk > 0) stage(0, 0);
+    if (nchunk > 0) {
+        fetch(0);
+        put(0);
+    }
+    // the channel factors (loaded once above) are in registers before the
+    // loop, so no wait inside it is held for them
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
     __syncthreads();
     for (int64_t ch = 0; ch < nchunk; ++ch) {
         const int buf = (int)(ch & 1);
-        if (ch + 1 < nchunk) stage(buf ^ 1, (ch + 1) * 64);
+        if (ch + 1 < nchunk) fetch((ch + 1) * 64);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = 4 * w + q;
@@ -297,6 +317,7 @@ __global__ __launch_bounds__(1024) void ssq16_kernel(const float* __restrict__ x
             }
             p[q] = __builtin_fmaf(v, v, p[q]);
         }
+        if (ch + 1 < nchunk) put(buf ^ 1);
         __syncthreads();
     }
 #pragma unroll
