@@ -116,8 +116,9 @@ sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
 /* Handle options (integers):
  *   "workspace_fixed"  1: no call grows the workspace any more -- a call that
  *                      would need more returns SL_ERR_WORKSPACE before
- *                      launching, and a GEMM whose split tail does not fit the
- *                      scratch runs every tile whole.  For steady-state steps
+ *                      launching, and a GEMM whose split tail (bf16) or K
+ *                      split (fp32) does not fit the scratch runs every tile
+ *                      whole.  For steady-state steps
  *                      after a first step has sized the workspace: no
  *                      allocation, free or synchronisation happens in them.
  *   "debug"            1: before launching, calls that take index lists
@@ -128,7 +129,9 @@ sl_status sl_workspace_bytes(sl_handle* h, size_t* bytes);
  *   "gemm_cfg", "gemm_grp", "gemm_split", "splitk_max", "splitk_min",
  *   "lora_xl_split", "swiglu_rows", "merge_rows"
  *                      launch tuning of the GEMM and LoRA kernels (tile
- *                      configuration, tile-order group, split tail on/off,
+ *                      configuration, tile-order group, split tail of bf16
+ *                      launches and K split of fp32 launches with few tiles
+ *                      on/off,
  *                      largest and smallest split-K of the dense output rows
  *                      of an input-sparse product, x A^T split form, rows per
  *                      partial of the fused SwiGLU backward, rows per wave of
