@@ -1,5 +1,6 @@
 """GPU estimator factors (randomized subspace iteration) against the oracle's
-truncated SVD: a planted spectrum with a gap is recovered entry by entry, a
+truncated SVD: a planted spectrum with a gap is recovered entry by entry (up
+to the full LLaMA3-8B gate/up weight shape), a
 flat Gaussian spectrum is approximated within a few percent of the optimal
 rank-k error, and the estimator driven by the GPU factors selects exactly
 what the oracle selects with those factors."""
@@ -27,8 +28,11 @@ def _factors(W_lin, dtype, k, iters=3, oversample=16, seed=1):
     return host(WA_t), host(WB)
 
 
-@pytest.mark.parametrize("dtype,D_out,D_in", [("f32", 700, 256), ("bf16", 1400, 520), ("bf16", 520, 1400)])
+@pytest.mark.parametrize("dtype,D_out,D_in", [("f32", 700, 256), ("bf16", 1400, 520), ("bf16", 520, 1400),
+                                               ("bf16", 14336, 4096)])
 def test_planted_spectrum(dtype, D_out, D_in, rng):
+    """(the last case is a LLaMA3-8B gate or up weight at full size; the
+    oracle's exact SVD of it takes about half a minute on the host)"""
     k, n = 16, 48
     print(f"[factors] planted {dtype} {D_out}x{D_in}", flush=True)
     U0, _ = np.linalg.qr(rng.standard_normal((D_in, n)))
