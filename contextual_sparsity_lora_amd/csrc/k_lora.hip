@@ -890,22 +890,30 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
     f32x4 acc[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) acc[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int64_t cs = cw; cs < cw + SFW && cs < F; cs += 128) {
-        uint4 gv[4], uv[4], av[4][NR];
+    // the loads of a 128-channel step; step cs + 128's go out before step cs
+    // is processed
+    uint4 gv[4], uv[4], av[4][NR], gn[4], un[4], an[4][NR];
+    const int64_t cend = (cw + SFW < F) ? cw + SFW : F;
+    auto fetch = [&](int64_t cs, uint4 (&g4)[4], uint4 (&u4)[4], uint4 (&a4)[4][NR]) {
         const int64_t cl = cs + 8 * cg;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const int64_t m = t0 + 4 * s + rs;
             const bool ok = m < Tn && cl < F;
             const int64_t t = (rows && m < Tn) ? (int64_t)rows[m] : m;
-            gv[s] = ok ? *(const uint4*)(g + t * ldg + cl) : zero;
-            uv[s] = ok ? *(const uint4*)(u + t * ldu + cl) : zero;
+            g4[s] = ok ? *(const uint4*)(g + t * ldg + cl) : zero;
+            u4[s] = ok ? *(const uint4*)(u + t * ldu + cl) : zero;
 #pragma unroll
             for (int k = 0; k < NR; ++k) {
                 const int64_t j = 16 * k + rr, c = cs + 32 * s + 8 * kq;
-                av[s][k] = (c < F && j < r) ? *(const uint4*)(A + j * lda + c) : zero;
+                a4[s][k] = (c < F && j < r) ? *(const uint4*)(A + j * lda + c) : zero;
             }
         }
+    };
+    if (cw < cend) fetch(cw, gv, uv, av);
+    for (int64_t cs = cw; cs < cend; cs += 128) {
+        const int64_t cl = cs + 8 * cg;
+        if (cs + 128 < cend) fetch(cs + 128, gn, un, an);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             float gf[8], uf[8];
@@ -939,6 +947,15 @@ __global__ __launch_bounds__(256) void swiglu_fwd_lora_kernel(
             }
         }
         wave_lds_sync();
+        if (cs + 128 < cend) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                gv[s] = gn[s];
+                uv[s] = un[s];
+#pragma unroll
+                for (int k = 0; k < NR; ++k) av[s][k] = an[s][k];
+            }
+        }
     }
     // lane holds D[4 (l / 16) + i][l % 16]: row t0 + 4 kq + i, rank 16 k + rr
 #pragma unroll
