@@ -1102,8 +1102,17 @@ __global__ __launch_bounds__(256) void chunk_sum_kernel(const float* __restrict_
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (q >= Adim * r) return;
     const int64_t a = q / r, j = q % r;
+    // (eight chunks' loads go out together; the sum keeps chunk order)
     float s = 0.0f;
-    for (int64_t ch = 0; ch < nch; ++ch) s += part[(ch * Adim + a) * RW + j];
+    int64_t ch = 0;
+    for (; ch + 8 <= nch; ch += 8) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = part[((ch + e) * Adim + a) * RW + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[e];
+    }
+    for (; ch < nch; ++ch) s += part[(ch * Adim + a) * RW + j];
     const int64_t ao = amap ? (int64_t)amap[a] : a;   // output row of partial row a
     out[ao * soa + j * soj] = scale * s;
 }
@@ -1123,7 +1132,15 @@ __global__ __launch_bounds__(256) void chunk_sum3_kernel(const float* __restrict
     const int64_t a = q / r, j = q % r;
     const float* __restrict__ pp = part + p * pstride;
     float s = 0.0f;
-    for (int64_t ch = 0; ch < nch; ++ch) s += pp[(ch * Adim + a) * RW + j];
+    int64_t ch = 0;
+    for (; ch + 8 <= nch; ch += 8) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = pp[((ch + e) * Adim + a) * RW + j];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s += v[e];
+    }
+    for (; ch < nch; ++ch) s += pp[(ch * Adim + a) * RW + j];
     o.out[p][a * o.soa[p] + j * o.soj[p]] = scale * s;
 }
 
