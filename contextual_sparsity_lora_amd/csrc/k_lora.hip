@@ -458,6 +458,7 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
     float scale, const bf16_t* __restrict__ Yc, int64_t ldyc, const int32_t* __restrict__ idx, int64_t n) {
     constexpr int KS = (R + 31) / 32;     // 32-wide rank steps
     __shared__ __attribute__((aligned(16))) bf16_t tile[4][16][128 + 8];
+    __shared__ __attribute__((aligned(16))) bf16_t cb[4][16][136];   // compact runs of the wave's 16 rows
     static_assert(MTW == 16 || MTW == 32 || MTW == 64, "rows per wave");
     const int lane = threadIdx.x & 63, wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t c0 = (int64_t)blockIdx.x * 128;
@@ -504,7 +505,16 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
     // without a selected channel puts its value in the tile's padding columns.
     const bool any = j1 > j0, run64 = j1 - j0 > 64;      // wave-uniform
     const int ds0 = has0 ? sl0 : 128 + (lane & 7), ds1 = has1 ? sl1 : 128 + (lane & 7);
-    const int64_t jc0 = has0 ? j0 + lane : j0, jc1 = has1 ? j0 + 64 + lane : j0;
+    // the compact values of a row's run (positions j0 .. j1) come in as
+    // 16-byte chunks from jb = j0 rounded down to 8 (lane l: chunk l % 16 of
+    // row 4 s + l / 16; lanes 0-15 also chunk 16 of row l when the run needs
+    // it); the chunks go to the wave's LDS rows cb, from which lane l takes
+    // its entry j0 + l (and j0 + 64 + l) at og + l (og + 64 + l)
+    const int64_t jb = j0 & ~(int64_t)7;
+    const int og = (int)(j0 - jb);
+    const bool two = j1 - jb > 128;                       // a 17th chunk (wave-uniform)
+    const int cq = lane & 15, rq = lane >> 4;
+    const bool ldc = jb + 8 * cq < j1, ldc17 = two && jb + 128 < j1 && lane < 16;
     const bool pfast = lora && pvec && r % 8 == 0;        // whole 8-rank runs of P
     const bool aligned = (ldy % 8 == 0) && (((uintptr_t)y & 15) == 0);
     const bool whole = aligned && c0 + 128 <= C;
@@ -534,13 +544,17 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
                 for (int q = 0; q < 8; ++q) pv[ks][q] = (lora && mv && k + q < r) ? P[row * ldp + k + q] : 0.0f;
             }
         }
-        bf16_t cv0[16], cv1[16];
+        uint4 cc[4], cx = make_uint4(0u, 0u, 0u, 0u);
         if (any) {
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) {
-                const bf16_t* yc = Yc + (tg + rr < nrows ? tg + rr : nrows - 1) * ldyc;
-                cv0[rr] = yc[jc0];
-                cv1[rr] = run64 ? yc[jc1] : (bf16_t)0;
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int64_t mr = tg + 4 * s4 + rq;
+                const bf16_t* yc = Yc + (mr < nrows ? mr : nrows - 1) * ldyc;
+                cc[s4] = ldc ? *(const uint4*)(yc + jb + 8 * cq) : make_uint4(0u, 0u, 0u, 0u);
+            }
+            if (ldc17) {
+                const int64_t mr = tg + lane;
+                cx = *(const uint4*)(Yc + (mr < nrows ? mr : nrows - 1) * ldyc + jb + 128);
             }
         }
         bf16x8 pb[KS];
@@ -573,14 +587,18 @@ __global__ __launch_bounds__(256) void lora_merge_rows_kernel(
         }
         // (this wave's own LDS rows: in-order LDS access within the wave)
         wave_lds_sync();
-        // the selected channels from the compact rows
+        // the selected channels from the compact rows, through cb
         if (any) {
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds0] = cv0[rr];
-        }
-        if (run64) {
+            for (int s4 = 0; s4 < 4; ++s4) *(uint4*)&cb[wid][4 * s4 + rq][8 * cq] = cc[s4];
+            if (two && lane < 16) *(uint4*)&cb[wid][lane][128] = cx;
+            wave_lds_sync();
 #pragma unroll
-            for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds1] = cv1[rr];
+            for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds0] = cb[wid][rr][og + lane];
+            if (run64) {
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) tile[wid][rr][ds1] = cb[wid][rr][og + 64 + lane];
+            }
         }
         wave_lds_sync();
 #pragma unroll
