@@ -185,7 +185,7 @@ hipError_t launch_token_split(const uint8_t* roles, int64_t T, int32_t* ctx, int
 hipError_t launch_stage1(const void* x, bool bf16, int64_t ldx, const int32_t* rows, int64_t Tc,
                          int64_t D, const float* WA_t, int64_t kt, float* xa, hipStream_t st);
 // part: 64 * C floats of scratch for the chain-split form (C < SSQ_SPLIT_C, k = 16), or null
-constexpr int64_t SSQ_SPLIT_C = 8192;
+constexpr int64_t SSQ_SPLIT_C = 16384;
 hipError_t launch_ssq(int crit, const float* xa, int64_t ld, int64_t Tc, int64_t off0,
                       const float* WB0, int64_t off1, const float* WB1, int64_t k, int64_t C,
                       float* ssq, hipStream_t st, float* part = nullptr);
